@@ -1,0 +1,7 @@
+"""Sign-Muon optimizer step for MI355X (gfx950): HIP kernels behind a C ABI.
+
+The compute path lives in ``libsignmuon.so`` (built from ``csrc/``); the
+Python side only marshals arguments (see ``binding``).  ``workloads`` holds
+seeded synthetic inputs.
+"""
+__all__ = ["binding", "workloads"]
