@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Sign-Muon optimizer-step benchmark on one MI355X.
+
+Times the fused step (signmuon_step: momentum sweep, PolarNS by Newton-Schulz
+on the matrix cores, sign + 1-bit pack into the local worker's buffer, vote
+over the M resident packed buffers fused with the update of W) on a synthetic
+parameter set with all inputs resident in HBM.  Prints one JSON line with
+steps/s, a per-phase breakdown measured with HIP events recorded on the
+launch stream inside every timed step, the roofline of the dominant kernel
+(the Newton-Schulz GEMM) and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload nanogpt]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Sign-Muon steps/s on nanoGPT-124M params; NS MFMA util %; vote GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
+PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 matrix-core peak
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+
+def hip_runtime():
+    L = ctypes.CDLL("libamdhip64.so")
+    L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    return L
+
+
+def describe(w):
+    shapes = {}
+    for s in w.mats:
+        shapes[s] = shapes.get(s, 0) + 1
+    parts = ", ".join(f"{n}x({r}x{c})" for (r, c), n in shapes.items())
+    ns = {"f32": "f32", "bf16": "bf16 operands / f32 accumulate",
+          "bf16x3": "split-bf16 (x3)"}[w.ns_precision]
+    coeffs = "quintic" if w.coeffs[2] else "cubic"
+    return (f"{w.name}: {parts}; W {w.w_dtype}, momentum f32; M={w.M} resident packed "
+            f"sign buffers; K={w.K} {coeffs} Newton-Schulz ({ns}), {w.scale} scaling"
+            + (f" P={w.P}" if w.scale == "spectral" else "")
+            + ("; post-vote polar" if w.post_vote else ""))
+
+
+def cpu_baseline(w, budget_s):
+    """Oracle seconds per step on a bounded sample, scaled to the whole set."""
+    import oracle as O
+    from distributed_bit_matrix_amd import workloads as WL
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:   # threadpoolctl missing: report the visible CPUs
+        cores = os.cpu_count()
+    # sample: the first 1/L of the matrices (one transformer layer for the
+    # nanoGPT set), worker 0's pipeline + vote over M + apply
+    per_layer = 4 if w.name == "nanogpt" else 1
+    n_layers = len(w.mats) // per_layer
+    sub = WL.scaled(w, w.mats[:per_layer], name=w.name + "-sample")
+    hp = dict(eta=w.eta, beta=w.beta, lam=w.lam, eps=w.eps, K=w.K, scale=w.scale,
+              P=w.P, coeffs=w.coeffs)
+    W = WL.init_weights(sub).astype(np.float64)
+    Mom = np.zeros(sub.d)
+    G = WL.gradient(sub, 0, 0).astype(np.float64)
+    others = WL.random_bits(sub, w.M)
+    u0s = WL.power_start(sub) if w.scale == "spectral" else None
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        Mn = O.momentum_update(Mom, G, W, hp["beta"], hp["lam"])
+        bits = others.copy()
+        for i, ((r, c), off, woff) in enumerate(zip(sub.mats, sub.elem_offsets,
+                                                    sub.word_offsets)):
+            U, _ = O.polar_ns(Mn[off:off + r * c].reshape(r, c), hp["K"], hp["eps"],
+                              hp["scale"], hp["P"], hp["coeffs"],
+                              None if u0s is None else u0s[i])
+            bits[0, woff:woff + (r * c + 31) // 32] = O.pack_signs(U)
+            sums = O.vote_sums_from_bits(bits[:, woff:woff + (r * c + 31) // 32], r * c)
+            D = O.majority_from_sums(sums, w.tie_value)
+            O.apply_update(W[off:off + r * c], D, hp["eta"], w.w_dtype)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all > budget_s or len(times) >= 5:
+            break
+    t_sample = float(np.median(times))
+    t_step = t_sample * n_layers
+    return {"value": 1.0 / t_step, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"{per_layer} of {len(w.mats)} matrices ({sub.d} of {w.d} parameters), "
+                       f"worker-0 momentum + float64 Newton-Schulz + pack, vote over M={w.M} "
+                       f"and apply; median of {len(times)} runs = {t_sample:.3f} s, "
+                       f"x{n_layers} for the whole set"),
+            "seconds_per_step": t_step}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="nanogpt")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        sys.exit("bench.py measures one GPU: the method's M workers are resident sign "
+                 "buffers on a single MI355X; --gpus above 1 is not supported")
+
+    import torch
+    from distributed_bit_matrix_amd import binding as B
+    from distributed_bit_matrix_amd import workloads as WL
+
+    w = WL.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hp = B.HParams(eta=w.eta, beta=w.beta, lam=w.lam, eps=w.eps, K=w.K, scale=w.scale,
+                   P=w.P, coeffs=w.coeffs, precision=w.ns_precision,
+                   tie_value=w.tie_value)
+    layout, d, words = B.default_layout(w.mats)
+    plan = B.StepPlan(layout, hp, w.post_vote, device=dev)
+    wdt = torch.bfloat16 if w.w_dtype == "bf16" else torch.float32
+    W = torch.from_numpy(WL.init_weights(w)).to(dev).to(wdt)
+    Mom = torch.zeros(d, dtype=torch.float32, device=dev)
+    G = torch.from_numpy(WL.gradient(w, 0, 0)).to(dev)
+    bits = torch.from_numpy(WL.random_bits(w, w.M).view(np.int32)).to(dev)
+    u0 = (torch.from_numpy(np.concatenate(WL.power_start(w))).to(dev)
+          if w.scale == "spectral" else None)
+    torch.cuda.synchronize()
+
+    def step():
+        plan(G, W, Mom, bits, words, w.M, 0, u0=u0)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # events for the instrumented steps of the timed region
+    hip = hip_runtime()
+    cap = 64
+    K = args.steps
+    evs = (ctypes.c_void_p * (cap * K))()
+    ev_list = []
+    for i in range(cap * K):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        ev_list.append(e.value)
+        evs[i] = e.value
+    kinds = (ctypes.c_int32 * (cap * K))()
+    profs = []
+    for k in range(K):
+        p = B.SmProfile()
+        p.events = ctypes.cast(ctypes.byref(evs, k * cap * ctypes.sizeof(ctypes.c_void_p)),
+                               ctypes.POINTER(ctypes.c_void_p))
+        p.kinds = ctypes.cast(ctypes.byref(kinds, k * cap * 4), ctypes.POINTER(ctypes.c_int32))
+        p.capacity = cap
+        p.count = 0
+        profs.append(p)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        plan.profiled(profs[k], G, W, Mom, bits, words, w.M, 0, u0=u0)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # per-phase durations from consecutive events of each step
+    phase = {}
+    gemm_launches = 0
+    ms = ctypes.c_float()
+    for k in range(K):
+        p = profs[k]
+        base = k * cap
+        for i in range(1, p.count):
+            hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(evs[base + i - 1]),
+                                    ctypes.c_void_p(evs[base + i]))
+            name = B.PHASES[kinds[base + i]]
+            phase[name] = phase.get(name, 0.0) + ms.value * 1e3
+            if name == "gemm":
+                gemm_launches += 1
+    for e in ev_list:
+        hip.hipEventDestroy(ctypes.c_void_p(e))
+    phase_us = {k: v / K for k, v in phase.items()}
+    gemm_us = phase_us.get("gemm", float("nan"))
+    gemm_per_step = gemm_launches / K
+
+    ns_flop = w.ns_gflop() * 1e9
+    ns_tflops = ns_flop / (gemm_us * 1e-6) / 1e12
+    peak = PEAK_F32_TFLOPS if w.ns_precision == "f32" else PEAK_BF16_TFLOPS
+    wbytes = 2 if w.w_dtype == "bf16" else 4
+    vote_bytes = (w.M / 8.0 + 2 * wbytes) * d
+    vote_gbps = vote_bytes / (phase_us.get("vote", float("nan")) * 1e-6) / 1e9
+    mom_bytes = (4 + wbytes + 4 + 4 + 2) * d
+    mom_gbps = mom_bytes / (phase_us.get("momentum", float("nan")) * 1e-6) / 1e9
+
+    steps_per_s = K / elapsed
+    out = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.ns_precision != "f32" else "f32",
+        "data": "synthetic",
+        "config": {"workload": describe(w), "params": d, "matrices": len(w.mats),
+                   "workers": w.M, "reading": "local worker pipeline + vote over M "
+                   "resident buffers + apply"},
+        "roofline": {"bound": "mfma", "achieved": round(ns_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(ns_tflops / peak, 4),
+                     "traffic": None, "kernel": "k_gemm (Newton-Schulz products)",
+                     "launches_per_step": gemm_per_step,
+                     "avg_launch_us": round(gemm_us / max(gemm_per_step, 1), 2)},
+        "ns_mfma_util_pct": round(100 * ns_tflops / peak, 2),
+        "vote_gbps": round(vote_bytes / (phase_us.get("vote", float("nan")) * 1e-6) / 1e9, 1),
+        "vote_frac_hbm": round(vote_gbps / PEAK_HBM_GBPS, 4),
+        "momentum_gbps": round(mom_gbps, 1),
+        "phases_us": {k: round(v, 2) for k, v in phase_us.items()},
+    }
+    if args.cpu_budget > 0:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,806 @@
+// C ABI of libsignmuon: argument validation, the workspace plan, grouping of
+// matrices into launch runs, and the order of kernels of one step.
+//
+// Step order (SignMuon paper, Algorithm 2 and Figure 1, for the local
+// worker; the other workers' buffers are already resident):
+//   momentum sweep  -> padded operand copy of Mom, partial sums, status
+//   pre-scale       -> c = 1/(s+eps) per matrix (Frobenius from the partial
+//                      sums; spectral from P power steps on the raw Gram)
+//   K Newton-Schulz steps, each a Gram GEMM and an update GEMM (the quintic
+//   adds the A*A GEMM); the last update's epilogue packs sign(U) straight
+//   into the local worker's buffer
+//   vote over the M buffers fused with W <- W - eta * majority.
+// Post-vote variant: momentum + sign-pack, vote -> majority matrix, PolarNS
+// of the majority matrix whose last epilogue applies W <- W - eta * U.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "sm_internal.h"
+#include "sm_launch.h"
+
+using namespace sm;
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+constexpr int64_t kMaxDim = 1 << 20;          // rows / cols
+constexpr int64_t kMaxPadded = (int64_t)1 << 31;  // padded rows * cols
+
+bool finite(float x) { return std::isfinite(x); }
+
+sm_status check_hparams(const sm_hparams* hp, bool need_momentum) {
+  if (!hp) return SM_EINVAL;
+  if (!finite(hp->eps) || hp->eps <= 0.f) return SM_EINVAL;
+  if (hp->K < 0 || hp->K > 64) return SM_EINVAL;
+  if (hp->scale != SM_SCALE_FRO && hp->scale != SM_SCALE_SPECTRAL) return SM_EINVAL;
+  if (hp->scale == SM_SCALE_SPECTRAL && (hp->P < 1 || hp->P > 256)) return SM_EINVAL;
+  if (!finite(hp->ns_a) || !finite(hp->ns_b) || !finite(hp->ns_c)) return SM_EINVAL;
+  if (hp->ns_precision < SM_NS_F32 || hp->ns_precision > SM_NS_BF16X3) return SM_EINVAL;
+  if (need_momentum) {
+    if (!finite(hp->beta) || hp->beta < 0.f || hp->beta >= 1.f) return SM_EINVAL;
+    if (!finite(hp->lambda) || hp->lambda < 0.f) return SM_EINVAL;
+    if (!finite(hp->eta)) return SM_EINVAL;
+    if (hp->tie_value != 0 && hp->tie_value != 1) return SM_EINVAL;
+  }
+  return SM_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Per-matrix placement.  Returns SM_OK or SM_EINVAL for unusable shapes.
+sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
+                     bool post_vote, bool need_u, Plan& P,
+                     std::vector<MatPlan>& mp) {
+  mp.assign(nm, MatPlan{});
+  P = Plan{};
+  P.nm = nm;
+  P.precision = hp->ns_precision == SM_NS_F32 ? P_F32
+              : hp->ns_precision == SM_NS_BF16X3 ? P_BF16X3 : P_BF16;
+  P.quintic = hp->ns_c != 0.0f;
+  P.spectral = hp->scale == SM_SCALE_SPECTRAL;
+  int64_t x = 0, r2 = 0, v = 0, c = 0, u0 = 0, umax = 0;
+  for (int i = 0; i < nm; ++i) {
+    const sm_matrix& m = mats[i];
+    if (m.rows < 1 || m.cols < 1 || m.rows > kMaxDim || m.cols > kMaxDim) return SM_EINVAL;
+    if (m.elem_off < 0 || m.word_off < 0) return SM_EINVAL;
+    MatPlan& q = mp[i];
+    q.rows = m.rows; q.cols = m.cols;
+    q.r = std::min(m.rows, m.cols);
+    q.tall = m.rows > m.cols;
+    q.Mp = round_up(m.rows, kPad);
+    q.Np = round_up(m.cols, kPad);
+    q.Rp = round_up(q.r, kPad);
+    if (q.Mp * q.Np >= kMaxPadded) return SM_EINVAL;
+    q.elem_off = m.elem_off; q.word_off = m.word_off;
+    q.x_off = x; x += q.Mp * q.Np;
+    q.r_off = r2; r2 += q.Rp * q.Rp;
+    q.v_off = v; v += q.Rp;
+    q.u0_off = u0; u0 += q.r;
+    int64_t nw = (m.rows * m.cols + 31) / 32;
+    q.chunks = std::max<int64_t>(q.Mp * q.Np / kChunk, (nw + 255) / 256);
+    q.c_off = c; c += q.chunks;
+    q.idx = i;
+    umax = std::max<int64_t>(umax, m.elem_off + m.rows * m.cols);
+  }
+  P.x_total = x; P.r_total = r2; P.v_total = v; P.c_total = c;
+  const size_t opb = P.precision == P_F32 ? 4 : 2;   // bytes per operand part
+  const bool split = P.precision == P_BF16X3;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  take(256);                                  // status word (+ padding)
+  P.off_status = 0;
+  const bool ns = hp->K > 0;
+  for (int pp = 0; pp < (ns ? 2 : 1); ++pp) {
+    P.off_x[pp][0] = take(x * opb);
+    if (split) P.off_x[pp][1] = take(x * opb);
+  }
+  if (ns) {
+    P.off_b[0] = take(r2 * opb);
+    if (split) P.off_b[1] = take(r2 * opb);
+    if (P.quintic) {
+      P.off_a[0] = take(r2 * opb);
+      if (split) P.off_a[1] = take(r2 * opb);
+    }
+  }
+  if (P.spectral) {
+    P.off_araw = take(r2 * 4);
+    P.off_vec = take(2 * v * 4);
+  }
+  P.off_part = take(c * 4);
+  P.off_scal = take((size_t)nm * 4);
+  if (need_u) P.off_u = take(umax * 4);
+  (void)post_vote;
+  P.total = off;
+  return SM_OK;
+}
+
+// Split matrices (a subset, by index) into runs of equal shape and constant
+// strides of every offset family.
+std::vector<Group> make_groups(const std::vector<MatPlan>& mp,
+                               const std::vector<int>& sel) {
+  std::vector<Group> out;
+  for (size_t t = 0; t < sel.size(); ++t) {
+    const MatPlan& q = mp[sel[t]];
+    if (!out.empty()) {
+      Group& g = out.back();
+      const MatPlan& f = mp[g.idx0];
+      if (g.rows == q.rows && g.cols == q.cols) {
+        int64_t k = g.count;
+        if (g.count == 1) {
+          int64_t de = q.elem_off - f.elem_off, dw = q.word_off - f.word_off;
+          if (de > 0 && dw >= 0 && q.idx - f.idx > 0) {
+            g.elem_stride = de; g.word_stride = dw;
+            g.x_stride = q.x_off - f.x_off; g.r_stride = q.r_off - f.r_off;
+            g.v_stride = q.v_off - f.v_off; g.u0_stride = q.u0_off - f.u0_off;
+            g.c_stride = q.c_off - f.c_off; g.idx_stride = q.idx - f.idx;
+            g.count = 2;
+            continue;
+          }
+        } else if (q.elem_off == f.elem_off + k * g.elem_stride &&
+                   q.word_off == f.word_off + k * g.word_stride &&
+                   q.x_off == f.x_off + k * g.x_stride &&
+                   q.r_off == f.r_off + k * g.r_stride &&
+                   q.v_off == f.v_off + k * g.v_stride &&
+                   q.u0_off == f.u0_off + k * g.u0_stride &&
+                   q.c_off == f.c_off + k * g.c_stride &&
+                   q.idx == f.idx + k * g.idx_stride) {
+          g.count += 1;
+          continue;
+        }
+      }
+    }
+    Group g;
+    std::memset(&g, 0, sizeof(g));
+    g.count = 1;
+    g.rows = (int32_t)q.rows; g.cols = (int32_t)q.cols;
+    g.idx0 = q.idx; g.idx_stride = 0;
+    g.elem0 = q.elem_off; g.word0 = q.word_off;
+    g.x0 = q.x_off; g.r0 = q.r_off; g.v0 = q.v_off; g.u0_0 = q.u0_off;
+    g.c0 = q.c_off;
+    out.push_back(g);
+  }
+  return out;
+}
+
+// Issue one kernel per chunk of at most kMaxGroups runs.  `fill` sets the
+// per-group launch fields (blocks_per_mat, gm, gn, gk, tiles_n, ops) and
+// returns false to drop a group; `go` launches.
+template <class Fill, class Go>
+hipError_t for_launches(const std::vector<Group>& groups, Fill fill, Go go) {
+  std::vector<Group> gs;
+  for (const Group& g0 : groups) {
+    Group g = g0;
+    if (fill(g)) gs.push_back(g);
+  }
+  for (size_t s = 0; s < gs.size(); s += kMaxGroups) {
+    Groups G;
+    std::memset(&G, 0, sizeof(G));
+    int64_t blocks = 0;
+    size_t e = std::min(gs.size(), s + kMaxGroups);
+    for (size_t i = s; i < e; ++i) {
+      Group g = gs[i];
+      g.block0 = (int32_t)blocks;
+      blocks += (int64_t)g.blocks_per_mat * g.count;
+      G.g[G.n++] = g;
+    }
+    if (blocks == 0) continue;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    G.total_blocks = (int32_t)blocks;
+    hipError_t err = go(G);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+struct Bufs {
+  char* base;
+  int32_t* status;
+  void* x[2][2];
+  void* b[2];
+  void* a[2];
+  float* araw;
+  float* vec;
+  float* part;
+  float* scal;
+  float* u;
+};
+
+Bufs bind(const Plan& P, void* ws) {
+  Bufs B;
+  std::memset(&B, 0, sizeof(B));
+  B.base = static_cast<char*>(ws);
+  auto at = [&](size_t off) -> void* { return off ? B.base + off : nullptr; };
+  B.status = reinterpret_cast<int32_t*>(B.base + P.off_status);
+  for (int p = 0; p < 2; ++p)
+    for (int h = 0; h < 2; ++h) B.x[p][h] = at(P.off_x[p][h]);
+  B.b[0] = at(P.off_b[0]); B.b[1] = at(P.off_b[1]);
+  B.a[0] = at(P.off_a[0]); B.a[1] = at(P.off_a[1]);
+  B.araw = static_cast<float*>(at(P.off_araw));
+  B.vec = static_cast<float*>(at(P.off_vec));
+  B.part = static_cast<float*>(at(P.off_part));
+  B.scal = static_cast<float*>(at(P.off_scal));
+  B.u = static_cast<float*>(at(P.off_u));
+  return B;
+}
+
+std::once_flag g_attr_once[64];
+hipError_t g_attr_err[64];
+
+hipError_t ensure_attributes() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return gemm_set_attributes();
+  std::call_once(g_attr_once[dev], [&] { g_attr_err[dev] = gemm_set_attributes(); });
+  return g_attr_err[dev];
+}
+
+#define HIP_TRY(x)                         \
+  do {                                     \
+    hipError_t _e = (x);                   \
+    if (_e != hipSuccess) return SM_EHIP;  \
+  } while (0)
+
+// Event after a phase (instrumented step only).
+hipError_t mark(sm_profile* prof, int kind, hipStream_t s) {
+  if (!prof || prof->count >= prof->capacity) return hipSuccess;
+  hipError_t e = hipEventRecord(prof->events[prof->count], s);
+  prof->kinds[prof->count++] = kind;
+  return e;
+}
+
+// ---------------------------------------------------------------------------
+// PolarNS pipeline over all matrices of a plan, starting from the padded
+// operand copy in x[0] with partial sums in part (Frobenius).
+//   first: XS_USER (src_user in caller layout, e.g. the momentum) or XS_OP
+//   (the operand copy itself, e.g. the majority matrix).
+//   final: O_U (write U), O_BITS (pack into bits), O_APPLY (update W).
+// `fusable[i]` says whether matrix i may use O_BITS; others write U into
+// the workspace and are packed afterwards.
+// ---------------------------------------------------------------------------
+struct NsIO {
+  int first_xsrc;
+  const float* src_user;
+  int final_out;
+  float* U;
+  uint32_t* bits;         // local worker buffer base
+  void* W; int w_bf16; float eta;
+  const float* u0;
+  const int32_t* status;
+  sm_profile* prof;
+};
+
+sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
+                        const std::vector<Group>& groups, const sm_hparams* hp,
+                        Bufs& B, const NsIO& io, int part_kind,
+                        hipStream_t s) {
+  const int prec = P.precision;
+  const bool quin = P.quintic;
+  const float gram_mul = quin ? 1.0f : hp->ns_b;   // cubic folds b into B
+  // operand that receives the scaled first Gram
+  void* dst_hi = quin ? B.a[0] : B.b[0];
+  void* dst_lo = quin ? B.a[1] : B.b[1];
+  auto gram_fill = [&](Group& g) {
+    const MatPlan& q = mp[g.idx0];
+    g.gm = g.gn = (int32_t)q.Rp;
+    g.gk = (int32_t)(q.tall ? q.Mp : q.Np);
+    g.tiles_n = (int32_t)(q.Rp / 128);
+    g.blocks_per_mat = g.tiles_n * g.tiles_n;
+    g.ops = q.tall ? gemm_ops(FAM_X, 0, FAM_X, 0) : gemm_ops(FAM_X, 1, FAM_X, 1);
+    return true;
+  };
+  if (!P.spectral) {
+    HIP_TRY(for_launches(groups, [&](Group& g) {
+      g.blocks_per_mat = 1;
+      g.gk = (int32_t)(part_kind == 0 ? mp[g.idx0].Mp * mp[g.idx0].Np / kChunk
+                                      : (((mp[g.idx0].rows * mp[g.idx0].cols + 31) / 32) + 255) / 256);
+      return true;
+    }, [&](const Groups& G) { return launch_fro_finalize(G, B.part, hp->eps, B.scal, s); }));
+    HIP_TRY(mark(io.prof, SM_PHASE_PRESCALE, s));
+    if (hp->K == 0) return SM_OK;
+    HIP_TRY(for_launches(groups, gram_fill, [&](const Groups& G) {
+      GemmArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.G = G;
+      a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
+      a.epi = E_OP; a.mul = gram_mul; a.scal = B.scal; a.scal_pow = 2;
+      a.o_hi = dst_hi; a.o_lo = dst_lo;
+      return launch_gemm(prec, a, s);
+    }));
+    HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+  } else {
+    HIP_TRY(for_launches(groups, gram_fill, [&](const Groups& G) {
+      GemmArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.G = G;
+      a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
+      a.epi = E_RAW; a.o_raw = B.araw;
+      return launch_gemm(prec, a, s);
+    }));
+    HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+    float* va = B.vec;
+    float* vb = B.vec + P.v_total;
+    HIP_TRY(for_launches(groups, [&](Group& g) {
+      g.blocks_per_mat = (int32_t)((mp[g.idx0].Rp + 255) / 256);
+      return true;
+    }, [&](const Groups& G) { return launch_power_init(G, io.u0, va, s); }));
+    for (int p = 0; p < hp->P; ++p) {
+      HIP_TRY(for_launches(groups, [&](Group& g) {
+        g.blocks_per_mat = (int32_t)(mp[g.idx0].Rp / 64);
+        return true;
+      }, [&](const Groups& G) { return launch_power_step(G, B.araw, va, vb, s); }));
+      std::swap(va, vb);
+    }
+    HIP_TRY(for_launches(groups, [&](Group& g) { g.blocks_per_mat = 1; return true; },
+                         [&](const Groups& G) {
+                           return launch_power_finalize(G, va, hp->eps, B.scal, s);
+                         }));
+    HIP_TRY(mark(io.prof, SM_PHASE_PRESCALE, s));
+    if (hp->K == 0) return SM_OK;
+    HIP_TRY(for_launches(groups, [&](Group& g) {
+      g.blocks_per_mat = (int32_t)(mp[g.idx0].Rp * mp[g.idx0].Rp / kChunk);
+      return true;
+    }, [&](const Groups& G) {
+      return launch_prescale(G, prec, B.araw, B.scal, gram_mul, dst_hi, dst_lo, s);
+    }));
+    HIP_TRY(mark(io.prof, SM_PHASE_PRESCALE, s));
+  }
+  return SM_OK;
+}
+
+// B = b A + c A^2 from the operand A (quintic).
+hipError_t run_square(const Plan& P, const std::vector<MatPlan>& mp,
+                      const std::vector<Group>& groups, const sm_hparams* hp,
+                      Bufs& B, hipStream_t s) {
+  return for_launches(groups, [&](Group& g) {
+    const MatPlan& q = mp[g.idx0];
+    g.gm = g.gn = g.gk = (int32_t)q.Rp;
+    g.tiles_n = (int32_t)(q.Rp / 128);
+    g.blocks_per_mat = g.tiles_n * g.tiles_n;
+    g.ops = gemm_ops(FAM_R, 1, FAM_R, 1);
+    return true;
+  }, [&](const Groups& G) {
+    GemmArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.G = G;
+    a.r_hi = B.a[0]; a.r_lo = B.a[1];
+    a.epi = E_SQUARE; a.cb = hp->ns_b; a.cc = hp->ns_c;
+    a.sq_hi = B.a[0]; a.sq_lo = B.a[1];
+    a.o_hi = B.b[0]; a.o_lo = B.b[1];
+    return launch_gemm(P.precision, a, s);
+  });
+}
+
+sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
+                 const std::vector<Group>& groups, const std::vector<bool>& fusable,
+                 const sm_hparams* hp, Bufs& B, const NsIO& io, hipStream_t s) {
+  const int prec = P.precision;
+  const int K = hp->K;
+  int cur = 0;
+  for (int k = 1; k <= K; ++k) {
+    if (k > 1) {
+      // Gram of the current iterate: cubic -> B = b A, quintic -> A
+      HIP_TRY(for_launches(groups, [&](Group& g) {
+        const MatPlan& q = mp[g.idx0];
+        g.gm = g.gn = (int32_t)q.Rp;
+        g.gk = (int32_t)(q.tall ? q.Mp : q.Np);
+        g.tiles_n = (int32_t)(q.Rp / 128);
+        g.blocks_per_mat = g.tiles_n * g.tiles_n;
+        g.ops = q.tall ? gemm_ops(FAM_X, 0, FAM_X, 0) : gemm_ops(FAM_X, 1, FAM_X, 1);
+        return true;
+      }, [&](const Groups& G) {
+        GemmArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.G = G;
+        a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
+        a.epi = E_OP; a.mul = P.quintic ? 1.0f : hp->ns_b; a.scal_pow = 0;
+        a.o_hi = P.quintic ? B.a[0] : B.b[0];
+        a.o_lo = P.quintic ? B.a[1] : B.b[1];
+        return launch_gemm(prec, a, s);
+      }));
+      HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+    }
+    if (P.quintic) {
+      HIP_TRY(run_square(P, mp, groups, hp, B, s));
+      HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+    }
+    // update: X <- a X + B X (wide) / a X + X B (tall)
+    const bool last = k == K;
+    for (int pass = 0; pass < 2; ++pass) {
+      // pass 0: matrices using the requested final output; pass 1: the
+      // unfusable ones writing U into the workspace (only when last).
+      if (pass == 1 && !(last && io.final_out == O_BITS)) break;
+      HIP_TRY(for_launches(groups, [&](Group& g) {
+        const MatPlan& q = mp[g.idx0];
+        if (last && io.final_out == O_BITS && fusable[g.idx0] != (pass == 0)) return false;
+        g.gm = (int32_t)q.Mp; g.gn = (int32_t)q.Np;
+        g.gk = (int32_t)q.Rp;
+        g.tiles_n = (int32_t)(q.Np / 128);
+        g.blocks_per_mat = (int32_t)((q.Mp / 128) * g.tiles_n);
+        g.ops = q.tall ? gemm_ops(FAM_X, 1, FAM_R, 1) : gemm_ops(FAM_R, 1, FAM_X, 0);
+        return true;
+      }, [&](const Groups& G) {
+        GemmArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.G = G;
+        a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
+        a.r_hi = B.b[0]; a.r_lo = B.b[1];
+        a.epi = E_UPDATE; a.ca = hp->ns_a;
+        a.xsrc = k == 1 ? io.first_xsrc : XS_OP;
+        a.scal = B.scal; a.scal_pow = k == 1 ? 1 : 0;
+        a.xs_user = io.src_user;
+        a.xs_hi = B.x[cur][0]; a.xs_lo = B.x[cur][1];
+        if (!last) {
+          a.out = O_X;
+          a.o_hi = B.x[cur ^ 1][0]; a.o_lo = B.x[cur ^ 1][1];
+        } else if (io.final_out == O_BITS && pass == 1) {
+          a.out = O_U; a.U = B.u;
+        } else {
+          a.out = io.final_out;
+          a.U = io.U; a.bits = io.bits;
+          a.W = io.W; a.w_bf16 = io.w_bf16; a.eta = io.eta;
+          a.status = io.status;
+        }
+        return launch_gemm(prec, a, s);
+      }));
+      HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+    }
+    cur ^= 1;
+  }
+  return SM_OK;
+}
+
+void set_vec_ok(std::vector<Group>& groups, bool ptrs_aligned) {
+  for (Group& g : groups)
+    g.vec_ok = ptrs_aligned && g.elem0 % 8 == 0 && g.elem_stride % 8 == 0 &&
+               g.cols % 8 == 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+// ===========================================================================
+// Exported entry points
+// ===========================================================================
+extern "C" {
+
+const char* signmuon_strerror(int status) {
+  switch (status) {
+    case SM_OK: return "ok";
+    case SM_EINVAL: return "invalid argument";
+    case SM_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case SM_EHIP: return "HIP runtime or launch error";
+    case SM_ENONFINITE: return "non-finite gradient, weight or momentum; update skipped";
+    case SM_ERANGE: return "worker count or size out of range";
+    case SM_EUNSUPPORTED: return "unsupported configuration";
+    default: return "unknown status";
+  }
+}
+
+int32_t signmuon_abi_version(void) { return kAbiVersion; }
+
+sm_status signmuon_momentum(const float* G, const void* W, int32_t w_dtype,
+                            float* Mom, int64_t n, float beta, float lambda,
+                            hipStream_t stream) {
+  if (n < 0) return SM_EINVAL;
+  if (w_dtype != SM_F32 && w_dtype != SM_BF16) return SM_EINVAL;
+  if (!finite(beta) || beta < 0.f || beta >= 1.f) return SM_EINVAL;
+  if (!finite(lambda) || lambda < 0.f) return SM_EINVAL;
+  if (n == 0) return SM_OK;
+  if (!G || !W || !Mom) return SM_EINVAL;
+  HIP_TRY(launch_momentum_flat(G, W, w_dtype == SM_BF16, Mom, n, beta, lambda, stream));
+  return SM_OK;
+}
+
+sm_status signmuon_sign_pack(const float* U, uint32_t* bits, int64_t n,
+                             hipStream_t stream) {
+  if (n < 0) return SM_EINVAL;
+  if (n == 0) return SM_OK;
+  if (!U || !bits) return SM_EINVAL;
+  HIP_TRY(launch_sign_pack_flat(U, bits, n, stream));
+  return SM_OK;
+}
+
+sm_status signmuon_majority_vote(const uint32_t* bits, int64_t worker_stride_words,
+                                 int32_t M, int64_t n, int32_t tie_value, int8_t* D,
+                                 int16_t* sums, hipStream_t stream) {
+  if (n < 0) return SM_EINVAL;
+  if (M < 1 || M > SM_MAX_WORKERS) return SM_ERANGE;
+  if (tie_value != 0 && tie_value != 1) return SM_EINVAL;
+  if (n == 0) return SM_OK;
+  if (!bits || !D) return SM_EINVAL;
+  if (M > 1 && worker_stride_words < (n + 31) / 32) return SM_EINVAL;
+  if (worker_stride_words < 0) return SM_EINVAL;
+  HIP_TRY(launch_vote_flat(bits, worker_stride_words, M, n, tie_value, D, sums, stream));
+  return SM_OK;
+}
+
+sm_status signmuon_apply(void* W, int32_t w_dtype, const int8_t* D, const float* Df,
+                         float eta, int64_t n, hipStream_t stream) {
+  if (n < 0) return SM_EINVAL;
+  if (w_dtype != SM_F32 && w_dtype != SM_BF16) return SM_EINVAL;
+  if ((D == nullptr) == (Df == nullptr)) return SM_EINVAL;
+  if (!finite(eta)) return SM_EINVAL;
+  if (n == 0) return SM_OK;
+  if (!W) return SM_EINVAL;
+  HIP_TRY(launch_apply_flat(W, w_dtype == SM_BF16, D, Df, eta, n, stream));
+  return SM_OK;
+}
+
+size_t signmuon_polar_ns_workspace(int64_t rows, int64_t cols, const sm_hparams* hp) {
+  if (check_hparams(hp, false) != SM_OK) return 0;
+  sm_matrix m{rows, cols, 0, 0};
+  Plan P;
+  std::vector<MatPlan> mp;
+  if (build_plan(&m, 1, hp, false, false, P, mp) != SM_OK) return 0;
+  return P.total;
+}
+
+sm_status signmuon_polar_ns(const float* X, float* U, int64_t rows, int64_t cols,
+                            const sm_hparams* hp, const float* u0, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  sm_status st = check_hparams(hp, false);
+  if (st != SM_OK) return st;
+  if (!X || !U || X == U) return SM_EINVAL;
+  sm_matrix m{rows, cols, 0, 0};
+  Plan P;
+  std::vector<MatPlan> mp;
+  st = build_plan(&m, 1, hp, false, false, P, mp);
+  if (st != SM_OK) return st;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < P.total)
+    return SM_EWORKSPACE;
+  HIP_TRY(ensure_attributes());
+  Bufs B = bind(P, ws);
+  std::vector<Group> groups = make_groups(mp, {0});
+  set_vec_ok(groups, aligned16(X));
+  SweepArgs sw;
+  std::memset(&sw, 0, sizeof(sw));
+  sw.ema = 0; sw.precision = P.precision; sw.src = X;
+  sw.o_hi = B.x[0][0]; sw.o_lo = B.x[0][1]; sw.part = B.part;
+  HIP_TRY(for_launches(groups, [&](Group& g) {
+    g.blocks_per_mat = (int32_t)(mp[g.idx0].Mp * mp[g.idx0].Np / kChunk);
+    return true;
+  }, [&](const Groups& G) { sw.G = G; return launch_sweep(sw, stream); }));
+  NsIO io;
+  std::memset(&io, 0, sizeof(io));
+  io.first_xsrc = XS_USER; io.src_user = X; io.final_out = O_U; io.U = U; io.u0 = u0;
+  st = run_pre_scale(P, mp, groups, hp, B, io, 0, stream);
+  if (st != SM_OK) return st;
+  if (hp->K == 0) {
+    ScaledOutArgs so;
+    std::memset(&so, 0, sizeof(so));
+    so.precision = P.precision; so.from_op = 0; so.apply = 0;
+    so.x_user = X; so.scal = B.scal; so.U = U;
+    HIP_TRY(for_launches(groups, [&](Group& g) {
+      g.blocks_per_mat = (int32_t)((rows * cols + kChunk - 1) / kChunk);
+      return true;
+    }, [&](const Groups& G) { so.G = G; return launch_scaled_out(so, stream); }));
+    return SM_OK;
+  }
+  std::vector<bool> fus(1, true);
+  return run_ns(P, mp, groups, fus, hp, B, io, stream);
+}
+
+size_t signmuon_step_workspace(const sm_matrix* mats, int32_t n_mats,
+                               const sm_hparams* hp, int32_t post_vote) {
+  if (!mats || n_mats < 1 || n_mats > 65536) return 0;
+  if (check_hparams(hp, true) != SM_OK) return 0;
+  bool need_u = false;
+  for (int i = 0; i < n_mats; ++i)
+    if (!post_vote && hp->K > 0 && mats[i].cols % 32 != 0) need_u = true;
+  Plan P;
+  std::vector<MatPlan> mp;
+  if (build_plan(mats, n_mats, hp, post_vote != 0, need_u, P, mp) != SM_OK) return 0;
+  return P.total;
+}
+
+}  // extern "C"
+
+namespace {
+sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
+                    const float* G, void* W, int32_t w_dtype, float* Mom,
+                    uint32_t* bits, int64_t worker_stride_words, int32_t M,
+                    int32_t local_worker, int32_t post_vote, const float* u0,
+                    void* ws, size_t ws_bytes, sm_profile* prof, hipStream_t stream) {
+  if (prof) {
+    if (!prof->events || !prof->kinds || prof->capacity < 0) return SM_EINVAL;
+    prof->count = 0;
+  }
+  if (!mats || n_mats < 1 || n_mats > 65536) return SM_EINVAL;
+  sm_status st = check_hparams(hp, true);
+  if (st != SM_OK) return st;
+  if (M < 1 || M > SM_MAX_WORKERS) return SM_ERANGE;
+  if (local_worker < 0 || local_worker >= M) return SM_EINVAL;
+  if (post_vote != 0 && post_vote != 1) return SM_EINVAL;
+  if (w_dtype != SM_F32 && w_dtype != SM_BF16) return SM_EINVAL;
+  if (!G || !W || !Mom || !bits) return SM_EINVAL;
+  if (worker_stride_words < 0) return SM_EINVAL;
+  // shapes, offsets and overlap
+  {
+    std::vector<std::pair<int64_t, int64_t>> es, wsg;
+    for (int i = 0; i < n_mats; ++i) {
+      const sm_matrix& m = mats[i];
+      if (m.rows < 1 || m.cols < 1 || m.rows > kMaxDim || m.cols > kMaxDim) return SM_EINVAL;
+      if (m.elem_off < 0 || m.word_off < 0) return SM_EINVAL;
+      int64_t mn = m.rows * m.cols, nw = (mn + 31) / 32;
+      if (m.word_off + nw > worker_stride_words) return SM_EINVAL;
+      es.push_back({m.elem_off, m.elem_off + mn});
+      wsg.push_back({m.word_off, m.word_off + nw});
+    }
+    std::sort(es.begin(), es.end());
+    std::sort(wsg.begin(), wsg.end());
+    for (int i = 1; i < n_mats; ++i)
+      if (es[i].first < es[i - 1].second || wsg[i].first < wsg[i - 1].second) return SM_EINVAL;
+  }
+  std::vector<bool> fus(n_mats);
+  bool need_u = false;
+  for (int i = 0; i < n_mats; ++i) {
+    fus[i] = mats[i].cols % 32 == 0;
+    if (!post_vote && hp->K > 0 && !fus[i]) need_u = true;
+  }
+  Plan P;
+  std::vector<MatPlan> mp;
+  st = build_plan(mats, n_mats, hp, post_vote != 0, need_u, P, mp);
+  if (st != SM_OK) return st;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < P.total)
+    return SM_EWORKSPACE;
+  HIP_TRY(ensure_attributes());
+  Bufs B = bind(P, ws);
+  std::vector<int> all(n_mats);
+  for (int i = 0; i < n_mats; ++i) all[i] = i;
+  std::vector<Group> groups = make_groups(mp, all);
+  set_vec_ok(groups, aligned16(G) && aligned16(W) && aligned16(Mom));
+  uint32_t* local_bits = bits + (int64_t)local_worker * worker_stride_words;
+  const int w_bf16 = w_dtype == SM_BF16;
+  HIP_TRY(mark(prof, SM_PHASE_START, stream));
+  HIP_TRY(launch_clear_status(B.status, stream));
+
+  NsIO io;
+  std::memset(&io, 0, sizeof(io));
+  io.u0 = u0; io.status = B.status; io.prof = prof;
+  io.W = W; io.w_bf16 = w_bf16; io.eta = hp->eta;
+
+  VoteArgs va;
+  std::memset(&va, 0, sizeof(va));
+  va.M = M; va.tie = hp->tie_value; va.w_bf16 = w_bf16; va.precision = P.precision;
+  va.bits = bits; va.stride = worker_stride_words;
+  va.W = W; va.eta = hp->eta; va.status = B.status;
+  auto vote_fill = [&](Group& g) {
+    int64_t nw = ((int64_t)g.rows * g.cols + 31) / 32;
+    g.blocks_per_mat = (int32_t)((nw + 255) / 256);
+    return true;
+  };
+
+  if (!post_vote) {
+    if (hp->K == 0) {
+      // U = Mom/(s+eps) has the signs of Mom: pack them directly.
+      MomSignArgs ms;
+      std::memset(&ms, 0, sizeof(ms));
+      ms.w_bf16 = w_bf16; ms.beta = hp->beta; ms.lam = hp->lambda;
+      ms.Gr = G; ms.W = W; ms.Mom = Mom; ms.bits = local_bits; ms.status = B.status;
+      HIP_TRY(for_launches(groups, [&](Group& g) {
+        g.blocks_per_mat = (int32_t)(((int64_t)g.rows * g.cols + kChunk - 1) / kChunk);
+        return true;
+      }, [&](const Groups& Gs) { ms.G = Gs; return launch_momentum_sign(ms, stream); }));
+      HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
+    } else {
+      SweepArgs sw;
+      std::memset(&sw, 0, sizeof(sw));
+      sw.ema = 1; sw.precision = P.precision; sw.w_bf16 = w_bf16;
+      sw.beta = hp->beta; sw.lam = hp->lambda;
+      sw.Gr = G; sw.W = W; sw.Mom = Mom;
+      sw.o_hi = B.x[0][0]; sw.o_lo = B.x[0][1];
+      sw.part = P.spectral ? nullptr : B.part;
+      sw.status = B.status;
+      HIP_TRY(for_launches(groups, [&](Group& g) {
+        g.blocks_per_mat = (int32_t)(mp[g.idx0].Mp * mp[g.idx0].Np / kChunk);
+        return true;
+      }, [&](const Groups& Gs) { sw.G = Gs; return launch_sweep(sw, stream); }));
+      HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
+      io.first_xsrc = XS_USER; io.src_user = Mom;
+      io.final_out = O_BITS; io.bits = local_bits; io.U = nullptr;
+      st = run_pre_scale(P, mp, groups, hp, B, io, 0, stream);
+      if (st != SM_OK) return st;
+      st = run_ns(P, mp, groups, fus, hp, B, io, stream);
+      if (st != SM_OK) return st;
+      if (need_u) {
+        for (int i = 0; i < n_mats; ++i) {
+          if (fus[i]) continue;
+          HIP_TRY(launch_sign_pack_flat(B.u + mats[i].elem_off, local_bits + mats[i].word_off,
+                                        mats[i].rows * mats[i].cols, stream));
+        }
+        HIP_TRY(mark(prof, SM_PHASE_PACK, stream));
+      }
+    }
+    va.mode = VA_APPLY;
+    HIP_TRY(for_launches(groups, vote_fill, [&](const Groups& Gs) {
+      va.G = Gs; return launch_vote_groups(va, stream);
+    }));
+    HIP_TRY(mark(prof, SM_PHASE_VOTE, stream));
+    return SM_OK;
+  }
+
+  // ---- post-vote variant
+  MomSignArgs ms;
+  std::memset(&ms, 0, sizeof(ms));
+  ms.w_bf16 = w_bf16; ms.beta = hp->beta; ms.lam = hp->lambda;
+  ms.Gr = G; ms.W = W; ms.Mom = Mom; ms.bits = local_bits; ms.status = B.status;
+  HIP_TRY(for_launches(groups, [&](Group& g) {
+    g.blocks_per_mat = (int32_t)(((int64_t)g.rows * g.cols + kChunk - 1) / kChunk);
+    return true;
+  }, [&](const Groups& Gs) { ms.G = Gs; return launch_momentum_sign(ms, stream); }));
+  HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
+  // padding of the operand copy (only matrices with a ragged shape)
+  HIP_TRY(for_launches(groups, [&](Group& g) {
+    const MatPlan& q = mp[g.idx0];
+    if (q.Mp == q.rows && q.Np == q.cols) return false;
+    g.blocks_per_mat = (int32_t)(q.Mp * q.Np / kChunk);
+    return true;
+  }, [&](const Groups& Gs) {
+    return launch_zero_pad(Gs, P.precision, B.x[0][0], B.x[0][1], stream);
+  }));
+  va.mode = VA_SBAR;
+  va.o_hi = B.x[0][0]; va.o_lo = B.x[0][1];
+  va.part = B.part;
+  HIP_TRY(for_launches(groups, vote_fill, [&](const Groups& Gs) {
+    va.G = Gs; return launch_vote_groups(va, stream);
+  }));
+  HIP_TRY(mark(prof, SM_PHASE_VOTE, stream));
+  io.first_xsrc = XS_OP; io.src_user = nullptr;
+  io.final_out = O_APPLY;
+  st = run_pre_scale(P, mp, groups, hp, B, io, 1, stream);
+  if (st != SM_OK) return st;
+  if (hp->K == 0) {
+    ScaledOutArgs so;
+    std::memset(&so, 0, sizeof(so));
+    so.precision = P.precision; so.from_op = 1; so.apply = 1; so.w_bf16 = w_bf16;
+    so.x_hi = B.x[0][0]; so.x_lo = B.x[0][1]; so.scal = B.scal;
+    so.W = W; so.eta = hp->eta; so.status = B.status;
+    HIP_TRY(for_launches(groups, [&](Group& g) {
+      g.blocks_per_mat = (int32_t)(((int64_t)g.rows * g.cols + kChunk - 1) / kChunk);
+      return true;
+    }, [&](const Groups& Gs) { so.G = Gs; return launch_scaled_out(so, stream); }));
+    return SM_OK;
+  }
+  std::vector<bool> fus_all(n_mats, true);
+  return run_ns(P, mp, groups, fus_all, hp, B, io, stream);
+}
+}  // namespace
+
+extern "C" {
+
+sm_status signmuon_step(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
+                        const float* G, void* W, int32_t w_dtype, float* Mom,
+                        uint32_t* bits, int64_t worker_stride_words, int32_t M,
+                        int32_t local_worker, int32_t post_vote, const float* u0,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  return step_impl(mats, n_mats, hp, G, W, w_dtype, Mom, bits, worker_stride_words, M,
+                   local_worker, post_vote, u0, ws, ws_bytes, nullptr, stream);
+}
+
+sm_status signmuon_step_profiled(const sm_matrix* mats, int32_t n_mats,
+                                 const sm_hparams* hp, const float* G, void* W,
+                                 int32_t w_dtype, float* Mom, uint32_t* bits,
+                                 int64_t worker_stride_words, int32_t M,
+                                 int32_t local_worker, int32_t post_vote,
+                                 const float* u0, void* ws, size_t ws_bytes,
+                                 sm_profile* prof, hipStream_t stream) {
+  if (!prof) return SM_EINVAL;
+  return step_impl(mats, n_mats, hp, G, W, w_dtype, Mom, bits, worker_stride_words, M,
+                   local_worker, post_vote, u0, ws, ws_bytes, prof, stream);
+}
+
+sm_status signmuon_get_status(const void* ws, hipStream_t stream) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return SM_EWORKSPACE;
+  int32_t h = 0;
+  if (hipMemcpyAsync(&h, ws, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return SM_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SM_EHIP;
+  return h ? SM_ENONFINITE : SM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,738 @@
+// HBM-bound passes of the Sign-Muon step: momentum EMA (Algorithm 1/2
+// momentum lines), entrywise sign with 1-bit packing (section 3; section 6
+// packing), majority vote over M packed worker buffers (Algorithm 2 sum and
+// threshold, blog tie rule), the update of W (Algorithm 1/2 last line), and
+// the small pre-scale kernels of PolarNS (section 4: Frobenius norm or power
+// iteration).  No floating-point atomics: every reduction has a fixed order.
+#include "sm_internal.h"
+#include "sm_launch.h"
+
+namespace sm {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+// Sum over a 256-thread block in a fixed order; result valid in every thread.
+__device__ __forceinline__ float block_sum(float v) {
+  __shared__ float sh[4];
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (sh[0] + sh[1]) + (sh[2] + sh[3]);
+}
+
+__device__ __forceinline__ void group_of_block(const Groups& G, int b, int& gi,
+                                               int& mi, int& q) {
+  gi = find_group(G, b);
+  int lb = b - G.g[gi].block0;
+  mi = lb / G.g[gi].blocks_per_mat;
+  q = lb - mi * G.g[gi].blocks_per_mat;
+}
+
+__device__ __forceinline__ float load_w(const void* W, int w_bf16, int64_t i) {
+  return w_bf16 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(W)[i])
+                : reinterpret_cast<const float*>(W)[i];
+}
+
+// Update of one parameter entry: product and difference each rounded to
+// float32 (no contraction), then nearest-even to bfloat16 for a bf16 W.
+__device__ __forceinline__ float apply_value(float w, float eta, float d) {
+#pragma clang fp contract(off)
+  float t = eta * d;
+  return w - t;
+}
+__device__ __forceinline__ void apply_store(void* W, int w_bf16, int64_t i,
+                                            float eta, float d) {
+  if (w_bf16) {
+    bf16_t* w = reinterpret_cast<bf16_t*>(W);
+    w[i] = f32_to_bf16(apply_value(bf16_to_f32(w[i]), eta, d));
+  } else {
+    float* w = reinterpret_cast<float*>(W);
+    w[i] = apply_value(w[i], eta, d);
+  }
+}
+
+__device__ __forceinline__ float ema(float mom, float g, float w, float beta,
+                                     float lam) {
+  float gt = g + lam * w;
+  return beta * mom + (1.0f - beta) * gt;
+}
+
+__device__ __forceinline__ void store_opv(int precision, void* hi, void* lo,
+                                          int64_t i, float v) {
+  if (precision == P_F32) {
+    reinterpret_cast<float*>(hi)[i] = v;
+  } else if (precision == P_BF16X3) {
+    bf16_t h, l;
+    split_bf16(v, h, l);
+    reinterpret_cast<bf16_t*>(hi)[i] = h;
+    reinterpret_cast<bf16_t*>(lo)[i] = l;
+  } else {
+    reinterpret_cast<bf16_t*>(hi)[i] = f32_to_bf16(v);
+  }
+}
+__device__ __forceinline__ float load_opv(int precision, const void* hi,
+                                          const void* lo, int64_t i) {
+  if (precision == P_F32) return reinterpret_cast<const float*>(hi)[i];
+  float v = bf16_to_f32(reinterpret_cast<const bf16_t*>(hi)[i]);
+  if (precision == P_BF16X3) v += bf16_to_f32(reinterpret_cast<const bf16_t*>(lo)[i]);
+  return v;
+}
+// 8 consecutive operand values (16-byte aligned destination).
+__device__ __forceinline__ void store_op8(int precision, void* hi, void* lo,
+                                          int64_t i, const float (&v)[8]) {
+  if (precision == P_F32) {
+    f32x4_t a{v[0], v[1], v[2], v[3]}, b{v[4], v[5], v[6], v[7]};
+    reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(hi) + i)[0] = a;
+    reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(hi) + i)[1] = b;
+    return;
+  }
+  u32x4_t h, l;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    bf16_t h0, h1, l0, l1;
+    if (precision == P_BF16X3) {
+      split_bf16(v[2 * k], h0, l0);
+      split_bf16(v[2 * k + 1], h1, l1);
+    } else {
+      h0 = f32_to_bf16(v[2 * k]);
+      h1 = f32_to_bf16(v[2 * k + 1]);
+      l0 = l1 = 0;
+    }
+    h[k] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    l[k] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
+  *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(hi) + i) = h;
+  if (precision == P_BF16X3)
+    *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(lo) + i) = l;
+}
+
+// ---------------------------------------------------------------------------
+// Vote counting: vertical (bit-sliced) counters.  c[k] holds bit k of the
+// count of set bits (negative votes) at each of the 32 positions of a word.
+// ---------------------------------------------------------------------------
+template <int NB>
+__device__ __forceinline__ void count_votes(const uint32_t* bits, int64_t stride,
+                                            int M, int64_t w, uint32_t (&c)[NB]) {
+#pragma unroll
+  for (int k = 0; k < NB; ++k) c[k] = 0;
+#pragma unroll 4
+  for (int m = 0; m < M; ++m) {
+    uint32_t carry = bits[(int64_t)m * stride + w];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      uint32_t t = c[k] & carry;
+      c[k] ^= carry;
+      carry = t;
+    }
+  }
+}
+template <int NB>
+__device__ __forceinline__ int vote_sum_at(const uint32_t (&c)[NB], int M, int b) {
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < NB; ++k) cnt |= (int)((c[k] >> b) & 1u) << k;
+  return M - 2 * cnt;
+}
+__device__ __forceinline__ int majority(int sum, int tie) {
+  return sum > 0 ? 1 : (sum < 0 ? -1 : tie);
+}
+
+// ---------------------------------------------------------------------------
+// ABI: momentum over a flat array
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_momentum_flat(
+    const float* __restrict__ G, const void* __restrict__ W, int w_bf16,
+    float* __restrict__ Mom, int64_t n, float beta, float lam, int vec) {
+  int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i0 >= n) return;
+  if (vec && i0 + 4 <= n) {
+    f32x4_t g = *reinterpret_cast<const f32x4_t*>(G + i0);
+    f32x4_t m = *reinterpret_cast<const f32x4_t*>(Mom + i0);
+    float w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = load_w(W, w_bf16, i0 + k);
+    f32x4_t o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = ema(m[k], g[k], w[k], beta, lam);
+    *reinterpret_cast<f32x4_t*>(Mom + i0) = o;
+    return;
+  }
+  for (int64_t i = i0; i < n && i < i0 + 4; ++i)
+    Mom[i] = ema(Mom[i], G[i], load_w(W, w_bf16, i), beta, lam);
+}
+
+hipError_t launch_momentum_flat(const float* G, const void* W, int w_bf16,
+                                float* Mom, int64_t n, float beta, float lam,
+                                hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int vec = ((uintptr_t)G % 16 == 0) && ((uintptr_t)Mom % 16 == 0);
+  int64_t blocks = (n + 1023) / 1024;
+  hipLaunchKernelGGL(k_momentum_flat, dim3((unsigned)blocks), dim3(256), 0, s,
+                     G, W, w_bf16, Mom, n, beta, lam, vec);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// ABI: sign + 1-bit pack of a flat array.  One element per lane; a wave
+// ballot yields two 32-bit words.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_sign_pack_flat(
+    const float* __restrict__ U, uint32_t* __restrict__ bits, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  bool neg = (i < n) && (U[i < n ? i : 0] < 0.0f);
+  uint64_t m = __ballot(neg);
+  int lane = threadIdx.x & 63;
+  int64_t w0 = (i - lane) >> 5;
+  int64_t nw = (n + 31) >> 5;
+  if (lane < 2 && w0 + lane < nw)
+    bits[w0 + lane] = (uint32_t)(m >> (32 * lane));
+}
+
+hipError_t launch_sign_pack_flat(const float* U, uint32_t* bits, int64_t n,
+                                 hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_sign_pack_flat, dim3((unsigned)blocks), dim3(256), 0, s,
+                     U, bits, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// ABI: majority vote over a flat segment, one thread per 32-entry word.
+// ---------------------------------------------------------------------------
+template <int NB>
+__global__ __launch_bounds__(256) void k_vote_flat(
+    const uint32_t* __restrict__ bits, int64_t stride, int M, int64_t n,
+    int tie, int8_t* __restrict__ D, int16_t* __restrict__ sums, int vec) {
+  int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t nw = (n + 31) >> 5;
+  if (w >= nw) return;
+  uint32_t c[NB];
+  count_votes<NB>(bits, stride, M, w, c);
+  int64_t e0 = w * 32;
+  if (vec && e0 + 32 <= n) {
+    u32x4_t d0, d1;
+    uint32_t dw[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int s = vote_sum_at<NB>(c, M, 4 * k + j);
+        v |= ((uint32_t)(uint8_t)(int8_t)majority(s, tie)) << (8 * j);
+      }
+      dw[k] = v;
+    }
+    d0 = u32x4_t{dw[0], dw[1], dw[2], dw[3]};
+    d1 = u32x4_t{dw[4], dw[5], dw[6], dw[7]};
+    reinterpret_cast<u32x4_t*>(D + e0)[0] = d0;
+    reinterpret_cast<u32x4_t*>(D + e0)[1] = d1;
+    if (sums) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        u32x4_t v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          int s0 = vote_sum_at<NB>(c, M, 8 * k + 2 * j);
+          int s1 = vote_sum_at<NB>(c, M, 8 * k + 2 * j + 1);
+          v[j] = (uint32_t)(uint16_t)(int16_t)s0 | ((uint32_t)(uint16_t)(int16_t)s1 << 16);
+        }
+        reinterpret_cast<u32x4_t*>(sums + e0)[k] = v;
+      }
+    }
+    return;
+  }
+  for (int b = 0; b < 32 && e0 + b < n; ++b) {
+    int s = vote_sum_at<NB>(c, M, b);
+    D[e0 + b] = (int8_t)majority(s, tie);
+    if (sums) sums[e0 + b] = (int16_t)s;
+  }
+}
+
+hipError_t launch_vote_flat(const uint32_t* bits, int64_t stride, int M,
+                            int64_t n, int tie, int8_t* D, int16_t* sums,
+                            hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t nw = (n + 31) / 32;
+  dim3 grid((unsigned)((nw + 255) / 256)), block(256);
+  int vec = ((uintptr_t)D % 16 == 0) && (!sums || (uintptr_t)sums % 16 == 0);
+  if (M <= 15)
+    hipLaunchKernelGGL(k_vote_flat<4>, grid, block, 0, s, bits, stride, M, n, tie, D, sums, vec);
+  else if (M <= 255)
+    hipLaunchKernelGGL(k_vote_flat<8>, grid, block, 0, s, bits, stride, M, n, tie, D, sums, vec);
+  else
+    hipLaunchKernelGGL(k_vote_flat<16>, grid, block, 0, s, bits, stride, M, n, tie, D, sums, vec);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// ABI: apply over a flat array
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_apply_flat(
+    void* __restrict__ W, int w_bf16, const int8_t* __restrict__ D,
+    const float* __restrict__ Df, float eta, int64_t n) {
+  int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  for (int64_t i = i0; i < n && i < i0 + 4; ++i) {
+    float d = D ? (float)D[i] : Df[i];
+    apply_store(W, w_bf16, i, eta, d);
+  }
+}
+
+hipError_t launch_apply_flat(void* W, int w_bf16, const int8_t* D,
+                             const float* Df, float eta, int64_t n,
+                             hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 1023) / 1024;
+  hipLaunchKernelGGL(k_apply_flat, dim3((unsigned)blocks), dim3(256), 0, s, W,
+                     w_bf16, D, Df, eta, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Padded sweep: momentum (or a plain float32 source) -> padded operand copy
+// + partial sums of squares + non-finite flag.  8 entries per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_sweep(SweepArgs a) {
+  int gi, mi, q;
+  group_of_block(a.G, blockIdx.x, gi, mi, q);
+  const Group& g = a.G.g[gi];
+  const int rows = g.rows, cols = g.cols;
+  const int64_t Np = round_up(cols, kPad);
+  const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
+  const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
+  const int64_t p = (int64_t)q * kChunk + threadIdx.x * 8;
+  const int row = (int)(p / Np), col = (int)(p - (int64_t)row * Np);
+  float v[8];
+  float ss = 0.0f;
+  bool bad = false;
+  const int64_t u = eoff + (int64_t)row * cols + col;
+  if (row < rows && col + 8 <= cols && g.vec_ok) {
+    if (a.ema) {
+      f32x4_t g0 = reinterpret_cast<const f32x4_t*>(a.Gr + u)[0];
+      f32x4_t g1 = reinterpret_cast<const f32x4_t*>(a.Gr + u)[1];
+      f32x4_t m0 = reinterpret_cast<const f32x4_t*>(a.Mom + u)[0];
+      f32x4_t m1 = reinterpret_cast<const f32x4_t*>(a.Mom + u)[1];
+      float w[8];
+      if (a.w_bf16) {
+        u32x4_t wb = *reinterpret_cast<const u32x4_t*>(
+            reinterpret_cast<const bf16_t*>(a.W) + u);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          w[2 * k] = __uint_as_float(wb[k] << 16);
+          w[2 * k + 1] = __uint_as_float(wb[k] & 0xFFFF0000u);
+        }
+      } else {
+        f32x4_t w0 = reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(a.W) + u)[0];
+        f32x4_t w1 = reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(a.W) + u)[1];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { w[k] = w0[k]; w[4 + k] = w1[k]; }
+      }
+      float gg[8], mm[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        gg[k] = g0[k]; gg[4 + k] = g1[k]; mm[k] = m0[k]; mm[4 + k] = m1[k];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        v[k] = ema(mm[k], gg[k], w[k], a.beta, a.lam);
+        bad |= !__builtin_isfinite(gg[k]) || !__builtin_isfinite(w[k]) ||
+               !__builtin_isfinite(v[k]);
+      }
+      reinterpret_cast<f32x4_t*>(a.Mom + u)[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+      reinterpret_cast<f32x4_t*>(a.Mom + u)[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+    } else {
+      f32x4_t s0 = reinterpret_cast<const f32x4_t*>(a.src + u)[0];
+      f32x4_t s1 = reinterpret_cast<const f32x4_t*>(a.src + u)[1];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { v[k] = s0[k]; v[4 + k] = s1[k]; }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[k] = 0.0f;
+      if (row < rows && col + k < cols) {
+        int64_t uk = u + k;
+        if (a.ema) {
+          float gk = a.Gr[uk], wk = load_w(a.W, a.w_bf16, uk);
+          float mk = ema(a.Mom[uk], gk, wk, a.beta, a.lam);
+          a.Mom[uk] = mk;
+          bad |= !__builtin_isfinite(gk) || !__builtin_isfinite(wk) ||
+                 !__builtin_isfinite(mk);
+          v[k] = mk;
+        } else {
+          v[k] = a.src[uk];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ss += v[k] * v[k];
+  store_op8(a.precision, a.o_hi, a.o_lo, xoff + p, v);
+  if (bad && a.status) a.status[0] = 1;
+  if (a.part) {
+    float t = block_sum(ss);
+    if (threadIdx.x == 0) a.part[g.c0 + (int64_t)mi * g.c_stride + q] = t;
+  }
+}
+
+hipError_t launch_sweep(const SweepArgs& a, hipStream_t s) {
+  if (a.G.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_sweep, dim3(a.G.total_blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Momentum + sign-pack of the new momentum (caller layout, per matrix).
+// Block = 2048 consecutive entries of one matrix; one entry per lane.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_momentum_sign(MomSignArgs a) {
+  int gi, mi, q;
+  group_of_block(a.G, blockIdx.x, gi, mi, q);
+  const Group& g = a.G.g[gi];
+  const int64_t mn = (int64_t)g.rows * g.cols;
+  const int64_t nw = (mn + 31) >> 5;
+  const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
+  const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  bool bad = false;
+#pragma unroll 1
+  for (int it = 0; it < kChunk / 256; ++it) {
+    int64_t base = (int64_t)q * kChunk + (it * 4 + wave) * 64;
+    int64_t e = base + lane;
+    bool neg = false;
+    if (e < mn) {
+      int64_t u = eoff + e;
+      float gk = a.Gr[u], wk = load_w(a.W, a.w_bf16, u);
+      float mk = ema(a.Mom[u], gk, wk, a.beta, a.lam);
+      a.Mom[u] = mk;
+      bad |= !__builtin_isfinite(gk) || !__builtin_isfinite(wk) ||
+             !__builtin_isfinite(mk);
+      neg = mk < 0.0f;
+    }
+    uint64_t m = __ballot(neg);
+    int64_t w0 = base >> 5;
+    if (lane < 2 && w0 + lane < nw) a.bits[woff + w0 + lane] = (uint32_t)(m >> (32 * lane));
+  }
+  if (bad && a.status) a.status[0] = 1;
+}
+
+hipError_t launch_momentum_sign(const MomSignArgs& a, hipStream_t s) {
+  if (a.G.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_momentum_sign, dim3(a.G.total_blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Vote over the M resident buffers of each matrix, thread per word.
+// ---------------------------------------------------------------------------
+template <int NB>
+__global__ __launch_bounds__(256) void k_vote_groups(VoteArgs a) {
+  if (a.mode == VA_APPLY && a.status && a.status[0] != 0) return;
+  int gi, mi, q;
+  group_of_block(a.G, blockIdx.x, gi, mi, q);
+  const Group& g = a.G.g[gi];
+  const int rows = g.rows, cols = g.cols;
+  const int64_t mn = (int64_t)rows * cols;
+  const int64_t nw = (mn + 31) >> 5;
+  const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
+  const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
+  const int64_t w = (int64_t)q * 256 + threadIdx.x;
+  float ss = 0.0f;
+  if (w < nw) {
+    uint32_t c[NB];
+    count_votes<NB>(a.bits, a.stride, a.M, woff + w, c);
+    const int64_t e0 = w * 32;
+    if (a.mode == VA_APPLY) {
+      const int64_t u = eoff + e0;
+      if (g.vec_ok && e0 + 32 <= mn) {
+        if (a.w_bf16) {
+          u32x4_t* wp = reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(a.W) + u);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            u32x4_t x = wp[k];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              int b0 = 8 * k + 2 * j;
+              float d0 = (float)majority(vote_sum_at<NB>(c, a.M, b0), a.tie);
+              float d1 = (float)majority(vote_sum_at<NB>(c, a.M, b0 + 1), a.tie);
+              float w0 = __uint_as_float(x[j] << 16);
+              float w1 = __uint_as_float(x[j] & 0xFFFF0000u);
+              bf16_t r0 = f32_to_bf16(apply_value(w0, a.eta, d0));
+              bf16_t r1 = f32_to_bf16(apply_value(w1, a.eta, d1));
+              x[j] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+            }
+            wp[k] = x;
+          }
+        } else {
+          f32x4_t* wp = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.W) + u);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            f32x4_t x = wp[k];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              x[j] = apply_value(x[j], a.eta,
+                                 (float)majority(vote_sum_at<NB>(c, a.M, 4 * k + j), a.tie));
+            wp[k] = x;
+          }
+        }
+      } else {
+        for (int b = 0; b < 32 && e0 + b < mn; ++b)
+          apply_store(a.W, a.w_bf16, u + b, a.eta,
+                      (float)majority(vote_sum_at<NB>(c, a.M, b), a.tie));
+      }
+    } else {
+      // VA_SBAR: majority matrix into the padded operand copy
+      const int64_t Np = round_up(cols, kPad);
+      const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
+      if (cols % 32 == 0) {
+        int row = (int)(e0 / cols), col = (int)(e0 - (int64_t)row * cols);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          float v[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            v[k] = (float)majority(vote_sum_at<NB>(c, a.M, 8 * h + k), a.tie);
+            ss += v[k] * v[k];
+          }
+          store_op8(a.precision, a.o_hi, a.o_lo, xoff + (int64_t)row * Np + col + 8 * h, v);
+        }
+      } else {
+        for (int b = 0; b < 32 && e0 + b < mn; ++b) {
+          int64_t e = e0 + b;
+          int row = (int)(e / cols), col = (int)(e - (int64_t)row * cols);
+          float v = (float)majority(vote_sum_at<NB>(c, a.M, b), a.tie);
+          ss += v * v;
+          store_opv(a.precision, a.o_hi, a.o_lo, xoff + (int64_t)row * Np + col, v);
+        }
+      }
+    }
+  }
+  if (a.mode == VA_SBAR && a.part) {
+    float t = block_sum(ss);
+    if (threadIdx.x == 0) a.part[g.c0 + (int64_t)mi * g.c_stride + q] = t;
+  }
+}
+
+hipError_t launch_vote_groups(const VoteArgs& a, hipStream_t s) {
+  if (a.G.total_blocks <= 0) return hipSuccess;
+  dim3 grid(a.G.total_blocks), block(256);
+  if (a.M <= 15)
+    hipLaunchKernelGGL(k_vote_groups<4>, grid, block, 0, s, a);
+  else if (a.M <= 255)
+    hipLaunchKernelGGL(k_vote_groups<8>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(k_vote_groups<16>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Zero the padding of padded operand copies (padded sweep layout).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_zero_pad(Groups G, int precision,
+                                                  void* hi, void* lo) {
+  int gi, mi, q;
+  group_of_block(G, blockIdx.x, gi, mi, q);
+  const Group& g = G.g[gi];
+  const int64_t Np = round_up(g.cols, kPad);
+  const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
+  const int64_t p = (int64_t)q * kChunk + threadIdx.x * 8;
+  const int row = (int)(p / Np), col = (int)(p - (int64_t)row * Np);
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (row >= g.rows || col + k >= g.cols) store_opv(precision, hi, lo, xoff + p + k, 0.0f);
+}
+
+hipError_t launch_zero_pad(const Groups& G, int precision, void* hi, void* lo,
+                           hipStream_t s) {
+  if (G.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_pad, dim3(G.total_blocks), dim3(256), 0, s, G,
+                     precision, hi, lo);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Pre-scale: Frobenius finalize, power iteration, scaled Gram operand.
+// One block per matrix for the finalize kernels (blocks_per_mat = 1).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_fro_finalize(Groups G, const float* part,
+                                                      float eps, float* scal) {
+  int gi, mi, q;
+  group_of_block(G, blockIdx.x, gi, mi, q);
+  const Group& g = G.g[gi];
+  const int64_t c0 = g.c0 + (int64_t)mi * g.c_stride;
+  float s = 0.0f;
+  for (int64_t i = threadIdx.x; i < g.gk; i += 256) s += part[c0 + i];
+  s = block_sum(s);
+  if (threadIdx.x == 0) scal[g.idx0 + mi * g.idx_stride] = 1.0f / (sqrtf(s) + eps);
+}
+
+hipError_t launch_fro_finalize(const Groups& G, const float* part, float eps,
+                               float* scal, hipStream_t s) {
+  if (G.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fro_finalize, dim3(G.total_blocks), dim3(256), 0, s, G,
+                     part, eps, scal);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_power_init(Groups G, const float* u0,
+                                                    float* vec) {
+  int gi, mi, q;
+  group_of_block(G, blockIdx.x, gi, mi, q);
+  const Group& g = G.g[gi];
+  const int r = g.rows < g.cols ? g.rows : g.cols;
+  const int64_t Rp = round_up(r, kPad);
+  const int64_t i = (int64_t)q * 256 + threadIdx.x;
+  if (i >= Rp) return;
+  float v = 0.0f;
+  if (i < r) v = u0 ? u0[g.u0_0 + (int64_t)mi * g.u0_stride + i] : 1.0f;
+  vec[g.v0 + (int64_t)mi * g.v_stride + i] = v;
+}
+
+hipError_t launch_power_init(const Groups& G, const float* u0, float* vec,
+                             hipStream_t s) {
+  if (G.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_power_init, dim3(G.total_blocks), dim3(256), 0, s, G, u0, vec);
+  return hipGetLastError();
+}
+
+// dst = A * (src / |src|) for 64 rows per block (16 per wave).
+__global__ __launch_bounds__(256) void k_power_step(Groups G, const float* araw,
+                                                    const float* src, float* dst) {
+  int gi, mi, q;
+  group_of_block(G, blockIdx.x, gi, mi, q);
+  const Group& g = G.g[gi];
+  const int r = g.rows < g.cols ? g.rows : g.cols;
+  const int64_t Rp = round_up(r, kPad);
+  const int64_t voff = g.v0 + (int64_t)mi * g.v_stride;
+  const int64_t roff = g.r0 + (int64_t)mi * g.r_stride;
+  const float* x = src + voff;
+  float ss = 0.0f;
+  for (int64_t i = threadIdx.x; i < Rp; i += 256) ss += x[i] * x[i];
+  ss = block_sum(ss);
+  const float inv = ss > 0.0f ? 1.0f / sqrtf(ss) : 0.0f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int rr = 0; rr < 16; ++rr) {
+    int64_t row = (int64_t)q * 64 + wave * 16 + rr;
+    const float* a = araw + roff + row * Rp;
+    float acc = 0.0f;
+    for (int64_t k = lane; k < Rp; k += 64) acc += a[k] * (x[k] * inv);
+    acc = wave_sum(acc);
+    if (lane == 0) dst[voff + row] = acc;
+  }
+}
+
+hipError_t launch_power_step(const Groups& G, const float* araw,
+                             const float* src, float* dst, hipStream_t s) {
+  if (G.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_power_step, dim3(G.total_blocks), dim3(256), 0, s, G,
+                     araw, src, dst);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_power_finalize(Groups G, const float* w,
+                                                        float eps, float* scal) {
+  int gi, mi, q;
+  group_of_block(G, blockIdx.x, gi, mi, q);
+  const Group& g = G.g[gi];
+  const int r = g.rows < g.cols ? g.rows : g.cols;
+  const int64_t Rp = round_up(r, kPad);
+  const float* x = w + g.v0 + (int64_t)mi * g.v_stride;
+  float ss = 0.0f;
+  for (int64_t i = threadIdx.x; i < Rp; i += 256) ss += x[i] * x[i];
+  ss = block_sum(ss);
+  if (threadIdx.x == 0) {
+    float lam = sqrtf(ss);
+    scal[g.idx0 + mi * g.idx_stride] = 1.0f / (sqrtf(lam) + eps);
+  }
+}
+
+hipError_t launch_power_finalize(const Groups& G, const float* w, float eps,
+                                 float* scal, hipStream_t s) {
+  if (G.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_power_finalize, dim3(G.total_blocks), dim3(256), 0, s, G,
+                     w, eps, scal);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_prescale(Groups G, int precision,
+                                                  const float* araw,
+                                                  const float* scal, float mul,
+                                                  void* hi, void* lo) {
+  int gi, mi, q;
+  group_of_block(G, blockIdx.x, gi, mi, q);
+  const Group& g = G.g[gi];
+  const int64_t roff = g.r0 + (int64_t)mi * g.r_stride;
+  const float c = scal[g.idx0 + mi * g.idx_stride];
+  const float m = mul * c * c;
+  const int64_t p = roff + (int64_t)q * kChunk + threadIdx.x * 8;
+  float v[8];
+  f32x4_t a0 = reinterpret_cast<const f32x4_t*>(araw + p)[0];
+  f32x4_t a1 = reinterpret_cast<const f32x4_t*>(araw + p)[1];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) { v[k] = m * a0[k]; v[4 + k] = m * a1[k]; }
+  store_op8(precision, hi, lo, p, v);
+}
+
+hipError_t launch_prescale(const Groups& G, int precision, const float* araw,
+                           const float* scal, float mul, void* hi, void* lo,
+                           hipStream_t s) {
+  if (G.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_prescale, dim3(G.total_blocks), dim3(256), 0, s, G,
+                     precision, araw, scal, mul, hi, lo);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// K = 0: U = c * X (caller layout), or W -= eta * c * S from the operand.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_scaled_out(ScaledOutArgs a) {
+  if (a.apply && a.status && a.status[0] != 0) return;
+  int gi, mi, q;
+  group_of_block(a.G, blockIdx.x, gi, mi, q);
+  const Group& g = a.G.g[gi];
+  const int64_t mn = (int64_t)g.rows * g.cols;
+  const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
+  const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
+  const int64_t Np = round_up(g.cols, kPad);
+  const float c = a.scal[g.idx0 + mi * g.idx_stride];
+  for (int k = 0; k < 8; ++k) {
+    int64_t e = (int64_t)q * kChunk + k * 256 + threadIdx.x;
+    if (e >= mn) break;
+    float x;
+    if (a.from_op) {
+      int64_t row = e / g.cols, col = e - row * g.cols;
+      x = load_opv(a.precision, a.x_hi, a.x_lo, xoff + row * Np + col);
+    } else {
+      x = a.x_user[eoff + e];
+    }
+    float v = c * x;
+    if (a.apply) apply_store(a.W, a.w_bf16, eoff + e, a.eta, v);
+    else a.U[eoff + e] = v;
+  }
+}
+
+hipError_t launch_scaled_out(const ScaledOutArgs& a, hipStream_t s) {
+  if (a.G.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_scaled_out, dim3(a.G.total_blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+__global__ void k_clear_status(int32_t* status) {
+  if (threadIdx.x == 0) status[0] = 0;
+}
+hipError_t launch_clear_status(int32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(64), 0, s, status);
+  return hipGetLastError();
+}
+
+}  // namespace sm

@@ -1,0 +1,126 @@
+// Launch-side declarations of the kernels of libsignmuon.
+#pragma once
+
+#include "sm_internal.h"
+
+namespace sm {
+
+// Operand families of the batched GEMM: padded copies of X (Mp x Np) or the
+// padded Gram-sized buffers (Rp x Rp).
+enum { FAM_X = 0, FAM_R = 1 };
+// Group.ops bits: A-operand family, A k-contiguous, B family, B k-contiguous.
+__host__ __device__ inline int gemm_ops(int a_fam, int a_kc, int b_fam, int b_kc) {
+  return a_fam | (a_kc << 1) | (b_fam << 2) | (b_kc << 3);
+}
+
+enum Epi { E_RAW = 0, E_OP = 1, E_SQUARE = 2, E_UPDATE = 3 };
+enum Out { O_X = 0, O_U = 1, O_BITS = 2, O_APPLY = 3 };
+enum XSrc { XS_USER = 0, XS_OP = 1 };
+
+struct GemmArgs {
+  Groups G;
+  const void* x_hi; const void* x_lo;   // FAM_X operand buffers
+  const void* r_hi; const void* r_lo;   // FAM_R operand buffers
+  int32_t epi, out, xsrc, scal_pow;
+  float mul, ca, cb, cc;
+  void* o_hi; void* o_lo;          // E_OP / E_SQUARE (R family), O_X (X family)
+  float* o_raw;                    // E_RAW
+  const void* sq_hi; const void* sq_lo;   // E_SQUARE: A for the b*A term
+  const float* scal;               // per-matrix c = 1/(s+eps) or NULL
+  const float* xs_user;            // XS_USER: float32 source in caller layout
+  const void* xs_hi; const void* xs_lo;   // XS_OP: padded operand source
+  float* U;                        // O_U
+  uint32_t* bits;                  // O_BITS (buffer of the local worker)
+  void* W; int32_t w_bf16; float eta;   // O_APPLY
+  const int32_t* status;           // O_APPLY is skipped when *status != 0
+};
+
+hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s);
+hipError_t gemm_set_attributes();
+
+// ---- elementwise and small kernels (sm_elementwise.hip) ----
+hipError_t launch_momentum_flat(const float* G, const void* W, int w_bf16,
+                                float* Mom, int64_t n, float beta, float lam,
+                                hipStream_t s);
+hipError_t launch_sign_pack_flat(const float* U, uint32_t* bits, int64_t n,
+                                 hipStream_t s);
+hipError_t launch_vote_flat(const uint32_t* bits, int64_t stride, int M,
+                            int64_t n, int tie, int8_t* D, int16_t* sums,
+                            hipStream_t s);
+hipError_t launch_apply_flat(void* W, int w_bf16, const int8_t* D,
+                             const float* Df, float eta, int64_t n,
+                             hipStream_t s);
+
+// Padded sweep: writes the padded operand copy of each matrix (and the
+// partial sums of squares).  ema = 1: Mom <- beta Mom + (1-beta)(G + lam W)
+// first (G, W, Mom in caller layout), else the source is `src` (caller
+// layout, float32).
+struct SweepArgs {
+  Groups G;
+  int32_t ema, precision, w_bf16;
+  float beta, lam;
+  const float* src; const float* Gr; const void* W; float* Mom;
+  void* o_hi; void* o_lo;
+  float* part;          // partial sums per chunk, NULL to skip
+  int32_t* status;      // non-finite flag, NULL to skip
+};
+hipError_t launch_sweep(const SweepArgs& a, hipStream_t s);
+
+// Momentum with the signs of the new momentum packed into `bits` (post-vote
+// variant and K = 0).
+struct MomSignArgs {
+  Groups G;
+  int32_t w_bf16;
+  float beta, lam;
+  const float* Gr; const void* W; float* Mom; uint32_t* bits;
+  int32_t* status;
+};
+hipError_t launch_momentum_sign(const MomSignArgs& a, hipStream_t s);
+
+// Vote over M buffers per matrix: mode VA_APPLY updates W, VA_SBAR writes
+// the majority matrix into the padded operand (+ partial sums of squares).
+enum { VA_APPLY = 0, VA_SBAR = 1 };
+struct VoteArgs {
+  Groups G;
+  int32_t mode, M, tie, w_bf16, precision;
+  const uint32_t* bits; int64_t stride;
+  void* W; float eta;
+  void* o_hi; void* o_lo; float* part;
+  const int32_t* status;
+};
+hipError_t launch_vote_groups(const VoteArgs& a, hipStream_t s);
+
+// Zero the padding of the padded operand copies.
+hipError_t launch_zero_pad(const Groups& G, int precision, void* hi, void* lo,
+                           hipStream_t s);
+
+// c = 1 / (sqrt(sum of partials) + eps) per matrix (Frobenius).
+hipError_t launch_fro_finalize(const Groups& G, const float* part, float eps,
+                               float* scal, hipStream_t s);
+
+// Power iteration on the padded raw Gram.
+hipError_t launch_power_init(const Groups& G, const float* u0, float* vec,
+                             hipStream_t s);
+hipError_t launch_power_step(const Groups& G, const float* araw,
+                             const float* src, float* dst, hipStream_t s);
+hipError_t launch_power_finalize(const Groups& G, const float* w, float eps,
+                                 float* scal, hipStream_t s);
+// op = mul * c^2 * araw (padded Rp x Rp) in the operand precision.
+hipError_t launch_prescale(const Groups& G, int precision, const float* araw,
+                           const float* scal, float mul, void* hi, void* lo,
+                           hipStream_t s);
+// K = 0 output: v = c * x (x from caller-layout float32 or padded operand);
+// writes U (caller layout) or applies W -= eta * v.
+struct ScaledOutArgs {
+  Groups G;
+  int32_t precision, from_op, apply, w_bf16;
+  const float* x_user; const void* x_hi; const void* x_lo;
+  const float* scal;
+  float* U; void* W; float eta;
+  const int32_t* status;
+};
+hipError_t launch_scaled_out(const ScaledOutArgs& a, hipStream_t s);
+
+hipError_t launch_clear_status(int32_t* status, hipStream_t s);
+
+}  // namespace sm

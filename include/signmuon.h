@@ -1,0 +1,238 @@
+/*
+ * signmuon.h - C ABI of libsignmuon.so: the Sign-Muon optimizer step on
+ * AMD Instinct MI355X (gfx950), written as HIP kernels.
+ *
+ * Method: "SignMuon: Communication-Efficient Distributed Muon Optimization"
+ * (Mishra, Trivedi, Kumar; arXiv 2605.16311).  Algorithm 1 gives one
+ * worker's step (weight decay, momentum EMA, PolarNS, entrywise sign,
+ * update); Algorithm 2 and Figure 1 give the distributed step (each worker
+ * sends its signs, an integer sum across workers is thresholded by sign,
+ * every worker applies the same update).  The first author's blog ("SignMuon:
+ * Matrix Directions, Majority Votes, and the Actual Bytes Sent") fixes the
+ * tie policy (a tied vote gives 0) and the 1-bit payload of d/8 bytes.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array pointer is a DEVICE pointer unless stated otherwise; the
+ *   caller owns all memory.  The library allocates nothing and keeps no
+ *   state between calls; it is reentrant.
+ * - Work is enqueued asynchronously on the caller's stream (NULL = the null
+ *   stream) and never synchronises, except signmuon_get_status.
+ * - Matrices are row-major and contiguous.  A parameter set is one flat
+ *   array per quantity (G, W, Mom) holding every matrix back to back at
+ *   sm_matrix.elem_off.
+ * - Packed signs: flat index j of a matrix lives in bit (j % 32) of word
+ *   j / 32 of that matrix's segment (little-endian uint32), and the bit is 1
+ *   exactly when the value is negative (so 0 and -0 pack as the +1 bit).
+ *   Tail bits past the last entry are written as 0 and ignored on input.
+ * - Argument errors return SM_EINVAL (or SM_ERANGE / SM_EWORKSPACE) before
+ *   anything is enqueued.  A failed launch returns SM_EHIP.  Faults inside
+ *   kernels surface at the caller's next synchronisation.
+ * - Floating-point work never uses atomics: results are deterministic and
+ *   bit-reproducible run to run.
+ */
+#ifndef SIGNMUON_H
+#define SIGNMUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sm_status {
+  SM_OK = 0,
+  SM_EINVAL = -1,        /* bad argument; nothing enqueued */
+  SM_EWORKSPACE = -2,    /* workspace missing or too small; nothing enqueued */
+  SM_EHIP = -3,          /* a HIP launch or runtime call failed */
+  SM_ENONFINITE = -4,    /* a step saw a non-finite G, W or momentum */
+  SM_ERANGE = -5,        /* worker count or size outside the supported range */
+  SM_EUNSUPPORTED = -6   /* valid request this build does not implement */
+} sm_status;
+
+typedef enum sm_dtype { SM_F32 = 0, SM_BF16 = 1 } sm_dtype;
+
+/* Arithmetic of the Newton-Schulz products.  BF16: bfloat16 operands with
+ * float32 accumulation.  BF16X3: each operand split into hi + lo bfloat16
+ * parts, products hi*hi + hi*lo + lo*hi (near-float32 accuracy at three
+ * times the matrix-core work).  F32: float32 operands and accumulation. */
+typedef enum sm_ns_precision {
+  SM_NS_F32 = 0, SM_NS_BF16 = 1, SM_NS_BF16X3 = 2
+} sm_ns_precision;
+
+/* Pre-scale of PolarNS (paper, section 4): X0 = Mom / (s + eps) with
+ * s = ||Mom||_F (FRO) or s = an estimate of sigma_max(Mom) from P steps of
+ * power iteration on the smaller Gram matrix (SPECTRAL): u <- A u / |A u|,
+ * s = sqrt(|A u|) at the last step. */
+typedef enum sm_scale { SM_SCALE_FRO = 0, SM_SCALE_SPECTRAL = 1 } sm_scale;
+
+/* Hyper-parameters: the inputs of Algorithm 1 (eta, beta, lambda, K, eps,
+ * scale, P) plus the Newton-Schulz coefficients, the product precision and
+ * the tie policy.  One Newton-Schulz step is X <- a X + (b A + c A^2) X with
+ * A = X X^T for a wide matrix (rows <= cols), and X <- a X + X (b A + c A^2)
+ * with A = X^T X for a tall one; the cubic of section 4 is (1.5, -0.5, 0). */
+typedef struct sm_hparams {
+  float eta;             /* step size of this call, any finite value */
+  float beta;            /* momentum, 0 <= beta < 1 */
+  float lambda;          /* weight decay, >= 0 */
+  float eps;             /* pre-scale stability constant, > 0 */
+  int32_t K;             /* Newton-Schulz steps, 0 <= K <= 64 */
+  int32_t scale;         /* sm_scale */
+  int32_t P;             /* power-iteration steps, 1..256 when SPECTRAL */
+  float ns_a, ns_b, ns_c;
+  int32_t ns_precision;  /* sm_ns_precision */
+  int32_t tie_value;     /* value of a tied vote: 0 (default) or 1 */
+} sm_hparams;
+
+/* One matrix of a parameter set. */
+typedef struct sm_matrix {
+  int64_t rows, cols;    /* both >= 1 */
+  int64_t elem_off;      /* element offset in the flat G / W / Mom arrays */
+  int64_t word_off;      /* word offset of its packed signs in a worker buffer */
+} sm_matrix;
+
+/* Largest worker count: vote sums are kept in int16 (the blog notes that an
+ * int8 accumulator overflows once more than 127 workers agree). */
+#define SM_MAX_WORKERS 32767
+
+const char *signmuon_strerror(int status);
+int32_t signmuon_abi_version(void);
+
+/*
+ * Momentum (Algorithm 1 and 2, weight-decay and momentum lines):
+ *   Mom[i] <- beta * Mom[i] + (1 - beta) * (G[i] + lambda * W[i]),
+ * in float32, for i < n.  G, Mom: float32[n]; W: float32 or bfloat16[n]
+ * (w_dtype).  Mom is updated in place; G and W are read only.  n = 0 is a
+ * no-op.
+ */
+sm_status signmuon_momentum(const float *G, const void *W, int32_t w_dtype,
+                            float *Mom, int64_t n, float beta, float lambda,
+                            hipStream_t stream);
+
+/*
+ * PolarNS of one matrix (Algorithm 1 polar line; section 4): pre-scale by
+ * hp->scale, then hp->K Newton-Schulz steps with (ns_a, ns_b, ns_c) in
+ * hp->ns_precision.  X: float32[rows*cols] input, U: float32[rows*cols]
+ * output (must not alias X).  u0: float32[min(rows, cols)] start vector of
+ * the power iteration, or NULL for the all-ones vector; ignored for FRO.
+ * ws: device workspace of at least signmuon_polar_ns_workspace() bytes,
+ * 256-byte aligned; its contents on entry do not matter.  eta, beta, lambda
+ * and tie_value are ignored.
+ */
+size_t signmuon_polar_ns_workspace(int64_t rows, int64_t cols,
+                                   const sm_hparams *hp);
+sm_status signmuon_polar_ns(const float *X, float *U, int64_t rows,
+                            int64_t cols, const sm_hparams *hp,
+                            const float *u0, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/*
+ * Entrywise sign with 1-bit packing (section 3 sign; section 6 packing):
+ * bits[j/32] bit (j%32) = (U[j] < 0) for j < n; ceil(n/32) words written,
+ * tail bits 0.  U: float32[n].
+ */
+sm_status signmuon_sign_pack(const float *U, uint32_t *bits, int64_t n,
+                             hipStream_t stream);
+
+/*
+ * Majority vote (Algorithm 2 sum all-reduce and local threshold; blog tie
+ * rule): for j < n, sum_j = sum over m < M of (bit_{m,j} ? -1 : +1) and
+ * D[j] = sign(sum_j), a zero sum giving tie_value.  Worker m's buffer starts
+ * at bits + m * worker_stride_words (worker_stride_words >= ceil(n/32)).
+ * D: int8[n] output; sums: int16[n] output or NULL.  1 <= M <= 32767 else
+ * SM_ERANGE.
+ */
+sm_status signmuon_majority_vote(const uint32_t *bits,
+                                 int64_t worker_stride_words, int32_t M,
+                                 int64_t n, int32_t tie_value, int8_t *D,
+                                 int16_t *sums, hipStream_t stream);
+
+/*
+ * Update (Algorithm 1 and 2, last line): W[i] <- W[i] - eta * D[i] with the
+ * product and the difference each rounded to float32 (no fused
+ * multiply-add) and, for a bfloat16 W, the result rounded to nearest even.
+ * Exactly one of D (int8[n], values -1/0/+1) and Df (float32[n]) is
+ * non-NULL.
+ */
+sm_status signmuon_apply(void *W, int32_t w_dtype, const int8_t *D,
+                         const float *Df, float eta, int64_t n,
+                         hipStream_t stream);
+
+/*
+ * One fused Sign-Muon step for the local worker over a parameter set, with
+ * the M workers' packed sign buffers resident on this GPU (they stand for
+ * this GPU's copy after an exchange of sign buffers).
+ *
+ * post_vote = 0 (Algorithm 2): for every matrix, momentum (in place in
+ *   Mom), PolarNS of the new momentum, its signs packed into worker buffer
+ *   local_worker; then the vote over all M buffers and
+ *   W <- W - eta * majority.
+ * post_vote = 1 (the variant with the polar step after the vote): the signs
+ *   of the new momentum go to buffer local_worker; the majority matrix S of
+ *   each matrix is voted, U = PolarNS(S), and W <- W - eta * U.
+ *
+ * mats[n_mats]: HOST array of matrix descriptors (1 <= n_mats <= 65536);
+ * matrices must not overlap in the flat arrays or in a worker buffer.
+ * G, Mom: float32 flat arrays; W: w_dtype flat array.  bits: M worker
+ * buffers, worker m at bits + m * worker_stride_words.  u0: float32, the
+ * concatenation of every matrix's min(rows, cols) power-iteration start
+ * vector, or NULL (all ones).  ws: workspace of signmuon_step_workspace()
+ * bytes, 256-byte aligned; its contents on entry do not matter.
+ *
+ * If any G, W or new momentum value is non-finite the update of W is
+ * skipped (Mom and the local buffer are still written) and the next
+ * signmuon_get_status on the same workspace returns SM_ENONFINITE.
+ */
+size_t signmuon_step_workspace(const sm_matrix *mats, int32_t n_mats,
+                               const sm_hparams *hp, int32_t post_vote);
+sm_status signmuon_step(const sm_matrix *mats, int32_t n_mats,
+                        const sm_hparams *hp, const float *G, void *W,
+                        int32_t w_dtype, float *Mom, uint32_t *bits,
+                        int64_t worker_stride_words, int32_t M,
+                        int32_t local_worker, int32_t post_vote,
+                        const float *u0, void *ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/*
+ * Instrumented step: identical work to signmuon_step, plus a hipEventRecord
+ * on `stream` after each phase so a caller can time the kernels of one step
+ * (events[i] closes the phase kinds[i]; the first event opens the step).
+ * events[capacity]: caller-created events (HOST array of handles);
+ * kinds[capacity]: HOST array receiving the phase of each event
+ * (SM_PHASE_*); *count receives the number of events recorded.  If the
+ * capacity is too small, recording stops and *count == capacity.
+ */
+typedef enum sm_phase {
+  SM_PHASE_START = 0,     /* opening event */
+  SM_PHASE_MOMENTUM = 1,  /* momentum sweep (+ signs in the post-vote form) */
+  SM_PHASE_PRESCALE = 2,  /* Frobenius finalize / power iteration */
+  SM_PHASE_GEMM = 3,      /* one Newton-Schulz matrix-core launch */
+  SM_PHASE_PACK = 4,      /* unfused sign packing */
+  SM_PHASE_VOTE = 5       /* vote (+ apply, or majority matrix) */
+} sm_phase;
+typedef struct sm_profile {
+  hipEvent_t *events;
+  int32_t *kinds;
+  int32_t capacity;
+  int32_t count;
+} sm_profile;
+sm_status signmuon_step_profiled(const sm_matrix *mats, int32_t n_mats,
+                                 const sm_hparams *hp, const float *G, void *W,
+                                 int32_t w_dtype, float *Mom, uint32_t *bits,
+                                 int64_t worker_stride_words, int32_t M,
+                                 int32_t local_worker, int32_t post_vote,
+                                 const float *u0, void *ws, size_t ws_bytes,
+                                 sm_profile *prof, hipStream_t stream);
+
+/*
+ * Status of the last signmuon_step that used workspace ws: waits for the
+ * stream, then returns SM_OK or SM_ENONFINITE (SM_EHIP if the copy fails).
+ */
+sm_status signmuon_get_status(const void *ws, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SIGNMUON_H */

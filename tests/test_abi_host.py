@@ -1,0 +1,151 @@
+"""Host-only checks of libsignmuon.so: it loads, exports every function that
+include/signmuon.h declares, and rejects bad arguments before touching the
+GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from distributed_bit_matrix_amd import binding as B
+from distributed_bit_matrix_amd import workloads as WL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="libsignmuon.so not built")
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "signmuon.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(signmuon_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 12
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_version_and_strerror():
+    L = B.lib()
+    assert L.signmuon_abi_version() == 1
+    for code in [0, -1, -2, -3, -4, -5, -6]:
+        assert len(B.strerror(code)) >= 2
+    assert B.strerror(-99) == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+
+
+def test_apply_validation():
+    L = B.lib()
+    assert L.signmuon_apply(FAKE, 0, None, None, 0.1, 10, None) == B.SM_EINVAL
+    assert L.signmuon_apply(FAKE, 0, FAKE, FAKE, 0.1, 10, None) == B.SM_EINVAL
+    assert L.signmuon_apply(FAKE, 2, FAKE, None, 0.1, 10, None) == B.SM_EINVAL
+    assert L.signmuon_apply(FAKE, 0, FAKE, None, 0.1, -1, None) == B.SM_EINVAL
+    assert L.signmuon_apply(FAKE, 0, FAKE, None, float("nan"), 4, None) == B.SM_EINVAL
+    assert L.signmuon_apply(FAKE, 0, FAKE, None, 0.1, 0, None) == B.SM_OK  # no-op
+
+
+def test_vote_validation():
+    L = B.lib()
+    assert L.signmuon_majority_vote(FAKE, 1, 0, 32, 0, FAKE, None, None) == B.SM_ERANGE
+    assert L.signmuon_majority_vote(FAKE, 1, 32768, 32, 0, FAKE, None, None) == B.SM_ERANGE
+    assert L.signmuon_majority_vote(FAKE, 1, 3, 32, 2, FAKE, None, None) == B.SM_EINVAL
+    assert L.signmuon_majority_vote(FAKE, 1, 3, 64, 0, FAKE, None, None) == B.SM_EINVAL
+    assert L.signmuon_majority_vote(None, 1, 3, 32, 0, FAKE, None, None) == B.SM_EINVAL
+    assert L.signmuon_majority_vote(FAKE, 1, 3, 0, 0, FAKE, None, None) == B.SM_OK
+
+
+def test_momentum_and_pack_validation():
+    L = B.lib()
+    assert L.signmuon_momentum(FAKE, FAKE, 0, FAKE, 8, 1.0, 0.0, None) == B.SM_EINVAL
+    assert L.signmuon_momentum(FAKE, FAKE, 0, FAKE, 8, 0.9, -1.0, None) == B.SM_EINVAL
+    assert L.signmuon_momentum(FAKE, FAKE, 5, FAKE, 8, 0.9, 0.0, None) == B.SM_EINVAL
+    assert L.signmuon_momentum(None, FAKE, 0, FAKE, 8, 0.9, 0.0, None) == B.SM_EINVAL
+    assert L.signmuon_sign_pack(FAKE, FAKE, -3, None) == B.SM_EINVAL
+    assert L.signmuon_sign_pack(None, FAKE, 3, None) == B.SM_EINVAL
+    assert L.signmuon_sign_pack(FAKE, FAKE, 0, None) == B.SM_OK
+
+
+def _hp(**kw):
+    return B.HParams(**kw)
+
+
+def test_polar_workspace_and_validation():
+    L = B.lib()
+    hp = _hp(K=5, scale="fro")
+    w = B.polar_ns_workspace(256, 512, hp)
+    assert w > 0 and w % 256 == 0
+    assert B.polar_ns_workspace(512, 256, hp) == w            # transposed shape
+    assert B.polar_ns_workspace(256, 512, _hp(K=5, precision="bf16x3")) > w
+    assert B.polar_ns_workspace(256, 512, _hp(K=5, scale="spectral", P=3)) > w
+    assert B.polar_ns_workspace(256, 512, _hp(K=5, coeffs=(3.4445, -4.775, 2.0315))) > w
+    assert B.polar_ns_workspace(256, 512, _hp(K=0)) < w
+    # invalid hyper-parameters or shapes give 0
+    assert B.polar_ns_workspace(0, 512, hp) == 0
+    assert B.polar_ns_workspace(256, 512, _hp(eps=0.0)) == 0
+    assert B.polar_ns_workspace(256, 512, _hp(scale="spectral", P=0)) == 0
+    assert B.polar_ns_workspace(256, 512, _hp(K=65)) == 0
+    c = hp.to_c()
+    U = ctypes.c_void_p(0x20000)
+    assert L.signmuon_polar_ns(FAKE, U, 256, 512, ctypes.byref(c), None, FAKE, 16,
+                               None) == B.SM_EWORKSPACE
+    assert L.signmuon_polar_ns(FAKE, U, 256, 512, ctypes.byref(c), None,
+                               ctypes.c_void_p(0x10010), w, None) == B.SM_EWORKSPACE
+    assert L.signmuon_polar_ns(FAKE, FAKE, 256, 512, ctypes.byref(c), None, FAKE, w,
+                               None) == B.SM_EINVAL              # X aliases U
+    c.ns_precision = 7
+    assert L.signmuon_polar_ns(FAKE, ctypes.c_void_p(0x20000), 256, 512, ctypes.byref(c),
+                               None, FAKE, w, None) == B.SM_EINVAL
+
+
+def _step(L, mats, hp, M=3, local=0, stride=None, post=0, ws_bytes=None, G=FAKE):
+    arr = B.mats_array(mats)
+    if stride is None:
+        stride = sum((r * c + 31) // 32 for r, c, _, _ in mats)
+    if ws_bytes is None:
+        ws_bytes = B.step_workspace(mats, hp, bool(post))
+    return L.signmuon_step(arr, len(mats), ctypes.byref(hp.to_c()), G, FAKE, 1, FAKE,
+                           FAKE, stride, M, local, post, None, FAKE, ws_bytes, None)
+
+
+def test_step_validation():
+    L = B.lib()
+    hp = _hp()
+    mats, d, words = B.default_layout([(64, 96), (96, 64)])
+    assert _step(L, mats, hp, M=0) == B.SM_ERANGE
+    assert _step(L, mats, hp, M=40000) == B.SM_ERANGE
+    assert _step(L, mats, hp, M=3, local=3) == B.SM_EINVAL
+    assert _step(L, mats, hp, post=2) == B.SM_EINVAL
+    assert _step(L, mats, hp, G=None) == B.SM_EINVAL
+    assert _step(L, mats, hp, stride=words - 1) == B.SM_EINVAL
+    overlap = [mats[0], (96, 64, 64 * 96 - 1, mats[1][3])]
+    assert _step(L, overlap, hp) == B.SM_EINVAL
+    overlap_w = [mats[0], (96, 64, mats[1][2], mats[1][3] - 1)]
+    assert _step(L, overlap_w, hp) == B.SM_EINVAL
+    assert _step(L, mats, hp, ws_bytes=1024) == B.SM_EWORKSPACE
+    assert _step(L, mats, _hp(beta=1.0)) == B.SM_EINVAL
+    assert _step(L, mats, _hp(tie_value=2)) == B.SM_EINVAL
+    assert _step(L, [(0, 5, 0, 0)], hp) == B.SM_EINVAL
+
+
+def test_step_workspace_sizes():
+    w = WL.get("nanogpt")
+    mats, d, words = B.default_layout(w.mats)
+    hp = _hp()
+    ws = B.step_workspace(mats, hp, False)
+    # two bfloat16 operand copies of every matrix plus the Gram-sized factor
+    x = 2 * 2 * d
+    r = 2 * sum(min(a, b) ** 2 for a, b in w.mats)
+    assert x + r <= ws <= x + r + 4 * 1024 * 1024
+    assert B.step_workspace(mats, _hp(K=0), False) < ws
+    assert B.step_workspace(mats[:4], hp, False) < ws
+    # ragged shapes are padded to multiples of 128
+    m1, _, _ = B.default_layout([(10, 2048)])
+    assert B.step_workspace(m1, hp, False) >= 2 * 2 * 128 * 2048

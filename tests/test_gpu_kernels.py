@@ -1,0 +1,186 @@
+"""GPU parity of the unit entry points (sign_pack, majority_vote, apply,
+momentum) against the CPU oracle, through the C ABI."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from distributed_bit_matrix_amd import binding as B
+from tests.gpu_common import f32, momentum_tol
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def u32(t):
+    return host(t).view(np.uint32)
+
+
+# --------------------------------------------------------------------------
+# sign + 1-bit pack
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 64, 65, 1000, 100003, 1 << 20])
+def test_sign_pack_bit_exact(n):
+    print(f"sign_pack n={n}", flush=True)
+    rng = np.random.default_rng(n)
+    U = rng.standard_normal(n).astype(np.float32)
+    U[rng.random(n) < 0.05] = 0.0
+    U[rng.random(n) < 0.05] = -0.0
+    bits = B.sign_pack(dev(U))
+    assert np.array_equal(u32(bits), O.pack_signs(U))
+
+
+def test_sign_pack_tail_bits_zero():
+    U = -np.ones(40, np.float32)
+    out = dev(np.full(2, -1, np.int32))
+    B.sign_pack(dev(U), bits=out)
+    assert u32(out).tolist() == [0xFFFFFFFF, 0x000000FF]
+
+
+# --------------------------------------------------------------------------
+# majority vote
+# --------------------------------------------------------------------------
+def test_vote_blog_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "blog_vote_example.json")))
+    dirs = np.array(g["directions"], np.float32).reshape(3, 4)
+    bits = torch.cat([B.sign_pack(dev(dirs[m])) for m in range(3)])
+    D, S = B.majority_vote(bits, 3, 4, 0, stride=1, want_sums=True)
+    assert host(D).reshape(2, 2).tolist() == g["majority"]
+    assert host(S).tolist() == [-1, -1, 3, 1]
+
+
+def test_vote_mean_versus_majority(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "blog_mean_vs_majority.json")))
+    x = np.array(g["directions"], np.float32)
+    bits = torch.cat([B.sign_pack(dev(x[m:m + 1])) for m in range(3)])
+    assert host(B.majority_vote(bits, 3, 1, 0, stride=1)).tolist() == [g["majority"]]
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 15, 16, 200, 255, 256, 1001])
+@pytest.mark.parametrize("n", [7, 32, 1000, 65536 + 17])
+def test_vote_bit_exact(M, n):
+    print(f"vote M={M} n={n}", flush=True)
+    rng = np.random.default_rng(M * 7919 + n)
+    words = (n + 31) // 32
+    stride = words + (3 if M > 1 else 0)
+    bits = rng.integers(0, 2 ** 32, size=(M, stride), dtype=np.uint32)
+    for tie in (0, 1):
+        D, S = B.majority_vote(dev(bits.view(np.int32)), M, n, tie, stride=stride,
+                               want_sums=True)
+        sums = O.vote_sums_from_bits(bits[:, :words], n)
+        assert np.array_equal(host(S).astype(np.int32), sums)
+        assert np.array_equal(host(D), O.majority_from_sums(sums, tie))
+
+
+@pytest.mark.parametrize("M", [2, 8, 200, 1000])
+def test_vote_planted_ties(M):
+    rng = np.random.default_rng(M)
+    n = 4096 * 8
+    words = n // 32
+    bits = rng.integers(0, 2 ** 32, size=(M, words), dtype=np.uint32)
+    mask = rng.integers(0, 2 ** 32, size=words, dtype=np.uint32) & \
+        rng.integers(0, 2 ** 32, size=words, dtype=np.uint32)   # ~25% of entries
+    bits[: M // 2] &= ~mask
+    bits[M // 2:] |= mask
+    sums = O.vote_sums_from_bits(bits, n)
+    assert (sums == 0).mean() > 0.2
+    for tie in (0, 1):
+        D = B.majority_vote(dev(bits.view(np.int32)), M, n, tie)
+        assert np.array_equal(host(D), O.majority_from_sums(sums, tie))
+
+
+def test_vote_sums_beyond_int8():
+    # 200 agreeing workers: sums of +-200 need more than int8
+    M, n = 200, 64
+    bits = np.zeros((M, 2), np.uint32)
+    bits[:, 1] = 0xFFFFFFFF
+    D, S = B.majority_vote(dev(bits.view(np.int32)), M, n, 0, want_sums=True)
+    assert host(S).tolist() == [200] * 32 + [-200] * 32
+    assert host(D).tolist() == [1] * 32 + [-1] * 32
+
+
+# --------------------------------------------------------------------------
+# apply
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("w_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["ternary", "float"])
+@pytest.mark.parametrize("n", [5, 4096, 1000003])
+def test_apply_bit_exact(w_dtype, kind, n):
+    print(f"apply {w_dtype} {kind} n={n}", flush=True)
+    rng = np.random.default_rng(n)
+    W = (0.05 * rng.standard_normal(n)).astype(np.float32)
+    if w_dtype == "bf16":
+        W = O.bf16_round_nearest_even(W)
+    eta = 0.0123
+    if kind == "ternary":
+        D = rng.integers(-1, 2, n).astype(np.int8)
+        Wt = dev(W, torch.bfloat16 if w_dtype == "bf16" else None)
+        B.apply(Wt, eta, D=dev(D))
+    else:
+        D = (0.3 * rng.standard_normal(n)).astype(np.float32)
+        Wt = dev(W, torch.bfloat16 if w_dtype == "bf16" else None)
+        B.apply(Wt, eta, Df=dev(D))
+    want = O.apply_update(W, D, f32(eta), w_dtype)
+    got = host(Wt.float())
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_apply_bf16_rounding_ties_by_hand():
+    # W = 1.0; see the oracle pins for the derivation of each expected pattern
+    cases = [(2.0 ** -9, 1, 0x3F80), (3 * 2.0 ** -9, 1, 0x3F7E), (2.0 ** -9, -1, 0x3F80),
+             (2.0 ** -8, -1, 0x3F80), (3 * 2.0 ** -8, -1, 0x3F82)]
+    for eta, d, want in cases:
+        Wt = torch.ones(1, dtype=torch.bfloat16, device="cuda")
+        B.apply(Wt, eta, D=torch.tensor([d], dtype=torch.int8, device="cuda"))
+        assert int(host(Wt.view(torch.int16))[0]) & 0xFFFF == want
+
+
+def test_apply_eta_zero_identity():
+    W = torch.randn(10000, device="cuda").to(torch.bfloat16)
+    W0 = W.clone()
+    B.apply(W, 0.0, D=torch.ones(10000, dtype=torch.int8, device="cuda"))
+    assert torch.equal(W.view(torch.int16), W0.view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# momentum
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("w_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [3, 1024, 500001])
+def test_momentum_tolerance(w_dtype, n):
+    rng = np.random.default_rng(n)
+    G = rng.standard_normal(n).astype(np.float32)
+    Mom = (0.3 * rng.standard_normal(n)).astype(np.float32)
+    W = (0.02 * rng.standard_normal(n)).astype(np.float32)
+    if w_dtype == "bf16":
+        W = O.bf16_round_nearest_even(W)
+    beta, lam = 0.9, 0.01
+    Mt = dev(Mom)
+    B.momentum(dev(G), dev(W, torch.bfloat16 if w_dtype == "bf16" else None), Mt, beta, lam)
+    want = O.momentum_update(Mom, G, W, f32(beta), f32(lam))
+    got = host(Mt).astype(np.float64)
+    tol = momentum_tol(Mom, G, W, f32(beta), f32(lam))
+    assert np.all(np.abs(got - want) <= tol)
+
+
+def test_momentum_beta_zero_exact():
+    # beta = 0, lambda = 0: Mom' = G exactly
+    G = np.random.default_rng(0).standard_normal(999).astype(np.float32)
+    Mt = dev(np.zeros(999, np.float32))
+    B.momentum(dev(G), dev(np.zeros(999, np.float32)), Mt, 0.0, 0.0)
+    assert np.array_equal(host(Mt), G)

@@ -1,0 +1,237 @@
+"""GPU parity of the fused signmuon_step against the oracle's step.
+
+Every step starts from a state the oracle produced (its W_t and its float64
+momentum rounded to float32), so differences do not compound; the other
+workers' packed buffers are the oracle's own.  The checks per step:
+* momentum of the local worker within the float32 evaluation bound;
+* the local worker's packed signs pass the sign gate against the oracle's
+  polar factor (post-vote: against its momentum);
+* W is bit-exact wherever the local worker's bit equals the oracle's (every
+  vote input is then identical), and otherwise moves by at most one step;
+* post-vote: the polar factor recovered from the W update is within the
+  polar tolerance of the oracle's and passes the sign gate.
+Full-size workloads are checked on sampled matrices the oracle can afford.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from distributed_bit_matrix_amd import binding as B
+from distributed_bit_matrix_amd import workloads as WL
+from tests.gpu_common import f32, momentum_tol, oracle_hp, polar_tol, sign_gate, unpack_neg
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def hparams(w):
+    return B.HParams(eta=w.eta, beta=w.beta, lam=w.lam, eps=w.eps, K=w.K, scale=w.scale,
+                     P=w.P, coeffs=w.coeffs, precision=w.ns_precision,
+                     tie_value=w.tie_value)
+
+
+class GpuState:
+    def __init__(self, w, hp):
+        self.w = w
+        self.layout, self.d, self.words = B.default_layout(w.mats)
+        self.plan = B.StepPlan(self.layout, hp, w.post_vote)
+        self.wdt = torch.bfloat16 if w.w_dtype == "bf16" else torch.float32
+
+    def run(self, W, Mom0, G0, bits, u0):
+        W_t = torch.from_numpy(np.ascontiguousarray(W, np.float32)).cuda().to(self.wdt)
+        M_t = torch.from_numpy(np.ascontiguousarray(Mom0, np.float32)).cuda()
+        G_t = torch.from_numpy(np.ascontiguousarray(G0, np.float32)).cuda()
+        b_t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int32)).cuda()
+        u_t = None if u0 is None else torch.from_numpy(u0).cuda()
+        self.plan(G_t, W_t, M_t, b_t, self.words, bits.shape[0], 0, u0=u_t)
+        st = self.plan.status()
+        torch.cuda.synchronize()
+        return (W_t.float().cpu().numpy(), M_t.cpu().numpy(),
+                b_t.cpu().numpy().view(np.uint32), st)
+
+
+def u0_concat(w):
+    return np.concatenate(WL.power_start(w)).astype(np.float32) if w.scale == "spectral" \
+        else None
+
+
+def check_step(w, st, hp, W, Moms, Gs, u0s, sample=None, other_bits=None):
+    """One step from the oracle's state; returns the oracle's output."""
+    o = oracle_hp(hp)
+    mats = list(w.mats)
+    offs, woffs = w.elem_offsets, w.word_offsets
+    idx = list(range(len(mats))) if sample is None else sample
+    M = len(Gs) if other_bits is None else other_bits.shape[0]
+    # oracle: local worker (0) on the sampled matrices
+    Mom_new0 = O.momentum_update(Moms[0], Gs[0], W, o["beta"], o["lam"])
+    U0 = {}
+    for i in idx:
+        r, c = mats[i]
+        blk = Mom_new0[offs[i]:offs[i] + r * c].reshape(r, c)
+        if w.post_vote:
+            U0[i] = blk
+        else:
+            U0[i], _ = O.polar_ns(blk, o["K"], o["eps"], o["scale"], o["P"], o["coeffs"],
+                                  None if u0s is None else u0s[i].astype(np.float64))
+    if other_bits is None:
+        # the other workers are the oracle's own pipelines
+        out = O.step(mats, W, Moms, Gs, o, w.tie_value, w.post_vote, w.w_dtype,
+                     None if u0s is None else [u.astype(np.float64) for u in u0s])
+        bits_in = out["bits"].copy()
+    else:
+        out = None
+        bits_in = other_bits.copy()
+        for i in idx:
+            bits_in[0, woffs[i]:woffs[i] + (mats[i][0] * mats[i][1] + 31) // 32] = \
+                O.pack_signs(U0[i])
+    u0 = None if u0s is None else np.concatenate(u0s).astype(np.float32)
+    Wg, Mg, bg, status = st.run(W, np.float32(Moms[0]), Gs[0], bits_in, u0)
+    assert status == B.SM_OK
+    # momentum (all entries)
+    tol = momentum_tol(np.float32(Moms[0]), Gs[0], W, o["beta"], o["lam"])
+    assert np.all(np.abs(Mg.astype(np.float64) - Mom_new0) <= tol)
+    for i in idx:
+        r, c = mats[i]
+        n = r * c
+        sl = slice(offs[i], offs[i] + n)
+        wsl = slice(woffs[i], woffs[i] + (n + 31) // 32)
+        gneg = unpack_neg(bg[0, wsl], n)
+        ok, stats = sign_gate(gneg, U0[i])
+        assert ok, (i, mats[i], stats)
+        oneg = unpack_neg(bits_in[0, wsl], n)
+        same = gneg == oneg
+        # vote inputs identical where the local bit agrees
+        sums = O.vote_sums_from_bits(bits_in[:, wsl], n)
+        if w.post_vote:
+            D = O.majority_from_sums(sums, w.tie_value).astype(np.float64).reshape(r, c)
+            Upost, _ = O.polar_ns(D, o["K"], o["eps"], o["scale"], o["P"], o["coeffs"],
+                                  None if u0s is None else u0s[i].astype(np.float64))
+            if same.all():
+                Ug = (W[sl].astype(np.float64) - Wg[sl].astype(np.float64)) / o["eta"]
+                assert np.abs(Ug - Upost.reshape(-1)).max() <= polar_tol(hp.precision) + 1e-6
+                ok, stats = sign_gate(Ug < 0, Upost.reshape(-1))
+                assert ok, (i, "post-vote", stats)
+            continue
+        D = O.majority_from_sums(sums, w.tie_value)
+        Wn = O.apply_update(W[sl], D, o["eta"], w.w_dtype)
+        assert np.array_equal(Wg[sl][same].view(np.uint32), Wn[same].view(np.uint32)), i
+        moved = np.abs(Wg[sl][~same].astype(np.float64) - W[sl][~same])
+        assert np.all(moved <= 1.01 * o["eta"] + 1e-2 * np.abs(W[sl][~same])), i
+    return out
+
+
+def gradients(w, t, M):
+    return [WL.gradient(w, t, m).astype(np.float64) for m in range(M)]
+
+
+# --------------------------------------------------------------------------
+# Oracle-sized workloads, several steps (common state from the oracle)
+# --------------------------------------------------------------------------
+SMALL = {
+    "single": (WL.get("single"), None, 10),
+    "resnet50": (WL.scaled(WL.get("resnet50"), [(64, 147), (128, 576), (256, 512),
+                                                (512, 256), (10, 256)]), None, 3),
+    "nanogpt": (WL.scaled(WL.get("nanogpt"), [(192, 576), (192, 192), (192, 768),
+                                              (768, 192)] * 2), None, 3),
+    "llm_mlp": (WL.scaled(WL.get("llm_mlp"), [(256, 256), (256, 1024)]), None, 2),
+    "llm_mlp_quintic": (WL.scaled(WL.get("llm_mlp"), [(256, 256), (256, 1024)],
+                                  name="llm_mlp-q").replace(coeffs=WL.QUINTIC,
+                                                            ns_precision="bf16x3"), None, 2),
+    "postvote": (WL.scaled(WL.get("postvote"), [(128, 128)] * 6 + [(256, 512)] * 2,
+                           M=40), None, 3),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_step_multistep_small(name):
+    w, _, T = SMALL[name]
+    print(f"step {name} mats={len(w.mats)} M={w.M} T={T}", flush=True)
+    hp = hparams(w)
+    st = GpuState(w, hp)
+    W = WL.init_weights(w)
+    Moms = [np.zeros(w.d) for _ in range(w.M)]
+    u0s = WL.power_start(w) if w.scale == "spectral" else None
+    for t in range(T):
+        Gs = gradients(w, t, w.M)
+        out = check_step(w, st, hp, W, Moms, Gs, u0s)
+        W, Moms = out["Wn"], out["Mom"]
+
+
+def test_step_nonfinite_skips_update():
+    w = SMALL["nanogpt"][0]
+    hp = hparams(w)
+    st = GpuState(w, hp)
+    W = WL.init_weights(w)
+    G = WL.gradient(w, 0, 0)
+    G[12345] = np.inf
+    bits = WL.random_bits(w, w.M)
+    Wg, Mg, bg, status = st.run(W, np.zeros(w.d, np.float32), G, bits, None)
+    assert status == B.SM_ENONFINITE
+    assert np.array_equal(Wg.view(np.uint32), W.view(np.uint32))
+    # the next finite step clears the flag
+    Wg, Mg, bg, status = st.run(W, np.zeros(w.d, np.float32), WL.gradient(w, 0, 0), bits,
+                                None)
+    assert status == B.SM_OK
+
+
+def test_step_deterministic_and_permutation_invariant():
+    w = SMALL["nanogpt"][0]
+    hp = hparams(w)
+    st = GpuState(w, hp)
+    W = WL.init_weights(w)
+    Mom = WL.init_momentum(w, 0, std=0.1)
+    G = WL.gradient(w, 0, 0)
+    bits = WL.random_bits(w, w.M)
+    a = st.run(W, Mom, G, bits, None)
+    b = st.run(W, Mom, G, bits, None)
+    assert all(np.array_equal(x, y) for x, y in zip(a[:3], b[:3]))
+    perm = np.concatenate([[0], 1 + np.random.default_rng(0).permutation(w.M - 1)])
+    c = st.run(W, Mom, G, bits[perm], None)
+    assert np.array_equal(a[0].view(np.uint32), c[0].view(np.uint32))
+
+
+def test_step_zero_steps_K0():
+    w = SMALL["nanogpt"][0].replace(K=0)
+    hp = hparams(w)
+    st = GpuState(w, hp)
+    W = WL.init_weights(w)
+    Moms = [WL.init_momentum(w, m, std=0.1).astype(np.float64) for m in range(w.M)]
+    check_step(w, st, hp, W, Moms, gradients(w, 0, w.M), None)
+
+
+# --------------------------------------------------------------------------
+# Full-size workloads (the shapes the benchmark times), sampled matrices
+# --------------------------------------------------------------------------
+def full_case(name, sample, bits_kind="random"):
+    w = WL.get(name)
+    print(f"full-size step {name} d={w.d} M={w.M} sample={sample}", flush=True)
+    hp = hparams(w)
+    st = GpuState(w, hp)
+    W = WL.init_weights(w)
+    Mom0 = WL.init_momentum(w, 0, std=0.05).astype(np.float64)
+    G0 = WL.gradient(w, 0, 0).astype(np.float64)
+    if bits_kind == "ties":
+        bits, _ = WL.planted_tie_bits(w)
+    else:
+        bits = WL.random_bits(w, w.M)
+    u0s = WL.power_start(w) if w.scale == "spectral" else None
+    check_step(w, st, hp, W, [Mom0], [G0], u0s, sample=sample, other_bits=bits)
+
+
+def test_step_full_nanogpt():
+    full_case("nanogpt", sample=[0, 1, 2, 3, 46, 47])
+
+
+def test_step_full_resnet50():
+    full_case("resnet50", sample=list(range(9)))
+
+
+@pytest.mark.slow
+def test_step_full_llm_mlp():
+    full_case("llm_mlp", sample=[0])
+
+
+@pytest.mark.slow
+def test_step_full_postvote():
+    full_case("postvote", sample=[0, 1, 511, 512], bits_kind="ties")
