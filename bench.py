@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--workload", default="nanogpt")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one plain elementwise kernel that reads and writes "
+                         "MIB MiB (reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         sys.exit("bench.py measures one GPU: the method's M workers are resident sign "
@@ -140,6 +143,15 @@ def main():
 
     def step():
         plan(G, W, Mom, bits, words, w.M, 0, u0=u0)
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)          # reads and writes n * 4 bytes
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

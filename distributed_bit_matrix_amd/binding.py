@@ -14,7 +14,9 @@ import os
 from typing import Optional, Sequence, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsignmuon.so")
+# SIGNMUON_LIB may name another build of the same library (e.g. a tuning
+# variant); the default is the in-tree build.
+LIB_PATH = os.environ.get("SIGNMUON_LIB") or os.path.join(_HERE, "libsignmuon.so")
 
 SM_OK, SM_EINVAL, SM_EWORKSPACE, SM_EHIP, SM_ENONFINITE, SM_ERANGE, SM_EUNSUPPORTED = \
     0, -1, -2, -3, -4, -5, -6

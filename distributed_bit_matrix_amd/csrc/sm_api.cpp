@@ -96,6 +96,10 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
   for (int pp = 0; pp < (ns ? 2 : 1); ++pp) {
     P.off_x[pp][0] = take(x * opb);
     if (split) P.off_x[pp][1] = take(x * opb);
+    if (ns) {
+      P.off_xt[pp][0] = take(x * opb);
+      if (split) P.off_xt[pp][1] = take(x * opb);
+    }
   }
   if (ns) {
     P.off_b[0] = take(r2 * opb);
@@ -118,9 +122,17 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
 }
 
 // Split matrices (a subset, by index) into runs of equal shape and constant
-// strides of every offset family.
+// strides of every offset family.  Matrices are visited shape by shape (in
+// their original order within a shape), so a layout that interleaves shapes,
+// such as the projections of successive transformer layers, still gives one
+// run per shape.
 std::vector<Group> make_groups(const std::vector<MatPlan>& mp,
-                               const std::vector<int>& sel) {
+                               const std::vector<int>& sel_in) {
+  std::vector<int> sel(sel_in);
+  std::stable_sort(sel.begin(), sel.end(), [&](int a, int b) {
+    if (mp[a].rows != mp[b].rows) return mp[a].rows < mp[b].rows;
+    return mp[a].cols < mp[b].cols;
+  });
   std::vector<Group> out;
   for (size_t t = 0; t < sel.size(); ++t) {
     const MatPlan& q = mp[sel[t]];
@@ -169,7 +181,9 @@ std::vector<Group> make_groups(const std::vector<MatPlan>& mp,
 // per-group launch fields (blocks_per_mat, gm, gn, gk, tiles_n, ops) and
 // returns false to drop a group; `go` launches.
 template <class Fill, class Go>
-hipError_t for_launches(const std::vector<Group>& groups, Fill fill, Go go) {
+hipError_t for_launches(const std::vector<Group>& groups, Fill fill, Go go,
+                        int* launched = nullptr) {
+  if (launched) *launched = 0;
   std::vector<Group> gs;
   for (const Group& g0 : groups) {
     Group g = g0;
@@ -191,6 +205,7 @@ hipError_t for_launches(const std::vector<Group>& groups, Fill fill, Go go) {
     G.total_blocks = (int32_t)blocks;
     hipError_t err = go(G);
     if (err != hipSuccess) return err;
+    if (launched) ++*launched;
   }
   return hipSuccess;
 }
@@ -199,6 +214,7 @@ struct Bufs {
   char* base;
   int32_t* status;
   void* x[2][2];
+  void* xt[2][2];
   void* b[2];
   void* a[2];
   float* araw;
@@ -215,7 +231,10 @@ Bufs bind(const Plan& P, void* ws) {
   auto at = [&](size_t off) -> void* { return off ? B.base + off : nullptr; };
   B.status = reinterpret_cast<int32_t*>(B.base + P.off_status);
   for (int p = 0; p < 2; ++p)
-    for (int h = 0; h < 2; ++h) B.x[p][h] = at(P.off_x[p][h]);
+    for (int h = 0; h < 2; ++h) {
+      B.x[p][h] = at(P.off_x[p][h]);
+      B.xt[p][h] = at(P.off_xt[p][h]);
+    }
   B.b[0] = at(P.off_b[0]); B.b[1] = at(P.off_b[1]);
   B.a[0] = at(P.off_a[0]); B.a[1] = at(P.off_a[1]);
   B.araw = static_cast<float*>(at(P.off_araw));
@@ -289,13 +308,13 @@ sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
     g.gk = (int32_t)(q.tall ? q.Mp : q.Np);
     g.tiles_n = (int32_t)(q.Rp / 128);
     g.blocks_per_mat = g.tiles_n * g.tiles_n;
-    g.ops = q.tall ? gemm_ops(FAM_X, 0, FAM_X, 0) : gemm_ops(FAM_X, 1, FAM_X, 1);
+    g.ops = q.tall ? gemm_ops(FAM_XT, FAM_XT) : gemm_ops(FAM_X, FAM_X);
     return true;
   };
   if (!P.spectral) {
     HIP_TRY(for_launches(groups, [&](Group& g) {
       g.blocks_per_mat = 1;
-      g.gk = (int32_t)(part_kind == 0 ? mp[g.idx0].Mp * mp[g.idx0].Np / kChunk
+      g.gk = (int32_t)(part_kind == 0 ? mp[g.idx0].Mp * mp[g.idx0].Np / 4096
                                       : (((mp[g.idx0].rows * mp[g.idx0].cols + 31) / 32) + 255) / 256);
       return true;
     }, [&](const Groups& G) { return launch_fro_finalize(G, B.part, hp->eps, B.scal, s); }));
@@ -306,6 +325,7 @@ sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
       std::memset(&a, 0, sizeof(a));
       a.G = G;
       a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
+      a.xt_hi = B.xt[0][0]; a.xt_lo = B.xt[0][1];
       a.epi = E_OP; a.mul = gram_mul; a.scal = B.scal; a.scal_pow = 2;
       a.o_hi = dst_hi; a.o_lo = dst_lo;
       return launch_gemm(prec, a, s);
@@ -317,6 +337,7 @@ sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
       std::memset(&a, 0, sizeof(a));
       a.G = G;
       a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
+      a.xt_hi = B.xt[0][0]; a.xt_lo = B.xt[0][1];
       a.epi = E_RAW; a.o_raw = B.araw;
       return launch_gemm(prec, a, s);
     }));
@@ -329,7 +350,7 @@ sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
     }, [&](const Groups& G) { return launch_power_init(G, io.u0, va, s); }));
     for (int p = 0; p < hp->P; ++p) {
       HIP_TRY(for_launches(groups, [&](Group& g) {
-        g.blocks_per_mat = (int32_t)(mp[g.idx0].Rp / 64);
+        g.blocks_per_mat = (int32_t)(mp[g.idx0].Rp / 16);
         return true;
       }, [&](const Groups& G) { return launch_power_step(G, B.araw, va, vb, s); }));
       std::swap(va, vb);
@@ -360,7 +381,7 @@ hipError_t run_square(const Plan& P, const std::vector<MatPlan>& mp,
     g.gm = g.gn = g.gk = (int32_t)q.Rp;
     g.tiles_n = (int32_t)(q.Rp / 128);
     g.blocks_per_mat = g.tiles_n * g.tiles_n;
-    g.ops = gemm_ops(FAM_R, 1, FAM_R, 1);
+    g.ops = gemm_ops(FAM_R, FAM_R);
     return true;
   }, [&](const Groups& G) {
     GemmArgs a;
@@ -389,13 +410,14 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
         g.gk = (int32_t)(q.tall ? q.Mp : q.Np);
         g.tiles_n = (int32_t)(q.Rp / 128);
         g.blocks_per_mat = g.tiles_n * g.tiles_n;
-        g.ops = q.tall ? gemm_ops(FAM_X, 0, FAM_X, 0) : gemm_ops(FAM_X, 1, FAM_X, 1);
+        g.ops = q.tall ? gemm_ops(FAM_XT, FAM_XT) : gemm_ops(FAM_X, FAM_X);
         return true;
       }, [&](const Groups& G) {
         GemmArgs a;
         std::memset(&a, 0, sizeof(a));
         a.G = G;
         a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
+        a.xt_hi = B.xt[cur][0]; a.xt_lo = B.xt[cur][1];
         a.epi = E_OP; a.mul = P.quintic ? 1.0f : hp->ns_b; a.scal_pow = 0;
         a.o_hi = P.quintic ? B.a[0] : B.b[0];
         a.o_lo = P.quintic ? B.a[1] : B.b[1];
@@ -413,6 +435,7 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
       // pass 0: matrices using the requested final output; pass 1: the
       // unfusable ones writing U into the workspace (only when last).
       if (pass == 1 && !(last && io.final_out == O_BITS)) break;
+      int launched = 0;
       HIP_TRY(for_launches(groups, [&](Group& g) {
         const MatPlan& q = mp[g.idx0];
         if (last && io.final_out == O_BITS && fusable[g.idx0] != (pass == 0)) return false;
@@ -420,22 +443,24 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
         g.gk = (int32_t)q.Rp;
         g.tiles_n = (int32_t)(q.Np / 128);
         g.blocks_per_mat = (int32_t)((q.Mp / 128) * g.tiles_n);
-        g.ops = q.tall ? gemm_ops(FAM_X, 1, FAM_R, 1) : gemm_ops(FAM_R, 1, FAM_X, 0);
+        g.ops = q.tall ? gemm_ops(FAM_X, FAM_R) : gemm_ops(FAM_R, FAM_XT);
         return true;
       }, [&](const Groups& G) {
         GemmArgs a;
         std::memset(&a, 0, sizeof(a));
         a.G = G;
         a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
+        a.xt_hi = B.xt[cur][0]; a.xt_lo = B.xt[cur][1];
         a.r_hi = B.b[0]; a.r_lo = B.b[1];
         a.epi = E_UPDATE; a.ca = hp->ns_a;
         a.xsrc = k == 1 ? io.first_xsrc : XS_OP;
         a.scal = B.scal; a.scal_pow = k == 1 ? 1 : 0;
         a.xs_user = io.src_user;
-        a.xs_hi = B.x[cur][0]; a.xs_lo = B.x[cur][1];
+        a.xs_hi = B.xt[cur][0]; a.xs_lo = B.xt[cur][1];   // read as X^T
         if (!last) {
           a.out = O_X;
           a.o_hi = B.x[cur ^ 1][0]; a.o_lo = B.x[cur ^ 1][1];
+          a.ot_hi = B.xt[cur ^ 1][0]; a.ot_lo = B.xt[cur ^ 1][1];
         } else if (io.final_out == O_BITS && pass == 1) {
           a.out = O_U; a.U = B.u;
         } else {
@@ -445,8 +470,8 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
           a.status = io.status;
         }
         return launch_gemm(prec, a, s);
-      }));
-      HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+      }, &launched));
+      if (launched) HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
     }
     cur ^= 1;
   }
@@ -561,8 +586,10 @@ sm_status signmuon_polar_ns(const float* X, float* U, int64_t rows, int64_t cols
   std::memset(&sw, 0, sizeof(sw));
   sw.ema = 0; sw.precision = P.precision; sw.src = X;
   sw.o_hi = B.x[0][0]; sw.o_lo = B.x[0][1]; sw.part = B.part;
+  sw.ot_hi = B.xt[0][0]; sw.ot_lo = B.xt[0][1];
+  if (hp->K == 0) sw.ot_hi = sw.ot_lo = nullptr;
   HIP_TRY(for_launches(groups, [&](Group& g) {
-    g.blocks_per_mat = (int32_t)(mp[g.idx0].Mp * mp[g.idx0].Np / kChunk);
+    g.blocks_per_mat = (int32_t)(mp[g.idx0].Mp * mp[g.idx0].Np / 4096);
     return true;
   }, [&](const Groups& G) { sw.G = G; return launch_sweep(sw, stream); }));
   NsIO io;
@@ -694,10 +721,11 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
       sw.beta = hp->beta; sw.lam = hp->lambda;
       sw.Gr = G; sw.W = W; sw.Mom = Mom;
       sw.o_hi = B.x[0][0]; sw.o_lo = B.x[0][1];
+      sw.ot_hi = B.xt[0][0]; sw.ot_lo = B.xt[0][1];
       sw.part = P.spectral ? nullptr : B.part;
       sw.status = B.status;
       HIP_TRY(for_launches(groups, [&](Group& g) {
-        g.blocks_per_mat = (int32_t)(mp[g.idx0].Mp * mp[g.idx0].Np / kChunk);
+        g.blocks_per_mat = (int32_t)(mp[g.idx0].Mp * mp[g.idx0].Np / 4096);
         return true;
       }, [&](const Groups& Gs) { sw.G = Gs; return launch_sweep(sw, stream); }));
       HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
@@ -749,6 +777,15 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   HIP_TRY(for_launches(groups, vote_fill, [&](const Groups& Gs) {
     va.G = Gs; return launch_vote_groups(va, stream);
   }));
+  if (hp->K > 0) {
+    HIP_TRY(for_launches(groups, [&](Group& g) {
+      g.blocks_per_mat = (int32_t)(mp[g.idx0].Mp * mp[g.idx0].Np / 4096);
+      return true;
+    }, [&](const Groups& Gs) {
+      return launch_transpose_op(Gs, P.precision, B.x[0][0], B.x[0][1], B.xt[0][0],
+                                 B.xt[0][1], stream);
+    }));
+  }
   HIP_TRY(mark(prof, SM_PHASE_VOTE, stream));
   io.first_xsrc = XS_OP; io.src_user = nullptr;
   io.final_out = O_APPLY;

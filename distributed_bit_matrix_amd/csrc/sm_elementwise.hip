@@ -299,85 +299,135 @@ hipError_t launch_apply_flat(void* W, int w_bf16, const int8_t* D,
 }
 
 // ---------------------------------------------------------------------------
-// Padded sweep: momentum (or a plain float32 source) -> padded operand copy
-// + partial sums of squares + non-finite flag.  8 entries per thread.
+// Padded sweep over 64x64 tiles of the padded matrix: momentum (or a plain
+// float32 source) -> padded operand copy X and its transpose X^T, partial
+// sums of squares per tile, non-finite flag.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_op4v(int precision, void* hi, void* lo,
+                                           int64_t i, const float (&v)[4]) {
+  if (precision == P_F32) {
+    *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(hi) + i) = f32x4_t{v[0], v[1], v[2], v[3]};
+    return;
+  }
+  bf16_t h[4], l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (precision == P_BF16X3) split_bf16(v[k], h[k], l[k]);
+    else { h[k] = f32_to_bf16(v[k]); l[k] = 0; }
+  }
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<u32x2_t*>(reinterpret_cast<bf16_t*>(hi) + i) =
+      u32x2_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+  if (precision == P_BF16X3)
+    *reinterpret_cast<u32x2_t*>(reinterpret_cast<bf16_t*>(lo) + i) =
+        u32x2_t{(uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16)};
+}
+
+// Phase 2 of a tile: write the transpose of the 64x64 tile held in LDS.
+__device__ __forceinline__ void write_tile_t(const float (*tile)[65], int precision,
+                                             void* t_hi, void* t_lo, int64_t xoff,
+                                             int64_t Mp, int r0, int c0) {
+  const int cc = threadIdx.x >> 2, rr0 = (threadIdx.x & 3) * 16;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = tile[rr0 + 4 * k + e][cc];
+    store_op4v(precision, t_hi, t_lo, xoff + (int64_t)(c0 + cc) * Mp + r0 + rr0 + 4 * k, v);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_sweep(SweepArgs a) {
+  __shared__ float tile[64][65];
   int gi, mi, q;
   group_of_block(a.G, blockIdx.x, gi, mi, q);
   const Group& g = a.G.g[gi];
   const int rows = g.rows, cols = g.cols;
-  const int64_t Np = round_up(cols, kPad);
+  const int64_t Mp = round_up(rows, kPad), Np = round_up(cols, kPad);
   const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
   const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
-  const int64_t p = (int64_t)q * kChunk + threadIdx.x * 8;
-  const int row = (int)(p / Np), col = (int)(p - (int64_t)row * Np);
-  float v[8];
-  float ss = 0.0f;
-  bool bad = false;
-  const int64_t u = eoff + (int64_t)row * cols + col;
-  if (row < rows && col + 8 <= cols && g.vec_ok) {
-    if (a.ema) {
-      f32x4_t g0 = reinterpret_cast<const f32x4_t*>(a.Gr + u)[0];
-      f32x4_t g1 = reinterpret_cast<const f32x4_t*>(a.Gr + u)[1];
-      f32x4_t m0 = reinterpret_cast<const f32x4_t*>(a.Mom + u)[0];
-      f32x4_t m1 = reinterpret_cast<const f32x4_t*>(a.Mom + u)[1];
-      float w[8];
-      if (a.w_bf16) {
-        u32x4_t wb = *reinterpret_cast<const u32x4_t*>(
-            reinterpret_cast<const bf16_t*>(a.W) + u);
+  const int tiles_c = (int)(Np / 64);
+  const int r0 = (q / tiles_c) * 64, c0 = (q % tiles_c) * 64;
+  const int lr0 = threadIdx.x >> 4, lc = (threadIdx.x & 15) * 4;
+  const int col = c0 + lc;
+  // Each thread owns a 4-wide column strip in rows lr0 + 16 p (p < 4).  All
+  // loads are issued before any store (the momentum is read and written).
+  float gv[4][4], wv[4][4], mv[4][4];
+  bool full[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          w[2 * k] = __uint_as_float(wb[k] << 16);
-          w[2 * k + 1] = __uint_as_float(wb[k] & 0xFFFF0000u);
+  for (int p = 0; p < 4; ++p) {
+    const int row = r0 + lr0 + 16 * p;
+    const int64_t u = eoff + (int64_t)row * cols + col;
+    full[p] = row < rows && col + 4 <= cols && g.vec_ok;
+    if (full[p]) {
+      if (a.ema) {
+        f32x4_t gg = *reinterpret_cast<const f32x4_t*>(a.Gr + u);
+        f32x4_t mm = *reinterpret_cast<const f32x4_t*>(a.Mom + u);
+        if (a.w_bf16) {
+          typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+          u32x2_t wb = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const bf16_t*>(a.W) + u);
+          wv[p][0] = __uint_as_float(wb[0] << 16); wv[p][1] = __uint_as_float(wb[0] & 0xFFFF0000u);
+          wv[p][2] = __uint_as_float(wb[1] << 16); wv[p][3] = __uint_as_float(wb[1] & 0xFFFF0000u);
+        } else {
+          f32x4_t wf = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(a.W) + u);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) wv[p][k] = wf[k];
         }
-      } else {
-        f32x4_t w0 = reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(a.W) + u)[0];
-        f32x4_t w1 = reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(a.W) + u)[1];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) { w[k] = w0[k]; w[4 + k] = w1[k]; }
+        for (int k = 0; k < 4; ++k) { gv[p][k] = gg[k]; mv[p][k] = mm[k]; }
+      } else {
+        f32x4_t sv = *reinterpret_cast<const f32x4_t*>(a.src + u);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) mv[p][k] = sv[k];
       }
-      float gg[8], mm[8];
+    } else {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        gg[k] = g0[k]; gg[4 + k] = g1[k]; mm[k] = m0[k]; mm[4 + k] = m1[k];
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        v[k] = ema(mm[k], gg[k], w[k], a.beta, a.lam);
-        bad |= !__builtin_isfinite(gg[k]) || !__builtin_isfinite(w[k]) ||
-               !__builtin_isfinite(v[k]);
-      }
-      reinterpret_cast<f32x4_t*>(a.Mom + u)[0] = f32x4_t{v[0], v[1], v[2], v[3]};
-      reinterpret_cast<f32x4_t*>(a.Mom + u)[1] = f32x4_t{v[4], v[5], v[6], v[7]};
-    } else {
-      f32x4_t s0 = reinterpret_cast<const f32x4_t*>(a.src + u)[0];
-      f32x4_t s1 = reinterpret_cast<const f32x4_t*>(a.src + u)[1];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) { v[k] = s0[k]; v[4 + k] = s1[k]; }
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      v[k] = 0.0f;
-      if (row < rows && col + k < cols) {
-        int64_t uk = u + k;
-        if (a.ema) {
-          float gk = a.Gr[uk], wk = load_w(a.W, a.w_bf16, uk);
-          float mk = ema(a.Mom[uk], gk, wk, a.beta, a.lam);
-          a.Mom[uk] = mk;
-          bad |= !__builtin_isfinite(gk) || !__builtin_isfinite(wk) ||
-                 !__builtin_isfinite(mk);
-          v[k] = mk;
-        } else {
-          v[k] = a.src[uk];
+        gv[p][k] = 0.0f; wv[p][k] = 0.0f; mv[p][k] = 0.0f;
+        if (row < rows && col + k < cols) {
+          if (a.ema) {
+            gv[p][k] = a.Gr[u + k];
+            wv[p][k] = load_w(a.W, a.w_bf16, u + k);
+            mv[p][k] = a.Mom[u + k];
+          } else {
+            mv[p][k] = a.src[u + k];
+          }
         }
       }
     }
   }
+  float ss = 0.0f;
+  bool bad = false;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) ss += v[k] * v[k];
-  store_op8(a.precision, a.o_hi, a.o_lo, xoff + p, v);
+  for (int p = 0; p < 4; ++p) {
+    const int row = r0 + lr0 + 16 * p;
+    const int64_t u = eoff + (int64_t)row * cols + col;
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool valid = row < rows && col + k < cols;
+      v[k] = mv[p][k];
+      if (a.ema && valid) {
+        v[k] = ema(mv[p][k], gv[p][k], wv[p][k], a.beta, a.lam);
+        bad |= !__builtin_isfinite(gv[p][k]) || !__builtin_isfinite(wv[p][k]) ||
+               !__builtin_isfinite(v[k]);
+      }
+      ss += v[k] * v[k];
+      tile[lr0 + 16 * p][lc + k] = v[k];
+    }
+    if (a.ema) {
+      if (full[p]) {
+        *reinterpret_cast<f32x4_t*>(a.Mom + u) = f32x4_t{v[0], v[1], v[2], v[3]};
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (row < rows && col + k < cols) a.Mom[u + k] = v[k];
+      }
+    }
+    store_op4v(a.precision, a.o_hi, a.o_lo, xoff + (int64_t)row * Np + col, v);
+  }
+  __syncthreads();
+  if (a.ot_hi) write_tile_t(tile, a.precision, a.ot_hi, a.ot_lo, xoff, Mp, r0, c0);
   if (bad && a.status) a.status[0] = 1;
   if (a.part) {
     float t = block_sum(ss);
@@ -388,6 +438,38 @@ __global__ __launch_bounds__(256) void k_sweep(SweepArgs a) {
 hipError_t launch_sweep(const SweepArgs& a, hipStream_t s) {
   if (a.G.total_blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_sweep, dim3(a.G.total_blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Transposed copy X -> X^T of padded operand copies, 64x64 tiles.
+__global__ __launch_bounds__(256) void k_transpose_op(Groups G, int precision,
+                                                      const void* hi, const void* lo,
+                                                      void* t_hi, void* t_lo) {
+  __shared__ float tile[64][65];
+  int gi, mi, q;
+  group_of_block(G, blockIdx.x, gi, mi, q);
+  const Group& g = G.g[gi];
+  const int64_t Mp = round_up(g.rows, kPad), Np = round_up(g.cols, kPad);
+  const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
+  const int tiles_c = (int)(Np / 64);
+  const int r0 = (q / tiles_c) * 64, c0 = (q % tiles_c) * 64;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int lr = (threadIdx.x >> 4) + 16 * p, lc = (threadIdx.x & 15) * 4;
+    const int64_t o = xoff + (int64_t)(r0 + lr) * Np + c0 + lc;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) tile[lr][lc + k] = load_opv(precision, hi, lo, o + k);
+  }
+  __syncthreads();
+  write_tile_t(tile, precision, t_hi, t_lo, xoff, Mp, r0, c0);
+}
+
+hipError_t launch_transpose_op(const Groups& G, int precision, const void* hi,
+                               const void* lo, void* t_hi, void* t_lo,
+                               hipStream_t s) {
+  if (G.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_transpose_op, dim3(G.total_blocks), dim3(256), 0, s, G,
+                     precision, hi, lo, t_hi, t_lo);
   return hipGetLastError();
 }
 
@@ -404,23 +486,34 @@ __global__ __launch_bounds__(256) void k_momentum_sign(MomSignArgs a) {
   const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
   const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int IT = kChunk / 256;
+  float gv[IT], wv[IT], mv[IT];
+  // all loads first: the momentum is read and written
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int64_t e = (int64_t)q * kChunk + (it * 4 + wave) * 64 + lane;
+    gv[it] = wv[it] = mv[it] = 0.0f;
+    if (e < mn) {
+      gv[it] = a.Gr[eoff + e];
+      wv[it] = load_w(a.W, a.w_bf16, eoff + e);
+      mv[it] = a.Mom[eoff + e];
+    }
+  }
   bool bad = false;
-#pragma unroll 1
-  for (int it = 0; it < kChunk / 256; ++it) {
-    int64_t base = (int64_t)q * kChunk + (it * 4 + wave) * 64;
-    int64_t e = base + lane;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int64_t base = (int64_t)q * kChunk + (it * 4 + wave) * 64;
+    const int64_t e = base + lane;
     bool neg = false;
     if (e < mn) {
-      int64_t u = eoff + e;
-      float gk = a.Gr[u], wk = load_w(a.W, a.w_bf16, u);
-      float mk = ema(a.Mom[u], gk, wk, a.beta, a.lam);
-      a.Mom[u] = mk;
-      bad |= !__builtin_isfinite(gk) || !__builtin_isfinite(wk) ||
+      const float mk = ema(mv[it], gv[it], wv[it], a.beta, a.lam);
+      a.Mom[eoff + e] = mk;
+      bad |= !__builtin_isfinite(gv[it]) || !__builtin_isfinite(wv[it]) ||
              !__builtin_isfinite(mk);
       neg = mk < 0.0f;
     }
-    uint64_t m = __ballot(neg);
-    int64_t w0 = base >> 5;
+    const uint64_t m = __ballot(neg);
+    const int64_t w0 = base >> 5;
     if (lane < 2 && w0 + lane < nw) a.bits[woff + w0 + lane] = (uint32_t)(m >> (32 * lane));
   }
   if (bad && a.status) a.status[0] = 1;
@@ -457,9 +550,12 @@ __global__ __launch_bounds__(256) void k_vote_groups(VoteArgs a) {
       if (g.vec_ok && e0 + 32 <= mn) {
         if (a.w_bf16) {
           u32x4_t* wp = reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(a.W) + u);
+          u32x4_t xs[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) xs[k] = wp[k];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            u32x4_t x = wp[k];
+            u32x4_t x = xs[k];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               int b0 = 8 * k + 2 * j;
@@ -475,9 +571,12 @@ __global__ __launch_bounds__(256) void k_vote_groups(VoteArgs a) {
           }
         } else {
           f32x4_t* wp = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.W) + u);
+          f32x4_t xs[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) xs[k] = wp[k];
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            f32x4_t x = wp[k];
+            f32x4_t x = xs[k];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               x[j] = apply_value(x[j], a.eta,
@@ -605,7 +704,8 @@ hipError_t launch_power_init(const Groups& G, const float* u0, float* vec,
   return hipGetLastError();
 }
 
-// dst = A * (src / |src|) for 64 rows per block (16 per wave).
+// dst = A * (src / |src|) for 16 rows per block (4 per wave); each lane
+// takes 4 consecutive entries per 256-entry stretch of a row.
 __global__ __launch_bounds__(256) void k_power_step(Groups G, const float* araw,
                                                     const float* src, float* dst) {
   int gi, mi, q;
@@ -621,13 +721,21 @@ __global__ __launch_bounds__(256) void k_power_step(Groups G, const float* araw,
   ss = block_sum(ss);
   const float inv = ss > 0.0f ? 1.0f / sqrtf(ss) : 0.0f;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int rr = 0; rr < 16; ++rr) {
-    int64_t row = (int64_t)q * 64 + wave * 16 + rr;
-    const float* a = araw + roff + row * Rp;
-    float acc = 0.0f;
-    for (int64_t k = lane; k < Rp; k += 64) acc += a[k] * (x[k] * inv);
-    acc = wave_sum(acc);
-    if (lane == 0) dst[voff + row] = acc;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int64_t row0 = (int64_t)q * 16 + wave * 4;
+  for (int64_t k = 4 * lane; k < Rp; k += 256) {
+    const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(x + k);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const f32x4_t av = *reinterpret_cast<const f32x4_t*>(araw + roff + (row0 + rr) * Rp + k);
+      acc[rr] += av[0] * (xv[0] * inv) + av[1] * (xv[1] * inv) + av[2] * (xv[2] * inv) +
+                 av[3] * (xv[3] * inv);
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const float t = wave_sum(acc[rr]);
+    if (lane == 0) dst[voff + row0 + rr] = t;
   }
 }
 

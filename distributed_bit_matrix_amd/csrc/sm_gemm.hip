@@ -8,13 +8,15 @@
 // 4 waves (2x2), each wave a 64x64 sub-tile built from 16x16 MFMA tiles:
 //   bf16 / split-bf16: v_mfma_f32_16x16x32_bf16
 //   f32:               v_mfma_f32_16x16x4_f32
-// Operands are staged through LDS in a [mn][k] layout (k contiguous) with
-// 128-byte rows and an XOR swizzle of 16-byte chunks; operands whose k axis
-// is strided in memory are transposed in registers on the way in (4 k-rows
-// per thread, written as 8- or 16-byte k-vectors).  Two LDS stages: the
-// next k-slab is fetched into registers while the current one is consumed.
-// All operand copies are zero padded to multiples of 128, so no loads are
-// predicated and padding contributes exact zeros.
+// Every operand is read k-contiguous (the iterate is kept both as X and as
+// X^T), so each 128-byte k-slab of a 128-row operand tile is fetched with
+// global_load_lds_dwordx4 straight into LDS: lane l of a wave writes the 16
+// bytes at the wave's LDS base + 16 l, and the XOR swizzle of 16-byte chunks
+// (against bank conflicts of the fragment reads) is applied by permuting
+// which global chunk each lane fetches.  NSTG LDS stages form the prefetch
+// pipeline; completion is tracked with explicit vmcnt waits and a bare
+// s_barrier.  All operand copies are zero padded to multiples of 128, so no
+// load is predicated and padding contributes exact zeros.
 #include "sm_internal.h"
 #include "sm_launch.h"
 
@@ -24,102 +26,42 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = 128;          // block tile (both dims)
 constexpr int ROWB = 128;        // bytes per LDS row (one k-slab)
 constexpr int TILEB = BM * ROWB; // bytes per operand tile per stage
+
+#ifndef SM_GEMM_STAGES
+#define SM_GEMM_STAGES 2
+#endif
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * ROWB + ((chunk ^ swz(row)) << 4);
 }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> { static constexpr int per16 = 8; };
 template <> struct Elem<float>  { static constexpr int per16 = 4; };
 
-// Per-matrix pointer offset of an operand family.
+// Per-matrix offset and row length of an operand family.
 __device__ __forceinline__ int64_t fam_off(const Group& g, int fam, int mi) {
-  return fam == FAM_X ? g.x0 + (int64_t)mi * g.x_stride
-                      : g.r0 + (int64_t)mi * g.r_stride;
+  return fam == FAM_R ? g.r0 + (int64_t)mi * g.r_stride
+                      : g.x0 + (int64_t)mi * g.x_stride;
 }
 __device__ __forceinline__ int64_t fam_ld(const Group& g, int fam) {
-  return fam == FAM_X ? round_up(g.cols, kPad)
-                      : round_up(g.rows < g.cols ? g.rows : g.cols, kPad);
-}
-
-// Fetch of one operand slab (128 mn x 128 bytes of k) into registers.
-// K-contiguous: 4 chunks of 16 bytes per thread (8 threads per row).
-// MN-contiguous: one 4(k) x (16 bytes of mn) patch per thread.
-template <typename T>
-struct SlabRegs { u32x4_t v[4]; };
-
-template <typename T>
-__device__ __forceinline__ void fetch_slab(SlabRegs<T>& R, const T* base,
-                                           int64_t ld, int kc, int mn0,
-                                           int k0, int tid) {
-  constexpr int P = Elem<T>::per16;           // elements per 16 bytes
-  constexpr int BK = ROWB / sizeof(T);        // k per slab
-  if (kc) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      int c = tid + 256 * q;
-      int row = c >> 3, ch = c & 7;
-      const T* p = base + (int64_t)(mn0 + row) * ld + k0 + ch * P;
-      R.v[q] = *reinterpret_cast<const u32x4_t*>(p);
-    }
-  } else {
-    constexpr int NQ = BM / P;               // patches along mn (16 or 32)
-    int mnq = tid % NQ, kq = tid / NQ;       // kq < BK/4
-    (void)BK;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const T* p = base + (int64_t)(k0 + 4 * kq + q) * ld + mn0 + mnq * P;
-      R.v[q] = *reinterpret_cast<const u32x4_t*>(p);
-    }
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ void store_slab(const SlabRegs<T>& R, char* lds,
-                                           int kc, int tid) {
-  if (kc) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      int c = tid + 256 * q;
-      int row = c >> 3, ch = c & 7;
-      *reinterpret_cast<u32x4_t*>(lds + lds_off(row, ch)) = R.v[q];
-    }
-  } else if constexpr (sizeof(T) == 2) {
-    // patch: 4 k-rows x 8 mn; emit 8 k-vectors of 4 bf16 (8 bytes)
-    int mnq = tid % 16, kq = tid / 16;       // kq in [0,16)
-    int ch = kq >> 1, half = kq & 1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      int w = e >> 1;
-      uint32_t a0 = R.v[0][w], a1 = R.v[1][w], a2 = R.v[2][w], a3 = R.v[3][w];
-      u32x2_t o;
-      if (e & 1) {
-        o[0] = (a0 >> 16) | (a1 & 0xFFFF0000u);
-        o[1] = (a2 >> 16) | (a3 & 0xFFFF0000u);
-      } else {
-        o[0] = (a0 & 0xFFFFu) | (a1 << 16);
-        o[1] = (a2 & 0xFFFFu) | (a3 << 16);
-      }
-      int row = mnq * 8 + e;
-      *reinterpret_cast<u32x2_t*>(lds + lds_off(row, ch) + half * 8) = o;
-    }
-  } else {
-    // patch: 4 k-rows x 4 mn floats; emit 4 k-vectors of 4 floats
-    int mnq = tid % 32, kq = tid / 32;       // kq in [0,8)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      u32x4_t o;
-      o[0] = R.v[0][e]; o[1] = R.v[1][e]; o[2] = R.v[2][e]; o[3] = R.v[3][e];
-      int row = mnq * 4 + e;
-      *reinterpret_cast<u32x4_t*>(lds + lds_off(row, kq)) = o;
-    }
-  }
+  if (fam == FAM_X) return round_up(g.cols, kPad);
+  if (fam == FAM_XT) return round_up(g.rows, kPad);
+  return round_up(g.rows < g.cols ? g.rows : g.cols, kPad);
 }
 
 // ---------------------------------------------------------------------------
@@ -149,6 +91,28 @@ __device__ __forceinline__ void store_op(void* hi, void* lo, int64_t i, float v)
     reinterpret_cast<bf16_t*>(hi)[i] = f32_to_bf16(v);
   }
 }
+// Four consecutive values (one column of a 16x16 accumulator tile, i.e. one
+// row segment of the transposed copy) stored with one 8- or 16-byte store.
+template <typename T, int SPLIT>
+__device__ __forceinline__ void store_op4(void* hi, void* lo, int64_t i,
+                                          const float (&v)[4]) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(hi) + i) =
+        f32x4_t{v[0], v[1], v[2], v[3]};
+  } else {
+    bf16_t h[4], l[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (SPLIT == 2) split_bf16(v[k], h[k], l[k]);
+      else h[k] = f32_to_bf16(v[k]);
+    }
+    *reinterpret_cast<u32x2_t*>(reinterpret_cast<bf16_t*>(hi) + i) =
+        u32x2_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+    if constexpr (SPLIT == 2)
+      *reinterpret_cast<u32x2_t*>(reinterpret_cast<bf16_t*>(lo) + i) =
+          u32x2_t{(uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16)};
+  }
+}
 
 __device__ __forceinline__ void apply_one(void* W, int w_bf16, int64_t i,
                                           float eta, float u) {
@@ -165,16 +129,88 @@ __device__ __forceinline__ void apply_one(void* W, int w_bf16, int64_t i,
   }
 }
 
+
+template <typename T>
+__device__ __forceinline__ void* offset_ptr(void* p, int64_t off) {
+  return p ? static_cast<void*>(reinterpret_cast<T*>(p) + off) : nullptr;
+}
+
+// Four consecutive operand values (8 or 16 bytes, aligned) as floats.
+template <typename T, int SPLIT>
+__device__ __forceinline__ void load_op4(const void* hi, const void* lo, int64_t i,
+                                         float (&v)[4]) {
+  if constexpr (sizeof(T) == 4) {
+    f32x4_t x = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(hi) + i);
+    v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+  } else {
+    u32x2_t h = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const bf16_t*>(hi) + i);
+    v[0] = __uint_as_float(h[0] << 16); v[1] = __uint_as_float(h[0] & 0xFFFF0000u);
+    v[2] = __uint_as_float(h[1] << 16); v[3] = __uint_as_float(h[1] & 0xFFFF0000u);
+    if constexpr (SPLIT == 2) {
+      u32x2_t l = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const bf16_t*>(lo) + i);
+      v[0] += __uint_as_float(l[0] << 16); v[1] += __uint_as_float(l[0] & 0xFFFF0000u);
+      v[2] += __uint_as_float(l[1] << 16); v[3] += __uint_as_float(l[1] & 0xFFFF0000u);
+    }
+  }
+}
+
+// Store a 128x128 output tile (values in accumulator layout) row-major at
+// dst (row length ld) through LDS: each wave writes its 64x64 sub-tile into
+// an LDS image of the tile, then every thread stores 16-byte row segments.
+// For split-bf16 the hi and lo images sit side by side.  The LDS row pitch
+// is padded by 16 bytes against bank conflicts.
+template <typename T, int SPLIT>
+__device__ __forceinline__ void stage_store_tile(const float (&v)[4][4][4], char* smem,
+                                                 void* dst_hi, void* dst_lo, int64_t ld,
+                                                 int m0, int n0, int wm, int wn, int lane,
+                                                 int tid) {
+  constexpr int ES = sizeof(T);
+  constexpr int PITCH = BM * ES + 16;
+  constexpr int IMG = BM * PITCH;
+  const int r0 = wm * 64 + 4 * (lane >> 4), c0 = wn * 64 + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        char* p = smem + (r0 + i * 16 + r) * PITCH + (c0 + j * 16) * ES;
+        if constexpr (ES == 4) {
+          *reinterpret_cast<float*>(p) = v[i][j][r];
+        } else if constexpr (SPLIT == 2) {
+          bf16_t h, l;
+          split_bf16(v[i][j][r], h, l);
+          *reinterpret_cast<bf16_t*>(p) = h;
+          *reinterpret_cast<bf16_t*>(p + IMG) = l;
+        } else {
+          *reinterpret_cast<bf16_t*>(p) = f32_to_bf16(v[i][j][r]);
+        }
+      }
+  __syncthreads();
+  constexpr int CH = BM * ES / 16;          // 16-byte chunks per row
+#pragma unroll
+  for (int p = 0; p < BM * CH / 256; ++p) {
+    const int c = tid + 256 * p;
+    const int row = c / CH, ch = c % CH;
+    const char* src = smem + row * PITCH + ch * 16;
+    const int64_t o = (int64_t)(m0 + row) * ld * ES + (int64_t)n0 * ES + ch * 16;
+    *reinterpret_cast<u32x4_t*>(static_cast<char*>(dst_hi) + o) = *reinterpret_cast<const u32x4_t*>(src);
+    if constexpr (SPLIT == 2)
+      *reinterpret_cast<u32x4_t*>(static_cast<char*>(dst_lo) + o) =
+          *reinterpret_cast<const u32x4_t*>(src + IMG);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
-template <typename T, int SPLIT>
+template <typename T, int SPLIT, int EPI, int NSTG>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  // smem layout: [stage 2][operand 2][split SPLIT][TILEB]
-  auto tile = [&](int st, int op, int sp) -> char* {
-    return smem + ((st * 2 + op) * SPLIT + sp) * TILEB;
-  };
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  constexpr int STAGEB = 2 * SPLIT * TILEB;
+  constexpr int P = Elem<T>::per16;           // elements per 16 bytes
+  constexpr int BK = ROWB / sizeof(T);        // k per slab
+  constexpr int LOADS = 2 * SPLIT * 4;        // vector loads per thread per slab
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -195,19 +231,61 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
   const int t = lb - mi * g.blocks_per_mat;
   const int tm = t / g.tiles_n, tn = t - tm * g.tiles_n;
   const int m0 = tm * BM, n0 = tn * BM;
-  const int a_fam = g.ops & 1, a_kc = (g.ops >> 1) & 1;
-  const int b_fam = (g.ops >> 2) & 1, b_kc = (g.ops >> 3) & 1;
-  const int64_t a_off = fam_off(g, a_fam, mi), b_off = fam_off(g, b_fam, mi);
+  const int a_fam = g.ops & 3, b_fam = (g.ops >> 2) & 3;
   const int64_t lda = fam_ld(g, a_fam), ldb = fam_ld(g, b_fam);
-  const T* a_hi = reinterpret_cast<const T*>(a_fam == FAM_X ? A.x_hi : A.r_hi) + a_off;
-  const T* b_hi = reinterpret_cast<const T*>(b_fam == FAM_X ? A.x_hi : A.r_hi) + b_off;
-  const T* a_lo = SPLIT == 2
-      ? reinterpret_cast<const T*>(a_fam == FAM_X ? A.x_lo : A.r_lo) + a_off : nullptr;
-  const T* b_lo = SPLIT == 2
-      ? reinterpret_cast<const T*>(b_fam == FAM_X ? A.x_lo : A.r_lo) + b_off : nullptr;
+  const void* a_hi = a_fam == FAM_X ? A.x_hi : (a_fam == FAM_XT ? A.xt_hi : A.r_hi);
+  const void* b_hi = b_fam == FAM_X ? A.x_hi : (b_fam == FAM_XT ? A.xt_hi : A.r_hi);
+  const void* a_lo = a_fam == FAM_X ? A.x_lo : (a_fam == FAM_XT ? A.xt_lo : A.r_lo);
+  const void* b_lo = b_fam == FAM_X ? A.x_lo : (b_fam == FAM_XT ? A.xt_lo : A.r_lo);
+  const T* a_src[SPLIT];
+  const T* b_src[SPLIT];
+  a_src[0] = reinterpret_cast<const T*>(a_hi) + fam_off(g, a_fam, mi);
+  b_src[0] = reinterpret_cast<const T*>(b_hi) + fam_off(g, b_fam, mi);
+  if constexpr (SPLIT == 2) {
+    a_src[SPLIT - 1] = reinterpret_cast<const T*>(a_lo) + fam_off(g, a_fam, mi);
+    b_src[SPLIT - 1] = reinterpret_cast<const T*>(b_lo) + fam_off(g, b_fam, mi);
+  }
 
-  constexpr int BK = ROWB / sizeof(T);
+  // Per-lane source offsets of the 4 loads per operand and slab: wave w's
+  // load q fills LDS rows (4w+q)*8 .. +7; lane l writes row (4w+q)*8 + l/8
+  // at chunk position l%8, so it fetches global chunk (l%8) ^ swz(row).
+  int64_t aoff[4], boff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    int row = (wave * 4 + q) * 8 + (lane >> 3);
+    int ch = (lane & 7) ^ swz(row);
+    aoff[q] = (int64_t)(m0 + row) * lda + ch * P;
+    boff[q] = (int64_t)(n0 + row) * ldb + ch * P;
+  }
+  // Per-lane LDS offsets of the fragment reads: row within the tile and
+  // 16-byte chunk (kk*4 + lane/16) of the 128-byte slab row.
+  int fa_off[2][4], fb_off[2][4];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa_off[kk][i] = lds_off(wm * 64 + i * 16 + (lane & 15), kk * 4 + (lane >> 4));
+      fb_off[kk][i] = lds_off(wn * 64 + i * 16 + (lane & 15), kk * 4 + (lane >> 4));
+    }
+
   const int nslab = g.gk / BK;
+
+  auto issue = [&](int s) {
+    char* st = smem + (s % NSTG) * STAGEB;
+    const int64_t k0 = (int64_t)s * BK;
+#pragma unroll
+    for (int sp = 0; sp < SPLIT; ++sp) {
+      char* ta = st + (0 * SPLIT + sp) * TILEB + wave * 4096;
+      char* tb = st + (1 * SPLIT + sp) * TILEB + wave * 4096;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_global_load_lds((const void*)(a_src[sp] + aoff[q] + k0),
+                                         (lds_void*)(ta + q * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(b_src[sp] + boff[q] + k0),
+                                         (lds_void*)(tb + q * 1024), 16, 0, 0);
+      }
+    }
+  };
 
   f32x4_t acc[4][4];
 #pragma unroll
@@ -215,224 +293,259 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  SlabRegs<T> ra[SPLIT], rb[SPLIT];
-  auto fetch = [&](int s) {
-    int k0 = s * BK;
-    fetch_slab<T>(ra[0], a_hi, lda, a_kc, m0, k0, tid);
-    fetch_slab<T>(rb[0], b_hi, ldb, b_kc, n0, k0, tid);
-    if constexpr (SPLIT == 2) {
-      fetch_slab<T>(ra[1], a_lo, lda, a_kc, m0, k0, tid);
-      fetch_slab<T>(rb[1], b_lo, ldb, b_kc, n0, k0, tid);
-    }
-  };
-  auto stash = [&](int st) {
 #pragma unroll
-    for (int sp = 0; sp < SPLIT; ++sp) {
-      store_slab<T>(ra[sp], tile(st, 0, sp), a_kc, tid);
-      store_slab<T>(rb[sp], tile(st, 1, sp), b_kc, tid);
-    }
-  };
-
-  if (nslab > 0) {
-    fetch(0);
-    stash(0);
-  }
-  __syncthreads();
+  for (int s = 0; s < NSTG - 1; ++s)
+    if (s < nslab) issue(s);
 
   for (int s = 0; s < nslab; ++s) {
-    const int st = s & 1;
-    if (s + 1 < nslab) fetch(s + 1);
+    // slab s has landed for this wave once at most the later slabs' loads
+    // are outstanding; the barrier extends that to every wave and also
+    // frees stage (s-1) % NSTG for the next fetch.
+    if constexpr (NSTG >= 3) {
+      if (s + NSTG - 2 < nslab) wait_vmcnt<(NSTG - 2) * LOADS>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (s + NSTG - 1 < nslab) issue(s + NSTG - 1);
+
+    const char* st = smem + (s % NSTG) * STAGEB;
+    u32x4_t fa[2][SPLIT][4], fb[2][SPLIT][4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int ch = kk * 4 + (lane >> 4);
-      u32x4_t fa[SPLIT][4], fb[SPLIT][4];
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int sp = 0; sp < SPLIT; ++sp) {
+      for (int sp = 0; sp < SPLIT; ++sp)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          int ra_ = wm * 64 + i * 16 + (lane & 15);
-          int rb_ = wn * 64 + i * 16 + (lane & 15);
-          fa[sp][i] = *reinterpret_cast<const u32x4_t*>(tile(st, 0, sp) + lds_off(ra_, ch));
-          fb[sp][i] = *reinterpret_cast<const u32x4_t*>(tile(st, 1, sp) + lds_off(rb_, ch));
+          fa[kk][sp][i] = *reinterpret_cast<const u32x4_t*>(st + (0 * SPLIT + sp) * TILEB + fa_off[kk][i]);
+          fb[kk][sp][i] = *reinterpret_cast<const u32x4_t*>(st + (1 * SPLIT + sp) * TILEB + fb_off[kk][i]);
         }
-      }
+    // keep every fragment read of the slab ahead of the MFMAs, so the waits
+    // before them count down outstanding reads instead of draining them
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if constexpr (sizeof(T) == 2) {
-            bf16x8_t ah = __builtin_bit_cast(bf16x8_t, fa[0][i]);
-            bf16x8_t bh = __builtin_bit_cast(bf16x8_t, fb[0][j]);
+            bf16x8_t ah = __builtin_bit_cast(bf16x8_t, fa[kk][0][i]);
+            bf16x8_t bh = __builtin_bit_cast(bf16x8_t, fb[kk][0][j]);
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[i][j], 0, 0, 0);
             if constexpr (SPLIT == 2) {
-              bf16x8_t al = __builtin_bit_cast(bf16x8_t, fa[1][i]);
-              bf16x8_t bl = __builtin_bit_cast(bf16x8_t, fb[1][j]);
+              bf16x8_t al = __builtin_bit_cast(bf16x8_t, fa[kk][1][i]);
+              bf16x8_t bl = __builtin_bit_cast(bf16x8_t, fb[kk][1][j]);
               acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[i][j], 0, 0, 0);
               acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[i][j], 0, 0, 0);
             }
           } else {
-            f32x4_t av = __builtin_bit_cast(f32x4_t, fa[0][i]);
-            f32x4_t bv = __builtin_bit_cast(f32x4_t, fb[0][j]);
+            f32x4_t av = __builtin_bit_cast(f32x4_t, fa[kk][0][i]);
+            f32x4_t bv = __builtin_bit_cast(f32x4_t, fb[kk][0][j]);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc[i][j], 0, 0, 0);
           }
         }
-    }
-    if (s + 1 < nslab) stash(st ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue.  acc[i][j][r] holds C(row, col) with
   //   row = m0 + wm*64 + i*16 + 4*(lane/16) + r,  col = n0 + wn*64 + j*16 + lane%16
+  // i.e. the 4 registers of a tile are 4 consecutive rows of one column.
   const int idx = g.idx0 + mi * g.idx_stride;
   const float cs = A.scal ? A.scal[idx] : 1.0f;
   const int rows = g.rows, cols = g.cols;
   const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
   const int64_t roff = g.r0 + (int64_t)mi * g.r_stride;
   const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
+  const int64_t Mp = round_up(rows, kPad);
   const int64_t Np = round_up(cols, kPad);
   const int64_t Rp = round_up(rows < cols ? rows : cols, kPad);
   const int rbase = m0 + wm * 64 + 4 * (lane >> 4);
   const int cbase = n0 + wn * 64 + (lane & 15);
+  // every wave is done reading the operand stages: LDS is free for staging
+  __syncthreads();
 
-  if (A.epi == E_RAW) {
+  float v[4][4][4];
+  if constexpr (EPI == E_RAW) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int row = rbase + i * 16 + r, col = cbase + j * 16;
-          A.o_raw[roff + (int64_t)row * Rp + col] = acc[i][j][r];
-        }
-    return;
-  }
-  if (A.epi == E_OP) {
-    float m = A.mul * (A.scal_pow == 2 ? cs * cs : 1.0f);
+        for (int r = 0; r < 4; ++r) v[i][j][r] = acc[i][j][r];
+    stage_store_tile<float, 1>(v, smem, A.o_raw + roff, nullptr, Rp, m0, n0, wm, wn, lane, tid);
+  } else if constexpr (EPI == E_OP) {
+    const float m = A.mul * (A.scal_pow == 2 ? cs * cs : 1.0f);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int row = rbase + i * 16 + r, col = cbase + j * 16;
-          store_op<T, SPLIT>(A.o_hi, A.o_lo, roff + (int64_t)row * Rp + col,
-                             m * acc[i][j][r]);
-        }
-    return;
-  }
-  if (A.epi == E_SQUARE) {
+        for (int r = 0; r < 4; ++r) v[i][j][r] = m * acc[i][j][r];
+    stage_store_tile<T, SPLIT>(v, smem, offset_ptr<T>(A.o_hi, roff), offset_ptr<T>(A.o_lo, roff),
+                               Rp, m0, n0, wm, wn, lane, tid);
+  } else if constexpr (EPI == E_SQUARE) {
+    // b A + c A^2; A is symmetric, so A(row..row+3, col) = A(col, row..row+3)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        load_op4<T, SPLIT>(A.sq_hi, A.sq_lo, roff + (int64_t)(cbase + j * 16) * Rp + rbase + i * 16,
+                           v[i][j]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int row = rbase + i * 16 + r, col = cbase + j * 16;
-          int64_t o = roff + (int64_t)row * Rp + col;
-          float a = load_op<T, SPLIT>(A.sq_hi, A.sq_lo, o);
-          store_op<T, SPLIT>(A.o_hi, A.o_lo, o, A.cb * a + A.cc * acc[i][j][r]);
-        }
-    return;
-  }
-
-  // E_UPDATE:  v = (ca * c^p) * Xsrc + (c^p) * acc
-  const float gam = A.scal_pow == 1 ? cs : 1.0f;
-  const float alp = A.ca * gam;
-  auto xsrc = [&](int row, int col) -> float {
-    if (A.xsrc == XS_USER)
-      return (row < rows && col < cols) ? A.xs_user[eoff + (int64_t)row * cols + col] : 0.0f;
-    return load_op<T, SPLIT>(A.xs_hi, A.xs_lo, xoff + (int64_t)row * Np + col);
-  };
-
-  if (A.out == O_X) {
+        for (int r = 0; r < 4; ++r) v[i][j][r] = A.cb * v[i][j][r] + A.cc * acc[i][j][r];
+    stage_store_tile<T, SPLIT>(v, smem, offset_ptr<T>(A.o_hi, roff), offset_ptr<T>(A.o_lo, roff),
+                               Rp, m0, n0, wm, wn, lane, tid);
+  } else {
+    // E_UPDATE:  v = (ca * c^p) * Xsrc + (c^p) * acc.  All source loads are
+    // issued before any store.
+    const float gam = A.scal_pow == 1 ? cs : 1.0f;
+    const float alp = A.ca * gam;
+    if (A.xsrc == XS_USER) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int row = rbase + i * 16 + r, col = cbase + j * 16;
-          float v = alp * xsrc(row, col) + gam * acc[i][j][r];
-          store_op<T, SPLIT>(A.o_hi, A.o_lo, xoff + (int64_t)row * Np + col, v);
-        }
-    return;
-  }
-  if (A.out == O_U || A.out == O_APPLY) {
-    if (A.out == O_APPLY && A.status && A.status[0] != 0) return;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int row = rbase + i * 16 + r, col = cbase + j * 16;
-          if (row < rows && col < cols) {
-            float v = alp * xsrc(row, col) + gam * acc[i][j][r];
-            int64_t e = eoff + (int64_t)row * cols + col;
-            if (A.out == O_U) A.U[e] = v;
-            else apply_one(A.W, A.w_bf16, e, A.eta, v);
+          for (int r = 0; r < 4; ++r) {
+            const int row = rbase + i * 16 + r, col = cbase + j * 16;
+            v[i][j][r] = (row < rows && col < cols)
+                             ? A.xs_user[eoff + (int64_t)row * cols + col] : 0.0f;
           }
-        }
-    return;
+    } else {
+      // X(row..row+3, col) = X^T(col, row..row+3): one 8- or 16-byte load
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          load_op4<T, SPLIT>(A.xs_hi, A.xs_lo, xoff + (int64_t)(cbase + j * 16) * Mp + rbase + i * 16,
+                             v[i][j]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[i][j][r] = alp * v[i][j][r] + gam * acc[i][j][r];
+
+    if (A.out == O_X) {
+      // X^T rows directly (4 consecutive entries per tile), X rows via LDS
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          store_op4<T, SPLIT>(A.ot_hi, A.ot_lo, xoff + (int64_t)(cbase + j * 16) * Mp + rbase + i * 16,
+                              v[i][j]);
+      stage_store_tile<T, SPLIT>(v, smem, offset_ptr<T>(A.o_hi, xoff), offset_ptr<T>(A.o_lo, xoff),
+                                 Np, m0, n0, wm, wn, lane, tid);
+    } else if (A.out == O_U || A.out == O_APPLY) {
+      if (A.out == O_APPLY && A.status && A.status[0] != 0) return;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = rbase + i * 16 + r, col = cbase + j * 16;
+            if (row < rows && col < cols) {
+              const int64_t e = eoff + (int64_t)row * cols + col;
+              if (A.out == O_U) A.U[e] = v[i][j][r];
+              else apply_one(A.W, A.w_bf16, e, A.eta, v[i][j][r]);
+            }
+          }
+    } else {
+      // O_BITS: entrywise sign packed into 32-bit words (cols % 32 == 0).
+      // For a 16x16 MFMA tile and accumulator register r, a wave ballot
+      // gives 4 rows x 16 columns; two neighbouring tiles give 32 columns.
+      const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jp = 0; jp < 2; ++jp)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            uint64_t m0b = __ballot(v[i][2 * jp][r] < 0.0f);
+            uint64_t m1b = __ballot(v[i][2 * jp + 1][r] < 0.0f);
+            if (lane < 4) {
+              uint32_t w = (uint32_t)((m0b >> (16 * lane)) & 0xFFFFu) |
+                           ((uint32_t)((m1b >> (16 * lane)) & 0xFFFFu) << 16);
+              int wrow = m0 + wm * 64 + i * 16 + 4 * lane + r;
+              int wcol = n0 + wn * 64 + jp * 32;
+              if (wrow < rows && wcol < cols)
+                A.bits[woff + ((int64_t)wrow * cols + wcol) / 32] = w;
+            }
+          }
+    }
   }
-  // O_BITS: entrywise sign packed into 32-bit words (cols % 32 == 0).
-  // For a 16x16 MFMA tile and accumulator register r, a wave ballot gives
-  // 4 rows x 16 columns; two neighbouring tiles give 32 columns of a row.
-  const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jp = 0; jp < 2; ++jp)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int row = rbase + i * 16 + r;
-        int c0 = cbase + (2 * jp) * 16, c1 = c0 + 16;
-        float v0 = alp * xsrc(row, c0) + gam * acc[i][2 * jp][r];
-        float v1 = alp * xsrc(row, c1) + gam * acc[i][2 * jp + 1][r];
-        uint64_t m0b = __ballot(v0 < 0.0f);
-        uint64_t m1b = __ballot(v1 < 0.0f);
-        if (lane < 4) {
-          uint32_t w = (uint32_t)((m0b >> (16 * lane)) & 0xFFFFu) |
-                       ((uint32_t)((m1b >> (16 * lane)) & 0xFFFFu) << 16);
-          int wrow = m0 + wm * 64 + i * 16 + 4 * lane + r;
-          int wcol = n0 + wn * 64 + jp * 32;
-          if (wrow < rows && wcol < cols)
-            A.bits[woff + ((int64_t)wrow * cols + wcol) / 32] = w;
-        }
-      }
 }
 
 // ---------------------------------------------------------------------------
 // Host launcher
 // ---------------------------------------------------------------------------
-hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s) {
-  if (args.G.total_blocks <= 0) return hipSuccess;
+// Pipeline depth per variant: the split-bf16 tiles are twice as large, so
+// they keep two stages within the 160 KB of LDS.
+template <typename T, int SPLIT>
+constexpr int stages() { return SPLIT == 2 ? 2 : SM_GEMM_STAGES; }
+// LDS of a block: the pipeline stages, or the epilogue's staging image of
+// the output tile if that is larger.
+// (the raw float32 Gram is staged as float32 whatever the operand type).
+template <typename T, int SPLIT>
+constexpr size_t lds_bytes() {
+  size_t pipe = (size_t)stages<T, SPLIT>() * 2 * SPLIT * TILEB;
+  size_t img = (size_t)SPLIT * BM * (BM * sizeof(T) + 16);
+  size_t raw = (size_t)BM * (BM * sizeof(float) + 16);
+  size_t m = pipe > img ? pipe : img;
+  return m > raw ? m : raw;
+}
+
+template <typename T, int SPLIT>
+static hipError_t launch_epi(const GemmArgs& args, hipStream_t s) {
   dim3 grid(args.G.total_blocks), block(256);
-  if (precision == P_F32) {
-    size_t lds = 2 * 2 * 1 * TILEB;
-    hipLaunchKernelGGL((k_gemm<float, 1>), grid, block, lds, s, args);
-  } else if (precision == P_BF16X3) {
-    size_t lds = 2 * 2 * 2 * TILEB;
-    hipLaunchKernelGGL((k_gemm<bf16_t, 2>), grid, block, lds, s, args);
-  } else {
-    size_t lds = 2 * 2 * 1 * TILEB;
-    hipLaunchKernelGGL((k_gemm<bf16_t, 1>), grid, block, lds, s, args);
+  constexpr int NS = stages<T, SPLIT>();
+  size_t lds = lds_bytes<T, SPLIT>();
+  switch (args.epi) {
+    case E_RAW: hipLaunchKernelGGL((k_gemm<T, SPLIT, E_RAW, NS>), grid, block, lds, s, args); break;
+    case E_OP: hipLaunchKernelGGL((k_gemm<T, SPLIT, E_OP, NS>), grid, block, lds, s, args); break;
+    case E_SQUARE: hipLaunchKernelGGL((k_gemm<T, SPLIT, E_SQUARE, NS>), grid, block, lds, s, args); break;
+    default: hipLaunchKernelGGL((k_gemm<T, SPLIT, E_UPDATE, NS>), grid, block, lds, s, args); break;
   }
   return hipGetLastError();
 }
 
+hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s) {
+  if (args.G.total_blocks <= 0) return hipSuccess;
+  if (precision == P_F32) return launch_epi<float, 1>(args, s);
+  if (precision == P_BF16X3) return launch_epi<bf16_t, 2>(args, s);
+  return launch_epi<bf16_t, 1>(args, s);
+}
+
+template <typename T, int SPLIT, int EPI>
+static hipError_t set_lds() {
+  return hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_gemm<T, SPLIT, EPI, stages<T, SPLIT>()>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes<T, SPLIT>());
+}
+template <typename T, int SPLIT>
+static hipError_t set_lds_all() {
+  hipError_t e;
+  if ((e = set_lds<T, SPLIT, E_RAW>()) != hipSuccess) return e;
+  if ((e = set_lds<T, SPLIT, E_OP>()) != hipSuccess) return e;
+  if ((e = set_lds<T, SPLIT, E_SQUARE>()) != hipSuccess) return e;
+  return set_lds<T, SPLIT, E_UPDATE>();
+}
+
 hipError_t gemm_set_attributes() {
-  hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_gemm<bf16_t, 2>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, 2 * 2 * 2 * TILEB);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<bf16_t, 1>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 2 * 2 * TILEB);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<float, 1>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, 2 * 2 * TILEB);
+  hipError_t e;
+  if ((e = set_lds_all<bf16_t, 1>()) != hipSuccess) return e;
+  if ((e = set_lds_all<bf16_t, 2>()) != hipSuccess) return e;
+  return set_lds_all<float, 1>();
 }
 
 }  // namespace sm

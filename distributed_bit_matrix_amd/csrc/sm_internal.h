@@ -109,6 +109,7 @@ struct Plan {
   int64_t x_total = 0, r_total = 0, v_total = 0, c_total = 0;
   // workspace byte offsets (0 = absent)
   size_t off_x[2][2] = {{0, 0}, {0, 0}};  // [pingpong][hi/lo] (or f32 in [p][0])
+  size_t off_xt[2][2] = {{0, 0}, {0, 0}}; // transposed copies, same shape
   size_t off_b[2] = {0, 0};   // Newton-Schulz right/left factor B (hi/lo)
   size_t off_a[2] = {0, 0};   // quintic: A (hi/lo)
   size_t off_araw = 0;        // spectral: raw float32 Gram
