@@ -307,7 +307,7 @@ sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
     g.gm = g.gn = (int32_t)q.Rp;
     g.gk = (int32_t)(q.tall ? q.Mp : q.Np);
     g.tiles_n = (int32_t)(q.Rp / 128);
-    g.blocks_per_mat = g.tiles_n * g.tiles_n;
+    g.blocks_per_mat = g.tiles_n * (g.tiles_n + 1) / 2;  // upper triangle
     g.ops = q.tall ? gemm_ops(FAM_XT, FAM_XT) : gemm_ops(FAM_X, FAM_X);
     return true;
   };
@@ -380,7 +380,7 @@ hipError_t run_square(const Plan& P, const std::vector<MatPlan>& mp,
     const MatPlan& q = mp[g.idx0];
     g.gm = g.gn = g.gk = (int32_t)q.Rp;
     g.tiles_n = (int32_t)(q.Rp / 128);
-    g.blocks_per_mat = g.tiles_n * g.tiles_n;
+    g.blocks_per_mat = g.tiles_n * (g.tiles_n + 1) / 2;  // upper triangle
     g.ops = gemm_ops(FAM_R, FAM_R);
     return true;
   }, [&](const Groups& G) {
@@ -409,7 +409,7 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
         g.gm = g.gn = (int32_t)q.Rp;
         g.gk = (int32_t)(q.tall ? q.Mp : q.Np);
         g.tiles_n = (int32_t)(q.Rp / 128);
-        g.blocks_per_mat = g.tiles_n * g.tiles_n;
+        g.blocks_per_mat = g.tiles_n * (g.tiles_n + 1) / 2;  // upper triangle
         g.ops = q.tall ? gemm_ops(FAM_XT, FAM_XT) : gemm_ops(FAM_X, FAM_X);
         return true;
       }, [&](const Groups& G) {

@@ -201,6 +201,19 @@ __device__ __forceinline__ void stage_store_tile(const float (&v)[4][4][4], char
   }
 }
 
+
+// Mirror tile of a symmetric output: C(row..row+3, col) goes to row `col`,
+// columns row..row+3 (one 8- or 16-byte store per accumulator tile).
+template <typename T, int SPLIT>
+__device__ __forceinline__ void store_mirror(const float (&v)[4][4][4], void* hi, void* lo,
+                                             int64_t off, int64_t ld, int rbase, int cbase) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      store_op4<T, SPLIT>(hi, lo, off + (int64_t)(cbase + j * 16) * ld + rbase + i * 16, v[i][j]);
+}
+
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
@@ -229,7 +242,19 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
   const int lb = b - g.block0;
   const int mi = lb / g.blocks_per_mat;
   const int t = lb - mi * g.blocks_per_mat;
-  const int tm = t / g.tiles_n, tn = t - tm * g.tiles_n;
+  // Symmetric outputs (Gram, raw Gram, quintic square) are computed on the
+  // upper-triangular tiles only; the epilogue also writes the mirror tile.
+  constexpr bool SYM = EPI != E_UPDATE;
+  int tm, tn;
+  if constexpr (SYM) {
+    tm = 0;
+    int rem = t;
+    while (rem >= g.tiles_n - tm) { rem -= g.tiles_n - tm; ++tm; }
+    tn = tm + rem;
+  } else {
+    tm = t / g.tiles_n;
+    tn = t - tm * g.tiles_n;
+  }
   const int m0 = tm * BM, n0 = tn * BM;
   const int a_fam = g.ops & 3, b_fam = (g.ops >> 2) & 3;
   const int64_t lda = fam_ld(g, a_fam), ldb = fam_ld(g, b_fam);
@@ -288,10 +313,37 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
   };
 
   f32x4_t acc[4][4];
+  if constexpr (EPI == E_UPDATE) {
+    // a X + B X: start the accumulator at a * X so that its loads overlap
+    // the k-loop.  X comes from the caller's float32 array (first step) or
+    // from X^T (4 consecutive rows of a column are 4 consecutive entries).
+    const int rb = m0 + wm * 64 + 4 * (lane >> 4), cb = n0 + wn * 64 + (lane & 15);
+    const int64_t xo = g.x0 + (int64_t)mi * g.x_stride;
+    const int64_t eo = g.elem0 + (int64_t)mi * g.elem_stride;
+    const int64_t mp = round_up(g.rows, kPad);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4; ++j) {
+        float x[4];
+        if (A.xsrc == XS_USER) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = rb + i * 16 + r, col = cb + j * 16;
+            x[r] = (row < g.rows && col < g.cols)
+                       ? A.xs_user[eo + (int64_t)row * g.cols + col] : 0.0f;
+          }
+        } else {
+          load_op4<T, SPLIT>(A.xs_hi, A.xs_lo, xo + (int64_t)(cb + j * 16) * mp + rb + i * 16, x);
+        }
+        acc[i][j] = f32x4_t{A.ca * x[0], A.ca * x[1], A.ca * x[2], A.ca * x[3]};
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
 #pragma unroll
   for (int s = 0; s < NSTG - 1; ++s)
@@ -377,6 +429,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[i][j][r] = acc[i][j][r];
     stage_store_tile<float, 1>(v, smem, A.o_raw + roff, nullptr, Rp, m0, n0, wm, wn, lane, tid);
+    if (tm != tn) store_mirror<float, 1>(v, A.o_raw, nullptr, roff, Rp, rbase, cbase);
   } else if constexpr (EPI == E_OP) {
     const float m = A.mul * (A.scal_pow == 2 ? cs * cs : 1.0f);
 #pragma unroll
@@ -387,6 +440,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
         for (int r = 0; r < 4; ++r) v[i][j][r] = m * acc[i][j][r];
     stage_store_tile<T, SPLIT>(v, smem, offset_ptr<T>(A.o_hi, roff), offset_ptr<T>(A.o_lo, roff),
                                Rp, m0, n0, wm, wn, lane, tid);
+    if (tm != tn) store_mirror<T, SPLIT>(v, A.o_hi, A.o_lo, roff, Rp, rbase, cbase);
   } else if constexpr (EPI == E_SQUARE) {
     // b A + c A^2; A is symmetric, so A(row..row+3, col) = A(col, row..row+3)
 #pragma unroll
@@ -403,37 +457,17 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
         for (int r = 0; r < 4; ++r) v[i][j][r] = A.cb * v[i][j][r] + A.cc * acc[i][j][r];
     stage_store_tile<T, SPLIT>(v, smem, offset_ptr<T>(A.o_hi, roff), offset_ptr<T>(A.o_lo, roff),
                                Rp, m0, n0, wm, wn, lane, tid);
+    if (tm != tn) store_mirror<T, SPLIT>(v, A.o_hi, A.o_lo, roff, Rp, rbase, cbase);
   } else {
-    // E_UPDATE:  v = (ca * c^p) * Xsrc + (c^p) * acc.  All source loads are
-    // issued before any store.
+    // E_UPDATE:  acc = a X + B X (first step: X = the unscaled source), and
+    // the iterate is c^p * acc with c = 1/(s+eps) on the first step.
     const float gam = A.scal_pow == 1 ? cs : 1.0f;
-    const float alp = A.ca * gam;
-    if (A.xsrc == XS_USER) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = rbase + i * 16 + r, col = cbase + j * 16;
-            v[i][j][r] = (row < rows && col < cols)
-                             ? A.xs_user[eoff + (int64_t)row * cols + col] : 0.0f;
-          }
-    } else {
-      // X(row..row+3, col) = X^T(col, row..row+3): one 8- or 16-byte load
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          load_op4<T, SPLIT>(A.xs_hi, A.xs_lo, xoff + (int64_t)(cbase + j * 16) * Mp + rbase + i * 16,
-                             v[i][j]);
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[i][j][r] = alp * v[i][j][r] + gam * acc[i][j][r];
+        for (int r = 0; r < 4; ++r) v[i][j][r] = gam * acc[i][j][r];
 
     if (A.out == O_X) {
       // X^T rows directly (4 consecutive entries per tile), X rows via LDS
