@@ -439,10 +439,11 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
       HIP_TRY(for_launches(groups, [&](Group& g) {
         const MatPlan& q = mp[g.idx0];
         if (last && io.final_out == O_BITS && fusable[g.idx0] != (pass == 0)) return false;
+        const int bmt = gemm_update_tile_rows(prec);
         g.gm = (int32_t)q.Mp; g.gn = (int32_t)q.Np;
         g.gk = (int32_t)q.Rp;
         g.tiles_n = (int32_t)(q.Np / 128);
-        g.blocks_per_mat = (int32_t)((q.Mp / 128) * g.tiles_n);
+        g.blocks_per_mat = (int32_t)(((q.Mp + bmt - 1) / bmt) * g.tiles_n);
         g.ops = q.tall ? gemm_ops(FAM_X, FAM_R) : gemm_ops(FAM_R, FAM_XT);
         return true;
       }, [&](const Groups& G) {

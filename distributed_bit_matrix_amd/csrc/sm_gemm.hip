@@ -154,19 +154,20 @@ __device__ __forceinline__ void load_op4(const void* hi, const void* lo, int64_t
   }
 }
 
-// Store a 128x128 output tile (values in accumulator layout) row-major at
+// Store a BMT x 128 output tile (values in accumulator layout) row-major at
 // dst (row length ld) through LDS: each wave writes its 64x64 sub-tile into
-// an LDS image of the tile, then every thread stores 16-byte row segments.
-// For split-bf16 the hi and lo images sit side by side.  The LDS row pitch
-// is padded by 16 bytes against bank conflicts.
-template <typename T, int SPLIT>
+// an LDS image of the tile, then every thread stores 16-byte row segments
+// (rows at or past row_lim are skipped).  For split-bf16 the hi and lo
+// images sit side by side.  The LDS row pitch is padded by 16 bytes
+// against bank conflicts.
+template <typename T, int SPLIT, int BMT, int NT>
 __device__ __forceinline__ void stage_store_tile(const float (&v)[4][4][4], char* smem,
                                                  void* dst_hi, void* dst_lo, int64_t ld,
-                                                 int m0, int n0, int wm, int wn, int lane,
-                                                 int tid) {
+                                                 int m0, int n0, int row_lim, int wm, int wn,
+                                                 int lane, int tid) {
   constexpr int ES = sizeof(T);
   constexpr int PITCH = BM * ES + 16;
-  constexpr int IMG = BM * PITCH;
+  constexpr int IMG = BMT * PITCH;
   const int r0 = wm * 64 + 4 * (lane >> 4), c0 = wn * 64 + (lane & 15);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -189,9 +190,10 @@ __device__ __forceinline__ void stage_store_tile(const float (&v)[4][4][4], char
   __syncthreads();
   constexpr int CH = BM * ES / 16;          // 16-byte chunks per row
 #pragma unroll
-  for (int p = 0; p < BM * CH / 256; ++p) {
-    const int c = tid + 256 * p;
+  for (int p = 0; p < BMT * CH / NT; ++p) {
+    const int c = tid + NT * p;
     const int row = c / CH, ch = c % CH;
+    if (m0 + row >= row_lim) continue;
     const char* src = smem + row * PITCH + ch * 16;
     const int64_t o = (int64_t)(m0 + row) * ld * ES + (int64_t)n0 * ES + ch * 16;
     *reinterpret_cast<u32x4_t*>(static_cast<char*>(dst_hi) + o) = *reinterpret_cast<const u32x4_t*>(src);
@@ -200,7 +202,6 @@ __device__ __forceinline__ void stage_store_tile(const float (&v)[4][4][4], char
           *reinterpret_cast<const u32x4_t*>(src + IMG);
   }
 }
-
 
 // Mirror tile of a symmetric output: C(row..row+3, col) goes to row `col`,
 // columns row..row+3 (one 8- or 16-byte store per accumulator tile).
@@ -217,13 +218,19 @@ __device__ __forceinline__ void store_mirror(const float (&v)[4][4][4], void* hi
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
-template <typename T, int SPLIT, int EPI, int NSTG>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
+template <typename T, int SPLIT, int EPI, int NSTG, int WM>
+__global__ __launch_bounds__(128 * WM) void k_gemm(GemmArgs A) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  constexpr int STAGEB = 2 * SPLIT * TILEB;
+  // Block tile BMT x 128 with WM x 2 waves of 64x64.
+  constexpr int BMT = 64 * WM;
+  constexpr int NW = 2 * WM, NT = 64 * NW;
+  constexpr int QB = 16 / NW;                 // B-operand loads per wave
+  constexpr int ATILE = BMT * ROWB;           // A-operand bytes per split
+  constexpr int STAGEB = SPLIT * (ATILE + TILEB);
   constexpr int P = Elem<T>::per16;           // elements per 16 bytes
   constexpr int BK = ROWB / sizeof(T);        // k per slab
-  constexpr int LOADS = 2 * SPLIT * 4;        // vector loads per thread per slab
+  constexpr int LOADS = SPLIT * (4 + QB);     // vector loads per thread per slab
+  static_assert(EPI == E_UPDATE || WM == 2, "symmetric outputs use square tiles");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -255,7 +262,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
     tm = t / g.tiles_n;
     tn = t - tm * g.tiles_n;
   }
-  const int m0 = tm * BM, n0 = tn * BM;
+  const int m0 = tm * BMT, n0 = tn * BM;
   const int a_fam = g.ops & 3, b_fam = (g.ops >> 2) & 3;
   const int64_t lda = fam_ld(g, a_fam), ldb = fam_ld(g, b_fam);
   const void* a_hi = a_fam == FAM_X ? A.x_hi : (a_fam == FAM_XT ? A.xt_hi : A.r_hi);
@@ -271,15 +278,23 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
     b_src[SPLIT - 1] = reinterpret_cast<const T*>(b_lo) + fam_off(g, b_fam, mi);
   }
 
-  // Per-lane source offsets of the 4 loads per operand and slab: wave w's
-  // load q fills LDS rows (4w+q)*8 .. +7; lane l writes row (4w+q)*8 + l/8
-  // at chunk position l%8, so it fetches global chunk (l%8) ^ swz(row).
-  int64_t aoff[4], boff[4];
+  // Per-lane source offsets of the loads per operand and slab: the A load q
+  // of wave w fills LDS rows (4w+q)*8 .. +7 (B: (QB w+q)*8 ..); lane l writes
+  // row ..+l/8 at chunk position l%8, so it fetches global chunk
+  // (l%8) ^ swz(row).  A rows past the operand (a ragged last BMT-row tile)
+  // read the last row instead; their results are never stored.
+  int64_t aoff[4], boff[QB];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     int row = (wave * 4 + q) * 8 + (lane >> 3);
     int ch = (lane & 7) ^ swz(row);
-    aoff[q] = (int64_t)(m0 + row) * lda + ch * P;
+    int arow = m0 + row < g.gm ? m0 + row : g.gm - 1;
+    aoff[q] = (int64_t)arow * lda + ch * P;
+  }
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    int row = (wave * QB + q) * 8 + (lane >> 3);
+    int ch = (lane & 7) ^ swz(row);
     boff[q] = (int64_t)(n0 + row) * ldb + ch * P;
   }
   // Per-lane LDS offsets of the fragment reads: row within the tile and
@@ -295,20 +310,26 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
 
   const int nslab = g.gk / BK;
 
+  // LDS stage: [A split 0][A split 1..][B split 0][B split 1..]
+  auto a_tile = [&](int st, int sp) -> char* { return smem + st * STAGEB + sp * ATILE; };
+  auto b_tile = [&](int st, int sp) -> char* {
+    return smem + st * STAGEB + SPLIT * ATILE + sp * TILEB;
+  };
   auto issue = [&](int s) {
-    char* st = smem + (s % NSTG) * STAGEB;
+    const int st = s % NSTG;
     const int64_t k0 = (int64_t)s * BK;
 #pragma unroll
     for (int sp = 0; sp < SPLIT; ++sp) {
-      char* ta = st + (0 * SPLIT + sp) * TILEB + wave * 4096;
-      char* tb = st + (1 * SPLIT + sp) * TILEB + wave * 4096;
+      char* ta = a_tile(st, sp) + wave * 4096;
+      char* tb = b_tile(st, sp) + wave * QB * 1024;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 4; ++q)
         __builtin_amdgcn_global_load_lds((const void*)(a_src[sp] + aoff[q] + k0),
                                          (lds_void*)(ta + q * 1024), 16, 0, 0);
+#pragma unroll
+      for (int q = 0; q < QB; ++q)
         __builtin_amdgcn_global_load_lds((const void*)(b_src[sp] + boff[q] + k0),
                                          (lds_void*)(tb + q * 1024), 16, 0, 0);
-      }
     }
   };
 
@@ -333,8 +354,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
             x[r] = (row < g.rows && col < g.cols)
                        ? A.xs_user[eo + (int64_t)row * g.cols + col] : 0.0f;
           }
-        } else {
+        } else if (rb + i * 16 < mp) {
           load_op4<T, SPLIT>(A.xs_hi, A.xs_lo, xo + (int64_t)(cb + j * 16) * mp + rb + i * 16, x);
+        } else {
+          x[0] = x[1] = x[2] = x[3] = 0.0f;
         }
         acc[i][j] = f32x4_t{A.ca * x[0], A.ca * x[1], A.ca * x[2], A.ca * x[3]};
       }
@@ -363,7 +386,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
     asm volatile("" ::: "memory");
     if (s + NSTG - 1 < nslab) issue(s + NSTG - 1);
 
-    const char* st = smem + (s % NSTG) * STAGEB;
+    const int stg = s % NSTG;
     u32x4_t fa[2][SPLIT][4], fb[2][SPLIT][4];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -371,8 +394,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
       for (int sp = 0; sp < SPLIT; ++sp)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          fa[kk][sp][i] = *reinterpret_cast<const u32x4_t*>(st + (0 * SPLIT + sp) * TILEB + fa_off[kk][i]);
-          fb[kk][sp][i] = *reinterpret_cast<const u32x4_t*>(st + (1 * SPLIT + sp) * TILEB + fb_off[kk][i]);
+          fa[kk][sp][i] = *reinterpret_cast<const u32x4_t*>(a_tile(stg, sp) + fa_off[kk][i]);
+          fb[kk][sp][i] = *reinterpret_cast<const u32x4_t*>(b_tile(stg, sp) + fb_off[kk][i]);
         }
     // keep every fragment read of the slab ahead of the MFMAs, so the waits
     // before them count down outstanding reads instead of draining them
@@ -428,7 +451,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[i][j][r] = acc[i][j][r];
-    stage_store_tile<float, 1>(v, smem, A.o_raw + roff, nullptr, Rp, m0, n0, wm, wn, lane, tid);
+    stage_store_tile<float, 1, BMT, NT>(v, smem, A.o_raw + roff, nullptr, Rp, m0, n0, (int)Rp, wm, wn, lane, tid);
     if (tm != tn) store_mirror<float, 1>(v, A.o_raw, nullptr, roff, Rp, rbase, cbase);
   } else if constexpr (EPI == E_OP) {
     const float m = A.mul * (A.scal_pow == 2 ? cs * cs : 1.0f);
@@ -438,8 +461,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[i][j][r] = m * acc[i][j][r];
-    stage_store_tile<T, SPLIT>(v, smem, offset_ptr<T>(A.o_hi, roff), offset_ptr<T>(A.o_lo, roff),
-                               Rp, m0, n0, wm, wn, lane, tid);
+    stage_store_tile<T, SPLIT, BMT, NT>(v, smem, offset_ptr<T>(A.o_hi, roff),
+                                        offset_ptr<T>(A.o_lo, roff), Rp, m0, n0, (int)Rp, wm,
+                                        wn, lane, tid);
     if (tm != tn) store_mirror<T, SPLIT>(v, A.o_hi, A.o_lo, roff, Rp, rbase, cbase);
   } else if constexpr (EPI == E_SQUARE) {
     // b A + c A^2; A is symmetric, so A(row..row+3, col) = A(col, row..row+3)
@@ -455,8 +479,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[i][j][r] = A.cb * v[i][j][r] + A.cc * acc[i][j][r];
-    stage_store_tile<T, SPLIT>(v, smem, offset_ptr<T>(A.o_hi, roff), offset_ptr<T>(A.o_lo, roff),
-                               Rp, m0, n0, wm, wn, lane, tid);
+    stage_store_tile<T, SPLIT, BMT, NT>(v, smem, offset_ptr<T>(A.o_hi, roff),
+                                        offset_ptr<T>(A.o_lo, roff), Rp, m0, n0, (int)Rp, wm,
+                                        wn, lane, tid);
     if (tm != tn) store_mirror<T, SPLIT>(v, A.o_hi, A.o_lo, roff, Rp, rbase, cbase);
   } else {
     // E_UPDATE:  acc = a X + B X (first step: X = the unscaled source), and
@@ -473,12 +498,15 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
       // X^T rows directly (4 consecutive entries per tile), X rows via LDS
 #pragma unroll
       for (int i = 0; i < 4; ++i)
+        if (rbase + i * 16 < Mp) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          store_op4<T, SPLIT>(A.ot_hi, A.ot_lo, xoff + (int64_t)(cbase + j * 16) * Mp + rbase + i * 16,
-                              v[i][j]);
-      stage_store_tile<T, SPLIT>(v, smem, offset_ptr<T>(A.o_hi, xoff), offset_ptr<T>(A.o_lo, xoff),
-                                 Np, m0, n0, wm, wn, lane, tid);
+          for (int j = 0; j < 4; ++j)
+            store_op4<T, SPLIT>(A.ot_hi, A.ot_lo,
+                                xoff + (int64_t)(cbase + j * 16) * Mp + rbase + i * 16, v[i][j]);
+        }
+      stage_store_tile<T, SPLIT, BMT, NT>(v, smem, offset_ptr<T>(A.o_hi, xoff),
+                                          offset_ptr<T>(A.o_lo, xoff), Np, m0, n0, (int)Mp, wm,
+                                          wn, lane, tid);
     } else if (A.out == O_U || A.out == O_APPLY) {
       if (A.out == O_APPLY && A.status && A.status[0] != 0) return;
 #pragma unroll
@@ -523,34 +551,46 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
 // ---------------------------------------------------------------------------
 // Host launcher
 // ---------------------------------------------------------------------------
-// Pipeline depth per variant: the split-bf16 tiles are twice as large, so
-// they keep two stages within the 160 KB of LDS.
-template <typename T, int SPLIT>
-constexpr int stages() { return SPLIT == 2 ? 2 : SM_GEMM_STAGES; }
-// LDS of a block: the pipeline stages, or the epilogue's staging image of
-// the output tile if that is larger.
-// (the raw float32 Gram is staged as float32 whatever the operand type).
-template <typename T, int SPLIT>
-constexpr size_t lds_bytes() {
-  size_t pipe = (size_t)stages<T, SPLIT>() * 2 * SPLIT * TILEB;
-  size_t img = (size_t)SPLIT * BM * (BM * sizeof(T) + 16);
-  size_t raw = (size_t)BM * (BM * sizeof(float) + 16);
-  size_t m = pipe > img ? pipe : img;
-  return m > raw ? m : raw;
+// Launch configuration: 128x128 tiles, 4 waves, two stages, which lets two
+// blocks share a CU so one block's pipeline fill and epilogue overlap the
+// other's k-loop.  (The kernel also supports 256x128 tiles with 8 waves and
+// three stages; on the Newton-Schulz shapes that measured slower, since one
+// block per CU leaves those phases exposed.)
+template <typename T, int SPLIT, int EPI>
+struct Cfg {
+  static constexpr int WM = 2;
+  static constexpr int NSTG = 2;
+  static constexpr int BMT = 64 * WM;
+  static constexpr size_t lds() {
+    size_t pipe = (size_t)NSTG * SPLIT * (BMT * ROWB + TILEB);
+    size_t img = (size_t)SPLIT * BMT * (BM * sizeof(T) + 16);
+    size_t raw = (size_t)BMT * (BM * sizeof(float) + 16);  // raw Gram is float32
+    size_t m = pipe > img ? pipe : img;
+    return m > raw ? m : raw;
+  }
+};
+
+int gemm_update_tile_rows(int precision) {
+  return precision == P_BF16X3 ? Cfg<bf16_t, 2, E_UPDATE>::BMT
+                               : Cfg<bf16_t, 1, E_UPDATE>::BMT;
+}
+
+template <typename T, int SPLIT, int EPI>
+static hipError_t launch_one(const GemmArgs& args, hipStream_t s) {
+  using C = Cfg<T, SPLIT, EPI>;
+  hipLaunchKernelGGL((k_gemm<T, SPLIT, EPI, C::NSTG, C::WM>), dim3(args.G.total_blocks),
+                     dim3(128 * C::WM), C::lds(), s, args);
+  return hipGetLastError();
 }
 
 template <typename T, int SPLIT>
 static hipError_t launch_epi(const GemmArgs& args, hipStream_t s) {
-  dim3 grid(args.G.total_blocks), block(256);
-  constexpr int NS = stages<T, SPLIT>();
-  size_t lds = lds_bytes<T, SPLIT>();
   switch (args.epi) {
-    case E_RAW: hipLaunchKernelGGL((k_gemm<T, SPLIT, E_RAW, NS>), grid, block, lds, s, args); break;
-    case E_OP: hipLaunchKernelGGL((k_gemm<T, SPLIT, E_OP, NS>), grid, block, lds, s, args); break;
-    case E_SQUARE: hipLaunchKernelGGL((k_gemm<T, SPLIT, E_SQUARE, NS>), grid, block, lds, s, args); break;
-    default: hipLaunchKernelGGL((k_gemm<T, SPLIT, E_UPDATE, NS>), grid, block, lds, s, args); break;
+    case E_RAW: return launch_one<T, SPLIT, E_RAW>(args, s);
+    case E_OP: return launch_one<T, SPLIT, E_OP>(args, s);
+    case E_SQUARE: return launch_one<T, SPLIT, E_SQUARE>(args, s);
+    default: return launch_one<T, SPLIT, E_UPDATE>(args, s);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s) {
@@ -562,9 +602,9 @@ hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s) {
 
 template <typename T, int SPLIT, int EPI>
 static hipError_t set_lds() {
-  return hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_gemm<T, SPLIT, EPI, stages<T, SPLIT>()>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes<T, SPLIT>());
+  using C = Cfg<T, SPLIT, EPI>;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<T, SPLIT, EPI, C::NSTG, C::WM>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::lds());
 }
 template <typename T, int SPLIT>
 static hipError_t set_lds_all() {

@@ -40,6 +40,8 @@ struct GemmArgs {
 
 hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s);
 hipError_t gemm_set_attributes();
+// Rows of the update GEMM's block tile for a precision (128 or 256).
+int gemm_update_tile_rows(int precision);
 
 // ---- elementwise and small kernels (sm_elementwise.hip) ----
 hipError_t launch_momentum_flat(const float* G, const void* W, int w_bf16,
