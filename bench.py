@@ -31,6 +31,28 @@ PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 matrix-core peak
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 
 
+def gemm_traffic(workload):
+    """HBM bytes per Newton-Schulz GEMM launch from the committed counter
+    summary, if it was taken on the current GEMM source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"k_gemm_{workload}_hbm_traffic.md")
+    src = os.path.join(ROOT, "distributed_bit_matrix_amd", "csrc", "sm_gemm.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("gemm_source_sha256") != digest:
+        return None
+    try:
+        return int(fields["gemm_traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def hip_runtime():
     L = ctypes.CDLL("libamdhip64.so")
     L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -235,7 +257,8 @@ def main():
                    "resident buffers + apply"},
         "roofline": {"bound": "mfma", "achieved": round(ns_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(ns_tflops / peak, 4),
-                     "traffic": None, "kernel": "k_gemm (Newton-Schulz products)",
+                     "traffic": gemm_traffic(w.name), "traffic_unit": "bytes per launch",
+                     "kernel": "k_gemm (Newton-Schulz products)",
                      "launches_per_step": gemm_per_step,
                      "avg_launch_us": round(gemm_us / max(gemm_per_step, 1), 2)},
         "ns_mfma_util_pct": round(100 * ns_tflops / peak, 2),
