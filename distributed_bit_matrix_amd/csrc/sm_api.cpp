@@ -189,11 +189,15 @@ hipError_t for_launches(const std::vector<Group>& groups, Fill fill, Go go,
     Group g = g0;
     if (fill(g)) gs.push_back(g);
   }
-  for (size_t s = 0; s < gs.size(); s += kMaxGroups) {
+  // launches hold at most kMaxGroups runs, all with the same GEMM tile
+  std::stable_sort(gs.begin(), gs.end(),
+                   [](const Group& a, const Group& b) { return a.tile < b.tile; });
+  for (size_t s = 0, e = 0; s < gs.size(); s = e) {
     Groups G;
     std::memset(&G, 0, sizeof(G));
     int64_t blocks = 0;
-    size_t e = std::min(gs.size(), s + kMaxGroups);
+    e = s;
+    while (e < gs.size() && e - s < (size_t)kMaxGroups && gs[e].tile == gs[s].tile) ++e;
     for (size_t i = s; i < e; ++i) {
       Group g = gs[i];
       g.block0 = (int32_t)blocks;
@@ -273,9 +277,10 @@ hipError_t mark(sm_profile* prof, int kind, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // PolarNS pipeline over all matrices of a plan, starting from the padded
-// operand copy in x[0] with partial sums in part (Frobenius).
-//   first: XS_USER (src_user in caller layout, e.g. the momentum) or XS_OP
-//   (the operand copy itself, e.g. the majority matrix).
+// operand copies in x[0] / xt[0] with partial sums in part (Frobenius).
+//   first: XS_USER (the first a X term from src_user, the caller's float32
+//   source, e.g. the momentum) or XS_OP (from the operand copy, e.g. the
+//   majority matrix, whose entries the operand holds exactly).
 //   final: O_U (write U), O_BITS (pack into bits), O_APPLY (update W).
 // `fusable[i]` says whether matrix i may use O_BITS; others write U into
 // the workspace and are packed afterwards.
@@ -292,6 +297,17 @@ struct NsIO {
   sm_profile* prof;
 };
 
+// GEMM launch fields of a group whose gm / gn are set: the tile size, the
+// tiles along n and the blocks per matrix (upper-triangular tiles of a
+// symmetric output).
+void set_gemm_tiles(Group& g, int prec, int epi) {
+  const int tile = gemm_tile(prec, epi, g.gm, g.gn);
+  g.tile = tile;
+  g.tiles_n = (g.gn + tile - 1) / tile;
+  const int tiles_m = (g.gm + tile - 1) / tile;
+  g.blocks_per_mat = epi == E_UPDATE ? tiles_m * g.tiles_n : g.tiles_n * (g.tiles_n + 1) / 2;
+}
+
 sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
                         const std::vector<Group>& groups, const sm_hparams* hp,
                         Bufs& B, const NsIO& io, int part_kind,
@@ -306,8 +322,7 @@ sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
     const MatPlan& q = mp[g.idx0];
     g.gm = g.gn = (int32_t)q.Rp;
     g.gk = (int32_t)(q.tall ? q.Mp : q.Np);
-    g.tiles_n = (int32_t)(q.Rp / 128);
-    g.blocks_per_mat = g.tiles_n * (g.tiles_n + 1) / 2;  // upper triangle
+    set_gemm_tiles(g, prec, P.spectral ? E_RAW : E_OP);
     g.ops = q.tall ? gemm_ops(FAM_XT, FAM_XT) : gemm_ops(FAM_X, FAM_X);
     return true;
   };
@@ -379,8 +394,7 @@ hipError_t run_square(const Plan& P, const std::vector<MatPlan>& mp,
   return for_launches(groups, [&](Group& g) {
     const MatPlan& q = mp[g.idx0];
     g.gm = g.gn = g.gk = (int32_t)q.Rp;
-    g.tiles_n = (int32_t)(q.Rp / 128);
-    g.blocks_per_mat = g.tiles_n * (g.tiles_n + 1) / 2;  // upper triangle
+    set_gemm_tiles(g, P.precision, E_SQUARE);
     g.ops = gemm_ops(FAM_R, FAM_R);
     return true;
   }, [&](const Groups& G) {
@@ -408,8 +422,7 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
         const MatPlan& q = mp[g.idx0];
         g.gm = g.gn = (int32_t)q.Rp;
         g.gk = (int32_t)(q.tall ? q.Mp : q.Np);
-        g.tiles_n = (int32_t)(q.Rp / 128);
-        g.blocks_per_mat = g.tiles_n * (g.tiles_n + 1) / 2;  // upper triangle
+        set_gemm_tiles(g, prec, E_OP);
         g.ops = q.tall ? gemm_ops(FAM_XT, FAM_XT) : gemm_ops(FAM_X, FAM_X);
         return true;
       }, [&](const Groups& G) {
@@ -439,11 +452,9 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
       HIP_TRY(for_launches(groups, [&](Group& g) {
         const MatPlan& q = mp[g.idx0];
         if (last && io.final_out == O_BITS && fusable[g.idx0] != (pass == 0)) return false;
-        const int bmt = gemm_update_tile_rows(prec);
         g.gm = (int32_t)q.Mp; g.gn = (int32_t)q.Np;
         g.gk = (int32_t)q.Rp;
-        g.tiles_n = (int32_t)(q.Np / 128);
-        g.blocks_per_mat = (int32_t)(((q.Mp + bmt - 1) / bmt) * g.tiles_n);
+        set_gemm_tiles(g, prec, E_UPDATE);
         g.ops = q.tall ? gemm_ops(FAM_X, FAM_R) : gemm_ops(FAM_R, FAM_XT);
         return true;
       }, [&](const Groups& G) {
@@ -455,9 +466,8 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
         a.r_hi = B.b[0]; a.r_lo = B.b[1];
         a.epi = E_UPDATE; a.ca = hp->ns_a;
         a.xsrc = k == 1 ? io.first_xsrc : XS_OP;
-        a.scal = B.scal; a.scal_pow = k == 1 ? 1 : 0;
         a.xs_user = io.src_user;
-        a.xs_hi = B.xt[cur][0]; a.xs_lo = B.xt[cur][1];   // read as X^T
+        a.scal = B.scal; a.scal_pow = k == 1 ? 1 : 0;
         if (!last) {
           a.out = O_X;
           a.o_hi = B.x[cur ^ 1][0]; a.o_lo = B.x[cur ^ 1][1];

@@ -17,6 +17,8 @@
 // pipeline; completion is tracked with explicit vmcnt waits and a bare
 // s_barrier.  All operand copies are zero padded to multiples of 128, so no
 // load is predicated and padding contributes exact zeros.
+#include <type_traits>
+
 #include "sm_internal.h"
 #include "sm_launch.h"
 
@@ -28,18 +30,45 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BM = 128;          // block tile (both dims)
-constexpr int ROWB = 128;        // bytes per LDS row (one k-slab)
-constexpr int TILEB = BM * ROWB; // bytes per operand tile per stage
+constexpr int BM = 128;          // block tile width (and height for WM = 2)
 
-#ifndef SM_GEMM_STAGES
-#define SM_GEMM_STAGES 2
-#endif
-
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * ROWB + ((chunk ^ swz(row)) << 4);
+// LDS image of one k-slab of an operand tile: RB bytes per row (64 or 128),
+// 16-byte chunks XOR-swizzled by row.  A fragment read (16 lanes on 16
+// consecutive rows, one chunk) then touches every bank group once in each
+// group of 8 lanes and in each group of 16 lanes.  The swizzle depends on
+// row bits 0..3 only, so rows 16 apart share it and a fragment offset
+// steps by a constant 16*RB bytes per 16-row tile.
+template <int RB>
+__host__ __device__ constexpr int swz(int row) {
+  if constexpr (RB == 128) return (row ^ ((row >> 3) & 1)) & 7;
+  else return ((row >> 1) & 3) ^ ((row >> 3) & 1);
 }
+template <int RB>
+__host__ __device__ constexpr int lds_off(int row, int chunk) {
+  return row * RB + ((chunk ^ swz<RB>(row)) << 4);
+}
+// Compile-time checks of the layout: constant 16-row stride, and distinct
+// 16-byte bank groups for every 8 and every 16 lanes of a fragment read
+// (banks repeat every 128 / 256 bytes).
+template <int RB>
+constexpr bool slab_layout_ok() {
+  for (int r0 = 0; r0 < 256; r0 += 16)
+    for (int ch = 0; ch < RB / 16; ++ch) {
+      for (int r = 0; r < 16; ++r)
+        if (lds_off<RB>(r0 + r, ch) != lds_off<RB>(r, ch) + r0 * RB) return false;
+      for (int span = 8; span <= 16; span *= 2)
+        for (int a = 0; a < 16; a += span) {
+          unsigned seen = 0;
+          for (int r = a; r < a + span; ++r) {
+            const int unit = (lds_off<RB>(r0 + r, ch) % (16 * span)) / 16;
+            if (seen & (1u << unit)) return false;
+            seen |= 1u << unit;
+          }
+        }
+    }
+  return true;
+}
+static_assert(slab_layout_ok<64>() && slab_layout_ok<128>(), "LDS slab swizzle");
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -154,25 +183,25 @@ __device__ __forceinline__ void load_op4(const void* hi, const void* lo, int64_t
   }
 }
 
-// Store a BMT x 128 output tile (values in accumulator layout) row-major at
-// dst (row length ld) through LDS: each wave writes its 64x64 sub-tile into
-// an LDS image of the tile, then every thread stores 16-byte row segments
-// (rows at or past row_lim are skipped).  For split-bf16 the hi and lo
-// images sit side by side.  The LDS row pitch is padded by 16 bytes
-// against bank conflicts.
-template <typename T, int SPLIT, int BMT, int NT>
-__device__ __forceinline__ void stage_store_tile(const float (&v)[4][4][4], char* smem,
+// Store a BMT x BNT output tile (values in accumulator layout) row-major at
+// dst (row length ld) through LDS: each wave writes its (16 TI) x (16 TJ)
+// sub-tile into an LDS image of the tile, then every thread stores 16-byte
+// row segments (rows at or past row_lim are skipped).  For split-bf16 the
+// hi and lo images sit side by side.  The LDS row pitch is padded by 16
+// bytes against bank conflicts.
+template <typename T, int SPLIT, int BMT, int BNT, int TI, int TJ, int NT>
+__device__ __forceinline__ void stage_store_tile(const f32x4_t (&v)[TI][TJ], char* smem,
                                                  void* dst_hi, void* dst_lo, int64_t ld,
                                                  int m0, int n0, int row_lim, int wm, int wn,
                                                  int lane, int tid) {
   constexpr int ES = sizeof(T);
-  constexpr int PITCH = BM * ES + 16;
+  constexpr int PITCH = BNT * ES + 16;
   constexpr int IMG = BMT * PITCH;
-  const int r0 = wm * 64 + 4 * (lane >> 4), c0 = wn * 64 + (lane & 15);
+  const int r0 = wm * TI * 16 + 4 * (lane >> 4), c0 = wn * TJ * 16 + (lane & 15);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         char* p = smem + (r0 + i * 16 + r) * PITCH + (c0 + j * 16) * ES;
@@ -188,7 +217,7 @@ __device__ __forceinline__ void stage_store_tile(const float (&v)[4][4][4], char
         }
       }
   __syncthreads();
-  constexpr int CH = BM * ES / 16;          // 16-byte chunks per row
+  constexpr int CH = BNT * ES / 16;         // 16-byte chunks per row
 #pragma unroll
   for (int p = 0; p < BMT * CH / NT; ++p) {
     const int c = tid + NT * p;
@@ -203,34 +232,51 @@ __device__ __forceinline__ void stage_store_tile(const float (&v)[4][4][4], char
   }
 }
 
+// Four consecutive values held in one accumulator register group.
+template <typename T, int SPLIT>
+__device__ __forceinline__ void store_acc4(void* hi, void* lo, int64_t i, const f32x4_t& a) {
+  const float v[4] = {a[0], a[1], a[2], a[3]};
+  store_op4<T, SPLIT>(hi, lo, i, v);
+}
+
 // Mirror tile of a symmetric output: C(row..row+3, col) goes to row `col`,
 // columns row..row+3 (one 8- or 16-byte store per accumulator tile).
-template <typename T, int SPLIT>
-__device__ __forceinline__ void store_mirror(const float (&v)[4][4][4], void* hi, void* lo,
+template <typename T, int SPLIT, int TI, int TJ>
+__device__ __forceinline__ void store_mirror(const f32x4_t (&v)[TI][TJ], void* hi, void* lo,
                                              int64_t off, int64_t ld, int rbase, int cbase) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      store_op4<T, SPLIT>(hi, lo, off + (int64_t)(cbase + j * 16) * ld + rbase + i * 16, v[i][j]);
+    for (int j = 0; j < TJ; ++j)
+      store_acc4<T, SPLIT>(hi, lo, off + (int64_t)(cbase + j * 16) * ld + rbase + i * 16, v[i][j]);
 }
 
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
-template <typename T, int SPLIT, int EPI, int NSTG, int WM>
-__global__ __launch_bounds__(128 * WM) void k_gemm(GemmArgs A) {
+// Template parameters: operand type and split (bf16 x2 = split-bf16), the
+// epilogue, NSTG pipeline stages of RB-byte slab rows, WM x 2 waves of
+// (16 TI) x (16 TJ) each, and the waves per SIMD that the register
+// allocation must leave room for.
+template <typename T, int SPLIT, int EPI, int NSTG, int WM, int TI, int TJ, int RB, int WPE>
+__global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  // Block tile BMT x 128 with WM x 2 waves of 64x64.
-  constexpr int BMT = 64 * WM;
+  constexpr int WTM = 16 * TI, WTN = 16 * TJ;  // wave tile
+  constexpr int BMT = WM * WTM, BNT = 2 * WTN; // block tile
   constexpr int NW = 2 * WM, NT = 64 * NW;
-  constexpr int QB = 16 / NW;                 // B-operand loads per wave
-  constexpr int ATILE = BMT * ROWB;           // A-operand bytes per split
-  constexpr int STAGEB = SPLIT * (ATILE + TILEB);
-  constexpr int P = Elem<T>::per16;           // elements per 16 bytes
-  constexpr int BK = ROWB / sizeof(T);        // k per slab
-  constexpr int LOADS = SPLIT * (4 + QB);     // vector loads per thread per slab
-  static_assert(EPI == E_UPDATE || WM == 2, "symmetric outputs use square tiles");
+  constexpr int CPR = RB / 16;                 // 16-byte chunks per slab row
+  constexpr int RPI = 1024 / RB;               // slab rows per wave-wide DMA load
+  constexpr int NKK = CPR / 4;                 // MFMA k-steps per slab
+  constexpr int QA = BMT * RB / 1024 / NW;     // A-operand loads per wave
+  constexpr int QB = BNT * RB / 1024 / NW;     // B-operand loads per wave
+  constexpr int ATILE = BMT * RB;              // A-operand bytes per split
+  constexpr int BTILE = BNT * RB;
+  constexpr int STAGEB = SPLIT * (ATILE + BTILE);
+  constexpr int P = Elem<T>::per16;            // elements per 16 bytes
+  constexpr int BK = RB / sizeof(T);           // k per slab
+  static_assert(QA >= 1 && QB >= 1 && NKK >= 1, "tile / slab shape");
+  static_assert(EPI == E_UPDATE || BMT == BNT, "symmetric outputs use square tiles");
+  static_assert(TI == TJ, "square wave tiles");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -252,18 +298,25 @@ __global__ __launch_bounds__(128 * WM) void k_gemm(GemmArgs A) {
   // Symmetric outputs (Gram, raw Gram, quintic square) are computed on the
   // upper-triangular tiles only; the epilogue also writes the mirror tile.
   constexpr bool SYM = EPI != E_UPDATE;
+  const int a_fam = g.ops & 3, b_fam = (g.ops >> 2) & 3;
   int tm, tn;
   if constexpr (SYM) {
     tm = 0;
     int rem = t;
     while (rem >= g.tiles_n - tm) { rem -= g.tiles_n - tm; ++tm; }
     tn = tm + rem;
+  } else if (a_fam == FAM_R) {
+    // the small operand (B = b X X^T) is the A side: consecutive tiles walk
+    // down m, so the tiles that share one X^T block run together on one XCD
+    // and fetch it from HBM once
+    const int tiles_m = (g.gm + BMT - 1) / BMT;
+    tn = t / tiles_m;
+    tm = t - tn * tiles_m;
   } else {
     tm = t / g.tiles_n;
     tn = t - tm * g.tiles_n;
   }
-  const int m0 = tm * BMT, n0 = tn * BM;
-  const int a_fam = g.ops & 3, b_fam = (g.ops >> 2) & 3;
+  const int m0 = tm * BMT, n0 = tn * BNT;
   const int64_t lda = fam_ld(g, a_fam), ldb = fam_ld(g, b_fam);
   const void* a_hi = a_fam == FAM_X ? A.x_hi : (a_fam == FAM_XT ? A.xt_hi : A.r_hi);
   const void* b_hi = b_fam == FAM_X ? A.x_hi : (b_fam == FAM_XT ? A.xt_hi : A.r_hi);
@@ -279,51 +332,52 @@ __global__ __launch_bounds__(128 * WM) void k_gemm(GemmArgs A) {
   }
 
   // Per-lane source offsets of the loads per operand and slab: the A load q
-  // of wave w fills LDS rows (4w+q)*8 .. +7 (B: (QB w+q)*8 ..); lane l writes
-  // row ..+l/8 at chunk position l%8, so it fetches global chunk
-  // (l%8) ^ swz(row).  A rows past the operand (a ragged last BMT-row tile)
-  // read the last row instead; their results are never stored.
-  int64_t aoff[4], boff[QB];
+  // of wave w fills LDS rows (QA w+q)*RPI .. +RPI-1 (B: (QB w+q)*RPI ..);
+  // lane l writes row ..+l/CPR at chunk position l%CPR, so it fetches global
+  // chunk (l%CPR) ^ swz(row).  Rows past the operand (a ragged last tile)
+  // read its last row instead; their results are never stored.
+  int64_t aoff[QA], boff[QB];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    int row = (wave * 4 + q) * 8 + (lane >> 3);
-    int ch = (lane & 7) ^ swz(row);
+  for (int q = 0; q < QA; ++q) {
+    int row = (wave * QA + q) * RPI + lane / CPR;
+    int ch = (lane % CPR) ^ swz<RB>(row);
     int arow = m0 + row < g.gm ? m0 + row : g.gm - 1;
     aoff[q] = (int64_t)arow * lda + ch * P;
   }
 #pragma unroll
   for (int q = 0; q < QB; ++q) {
-    int row = (wave * QB + q) * 8 + (lane >> 3);
-    int ch = (lane & 7) ^ swz(row);
-    boff[q] = (int64_t)(n0 + row) * ldb + ch * P;
+    int row = (wave * QB + q) * RPI + lane / CPR;
+    int ch = (lane % CPR) ^ swz<RB>(row);
+    int brow = n0 + row < g.gn ? n0 + row : g.gn - 1;
+    boff[q] = (int64_t)brow * ldb + ch * P;
   }
   // Per-lane LDS offsets of the fragment reads: row within the tile and
-  // 16-byte chunk (kk*4 + lane/16) of the 128-byte slab row.
-  int fa_off[2][4], fb_off[2][4];
+  // 16-byte chunk (kk*4 + lane/16) of the slab row.  The swizzle depends
+  // on row bits that i*16 does not touch, so one offset per kk serves all
+  // i (j) with a constant stride.
+  int fa_off[NKK], fb_off[NKK];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa_off[kk][i] = lds_off(wm * 64 + i * 16 + (lane & 15), kk * 4 + (lane >> 4));
-      fb_off[kk][i] = lds_off(wn * 64 + i * 16 + (lane & 15), kk * 4 + (lane >> 4));
-    }
+  for (int kk = 0; kk < NKK; ++kk) {
+    fa_off[kk] = lds_off<RB>(wm * WTM + (lane & 15), kk * 4 + (lane >> 4));
+    fb_off[kk] = lds_off<RB>(wn * WTN + (lane & 15), kk * 4 + (lane >> 4));
+  }
 
   const int nslab = g.gk / BK;
 
   // LDS stage: [A split 0][A split 1..][B split 0][B split 1..]
   auto a_tile = [&](int st, int sp) -> char* { return smem + st * STAGEB + sp * ATILE; };
   auto b_tile = [&](int st, int sp) -> char* {
-    return smem + st * STAGEB + SPLIT * ATILE + sp * TILEB;
+    return smem + st * STAGEB + SPLIT * ATILE + sp * BTILE;
   };
   auto issue = [&](int s) {
     const int st = s % NSTG;
     const int64_t k0 = (int64_t)s * BK;
 #pragma unroll
     for (int sp = 0; sp < SPLIT; ++sp) {
-      char* ta = a_tile(st, sp) + wave * 4096;
+      char* ta = a_tile(st, sp) + wave * QA * 1024;
       char* tb = b_tile(st, sp) + wave * QB * 1024;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < QA; ++q)
         __builtin_amdgcn_global_load_lds((const void*)(a_src[sp] + aoff[q] + k0),
                                          (lds_void*)(ta + q * 1024), 16, 0, 0);
 #pragma unroll
@@ -333,40 +387,120 @@ __global__ __launch_bounds__(128 * WM) void k_gemm(GemmArgs A) {
     }
   };
 
-  f32x4_t acc[4][4];
-  if constexpr (EPI == E_UPDATE) {
-    // a X + B X: start the accumulator at a * X so that its loads overlap
-    // the k-loop.  X comes from the caller's float32 array (first step) or
-    // from X^T (4 consecutive rows of a column are 4 consecutive entries).
-    const int rb = m0 + wm * 64 + 4 * (lane >> 4), cb = n0 + wn * 64 + (lane & 15);
-    const int64_t xo = g.x0 + (int64_t)mi * g.x_stride;
+  f32x4_t acc[TI][TJ];
+  const bool ax_user = EPI == E_UPDATE && A.xsrc == XS_USER;
+  if (ax_user) {
+    // first step: a X from the caller's float32 source (rows past the
+    // matrix are zero), loaded ahead of the k-loop
+    const int rb = m0 + wm * WTM + 4 * (lane >> 4), cb = n0 + wn * WTN + (lane & 15);
     const int64_t eo = g.elem0 + (int64_t)mi * g.elem_stride;
-    const int64_t mp = round_up(g.rows, kPad);
+    // (addresses clamped into the matrix so that every load is issued
+    // unconditionally and all of them overlap; out-of-range entries are
+    // replaced by zero afterwards)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float x[4];
-        if (A.xsrc == XS_USER) {
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = rb + i * 16 + r, col = cb + j * 16;
-            x[r] = (row < g.rows && col < g.cols)
-                       ? A.xs_user[eo + (int64_t)row * g.cols + col] : 0.0f;
-          }
-        } else if (rb + i * 16 < mp) {
-          load_op4<T, SPLIT>(A.xs_hi, A.xs_lo, xo + (int64_t)(cb + j * 16) * mp + rb + i * 16, x);
-        } else {
-          x[0] = x[1] = x[2] = x[3] = 0.0f;
+        for (int r = 0; r < 4; ++r) {
+          const int row = rb + i * 16 + r, col = cb + j * 16;
+          const int rc = row < g.rows ? row : g.rows - 1, cc = col < g.cols ? col : g.cols - 1;
+          const float x = A.xs_user[eo + (int64_t)rc * g.cols + cc];
+          acc[i][j][r] = row < g.rows && col < g.cols ? A.ca * x : 0.0f;
         }
-        acc[i][j] = f32x4_t{A.ca * x[0], A.ca * x[1], A.ca * x[2], A.ca * x[3]};
-      }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+
+  // Later steps read the update's a X term from the operand tiles in LDS
+  // while they pass through: for a wide X (A = B, B operand = X^T) the slab holding
+  // k = m0 + wm*WTM + i*16 .. +15 of the X^T block contains X(m, n) for this
+  // wave's output rows m and columns n; for a tall X (A operand = X) the
+  // slab holding k = n contains X(m, n).  Each k-block of 16 lies in one slab.
+  const bool ax_wide = a_fam == FAM_R;
+  const int ax_k0 = ax_wide ? m0 + wm * WTM : n0 + wn * WTN;  // first k of the a X block
+  // a X for the 16-wide k-block u (acc row block u for a wide X, column
+  // block u for a tall one) from the stage that holds it.
+  auto add_ax_block = [&](auto uc, int s, int stg) {
+    constexpr int u = decltype(uc)::value;
+    const int kb = ax_k0 + u * 16 - s * BK;
+    if (ax_wide) {
+      // X^T rows n, 4 consecutive k = m: one 8- (bf16) or 16-byte (f32) read
+      const int kk = kb + 4 * (lane >> 4);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int row = wn * WTN + j * 16 + (lane & 15);
+        const int off = lds_off<RB>(row, kk / P) + (kk % P) * (int)sizeof(T);
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sp = 0; sp < SPLIT; ++sp) {
+          const char* p = b_tile(stg, sp) + off;
+          if constexpr (sizeof(T) == 4) {
+            f32x4_t v = *reinterpret_cast<const f32x4_t*>(p);
+            x[0] += v[0]; x[1] += v[1]; x[2] += v[2]; x[3] += v[3];
+          } else {
+            u32x2_t h = *reinterpret_cast<const u32x2_t*>(p);
+            x[0] += __uint_as_float(h[0] << 16); x[1] += __uint_as_float(h[0] & 0xFFFF0000u);
+            x[2] += __uint_as_float(h[1] << 16); x[3] += __uint_as_float(h[1] & 0xFFFF0000u);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[u][j][r] += A.ca * x[r];
+      }
+    } else {
+      // X rows m (4 consecutive rows), one k = n each: element reads
+      const int kk = kb + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = wm * WTM + i * 16 + 4 * (lane >> 4) + r;
+          const int off = lds_off<RB>(row, kk / P) + (kk % P) * (int)sizeof(T);
+          float x = 0.0f;
+#pragma unroll
+          for (int sp = 0; sp < SPLIT; ++sp) {
+            const char* p = a_tile(stg, sp) + off;
+            if constexpr (sizeof(T) == 4) x += *reinterpret_cast<const float*>(p);
+            else x += bf16_to_f32(*reinterpret_cast<const bf16_t*>(p));
+          }
+          acc[i][u][r] += A.ca * x;
+        }
+    }
+  };
+  // every 16-wide k-block of the a X term that lies in slab s
+  auto add_ax = [&](int s, int stg) {
+    static_assert(TI == 4, "a X blocks");
+    if ((ax_k0 + 0) / BK == s) add_ax_block(std::integral_constant<int, 0>{}, s, stg);
+    if ((ax_k0 + 16) / BK == s) add_ax_block(std::integral_constant<int, 1>{}, s, stg);
+    if ((ax_k0 + 32) / BK == s) add_ax_block(std::integral_constant<int, 2>{}, s, stg);
+    if ((ax_k0 + 48) / BK == s) add_ax_block(std::integral_constant<int, 3>{}, s, stg);
+  };
+
+  constexpr int LOADS = SPLIT * (QA + QB);     // vector loads per thread per slab
+
+  // MFMAs of one k-step on one accumulator tile.
+  auto mfma_tile = [&](const u32x4_t* fa, const u32x4_t* fb, int i, int j) {
+    if constexpr (sizeof(T) == 2) {
+      bf16x8_t ah = __builtin_bit_cast(bf16x8_t, fa[0]);
+      bf16x8_t bh = __builtin_bit_cast(bf16x8_t, fb[0]);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[i][j], 0, 0, 0);
+      if constexpr (SPLIT == 2) {
+        bf16x8_t al = __builtin_bit_cast(bf16x8_t, fa[TI]);
+        bf16x8_t bl = __builtin_bit_cast(bf16x8_t, fb[TJ]);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[i][j], 0, 0, 0);
+      }
+    } else {
+      f32x4_t av = __builtin_bit_cast(f32x4_t, fa[0]);
+      f32x4_t bv = __builtin_bit_cast(f32x4_t, fb[0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc[i][j], 0, 0, 0);
+    }
+  };
 
 #pragma unroll
   for (int s = 0; s < NSTG - 1; ++s)
@@ -387,47 +521,39 @@ __global__ __launch_bounds__(128 * WM) void k_gemm(GemmArgs A) {
     if (s + NSTG - 1 < nslab) issue(s + NSTG - 1);
 
     const int stg = s % NSTG;
-    u32x4_t fa[2][SPLIT][4], fb[2][SPLIT][4];
+    // frags [kk][split][i] (A: TI tiles, B: TJ tiles)
+    u32x4_t fa[NKK][SPLIT * TI], fb[NKK][SPLIT * TJ];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int sp = 0; sp < SPLIT; ++sp)
+      for (int sp = 0; sp < SPLIT; ++sp) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          fa[kk][sp][i] = *reinterpret_cast<const u32x4_t*>(a_tile(stg, sp) + fa_off[kk][i]);
-          fb[kk][sp][i] = *reinterpret_cast<const u32x4_t*>(b_tile(stg, sp) + fb_off[kk][i]);
-        }
+        for (int i = 0; i < TI; ++i)
+          fa[kk][sp * TI + i] =
+              *reinterpret_cast<const u32x4_t*>(a_tile(stg, sp) + fa_off[kk] + i * 16 * RB);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          fb[kk][sp * TJ + j] =
+              *reinterpret_cast<const u32x4_t*>(b_tile(stg, sp) + fb_off[kk] + j * 16 * RB);
+      }
     // keep every fragment read of the slab ahead of the MFMAs, so the waits
     // before them count down outstanding reads instead of draining them
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (sizeof(T) == 2) {
-            bf16x8_t ah = __builtin_bit_cast(bf16x8_t, fa[kk][0][i]);
-            bf16x8_t bh = __builtin_bit_cast(bf16x8_t, fb[kk][0][j]);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[i][j], 0, 0, 0);
-            if constexpr (SPLIT == 2) {
-              bf16x8_t al = __builtin_bit_cast(bf16x8_t, fa[kk][1][i]);
-              bf16x8_t bl = __builtin_bit_cast(bf16x8_t, fb[kk][1][j]);
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[i][j], 0, 0, 0);
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[i][j], 0, 0, 0);
-            }
-          } else {
-            f32x4_t av = __builtin_bit_cast(f32x4_t, fa[kk][0][i]);
-            f32x4_t bv = __builtin_bit_cast(f32x4_t, fb[kk][0][j]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc[i][j], 0, 0, 0);
-          }
-        }
+        for (int j = 0; j < TJ; ++j) mfma_tile(&fa[kk][i], &fb[kk][j], i, j);
+    if constexpr (EPI == E_UPDATE) {
+      // after the slab's MFMAs, when the fragment registers are free again
+      __builtin_amdgcn_sched_barrier(0);
+      if (!ax_user && s * BK < ax_k0 + 16 * TI && ax_k0 < (s + 1) * BK) add_ax(s, stg);
+    }
   }
 
   // ---- epilogue.  acc[i][j][r] holds C(row, col) with
-  //   row = m0 + wm*64 + i*16 + 4*(lane/16) + r,  col = n0 + wn*64 + j*16 + lane%16
+  //   row = m0 + wm*WTM + i*16 + 4*(lane/16) + r,  col = n0 + wn*WTN + j*16 + lane%16
   // i.e. the 4 registers of a tile are 4 consecutive rows of one column.
   const int idx = g.idx0 + mi * g.idx_stride;
   const float cs = A.scal ? A.scal[idx] : 1.0f;
@@ -438,88 +564,78 @@ __global__ __launch_bounds__(128 * WM) void k_gemm(GemmArgs A) {
   const int64_t Mp = round_up(rows, kPad);
   const int64_t Np = round_up(cols, kPad);
   const int64_t Rp = round_up(rows < cols ? rows : cols, kPad);
-  const int rbase = m0 + wm * 64 + 4 * (lane >> 4);
-  const int cbase = n0 + wn * 64 + (lane & 15);
+  const int rbase = m0 + wm * WTM + 4 * (lane >> 4);
+  const int cbase = n0 + wn * WTN + (lane & 15);
   // every wave is done reading the operand stages: LDS is free for staging
   __syncthreads();
 
-  float v[4][4][4];
   if constexpr (EPI == E_RAW) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[i][j][r] = acc[i][j][r];
-    stage_store_tile<float, 1, BMT, NT>(v, smem, A.o_raw + roff, nullptr, Rp, m0, n0, (int)Rp, wm, wn, lane, tid);
-    if (tm != tn) store_mirror<float, 1>(v, A.o_raw, nullptr, roff, Rp, rbase, cbase);
+    stage_store_tile<float, 1, BMT, BNT, TI, TJ, NT>(acc, smem, A.o_raw + roff, nullptr, Rp, m0,
+                                                     n0, (int)Rp, wm, wn, lane, tid);
+    if (tm != tn) store_mirror<float, 1, TI, TJ>(acc, A.o_raw, nullptr, roff, Rp, rbase, cbase);
   } else if constexpr (EPI == E_OP) {
     const float m = A.mul * (A.scal_pow == 2 ? cs * cs : 1.0f);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[i][j][r] = m * acc[i][j][r];
-    stage_store_tile<T, SPLIT, BMT, NT>(v, smem, offset_ptr<T>(A.o_hi, roff),
-                                        offset_ptr<T>(A.o_lo, roff), Rp, m0, n0, (int)Rp, wm,
-                                        wn, lane, tid);
-    if (tm != tn) store_mirror<T, SPLIT>(v, A.o_hi, A.o_lo, roff, Rp, rbase, cbase);
+      for (int j = 0; j < TJ; ++j) acc[i][j] *= m;
+    stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
+                                                     offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
+                                                     (int)Rp, wm, wn, lane, tid);
+    if (tm != tn) store_mirror<T, SPLIT, TI, TJ>(acc, A.o_hi, A.o_lo, roff, Rp, rbase, cbase);
   } else if constexpr (EPI == E_SQUARE) {
     // b A + c A^2; A is symmetric, so A(row..row+3, col) = A(col, row..row+3)
+    // (combined tile by tile, so that the loaded values and the accumulator
+    // never have to be held in registers side by side)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < TJ; ++j) {
+        float x[4];
         load_op4<T, SPLIT>(A.sq_hi, A.sq_lo, roff + (int64_t)(cbase + j * 16) * Rp + rbase + i * 16,
-                           v[i][j]);
+                           x);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[i][j][r] = A.cb * v[i][j][r] + A.cc * acc[i][j][r];
-    stage_store_tile<T, SPLIT, BMT, NT>(v, smem, offset_ptr<T>(A.o_hi, roff),
-                                        offset_ptr<T>(A.o_lo, roff), Rp, m0, n0, (int)Rp, wm,
-                                        wn, lane, tid);
-    if (tm != tn) store_mirror<T, SPLIT>(v, A.o_hi, A.o_lo, roff, Rp, rbase, cbase);
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = A.cb * x[r] + A.cc * acc[i][j][r];
+      }
+    stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
+                                                     offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
+                                                     (int)Rp, wm, wn, lane, tid);
+    if (tm != tn) store_mirror<T, SPLIT, TI, TJ>(acc, A.o_hi, A.o_lo, roff, Rp, rbase, cbase);
   } else {
     // E_UPDATE:  acc = a X + B X (first step: X = the unscaled source), and
     // the iterate is c^p * acc with c = 1/(s+eps) on the first step.
     const float gam = A.scal_pow == 1 ? cs : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[i][j][r] = gam * acc[i][j][r];
+      for (int j = 0; j < TJ; ++j) acc[i][j] *= gam;
 
     if (A.out == O_X) {
       // X^T rows directly (4 consecutive entries per tile), X rows via LDS
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TI; ++i)
         if (rbase + i * 16 < Mp) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            store_op4<T, SPLIT>(A.ot_hi, A.ot_lo,
-                                xoff + (int64_t)(cbase + j * 16) * Mp + rbase + i * 16, v[i][j]);
+          for (int j = 0; j < TJ; ++j)
+            store_acc4<T, SPLIT>(A.ot_hi, A.ot_lo,
+                                 xoff + (int64_t)(cbase + j * 16) * Mp + rbase + i * 16, acc[i][j]);
         }
-      stage_store_tile<T, SPLIT, BMT, NT>(v, smem, offset_ptr<T>(A.o_hi, xoff),
-                                          offset_ptr<T>(A.o_lo, xoff), Np, m0, n0, (int)Mp, wm,
-                                          wn, lane, tid);
+      stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, xoff),
+                                                       offset_ptr<T>(A.o_lo, xoff), Np, m0, n0,
+                                                       (int)Mp, wm, wn, lane, tid);
     } else if (A.out == O_U || A.out == O_APPLY) {
       if (A.out == O_APPLY && A.status && A.status[0] != 0) return;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int row = rbase + i * 16 + r, col = cbase + j * 16;
             if (row < rows && col < cols) {
               const int64_t e = eoff + (int64_t)row * cols + col;
-              if (A.out == O_U) A.U[e] = v[i][j][r];
-              else apply_one(A.W, A.w_bf16, e, A.eta, v[i][j][r]);
+              if (A.out == O_U) A.U[e] = acc[i][j][r];
+              else apply_one(A.W, A.w_bf16, e, A.eta, acc[i][j][r]);
             }
           }
     } else {
@@ -528,18 +644,18 @@ __global__ __launch_bounds__(128 * WM) void k_gemm(GemmArgs A) {
       // gives 4 rows x 16 columns; two neighbouring tiles give 32 columns.
       const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int jp = 0; jp < 2; ++jp)
+        for (int jp = 0; jp < TJ / 2; ++jp)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            uint64_t m0b = __ballot(v[i][2 * jp][r] < 0.0f);
-            uint64_t m1b = __ballot(v[i][2 * jp + 1][r] < 0.0f);
+            uint64_t m0b = __ballot(acc[i][2 * jp][r] < 0.0f);
+            uint64_t m1b = __ballot(acc[i][2 * jp + 1][r] < 0.0f);
             if (lane < 4) {
               uint32_t w = (uint32_t)((m0b >> (16 * lane)) & 0xFFFFu) |
                            ((uint32_t)((m1b >> (16 * lane)) & 0xFFFFu) << 16);
-              int wrow = m0 + wm * 64 + i * 16 + 4 * lane + r;
-              int wcol = n0 + wn * 64 + jp * 32;
+              int wrow = m0 + wm * WTM + i * 16 + 4 * lane + r;
+              int wcol = n0 + wn * WTN + jp * 32;
               if (wrow < rows && wcol < cols)
                 A.bits[woff + ((int64_t)wrow * cols + wcol) / 32] = w;
             }
@@ -551,35 +667,38 @@ __global__ __launch_bounds__(128 * WM) void k_gemm(GemmArgs A) {
 // ---------------------------------------------------------------------------
 // Host launcher
 // ---------------------------------------------------------------------------
-// Launch configuration: 128x128 tiles, 4 waves, two stages, which lets two
-// blocks share a CU so one block's pipeline fill and epilogue overlap the
-// other's k-loop.  (The kernel also supports 256x128 tiles with 8 waves and
-// three stages; on the Newton-Schulz shapes that measured slower, since one
-// block per CU leaves those phases exposed.)
+// Launch configuration: 128x128 tiles, 4 waves of 64x64, two stages of
+// 128-byte slab rows (64 KB of LDS), so two blocks share a CU and one
+// block's pipeline fill and epilogue overlap the other's k-loop.  (Measured
+// on the Newton-Schulz shapes: 64-byte slab rows with four blocks per CU,
+// and 256x256 tiles with one wave of 128x128 per SIMD, were both slower;
+// they feed the LDS from global memory at a lower rate per CU.)
 template <typename T, int SPLIT, int EPI>
 struct Cfg {
   static constexpr int WM = 2;
+  static constexpr int TI = 4, TJ = 4;
+  static constexpr int RB = 128;
   static constexpr int NSTG = 2;
-  static constexpr int BMT = 64 * WM;
+  static constexpr int WPE = 2;
+  static constexpr int BMT = WM * 16 * TI, BNT = 32 * TJ;
   static constexpr size_t lds() {
-    size_t pipe = (size_t)NSTG * SPLIT * (BMT * ROWB + TILEB);
-    size_t img = (size_t)SPLIT * BMT * (BM * sizeof(T) + 16);
-    size_t raw = (size_t)BMT * (BM * sizeof(float) + 16);  // raw Gram is float32
+    size_t pipe = (size_t)NSTG * SPLIT * (BMT + BNT) * RB;
+    size_t img = (size_t)SPLIT * BMT * (BNT * sizeof(T) + 16);
+    size_t raw = (size_t)BMT * (BNT * sizeof(float) + 16);  // raw Gram is float32
     size_t m = pipe > img ? pipe : img;
-    return m > raw ? m : raw;
+    return EPI == E_RAW && m < raw ? raw : m;
   }
 };
 
-int gemm_update_tile_rows(int precision) {
-  return precision == P_BF16X3 ? Cfg<bf16_t, 2, E_UPDATE>::BMT
-                               : Cfg<bf16_t, 1, E_UPDATE>::BMT;
+int gemm_tile(int /*precision*/, int /*epi*/, int64_t /*gm*/, int64_t /*gn*/) {
+  return Cfg<bf16_t, 1, E_UPDATE>::BMT;
 }
 
 template <typename T, int SPLIT, int EPI>
 static hipError_t launch_one(const GemmArgs& args, hipStream_t s) {
   using C = Cfg<T, SPLIT, EPI>;
-  hipLaunchKernelGGL((k_gemm<T, SPLIT, EPI, C::NSTG, C::WM>), dim3(args.G.total_blocks),
-                     dim3(128 * C::WM), C::lds(), s, args);
+  hipLaunchKernelGGL((k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE>),
+                     dim3(args.G.total_blocks), dim3(128 * C::WM), C::lds(), s, args);
   return hipGetLastError();
 }
 
@@ -595,6 +714,9 @@ static hipError_t launch_epi(const GemmArgs& args, hipStream_t s) {
 
 hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s) {
   if (args.G.total_blocks <= 0) return hipSuccess;
+  const int tile = Cfg<bf16_t, 1, E_UPDATE>::BMT;
+  for (int i = 0; i < args.G.n; ++i)
+    if (args.G.g[i].tile != tile || args.G.g[i].gk % 128) return hipErrorInvalidValue;
   if (precision == P_F32) return launch_epi<float, 1>(args, s);
   if (precision == P_BF16X3) return launch_epi<bf16_t, 2>(args, s);
   return launch_epi<bf16_t, 1>(args, s);
@@ -603,8 +725,9 @@ hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s) {
 template <typename T, int SPLIT, int EPI>
 static hipError_t set_lds() {
   using C = Cfg<T, SPLIT, EPI>;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<T, SPLIT, EPI, C::NSTG, C::WM>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::lds());
+  return hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::lds());
 }
 template <typename T, int SPLIT>
 static hipError_t set_lds_all() {

@@ -16,6 +16,10 @@ __host__ __device__ inline int gemm_ops(int a_fam, int b_fam) {
 
 enum Epi { E_RAW = 0, E_OP = 1, E_SQUARE = 2, E_UPDATE = 3 };
 enum Out { O_X = 0, O_U = 1, O_BITS = 2, O_APPLY = 3 };
+
+// Source of the update's a X term on the first Newton-Schulz step: the
+// caller's float32 matrix (XS_USER, full precision) or the bf16/f32 operand
+// tiles as they pass through LDS (XS_OP).
 enum XSrc { XS_USER = 0, XS_OP = 1 };
 
 struct GemmArgs {
@@ -31,7 +35,6 @@ struct GemmArgs {
   const void* sq_hi; const void* sq_lo;   // E_SQUARE: A for the b*A term
   const float* scal;               // per-matrix c = 1/(s+eps) or NULL
   const float* xs_user;            // XS_USER: float32 source in caller layout
-  const void* xs_hi; const void* xs_lo;   // XS_OP: padded operand source
   float* U;                        // O_U
   uint32_t* bits;                  // O_BITS (buffer of the local worker)
   void* W; int32_t w_bf16; float eta;   // O_APPLY
@@ -40,8 +43,9 @@ struct GemmArgs {
 
 hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s);
 hipError_t gemm_set_attributes();
-// Rows of the update GEMM's block tile for a precision (128 or 256).
-int gemm_update_tile_rows(int precision);
+// Square block tile (128 or 256) of a GEMM with output gm x gn; every
+// group of one launch must carry the same tile in Group::tile.
+int gemm_tile(int precision, int epi, int64_t gm, int64_t gn);
 
 // ---- elementwise and small kernels (sm_elementwise.hip) ----
 hipError_t launch_momentum_flat(const float* G, const void* W, int w_bf16,
