@@ -276,7 +276,6 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   constexpr int BK = RB / sizeof(T);           // k per slab
   static_assert(QA >= 1 && QB >= 1 && NKK >= 1, "tile / slab shape");
   static_assert(EPI == E_UPDATE || BMT == BNT, "symmetric outputs use square tiles");
-  static_assert(TI == TJ, "square wave tiles");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -428,29 +427,31 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     constexpr int u = decltype(uc)::value;
     const int kb = ax_k0 + u * 16 - s * BK;
     if (ax_wide) {
-      // X^T rows n, 4 consecutive k = m: one 8- (bf16) or 16-byte (f32) read
-      const int kk = kb + 4 * (lane >> 4);
+      if constexpr (u < TI) {
+        // X^T rows n, 4 consecutive k = m: one 8- (bf16) or 16-byte (f32) read
+        const int kk = kb + 4 * (lane >> 4);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int row = wn * WTN + j * 16 + (lane & 15);
-        const int off = lds_off<RB>(row, kk / P) + (kk % P) * (int)sizeof(T);
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TJ; ++j) {
+          const int row = wn * WTN + j * 16 + (lane & 15);
+          const int off = lds_off<RB>(row, kk / P) + (kk % P) * (int)sizeof(T);
+          float x[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int sp = 0; sp < SPLIT; ++sp) {
-          const char* p = b_tile(stg, sp) + off;
-          if constexpr (sizeof(T) == 4) {
-            f32x4_t v = *reinterpret_cast<const f32x4_t*>(p);
-            x[0] += v[0]; x[1] += v[1]; x[2] += v[2]; x[3] += v[3];
-          } else {
-            u32x2_t h = *reinterpret_cast<const u32x2_t*>(p);
-            x[0] += __uint_as_float(h[0] << 16); x[1] += __uint_as_float(h[0] & 0xFFFF0000u);
-            x[2] += __uint_as_float(h[1] << 16); x[3] += __uint_as_float(h[1] & 0xFFFF0000u);
+          for (int sp = 0; sp < SPLIT; ++sp) {
+            const char* p = b_tile(stg, sp) + off;
+            if constexpr (sizeof(T) == 4) {
+              f32x4_t v = *reinterpret_cast<const f32x4_t*>(p);
+              x[0] += v[0]; x[1] += v[1]; x[2] += v[2]; x[3] += v[3];
+            } else {
+              u32x2_t h = *reinterpret_cast<const u32x2_t*>(p);
+              x[0] += __uint_as_float(h[0] << 16); x[1] += __uint_as_float(h[0] & 0xFFFF0000u);
+              x[2] += __uint_as_float(h[1] << 16); x[3] += __uint_as_float(h[1] & 0xFFFF0000u);
+            }
           }
-        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[u][j][r] += A.ca * x[r];
+          for (int r = 0; r < 4; ++r) acc[u][j][r] += A.ca * x[r];
+        }
       }
-    } else {
+    } else if constexpr (u < TJ) {
       // X rows m (4 consecutive rows), one k = n each: element reads
       const int kk = kb + (lane & 15);
 #pragma unroll
@@ -471,12 +472,19 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     }
   };
   // every 16-wide k-block of the a X term that lies in slab s
+  constexpr int NU = TI > TJ ? TI : TJ;
+  const int ax_nu = ax_wide ? TI : TJ;
   auto add_ax = [&](int s, int stg) {
-    static_assert(TI == 4, "a X blocks");
-    if ((ax_k0 + 0) / BK == s) add_ax_block(std::integral_constant<int, 0>{}, s, stg);
-    if ((ax_k0 + 16) / BK == s) add_ax_block(std::integral_constant<int, 1>{}, s, stg);
-    if ((ax_k0 + 32) / BK == s) add_ax_block(std::integral_constant<int, 2>{}, s, stg);
-    if ((ax_k0 + 48) / BK == s) add_ax_block(std::integral_constant<int, 3>{}, s, stg);
+    static_assert(NU <= 8, "a X blocks");
+    auto one = [&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u < NU)
+        if (u < ax_nu && (ax_k0 + 16 * u) / BK == s) add_ax_block(uc, s, stg);
+    };
+    one(std::integral_constant<int, 0>{}); one(std::integral_constant<int, 1>{});
+    one(std::integral_constant<int, 2>{}); one(std::integral_constant<int, 3>{});
+    one(std::integral_constant<int, 4>{}); one(std::integral_constant<int, 5>{});
+    one(std::integral_constant<int, 6>{}); one(std::integral_constant<int, 7>{});
   };
 
   constexpr int LOADS = SPLIT * (QA + QB);     // vector loads per thread per slab
@@ -521,23 +529,25 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     if (s + NSTG - 1 < nslab) issue(s + NSTG - 1);
 
     const int stg = s % NSTG;
-    // frags [kk][split][i] (A: TI tiles, B: TJ tiles)
-    u32x4_t fa[NKK][SPLIT * TI], fb[NKK][SPLIT * TJ];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
+    // fragments [kk][split * TI + i] (A) and [kk][split * TJ + j] (B)
+    auto read_frags = [&](u32x4_t (&fa)[SPLIT * TI], u32x4_t (&fb)[SPLIT * TJ], int kk) {
 #pragma unroll
       for (int sp = 0; sp < SPLIT; ++sp) {
 #pragma unroll
         for (int i = 0; i < TI; ++i)
-          fa[kk][sp * TI + i] =
+          fa[sp * TI + i] =
               *reinterpret_cast<const u32x4_t*>(a_tile(stg, sp) + fa_off[kk] + i * 16 * RB);
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
-          fb[kk][sp * TJ + j] =
+          fb[sp * TJ + j] =
               *reinterpret_cast<const u32x4_t*>(b_tile(stg, sp) + fb_off[kk] + j * 16 * RB);
       }
-    // keep every fragment read of the slab ahead of the MFMAs, so the waits
+    };
+    // every fragment read of the slab ahead of the MFMAs, so the waits
     // before them count down outstanding reads instead of draining them
+    u32x4_t fa[NKK][SPLIT * TI], fb[NKK][SPLIT * TJ];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) read_frags(fa[kk], fb[kk], kk);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
@@ -548,7 +558,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     if constexpr (EPI == E_UPDATE) {
       // after the slab's MFMAs, when the fragment registers are free again
       __builtin_amdgcn_sched_barrier(0);
-      if (!ax_user && s * BK < ax_k0 + 16 * TI && ax_k0 < (s + 1) * BK) add_ax(s, stg);
+      if (!ax_user && s * BK < ax_k0 + 16 * ax_nu && ax_k0 < (s + 1) * BK) add_ax(s, stg);
     }
   }
 
@@ -670,9 +680,11 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
 // Launch configuration: 128x128 tiles, 4 waves of 64x64, two stages of
 // 128-byte slab rows (64 KB of LDS), so two blocks share a CU and one
 // block's pipeline fill and epilogue overlap the other's k-loop.  (Measured
-// on the Newton-Schulz shapes: 64-byte slab rows with four blocks per CU,
-// and 256x256 tiles with one wave of 128x128 per SIMD, were both slower;
-// they feed the LDS from global memory at a lower rate per CU.)
+// on the Newton-Schulz shapes, where the outputs are only 768 wide: 64-byte
+// slab rows with four blocks per CU, and 256x256 tiles with 4 waves of
+// 128x128 or 8 waves of 64x128 and one block per CU, were all slower; the
+// large tiles leave too few blocks per launch and expose each block's fill
+// and epilogue.)
 template <typename T, int SPLIT, int EPI>
 struct Cfg {
   static constexpr int WM = 2;
@@ -689,10 +701,10 @@ struct Cfg {
     return EPI == E_RAW && m < raw ? raw : m;
   }
 };
+constexpr int kTile = Cfg<bf16_t, 1, E_UPDATE>::BMT;
+static_assert(Cfg<bf16_t, 1, E_UPDATE>::BNT == kTile, "square tile");
 
-int gemm_tile(int /*precision*/, int /*epi*/, int64_t /*gm*/, int64_t /*gn*/) {
-  return Cfg<bf16_t, 1, E_UPDATE>::BMT;
-}
+int gemm_tile(int /*precision*/, int /*epi*/, int64_t /*gm*/, int64_t /*gn*/) { return kTile; }
 
 template <typename T, int SPLIT, int EPI>
 static hipError_t launch_one(const GemmArgs& args, hipStream_t s) {
@@ -714,9 +726,8 @@ static hipError_t launch_epi(const GemmArgs& args, hipStream_t s) {
 
 hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s) {
   if (args.G.total_blocks <= 0) return hipSuccess;
-  const int tile = Cfg<bf16_t, 1, E_UPDATE>::BMT;
   for (int i = 0; i < args.G.n; ++i)
-    if (args.G.g[i].tile != tile || args.G.g[i].gk % 128) return hipErrorInvalidValue;
+    if (args.G.g[i].tile != kTile || args.G.g[i].gk % 128) return hipErrorInvalidValue;
   if (precision == P_F32) return launch_epi<float, 1>(args, s);
   if (precision == P_BF16X3) return launch_epi<bf16_t, 2>(args, s);
   return launch_epi<bf16_t, 1>(args, s);

@@ -43,8 +43,8 @@ struct GemmArgs {
 
 hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s);
 hipError_t gemm_set_attributes();
-// Square block tile (128 or 256) of a GEMM with output gm x gn; every
-// group of one launch must carry the same tile in Group::tile.
+// Square block tile of a GEMM with output gm x gn; every group of one
+// launch must carry the same tile in Group::tile.
 int gemm_tile(int precision, int epi, int64_t gm, int64_t gn);
 
 // ---- elementwise and small kernels (sm_elementwise.hip) ----
