@@ -96,10 +96,6 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
   for (int pp = 0; pp < (ns ? 2 : 1); ++pp) {
     P.off_x[pp][0] = take(x * opb);
     if (split) P.off_x[pp][1] = take(x * opb);
-    if (ns) {
-      P.off_xt[pp][0] = take(x * opb);
-      if (split) P.off_xt[pp][1] = take(x * opb);
-    }
   }
   if (ns) {
     P.off_b[0] = take(r2 * opb);
@@ -218,7 +214,6 @@ struct Bufs {
   char* base;
   int32_t* status;
   void* x[2][2];
-  void* xt[2][2];
   void* b[2];
   void* a[2];
   float* araw;
@@ -237,7 +232,6 @@ Bufs bind(const Plan& P, void* ws) {
   for (int p = 0; p < 2; ++p)
     for (int h = 0; h < 2; ++h) {
       B.x[p][h] = at(P.off_x[p][h]);
-      B.xt[p][h] = at(P.off_xt[p][h]);
     }
   B.b[0] = at(P.off_b[0]); B.b[1] = at(P.off_b[1]);
   B.a[0] = at(P.off_a[0]); B.a[1] = at(P.off_a[1]);
@@ -277,7 +271,7 @@ hipError_t mark(sm_profile* prof, int kind, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // PolarNS pipeline over all matrices of a plan, starting from the padded
-// operand copies in x[0] / xt[0] with partial sums in part (Frobenius).
+// operand copies in x[0] with partial sums in part (Frobenius).
 //   first: XS_USER (the first a X term from src_user, the caller's float32
 //   source, e.g. the momentum) or XS_OP (from the operand copy, e.g. the
 //   majority matrix, whose entries the operand holds exactly).
@@ -323,7 +317,7 @@ sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
     g.gm = g.gn = (int32_t)q.Rp;
     g.gk = (int32_t)(q.tall ? q.Mp : q.Np);
     set_gemm_tiles(g, prec, P.spectral ? E_RAW : E_OP);
-    g.ops = q.tall ? gemm_ops(FAM_XT, FAM_XT) : gemm_ops(FAM_X, FAM_X);
+    g.ops = gemm_ops(FAM_X, FAM_X);   // S S^T
     return true;
   };
   if (!P.spectral) {
@@ -340,7 +334,6 @@ sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
       std::memset(&a, 0, sizeof(a));
       a.G = G;
       a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
-      a.xt_hi = B.xt[0][0]; a.xt_lo = B.xt[0][1];
       a.epi = E_OP; a.mul = gram_mul; a.scal = B.scal; a.scal_pow = 2;
       a.o_hi = dst_hi; a.o_lo = dst_lo;
       return launch_gemm(prec, a, s);
@@ -352,7 +345,6 @@ sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
       std::memset(&a, 0, sizeof(a));
       a.G = G;
       a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
-      a.xt_hi = B.xt[0][0]; a.xt_lo = B.xt[0][1];
       a.epi = E_RAW; a.o_raw = B.araw;
       return launch_gemm(prec, a, s);
     }));
@@ -423,14 +415,13 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
         g.gm = g.gn = (int32_t)q.Rp;
         g.gk = (int32_t)(q.tall ? q.Mp : q.Np);
         set_gemm_tiles(g, prec, E_OP);
-        g.ops = q.tall ? gemm_ops(FAM_XT, FAM_XT) : gemm_ops(FAM_X, FAM_X);
+        g.ops = gemm_ops(FAM_X, FAM_X);   // S S^T
         return true;
       }, [&](const Groups& G) {
         GemmArgs a;
         std::memset(&a, 0, sizeof(a));
         a.G = G;
         a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
-        a.xt_hi = B.xt[cur][0]; a.xt_lo = B.xt[cur][1];
         a.epi = E_OP; a.mul = P.quintic ? 1.0f : hp->ns_b; a.scal_pow = 0;
         a.o_hi = P.quintic ? B.a[0] : B.b[0];
         a.o_lo = P.quintic ? B.a[1] : B.b[1];
@@ -442,7 +433,7 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
       HIP_TRY(run_square(P, mp, groups, hp, B, s));
       HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
     }
-    // update: X <- a X + B X (wide) / a X + X B (tall)
+    // update: S <- a S + B S
     const bool last = k == K;
     for (int pass = 0; pass < 2; ++pass) {
       // pass 0: matrices using the requested final output; pass 1: the
@@ -452,17 +443,16 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
       HIP_TRY(for_launches(groups, [&](Group& g) {
         const MatPlan& q = mp[g.idx0];
         if (last && io.final_out == O_BITS && fusable[g.idx0] != (pass == 0)) return false;
-        g.gm = (int32_t)q.Mp; g.gn = (int32_t)q.Np;
+        g.gm = (int32_t)q.Rp; g.gn = (int32_t)(q.tall ? q.Mp : q.Np);
         g.gk = (int32_t)q.Rp;
         set_gemm_tiles(g, prec, E_UPDATE);
-        g.ops = q.tall ? gemm_ops(FAM_X, FAM_R) : gemm_ops(FAM_R, FAM_XT);
+        g.ops = gemm_ops(FAM_R, FAM_XK);
         return true;
       }, [&](const Groups& G) {
         GemmArgs a;
         std::memset(&a, 0, sizeof(a));
         a.G = G;
         a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
-        a.xt_hi = B.xt[cur][0]; a.xt_lo = B.xt[cur][1];
         a.r_hi = B.b[0]; a.r_lo = B.b[1];
         a.epi = E_UPDATE; a.ca = hp->ns_a;
         a.xsrc = k == 1 ? io.first_xsrc : XS_OP;
@@ -471,7 +461,6 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
         if (!last) {
           a.out = O_X;
           a.o_hi = B.x[cur ^ 1][0]; a.o_lo = B.x[cur ^ 1][1];
-          a.ot_hi = B.xt[cur ^ 1][0]; a.ot_lo = B.xt[cur ^ 1][1];
         } else if (io.final_out == O_BITS && pass == 1) {
           a.out = O_U; a.U = B.u;
         } else {
@@ -597,8 +586,6 @@ sm_status signmuon_polar_ns(const float* X, float* U, int64_t rows, int64_t cols
   std::memset(&sw, 0, sizeof(sw));
   sw.ema = 0; sw.precision = P.precision; sw.src = X;
   sw.o_hi = B.x[0][0]; sw.o_lo = B.x[0][1]; sw.part = B.part;
-  sw.ot_hi = B.xt[0][0]; sw.ot_lo = B.xt[0][1];
-  if (hp->K == 0) sw.ot_hi = sw.ot_lo = nullptr;
   HIP_TRY(for_launches(groups, [&](Group& g) {
     g.blocks_per_mat = (int32_t)(mp[g.idx0].Mp * mp[g.idx0].Np / 4096);
     return true;
@@ -732,7 +719,6 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
       sw.beta = hp->beta; sw.lam = hp->lambda;
       sw.Gr = G; sw.W = W; sw.Mom = Mom;
       sw.o_hi = B.x[0][0]; sw.o_lo = B.x[0][1];
-      sw.ot_hi = B.xt[0][0]; sw.ot_lo = B.xt[0][1];
       sw.part = P.spectral ? nullptr : B.part;
       sw.status = B.status;
       HIP_TRY(for_launches(groups, [&](Group& g) {
@@ -788,15 +774,6 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   HIP_TRY(for_launches(groups, vote_fill, [&](const Groups& Gs) {
     va.G = Gs; return launch_vote_groups(va, stream);
   }));
-  if (hp->K > 0) {
-    HIP_TRY(for_launches(groups, [&](Group& g) {
-      g.blocks_per_mat = (int32_t)(mp[g.idx0].Mp * mp[g.idx0].Np / 4096);
-      return true;
-    }, [&](const Groups& Gs) {
-      return launch_transpose_op(Gs, P.precision, B.x[0][0], B.x[0][1], B.xt[0][0],
-                                 B.xt[0][1], stream);
-    }));
-  }
   HIP_TRY(mark(prof, SM_PHASE_VOTE, stream));
   io.first_xsrc = XS_OP; io.src_user = nullptr;
   io.final_out = O_APPLY;

@@ -300,8 +300,9 @@ hipError_t launch_apply_flat(void* W, int w_bf16, const int8_t* D,
 
 // ---------------------------------------------------------------------------
 // Padded sweep over 64x64 tiles of the padded matrix: momentum (or a plain
-// float32 source) -> padded operand copy X and its transpose X^T, partial
-// sums of squares per tile, non-finite flag.
+// float32 source) -> padded operand copy S (X, or X^T for a tall matrix,
+// transposed through LDS), partial sums of squares per tile, non-finite
+// flag.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void store_op4v(int precision, void* hi, void* lo,
                                            int64_t i, const float (&v)[4]) {
@@ -323,17 +324,18 @@ __device__ __forceinline__ void store_op4v(int precision, void* hi, void* lo,
         u32x2_t{(uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16)};
 }
 
-// Phase 2 of a tile: write the transpose of the 64x64 tile held in LDS.
+// Write the transpose of the 64x64 tile held in LDS (rows r0.., columns
+// c0.. of X) into S = X^T with row length ld.
 __device__ __forceinline__ void write_tile_t(const float (*tile)[65], int precision,
-                                             void* t_hi, void* t_lo, int64_t xoff,
-                                             int64_t Mp, int r0, int c0) {
+                                             void* hi, void* lo, int64_t xoff,
+                                             int64_t ld, int r0, int c0) {
   const int cc = threadIdx.x >> 2, rr0 = (threadIdx.x & 3) * 16;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = tile[rr0 + 4 * k + e][cc];
-    store_op4v(precision, t_hi, t_lo, xoff + (int64_t)(c0 + cc) * Mp + r0 + rr0 + 4 * k, v);
+    store_op4v(precision, hi, lo, xoff + (int64_t)(c0 + cc) * ld + r0 + rr0 + 4 * k, v);
   }
 }
 
@@ -344,6 +346,7 @@ __global__ __launch_bounds__(256) void k_sweep(SweepArgs a) {
   const Group& g = a.G.g[gi];
   const int rows = g.rows, cols = g.cols;
   const int64_t Mp = round_up(rows, kPad), Np = round_up(cols, kPad);
+  const bool tall = s_tall(g);
   const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
   const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
   const int tiles_c = (int)(Np / 64);
@@ -413,7 +416,7 @@ __global__ __launch_bounds__(256) void k_sweep(SweepArgs a) {
                !__builtin_isfinite(v[k]);
       }
       ss += v[k] * v[k];
-      tile[lr0 + 16 * p][lc + k] = v[k];
+      if (tall) tile[lr0 + 16 * p][lc + k] = v[k];
     }
     if (a.ema) {
       if (full[p]) {
@@ -424,10 +427,12 @@ __global__ __launch_bounds__(256) void k_sweep(SweepArgs a) {
           if (row < rows && col + k < cols) a.Mom[u + k] = v[k];
       }
     }
-    store_op4v(a.precision, a.o_hi, a.o_lo, xoff + (int64_t)row * Np + col, v);
+    if (!tall) store_op4v(a.precision, a.o_hi, a.o_lo, xoff + (int64_t)row * Np + col, v);
   }
-  __syncthreads();
-  if (a.ot_hi) write_tile_t(tile, a.precision, a.ot_hi, a.ot_lo, xoff, Mp, r0, c0);
+  if (tall) {
+    __syncthreads();
+    write_tile_t(tile, a.precision, a.o_hi, a.o_lo, xoff, Mp, r0, c0);
+  }
   if (bad && a.status) a.status[0] = 1;
   if (a.part) {
     float t = block_sum(ss);
@@ -438,38 +443,6 @@ __global__ __launch_bounds__(256) void k_sweep(SweepArgs a) {
 hipError_t launch_sweep(const SweepArgs& a, hipStream_t s) {
   if (a.G.total_blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_sweep, dim3(a.G.total_blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-// Transposed copy X -> X^T of padded operand copies, 64x64 tiles.
-__global__ __launch_bounds__(256) void k_transpose_op(Groups G, int precision,
-                                                      const void* hi, const void* lo,
-                                                      void* t_hi, void* t_lo) {
-  __shared__ float tile[64][65];
-  int gi, mi, q;
-  group_of_block(G, blockIdx.x, gi, mi, q);
-  const Group& g = G.g[gi];
-  const int64_t Mp = round_up(g.rows, kPad), Np = round_up(g.cols, kPad);
-  const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
-  const int tiles_c = (int)(Np / 64);
-  const int r0 = (q / tiles_c) * 64, c0 = (q % tiles_c) * 64;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int lr = (threadIdx.x >> 4) + 16 * p, lc = (threadIdx.x & 15) * 4;
-    const int64_t o = xoff + (int64_t)(r0 + lr) * Np + c0 + lc;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) tile[lr][lc + k] = load_opv(precision, hi, lo, o + k);
-  }
-  __syncthreads();
-  write_tile_t(tile, precision, t_hi, t_lo, xoff, Mp, r0, c0);
-}
-
-hipError_t launch_transpose_op(const Groups& G, int precision, const void* hi,
-                               const void* lo, void* t_hi, void* t_lo,
-                               hipStream_t s) {
-  if (G.total_blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_transpose_op, dim3(G.total_blocks), dim3(256), 0, s, G,
-                     precision, hi, lo, t_hi, t_lo);
   return hipGetLastError();
 }
 
@@ -590,10 +563,11 @@ __global__ __launch_bounds__(256) void k_vote_groups(VoteArgs a) {
                       (float)majority(vote_sum_at<NB>(c, a.M, b), a.tie));
       }
     } else {
-      // VA_SBAR: majority matrix into the padded operand copy
+      // VA_SBAR: majority matrix into the padded operand copy S (a tall
+      // matrix is written transposed, one element at a time)
       const int64_t Np = round_up(cols, kPad);
       const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
-      if (cols % 32 == 0) {
+      if (cols % 32 == 0 && !s_tall(g)) {
         int row = (int)(e0 / cols), col = (int)(e0 - (int64_t)row * cols);
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
@@ -611,7 +585,7 @@ __global__ __launch_bounds__(256) void k_vote_groups(VoteArgs a) {
           int row = (int)(e / cols), col = (int)(e - (int64_t)row * cols);
           float v = (float)majority(vote_sum_at<NB>(c, a.M, b), a.tie);
           ss += v * v;
-          store_opv(a.precision, a.o_hi, a.o_lo, xoff + (int64_t)row * Np + col, v);
+          store_opv(a.precision, a.o_hi, a.o_lo, xoff + s_index(g, row, col), v);
         }
       }
     }
@@ -635,20 +609,21 @@ hipError_t launch_vote_groups(const VoteArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Zero the padding of padded operand copies (padded sweep layout).
+// Zero the padding of padded operand copies S.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_zero_pad(Groups G, int precision,
                                                   void* hi, void* lo) {
   int gi, mi, q;
   group_of_block(G, blockIdx.x, gi, mi, q);
   const Group& g = G.g[gi];
-  const int64_t Np = round_up(g.cols, kPad);
+  const int sr = s_rows(g), sc = s_cols(g);
+  const int64_t ld = round_up(sc, kPad);
   const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
   const int64_t p = (int64_t)q * kChunk + threadIdx.x * 8;
-  const int row = (int)(p / Np), col = (int)(p - (int64_t)row * Np);
+  const int row = (int)(p / ld), col = (int)(p - (int64_t)row * ld);
 #pragma unroll
   for (int k = 0; k < 8; ++k)
-    if (row >= g.rows || col + k >= g.cols) store_opv(precision, hi, lo, xoff + p + k, 0.0f);
+    if (row >= sr || col + k >= sc) store_opv(precision, hi, lo, xoff + p + k, 0.0f);
 }
 
 hipError_t launch_zero_pad(const Groups& G, int precision, void* hi, void* lo,
@@ -811,7 +786,6 @@ __global__ __launch_bounds__(256) void k_scaled_out(ScaledOutArgs a) {
   const int64_t mn = (int64_t)g.rows * g.cols;
   const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
   const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
-  const int64_t Np = round_up(g.cols, kPad);
   const float c = a.scal[g.idx0 + mi * g.idx_stride];
   for (int k = 0; k < 8; ++k) {
     int64_t e = (int64_t)q * kChunk + k * 256 + threadIdx.x;
@@ -819,7 +793,7 @@ __global__ __launch_bounds__(256) void k_scaled_out(ScaledOutArgs a) {
     float x;
     if (a.from_op) {
       int64_t row = e / g.cols, col = e - row * g.cols;
-      x = load_opv(a.precision, a.x_hi, a.x_lo, xoff + row * Np + col);
+      x = load_opv(a.precision, a.x_hi, a.x_lo, xoff + s_index(g, row, col));
     } else {
       x = a.x_user[eoff + e];
     }

@@ -1,22 +1,26 @@
 // Batched matrix-core GEMM for the Newton-Schulz products of PolarNS
-// (SignMuon paper, section 4, Newton-Schulz paragraph): the Gram matrix
-// A = X X^T (X^T X for a tall X), the quintic square A*A, and the update
-// a X + B X (X B for a tall X), with the epilogues that finish each step.
+// (SignMuon paper, section 4, Newton-Schulz paragraph).  Each iterate is
+// kept as S, its short side as rows (S = X, or X^T for a tall X), so the
+// products are the Gram matrix A = S S^T, the quintic square A*A, and the
+// update a S + B S, with the epilogues that finish each step.
 //
 // One launch covers every matrix of a parameter set (up to kMaxGroups runs
 // of same-shaped matrices).  Each block owns a 128x128 output tile and runs
 // 4 waves (2x2), each wave a 64x64 sub-tile built from 16x16 MFMA tiles:
 //   bf16 / split-bf16: v_mfma_f32_16x16x32_bf16
 //   f32:               v_mfma_f32_16x16x4_f32
-// Every operand is read k-contiguous (the iterate is kept both as X and as
-// X^T), so each 128-byte k-slab of a 128-row operand tile is fetched with
-// global_load_lds_dwordx4 straight into LDS: lane l of a wave writes the 16
-// bytes at the wave's LDS base + 16 l, and the XOR swizzle of 16-byte chunks
-// (against bank conflicts of the fragment reads) is applied by permuting
-// which global chunk each lane fetches.  NSTG LDS stages form the prefetch
-// pipeline; completion is tracked with explicit vmcnt waits and a bare
-// s_barrier.  All operand copies are zero padded to multiples of 128, so no
-// load is predicated and padding contributes exact zeros.
+// Each k-slab of an operand tile is fetched with global_load_lds_dwordx4
+// straight into LDS: lane l of a wave writes the 16 bytes at the wave's LDS
+// base + 16 l, and the XOR swizzles of the LDS layouts (against bank
+// conflicts of the fragment reads) are applied by permuting which global
+// bytes each lane fetches.  Operands with k along their rows (S for the
+// Gram, B for the update) land as 128-byte slab rows and are read with
+// 16-byte loads; the update's S operand has k down its columns, lands as
+// k-rows and is read with the transposing LDS load (ds_read_b64_tr_b16),
+// so no transposed copy of S is ever stored.  NSTG LDS stages form the
+// prefetch pipeline; completion is tracked with explicit vmcnt waits and a
+// bare s_barrier.  All operand copies are zero padded to multiples of 128,
+// so no load is predicated and padding contributes exact zeros.
 #include <type_traits>
 
 #include "sm_internal.h"
@@ -70,6 +74,55 @@ constexpr bool slab_layout_ok() {
 }
 static_assert(slab_layout_ok<64>() && slab_layout_ok<128>(), "LDS slab swizzle");
 
+// k-major operand tiles (an X block with k down its columns): LDS row = k
+// within the slab, 128 * sizeof(T) bytes per row (the 128 output rows or
+// columns of the tile), 32-byte chunks XOR-swizzled by row bits 0, 1 and 3.
+// The 16 lanes of a transposing fragment read cover 4 consecutive rows of
+// one chunk, and lane groups 16 apart read rows 8 apart; both then land in
+// distinct bank groups.  The swizzle ignores row bit 2, so the second read
+// of a fragment (4 rows down) is a constant offset away.
+__host__ __device__ constexpr int km_swz(int row) { return (row & 3) ^ (((row >> 3) & 1) << 2); }
+template <typename T>
+__host__ __device__ constexpr int km_off(int row, int byte) {
+  return row * (128 * (int)sizeof(T)) + ((((byte >> 5) ^ km_swz(row)) << 5) | (byte & 31));
+}
+// Checks: a bijection of each row's chunks, and for the transposing read
+// (lane j of a 16-lane group at row r0 + j/4, byte c*32 + 8*(j%4)) 16
+// distinct 8-byte slots in 128 bytes, with lane groups 8 rows apart in the
+// other half of 256 bytes.
+constexpr bool km_layout_ok() {
+  for (int r0 = 0; r0 < 64; r0 += 4)
+    for (int c = 0; c < 8; ++c) {
+      unsigned seen = 0, seen2 = 0;
+      for (int j = 0; j < 16; ++j) {
+        const int o = km_off<bf16_t>(r0 + j / 4, c * 32 + 8 * (j % 4));
+        const int slot = (o % 128) / 8;
+        if (seen & (1u << slot)) return false;
+        seen |= 1u << slot;
+        if (km_off<bf16_t>(r0 + 4 + j / 4, c * 32 + 8 * (j % 4)) != o + 4 * 256) {
+          if ((r0 & 4) == 0) return false;
+        }
+        const int o8 = km_off<bf16_t>((r0 ^ 8) + j / 4, c * 32 + 8 * (j % 4));
+        if ((o8 % 256) / 128 == (o % 256) / 128) return false;
+        seen2 |= 1u << ((o8 % 128) / 8);
+      }
+      if (seen2 != 0xFFFFu) return false;
+    }
+  return true;
+}
+static_assert(km_layout_ok(), "k-major LDS swizzle");
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i receives element i % 4 of the 8 bytes addressed by lane
+// 4 e + i / 4, for e = 0..3 (16-bit elements).
+__device__ __forceinline__ u32x2_t lds_read_tr16(const char* p) {
+  i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(__attribute__((address_space(3))) char*)p);
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>
@@ -88,9 +141,7 @@ __device__ __forceinline__ int64_t fam_off(const Group& g, int fam, int mi) {
                       : g.x0 + (int64_t)mi * g.x_stride;
 }
 __device__ __forceinline__ int64_t fam_ld(const Group& g, int fam) {
-  if (fam == FAM_X) return round_up(g.cols, kPad);
-  if (fam == FAM_XT) return round_up(g.rows, kPad);
-  return round_up(g.rows < g.cols ? g.rows : g.cols, kPad);
+  return round_up(fam == FAM_R ? s_rows(g) : s_cols(g), kPad);
 }
 
 // ---------------------------------------------------------------------------
@@ -305,9 +356,9 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     while (rem >= g.tiles_n - tm) { rem -= g.tiles_n - tm; ++tm; }
     tn = tm + rem;
   } else if (a_fam == FAM_R) {
-    // the small operand (B = b X X^T) is the A side: consecutive tiles walk
-    // down m, so the tiles that share one X^T block run together on one XCD
-    // and fetch it from HBM once
+    // the small operand (B = b S S^T) is the A side: consecutive tiles walk
+    // down m, so the tiles that share one column block of S run together on
+    // one XCD and fetch it from HBM once
     const int tiles_m = (g.gm + BMT - 1) / BMT;
     tn = t / tiles_m;
     tm = t - tn * tiles_m;
@@ -317,10 +368,11 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   }
   const int m0 = tm * BMT, n0 = tn * BNT;
   const int64_t lda = fam_ld(g, a_fam), ldb = fam_ld(g, b_fam);
-  const void* a_hi = a_fam == FAM_X ? A.x_hi : (a_fam == FAM_XT ? A.xt_hi : A.r_hi);
-  const void* b_hi = b_fam == FAM_X ? A.x_hi : (b_fam == FAM_XT ? A.xt_hi : A.r_hi);
-  const void* a_lo = a_fam == FAM_X ? A.x_lo : (a_fam == FAM_XT ? A.xt_lo : A.r_lo);
-  const void* b_lo = b_fam == FAM_X ? A.x_lo : (b_fam == FAM_XT ? A.xt_lo : A.r_lo);
+  const bool a_km = a_fam == FAM_XK, b_km = b_fam == FAM_XK;
+  const void* a_hi = a_fam == FAM_R ? A.r_hi : A.x_hi;
+  const void* b_hi = b_fam == FAM_R ? A.r_hi : A.x_hi;
+  const void* a_lo = a_fam == FAM_R ? A.r_lo : A.x_lo;
+  const void* b_lo = b_fam == FAM_R ? A.r_lo : A.x_lo;
   const T* a_src[SPLIT];
   const T* b_src[SPLIT];
   a_src[0] = reinterpret_cast<const T*>(a_hi) + fam_off(g, a_fam, mi);
@@ -330,36 +382,71 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     b_src[SPLIT - 1] = reinterpret_cast<const T*>(b_lo) + fam_off(g, b_fam, mi);
   }
 
-  // Per-lane source offsets of the loads per operand and slab: the A load q
-  // of wave w fills LDS rows (QA w+q)*RPI .. +RPI-1 (B: (QB w+q)*RPI ..);
-  // lane l writes row ..+l/CPR at chunk position l%CPR, so it fetches global
-  // chunk (l%CPR) ^ swz(row).  Rows past the operand (a ragged last tile)
-  // read its last row instead; their results are never stored.
+  // Per-lane source offsets of the loads per operand and slab; load q of
+  // wave w fills the 1 KB piece c = QA w + q (B: QB w + q) of the tile and
+  // lane l writes its bytes 16 l .. 16 l + 15.
+  //  k along rows: LDS rows c*RPI .. +RPI-1; lane l writes row ..+l/CPR at
+  //   chunk position l%CPR, so it fetches global chunk (l%CPR) ^ swz(row).
+  //   Rows past the operand (a ragged last tile) read its last row instead;
+  //   their results are never stored.
+  //  k-major: LDS rows (k) c*RPK .. +RPK-1 of 128 * sizeof(T) bytes; lane l
+  //   writes 16 bytes of row ..+l/LPR, fetched from the swizzled position.
+  constexpr int RPK = 1024 / (128 * (int)sizeof(T));  // k-major rows per load
+  constexpr int LPR = 128 * (int)sizeof(T) / 16;      // lanes per k-major row
+  static_assert(BMT == 128 && BNT == 128, "k-major tiles are 128 wide");
+  auto dma_off = [&](bool km, int c, int mn0, int lim, int64_t ld) -> int64_t {
+    if (km) {
+      const int row = c * RPK + lane / LPR;
+      const int pb = (lane % LPR) * 16;                 // physical byte in the row
+      const int lb = (((pb >> 5) ^ km_swz(row)) << 5) | (pb & 31);
+      return (int64_t)row * ld + mn0 + lb / (int)sizeof(T);
+    }
+    const int row = c * RPI + lane / CPR;
+    const int ch = (lane % CPR) ^ swz<RB>(row);
+    const int r = mn0 + row < lim ? mn0 + row : lim - 1;
+    return (int64_t)r * ld + ch * P;
+  };
   int64_t aoff[QA], boff[QB];
 #pragma unroll
-  for (int q = 0; q < QA; ++q) {
-    int row = (wave * QA + q) * RPI + lane / CPR;
-    int ch = (lane % CPR) ^ swz<RB>(row);
-    int arow = m0 + row < g.gm ? m0 + row : g.gm - 1;
-    aoff[q] = (int64_t)arow * lda + ch * P;
-  }
+  for (int q = 0; q < QA; ++q) aoff[q] = dma_off(a_km, wave * QA + q, m0, g.gm, lda);
 #pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    int row = (wave * QB + q) * RPI + lane / CPR;
-    int ch = (lane % CPR) ^ swz<RB>(row);
-    int brow = n0 + row < g.gn ? n0 + row : g.gn - 1;
-    boff[q] = (int64_t)brow * ldb + ch * P;
-  }
-  // Per-lane LDS offsets of the fragment reads: row within the tile and
-  // 16-byte chunk (kk*4 + lane/16) of the slab row.  The swizzle depends
-  // on row bits that i*16 does not touch, so one offset per kk serves all
-  // i (j) with a constant stride.
+  for (int q = 0; q < QB; ++q) boff[q] = dma_off(b_km, wave * QB + q, n0, g.gn, ldb);
+  // elements between consecutive slabs
+  const int64_t a_kst = a_km ? (int64_t)BK * lda : BK, b_kst = b_km ? (int64_t)BK * ldb : BK;
+
+  // Per-lane LDS offsets of the fragment reads (k along rows): row within
+  // the tile and 16-byte chunk (kk*4 + lane/16) of the slab row.  The
+  // swizzle depends on row bits that i*16 does not touch, so one offset per
+  // kk serves all i (j) with a constant stride.
   int fa_off[NKK], fb_off[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     fa_off[kk] = lds_off<RB>(wm * WTM + (lane & 15), kk * 4 + (lane >> 4));
     fb_off[kk] = lds_off<RB>(wn * WTN + (lane & 15), kk * 4 + (lane >> 4));
   }
+  // A fragment of a k-major tile: MFMA tile columns c0 .. c0+15, k-step kk.
+  //  bf16: two transposing reads, rows kk*32 + 8 (lane/16) + (lane%16)/4 and
+  //   4 rows down, bytes 2 c0 + 8 (lane % 4): lane l gets k = 8 (l/16) .. +7
+  //   of column c0 + l % 16, the MFMA operand layout.
+  //  float32: the 16x16x4 MFMA takes k = 4 (kk*4 + l/16) + e, e = 0..3, of
+  //   column c0 + l % 16 in register e (as the k-along-rows reads).
+  auto km_frag = [&](const char* tile, int c0, int kk) -> u32x4_t {
+    if constexpr (sizeof(T) == 2) {
+      const int row = kk * 32 + 8 * (lane >> 4) + ((lane & 15) >> 2);
+      const int off = km_off<T>(row, 2 * c0 + 8 * (lane & 3));
+      const u32x2_t lo4 = lds_read_tr16(tile + off);
+      const u32x2_t hi4 = lds_read_tr16(tile + off + 4 * 128 * (int)sizeof(T));
+      return u32x4_t{lo4[0], lo4[1], hi4[0], hi4[1]};
+    } else {
+      u32x4_t v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 4 * (kk * 4 + (lane >> 4)) + e;
+        v[e] = *reinterpret_cast<const uint32_t*>(tile + km_off<T>(row, 4 * (c0 + (lane & 15))));
+      }
+      return v;
+    }
+  };
 
   const int nslab = g.gk / BK;
 
@@ -370,18 +457,17 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   };
   auto issue = [&](int s) {
     const int st = s % NSTG;
-    const int64_t k0 = (int64_t)s * BK;
 #pragma unroll
     for (int sp = 0; sp < SPLIT; ++sp) {
       char* ta = a_tile(st, sp) + wave * QA * 1024;
       char* tb = b_tile(st, sp) + wave * QB * 1024;
 #pragma unroll
       for (int q = 0; q < QA; ++q)
-        __builtin_amdgcn_global_load_lds((const void*)(a_src[sp] + aoff[q] + k0),
+        __builtin_amdgcn_global_load_lds((const void*)(a_src[sp] + aoff[q] + s * a_kst),
                                          (lds_void*)(ta + q * 1024), 16, 0, 0);
 #pragma unroll
       for (int q = 0; q < QB; ++q)
-        __builtin_amdgcn_global_load_lds((const void*)(b_src[sp] + boff[q] + k0),
+        __builtin_amdgcn_global_load_lds((const void*)(b_src[sp] + boff[q] + s * b_kst),
                                          (lds_void*)(tb + q * 1024), 16, 0, 0);
     }
   };
@@ -389,24 +475,44 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   f32x4_t acc[TI][TJ];
   const bool ax_user = EPI == E_UPDATE && A.xsrc == XS_USER;
   if (ax_user) {
-    // first step: a X from the caller's float32 source (rows past the
+    // first step: a X from the caller's float32 source (entries past the
     // matrix are zero), loaded ahead of the k-loop
+    // ((i, j) of S is (j, i) of a tall X; addresses are clamped into the
+    // matrix so that every load is issued unconditionally and all of them
+    // overlap; out-of-range entries are replaced by zero afterwards)
     const int rb = m0 + wm * WTM + 4 * (lane >> 4), cb = n0 + wn * WTN + (lane & 15);
     const int64_t eo = g.elem0 + (int64_t)mi * g.elem_stride;
-    // (addresses clamped into the matrix so that every load is issued
-    // unconditionally and all of them overlap; out-of-range entries are
-    // replaced by zero afterwards)
+    const int sr = s_rows(g), sc = s_cols(g);
+    const bool tall = s_tall(g);
+    if (tall && g.vec_ok && g.cols % 4 == 0) {
+      // the 4 registers of a tile are 4 consecutive entries of a row of X:
+      // one 16-byte load (sr = cols is a multiple of 4, so a group of 4 is
+      // either inside the matrix or wholly past it)
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
+        for (int j = 0; j < TJ; ++j) {
+          const int si = rb + i * 16, sj = cb + j * 16;
+          const int ic = si < sr ? si : sr - 4, jc = sj < sc ? sj : sc - 1;
+          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(A.xs_user + eo + (int64_t)jc * g.cols + ic);
+          const bool in = si < sr && sj < sc;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = rb + i * 16 + r, col = cb + j * 16;
-          const int rc = row < g.rows ? row : g.rows - 1, cc = col < g.cols ? col : g.cols - 1;
-          const float x = A.xs_user[eo + (int64_t)rc * g.cols + cc];
-          acc[i][j][r] = row < g.rows && col < g.cols ? A.ca * x : 0.0f;
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = in ? A.ca * x[r] : 0.0f;
         }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int si = rb + i * 16 + r, sj = cb + j * 16;
+            const int ic = si < sr ? si : sr - 1, jc = sj < sc ? sj : sc - 1;
+            const int64_t e = tall ? (int64_t)jc * g.cols + ic : (int64_t)ic * g.cols + jc;
+            const float x = A.xs_user[eo + e];
+            acc[i][j][r] = si < sr && sj < sc ? A.ca * x : 0.0f;
+          }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -414,72 +520,47 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Later steps read the update's a X term from the operand tiles in LDS
-  // while they pass through: for a wide X (A = B, B operand = X^T) the slab holding
-  // k = m0 + wm*WTM + i*16 .. +15 of the X^T block contains X(m, n) for this
-  // wave's output rows m and columns n; for a tall X (A operand = X) the
-  // slab holding k = n contains X(m, n).  Each k-block of 16 lies in one slab.
-  const bool ax_wide = a_fam == FAM_R;
-  const int ax_k0 = ax_wide ? m0 + wm * WTM : n0 + wn * WTN;  // first k of the a X block
-  // a X for the 16-wide k-block u (acc row block u for a wide X, column
-  // block u for a tall one) from the stage that holds it.
+  // Later steps read the update's a S term from the B operand tiles in LDS
+  // while they pass through: S is read k-major, and the slab holding
+  // k = m0 + wm*WTM + i*16 .. +15 contains S(m, n) for this wave's output
+  // rows m and columns n.  Each k-block of 16 lies in one slab.
+  const int ax_k0 = m0 + wm * WTM;  // first k of the a S block
+  // a S for the 16-row block u of the wave tile from the stage holding it:
+  // rows k = m, 4 consecutive m of one column n per lane (bf16: one
+  // transposing read per 16 columns; float32: 4 reads)
   auto add_ax_block = [&](auto uc, int s, int stg) {
     constexpr int u = decltype(uc)::value;
     const int kb = ax_k0 + u * 16 - s * BK;
-    if (ax_wide) {
-      if constexpr (u < TI) {
-        // X^T rows n, 4 consecutive k = m: one 8- (bf16) or 16-byte (f32) read
-        const int kk = kb + 4 * (lane >> 4);
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int row = wn * WTN + j * 16 + (lane & 15);
-          const int off = lds_off<RB>(row, kk / P) + (kk % P) * (int)sizeof(T);
-          float x[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TJ; ++j) {
+      const int c0 = wn * WTN + j * 16;
+      float x[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int sp = 0; sp < SPLIT; ++sp) {
-            const char* p = b_tile(stg, sp) + off;
-            if constexpr (sizeof(T) == 4) {
-              f32x4_t v = *reinterpret_cast<const f32x4_t*>(p);
-              x[0] += v[0]; x[1] += v[1]; x[2] += v[2]; x[3] += v[3];
-            } else {
-              u32x2_t h = *reinterpret_cast<const u32x2_t*>(p);
-              x[0] += __uint_as_float(h[0] << 16); x[1] += __uint_as_float(h[0] & 0xFFFF0000u);
-              x[2] += __uint_as_float(h[1] << 16); x[3] += __uint_as_float(h[1] & 0xFFFF0000u);
-            }
-          }
+      for (int sp = 0; sp < SPLIT; ++sp) {
+        const char* tile = b_tile(stg, sp);
+        if constexpr (sizeof(T) == 4) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[u][j][r] += A.ca * x[r];
+          for (int r = 0; r < 4; ++r)
+            x[r] += *reinterpret_cast<const float*>(
+                tile + km_off<T>(kb + 4 * (lane >> 4) + r, 4 * (c0 + (lane & 15))));
+        } else {
+          const u32x2_t h = lds_read_tr16(
+              tile + km_off<T>(kb + 4 * (lane >> 4) + ((lane & 15) >> 2), 2 * c0 + 8 * (lane & 3)));
+          x[0] += __uint_as_float(h[0] << 16); x[1] += __uint_as_float(h[0] & 0xFFFF0000u);
+          x[2] += __uint_as_float(h[1] << 16); x[3] += __uint_as_float(h[1] & 0xFFFF0000u);
         }
       }
-    } else if constexpr (u < TJ) {
-      // X rows m (4 consecutive rows), one k = n each: element reads
-      const int kk = kb + (lane & 15);
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = wm * WTM + i * 16 + 4 * (lane >> 4) + r;
-          const int off = lds_off<RB>(row, kk / P) + (kk % P) * (int)sizeof(T);
-          float x = 0.0f;
-#pragma unroll
-          for (int sp = 0; sp < SPLIT; ++sp) {
-            const char* p = a_tile(stg, sp) + off;
-            if constexpr (sizeof(T) == 4) x += *reinterpret_cast<const float*>(p);
-            else x += bf16_to_f32(*reinterpret_cast<const bf16_t*>(p));
-          }
-          acc[i][u][r] += A.ca * x;
-        }
+      for (int r = 0; r < 4; ++r) acc[u][j][r] += A.ca * x[r];
     }
   };
-  // every 16-wide k-block of the a X term that lies in slab s
-  constexpr int NU = TI > TJ ? TI : TJ;
-  const int ax_nu = ax_wide ? TI : TJ;
+  // every 16-row block of the a S term that lies in slab s
   auto add_ax = [&](int s, int stg) {
-    static_assert(NU <= 8, "a X blocks");
+    static_assert(TI <= 8, "a S blocks");
     auto one = [&](auto uc) {
       constexpr int u = decltype(uc)::value;
-      if constexpr (u < NU)
-        if (u < ax_nu && (ax_k0 + 16 * u) / BK == s) add_ax_block(uc, s, stg);
+      if constexpr (u < TI)
+        if ((ax_k0 + 16 * u) / BK == s) add_ax_block(uc, s, stg);
     };
     one(std::integral_constant<int, 0>{}); one(std::integral_constant<int, 1>{});
     one(std::integral_constant<int, 2>{}); one(std::integral_constant<int, 3>{});
@@ -533,14 +614,24 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     auto read_frags = [&](u32x4_t (&fa)[SPLIT * TI], u32x4_t (&fb)[SPLIT * TJ], int kk) {
 #pragma unroll
       for (int sp = 0; sp < SPLIT; ++sp) {
+        if (a_km) {
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
-          fa[sp * TI + i] =
-              *reinterpret_cast<const u32x4_t*>(a_tile(stg, sp) + fa_off[kk] + i * 16 * RB);
+          for (int i = 0; i < TI; ++i) fa[sp * TI + i] = km_frag(a_tile(stg, sp), wm * WTM + 16 * i, kk);
+        } else {
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          fb[sp * TJ + j] =
-              *reinterpret_cast<const u32x4_t*>(b_tile(stg, sp) + fb_off[kk] + j * 16 * RB);
+          for (int i = 0; i < TI; ++i)
+            fa[sp * TI + i] =
+                *reinterpret_cast<const u32x4_t*>(a_tile(stg, sp) + fa_off[kk] + i * 16 * RB);
+        }
+        if (b_km) {
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) fb[sp * TJ + j] = km_frag(b_tile(stg, sp), wn * WTN + 16 * j, kk);
+        } else {
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            fb[sp * TJ + j] =
+                *reinterpret_cast<const u32x4_t*>(b_tile(stg, sp) + fb_off[kk] + j * 16 * RB);
+        }
       }
     };
     // every fragment read of the slab ahead of the MFMAs, so the waits
@@ -558,22 +649,24 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     if constexpr (EPI == E_UPDATE) {
       // after the slab's MFMAs, when the fragment registers are free again
       __builtin_amdgcn_sched_barrier(0);
-      if (!ax_user && s * BK < ax_k0 + 16 * ax_nu && ax_k0 < (s + 1) * BK) add_ax(s, stg);
+      if (!ax_user && s * BK < ax_k0 + 16 * TI && ax_k0 < (s + 1) * BK) add_ax(s, stg);
     }
   }
 
   // ---- epilogue.  acc[i][j][r] holds C(row, col) with
   //   row = m0 + wm*WTM + i*16 + 4*(lane/16) + r,  col = n0 + wn*WTN + j*16 + lane%16
   // i.e. the 4 registers of a tile are 4 consecutive rows of one column.
+  // For the update C is the new S: (row, col) of S is (col, row) of a tall X.
   const int idx = g.idx0 + mi * g.idx_stride;
   const float cs = A.scal ? A.scal[idx] : 1.0f;
   const int rows = g.rows, cols = g.cols;
+  const int sr = s_rows(g), sc = s_cols(g);
+  const bool tall = s_tall(g);
   const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
   const int64_t roff = g.r0 + (int64_t)mi * g.r_stride;
   const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
-  const int64_t Mp = round_up(rows, kPad);
-  const int64_t Np = round_up(cols, kPad);
-  const int64_t Rp = round_up(rows < cols ? rows : cols, kPad);
+  const int64_t Rp = round_up(sr, kPad);   // rows of S (padded)
+  const int64_t Cp = round_up(sc, kPad);   // columns of S (padded)
   const int rbase = m0 + wm * WTM + 4 * (lane >> 4);
   const int cbase = n0 + wn * WTN + (lane & 15);
   // every wave is done reading the operand stages: LDS is free for staging
@@ -621,18 +714,9 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       for (int j = 0; j < TJ; ++j) acc[i][j] *= gam;
 
     if (A.out == O_X) {
-      // X^T rows directly (4 consecutive entries per tile), X rows via LDS
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-        if (rbase + i * 16 < Mp) {
-#pragma unroll
-          for (int j = 0; j < TJ; ++j)
-            store_acc4<T, SPLIT>(A.ot_hi, A.ot_lo,
-                                 xoff + (int64_t)(cbase + j * 16) * Mp + rbase + i * 16, acc[i][j]);
-        }
       stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, xoff),
-                                                       offset_ptr<T>(A.o_lo, xoff), Np, m0, n0,
-                                                       (int)Mp, wm, wn, lane, tid);
+                                                       offset_ptr<T>(A.o_lo, xoff), Cp, m0, n0,
+                                                       (int)Rp, wm, wn, lane, tid);
     } else if (A.out == O_U || A.out == O_APPLY) {
       if (A.out == O_APPLY && A.status && A.status[0] != 0) return;
 #pragma unroll
@@ -641,35 +725,62 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int row = rbase + i * 16 + r, col = cbase + j * 16;
-            if (row < rows && col < cols) {
-              const int64_t e = eoff + (int64_t)row * cols + col;
+            const int si = rbase + i * 16 + r, sj = cbase + j * 16;
+            if (si < sr && sj < sc) {
+              const int64_t e = eoff + (tall ? (int64_t)sj * cols + si : (int64_t)si * cols + sj);
               if (A.out == O_U) A.U[e] = acc[i][j][r];
               else apply_one(A.W, A.w_bf16, e, A.eta, acc[i][j][r]);
             }
           }
     } else {
-      // O_BITS: entrywise sign packed into 32-bit words (cols % 32 == 0).
-      // For a 16x16 MFMA tile and accumulator register r, a wave ballot
-      // gives 4 rows x 16 columns; two neighbouring tiles give 32 columns.
+      // O_BITS: entrywise sign packed into 32-bit words along the rows of
+      // X (cols % 32 == 0).
       const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
+      if (!tall) {
+        // S = X: for a 16x16 MFMA tile and accumulator register r, a wave
+        // ballot gives 4 rows x 16 columns; two neighbouring tiles give 32.
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int jp = 0; jp < TJ / 2; ++jp)
+          for (int jp = 0; jp < TJ / 2; ++jp)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            uint64_t m0b = __ballot(acc[i][2 * jp][r] < 0.0f);
-            uint64_t m1b = __ballot(acc[i][2 * jp + 1][r] < 0.0f);
-            if (lane < 4) {
-              uint32_t w = (uint32_t)((m0b >> (16 * lane)) & 0xFFFFu) |
-                           ((uint32_t)((m1b >> (16 * lane)) & 0xFFFFu) << 16);
-              int wrow = m0 + wm * WTM + i * 16 + 4 * lane + r;
-              int wcol = n0 + wn * WTN + jp * 32;
-              if (wrow < rows && wcol < cols)
-                A.bits[woff + ((int64_t)wrow * cols + wcol) / 32] = w;
+            for (int r = 0; r < 4; ++r) {
+              uint64_t m0b = __ballot(acc[i][2 * jp][r] < 0.0f);
+              uint64_t m1b = __ballot(acc[i][2 * jp + 1][r] < 0.0f);
+              if (lane < 4) {
+                uint32_t w = (uint32_t)((m0b >> (16 * lane)) & 0xFFFFu) |
+                             ((uint32_t)((m1b >> (16 * lane)) & 0xFFFFu) << 16);
+                int wrow = m0 + wm * WTM + i * 16 + 4 * lane + r;
+                int wcol = n0 + wn * WTN + jp * 32;
+                if (wrow < rows && wcol < cols)
+                  A.bits[woff + ((int64_t)wrow * cols + wcol) / 32] = w;
+              }
             }
+      } else {
+        // S = X^T: a row of X is a column of S, so a word collects the signs
+        // of 32 consecutive rows of S (two row tiles i) in one column.  Bit
+        // 16 ii + 4 g + r of the word of column c comes from ballot (ii, r),
+        // lane 16 g + c % 16.
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int ip = 0; ip < TI / 2; ++ip) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const uint64_t mb = __ballot(acc[2 * ip + ii][j][r] < 0.0f);
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                  w |= (uint32_t)((mb >> (16 * gq + (lane & 15))) & 1u) << (16 * ii + 4 * gq + r);
+              }
+            const int xrow = n0 + wn * WTN + j * 16 + (lane & 15);   // column of S
+            const int xcol = m0 + wm * WTM + ip * 32;                 // row of S
+            if (lane < 16 && xrow < rows && xcol < cols)
+              A.bits[woff + ((int64_t)xrow * cols + xcol) / 32] = w;
           }
+      }
     }
   }
 }

@@ -62,6 +62,19 @@ __host__ __device__ inline int64_t round_up(int64_t x, int64_t m) {
 #define SM_DEV __host__ __device__ inline
 #endif
 
+// Storage of the Newton-Schulz iterate: every matrix is kept as S with its
+// short side as rows (S = X when rows <= cols, S = X^T for a tall X),
+// zero padded to multiples of kPad.  Every Gram is then S S^T with k along
+// the rows of S and every update is S <- a S + B S.
+SM_DEV bool s_tall(const Group& g) { return g.rows > g.cols; }
+SM_DEV int s_rows(const Group& g) { return g.rows > g.cols ? g.cols : g.rows; }
+SM_DEV int s_cols(const Group& g) { return g.rows > g.cols ? g.rows : g.cols; }
+// Offset in the padded S of the caller-layout element (row, col).
+SM_DEV int64_t s_index(const Group& g, int64_t row, int64_t col) {
+  const int64_t ld = round_up(s_cols(g), kPad);
+  return g.rows > g.cols ? col * ld + row : row * ld + col;
+}
+
 // Locate the group and matrix of a block: linear scan over <= kMaxGroups.
 __device__ __forceinline__ int find_group(const Groups& G, int b) {
   int gi = 0;
@@ -110,7 +123,6 @@ struct Plan {
   int64_t x_total = 0, r_total = 0, v_total = 0, c_total = 0;
   // workspace byte offsets (0 = absent)
   size_t off_x[2][2] = {{0, 0}, {0, 0}};  // [pingpong][hi/lo] (or f32 in [p][0])
-  size_t off_xt[2][2] = {{0, 0}, {0, 0}}; // transposed copies, same shape
   size_t off_b[2] = {0, 0};   // Newton-Schulz right/left factor B (hi/lo)
   size_t off_a[2] = {0, 0};   // quintic: A (hi/lo)
   size_t off_araw = 0;        // spectral: raw float32 Gram

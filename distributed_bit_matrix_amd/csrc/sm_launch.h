@@ -5,10 +5,12 @@
 
 namespace sm {
 
-// Operand families of the batched GEMM, all read k-contiguous: the padded
-// copy of X (Mp x Np, row length Np), its transpose (Np x Mp, row length Mp)
-// and the padded Gram-sized buffers (Rp x Rp).
-enum { FAM_X = 0, FAM_XT = 1, FAM_R = 2 };
+// Operand families of the batched GEMM: the padded copy of X (Mp x Np, row
+// length Np) read with k along its rows (FAM_X) or with k down its columns
+// (FAM_XK: the LDS tile holds k as rows and the fragments are read with the
+// transposing LDS load), and the padded Gram-sized buffers (Rp x Rp, FAM_R,
+// k along rows).
+enum { FAM_X = 0, FAM_XK = 1, FAM_R = 2 };
 // Group.ops: A-operand family in bits 0-1, B-operand family in bits 2-3.
 __host__ __device__ inline int gemm_ops(int a_fam, int b_fam) {
   return a_fam | (b_fam << 2);
@@ -25,12 +27,10 @@ enum XSrc { XS_USER = 0, XS_OP = 1 };
 struct GemmArgs {
   Groups G;
   const void* x_hi; const void* x_lo;   // FAM_X operand buffers
-  const void* xt_hi; const void* xt_lo; // FAM_XT operand buffers
   const void* r_hi; const void* r_lo;   // FAM_R operand buffers
   int32_t epi, out, xsrc, scal_pow;
   float mul, ca, cb, cc;
   void* o_hi; void* o_lo;          // E_OP / E_SQUARE (R family), O_X (X family)
-  void* ot_hi; void* ot_lo;        // O_X: transposed copy (XT family)
   float* o_raw;                    // E_RAW
   const void* sq_hi; const void* sq_lo;   // E_SQUARE: A for the b*A term
   const float* scal;               // per-matrix c = 1/(s+eps) or NULL
@@ -61,7 +61,7 @@ hipError_t launch_apply_flat(void* W, int w_bf16, const int8_t* D,
                              hipStream_t s);
 
 // Padded sweep over 64x64 tiles: writes the padded operand copy of each
-// matrix and its transpose (and the partial sums of squares per tile).
+// matrix (and the partial sums of squares per tile).
 // ema = 1: Mom <- beta Mom + (1-beta)(G + lam W) first (G, W, Mom in caller
 // layout), else the source is `src` (caller layout, float32).
 struct SweepArgs {
@@ -70,7 +70,6 @@ struct SweepArgs {
   float beta, lam;
   const float* src; const float* Gr; const void* W; float* Mom;
   void* o_hi; void* o_lo;
-  void* ot_hi; void* ot_lo;
   float* part;          // partial sums per chunk, NULL to skip
   int32_t* status;      // non-finite flag, NULL to skip
 };
@@ -99,11 +98,6 @@ struct VoteArgs {
   const int32_t* status;
 };
 hipError_t launch_vote_groups(const VoteArgs& a, hipStream_t s);
-
-// Transposed copy of padded operand copies (64x64 tiles).
-hipError_t launch_transpose_op(const Groups& G, int precision, const void* hi,
-                               const void* lo, void* t_hi, void* t_lo,
-                               hipStream_t s);
 
 // Zero the padding of the padded operand copies.
 hipError_t launch_zero_pad(const Groups& G, int precision, void* hi, void* lo,
