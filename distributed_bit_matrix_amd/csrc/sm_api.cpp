@@ -295,10 +295,11 @@ struct NsIO {
 // tiles along n and the blocks per matrix (upper-triangular tiles of a
 // symmetric output).
 void set_gemm_tiles(Group& g, int prec, int epi) {
-  const int tile = gemm_tile(prec, epi, g.gm, g.gn);
-  g.tile = tile;
-  g.tiles_n = (g.gn + tile - 1) / tile;
-  const int tiles_m = (g.gm + tile - 1) / tile;
+  int tm, tn;
+  gemm_tile(prec, epi, g.gm, g.gn, &tm, &tn);
+  g.tile = tn;
+  g.tiles_n = (g.gn + tn - 1) / tn;
+  const int tiles_m = (g.gm + tm - 1) / tm;
   g.blocks_per_mat = epi == E_UPDATE ? tiles_m * g.tiles_n : g.tiles_n * (g.tiles_n + 1) / 2;
 }
 

@@ -75,16 +75,16 @@ constexpr bool slab_layout_ok() {
 static_assert(slab_layout_ok<64>() && slab_layout_ok<128>(), "LDS slab swizzle");
 
 // k-major operand tiles (an X block with k down its columns): LDS row = k
-// within the slab, 128 * sizeof(T) bytes per row (the 128 output rows or
-// columns of the tile), 32-byte chunks XOR-swizzled by row bits 0, 1 and 3.
+// within the slab, W * sizeof(T) bytes per row (the W output rows or columns
+// of the tile), 32-byte chunks XOR-swizzled by row bits 0, 1 and 3.
 // The 16 lanes of a transposing fragment read cover 4 consecutive rows of
 // one chunk, and lane groups 16 apart read rows 8 apart; both then land in
 // distinct bank groups.  The swizzle ignores row bit 2, so the second read
 // of a fragment (4 rows down) is a constant offset away.
 __host__ __device__ constexpr int km_swz(int row) { return (row & 3) ^ (((row >> 3) & 1) << 2); }
-template <typename T>
+template <typename T, int W = 128>
 __host__ __device__ constexpr int km_off(int row, int byte) {
-  return row * (128 * (int)sizeof(T)) + ((((byte >> 5) ^ km_swz(row)) << 5) | (byte & 31));
+  return row * (W * (int)sizeof(T)) + ((((byte >> 5) ^ km_swz(row)) << 5) | (byte & 31));
 }
 // Checks: a bijection of each row's chunks, and for the transposing read
 // (lane j of a 16-lane group at row r0 + j/4, byte c*32 + 8*(j%4)) 16
@@ -389,14 +389,13 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   //   chunk position l%CPR, so it fetches global chunk (l%CPR) ^ swz(row).
   //   Rows past the operand (a ragged last tile) read its last row instead;
   //   their results are never stored.
-  //  k-major: LDS rows (k) c*RPK .. +RPK-1 of 128 * sizeof(T) bytes; lane l
-  //   writes 16 bytes of row ..+l/LPR, fetched from the swizzled position.
-  constexpr int RPK = 1024 / (128 * (int)sizeof(T));  // k-major rows per load
-  constexpr int LPR = 128 * (int)sizeof(T) / 16;      // lanes per k-major row
-  static_assert(BMT == 128 && BNT == 128, "k-major tiles are 128 wide");
-  auto dma_off = [&](bool km, int c, int mn0, int lim, int64_t ld) -> int64_t {
+  //  k-major (tile width W): LDS rows (k) c*RPK .. +RPK-1 of W * sizeof(T)
+  //   bytes, RPK = 1024 / (W * sizeof(T)); lane l writes 16 bytes of row
+  //   ..+l/LPR (LPR lanes per row), fetched from the swizzled position.
+  auto dma_off = [&](bool km, int c, int mn0, int lim, int64_t ld, int W) -> int64_t {
     if (km) {
-      const int row = c * RPK + lane / LPR;
+      const int rowb = W * (int)sizeof(T), LPR = rowb / 16;
+      const int row = c * (1024 / rowb) + lane / LPR;
       const int pb = (lane % LPR) * 16;                 // physical byte in the row
       const int lb = (((pb >> 5) ^ km_swz(row)) << 5) | (pb & 31);
       return (int64_t)row * ld + mn0 + lb / (int)sizeof(T);
@@ -408,9 +407,9 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   };
   int64_t aoff[QA], boff[QB];
 #pragma unroll
-  for (int q = 0; q < QA; ++q) aoff[q] = dma_off(a_km, wave * QA + q, m0, g.gm, lda);
+  for (int q = 0; q < QA; ++q) aoff[q] = dma_off(a_km, wave * QA + q, m0, g.gm, lda, BMT);
 #pragma unroll
-  for (int q = 0; q < QB; ++q) boff[q] = dma_off(b_km, wave * QB + q, n0, g.gn, ldb);
+  for (int q = 0; q < QB; ++q) boff[q] = dma_off(b_km, wave * QB + q, n0, g.gn, ldb, BNT);
   // elements between consecutive slabs
   const int64_t a_kst = a_km ? (int64_t)BK * lda : BK, b_kst = b_km ? (int64_t)BK * ldb : BK;
 
@@ -430,19 +429,20 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   //   of column c0 + l % 16, the MFMA operand layout.
   //  float32: the 16x16x4 MFMA takes k = 4 (kk*4 + l/16) + e, e = 0..3, of
   //   column c0 + l % 16 in register e (as the k-along-rows reads).
-  auto km_frag = [&](const char* tile, int c0, int kk) -> u32x4_t {
+  auto km_frag = [&](auto wc, const char* tile, int c0, int kk) -> u32x4_t {
+    constexpr int W = decltype(wc)::value;
     if constexpr (sizeof(T) == 2) {
       const int row = kk * 32 + 8 * (lane >> 4) + ((lane & 15) >> 2);
-      const int off = km_off<T>(row, 2 * c0 + 8 * (lane & 3));
+      const int off = km_off<T, W>(row, 2 * c0 + 8 * (lane & 3));
       const u32x2_t lo4 = lds_read_tr16(tile + off);
-      const u32x2_t hi4 = lds_read_tr16(tile + off + 4 * 128 * (int)sizeof(T));
+      const u32x2_t hi4 = lds_read_tr16(tile + off + 4 * W * (int)sizeof(T));
       return u32x4_t{lo4[0], lo4[1], hi4[0], hi4[1]};
     } else {
       u32x4_t v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 4 * (kk * 4 + (lane >> 4)) + e;
-        v[e] = *reinterpret_cast<const uint32_t*>(tile + km_off<T>(row, 4 * (c0 + (lane & 15))));
+        v[e] = *reinterpret_cast<const uint32_t*>(tile + km_off<T, W>(row, 4 * (c0 + (lane & 15))));
       }
       return v;
     }
@@ -542,10 +542,10 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             x[r] += *reinterpret_cast<const float*>(
-                tile + km_off<T>(kb + 4 * (lane >> 4) + r, 4 * (c0 + (lane & 15))));
+                tile + km_off<T, BNT>(kb + 4 * (lane >> 4) + r, 4 * (c0 + (lane & 15))));
         } else {
           const u32x2_t h = lds_read_tr16(
-              tile + km_off<T>(kb + 4 * (lane >> 4) + ((lane & 15) >> 2), 2 * c0 + 8 * (lane & 3)));
+              tile + km_off<T, BNT>(kb + 4 * (lane >> 4) + ((lane & 15) >> 2), 2 * c0 + 8 * (lane & 3)));
           x[0] += __uint_as_float(h[0] << 16); x[1] += __uint_as_float(h[0] & 0xFFFF0000u);
           x[2] += __uint_as_float(h[1] << 16); x[3] += __uint_as_float(h[1] & 0xFFFF0000u);
         }
@@ -616,7 +616,9 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       for (int sp = 0; sp < SPLIT; ++sp) {
         if (a_km) {
 #pragma unroll
-          for (int i = 0; i < TI; ++i) fa[sp * TI + i] = km_frag(a_tile(stg, sp), wm * WTM + 16 * i, kk);
+          for (int i = 0; i < TI; ++i)
+            fa[sp * TI + i] =
+                km_frag(std::integral_constant<int, BMT>{}, a_tile(stg, sp), wm * WTM + 16 * i, kk);
         } else {
 #pragma unroll
           for (int i = 0; i < TI; ++i)
@@ -625,7 +627,9 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
         }
         if (b_km) {
 #pragma unroll
-          for (int j = 0; j < TJ; ++j) fb[sp * TJ + j] = km_frag(b_tile(stg, sp), wn * WTN + 16 * j, kk);
+          for (int j = 0; j < TJ; ++j)
+            fb[sp * TJ + j] =
+                km_frag(std::integral_constant<int, BNT>{}, b_tile(stg, sp), wn * WTN + 16 * j, kk);
         } else {
 #pragma unroll
           for (int j = 0; j < TJ; ++j)
@@ -788,20 +792,25 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
 // ---------------------------------------------------------------------------
 // Host launcher
 // ---------------------------------------------------------------------------
-// Launch configuration: 128x128 tiles, 4 waves of 64x64, two stages of
-// 128-byte slab rows (64 KB of LDS), so two blocks share a CU and one
-// block's pipeline fill and epilogue overlap the other's k-loop.  (Measured
-// on the Newton-Schulz shapes, where the outputs are only 768 wide: 64-byte
-// slab rows with four blocks per CU, and 256x256 tiles with 4 waves of
-// 128x128 or 8 waves of 64x128 and one block per CU, were all slower; the
-// large tiles leave too few blocks per launch and expose each block's fill
-// and epilogue.)
-template <typename T, int SPLIT, int EPI>
+// Launch configurations.
+//   128x128 tiles, 4 waves of 64x64, two stages of 128-byte slab rows
+//   (64 KB of LDS), so two blocks share a CU and one block's pipeline fill
+//   and epilogue overlap the other's k-loop.  (Measured on the
+//   Newton-Schulz shapes, where the outputs are only 768 wide: 64-byte slab
+//   rows with four blocks per CU, and 256x256 tiles with one block per CU,
+//   were all slower.)
+//   Wide update (bf16, columns a multiple of 256): 128x256 tiles, 4 waves of
+//   64x128, three stages of 64-byte slab rows (72 KB), still two blocks per
+//   CU; per output it moves a quarter fewer operand bytes from L2 into LDS.
+#ifndef SM_GEMM_WIDE_UPDATE
+#define SM_GEMM_WIDE_UPDATE 1
+#endif
+template <typename T, int SPLIT, int EPI, bool WIDE = false>
 struct Cfg {
   static constexpr int WM = 2;
-  static constexpr int TI = 4, TJ = 4;
-  static constexpr int RB = 128;
-  static constexpr int NSTG = 2;
+  static constexpr int TI = 4, TJ = WIDE ? 8 : 4;
+  static constexpr int RB = WIDE ? 64 : 128;
+  static constexpr int NSTG = WIDE ? 3 : 2;
   static constexpr int WPE = 2;
   static constexpr int BMT = WM * 16 * TI, BNT = 32 * TJ;
   static constexpr size_t lds() {
@@ -812,14 +821,22 @@ struct Cfg {
     return EPI == E_RAW && m < raw ? raw : m;
   }
 };
+using CfgWide = Cfg<bf16_t, 1, E_UPDATE, true>;
 constexpr int kTile = Cfg<bf16_t, 1, E_UPDATE>::BMT;
 static_assert(Cfg<bf16_t, 1, E_UPDATE>::BNT == kTile, "square tile");
+static_assert(CfgWide::BMT == kTile, "wide tiles keep the row height");
 
-int gemm_tile(int /*precision*/, int /*epi*/, int64_t /*gm*/, int64_t /*gn*/) { return kTile; }
+void gemm_tile(int precision, int epi, int64_t gm, int64_t gn, int* tm, int* tn) {
+  *tm = kTile;
+  *tn = kTile;
+  if (SM_GEMM_WIDE_UPDATE && epi == E_UPDATE && precision == P_BF16 && gm % kTile == 0 &&
+      gn % CfgWide::BNT == 0)
+    *tn = CfgWide::BNT;
+}
 
-template <typename T, int SPLIT, int EPI>
+template <typename T, int SPLIT, int EPI, bool WIDE = false>
 static hipError_t launch_one(const GemmArgs& args, hipStream_t s) {
-  using C = Cfg<T, SPLIT, EPI>;
+  using C = Cfg<T, SPLIT, EPI, WIDE>;
   hipLaunchKernelGGL((k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE>),
                      dim3(args.G.total_blocks), dim3(128 * C::WM), C::lds(), s, args);
   return hipGetLastError();
@@ -837,16 +854,24 @@ static hipError_t launch_epi(const GemmArgs& args, hipStream_t s) {
 
 hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s) {
   if (args.G.total_blocks <= 0) return hipSuccess;
-  for (int i = 0; i < args.G.n; ++i)
-    if (args.G.g[i].tile != kTile || args.G.g[i].gk % 128) return hipErrorInvalidValue;
+  // every group of a launch carries the same column tile (the host splits
+  // launches by it)
+  const int tile = args.G.g[0].tile;
+  for (int i = 0; i < args.G.n; ++i) {
+    const Group& g = args.G.g[i];
+    int tm, tn;
+    gemm_tile(precision, args.epi, g.gm, g.gn, &tm, &tn);
+    if (g.tile != tile || g.gk % 128 || g.tile != tn) return hipErrorInvalidValue;
+  }
+  if (tile == CfgWide::BNT) return launch_one<bf16_t, 1, E_UPDATE, true>(args, s);
   if (precision == P_F32) return launch_epi<float, 1>(args, s);
   if (precision == P_BF16X3) return launch_epi<bf16_t, 2>(args, s);
   return launch_epi<bf16_t, 1>(args, s);
 }
 
-template <typename T, int SPLIT, int EPI>
+template <typename T, int SPLIT, int EPI, bool WIDE = false>
 static hipError_t set_lds() {
-  using C = Cfg<T, SPLIT, EPI>;
+  using C = Cfg<T, SPLIT, EPI, WIDE>;
   return hipFuncSetAttribute(
       reinterpret_cast<const void*>(&k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::lds());
@@ -864,7 +889,8 @@ hipError_t gemm_set_attributes() {
   hipError_t e;
   if ((e = set_lds_all<bf16_t, 1>()) != hipSuccess) return e;
   if ((e = set_lds_all<bf16_t, 2>()) != hipSuccess) return e;
-  return set_lds_all<float, 1>();
+  if ((e = set_lds_all<float, 1>()) != hipSuccess) return e;
+  return set_lds<bf16_t, 1, E_UPDATE, true>();
 }
 
 }  // namespace sm

@@ -40,7 +40,7 @@ struct Group {
   int32_t tiles_n;        // GEMM tiles along n
   int32_t ops;            // GEMM operand flags (sm_launch.h OPS_*)
   int32_t vec_ok;         // flat offsets allow 16-byte vector access
-  int32_t tile;           // GEMM block tile (square), shared by a launch
+  int32_t tile;           // GEMM block tile width (columns), shared by a launch
 };
 
 struct Groups {
