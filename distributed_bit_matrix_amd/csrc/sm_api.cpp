@@ -479,6 +479,94 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
   return SM_OK;
 }
 
+// ---------------------------------------------------------------------------
+// PolarNS of all groups as up to kChains independent chains (pre-scale and
+// the K Newton-Schulz steps of a subset of the groups each), run on
+// internal streams forked from and joined back into the caller's stream.
+// A chain's launches depend only on its own matrices, so the GPU runs the
+// chains side by side and one chain's next launch fills the tail of
+// another's.  With one group everything runs on the caller's stream.
+// ---------------------------------------------------------------------------
+constexpr int kChains = 4;
+struct ChainRes {
+  hipStream_t s[kChains];
+  hipEvent_t fork, join[kChains];
+  hipError_t err = hipSuccess;
+  std::mutex mu;   // one enqueue at a time per device
+};
+ChainRes g_chain[64];
+std::once_flag g_chain_once[64];
+
+hipError_t chain_resources(ChainRes** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  ChainRes& R = g_chain[dev];
+  std::call_once(g_chain_once[dev], [&] {
+    for (int c = 0; c < kChains && R.err == hipSuccess; ++c)
+      R.err = hipStreamCreateWithFlags(&R.s[c], hipStreamNonBlocking);
+    if (R.err == hipSuccess) R.err = hipEventCreateWithFlags(&R.fork, hipEventDisableTiming);
+    for (int c = 0; c < kChains && R.err == hipSuccess; ++c)
+      R.err = hipEventCreateWithFlags(&R.join[c], hipEventDisableTiming);
+  });
+  *out = &R;
+  return R.err;
+}
+
+sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
+                    const std::vector<Group>& groups, const std::vector<bool>& fusable,
+                    const sm_hparams* hp, Bufs& B, const NsIO& io, int part_kind,
+                    hipStream_t s) {
+  const int nc = (int)std::min<size_t>(kChains, groups.size());
+  if (nc <= 1) {
+    sm_status st = run_pre_scale(P, mp, groups, hp, B, io, part_kind, s);
+    if (st != SM_OK || hp->K == 0) return st;
+    return run_ns(P, mp, groups, fusable, hp, B, io, s);
+  }
+  // longest-processing-time assignment of the groups to the chains, by
+  // Newton-Schulz work count * m^2 * n
+  std::vector<int> order(groups.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+  auto work = [&](const Group& g) {
+    const double m = std::min(g.rows, g.cols), n = std::max(g.rows, g.cols);
+    return (double)g.count * m * m * n;
+  };
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return work(groups[a]) > work(groups[b]); });
+  std::vector<std::vector<Group>> chain(nc);
+  std::vector<double> load(nc, 0.0);
+  for (int i : order) {
+    const int c = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    chain[c].push_back(groups[i]);
+    load[c] += work(groups[i]);
+  }
+  ChainRes* R = nullptr;
+  HIP_TRY(chain_resources(&R));
+  std::lock_guard<std::mutex> lock(R->mu);
+  HIP_TRY(hipEventRecord(R->fork, s));
+  NsIO cio = io;
+  cio.prof = nullptr;
+  sm_status st = SM_OK;
+  int forked = 0;
+  for (int c = 0; c < nc && st == SM_OK; ++c) {
+    if (hipStreamWaitEvent(R->s[c], R->fork, 0) != hipSuccess) { st = SM_EHIP; break; }
+    ++forked;
+    st = run_pre_scale(P, mp, chain[c], hp, B, cio, part_kind, R->s[c]);
+    if (st == SM_OK && hp->K > 0) st = run_ns(P, mp, chain[c], fusable, hp, B, cio, R->s[c]);
+  }
+  // join every forked chain, also after an error, so that the caller's
+  // stream orders after all work enqueued on the chains
+  for (int c = 0; c < forked; ++c) {
+    if (hipEventRecord(R->join[c], R->s[c]) != hipSuccess ||
+        hipStreamWaitEvent(s, R->join[c], 0) != hipSuccess)
+      st = SM_EHIP;
+  }
+  if (st != SM_OK) return st;
+  HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+  return SM_OK;
+}
+
 void set_vec_ok(std::vector<Group>& groups, bool ptrs_aligned) {
   for (Group& g : groups)
     g.vec_ok = ptrs_aligned && g.elem0 % 8 == 0 && g.elem_stride % 8 == 0 &&
@@ -729,9 +817,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
       HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
       io.first_xsrc = XS_USER; io.src_user = Mom;
       io.final_out = O_BITS; io.bits = local_bits; io.U = nullptr;
-      st = run_pre_scale(P, mp, groups, hp, B, io, 0, stream);
-      if (st != SM_OK) return st;
-      st = run_ns(P, mp, groups, fus, hp, B, io, stream);
+      st = run_polar(P, mp, groups, fus, hp, B, io, 0, stream);
       if (st != SM_OK) return st;
       if (need_u) {
         for (int i = 0; i < n_mats; ++i) {
@@ -778,9 +864,13 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   HIP_TRY(mark(prof, SM_PHASE_VOTE, stream));
   io.first_xsrc = XS_OP; io.src_user = nullptr;
   io.final_out = O_APPLY;
+  if (hp->K > 0) {
+    std::vector<bool> fus_all(n_mats, true);
+    return run_polar(P, mp, groups, fus_all, hp, B, io, 1, stream);
+  }
   st = run_pre_scale(P, mp, groups, hp, B, io, 1, stream);
   if (st != SM_OK) return st;
-  if (hp->K == 0) {
+  {
     ScaledOutArgs so;
     std::memset(&so, 0, sizeof(so));
     so.precision = P.precision; so.from_op = 1; so.apply = 1; so.w_bf16 = w_bf16;
@@ -792,8 +882,6 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
     }, [&](const Groups& Gs) { so.G = Gs; return launch_scaled_out(so, stream); }));
     return SM_OK;
   }
-  std::vector<bool> fus_all(n_mats, true);
-  return run_ns(P, mp, groups, fus_all, hp, B, io, stream);
 }
 }  // namespace
 
