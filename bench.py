@@ -6,8 +6,11 @@ on the matrix cores, sign + 1-bit pack into the local worker's buffer, vote
 over the M resident packed buffers fused with the update of W) on a synthetic
 parameter set with all inputs resident in HBM.  Prints one JSON line with
 steps/s, a per-phase breakdown measured with HIP events recorded on the
-launch stream inside every timed step, the roofline of the dominant kernel
-(the Newton-Schulz GEMM) and the CPU oracle timed on a bounded sample.
+launch stream inside instrumented steps (the same work with the phases in
+sequence), the roofline of the dominant kernel (the Newton-Schulz GEMM) and
+the CPU oracle timed on a bounded sample.  `value` times plain steps, in
+which the momentum sweep, Newton-Schulz and vote of different matrix groups
+overlap on the library's internal streams.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload nanogpt]
 """
@@ -202,12 +205,22 @@ def main():
         p.count = 0
         profs.append(p)
 
+    # timed region: K production steps (the whole step runs as concurrent
+    # chains on the library's streams), bracketed by device synchronization
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
-        plan.profiled(profs[k], G, W, Mom, bits, words, w.M, 0, u0=u0)
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+
+    # K instrumented steps for the phase breakdown: the same work with the
+    # phases in sequence and an event after each (Newton-Schulz chains only
+    # inside the polar phase)
+    torch.cuda.synchronize()
+    for k in range(K):
+        plan.profiled(profs[k], G, W, Mom, bits, words, w.M, 0, u0=u0)
+    torch.cuda.synchronize()
 
     # per-phase durations from consecutive events of each step
     phase = {}
@@ -267,6 +280,7 @@ def main():
         "vote_frac_hbm": round(vote_gbps / PEAK_HBM_GBPS, 4),
         "momentum_gbps": round(mom_gbps, 1),
         "phases_us": {k: round(v, 2) for k, v in phase_us.items()},
+        "instrumented_us_per_step": round(sum(phase_us.values()), 2),
     }
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
