@@ -296,7 +296,7 @@ struct NsIO {
 // symmetric output).
 void set_gemm_tiles(Group& g, int prec, int epi) {
   int tm, tn;
-  gemm_tile(prec, epi, g.gm, g.gn, &tm, &tn);
+  gemm_tile(prec, epi, g.gm, g.gn, g.gk, &tm, &tn);
   g.tile = tn;
   g.tiles_n = (g.gn + tn - 1) / tn;
   const int tiles_m = (g.gm + tm - 1) / tm;

@@ -33,6 +33,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
+// the kernel's helper lambdas take register arrays by reference: they must
+// be inlined, or the arrays would live in scratch memory
+#define SM_INLINE __attribute__((always_inline))
 
 constexpr int BM = 128;          // block tile width (and height for WM = 2)
 
@@ -309,7 +312,8 @@ __device__ __forceinline__ void store_mirror(const f32x4_t (&v)[TI][TJ], void* h
 // epilogue, NSTG pipeline stages of RB-byte slab rows, WM x 2 waves of
 // (16 TI) x (16 TJ) each, and the waves per SIMD that the register
 // allocation must leave room for.
-template <typename T, int SPLIT, int EPI, int NSTG, int WM, int TI, int TJ, int RB, int WPE>
+template <typename T, int SPLIT, int EPI, int NSTG, int WM, int TI, int TJ, int RB, int WPE,
+          bool PIPE>
 __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   constexpr int WTM = 16 * TI, WTN = 16 * TJ;  // wave tile
@@ -368,7 +372,9 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   }
   const int m0 = tm * BMT, n0 = tn * BNT;
   const int64_t lda = fam_ld(g, a_fam), ldb = fam_ld(g, b_fam);
-  const bool a_km = a_fam == FAM_XK, b_km = b_fam == FAM_XK;
+  // Operand layouts are fixed by the product: only the update's S operand
+  // (B) is read k-major.  (The host sets the operand families to match.)
+  constexpr bool a_km = false, b_km = EPI == E_UPDATE;
   const void* a_hi = a_fam == FAM_R ? A.r_hi : A.x_hi;
   const void* b_hi = b_fam == FAM_R ? A.r_hi : A.x_hi;
   const void* a_lo = a_fam == FAM_R ? A.r_lo : A.x_lo;
@@ -429,7 +435,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   //   of column c0 + l % 16, the MFMA operand layout.
   //  float32: the 16x16x4 MFMA takes k = 4 (kk*4 + l/16) + e, e = 0..3, of
   //   column c0 + l % 16 in register e (as the k-along-rows reads).
-  auto km_frag = [&](auto wc, const char* tile, int c0, int kk) -> u32x4_t {
+  auto km_frag = [&](auto wc, const char* tile, int c0, int kk) SM_INLINE -> u32x4_t {
     constexpr int W = decltype(wc)::value;
     if constexpr (sizeof(T) == 2) {
       const int row = kk * 32 + 8 * (lane >> 4) + ((lane & 15) >> 2);
@@ -455,7 +461,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   auto b_tile = [&](int st, int sp) -> char* {
     return smem + st * STAGEB + SPLIT * ATILE + sp * BTILE;
   };
-  auto issue = [&](int s) {
+  auto issue = [&](int s) SM_INLINE {
     const int st = s % NSTG;
 #pragma unroll
     for (int sp = 0; sp < SPLIT; ++sp) {
@@ -528,7 +534,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   // a S for the 16-row block u of the wave tile from the stage holding it:
   // rows k = m, 4 consecutive m of one column n per lane (bf16: one
   // transposing read per 16 columns; float32: 4 reads)
-  auto add_ax_block = [&](auto uc, int s, int stg) {
+  auto add_ax_block = [&](auto uc, int s, int stg) SM_INLINE {
     constexpr int u = decltype(uc)::value;
     const int kb = ax_k0 + u * 16 - s * BK;
 #pragma unroll
@@ -555,9 +561,9 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     }
   };
   // every 16-row block of the a S term that lies in slab s
-  auto add_ax = [&](int s, int stg) {
+  auto add_ax = [&](int s, int stg) SM_INLINE {
     static_assert(TI <= 8, "a S blocks");
-    auto one = [&](auto uc) {
+    auto one = [&](auto uc) SM_INLINE {
       constexpr int u = decltype(uc)::value;
       if constexpr (u < TI)
         if ((ax_k0 + 16 * u) / BK == s) add_ax_block(uc, s, stg);
@@ -571,7 +577,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   constexpr int LOADS = SPLIT * (QA + QB);     // vector loads per thread per slab
 
   // MFMAs of one k-step on one accumulator tile.
-  auto mfma_tile = [&](const u32x4_t* fa, const u32x4_t* fb, int i, int j) {
+  auto mfma_tile = [&](const u32x4_t* fa, const u32x4_t* fb, int i, int j) SM_INLINE {
     if constexpr (sizeof(T) == 2) {
       bf16x8_t ah = __builtin_bit_cast(bf16x8_t, fa[0]);
       bf16x8_t bh = __builtin_bit_cast(bf16x8_t, fb[0]);
@@ -591,69 +597,117 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     }
   };
 
-#pragma unroll
-  for (int s = 0; s < NSTG - 1; ++s)
-    if (s < nslab) issue(s);
-
-  for (int s = 0; s < nslab; ++s) {
-    // slab s has landed for this wave once at most the later slabs' loads
-    // are outstanding; the barrier extends that to every wave and also
-    // frees stage (s-1) % NSTG for the next fetch.
-    if constexpr (NSTG >= 3) {
-      if (s + NSTG - 2 < nslab) wait_vmcnt<(NSTG - 2) * LOADS>();
-      else wait_vmcnt<0>();
+  // fragments of one slab: [kk][split * TI + i] (A) and [kk][split * TJ + j] (B)
+  constexpr int NFA = SPLIT * TI, NFB = SPLIT * TJ, NF = NKK * (NFA + NFB);
+  // fragment q of a slab (q = kk * (NFA + NFB) + A fragments, then B)
+  auto read_one = [&](u32x4_t (&fa)[NKK][NFA], u32x4_t (&fb)[NKK][NFB], int stg, int q) SM_INLINE {
+    const int kk = q / (NFA + NFB), r = q % (NFA + NFB);
+    if (r < NFA) {
+      const int sp = r / TI, i = r % TI;
+      if constexpr (a_km)
+        fa[kk][r] = km_frag(std::integral_constant<int, BMT>{}, a_tile(stg, sp), wm * WTM + 16 * i, kk);
+      else
+        fa[kk][r] = *reinterpret_cast<const u32x4_t*>(a_tile(stg, sp) + fa_off[kk] + i * 16 * RB);
     } else {
-      wait_vmcnt<0>();
+      const int rb = r - NFA, sp = rb / TJ, j = rb % TJ;
+      if constexpr (b_km)
+        fb[kk][rb] = km_frag(std::integral_constant<int, BNT>{}, b_tile(stg, sp), wn * WTN + 16 * j, kk);
+      else
+        fb[kk][rb] = *reinterpret_cast<const u32x4_t*>(b_tile(stg, sp) + fb_off[kk] + j * 16 * RB);
     }
+  };
+  auto ax_here = [&](int s) {
+    if constexpr (EPI == E_UPDATE) return !ax_user && s * BK < ax_k0 + 16 * TI && ax_k0 < (s + 1) * BK;
+    else return false;
+  };
+
+  if constexpr (!PIPE) {
+#pragma unroll
+    for (int s = 0; s < NSTG - 1; ++s)
+      if (s < nslab) issue(s);
+
+    for (int s = 0; s < nslab; ++s) {
+      // slab s has landed for this wave once at most the later slabs' loads
+      // are outstanding; the barrier extends that to every wave and also
+      // frees stage (s-1) % NSTG for the next fetch.
+      if constexpr (NSTG >= 3) {
+        if (s + NSTG - 2 < nslab) wait_vmcnt<(NSTG - 2) * LOADS>();
+        else wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (s + NSTG - 1 < nslab) issue(s + NSTG - 1);
+
+      const int stg = s % NSTG;
+      // every fragment read of the slab ahead of the MFMAs, so the waits
+      // before them count down outstanding reads instead of draining them
+      u32x4_t fa[NKK][NFA], fb[NKK][NFB];
+#pragma unroll
+      for (int q = 0; q < NF; ++q) read_one(fa, fb, stg, q);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) mfma_tile(&fa[kk][i], &fb[kk][j], i, j);
+      if constexpr (EPI == E_UPDATE) {
+        // after the slab's MFMAs, when the fragment registers are free again
+        __builtin_amdgcn_sched_barrier(0);
+        if (ax_here(s)) add_ax(s, stg);
+      }
+    }
+  } else {
+    // Software-pipelined k-loop: the fragments of slab s+1 are read into a
+    // second register set while the MFMAs of slab s run, so no MFMA waits
+    // for LDS.  Per slab s: wait for slab s+1's fetch and for this wave's
+    // reads of slab s, barrier (then stage s % NSTG is free and slab s+1 is
+    // in LDS for every wave), fetch slab s+NSTG into stage s % NSTG, then the
+    // MFMAs of slab s with one read of slab s+1 after every second MFMA.  After the last slab those reads hit a stale stage and
+    // are never used, which keeps the MFMA sequence free of branches.  The
+    // slab count is even (k is a multiple of 128).
+    constexpr int NM = NKK * TI * TJ;                 // MFMA tiles per slab
+    u32x4_t fa0[NKK][NFA], fb0[NKK][NFB], fa1[NKK][NFA], fb1[NKK][NFB];
+#pragma unroll
+    for (int p = 0; p < NSTG; ++p) issue(p);
+    wait_vmcnt<(NSTG - 1) * LOADS>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (s + NSTG - 1 < nslab) issue(s + NSTG - 1);
-
-    const int stg = s % NSTG;
-    // fragments [kk][split * TI + i] (A) and [kk][split * TJ + j] (B)
-    auto read_frags = [&](u32x4_t (&fa)[SPLIT * TI], u32x4_t (&fb)[SPLIT * TJ], int kk) {
 #pragma unroll
-      for (int sp = 0; sp < SPLIT; ++sp) {
-        if (a_km) {
+    for (int q = 0; q < NF; ++q) read_one(fa0, fb0, 0, q);
+    if (ax_here(0)) add_ax(0, 0);
+    auto step = [&](int s, u32x4_t (&ca)[NKK][NFA], u32x4_t (&cb)[NKK][NFB],
+                    u32x4_t (&na)[NKK][NFA], u32x4_t (&nb)[NKK][NFB]) SM_INLINE {
+      if (s + 1 < nslab) {
+        // slab s+1 landed for this wave (later fetches may be in flight)
+        if (s + NSTG - 1 < nslab) wait_vmcnt<(NSTG - 2) * LOADS>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4) | 15 | (3 << 14));  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (s + NSTG < nslab) issue(s + NSTG);   // into stage s % NSTG, read out already
+      }
+      const int nst = (s + 1) % NSTG;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int i = 0; i < TI; ++i)
-            fa[sp * TI + i] =
-                km_frag(std::integral_constant<int, BMT>{}, a_tile(stg, sp), wm * WTM + 16 * i, kk);
-        } else {
+      for (int t = 0; t < NM; ++t) {
+        const int kk = t / (TI * TJ), i = (t / TJ) % TI, j = t % TJ;
+        mfma_tile(&ca[kk][i], &cb[kk][j], i, j);
+        if ((t & 1) && (t >> 1) < NF) read_one(na, nb, nst, t >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
-          for (int i = 0; i < TI; ++i)
-            fa[sp * TI + i] =
-                *reinterpret_cast<const u32x4_t*>(a_tile(stg, sp) + fa_off[kk] + i * 16 * RB);
-        }
-        if (b_km) {
-#pragma unroll
-          for (int j = 0; j < TJ; ++j)
-            fb[sp * TJ + j] =
-                km_frag(std::integral_constant<int, BNT>{}, b_tile(stg, sp), wn * WTN + 16 * j, kk);
-        } else {
-#pragma unroll
-          for (int j = 0; j < TJ; ++j)
-            fb[sp * TJ + j] =
-                *reinterpret_cast<const u32x4_t*>(b_tile(stg, sp) + fb_off[kk] + j * 16 * RB);
-        }
+      for (int q = NM / 2; q < NF; ++q) read_one(na, nb, nst, q);
+      if (s + 1 < nslab && ax_here(s + 1)) {
+        __builtin_amdgcn_sched_barrier(0);
+        add_ax(s + 1, nst);
       }
     };
-    // every fragment read of the slab ahead of the MFMAs, so the waits
-    // before them count down outstanding reads instead of draining them
-    u32x4_t fa[NKK][SPLIT * TI], fb[NKK][SPLIT * TJ];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) read_frags(fa[kk], fb[kk], kk);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) mfma_tile(&fa[kk][i], &fb[kk][j], i, j);
-    if constexpr (EPI == E_UPDATE) {
-      // after the slab's MFMAs, when the fragment registers are free again
-      __builtin_amdgcn_sched_barrier(0);
-      if (!ax_user && s * BK < ax_k0 + 16 * TI && ax_k0 < (s + 1) * BK) add_ax(s, stg);
+    for (int s = 0; s < nslab; s += 2) {
+      step(s, fa0, fb0, fa1, fb1);
+      step(s + 1, fa1, fb1, fa0, fb0);
     }
   }
 
@@ -799,11 +853,19 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
 //   Newton-Schulz shapes, where the outputs are only 768 wide: 64-byte slab
 //   rows with four blocks per CU, and 256x256 tiles with one block per CU,
 //   were all slower.)
-//   Wide update (bf16, columns a multiple of 256): 128x256 tiles, 4 waves of
-//   64x128, three stages of 64-byte slab rows (72 KB), still two blocks per
-//   CU; per output it moves a quarter fewer operand bytes from L2 into LDS.
+//   The bf16 kernels whose accumulators and two slabs of fragments fit in
+//   192 registers run the software-pipelined k-loop.
+//   Long bf16 updates (k >= 2048, columns a multiple of 256): 128x256
+//   tiles, 4 waves of 64x128, three stages of 64-byte slab rows (72 KB),
+//   still two blocks per CU; per output they move a quarter fewer operand
+//   bytes from L2 into LDS, which pays off on long k-loops (measured: the
+//   4096-wide MLP set gains 2%, the nanoGPT set, with k = 768, runs 3%
+//   faster with the pipelined 128x128 update).
 #ifndef SM_GEMM_WIDE_UPDATE
 #define SM_GEMM_WIDE_UPDATE 1
+#endif
+#ifndef SM_GEMM_PIPE
+#define SM_GEMM_PIPE 1
 #endif
 template <typename T, int SPLIT, int EPI, bool WIDE = false>
 struct Cfg {
@@ -812,6 +874,10 @@ struct Cfg {
   static constexpr int RB = WIDE ? 64 : 128;
   static constexpr int NSTG = WIDE ? 3 : 2;
   static constexpr int WPE = 2;
+  // software pipelining holds two slabs of fragments: used where those and
+  // the accumulators fit in 192 registers
+  static constexpr bool PIPE = SM_GEMM_PIPE && sizeof(T) == 2 && SPLIT == 1 &&
+                               TI * TJ * 4 + 2 * (RB / 64) * (TI + TJ) * 4 <= 192;
   static constexpr int BMT = WM * 16 * TI, BNT = 32 * TJ;
   static constexpr size_t lds() {
     size_t pipe = (size_t)NSTG * SPLIT * (BMT + BNT) * RB;
@@ -822,22 +888,23 @@ struct Cfg {
   }
 };
 using CfgWide = Cfg<bf16_t, 1, E_UPDATE, true>;
+constexpr int kWideMinK = 2048;
 constexpr int kTile = Cfg<bf16_t, 1, E_UPDATE>::BMT;
 static_assert(Cfg<bf16_t, 1, E_UPDATE>::BNT == kTile, "square tile");
 static_assert(CfgWide::BMT == kTile, "wide tiles keep the row height");
 
-void gemm_tile(int precision, int epi, int64_t gm, int64_t gn, int* tm, int* tn) {
+void gemm_tile(int precision, int epi, int64_t gm, int64_t gn, int64_t gk, int* tm, int* tn) {
   *tm = kTile;
   *tn = kTile;
   if (SM_GEMM_WIDE_UPDATE && epi == E_UPDATE && precision == P_BF16 && gm % kTile == 0 &&
-      gn % CfgWide::BNT == 0)
+      gn % CfgWide::BNT == 0 && gk >= kWideMinK)
     *tn = CfgWide::BNT;
 }
 
 template <typename T, int SPLIT, int EPI, bool WIDE = false>
 static hipError_t launch_one(const GemmArgs& args, hipStream_t s) {
   using C = Cfg<T, SPLIT, EPI, WIDE>;
-  hipLaunchKernelGGL((k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE>),
+  hipLaunchKernelGGL((k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE, C::PIPE>),
                      dim3(args.G.total_blocks), dim3(128 * C::WM), C::lds(), s, args);
   return hipGetLastError();
 }
@@ -860,7 +927,7 @@ hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s) {
   for (int i = 0; i < args.G.n; ++i) {
     const Group& g = args.G.g[i];
     int tm, tn;
-    gemm_tile(precision, args.epi, g.gm, g.gn, &tm, &tn);
+    gemm_tile(precision, args.epi, g.gm, g.gn, g.gk, &tm, &tn);
     if (g.tile != tile || g.gk % 128 || g.tile != tn) return hipErrorInvalidValue;
   }
   if (tile == CfgWide::BNT) return launch_one<bf16_t, 1, E_UPDATE, true>(args, s);
@@ -873,7 +940,7 @@ template <typename T, int SPLIT, int EPI, bool WIDE = false>
 static hipError_t set_lds() {
   using C = Cfg<T, SPLIT, EPI, WIDE>;
   return hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE>),
+      reinterpret_cast<const void*>(&k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE, C::PIPE>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::lds());
 }
 template <typename T, int SPLIT>

@@ -43,9 +43,10 @@ struct GemmArgs {
 
 hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s);
 hipError_t gemm_set_attributes();
-// Block tile (tm rows x tn columns) of a GEMM with output gm x gn; every
-// group of one launch must carry the same tn in Group::tile.
-void gemm_tile(int precision, int epi, int64_t gm, int64_t gn, int* tm, int* tn);
+// Block tile (tm rows x tn columns) of a GEMM with output gm x gn and
+// depth gk; every group of one launch must carry the same tn in
+// Group::tile.
+void gemm_tile(int precision, int epi, int64_t gm, int64_t gn, int64_t gk, int* tm, int* tn);
 
 // ---- elementwise and small kernels (sm_elementwise.hip) ----
 hipError_t launch_momentum_flat(const float* G, const void* W, int w_bf16,
