@@ -243,7 +243,10 @@ __device__ __forceinline__ void load_op4(const void* hi, const void* lo, int64_t
 // row segments (rows at or past row_lim are skipped).  For split-bf16 the
 // hi and lo images sit side by side.  The LDS row pitch is padded by 16
 // bytes against bank conflicts.
-template <typename T, int SPLIT, int BMT, int BNT, int TI, int TJ, int NT>
+// With TR the accumulators hold transposed tiles (4 consecutive columns of
+// one row per register group) and each lane writes them as one 8- or
+// 16-byte piece.
+template <typename T, int SPLIT, int BMT, int BNT, int TI, int TJ, int NT, bool TR = false>
 __device__ __forceinline__ void stage_store_tile(const f32x4_t (&v)[TI][TJ], char* smem,
                                                  void* dst_hi, void* dst_lo, int64_t ld,
                                                  int m0, int n0, int row_lim, int wm, int wn,
@@ -251,25 +254,50 @@ __device__ __forceinline__ void stage_store_tile(const f32x4_t (&v)[TI][TJ], cha
   constexpr int ES = sizeof(T);
   constexpr int PITCH = BNT * ES + 16;
   constexpr int IMG = BMT * PITCH;
-  const int r0 = wm * TI * 16 + 4 * (lane >> 4), c0 = wn * TJ * 16 + (lane & 15);
+  if constexpr (TR) {
+    const int r0 = wm * TI * 16 + (lane & 15), c0 = wn * TJ * 16 + 4 * (lane >> 4);
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        char* p = smem + (r0 + i * 16 + r) * PITCH + (c0 + j * 16) * ES;
+      for (int j = 0; j < TJ; ++j) {
+        char* p = smem + (r0 + i * 16) * PITCH + (c0 + j * 16) * ES;
         if constexpr (ES == 4) {
-          *reinterpret_cast<float*>(p) = v[i][j][r];
-        } else if constexpr (SPLIT == 2) {
-          bf16_t h, l;
-          split_bf16(v[i][j][r], h, l);
-          *reinterpret_cast<bf16_t*>(p) = h;
-          *reinterpret_cast<bf16_t*>(p + IMG) = l;
+          *reinterpret_cast<f32x4_t*>(p) = v[i][j];
         } else {
-          *reinterpret_cast<bf16_t*>(p) = f32_to_bf16(v[i][j][r]);
+          bf16_t h[4], l[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if constexpr (SPLIT == 2) split_bf16(v[i][j][r], h[r], l[r]);
+            else h[r] = f32_to_bf16(v[i][j][r]);
+          }
+          *reinterpret_cast<u32x2_t*>(p) = u32x2_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                                   (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+          if constexpr (SPLIT == 2)
+            *reinterpret_cast<u32x2_t*>(p + IMG) = u32x2_t{(uint32_t)l[0] | ((uint32_t)l[1] << 16),
+                                                           (uint32_t)l[2] | ((uint32_t)l[3] << 16)};
         }
       }
+  } else {
+    const int r0 = wm * TI * 16 + 4 * (lane >> 4), c0 = wn * TJ * 16 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          char* p = smem + (r0 + i * 16 + r) * PITCH + (c0 + j * 16) * ES;
+          if constexpr (ES == 4) {
+            *reinterpret_cast<float*>(p) = v[i][j][r];
+          } else if constexpr (SPLIT == 2) {
+            bf16_t h, l;
+            split_bf16(v[i][j][r], h, l);
+            *reinterpret_cast<bf16_t*>(p) = h;
+            *reinterpret_cast<bf16_t*>(p + IMG) = l;
+          } else {
+            *reinterpret_cast<bf16_t*>(p) = f32_to_bf16(v[i][j][r]);
+          }
+        }
+  }
   __syncthreads();
   constexpr int CH = BNT * ES / 16;         // 16-byte chunks per row
 #pragma unroll
@@ -310,10 +338,11 @@ __device__ __forceinline__ void store_mirror(const f32x4_t (&v)[TI][TJ], void* h
 // ---------------------------------------------------------------------------
 // Template parameters: operand type and split (bf16 x2 = split-bf16), the
 // epilogue, NSTG pipeline stages of RB-byte slab rows, WM x 2 waves of
-// (16 TI) x (16 TJ) each, and the waves per SIMD that the register
-// allocation must leave room for.
+// (16 TI) x (16 TJ) each, the waves per SIMD that the register allocation
+// must leave room for, the software-pipelined k-loop and the transposed
+// accumulator layout.
 template <typename T, int SPLIT, int EPI, int NSTG, int WM, int TI, int TJ, int RB, int WPE,
-          bool PIPE>
+          bool PIPE, bool TRACC>
 __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   constexpr int WTM = 16 * TI, WTN = 16 * TJ;  // wave tile
@@ -375,6 +404,20 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   // Operand layouts are fixed by the product: only the update's S operand
   // (B) is read k-major.  (The host sets the operand families to match.)
   constexpr bool a_km = false, b_km = EPI == E_UPDATE;
+  // Accumulator layout.  Register r of lane l in tile (i, j) holds C(row, col):
+  //   C tiles:       row = m0 + wm*WTM + 16 i + 4 (l/16) + r,  col = n0 + wn*WTN + 16 j + l % 16
+  //   transposed:    row = m0 + wm*WTM + 16 i + l % 16,  col = n0 + wn*WTN + 16 j + 4 (l/16) + r
+  // (4 consecutive rows of one column, or 4 consecutive columns of one row).
+  // An update with TRACC runs its MFMAs with the operands swapped, which
+  // gives the transposed tiles.
+  constexpr bool SWAP = TRACC;
+  static_assert(!TRACC || EPI == E_UPDATE, "transposed tiles are an update layout");
+  auto acc_row = [&](int i, int r) SM_INLINE {
+    return m0 + wm * WTM + (SWAP ? (lane & 15) : 4 * (lane >> 4) + r) + 16 * i;
+  };
+  auto acc_col = [&](int j, int r) SM_INLINE {
+    return n0 + wn * WTN + (SWAP ? 4 * (lane >> 4) + r : (lane & 15)) + 16 * j;
+  };
   const void* a_hi = a_fam == FAM_R ? A.r_hi : A.x_hi;
   const void* b_hi = b_fam == FAM_R ? A.r_hi : A.x_hi;
   const void* a_lo = a_fam == FAM_R ? A.r_lo : A.x_lo;
@@ -482,25 +525,26 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   const bool ax_user = EPI == E_UPDATE && A.xsrc == XS_USER;
   if (ax_user) {
     // first step: a X from the caller's float32 source (entries past the
-    // matrix are zero), loaded ahead of the k-loop
-    // ((i, j) of S is (j, i) of a tall X; addresses are clamped into the
-    // matrix so that every load is issued unconditionally and all of them
-    // overlap; out-of-range entries are replaced by zero afterwards)
-    const int rb = m0 + wm * WTM + 4 * (lane >> 4), cb = n0 + wn * WTN + (lane & 15);
+    // matrix are zero), loaded ahead of the k-loop.  (i, j) of S is (j, i)
+    // of a tall X.  Addresses are clamped into the matrix so that every
+    // load is issued unconditionally and all of them overlap; out-of-range
+    // entries are replaced by zero afterwards.
     const int64_t eo = g.elem0 + (int64_t)mi * g.elem_stride;
     const int sr = s_rows(g), sc = s_cols(g);
     const bool tall = s_tall(g);
-    if (tall && g.vec_ok && g.cols % 4 == 0) {
+    if (tall != SWAP && g.vec_ok && g.cols % 4 == 0) {
       // the 4 registers of a tile are 4 consecutive entries of a row of X:
-      // one 16-byte load (sr = cols is a multiple of 4, so a group of 4 is
+      // one 16-byte load (cols is a multiple of 4, so a group of 4 is
       // either inside the matrix or wholly past it)
+      const int xrows = tall ? sc : sr;
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
-          const int si = rb + i * 16, sj = cb + j * 16;
-          const int ic = si < sr ? si : sr - 4, jc = sj < sc ? sj : sc - 1;
-          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(A.xs_user + eo + (int64_t)jc * g.cols + ic);
+          const int si = acc_row(i, 0), sj = acc_col(j, 0);
+          const int xr = tall ? sj : si, xc = tall ? si : sj;
+          const int rc = xr < xrows ? xr : xrows - 1, cc = xc < g.cols ? xc : g.cols - 4;
+          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(A.xs_user + eo + (int64_t)rc * g.cols + cc);
           const bool in = si < sr && sj < sc;
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i][j][r] = in ? A.ca * x[r] : 0.0f;
@@ -512,7 +556,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int si = rb + i * 16 + r, sj = cb + j * 16;
+            const int si = acc_row(i, r), sj = acc_col(j, r);
             const int ic = si < sr ? si : sr - 1, jc = sj < sc ? sj : sc - 1;
             const int64_t e = tall ? (int64_t)jc * g.cols + ic : (int64_t)ic * g.cols + jc;
             const float x = A.xs_user[eo + e];
@@ -532,32 +576,56 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   // rows m and columns n.  Each k-block of 16 lies in one slab.
   const int ax_k0 = m0 + wm * WTM;  // first k of the a S block
   // a S for the 16-row block u of the wave tile from the stage holding it:
-  // rows k = m, 4 consecutive m of one column n per lane (bf16: one
-  // transposing read per 16 columns; float32: 4 reads)
+  // row k = m of the slab, 4 consecutive columns n per lane (one 8-byte
+  // read for bf16, 16 bytes for float32)
   auto add_ax_block = [&](auto uc, int s, int stg) SM_INLINE {
-    constexpr int u = decltype(uc)::value;
-    const int kb = ax_k0 + u * 16 - s * BK;
+    if constexpr (SWAP) {
+      constexpr int u = decltype(uc)::value;
+      const int row = ax_k0 + u * 16 - s * BK + (lane & 15);
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int c0 = wn * WTN + j * 16;
-      float x[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < TJ; ++j) {
+        const int byte = (acc_col(j, 0) - n0) * (int)sizeof(T);
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int sp = 0; sp < SPLIT; ++sp) {
-        const char* tile = b_tile(stg, sp);
-        if constexpr (sizeof(T) == 4) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            x[r] += *reinterpret_cast<const float*>(
-                tile + km_off<T, BNT>(kb + 4 * (lane >> 4) + r, 4 * (c0 + (lane & 15))));
-        } else {
-          const u32x2_t h = lds_read_tr16(
-              tile + km_off<T, BNT>(kb + 4 * (lane >> 4) + ((lane & 15) >> 2), 2 * c0 + 8 * (lane & 3)));
-          x[0] += __uint_as_float(h[0] << 16); x[1] += __uint_as_float(h[0] & 0xFFFF0000u);
-          x[2] += __uint_as_float(h[1] << 16); x[3] += __uint_as_float(h[1] & 0xFFFF0000u);
+        for (int sp = 0; sp < SPLIT; ++sp) {
+          const char* p = b_tile(stg, sp) + km_off<T, BNT>(row, byte);
+          if constexpr (sizeof(T) == 4) {
+            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p);
+            x[0] += v[0]; x[1] += v[1]; x[2] += v[2]; x[3] += v[3];
+          } else {
+            const u32x2_t h = *reinterpret_cast<const u32x2_t*>(p);
+            x[0] += __uint_as_float(h[0] << 16); x[1] += __uint_as_float(h[0] & 0xFFFF0000u);
+            x[2] += __uint_as_float(h[1] << 16); x[3] += __uint_as_float(h[1] & 0xFFFF0000u);
+          }
         }
-      }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[u][j][r] += A.ca * x[r];
+        for (int r = 0; r < 4; ++r) acc[u][j][r] += A.ca * x[r];
+      }
+    } else {
+      constexpr int u = decltype(uc)::value;
+      const int kb = ax_k0 + u * 16 - s * BK;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int c0 = wn * WTN + j * 16;
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sp = 0; sp < SPLIT; ++sp) {
+          const char* tile = b_tile(stg, sp);
+          if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              x[r] += *reinterpret_cast<const float*>(
+                  tile + km_off<T, BNT>(kb + 4 * (lane >> 4) + r, 4 * (c0 + (lane & 15))));
+          } else {
+            const u32x2_t h = lds_read_tr16(
+                tile + km_off<T, BNT>(kb + 4 * (lane >> 4) + ((lane & 15) >> 2), 2 * c0 + 8 * (lane & 3)));
+            x[0] += __uint_as_float(h[0] << 16); x[1] += __uint_as_float(h[0] & 0xFFFF0000u);
+            x[2] += __uint_as_float(h[1] << 16); x[3] += __uint_as_float(h[1] & 0xFFFF0000u);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[u][j][r] += A.ca * x[r];
+      }
     }
   };
   // every 16-row block of the a S term that lies in slab s
@@ -578,22 +646,25 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
 
   // MFMAs of one k-step on one accumulator tile.
   auto mfma_tile = [&](const u32x4_t* fa, const u32x4_t* fb, int i, int j) SM_INLINE {
-    if constexpr (sizeof(T) == 2) {
-      bf16x8_t ah = __builtin_bit_cast(bf16x8_t, fa[0]);
-      bf16x8_t bh = __builtin_bit_cast(bf16x8_t, fb[0]);
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[i][j], 0, 0, 0);
-      if constexpr (SPLIT == 2) {
-        bf16x8_t al = __builtin_bit_cast(bf16x8_t, fa[TI]);
-        bf16x8_t bl = __builtin_bit_cast(bf16x8_t, fb[TJ]);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[i][j], 0, 0, 0);
-      }
-    } else {
-      f32x4_t av = __builtin_bit_cast(f32x4_t, fa[0]);
-      f32x4_t bv = __builtin_bit_cast(f32x4_t, fb[0]);
+    // C tile (SWAP: C^T tile) += A B over one k-step
+    auto mm = [&](const u32x4_t& x, const u32x4_t& y) SM_INLINE {
+      const u32x4_t& p = SWAP ? y : x;
+      const u32x4_t& q = SWAP ? x : y;
+      if constexpr (sizeof(T) == 2) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, p),
+                                                            __builtin_bit_cast(bf16x8_t, q),
+                                                            acc[i][j], 0, 0, 0);
+      } else {
+        const f32x4_t pv = __builtin_bit_cast(f32x4_t, p), qv = __builtin_bit_cast(f32x4_t, q);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc[i][j], 0, 0, 0);
+        for (int e = 0; e < 4; ++e)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[e], qv[e], acc[i][j], 0, 0, 0);
+      }
+    };
+    mm(fa[0], fb[0]);
+    if constexpr (SPLIT == 2) {
+      mm(fa[0], fb[TJ]);   // hi * lo
+      mm(fa[TI], fb[0]);   // lo * hi
     }
   };
 
@@ -711,10 +782,8 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     }
   }
 
-  // ---- epilogue.  acc[i][j][r] holds C(row, col) with
-  //   row = m0 + wm*WTM + i*16 + 4*(lane/16) + r,  col = n0 + wn*WTN + j*16 + lane%16
-  // i.e. the 4 registers of a tile are 4 consecutive rows of one column.
-  // For the update C is the new S: (row, col) of S is (col, row) of a tall X.
+  // ---- epilogue (accumulator coordinates: acc_row / acc_col).  For the
+  // update C is the new S: (row, col) of S is (col, row) of a tall X.
   const int idx = g.idx0 + mi * g.idx_stride;
   const float cs = A.scal ? A.scal[idx] : 1.0f;
   const int rows = g.rows, cols = g.cols;
@@ -725,15 +794,14 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
   const int64_t Rp = round_up(sr, kPad);   // rows of S (padded)
   const int64_t Cp = round_up(sc, kPad);   // columns of S (padded)
-  const int rbase = m0 + wm * WTM + 4 * (lane >> 4);
-  const int cbase = n0 + wn * WTN + (lane & 15);
+  const int ar0 = acc_row(0, 0), ac0 = acc_col(0, 0);
   // every wave is done reading the operand stages: LDS is free for staging
   __syncthreads();
 
   if constexpr (EPI == E_RAW) {
     stage_store_tile<float, 1, BMT, BNT, TI, TJ, NT>(acc, smem, A.o_raw + roff, nullptr, Rp, m0,
                                                      n0, (int)Rp, wm, wn, lane, tid);
-    if (tm != tn) store_mirror<float, 1, TI, TJ>(acc, A.o_raw, nullptr, roff, Rp, rbase, cbase);
+    if (tm != tn) store_mirror<float, 1, TI, TJ>(acc, A.o_raw, nullptr, roff, Rp, ar0, ac0);
   } else if constexpr (EPI == E_OP) {
     const float m = A.mul * (A.scal_pow == 2 ? cs * cs : 1.0f);
 #pragma unroll
@@ -743,7 +811,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
                                                      offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
                                                      (int)Rp, wm, wn, lane, tid);
-    if (tm != tn) store_mirror<T, SPLIT, TI, TJ>(acc, A.o_hi, A.o_lo, roff, Rp, rbase, cbase);
+    if (tm != tn) store_mirror<T, SPLIT, TI, TJ>(acc, A.o_hi, A.o_lo, roff, Rp, ar0, ac0);
   } else if constexpr (EPI == E_SQUARE) {
     // b A + c A^2; A is symmetric, so A(row..row+3, col) = A(col, row..row+3)
     // (combined tile by tile, so that the loaded values and the accumulator
@@ -753,7 +821,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         float x[4];
-        load_op4<T, SPLIT>(A.sq_hi, A.sq_lo, roff + (int64_t)(cbase + j * 16) * Rp + rbase + i * 16,
+        load_op4<T, SPLIT>(A.sq_hi, A.sq_lo, roff + (int64_t)(ac0 + j * 16) * Rp + ar0 + i * 16,
                            x);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[i][j][r] = A.cb * x[r] + A.cc * acc[i][j][r];
@@ -761,7 +829,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
                                                      offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
                                                      (int)Rp, wm, wn, lane, tid);
-    if (tm != tn) store_mirror<T, SPLIT, TI, TJ>(acc, A.o_hi, A.o_lo, roff, Rp, rbase, cbase);
+    if (tm != tn) store_mirror<T, SPLIT, TI, TJ>(acc, A.o_hi, A.o_lo, roff, Rp, ar0, ac0);
   } else {
     // E_UPDATE:  acc = a X + B X (first step: X = the unscaled source), and
     // the iterate is c^p * acc with c = 1/(s+eps) on the first step.
@@ -772,9 +840,9 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       for (int j = 0; j < TJ; ++j) acc[i][j] *= gam;
 
     if (A.out == O_X) {
-      stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, xoff),
-                                                       offset_ptr<T>(A.o_lo, xoff), Cp, m0, n0,
-                                                       (int)Rp, wm, wn, lane, tid);
+      stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT, SWAP>(acc, smem, offset_ptr<T>(A.o_hi, xoff),
+                                                             offset_ptr<T>(A.o_lo, xoff), Cp, m0,
+                                                             n0, (int)Rp, wm, wn, lane, tid);
     } else if (A.out == O_U || A.out == O_APPLY) {
       if (A.out == O_APPLY && A.status && A.status[0] != 0) return;
 #pragma unroll
@@ -783,7 +851,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int si = rbase + i * 16 + r, sj = cbase + j * 16;
+            const int si = acc_row(i, r), sj = acc_col(j, r);
             if (si < sr && sj < sc) {
               const int64_t e = eoff + (tall ? (int64_t)sj * cols + si : (int64_t)si * cols + sj);
               if (A.out == O_U) A.U[e] = acc[i][j][r];
@@ -792,49 +860,55 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
           }
     } else {
       // O_BITS: entrywise sign packed into 32-bit words along the rows of
-      // X (cols % 32 == 0).
+      // X (cols % 32 == 0): along the rows of S, or down its columns when
+      // X is tall.  A word covers two neighbouring tiles.
       const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
-      if (!tall) {
-        // S = X: for a 16x16 MFMA tile and accumulator register r, a wave
-        // ballot gives 4 rows x 16 columns; two neighbouring tiles give 32.
+      if (tall == SWAP) {
+        // lanes 0..15 of a tile run along the word: a wave ballot of
+        // register r gives 4 x 16 sign bits, one 16-bit half-word for each
+        // lane group q, and lane q < 4 writes the word of line 4 q + r
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
+        for (int u = 0; u < (SWAP ? TI : TJ) / 2; ++u)
 #pragma unroll
-          for (int jp = 0; jp < TJ / 2; ++jp)
+          for (int v = 0; v < (SWAP ? TJ : TI); ++v)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              uint64_t m0b = __ballot(acc[i][2 * jp][r] < 0.0f);
-              uint64_t m1b = __ballot(acc[i][2 * jp + 1][r] < 0.0f);
+              const f32x4_t& t0 = SWAP ? acc[2 * u][v] : acc[v][2 * u];
+              const f32x4_t& t1 = SWAP ? acc[2 * u + 1][v] : acc[v][2 * u + 1];
+              const uint64_t b0 = __ballot(t0[r] < 0.0f);
+              const uint64_t b1 = __ballot(t1[r] < 0.0f);
               if (lane < 4) {
-                uint32_t w = (uint32_t)((m0b >> (16 * lane)) & 0xFFFFu) |
-                             ((uint32_t)((m1b >> (16 * lane)) & 0xFFFFu) << 16);
-                int wrow = m0 + wm * WTM + i * 16 + 4 * lane + r;
-                int wcol = n0 + wn * WTN + jp * 32;
-                if (wrow < rows && wcol < cols)
-                  A.bits[woff + ((int64_t)wrow * cols + wcol) / 32] = w;
+                const uint32_t w = (uint32_t)((b0 >> (16 * lane)) & 0xFFFFu) |
+                                   ((uint32_t)((b1 >> (16 * lane)) & 0xFFFFu) << 16);
+                // the word's row of X and its first column
+                const int line = 16 * v + 4 * lane + r, start = 32 * u;
+                const int xrow = SWAP ? n0 + wn * WTN + line : m0 + wm * WTM + line;
+                const int xcol = SWAP ? m0 + wm * WTM + start : n0 + wn * WTN + start;
+                if (xrow < rows && xcol < cols)
+                  A.bits[woff + ((int64_t)xrow * cols + xcol) / 32] = w;
               }
             }
       } else {
-        // S = X^T: a row of X is a column of S, so a word collects the signs
-        // of 32 consecutive rows of S (two row tiles i) in one column.  Bit
-        // 16 ii + 4 g + r of the word of column c comes from ballot (ii, r),
-        // lane 16 g + c % 16.
+        // the 4 registers of a tile run along the word: lane 16 q + t holds
+        // entries 4 q .. 4 q + 3 of line t of both tiles, whose signs go to
+        // bits 4 q + r and 16 + 4 q + r; the 4 lanes of a line combine
+        // theirs with two lane exchanges and lane t < 16 writes the word
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
+        for (int u = 0; u < (SWAP ? TJ : TI) / 2; ++u)
 #pragma unroll
-          for (int ip = 0; ip < TI / 2; ++ip) {
+          for (int v = 0; v < (SWAP ? TI : TJ); ++v) {
+            const f32x4_t& t0 = SWAP ? acc[v][2 * u] : acc[2 * u][v];
+            const f32x4_t& t1 = SWAP ? acc[v][2 * u + 1] : acc[2 * u + 1][v];
             uint32_t w = 0;
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const uint64_t mb = __ballot(acc[2 * ip + ii][j][r] < 0.0f);
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq)
-                  w |= (uint32_t)((mb >> (16 * gq + (lane & 15))) & 1u) << (16 * ii + 4 * gq + r);
-              }
-            const int xrow = n0 + wn * WTN + j * 16 + (lane & 15);   // column of S
-            const int xcol = m0 + wm * WTM + ip * 32;                 // row of S
+            for (int r = 0; r < 4; ++r)
+              w |= (t0[r] < 0.0f ? 1u : 0u) << r | (t1[r] < 0.0f ? 1u : 0u) << (16 + r);
+            w <<= 4 * (lane >> 4);
+            w |= (uint32_t)__shfl_xor((int)w, 16);
+            w |= (uint32_t)__shfl_xor((int)w, 32);
+            const int line = 16 * v + (lane & 15), start = 32 * u;
+            const int xrow = SWAP ? m0 + wm * WTM + line : n0 + wn * WTN + line;
+            const int xcol = SWAP ? n0 + wn * WTN + start : m0 + wm * WTM + start;
             if (lane < 16 && xrow < rows && xcol < cols)
               A.bits[woff + ((int64_t)xrow * cols + xcol) / 32] = w;
           }
@@ -878,6 +952,9 @@ struct Cfg {
   // the accumulators fit in 192 registers
   static constexpr bool PIPE = SM_GEMM_PIPE && sizeof(T) == 2 && SPLIT == 1 &&
                                TI * TJ * 4 + 2 * (RB / 64) * (TI + TJ) * 4 <= 192;
+  // transposed accumulator tiles for the 128x128 update (measured: the
+  // nanoGPT set gains 1.4%, the 128x256 update of the MLP set loses 0.6%)
+  static constexpr bool TRACC = EPI == E_UPDATE && !WIDE;
   static constexpr int BMT = WM * 16 * TI, BNT = 32 * TJ;
   static constexpr size_t lds() {
     size_t pipe = (size_t)NSTG * SPLIT * (BMT + BNT) * RB;
@@ -904,7 +981,7 @@ void gemm_tile(int precision, int epi, int64_t gm, int64_t gn, int64_t gk, int* 
 template <typename T, int SPLIT, int EPI, bool WIDE = false>
 static hipError_t launch_one(const GemmArgs& args, hipStream_t s) {
   using C = Cfg<T, SPLIT, EPI, WIDE>;
-  hipLaunchKernelGGL((k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE, C::PIPE>),
+  hipLaunchKernelGGL((k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE, C::PIPE, C::TRACC>),
                      dim3(args.G.total_blocks), dim3(128 * C::WM), C::lds(), s, args);
   return hipGetLastError();
 }
@@ -940,7 +1017,7 @@ template <typename T, int SPLIT, int EPI, bool WIDE = false>
 static hipError_t set_lds() {
   using C = Cfg<T, SPLIT, EPI, WIDE>;
   return hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE, C::PIPE>),
+      reinterpret_cast<const void*>(&k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE, C::PIPE, C::TRACC>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::lds());
 }
 template <typename T, int SPLIT>
