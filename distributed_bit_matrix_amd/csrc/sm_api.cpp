@@ -15,6 +15,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <vector>
 
@@ -303,17 +304,33 @@ void set_gemm_tiles(Group& g, int prec, int epi) {
   g.blocks_per_mat = epi == E_UPDATE ? tiles_m * g.tiles_n : g.tiles_n * (g.tiles_n + 1) / 2;
 }
 
-sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
-                        const std::vector<Group>& groups, const sm_hparams* hp,
-                        Bufs& B, const NsIO& io, int part_kind,
-                        hipStream_t s) {
+// The enqueue of a PolarNS program is split into stages (one launch run
+// each, plus its profiling mark), so that several independent programs can
+// be enqueued interleaved: each stage is a closure over the program's
+// arguments, which outlive the stage list.
+using Stage = std::function<sm_status()>;
+using Stages = std::vector<Stage>;
+
+sm_status run_stages(const Stages& st) {
+  for (const Stage& f : st) {
+    const sm_status r = f();
+    if (r != SM_OK) return r;
+  }
+  return SM_OK;
+}
+
+// Pre-scale: c = 1/(s+eps) per matrix, and (K > 0) the first Gram operand
+// scaled by c^2.
+void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
+                      const std::vector<Group>& groups, const sm_hparams* hp, Bufs& B,
+                      const NsIO& io, int part_kind, hipStream_t s, Stages& out) {
   const int prec = P.precision;
   const bool quin = P.quintic;
   const float gram_mul = quin ? 1.0f : hp->ns_b;   // cubic folds b into B
   // operand that receives the scaled first Gram
   void* dst_hi = quin ? B.a[0] : B.b[0];
   void* dst_lo = quin ? B.a[1] : B.b[1];
-  auto gram_fill = [&](Group& g) {
+  auto gram_fill = [&P, &mp, prec](Group& g) {
     const MatPlan& q = mp[g.idx0];
     g.gm = g.gn = (int32_t)q.Rp;
     g.gk = (int32_t)(q.tall ? q.Mp : q.Np);
@@ -322,25 +339,33 @@ sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
     return true;
   };
   if (!P.spectral) {
-    HIP_TRY(for_launches(groups, [&](Group& g) {
-      g.blocks_per_mat = 1;
-      g.gk = (int32_t)(part_kind == 0 ? mp[g.idx0].Mp * mp[g.idx0].Np / 4096
-                                      : (((mp[g.idx0].rows * mp[g.idx0].cols + 31) / 32) + 255) / 256);
-      return true;
-    }, [&](const Groups& G) { return launch_fro_finalize(G, B.part, hp->eps, B.scal, s); }));
-    HIP_TRY(mark(io.prof, SM_PHASE_PRESCALE, s));
-    if (hp->K == 0) return SM_OK;
-    HIP_TRY(for_launches(groups, gram_fill, [&](const Groups& G) {
-      GemmArgs a;
-      std::memset(&a, 0, sizeof(a));
-      a.G = G;
-      a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
-      a.epi = E_OP; a.mul = gram_mul; a.scal = B.scal; a.scal_pow = 2;
-      a.o_hi = dst_hi; a.o_lo = dst_lo;
-      return launch_gemm(prec, a, s);
-    }));
-    HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
-  } else {
+    out.push_back([&, hp, part_kind, s]() -> sm_status {
+      HIP_TRY(for_launches(groups, [&](Group& g) {
+        g.blocks_per_mat = 1;
+        g.gk = (int32_t)(part_kind == 0 ? mp[g.idx0].Mp * mp[g.idx0].Np / 4096
+                                        : (((mp[g.idx0].rows * mp[g.idx0].cols + 31) / 32) + 255) / 256);
+        return true;
+      }, [&](const Groups& G) { return launch_fro_finalize(G, B.part, hp->eps, B.scal, s); }));
+      HIP_TRY(mark(io.prof, SM_PHASE_PRESCALE, s));
+      return SM_OK;
+    });
+    if (hp->K == 0) return;
+    out.push_back([&, hp, gram_fill, gram_mul, dst_hi, dst_lo, prec, s]() -> sm_status {
+      HIP_TRY(for_launches(groups, gram_fill, [&](const Groups& G) {
+        GemmArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.G = G;
+        a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
+        a.epi = E_OP; a.mul = gram_mul; a.scal = B.scal; a.scal_pow = 2;
+        a.o_hi = dst_hi; a.o_lo = dst_lo;
+        return launch_gemm(prec, a, s);
+      }));
+      HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+      return SM_OK;
+    });
+    return;
+  }
+  out.push_back([&, hp, gram_fill, prec, s]() -> sm_status {
     HIP_TRY(for_launches(groups, gram_fill, [&](const Groups& G) {
       GemmArgs a;
       std::memset(&a, 0, sizeof(a));
@@ -350,25 +375,38 @@ sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
       return launch_gemm(prec, a, s);
     }));
     HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
-    float* va = B.vec;
-    float* vb = B.vec + P.v_total;
+    return SM_OK;
+  });
+  // power iteration: u0 -> va, then P steps alternating va / vb
+  float* va = B.vec;
+  float* vb = B.vec + P.v_total;
+  out.push_back([&, hp, va, s]() -> sm_status {
     HIP_TRY(for_launches(groups, [&](Group& g) {
       g.blocks_per_mat = (int32_t)((mp[g.idx0].Rp + 255) / 256);
       return true;
     }, [&](const Groups& G) { return launch_power_init(G, io.u0, va, s); }));
-    for (int p = 0; p < hp->P; ++p) {
+    return SM_OK;
+  });
+  for (int p = 0; p < hp->P; ++p) {
+    out.push_back([&, hp, va, vb, s]() -> sm_status {
       HIP_TRY(for_launches(groups, [&](Group& g) {
         g.blocks_per_mat = (int32_t)(mp[g.idx0].Rp / 16);
         return true;
       }, [&](const Groups& G) { return launch_power_step(G, B.araw, va, vb, s); }));
-      std::swap(va, vb);
-    }
+      return SM_OK;
+    });
+    std::swap(va, vb);
+  }
+  out.push_back([&, hp, va, s]() -> sm_status {
     HIP_TRY(for_launches(groups, [&](Group& g) { g.blocks_per_mat = 1; return true; },
                          [&](const Groups& G) {
                            return launch_power_finalize(G, va, hp->eps, B.scal, s);
                          }));
     HIP_TRY(mark(io.prof, SM_PHASE_PRESCALE, s));
-    if (hp->K == 0) return SM_OK;
+    return SM_OK;
+  });
+  if (hp->K == 0) return;
+  out.push_back([&, hp, gram_mul, dst_hi, dst_lo, prec, s]() -> sm_status {
     HIP_TRY(for_launches(groups, [&](Group& g) {
       g.blocks_per_mat = (int32_t)(mp[g.idx0].Rp * mp[g.idx0].Rp / kChunk);
       return true;
@@ -376,8 +414,17 @@ sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
       return launch_prescale(G, prec, B.araw, B.scal, gram_mul, dst_hi, dst_lo, s);
     }));
     HIP_TRY(mark(io.prof, SM_PHASE_PRESCALE, s));
-  }
-  return SM_OK;
+    return SM_OK;
+  });
+}
+
+sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
+                        const std::vector<Group>& groups, const sm_hparams* hp,
+                        Bufs& B, const NsIO& io, int part_kind,
+                        hipStream_t s) {
+  Stages st;
+  pre_scale_stages(P, mp, groups, hp, B, io, part_kind, s, st);
+  return run_stages(st);
 }
 
 // B = b A + c A^2 from the operand A (quintic).
@@ -402,81 +449,98 @@ hipError_t run_square(const Plan& P, const std::vector<MatPlan>& mp,
   });
 }
 
+// The K Newton-Schulz steps: step k reads the iterate from x[(k-1) & 1]
+// and writes x[k & 1] (the last one writes the final output instead).
+void ns_stages(const Plan& P, const std::vector<MatPlan>& mp,
+               const std::vector<Group>& groups, const std::vector<bool>& fusable,
+               const sm_hparams* hp, Bufs& B, const NsIO& io, hipStream_t s, Stages& out) {
+  const int prec = P.precision;
+  const int K = hp->K;
+  for (int k = 1; k <= K; ++k) {
+    const int cur = (k - 1) & 1;
+    if (k > 1) {
+      // Gram of the current iterate: cubic -> B = b A, quintic -> A
+      out.push_back([&, hp, cur, prec, s]() -> sm_status {
+        HIP_TRY(for_launches(groups, [&](Group& g) {
+          const MatPlan& q = mp[g.idx0];
+          g.gm = g.gn = (int32_t)q.Rp;
+          g.gk = (int32_t)(q.tall ? q.Mp : q.Np);
+          set_gemm_tiles(g, prec, E_OP);
+          g.ops = gemm_ops(FAM_X, FAM_X);   // S S^T
+          return true;
+        }, [&](const Groups& G) {
+          GemmArgs a;
+          std::memset(&a, 0, sizeof(a));
+          a.G = G;
+          a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
+          a.epi = E_OP; a.mul = P.quintic ? 1.0f : hp->ns_b; a.scal_pow = 0;
+          a.o_hi = P.quintic ? B.a[0] : B.b[0];
+          a.o_lo = P.quintic ? B.a[1] : B.b[1];
+          return launch_gemm(prec, a, s);
+        }));
+        HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+        return SM_OK;
+      });
+    }
+    if (P.quintic) {
+      out.push_back([&, hp, s]() -> sm_status {
+        HIP_TRY(run_square(P, mp, groups, hp, B, s));
+        HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+        return SM_OK;
+      });
+    }
+    // update: S <- a S + B S
+    out.push_back([&, hp, k, K, cur, prec, s]() -> sm_status {
+      const bool last = k == K;
+      for (int pass = 0; pass < 2; ++pass) {
+        // pass 0: matrices using the requested final output; pass 1: the
+        // unfusable ones writing U into the workspace (only when last).
+        if (pass == 1 && !(last && io.final_out == O_BITS)) break;
+        int launched = 0;
+        HIP_TRY(for_launches(groups, [&](Group& g) {
+          const MatPlan& q = mp[g.idx0];
+          if (last && io.final_out == O_BITS && fusable[g.idx0] != (pass == 0)) return false;
+          g.gm = (int32_t)q.Rp; g.gn = (int32_t)(q.tall ? q.Mp : q.Np);
+          g.gk = (int32_t)q.Rp;
+          set_gemm_tiles(g, prec, E_UPDATE);
+          g.ops = gemm_ops(FAM_R, FAM_XK);
+          return true;
+        }, [&](const Groups& G) {
+          GemmArgs a;
+          std::memset(&a, 0, sizeof(a));
+          a.G = G;
+          a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
+          a.r_hi = B.b[0]; a.r_lo = B.b[1];
+          a.epi = E_UPDATE; a.ca = hp->ns_a;
+          a.xsrc = k == 1 ? io.first_xsrc : XS_OP;
+          a.xs_user = io.src_user;
+          a.scal = B.scal; a.scal_pow = k == 1 ? 1 : 0;
+          if (!last) {
+            a.out = O_X;
+            a.o_hi = B.x[cur ^ 1][0]; a.o_lo = B.x[cur ^ 1][1];
+          } else if (io.final_out == O_BITS && pass == 1) {
+            a.out = O_U; a.U = B.u;
+          } else {
+            a.out = io.final_out;
+            a.U = io.U; a.bits = io.bits;
+            a.W = io.W; a.w_bf16 = io.w_bf16; a.eta = io.eta;
+            a.status = io.status;
+          }
+          return launch_gemm(prec, a, s);
+        }, &launched));
+        if (launched) HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+      }
+      return SM_OK;
+    });
+  }
+}
+
 sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
                  const std::vector<Group>& groups, const std::vector<bool>& fusable,
                  const sm_hparams* hp, Bufs& B, const NsIO& io, hipStream_t s) {
-  const int prec = P.precision;
-  const int K = hp->K;
-  int cur = 0;
-  for (int k = 1; k <= K; ++k) {
-    if (k > 1) {
-      // Gram of the current iterate: cubic -> B = b A, quintic -> A
-      HIP_TRY(for_launches(groups, [&](Group& g) {
-        const MatPlan& q = mp[g.idx0];
-        g.gm = g.gn = (int32_t)q.Rp;
-        g.gk = (int32_t)(q.tall ? q.Mp : q.Np);
-        set_gemm_tiles(g, prec, E_OP);
-        g.ops = gemm_ops(FAM_X, FAM_X);   // S S^T
-        return true;
-      }, [&](const Groups& G) {
-        GemmArgs a;
-        std::memset(&a, 0, sizeof(a));
-        a.G = G;
-        a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
-        a.epi = E_OP; a.mul = P.quintic ? 1.0f : hp->ns_b; a.scal_pow = 0;
-        a.o_hi = P.quintic ? B.a[0] : B.b[0];
-        a.o_lo = P.quintic ? B.a[1] : B.b[1];
-        return launch_gemm(prec, a, s);
-      }));
-      HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
-    }
-    if (P.quintic) {
-      HIP_TRY(run_square(P, mp, groups, hp, B, s));
-      HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
-    }
-    // update: S <- a S + B S
-    const bool last = k == K;
-    for (int pass = 0; pass < 2; ++pass) {
-      // pass 0: matrices using the requested final output; pass 1: the
-      // unfusable ones writing U into the workspace (only when last).
-      if (pass == 1 && !(last && io.final_out == O_BITS)) break;
-      int launched = 0;
-      HIP_TRY(for_launches(groups, [&](Group& g) {
-        const MatPlan& q = mp[g.idx0];
-        if (last && io.final_out == O_BITS && fusable[g.idx0] != (pass == 0)) return false;
-        g.gm = (int32_t)q.Rp; g.gn = (int32_t)(q.tall ? q.Mp : q.Np);
-        g.gk = (int32_t)q.Rp;
-        set_gemm_tiles(g, prec, E_UPDATE);
-        g.ops = gemm_ops(FAM_R, FAM_XK);
-        return true;
-      }, [&](const Groups& G) {
-        GemmArgs a;
-        std::memset(&a, 0, sizeof(a));
-        a.G = G;
-        a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
-        a.r_hi = B.b[0]; a.r_lo = B.b[1];
-        a.epi = E_UPDATE; a.ca = hp->ns_a;
-        a.xsrc = k == 1 ? io.first_xsrc : XS_OP;
-        a.xs_user = io.src_user;
-        a.scal = B.scal; a.scal_pow = k == 1 ? 1 : 0;
-        if (!last) {
-          a.out = O_X;
-          a.o_hi = B.x[cur ^ 1][0]; a.o_lo = B.x[cur ^ 1][1];
-        } else if (io.final_out == O_BITS && pass == 1) {
-          a.out = O_U; a.U = B.u;
-        } else {
-          a.out = io.final_out;
-          a.U = io.U; a.bits = io.bits;
-          a.W = io.W; a.w_bf16 = io.w_bf16; a.eta = io.eta;
-          a.status = io.status;
-        }
-        return launch_gemm(prec, a, s);
-      }, &launched));
-      if (launched) HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
-    }
-    cur ^= 1;
-  }
-  return SM_OK;
+  Stages st;
+  ns_stages(P, mp, groups, fusable, hp, B, io, s, st);
+  return run_stages(st);
 }
 
 // ---------------------------------------------------------------------------
@@ -485,9 +549,14 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
 // internal streams forked from and joined back into the caller's stream.
 // A chain's launches depend only on its own matrices, so the GPU runs the
 // chains side by side and one chain's next launch fills the tail of
-// another's.  With one group everything runs on the caller's stream.
+// another's.  The chains' launches are enqueued interleaved, one stage of
+// each chain in turn, so that no chain waits for the host to enqueue the
+// others.  With one group everything runs on the caller's stream.
+// Three chains: with the caller's stream they take four hardware queues,
+// HIP's default per process; a fourth stream would share a queue with
+// another chain and run behind it.
 // ---------------------------------------------------------------------------
-constexpr int kChains = 4;
+constexpr int kChains = 3;
 struct ChainRes {
   hipStream_t s[kChains];
   hipEvent_t fork, join[kChains];
@@ -547,14 +616,22 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
   HIP_TRY(hipEventRecord(R->fork, s));
   NsIO cio = io;
   cio.prof = nullptr;
+  std::vector<Stages> prog(nc);
+  for (int c = 0; c < nc; ++c) {
+    pre_scale_stages(P, mp, chain[c], hp, B, cio, part_kind, R->s[c], prog[c]);
+    if (hp->K > 0) ns_stages(P, mp, chain[c], fusable, hp, B, cio, R->s[c], prog[c]);
+  }
   sm_status st = SM_OK;
   int forked = 0;
   for (int c = 0; c < nc && st == SM_OK; ++c) {
     if (hipStreamWaitEvent(R->s[c], R->fork, 0) != hipSuccess) { st = SM_EHIP; break; }
     ++forked;
-    st = run_pre_scale(P, mp, chain[c], hp, B, cio, part_kind, R->s[c]);
-    if (st == SM_OK && hp->K > 0) st = run_ns(P, mp, chain[c], fusable, hp, B, cio, R->s[c]);
   }
+  size_t longest = 0;
+  for (const Stages& p : prog) longest = std::max(longest, p.size());
+  for (size_t i = 0; i < longest && st == SM_OK; ++i)
+    for (int c = 0; c < forked && st == SM_OK; ++c)
+      if (i < prog[c].size()) st = prog[c][i]();
   // join every forked chain, also after an error, so that the caller's
   // stream orders after all work enqueued on the chains
   for (int c = 0; c < forked; ++c) {
