@@ -40,39 +40,51 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int BM = 128;          // block tile width (and height for WM = 2)
 
 // LDS image of one k-slab of an operand tile: RB bytes per row (64 or 128),
-// 16-byte chunks XOR-swizzled by row.  A fragment read (16 lanes on 16
-// consecutive rows, one chunk) then touches every bank group once in each
-// group of 8 lanes and in each group of 16 lanes.  The swizzle depends on
-// row bits 0..3 only, so rows 16 apart share it and a fragment offset
-// steps by a constant 16*RB bytes per 16-row tile.
+// 16-byte chunks XOR-swizzled by row.  A fragment read is a ds_read_b128
+// with 16 lanes on 16 consecutive rows and lane groups 16 apart on
+// neighbouring chunks.  The LDS serves such a read per half-wave: it is
+// free of bank conflicts when the 32 lanes of each half hit 32 distinct
+// 16-byte units modulo 512 bytes (measured on gfx950 with the
+// SQ_LDS_BANK_CONFLICT counter over several lane patterns; a swizzle that
+// only separates groups of 8 or 16 lanes left a 2-way conflict).  Rows 4
+// apart (128-byte rows) or 8 apart (64-byte rows) share a unit modulo 512
+// bytes, so the swizzle separates exactly those.  It depends on row bits
+// 0..3 only, so rows 16 apart share it and a fragment offset steps by a
+// constant 16*RB bytes per 16-row tile.
 template <int RB>
 __host__ __device__ constexpr int swz(int row) {
-  if constexpr (RB == 128) return (row ^ ((row >> 3) & 1)) & 7;
-  else return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+  if constexpr (RB == 128) return (row >> 1) & 7;
+  else return (((row >> 3) & 1) << 1) | ((row >> 2) & 1);
 }
 template <int RB>
 __host__ __device__ constexpr int lds_off(int row, int chunk) {
   return row * RB + ((chunk ^ swz<RB>(row)) << 4);
 }
-// Compile-time checks of the layout: constant 16-row stride, and distinct
-// 16-byte bank groups for every 8 and every 16 lanes of a fragment read
-// (banks repeat every 128 / 256 bytes).
+// Compile-time checks of the layout: constant 16-row stride, a bijection of
+// each row's chunks, and distinct 16-byte units modulo 512 bytes in each
+// half-wave of a fragment read (lane l: row l % 16, chunk 4 kk + l / 16).
 template <int RB>
 constexpr bool slab_layout_ok() {
-  for (int r0 = 0; r0 < 256; r0 += 16)
-    for (int ch = 0; ch < RB / 16; ++ch) {
+  constexpr int CPR = RB / 16;
+  for (int r0 = 0; r0 < 256; r0 += 16) {
+    for (int ch = 0; ch < CPR; ++ch)
       for (int r = 0; r < 16; ++r)
         if (lds_off<RB>(r0 + r, ch) != lds_off<RB>(r, ch) + r0 * RB) return false;
-      for (int span = 8; span <= 16; span *= 2)
-        for (int a = 0; a < 16; a += span) {
-          unsigned seen = 0;
-          for (int r = a; r < a + span; ++r) {
-            const int unit = (lds_off<RB>(r0 + r, ch) % (16 * span)) / 16;
-            if (seen & (1u << unit)) return false;
-            seen |= 1u << unit;
-          }
-        }
+    for (int r = 0; r < 16; ++r) {
+      unsigned seen = 0;
+      for (int ch = 0; ch < CPR; ++ch) seen |= 1u << ((lds_off<RB>(r, ch) - r * RB) / 16);
+      if (seen != (1u << CPR) - 1) return false;
     }
+    for (int kk = 0; kk < CPR / 4; ++kk)
+      for (int half = 0; half < 2; ++half) {
+        unsigned seen = 0;
+        for (int l = 32 * half; l < 32 * half + 32; ++l) {
+          const int unit = (lds_off<RB>(r0 + (l & 15), 4 * kk + (l >> 4)) % 512) / 16;
+          if (seen & (1u << unit)) return false;
+          seen |= 1u << unit;
+        }
+      }
+  }
   return true;
 }
 static_assert(slab_layout_ok<64>() && slab_layout_ok<128>(), "LDS slab swizzle");
