@@ -74,7 +74,8 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
     q.Mp = round_up(m.rows, kPad);
     q.Np = round_up(m.cols, kPad);
     q.Rp = round_up(q.r, kPad);
-    if (q.Mp * q.Np >= kMaxPadded) return SM_EINVAL;
+    // the GEMM addresses one operand matrix with 32-bit byte offsets
+    if (q.Mp * q.Np >= (P.precision == P_F32 ? kMaxPadded / 2 : kMaxPadded)) return SM_EINVAL;
     q.elem_off = m.elem_off; q.word_off = m.word_off;
     q.x_off = x; x += q.Mp * q.Np;
     q.r_off = r2; r2 += q.Rp * q.Rp;

@@ -374,7 +374,8 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   static_assert(EPI == E_UPDATE || BMT == BNT, "symmetric outputs use square tiles");
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: keep it (and everything derived from it) scalar
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---- block -> (group, matrix, tile), XCD-aware: the 8 XCDs take blocks
@@ -466,11 +467,13 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     const int r = mn0 + row < lim ? mn0 + row : lim - 1;
     return (int64_t)r * ld + ch * P;
   };
-  int64_t aoff[QA], boff[QB];
+  // (element offsets within one matrix fit 32 bits: padded rows * cols of a
+  // matrix is at most 2^31; the slab's uniform base pointer carries the rest)
+  uint32_t aoff[QA], boff[QB];   // byte offsets
 #pragma unroll
-  for (int q = 0; q < QA; ++q) aoff[q] = dma_off(a_km, wave * QA + q, m0, g.gm, lda, BMT);
+  for (int q = 0; q < QA; ++q) aoff[q] = (uint32_t)(dma_off(a_km, wave * QA + q, m0, g.gm, lda, BMT) * (int64_t)sizeof(T));
 #pragma unroll
-  for (int q = 0; q < QB; ++q) boff[q] = dma_off(b_km, wave * QB + q, n0, g.gn, ldb, BNT);
+  for (int q = 0; q < QB; ++q) boff[q] = (uint32_t)(dma_off(b_km, wave * QB + q, n0, g.gn, ldb, BNT) * (int64_t)sizeof(T));
   // elements between consecutive slabs
   const int64_t a_kst = a_km ? (int64_t)BK * lda : BK, b_kst = b_km ? (int64_t)BK * ldb : BK;
 
@@ -522,13 +525,15 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     for (int sp = 0; sp < SPLIT; ++sp) {
       char* ta = a_tile(st, sp) + wave * QA * 1024;
       char* tb = b_tile(st, sp) + wave * QB * 1024;
+      const char* abase = reinterpret_cast<const char*>(a_src[sp] + s * a_kst);
+      const char* bbase = reinterpret_cast<const char*>(b_src[sp] + s * b_kst);
 #pragma unroll
       for (int q = 0; q < QA; ++q)
-        __builtin_amdgcn_global_load_lds((const void*)(a_src[sp] + aoff[q] + s * a_kst),
+        __builtin_amdgcn_global_load_lds((const void*)(abase + aoff[q]),
                                          (lds_void*)(ta + q * 1024), 16, 0, 0);
 #pragma unroll
       for (int q = 0; q < QB; ++q)
-        __builtin_amdgcn_global_load_lds((const void*)(b_src[sp] + boff[q] + s * b_kst),
+        __builtin_amdgcn_global_load_lds((const void*)(bbase + boff[q]),
                                          (lds_void*)(tb + q * 1024), 16, 0, 0);
     }
   };
@@ -721,14 +726,17 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       }
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (s + NSTG - 1 < nslab) issue(s + NSTG - 1);
 
       const int stg = s % NSTG;
       // every fragment read of the slab ahead of the MFMAs, so the waits
-      // before them count down outstanding reads instead of draining them
+      // before them count down outstanding reads instead of draining them;
+      // the reads also precede the next fetch, since a transposing LDS read
+      // waits for every LDS DMA load issued before it
       u32x4_t fa[NKK][NFA], fb[NKK][NFB];
 #pragma unroll
       for (int q = 0; q < NF; ++q) read_one(fa, fb, stg, q);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + NSTG - 1 < nslab) issue(s + NSTG - 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
@@ -747,10 +755,11 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     // second register set while the MFMAs of slab s run, so no MFMA waits
     // for LDS.  Per slab s: wait for slab s+1's fetch and for this wave's
     // reads of slab s, barrier (then stage s % NSTG is free and slab s+1 is
-    // in LDS for every wave), fetch slab s+NSTG into stage s % NSTG, then the
-    // MFMAs of slab s with one read of slab s+1 after every second MFMA.  After the last slab those reads hit a stale stage and
-    // are never used, which keeps the MFMA sequence free of branches.  The
-    // slab count is even (k is a multiple of 128).
+    // in LDS for every wave), then the MFMAs of slab s interleaved with the
+    // reads of slab s+1 and the fetch of slab s+NSTG into stage s % NSTG.
+    // After the last slab those reads hit a stale stage and are never used,
+    // which keeps the MFMA sequence free of branches.  The slab count is
+    // even (k is a multiple of 128).
     constexpr int NM = NKK * TI * TJ;                 // MFMA tiles per slab
     u32x4_t fa0[NKK][NFA], fb0[NKK][NFB], fa1[NKK][NFA], fb1[NKK][NFB];
 #pragma unroll
@@ -770,19 +779,43 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
         __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4) | 15 | (3 << 14));  // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (s + NSTG < nslab) issue(s + NSTG);   // into stage s % NSTG, read out already
       }
       const int nst = (s + 1) % NSTG;
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < NM; ++t) {
-        const int kk = t / (TI * TJ), i = (t / TJ) % TI, j = t % TJ;
-        mfma_tile(&ca[kk][i], &cb[kk][j], i, j);
-        if ((t & 1) && (t >> 1) < NF) read_one(na, nb, nst, t >> 1);
+      if constexpr (!b_km) {
+        // fetch first, then the MFMAs with one read of slab s+1 after every
+        // second MFMA
+        if (s + 1 < nslab && s + NSTG < nslab) issue(s + NSTG);   // into stage s % NSTG, read out already
         __builtin_amdgcn_sched_barrier(0);
-      }
 #pragma unroll
-      for (int q = NM / 2; q < NF; ++q) read_one(na, nb, nst, q);
+        for (int t = 0; t < NM; ++t) {
+          const int kk = t / (TI * TJ), i = (t / TJ) % TI, j = t % TJ;
+          mfma_tile(&ca[kk][i], &cb[kk][j], i, j);
+          if ((t & 1) && (t >> 1) < NF) read_one(na, nb, nst, t >> 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int q = NM / 2; q < NF; ++q) read_one(na, nb, nst, q);
+      } else {
+        // With transposing reads, every read must precede the fetch in
+        // program order: the compiler makes a transposing LDS read wait for
+        // all LDS DMA loads issued before it (vmcnt(0)), which would wait for
+        // the fetch just issued.  So the reads of slab s+1 go with the first
+        // NF MFMAs and the fetch follows them.
+#pragma unroll
+        for (int t = 0; t < NM; ++t) {
+          const int kk = t / (TI * TJ), i = (t / TJ) % TI, j = t % TJ;
+          mfma_tile(&ca[kk][i], &cb[kk][j], i, j);
+          if (t < NF) read_one(na, nb, nst, t);
+          if (t == NF - 1 && s + 1 < nslab && s + NSTG < nslab) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue(s + NSTG);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int q = NM; q < NF; ++q) read_one(na, nb, nst, q);
+      }
       if (s + 1 < nslab && ax_here(s + 1)) {
         __builtin_amdgcn_sched_barrier(0);
         add_ax(s + 1, nst);

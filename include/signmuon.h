@@ -88,7 +88,9 @@ typedef struct sm_hparams {
 
 /* One matrix of a parameter set. */
 typedef struct sm_matrix {
-  int64_t rows, cols;    /* both >= 1 */
+  int64_t rows, cols;    /* both in [1, 2^20]; with rows and cols rounded up
+                            to multiples of 128, rows*cols < 2^31 (2^30 when
+                            hp->ns_precision is SM_NS_F32), else SM_EINVAL */
   int64_t elem_off;      /* element offset in the flat G / W / Mom arrays */
   int64_t word_off;      /* word offset of its packed signs in a worker buffer */
 } sm_matrix;

@@ -92,6 +92,13 @@ def test_polar_workspace_and_validation():
     assert B.polar_ns_workspace(256, 512, _hp(eps=0.0)) == 0
     assert B.polar_ns_workspace(256, 512, _hp(scale="spectral", P=0)) == 0
     assert B.polar_ns_workspace(256, 512, _hp(K=65)) == 0
+    # size limits: dimensions up to 2^20; padded rows * cols below 2^31
+    # (2^30 for float32 Newton-Schulz operands, addressed with 32-bit byte offsets)
+    assert B.polar_ns_workspace(1, (1 << 20) + 1, hp) == 0
+    assert B.polar_ns_workspace(32768, 32768, hp) > 0
+    assert B.polar_ns_workspace(32768, 32768, _hp(K=5, precision="f32")) == 0
+    assert B.polar_ns_workspace(32768, 32640, _hp(K=5, precision="f32")) > 0
+    assert B.polar_ns_workspace(65536, 32768, hp) == 0
     c = hp.to_c()
     U = ctypes.c_void_p(0x20000)
     assert L.signmuon_polar_ns(FAKE, U, 256, 512, ctypes.byref(c), None, FAKE, 16,
