@@ -756,7 +756,9 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     // for LDS.  Per slab s: wait for slab s+1's fetch and for this wave's
     // reads of slab s, barrier (then stage s % NSTG is free and slab s+1 is
     // in LDS for every wave), then the MFMAs of slab s interleaved with the
-    // reads of slab s+1 and the fetch of slab s+NSTG into stage s % NSTG.
+    // reads of slab s+1 and the fetch of slab s+NSTG into stage s % NSTG
+    // (the Gram fetches first; the update reads its transposed fragments
+    // first, see below).
     // After the last slab those reads hit a stale stage and are never used,
     // which keeps the MFMA sequence free of branches.  The slab count is
     // even (k is a multiple of 128).
@@ -797,24 +799,27 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
 #pragma unroll
         for (int q = NM / 2; q < NF; ++q) read_one(na, nb, nst, q);
       } else {
-        // With transposing reads, every read must precede the fetch in
-        // program order: the compiler makes a transposing LDS read wait for
-        // all LDS DMA loads issued before it (vmcnt(0)), which would wait for
-        // the fetch just issued.  So the reads of slab s+1 go with the first
-        // NF MFMAs and the fetch follows them.
+        // The compiler makes a transposing LDS read wait for every LDS DMA
+        // load issued before it (vmcnt(0)), which would wait for the fetch
+        // just issued; plain reads get no such wait.  So the B fragments
+        // (transposing reads) go with the first MFMAs, then the fetch, then
+        // the A fragments.
+        constexpr int NB = NKK * NFB, NA = NKK * NFA;
+        static_assert(NB + NA <= NM, "read schedule");
+        auto qb = [&](int u) { return (u / NFB) * (NFA + NFB) + NFA + u % NFB; };
+        auto qa = [&](int u) { return (u / NFA) * (NFA + NFB) + u % NFA; };
 #pragma unroll
         for (int t = 0; t < NM; ++t) {
           const int kk = t / (TI * TJ), i = (t / TJ) % TI, j = t % TJ;
           mfma_tile(&ca[kk][i], &cb[kk][j], i, j);
-          if (t < NF) read_one(na, nb, nst, t);
-          if (t == NF - 1 && s + 1 < nslab && s + NSTG < nslab) {
+          if (t < NB) read_one(na, nb, nst, qb(t));
+          else if (t < NB + NA) read_one(na, nb, nst, qa(t - NB));
+          if (t == NB - 1 && s + 1 < nslab && s + NSTG < nslab) {
             __builtin_amdgcn_sched_barrier(0);
             issue(s + NSTG);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int q = NM; q < NF; ++q) read_one(na, nb, nst, q);
       }
       if (s + 1 < nslab && ax_here(s + 1)) {
         __builtin_amdgcn_sched_barrier(0);
