@@ -10,7 +10,9 @@ launch stream inside instrumented steps (the same work with the phases in
 sequence), the roofline of the dominant kernel (the Newton-Schulz GEMM) and
 the CPU oracle timed on a bounded sample.  `value` times plain steps, in
 which the momentum sweep, Newton-Schulz and vote of different matrix groups
-overlap on the library's internal streams.
+overlap on the library's internal streams.  An extra figure, `all_workers`,
+times steps in which all M workers' pipelines run on this GPU
+(signmuon_worker_pipeline for workers 1..M-1, then the step for worker 0).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload nanogpt]
 """
@@ -137,6 +139,9 @@ def main():
     ap.add_argument("--workload", default="nanogpt")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--rb-steps", type=int, default=5,
+                    help="timed steps of the all-workers figure (every worker's pipeline "
+                         "inside the step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain elementwise kernel that reads and writes "
                          "MIB MiB (reference for hardware byte counters)")
@@ -252,6 +257,31 @@ def main():
     mom_bytes = (4 + wbytes + 4 + 4 + 2) * d
     mom_gbps = mom_bytes / (phase_us.get("momentum", float("nan")) * 1e-6) / 1e9
 
+    # An extra figure: every worker's pipeline inside the step.
+    # Workers 1..M-1 run signmuon_worker_pipeline into their buffers with
+    # momenta of their own (the gradient values do not change the time, so
+    # they share G), then worker 0 runs the full step (its pipeline, the vote
+    # over the M fresh buffers and the apply).
+    # (At most 8 momentum buffers are kept and reused in turn: the work per
+    # worker is the same, and 200 workers' momenta would not fit in HBM.)
+    rb_steps = max(1, min(args.rb_steps, K))
+    n_mom = min(w.M - 1, 8)
+    Moms_b = [torch.zeros(d, dtype=torch.float32, device=dev) for _ in range(n_mom)]
+
+    def step_all_workers():
+        for m in range(1, w.M):
+            plan.worker_pipeline(G, W, Moms_b[(m - 1) % n_mom], bits, words, w.M, m, u0=u0)
+        step()
+
+    step_all_workers()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(rb_steps):
+        step_all_workers()
+    torch.cuda.synchronize()
+    rb_elapsed = time.perf_counter() - t0
+    del Moms_b
+
     steps_per_s = K / elapsed
     out = {
         "metric": METRIC,
@@ -281,6 +311,11 @@ def main():
         "momentum_gbps": round(mom_gbps, 1),
         "phases_us": {k: round(v, 2) for k, v in phase_us.items()},
         "instrumented_us_per_step": round(sum(phase_us.values()), 2),
+        "all_workers": {"value": round(rb_steps / rb_elapsed, 3), "unit": "steps/s",
+                      "steps": rb_steps, "ms_per_step": round(rb_elapsed / rb_steps * 1e3, 3),
+                      "what": f"all {w.M} workers' momentum + PolarNS + pack on this GPU, "
+                              "then the vote over the M buffers and the apply",
+                      "momentum_buffers": n_mom + 1},
     }
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

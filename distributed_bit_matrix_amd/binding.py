@@ -30,6 +30,7 @@ EXPORTS = (
     "signmuon_polar_ns_workspace", "signmuon_polar_ns", "signmuon_sign_pack",
     "signmuon_majority_vote", "signmuon_apply", "signmuon_step_workspace",
     "signmuon_step", "signmuon_step_profiled", "signmuon_get_status",
+    "signmuon_worker_pipeline",
 )
 PHASES = {0: "start", 1: "momentum", 2: "prescale", 3: "gemm", 4: "pack", 5: "vote"}
 
@@ -109,6 +110,8 @@ def lib():
             "signmuon_step_workspace": (sz, [mats, i32, hp, i32]),
             "signmuon_step": (i32, [mats, i32, hp, vp, vp, i32, vp, vp, i64, i32,
                                     i32, i32, vp, vp, sz, vp]),
+            "signmuon_worker_pipeline": (i32, [mats, i32, hp, vp, vp, i32, vp, vp, i64,
+                                               i32, i32, i32, vp, vp, sz, vp]),
             "signmuon_step_profiled": (i32, [mats, i32, hp, vp, vp, i32, vp, vp, i64,
                                              i32, i32, i32, vp, vp, sz,
                                              ctypes.POINTER(SmProfile), vp]),
@@ -273,6 +276,16 @@ class StepPlan:
         _check("signmuon_step", lib().signmuon_step(
             self.arr, len(self.mats), ctypes.byref(self.hpc), _ptr(G), _ptr(W),
             _wdtype(W), _ptr(Mom), _ptr(bits), stride, M, local_worker,
+            int(self.post_vote), _ptr(u0), _ptr(self.ws), self.ws.numel(),
+            _stream(stream)))
+
+    def worker_pipeline(self, G, W, Mom, bits, stride: int, M: int, worker: int,
+                        u0=None, stream=None):
+        """Worker `worker`'s momentum, PolarNS and sign packing (no vote,
+        W unchanged)."""
+        _check("signmuon_worker_pipeline", lib().signmuon_worker_pipeline(
+            self.arr, len(self.mats), ctypes.byref(self.hpc), _ptr(G), _ptr(W),
+            _wdtype(W), _ptr(Mom), _ptr(bits), stride, M, worker,
             int(self.post_vote), _ptr(u0), _ptr(self.ws), self.ws.numel(),
             _stream(stream)))
 

@@ -797,7 +797,8 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
                     const float* G, void* W, int32_t w_dtype, float* Mom,
                     uint32_t* bits, int64_t worker_stride_words, int32_t M,
                     int32_t local_worker, int32_t post_vote, const float* u0,
-                    void* ws, size_t ws_bytes, sm_profile* prof, hipStream_t stream) {
+                    void* ws, size_t ws_bytes, sm_profile* prof, hipStream_t stream,
+                    bool pipeline_only = false) {
   if (prof) {
     if (!prof->events || !prof->kinds || prof->capacity < 0) return SM_EINVAL;
     prof->count = 0;
@@ -906,6 +907,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
         HIP_TRY(mark(prof, SM_PHASE_PACK, stream));
       }
     }
+    if (pipeline_only) return SM_OK;
     va.mode = VA_APPLY;
     HIP_TRY(for_launches(groups, vote_fill, [&](const Groups& Gs) {
       va.G = Gs; return launch_vote_groups(va, stream);
@@ -924,6 +926,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
     return true;
   }, [&](const Groups& Gs) { ms.G = Gs; return launch_momentum_sign(ms, stream); }));
   HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
+  if (pipeline_only) return SM_OK;
   // padding of the operand copy (only matrices with a ragged shape)
   HIP_TRY(for_launches(groups, [&](Group& g) {
     const MatPlan& q = mp[g.idx0];
@@ -972,6 +975,18 @@ sm_status signmuon_step(const sm_matrix* mats, int32_t n_mats, const sm_hparams*
                         void* ws, size_t ws_bytes, hipStream_t stream) {
   return step_impl(mats, n_mats, hp, G, W, w_dtype, Mom, bits, worker_stride_words, M,
                    local_worker, post_vote, u0, ws, ws_bytes, nullptr, stream);
+}
+
+sm_status signmuon_worker_pipeline(const sm_matrix* mats, int32_t n_mats,
+                                   const sm_hparams* hp, const float* G, const void* W,
+                                   int32_t w_dtype, float* Mom, uint32_t* bits,
+                                   int64_t worker_stride_words, int32_t M, int32_t worker,
+                                   int32_t post_vote, const float* u0, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  // W is only read on this path
+  return step_impl(mats, n_mats, hp, G, const_cast<void*>(W), w_dtype, Mom, bits,
+                   worker_stride_words, M, worker, post_vote, u0, ws, ws_bytes, nullptr,
+                   stream, true);
 }
 
 sm_status signmuon_step_profiled(const sm_matrix* mats, int32_t n_mats,

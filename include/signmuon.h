@@ -198,6 +198,25 @@ sm_status signmuon_step(const sm_matrix *mats, int32_t n_mats,
                         hipStream_t stream);
 
 /*
+ * The per-worker half of signmuon_step for worker `worker` (Algorithm 2's
+ * local computation up to the packed signs, for every matrix of the set):
+ * post_vote = 0: momentum (in place in Mom), PolarNS of the new momentum and
+ * its signs packed into buffer `worker`; post_vote = 1: momentum and the
+ * signs of the new momentum packed into buffer `worker`.  No vote, and W is
+ * only read.  Arguments, validation and workspace as for signmuon_step (same
+ * workspace size); a non-finite G, W or momentum value is recorded for
+ * signmuon_get_status.  Calling it for workers 1..M-1 and signmuon_step for
+ * worker 0 runs every worker's pipeline of one step on this GPU.
+ */
+sm_status signmuon_worker_pipeline(const sm_matrix *mats, int32_t n_mats,
+                                   const sm_hparams *hp, const float *G,
+                                   const void *W, int32_t w_dtype, float *Mom,
+                                   uint32_t *bits, int64_t worker_stride_words,
+                                   int32_t M, int32_t worker, int32_t post_vote,
+                                   const float *u0, void *ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/*
  * Instrumented step: identical work to signmuon_step, plus a hipEventRecord
  * on `stream` after each phase so a caller can time the kernels of one step
  * (events[i] closes the phase kinds[i]; the first event opens the step).

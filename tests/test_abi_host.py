@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -120,6 +120,27 @@ def _step(L, mats, hp, M=3, local=0, stride=None, post=0, ws_bytes=None, G=FAKE)
         ws_bytes = B.step_workspace(mats, hp, bool(post))
     return L.signmuon_step(arr, len(mats), ctypes.byref(hp.to_c()), G, FAKE, 1, FAKE,
                            FAKE, stride, M, local, post, None, FAKE, ws_bytes, None)
+
+
+def test_worker_pipeline_validation():
+    # the per-worker half of the step validates like the step itself
+    L = B.lib()
+    hp = _hp()
+    mats, d, words = B.default_layout([(64, 96), (96, 64)])
+    arr = B.mats_array(mats)
+    ws = B.step_workspace(mats, hp, False)
+
+    def call(M=3, worker=0, post=0, G=FAKE, stride=words, ws_bytes=ws):
+        return L.signmuon_worker_pipeline(arr, len(mats), ctypes.byref(hp.to_c()), G, FAKE, 1,
+                                          FAKE, FAKE, stride, M, worker, post, None, FAKE,
+                                          ws_bytes, None)
+    assert call(M=0) == B.SM_ERANGE
+    assert call(worker=3) == B.SM_EINVAL
+    assert call(worker=-1) == B.SM_EINVAL
+    assert call(post=2) == B.SM_EINVAL
+    assert call(G=None) == B.SM_EINVAL
+    assert call(stride=words - 1) == B.SM_EINVAL
+    assert call(ws_bytes=1024) == B.SM_EWORKSPACE
 
 
 def test_step_validation():

@@ -235,3 +235,76 @@ def test_step_full_llm_mlp():
 @pytest.mark.slow
 def test_step_full_postvote():
     full_case("postvote", sample=[0, 1, 511, 512], bits_kind="ties")
+
+
+# --------------------------------------------------------------------------
+# Every worker's pipeline on the GPU (signmuon_worker_pipeline for workers
+# 1..M-1, then signmuon_step for worker 0): each buffer against the oracle's
+# worker, W unchanged by the worker calls, and the final W bit-exact wherever
+# every worker's bit equals the oracle's.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["nanogpt", "postvote"])
+def test_all_workers_on_gpu(name):
+    w, _, _ = SMALL[name]
+    if name == "postvote":
+        w = w.replace(M=12)
+    print(f"all workers {name} mats={len(w.mats)} M={w.M}", flush=True)
+    hp = hparams(w)
+    o = oracle_hp(hp)
+    st = GpuState(w, hp)
+    mats = list(w.mats)
+    offs, woffs = w.elem_offsets, w.word_offsets
+    M = w.M
+    W = WL.init_weights(w)
+    Moms = [0.05 * WL.init_momentum(w, m, std=1.0) for m in range(M)]
+    Gs = gradients(w, 0, M)
+    u0s = WL.power_start(w) if w.scale == "spectral" else None
+    out = O.step(mats, W, Moms, Gs, o, w.tie_value, w.post_vote, w.w_dtype,
+                 None if u0s is None else [u.astype(np.float64) for u in u0s])
+
+    W_t = torch.from_numpy(np.ascontiguousarray(W, np.float32)).cuda().to(st.wdt)
+    W_in = W_t.clone()
+    Mt = [torch.from_numpy(np.ascontiguousarray(np.float32(Moms[m]))).cuda() for m in range(M)]
+    Gt = [torch.from_numpy(np.ascontiguousarray(Gs[m], np.float32)).cuda() for m in range(M)]
+    rng = np.random.default_rng(7)
+    b_t = torch.from_numpy(rng.integers(0, 2**31, size=(M, st.words), dtype=np.int64)
+                           .astype(np.int32)).cuda()
+    u_t = None if u0s is None else torch.from_numpy(np.concatenate(u0s).astype(np.float32)).cuda()
+    for m in range(1, M):
+        st.plan.worker_pipeline(Gt[m], W_t, Mt[m], b_t, st.words, M, m, u0=u_t)
+    torch.cuda.synchronize()
+    assert st.plan.status() == B.SM_OK
+    assert torch.equal(W_t.view(torch.int16) if st.wdt == torch.bfloat16 else W_t.view(torch.int32),
+                       W_in.view(torch.int16) if st.wdt == torch.bfloat16 else W_in.view(torch.int32))
+    st.plan(Gt[0], W_t, Mt[0], b_t, st.words, M, 0, u0=u_t)
+    assert st.plan.status() == B.SM_OK
+    torch.cuda.synchronize()
+    Wg = W_t.float().cpu().numpy()
+    bg = b_t.cpu().numpy().view(np.uint32)
+    for m in range(M):
+        tol = momentum_tol(np.float32(Moms[m]), Gs[m], W, o["beta"], o["lam"])
+        assert np.all(np.abs(Mt[m].cpu().numpy().astype(np.float64) - out["Mom"][m]) <= tol), m
+    all_same = []
+    for i, (r, c) in enumerate(mats):
+        n = r * c
+        wsl = slice(woffs[i], woffs[i] + (n + 31) // 32)
+        same = np.ones(n, bool)
+        for m in range(M):
+            gneg = unpack_neg(bg[m, wsl], n)
+            ref = out["Mom"][m][offs[i]:offs[i] + n] if w.post_vote else out["U"][m][i].reshape(-1)
+            ok, stats = sign_gate(gneg, ref)
+            assert ok, (m, i, stats)
+            same &= gneg == unpack_neg(out["bits"][m, wsl], n)
+        all_same.append(same)
+        if not w.post_vote:
+            sl = slice(offs[i], offs[i] + n)
+            assert np.array_equal(Wg[sl][same].view(np.uint32),
+                                  out["Wn"][sl][same].view(np.uint32)), i
+    if w.post_vote:
+        # the post-vote update of a matrix is exact only if its whole majority matrix is
+        for i, (r, c) in enumerate(mats):
+            if all_same[i].all():
+                sl = slice(offs[i], offs[i] + r * c)
+                Ug = (W[sl].astype(np.float64) - Wg[sl].astype(np.float64)) / o["eta"]
+                Uo = (W[sl].astype(np.float64) - out["Wn"][sl].astype(np.float64)) / o["eta"]
+                assert np.abs(Ug - Uo).max() <= polar_tol(hp.precision) + 1e-6, i
