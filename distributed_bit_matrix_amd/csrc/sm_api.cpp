@@ -863,8 +863,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   va.bits = bits; va.stride = worker_stride_words;
   va.W = W; va.eta = hp->eta; va.status = B.status;
   auto vote_fill = [&](Group& g) {
-    int64_t nw = ((int64_t)g.rows * g.cols + 31) / 32;
-    g.blocks_per_mat = (int32_t)((nw + 255) / 256);
+    g.blocks_per_mat = vote_blocks_per_mat(va.mode, g.rows, g.cols);
     return true;
   };
 

@@ -499,18 +499,18 @@ hipError_t launch_momentum_sign(const MomSignArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Vote over the M resident buffers of each matrix, thread per word.
+// Vote over the M resident buffers of each matrix: the majority matrix into
+// the padded operand copy (VA_SBAR, a thread per packed word) or the update
+// of W (VA_APPLY, k_vote_apply8 below).
 // ---------------------------------------------------------------------------
 template <int NB>
 __global__ __launch_bounds__(256) void k_vote_groups(VoteArgs a) {
-  if (a.mode == VA_APPLY && a.status && a.status[0] != 0) return;
   int gi, mi, q;
   group_of_block(a.G, blockIdx.x, gi, mi, q);
   const Group& g = a.G.g[gi];
   const int rows = g.rows, cols = g.cols;
   const int64_t mn = (int64_t)rows * cols;
   const int64_t nw = (mn + 31) >> 5;
-  const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
   const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
   const int64_t w = (int64_t)q * 256 + threadIdx.x;
   float ss = 0.0f;
@@ -518,87 +518,106 @@ __global__ __launch_bounds__(256) void k_vote_groups(VoteArgs a) {
     uint32_t c[NB];
     count_votes<NB>(a.bits, a.stride, a.M, woff + w, c);
     const int64_t e0 = w * 32;
-    if (a.mode == VA_APPLY) {
-      const int64_t u = eoff + e0;
-      if (g.vec_ok && e0 + 32 <= mn) {
-        if (a.w_bf16) {
-          u32x4_t* wp = reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(a.W) + u);
-          u32x4_t xs[4];
+    // VA_SBAR: majority matrix into the padded operand copy S (a tall
+    // matrix is written transposed, one element at a time)
+    const int64_t Np = round_up(cols, kPad);
+    const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
+    if (cols % 32 == 0 && !s_tall(g)) {
+      int row = (int)(e0 / cols), col = (int)(e0 - (int64_t)row * cols);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) xs[k] = wp[k];
+      for (int h = 0; h < 4; ++h) {
+        float v[8];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            u32x4_t x = xs[k];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              int b0 = 8 * k + 2 * j;
-              float d0 = (float)majority(vote_sum_at<NB>(c, a.M, b0), a.tie);
-              float d1 = (float)majority(vote_sum_at<NB>(c, a.M, b0 + 1), a.tie);
-              float w0 = __uint_as_float(x[j] << 16);
-              float w1 = __uint_as_float(x[j] & 0xFFFF0000u);
-              bf16_t r0 = f32_to_bf16(apply_value(w0, a.eta, d0));
-              bf16_t r1 = f32_to_bf16(apply_value(w1, a.eta, d1));
-              x[j] = (uint32_t)r0 | ((uint32_t)r1 << 16);
-            }
-            wp[k] = x;
-          }
-        } else {
-          f32x4_t* wp = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.W) + u);
-          f32x4_t xs[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) xs[k] = wp[k];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            f32x4_t x = xs[k];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              x[j] = apply_value(x[j], a.eta,
-                                 (float)majority(vote_sum_at<NB>(c, a.M, 4 * k + j), a.tie));
-            wp[k] = x;
-          }
+        for (int k = 0; k < 8; ++k) {
+          v[k] = (float)majority(vote_sum_at<NB>(c, a.M, 8 * h + k), a.tie);
+          ss += v[k] * v[k];
         }
-      } else {
-        for (int b = 0; b < 32 && e0 + b < mn; ++b)
-          apply_store(a.W, a.w_bf16, u + b, a.eta,
-                      (float)majority(vote_sum_at<NB>(c, a.M, b), a.tie));
+        store_op8(a.precision, a.o_hi, a.o_lo, xoff + (int64_t)row * Np + col + 8 * h, v);
       }
     } else {
-      // VA_SBAR: majority matrix into the padded operand copy S (a tall
-      // matrix is written transposed, one element at a time)
-      const int64_t Np = round_up(cols, kPad);
-      const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
-      if (cols % 32 == 0 && !s_tall(g)) {
-        int row = (int)(e0 / cols), col = (int)(e0 - (int64_t)row * cols);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          float v[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            v[k] = (float)majority(vote_sum_at<NB>(c, a.M, 8 * h + k), a.tie);
-            ss += v[k] * v[k];
-          }
-          store_op8(a.precision, a.o_hi, a.o_lo, xoff + (int64_t)row * Np + col + 8 * h, v);
-        }
-      } else {
-        for (int b = 0; b < 32 && e0 + b < mn; ++b) {
-          int64_t e = e0 + b;
-          int row = (int)(e / cols), col = (int)(e - (int64_t)row * cols);
-          float v = (float)majority(vote_sum_at<NB>(c, a.M, b), a.tie);
-          ss += v * v;
-          store_opv(a.precision, a.o_hi, a.o_lo, xoff + s_index(g, row, col), v);
-        }
+      for (int b = 0; b < 32 && e0 + b < mn; ++b) {
+        int64_t e = e0 + b;
+        int row = (int)(e / cols), col = (int)(e - (int64_t)row * cols);
+        float v = (float)majority(vote_sum_at<NB>(c, a.M, b), a.tie);
+        ss += v * v;
+        store_opv(a.precision, a.o_hi, a.o_lo, xoff + s_index(g, row, col), v);
       }
     }
   }
-  if (a.mode == VA_SBAR && a.part) {
+  if (a.part) {
     float t = block_sum(ss);
     if (threadIdx.x == 0) a.part[g.c0 + (int64_t)mi * g.c_stride + q] = t;
   }
 }
 
+// VA_APPLY with 8 entries per thread, so that the W accesses of a wave are
+// contiguous (one 16-byte access per lane for bfloat16 W, two for float32);
+// the 4 lanes of one packed word each count its votes and use their 8 bits.
+template <int NB>
+__global__ __launch_bounds__(256) void k_vote_apply8(VoteArgs a) {
+  if (a.status && a.status[0] != 0) return;
+  int gi, mi, q;
+  group_of_block(a.G, blockIdx.x, gi, mi, q);
+  const Group& g = a.G.g[gi];
+  const int64_t mn = (int64_t)g.rows * g.cols;
+  const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
+  const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
+  const int64_t e0 = ((int64_t)q * 256 + threadIdx.x) * 8;
+  if (e0 >= mn) return;
+  uint32_t c[NB];
+  count_votes<NB>(a.bits, a.stride, a.M, woff + (e0 >> 5), c);
+  const int sh = (int)(e0 & 31);   // first bit of this thread's 8 in the word
+  const int64_t u = eoff + e0;
+  if (g.vec_ok && e0 + 8 <= mn) {
+    if (a.w_bf16) {
+      u32x4_t* wp = reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(a.W) + u);
+      u32x4_t x = *wp;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float d0 = (float)majority(vote_sum_at<NB>(c, a.M, sh + 2 * j), a.tie);
+        const float d1 = (float)majority(vote_sum_at<NB>(c, a.M, sh + 2 * j + 1), a.tie);
+        const bf16_t r0 = f32_to_bf16(apply_value(__uint_as_float(x[j] << 16), a.eta, d0));
+        const bf16_t r1 = f32_to_bf16(apply_value(__uint_as_float(x[j] & 0xFFFF0000u), a.eta, d1));
+        x[j] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+      }
+      *wp = x;
+    } else {
+      f32x4_t* wp = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.W) + u);
+      f32x4_t x0 = wp[0], x1 = wp[1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x0[j] = apply_value(x0[j], a.eta, (float)majority(vote_sum_at<NB>(c, a.M, sh + j), a.tie));
+        x1[j] = apply_value(x1[j], a.eta,
+                            (float)majority(vote_sum_at<NB>(c, a.M, sh + 4 + j), a.tie));
+      }
+      wp[0] = x0;
+      wp[1] = x1;
+    }
+  } else {
+    for (int b = 0; b < 8 && e0 + b < mn; ++b)
+      apply_store(a.W, a.w_bf16, u + b, a.eta,
+                  (float)majority(vote_sum_at<NB>(c, a.M, sh + b), a.tie));
+  }
+}
+
+int vote_blocks_per_mat(int mode, int64_t rows, int64_t cols) {
+  const int64_t mn = rows * cols;
+  if (mode == VA_APPLY) return (int)(((mn + 7) / 8 + 255) / 256);
+  return (int)(((mn + 31) / 32 + 255) / 256);
+}
+
 hipError_t launch_vote_groups(const VoteArgs& a, hipStream_t s) {
   if (a.G.total_blocks <= 0) return hipSuccess;
   dim3 grid(a.G.total_blocks), block(256);
+  if (a.mode == VA_APPLY) {
+    if (a.M <= 15)
+      hipLaunchKernelGGL(k_vote_apply8<4>, grid, block, 0, s, a);
+    else if (a.M <= 255)
+      hipLaunchKernelGGL(k_vote_apply8<8>, grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL(k_vote_apply8<16>, grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   if (a.M <= 15)
     hipLaunchKernelGGL(k_vote_groups<4>, grid, block, 0, s, a);
   else if (a.M <= 255)

@@ -99,6 +99,8 @@ struct VoteArgs {
   const int32_t* status;
 };
 hipError_t launch_vote_groups(const VoteArgs& a, hipStream_t s);
+// Group::blocks_per_mat of a vote launch in mode `mode`.
+int vote_blocks_per_mat(int mode, int64_t rows, int64_t cols);
 
 // Zero the padding of the padded operand copies.
 hipError_t launch_zero_pad(const Groups& G, int precision, void* hi, void* lo,
