@@ -560,7 +560,7 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
 constexpr int kChains = 3;
 struct ChainRes {
   hipStream_t s[kChains];
-  hipEvent_t fork, join[kChains];
+  hipEvent_t fork, join[kChains], head[kChains];
   hipError_t err = hipSuccess;
   std::mutex mu;   // one enqueue at a time per device
 };
@@ -579,20 +579,34 @@ hipError_t chain_resources(ChainRes** out) {
     if (R.err == hipSuccess) R.err = hipEventCreateWithFlags(&R.fork, hipEventDisableTiming);
     for (int c = 0; c < kChains && R.err == hipSuccess; ++c)
       R.err = hipEventCreateWithFlags(&R.join[c], hipEventDisableTiming);
+    for (int c = 0; c < kChains && R.err == hipSuccess; ++c)
+      R.err = hipEventCreateWithFlags(&R.head[c], hipEventDisableTiming);
   });
   *out = &R;
   return R.err;
 }
 
+// Optional work of a chain around its PolarNS: `head` stages run before the
+// pre-scale on the chain's stream, `tail` stages after the last
+// Newton-Schulz step, and every chain's tail waits until every chain's head
+// has finished (so work that must follow all heads, like a vote that is
+// skipped when any head found a non-finite value, can go in a tail).
+struct ChainHooks {
+  std::function<void(const std::vector<Group>&, hipStream_t, Stages&)> head, tail;
+};
+
 sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
                     const std::vector<Group>& groups, const std::vector<bool>& fusable,
                     const sm_hparams* hp, Bufs& B, const NsIO& io, int part_kind,
-                    hipStream_t s) {
+                    hipStream_t s, const ChainHooks* hooks = nullptr) {
   const int nc = (int)std::min<size_t>(kChains, groups.size());
   if (nc <= 1) {
-    sm_status st = run_pre_scale(P, mp, groups, hp, B, io, part_kind, s);
-    if (st != SM_OK || hp->K == 0) return st;
-    return run_ns(P, mp, groups, fusable, hp, B, io, s);
+    Stages st;
+    if (hooks) hooks->head(groups, s, st);
+    pre_scale_stages(P, mp, groups, hp, B, io, part_kind, s, st);
+    if (hp->K > 0) ns_stages(P, mp, groups, fusable, hp, B, io, s, st);
+    if (hooks) hooks->tail(groups, s, st);
+    return run_stages(st);
   }
   // longest-processing-time assignment of the groups to the chains, by
   // Newton-Schulz work count * m^2 * n
@@ -617,10 +631,27 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
   HIP_TRY(hipEventRecord(R->fork, s));
   NsIO cio = io;
   cio.prof = nullptr;
-  std::vector<Stages> prog(nc);
+  // heads[c] run (for every chain) before any stage of prog, so every head
+  // event is recorded before a tail waits for it
+  std::vector<Stages> heads(nc), prog(nc);
   for (int c = 0; c < nc; ++c) {
-    pre_scale_stages(P, mp, chain[c], hp, B, cio, part_kind, R->s[c], prog[c]);
-    if (hp->K > 0) ns_stages(P, mp, chain[c], fusable, hp, B, cio, R->s[c], prog[c]);
+    hipStream_t cs = R->s[c];
+    if (hooks) {
+      hooks->head(chain[c], cs, heads[c]);
+      heads[c].push_back([R, c, cs]() -> sm_status {
+        HIP_TRY(hipEventRecord(R->head[c], cs));
+        return SM_OK;
+      });
+    }
+    pre_scale_stages(P, mp, chain[c], hp, B, cio, part_kind, cs, prog[c]);
+    if (hp->K > 0) ns_stages(P, mp, chain[c], fusable, hp, B, cio, cs, prog[c]);
+    if (hooks) {
+      prog[c].push_back([R, nc, cs]() -> sm_status {
+        for (int o = 0; o < nc; ++o) HIP_TRY(hipStreamWaitEvent(cs, R->head[o], 0));
+        return SM_OK;
+      });
+      hooks->tail(chain[c], cs, prog[c]);
+    }
   }
   sm_status st = SM_OK;
   int forked = 0;
@@ -628,11 +659,13 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
     if (hipStreamWaitEvent(R->s[c], R->fork, 0) != hipSuccess) { st = SM_EHIP; break; }
     ++forked;
   }
-  size_t longest = 0;
-  for (const Stages& p : prog) longest = std::max(longest, p.size());
-  for (size_t i = 0; i < longest && st == SM_OK; ++i)
-    for (int c = 0; c < forked && st == SM_OK; ++c)
-      if (i < prog[c].size()) st = prog[c][i]();
+  for (const std::vector<Stages>* lists : {&heads, &prog}) {
+    size_t longest = 0;
+    for (const Stages& p : *lists) longest = std::max(longest, p.size());
+    for (size_t i = 0; i < longest && st == SM_OK; ++i)
+      for (int c = 0; c < forked && st == SM_OK; ++c)
+        if (i < (*lists)[c].size()) st = (*lists)[c][i]();
+  }
   // join every forked chain, also after an error, so that the caller's
   // stream orders after all work enqueued on the chains
   for (int c = 0; c < forked; ++c) {
@@ -888,13 +921,54 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
       sw.o_hi = B.x[0][0]; sw.o_lo = B.x[0][1];
       sw.part = P.spectral ? nullptr : B.part;
       sw.status = B.status;
-      HIP_TRY(for_launches(groups, [&](Group& g) {
+      auto sweep_fill = [&](Group& g) {
         g.blocks_per_mat = (int32_t)(mp[g.idx0].Mp * mp[g.idx0].Np / 4096);
         return true;
-      }, [&](const Groups& Gs) { sw.G = Gs; return launch_sweep(sw, stream); }));
-      HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
+      };
       io.first_xsrc = XS_USER; io.src_user = Mom;
       io.final_out = O_BITS; io.bits = local_bits; io.U = nullptr;
+      if (!prof) {
+        // Each chain sweeps its own matrices, runs their PolarNS, packs the
+        // signs the last epilogue could not, and votes over them, so one
+        // chain's memory-bound sweep and vote overlap another's GEMMs.  The
+        // votes wait for every chain's sweep: the update of W is skipped when
+        // any sweep found a non-finite value.
+        ChainHooks hooks;
+        hooks.head = [&](const std::vector<Group>& cg, hipStream_t cs, Stages& out) {
+          out.push_back([&, cs, pcg = &cg]() -> sm_status {
+            SweepArgs a = sw;
+            HIP_TRY(for_launches(*pcg, sweep_fill, [&](const Groups& Gs) {
+              a.G = Gs; return launch_sweep(a, cs);
+            }));
+            return SM_OK;
+          });
+        };
+        hooks.tail = [&](const std::vector<Group>& cg, hipStream_t cs, Stages& out) {
+          out.push_back([&, cs, pcg = &cg]() -> sm_status {
+            if (need_u)
+              for (const Group& g : *pcg)
+                for (int k = 0; k < g.count; ++k) {
+                  const int i = g.idx0 + k * g.idx_stride;
+                  if (fus[i]) continue;
+                  HIP_TRY(launch_sign_pack_flat(B.u + mats[i].elem_off,
+                                                local_bits + mats[i].word_off,
+                                                mats[i].rows * mats[i].cols, cs));
+                }
+            if (pipeline_only) return SM_OK;
+            VoteArgs a = va;
+            a.mode = VA_APPLY;
+            HIP_TRY(for_launches(*pcg, [&](Group& g) {
+              g.blocks_per_mat = vote_blocks_per_mat(VA_APPLY, g.rows, g.cols);
+              return true;
+            }, [&](const Groups& Gs) { a.G = Gs; return launch_vote_groups(a, cs); }));
+            return SM_OK;
+          });
+        };
+        return run_polar(P, mp, groups, fus, hp, B, io, 0, stream, &hooks);
+      }
+      HIP_TRY(for_launches(groups, sweep_fill,
+                           [&](const Groups& Gs) { sw.G = Gs; return launch_sweep(sw, stream); }));
+      HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
       st = run_polar(P, mp, groups, fus, hp, B, io, 0, stream);
       if (st != SM_OK) return st;
       if (need_u) {
