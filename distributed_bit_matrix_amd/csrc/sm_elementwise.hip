@@ -326,16 +326,19 @@ __device__ __forceinline__ void store_op4v(int precision, void* hi, void* lo,
 
 // Write the transpose of the 64x64 tile held in LDS (rows r0.., columns
 // c0.. of X) into S = X^T with row length ld.
+// Eight consecutive threads write one 64-entry row of S as 8-entry pieces,
+// so each store instruction covers whole rows.
 __device__ __forceinline__ void write_tile_t(const float (*tile)[65], int precision,
                                              void* hi, void* lo, int64_t xoff,
                                              int64_t ld, int r0, int c0) {
-  const int cc = threadIdx.x >> 2, rr0 = (threadIdx.x & 3) * 16;
+  const int ch = threadIdx.x & 7;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float v[4];
+  for (int pass = 0; pass < 2; ++pass) {
+    const int cc = (threadIdx.x >> 3) + 32 * pass;   // row of S = column of the tile
+    float v[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = tile[rr0 + 4 * k + e][cc];
-    store_op4v(precision, hi, lo, xoff + (int64_t)(c0 + cc) * ld + r0 + rr0 + 4 * k, v);
+    for (int e = 0; e < 8; ++e) v[e] = tile[8 * ch + e][cc];
+    store_op8(precision, hi, lo, xoff + (int64_t)(c0 + cc) * ld + r0 + 8 * ch, v);
   }
 }
 
