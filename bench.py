@@ -36,6 +36,24 @@ PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 matrix-core peak
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 
 
+def executed_ns_gflop(w) -> float:
+    """MFMA flops the library executes for one step's Newton-Schulz work:
+    operands padded to multiples of 128, the Gram (and the quintic square)
+    on the upper-triangular 128x128 tiles only, the update on every tile;
+    split-bfloat16 runs three MFMAs per product."""
+    r128 = lambda x: (x + 127) // 128 * 128  # noqa: E731
+    tot = 0.0
+    for r, c in w.mats:
+        Rp, Np = r128(min(r, c)), r128(max(r, c))
+        T = Rp // 128
+        sym = T * (T + 1) // 2 * 2.0 * 128 * 128
+        per = sym * Np + 2.0 * Rp * Rp * Np
+        if w.coeffs[2] != 0.0:
+            per += sym * Rp
+        tot += w.K * per
+    return tot * (3 if w.ns_precision == "bf16x3" else 1) / 1e9
+
+
 def gemm_traffic(workload):
     """HBM bytes of one step's Newton-Schulz GEMM launches from the committed
     counter summary, if it was taken on the current GEMM source; else None."""
@@ -250,6 +268,7 @@ def main():
 
     ns_flop = w.ns_gflop() * 1e9
     ns_tflops = ns_flop / (gemm_us * 1e-6) / 1e12
+    exec_tflops = executed_ns_gflop(w) * 1e9 / (gemm_us * 1e-6) / 1e12
     peak = PEAK_F32_TFLOPS if w.ns_precision == "f32" else PEAK_BF16_TFLOPS
     wbytes = 2 if w.w_dtype == "bf16" else 4
     vote_bytes = (w.M / 8.0 + 2 * wbytes) * d
@@ -306,6 +325,10 @@ def main():
                      "gemm_phases_per_step": gemm_per_step,
                      "ns_phase_us": round(gemm_us, 2)},
         "ns_mfma_util_pct": round(100 * ns_tflops / peak, 2),
+        # the same phase on the MFMA flops actually executed (symmetric Gram
+        # on its upper-triangular tiles, padded operands)
+        "ns_mfma_util_executed_pct": round(100 * exec_tflops / peak, 2),
+        "ns_executed_tflops": round(exec_tflops, 2),
         "vote_gbps": round(vote_bytes / (phase_us.get("vote", float("nan")) * 1e-6) / 1e9, 1),
         "vote_frac_hbm": round(vote_gbps / PEAK_HBM_GBPS, 4),
         "momentum_gbps": round(mom_gbps, 1),
