@@ -128,19 +128,28 @@ __device__ __forceinline__ void store_op8(int precision, void* hi, void* lo,
 // count of set bits (negative votes) at each of the 32 positions of a word.
 // ---------------------------------------------------------------------------
 template <int NB>
+__device__ __forceinline__ void add_vote(uint32_t (&c)[NB], uint32_t carry) {
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    uint32_t t = c[k] & carry;
+    c[k] ^= carry;
+    carry = t;
+  }
+}
+// The words of 8 workers are loaded together (a word of zeros past the
+// last worker adds nothing), so that 8 loads are in flight per lane.
+template <int NB>
 __device__ __forceinline__ void count_votes(const uint32_t* bits, int64_t stride,
                                             int M, int64_t w, uint32_t (&c)[NB]) {
 #pragma unroll
   for (int k = 0; k < NB; ++k) c[k] = 0;
-#pragma unroll 4
-  for (int m = 0; m < M; ++m) {
-    uint32_t carry = ld_nt(bits + (int64_t)m * stride + w);
+  for (int m = 0; m < M; m += 8) {
+    uint32_t v[8];
 #pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      uint32_t t = c[k] & carry;
-      c[k] ^= carry;
-      carry = t;
-    }
+    for (int j = 0; j < 8; ++j)
+      v[j] = m + j < M ? ld_nt(bits + (int64_t)(m + j) * stride + w) : 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) add_vote<NB>(c, v[j]);
   }
 }
 template <int NB>
@@ -605,13 +614,59 @@ __global__ __launch_bounds__(256) void k_vote_apply(VoteArgs a) {
   const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
   const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
   const int64_t wi = (ew >> 5) + lane;
-  uint32_t pos = 0, neg = 0;
-  if (wi < nw) {
-    uint32_t c[NB];
-    count_votes<NB>(a.bits, a.stride, a.M, woff + wi, c);
-    neg = count_gt<NB>(c, a.M / 2);           // 2 cnt > M
-    pos = ~count_gt<NB>(c, (a.M - 1) / 2);    // 2 cnt < M
+  auto masks = [&](uint32_t& pos, uint32_t& neg) {
+    pos = neg = 0;
+    if (wi < nw) {
+      uint32_t c[NB];
+      count_votes<NB>(a.bits, a.stride, a.M, woff + wi, c);
+      neg = count_gt<NB>(c, a.M / 2);           // 2 cnt > M
+      pos = ~count_gt<NB>(c, (a.M - 1) / 2);    // 2 cnt < M
+    }
+  };
+  uint32_t pos, neg;
+  if (g.vec_ok && ew + 2048 <= mn) {
+    // whole stretch, aligned: the W loads go out before the sign-word loads
+    if (a.w_bf16) {
+      u32x4_t* wp = reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(a.W) + eoff + ew) + lane;
+      u32x4_t x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = ld_nt(wp + 64 * j);
+      masks(pos, neg);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int src = 16 * j + (lane >> 2), sh = 8 * (lane & 3);
+        const uint32_t pb = (uint32_t)__shfl((int)pos, src) >> sh;
+        const uint32_t nb = (uint32_t)__shfl((int)neg, src) >> sh;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const bf16_t r0 = f32_to_bf16(apply_value(__uint_as_float(x[j][k] << 16), a.eta,
+                                                    vote_of(pb, nb, 2 * k, a.tie)));
+          const bf16_t r1 = f32_to_bf16(apply_value(__uint_as_float(x[j][k] & 0xFFFF0000u),
+                                                    a.eta, vote_of(pb, nb, 2 * k + 1, a.tie)));
+          x[j][k] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+        }
+        st_nt(wp + 64 * j, x[j]);
+      }
+    } else {
+      f32x4_t* wp = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.W) + eoff + ew) + lane;
+      f32x4_t x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = ld_nt(wp + 64 * j);
+      masks(pos, neg);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int src = 8 * j + (lane >> 3), sh = 4 * (lane & 7);
+        const uint32_t pb = (uint32_t)__shfl((int)pos, src) >> sh;
+        const uint32_t nb = (uint32_t)__shfl((int)neg, src) >> sh;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[j][k] = apply_value(x[j][k], a.eta, vote_of(pb, nb, k, a.tie));
+        st_nt(wp + 64 * j, x[j]);
+      }
+    }
+    return;
   }
+  // the last, partial stretch of a matrix, or unaligned W
+  masks(pos, neg);
   if (a.w_bf16) {
     bf16_t* W = reinterpret_cast<bf16_t*>(a.W);
 #pragma unroll

@@ -158,6 +158,30 @@ def test_step_multistep_small(name):
         W, Moms = out["Wn"], out["Mom"]
 
 
+# Sizes whose entry counts are odd: matrices start at unaligned offsets (no
+# 16-byte vector access of W), widths are not multiples of 32 (signs packed
+# by the separate pass), and the vote covers partial 2048-entry stretches.
+ODD_MATS = [(5, 37), (33, 7), (45, 71), (64, 19), (3, 3)]
+ODD = {
+    "f32_M5": WL.scaled(WL.get("single"), ODD_MATS, M=5, name="odd-f32"),
+    "bf16_M6": WL.scaled(WL.get("nanogpt"), ODD_MATS, M=6, name="odd-bf16"),
+}
+
+
+@pytest.mark.parametrize("name", list(ODD))
+def test_step_odd_sizes(name):
+    w = ODD[name]
+    assert any(o % 8 for o in w.elem_offsets)
+    print(f"odd-size step {name} mats={w.mats} M={w.M}", flush=True)
+    hp = hparams(w)
+    st = GpuState(w, hp)
+    W = WL.init_weights(w)
+    Moms = [np.zeros(w.d) for _ in range(w.M)]
+    for t in range(2):
+        out = check_step(w, st, hp, W, Moms, gradients(w, t, w.M), None)
+        W, Moms = out["Wn"], out["Mom"]
+
+
 def test_step_nonfinite_skips_update():
     w = SMALL["nanogpt"][0]
     hp = hparams(w)
