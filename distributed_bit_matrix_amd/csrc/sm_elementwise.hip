@@ -315,7 +315,7 @@ hipError_t launch_apply_flat(void* W, int w_bf16, const int8_t* D,
 }
 
 // ---------------------------------------------------------------------------
-// Padded sweep over 64x64 tiles of the padded matrix: momentum (or a plain
+// Padded sweep over 4096-entry tiles of the padded matrix: momentum (or a plain
 // float32 source) -> padded operand copy S (X, or X^T for a tall matrix,
 // transposed through LDS), partial sums of squares per tile, non-finite
 // flag.
@@ -368,17 +368,24 @@ __global__ __launch_bounds__(256) void k_sweep(SweepArgs a) {
   const bool tall = s_tall(g);
   const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
   const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
-  const int tiles_c = (int)(Np / 64);
-  const int r0 = (q / tiles_c) * 64, c0 = (q % tiles_c) * 64;
-  const int lr0 = threadIdx.x >> 4, lc = (threadIdx.x & 15) * 4;
+  // A block covers 4096 entries: a 64x64 tile when X is tall (transposed
+  // through LDS), else whole 256- or 128-column stretches of 16 or 32 rows,
+  // so that a wave's accesses are one or two contiguous row pieces.
+  // 2^lw threads share a row of the tile.
+  const int lw = tall ? 4 : (Np % 256 == 0 ? 6 : 5);
+  const int rstep = 256 >> lw;                     // rows per pass
+  const int tiles_c = (int)(Np >> (lw + 2));
+  const int r0 = (q / tiles_c) * 4 * rstep, c0 = (q % tiles_c) << (lw + 2);
+  const int lr0 = threadIdx.x >> lw, lc = (threadIdx.x & ((1 << lw) - 1)) * 4;
   const int col = c0 + lc;
-  // Each thread owns a 4-wide column strip in rows lr0 + 16 p (p < 4).  All
-  // loads are issued before any store (the momentum is read and written).
+  // Each thread owns a 4-wide column strip in rows lr0 + rstep p (p < 4).
+  // All loads are issued before any store (the momentum is read and
+  // written).
   float gv[4][4], wv[4][4], mv[4][4];
   bool full[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int row = r0 + lr0 + 16 * p;
+    const int row = r0 + lr0 + rstep * p;
     const int64_t u = eoff + (int64_t)row * cols + col;
     full[p] = row < rows && col + 4 <= cols && g.vec_ok;
     if (full[p]) {
@@ -422,7 +429,7 @@ __global__ __launch_bounds__(256) void k_sweep(SweepArgs a) {
   bool bad = false;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int row = r0 + lr0 + 16 * p;
+    const int row = r0 + lr0 + rstep * p;
     const int64_t u = eoff + (int64_t)row * cols + col;
     float v[4];
 #pragma unroll
