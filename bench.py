@@ -14,7 +14,11 @@ overlap on the library's internal streams.  An extra figure, `all_workers`,
 times steps in which all M workers' pipelines run on this GPU
 (signmuon_worker_pipeline for workers 1..M-1, then the step for worker 0).
 
+`other_workloads` gives the plain steps/s and phase times of further sets
+(by default the ResNet-50-shaped one).
+
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload nanogpt]
+                    [--also resnet50]
 """
 from __future__ import annotations
 
@@ -148,6 +152,99 @@ def cpu_baseline(w, budget_s):
             "seconds_per_step": t_step}
 
 
+class Run:
+    """One workload on the GPU: its plan, resident inputs, and the timing of
+    K plain steps followed by K instrumented steps (phases in sequence, an
+    event after each phase)."""
+
+    def __init__(self, w, dev):
+        import torch
+        from distributed_bit_matrix_amd import binding as B
+        from distributed_bit_matrix_amd import workloads as WL
+        self.w = w
+        hp = B.HParams(eta=w.eta, beta=w.beta, lam=w.lam, eps=w.eps, K=w.K, scale=w.scale,
+                       P=w.P, coeffs=w.coeffs, precision=w.ns_precision,
+                       tie_value=w.tie_value)
+        layout, self.d, self.words = B.default_layout(w.mats)
+        self.plan = B.StepPlan(layout, hp, w.post_vote, device=dev)
+        wdt = torch.bfloat16 if w.w_dtype == "bf16" else torch.float32
+        self.W = torch.from_numpy(WL.init_weights(w)).to(dev).to(wdt)
+        self.Mom = torch.zeros(self.d, dtype=torch.float32, device=dev)
+        self.G = torch.from_numpy(WL.gradient(w, 0, 0)).to(dev)
+        self.bits = torch.from_numpy(WL.random_bits(w, w.M).view(np.int32)).to(dev)
+        self.u0 = (torch.from_numpy(np.concatenate(WL.power_start(w))).to(dev)
+                   if w.scale == "spectral" else None)
+        torch.cuda.synchronize()
+
+    def step(self):
+        self.plan(self.G, self.W, self.Mom, self.bits, self.words, self.w.M, 0, u0=self.u0)
+
+    def measure(self, K, warmup):
+        """Returns (seconds for K plain steps, mean per-phase microseconds)."""
+        import torch
+        from distributed_bit_matrix_amd import binding as B
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+
+        # events for the instrumented steps
+        hip = hip_runtime()
+        cap = 64
+        evs = (ctypes.c_void_p * (cap * K))()
+        ev_list = []
+        for i in range(cap * K):
+            e = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            ev_list.append(e.value)
+            evs[i] = e.value
+        kinds = (ctypes.c_int32 * (cap * K))()
+        profs = []
+        for k in range(K):
+            p = B.SmProfile()
+            p.events = ctypes.cast(ctypes.byref(evs, k * cap * ctypes.sizeof(ctypes.c_void_p)),
+                                   ctypes.POINTER(ctypes.c_void_p))
+            p.kinds = ctypes.cast(ctypes.byref(kinds, k * cap * 4),
+                                  ctypes.POINTER(ctypes.c_int32))
+            p.capacity = cap
+            p.count = 0
+            profs.append(p)
+
+        # timed region: K production steps (the whole step runs as concurrent
+        # chains on the library's streams), bracketed by device synchronization
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(K):
+            self.step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+
+        # K instrumented steps for the phase breakdown: the same work with the
+        # phases in sequence and an event after each (Newton-Schulz chains
+        # only inside the polar phase)
+        torch.cuda.synchronize()
+        w = self.w
+        for k in range(K):
+            self.plan.profiled(profs[k], self.G, self.W, self.Mom, self.bits, self.words,
+                               w.M, 0, u0=self.u0)
+        torch.cuda.synchronize()
+
+        # per-phase durations from consecutive events of each step
+        phase = {}
+        ms = ctypes.c_float()
+        for k in range(K):
+            p = profs[k]
+            base = k * cap
+            for i in range(1, p.count):
+                hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(evs[base + i - 1]),
+                                        ctypes.c_void_p(evs[base + i]))
+                name = B.PHASES[kinds[base + i]]
+                phase[name] = phase.get(name, 0.0) + ms.value * 1e3
+        for e in ev_list:
+            hip.hipEventDestroy(ctypes.c_void_p(e))
+        return elapsed, {k: v / K for k, v in phase.items()}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -160,6 +257,9 @@ def main():
     ap.add_argument("--rb-steps", type=int, default=5,
                     help="timed steps of the all-workers figure (every worker's pipeline "
                          "inside the step)")
+    ap.add_argument("--also", default="resnet50",
+                    help="comma-separated further workloads whose plain steps/s and phase "
+                         "times are reported under other_workloads ('' = none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain elementwise kernel that reads and writes "
                          "MIB MiB (reference for hardware byte counters)")
@@ -169,28 +269,11 @@ def main():
                  "buffers on a single MI355X; --gpus above 1 is not supported")
 
     import torch
-    from distributed_bit_matrix_amd import binding as B
     from distributed_bit_matrix_amd import workloads as WL
 
     w = WL.get(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    hp = B.HParams(eta=w.eta, beta=w.beta, lam=w.lam, eps=w.eps, K=w.K, scale=w.scale,
-                   P=w.P, coeffs=w.coeffs, precision=w.ns_precision,
-                   tie_value=w.tie_value)
-    layout, d, words = B.default_layout(w.mats)
-    plan = B.StepPlan(layout, hp, w.post_vote, device=dev)
-    wdt = torch.bfloat16 if w.w_dtype == "bf16" else torch.float32
-    W = torch.from_numpy(WL.init_weights(w)).to(dev).to(wdt)
-    Mom = torch.zeros(d, dtype=torch.float32, device=dev)
-    G = torch.from_numpy(WL.gradient(w, 0, 0)).to(dev)
-    bits = torch.from_numpy(WL.random_bits(w, w.M).view(np.int32)).to(dev)
-    u0 = (torch.from_numpy(np.concatenate(WL.power_start(w))).to(dev)
-          if w.scale == "spectral" else None)
-    torch.cuda.synchronize()
-
-    def step():
-        plan(G, W, Mom, bits, words, w.M, 0, u0=u0)
 
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4
@@ -201,64 +284,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # events for the instrumented steps of the timed region
-    hip = hip_runtime()
-    cap = 64
+    run = Run(w, dev)
     K = args.steps
-    evs = (ctypes.c_void_p * (cap * K))()
-    ev_list = []
-    for i in range(cap * K):
-        e = ctypes.c_void_p()
-        if hip.hipEventCreate(ctypes.byref(e)) != 0:
-            raise RuntimeError("hipEventCreate failed")
-        ev_list.append(e.value)
-        evs[i] = e.value
-    kinds = (ctypes.c_int32 * (cap * K))()
-    profs = []
-    for k in range(K):
-        p = B.SmProfile()
-        p.events = ctypes.cast(ctypes.byref(evs, k * cap * ctypes.sizeof(ctypes.c_void_p)),
-                               ctypes.POINTER(ctypes.c_void_p))
-        p.kinds = ctypes.cast(ctypes.byref(kinds, k * cap * 4), ctypes.POINTER(ctypes.c_int32))
-        p.capacity = cap
-        p.count = 0
-        profs.append(p)
-
-    # timed region: K production steps (the whole step runs as concurrent
-    # chains on the library's streams), bracketed by device synchronization
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(K):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    # K instrumented steps for the phase breakdown: the same work with the
-    # phases in sequence and an event after each (Newton-Schulz chains only
-    # inside the polar phase)
-    torch.cuda.synchronize()
-    for k in range(K):
-        plan.profiled(profs[k], G, W, Mom, bits, words, w.M, 0, u0=u0)
-    torch.cuda.synchronize()
-
-    # per-phase durations from consecutive events of each step
-    phase = {}
-    ms = ctypes.c_float()
-    for k in range(K):
-        p = profs[k]
-        base = k * cap
-        for i in range(1, p.count):
-            hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(evs[base + i - 1]),
-                                    ctypes.c_void_p(evs[base + i]))
-            name = B.PHASES[kinds[base + i]]
-            phase[name] = phase.get(name, 0.0) + ms.value * 1e3
-    for e in ev_list:
-        hip.hipEventDestroy(ctypes.c_void_p(e))
-    phase_us = {k: v / K for k, v in phase.items()}
+    elapsed, phase_us = run.measure(K, args.warmup)
+    d, words, plan = run.d, run.words, run.plan
+    G, W, bits, u0 = run.G, run.W, run.bits, run.u0
+    step = run.step
     # The Newton-Schulz GEMM launches of a step run as concurrent chains on
     # the library's internal streams; the "gemm" phase is the span from the
     # fork to the join on the launching stream (pre-scale included).
@@ -301,6 +332,20 @@ def main():
     rb_elapsed = time.perf_counter() - t0
     del Moms_b
 
+    # Further workloads (the ResNet-50-shaped set by default): plain steps/s
+    # and the instrumented phase times, same method as above.
+    others = {}
+    for name in [n for n in args.also.split(",") if n and n != w.name]:
+        wo = WL.get(name)
+        ro = Run(wo, dev)
+        el, ph = ro.measure(K, args.warmup)
+        others[name] = {"value": round(K / el, 3), "unit": "steps/s",
+                        "ms_per_step": round(el / K * 1e3, 4), "config": describe(wo),
+                        "params": ro.d,
+                        "phases_us": {k: round(v, 2) for k, v in ph.items()}}
+        del ro
+        torch.cuda.synchronize()
+
     steps_per_s = K / elapsed
     out = {
         "metric": METRIC,
@@ -339,6 +384,7 @@ def main():
                       "what": f"all {w.M} workers' momentum + PolarNS + pack on this GPU, "
                               "then the vote over the M buffers and the apply",
                       "momentum_buffers": n_mom + 1},
+        "other_workloads": others,
     }
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstring>
 #include <functional>
+#include <map>
 #include <mutex>
 #include <vector>
 
@@ -87,7 +88,21 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
     q.idx = i;
     umax = std::max<int64_t>(umax, m.elem_off + m.rows * m.cols);
   }
-  P.x_total = x; P.r_total = r2; P.v_total = v; P.c_total = c;
+  // split-k of the long-k Grams of shapes with few triangular tiles (the
+  // decision counts every matrix of the shape, as one launch holds them)
+  std::map<std::pair<int64_t, int64_t>, int64_t> shape_count;
+  for (int i = 0; i < nm; ++i) ++shape_count[{mp[i].rows, mp[i].cols}];
+  int64_t kp = 0;
+  for (int i = 0; i < nm; ++i) {
+    MatPlan& q = mp[i];
+    const int64_t same = shape_count[{q.rows, q.cols}];
+    int slabs = 0;
+    q.ks = gemm_sym_ksplit(P.precision, q.Rp, q.tall ? q.Mp : q.Np, same, &slabs);
+    q.kslabs = slabs;
+    q.kp_off = kp;
+    kp += gemm_sym_kpart_floats(q.Rp, q.ks);
+  }
+  P.x_total = x; P.r_total = r2; P.v_total = v; P.c_total = c; P.kp_total = kp;
   const size_t opb = P.precision == P_F32 ? 4 : 2;   // bytes per operand part
   const bool split = P.precision == P_BF16X3;
   size_t off = 0;
@@ -112,6 +127,7 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
     P.off_vec = take(2 * v * 4);
   }
   P.off_part = take(c * 4);
+  if ((ns || P.spectral) && kp > 0) P.off_kpart = take(kp * 4);
   P.off_scal = take((size_t)nm * 4);
   if (need_u) P.off_u = take(umax * 4);
   (void)post_vote;
@@ -146,6 +162,7 @@ std::vector<Group> make_groups(const std::vector<MatPlan>& mp,
             g.x_stride = q.x_off - f.x_off; g.r_stride = q.r_off - f.r_off;
             g.v_stride = q.v_off - f.v_off; g.u0_stride = q.u0_off - f.u0_off;
             g.c_stride = q.c_off - f.c_off; g.idx_stride = q.idx - f.idx;
+            g.kp_stride = q.kp_off - f.kp_off;
             g.count = 2;
             continue;
           }
@@ -156,6 +173,7 @@ std::vector<Group> make_groups(const std::vector<MatPlan>& mp,
                    q.v_off == f.v_off + k * g.v_stride &&
                    q.u0_off == f.u0_off + k * g.u0_stride &&
                    q.c_off == f.c_off + k * g.c_stride &&
+                   q.kp_off == f.kp_off + k * g.kp_stride &&
                    q.idx == f.idx + k * g.idx_stride) {
           g.count += 1;
           continue;
@@ -170,6 +188,7 @@ std::vector<Group> make_groups(const std::vector<MatPlan>& mp,
     g.elem0 = q.elem_off; g.word0 = q.word_off;
     g.x0 = q.x_off; g.r0 = q.r_off; g.v0 = q.v_off; g.u0_0 = q.u0_off;
     g.c0 = q.c_off;
+    g.kp0 = q.kp_off; g.ksplit = q.ks; g.kslabs = q.kslabs;
     out.push_back(g);
   }
   return out;
@@ -221,6 +240,7 @@ struct Bufs {
   float* araw;
   float* vec;
   float* part;
+  float* kpart;
   float* scal;
   float* u;
 };
@@ -240,6 +260,7 @@ Bufs bind(const Plan& P, void* ws) {
   B.araw = static_cast<float*>(at(P.off_araw));
   B.vec = static_cast<float*>(at(P.off_vec));
   B.part = static_cast<float*>(at(P.off_part));
+  B.kpart = static_cast<float*>(at(P.off_kpart));
   B.scal = static_cast<float*>(at(P.off_scal));
   B.u = static_cast<float*>(at(P.off_u));
   return B;
@@ -302,7 +323,10 @@ void set_gemm_tiles(Group& g, int prec, int epi) {
   g.tile = tn;
   g.tiles_n = (g.gn + tn - 1) / tn;
   const int tiles_m = (g.gm + tm - 1) / tm;
-  g.blocks_per_mat = epi == E_UPDATE ? tiles_m * g.tiles_n : g.tiles_n * (g.tiles_n + 1) / 2;
+  // only the Gram and the raw Gram (k = the long side) are split
+  if (epi != E_OP && epi != E_RAW) g.ksplit = 1;
+  g.blocks_per_mat = epi == E_UPDATE ? tiles_m * g.tiles_n
+                                     : g.tiles_n * (g.tiles_n + 1) / 2 * (g.ksplit > 1 ? g.ksplit : 1);
 }
 
 // The enqueue of a PolarNS program is split into stages (one launch run
@@ -358,6 +382,7 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
         a.G = G;
         a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
         a.epi = E_OP; a.mul = gram_mul; a.scal = B.scal; a.scal_pow = 2;
+        a.kpart = B.kpart;
         a.o_hi = dst_hi; a.o_lo = dst_lo;
         return launch_gemm(prec, a, s);
       }));
@@ -373,6 +398,7 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
       a.G = G;
       a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
       a.epi = E_RAW; a.o_raw = B.araw;
+      a.kpart = B.kpart;
       return launch_gemm(prec, a, s);
     }));
     HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
@@ -475,6 +501,7 @@ void ns_stages(const Plan& P, const std::vector<MatPlan>& mp,
           a.G = G;
           a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
           a.epi = E_OP; a.mul = P.quintic ? 1.0f : hp->ns_b; a.scal_pow = 0;
+          a.kpart = B.kpart;
           a.o_hi = P.quintic ? B.a[0] : B.b[0];
           a.o_lo = P.quintic ? B.a[1] : B.b[1];
           return launch_gemm(prec, a, s);

@@ -21,6 +21,8 @@
 // prefetch pipeline; completion is tracked with explicit vmcnt waits and a
 // bare s_barrier.  All operand copies are zero padded to multiples of 128,
 // so no load is predicated and padding contributes exact zeros.
+#include <algorithm>
+#include <cstring>
 #include <type_traits>
 
 #include "sm_internal.h"
@@ -345,6 +347,9 @@ __device__ __forceinline__ void store_mirror(const f32x4_t (&v)[TI][TJ], void* h
       store_acc4<T, SPLIT>(hi, lo, off + (int64_t)(cbase + j * 16) * ld + rbase + i * 16, v[i][j]);
 }
 
+// Tile of the symmetric outputs (Gram, raw Gram, quintic square).
+constexpr int kTileSym = 128;
+
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
@@ -396,9 +401,15 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   constexpr bool SYM = EPI != E_UPDATE;
   const int a_fam = g.ops & 3, b_fam = (g.ops >> 2) & 3;
   int tm, tn;
+  // split-k (symmetric outputs with few tiles and long k): block t takes
+  // triangular tile t % ntri over the slabs of split t / ntri
+  int ks = 0, ttri = t;
   if constexpr (SYM) {
+    const int ntri = g.tiles_n * (g.tiles_n + 1) / 2;
+    ks = t / ntri;
+    ttri = t - ks * ntri;
     tm = 0;
-    int rem = t;
+    int rem = ttri;
     while (rem >= g.tiles_n - tm) { rem -= g.tiles_n - tm; ++tm; }
     tn = tm + rem;
   } else if (a_fam == FAM_R) {
@@ -512,7 +523,19 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     }
   };
 
-  const int nslab = g.gk / BK;
+  // slabs of this block: all of k, or those of split ks (the host makes
+  // every split non-empty and of an even slab count)
+  int nslab = g.gk / BK;
+  if (SYM && g.ksplit > 1) {
+    const int per = g.kslabs;
+    const int s0 = ks * per;
+    nslab = nslab - s0 < per ? nslab - s0 : per;
+#pragma unroll
+    for (int sp = 0; sp < SPLIT; ++sp) {
+      a_src[sp] += (int64_t)s0 * a_kst;
+      b_src[sp] += (int64_t)s0 * b_kst;
+    }
+  }
 
   // LDS stage: [A split 0][A split 1..][B split 0][B split 1..]
   auto a_tile = [&](int st, int sp) -> char* { return smem + st * STAGEB + sp * ATILE; };
@@ -826,6 +849,8 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
         add_ax(s + 1, nst);
       }
     };
+    // (slab counts are even here: k is a multiple of 128 elements, and
+    // split-k ranges are even)
     for (int s = 0; s < nslab; s += 2) {
       step(s, fa0, fb0, fa1, fb1);
       step(s + 1, fa1, fb1, fa0, fb0);
@@ -848,6 +873,23 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   // every wave is done reading the operand stages: LDS is free for staging
   __syncthreads();
 
+  if constexpr (SYM) {
+    if (g.ksplit > 1) {
+      // split-k: the raw float32 tile of this split in accumulator order
+      // (register group (i, j) of lane l of wave w at float4 index
+      // ((w TI + i) TJ + j) 64 + l, one coalesced 16-byte store each); the
+      // tile is summed over the splits and finished by k_split_reduce
+      static_assert(!SWAP && NW == 4 && TI == 4 && TJ == 4, "split-k accumulator order");
+      const int ntri = g.tiles_n * (g.tiles_n + 1) / 2;
+      f32x4_t* dst = reinterpret_cast<f32x4_t*>(A.kpart + g.kp0 + (int64_t)mi * g.kp_stride +
+                                                ((int64_t)ks * ntri + ttri) * (BMT * BNT));
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) dst[((wave * TI + i) * TJ + j) * 64 + lane] = acc[i][j];
+      return;
+    }
+  }
   if constexpr (EPI == E_RAW) {
     stage_store_tile<float, 1, BMT, BNT, TI, TJ, NT>(acc, smem, A.o_raw + roff, nullptr, Rp, m0,
                                                      n0, (int)Rp, wm, wn, lane, tid);
@@ -968,6 +1010,97 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
 }
 
 // ---------------------------------------------------------------------------
+// Split-k reduction of a symmetric output.  A block takes one 16-row block
+// of an upper-triangular 128x128 tile: the partial tiles are stored in the
+// GEMM's accumulator order, where the 16 rows 16 rb .. +15 (rb = 4 wm + i)
+// are register groups (i, j) of the two waves (wm, wn), wn = 0, 1: 8 x 64
+// float4 entries, float4 e of lane l holding rows 4 (l / 16) + 0..3 of
+// column 64 wn + 16 j + l % 16.  The block sums them over the splits in
+// split order (four splits in flight), transposes the sum through LDS into
+// rows, and finishes as the unsplit epilogue does: the raw Gram (RAW), or
+// the Gram operand scaled by mul (times c^2 for the first Gram), written in
+// place and, off the diagonal, as the mirror rows.
+// ---------------------------------------------------------------------------
+constexpr int kReduceRows = 16;
+template <typename T, int SPLIT, bool RAW>
+__global__ __launch_bounds__(256) void k_split_reduce(GemmArgs A) {
+  constexpr int TT = kTileSym, RR = kReduceRows, NRB = TT / RR;
+  __shared__ float img[RR][TT + 1];
+  const int gi = find_group(A.G, blockIdx.x);
+  const Group& g = A.G.g[gi];
+  const int lb = blockIdx.x - g.block0;
+  const int mi = lb / g.blocks_per_mat;
+  const int rest = lb - mi * g.blocks_per_mat;
+  const int t = rest / NRB, rb = rest - t * NRB;   // triangular tile, row block
+  int tm = 0, rem = t;
+  while (rem >= g.tiles_n - tm) { rem -= g.tiles_n - tm; ++tm; }
+  const int tn = tm + rem;
+  const int ntri = g.tiles_n * (g.tiles_n + 1) / 2;
+  const int64_t Rp = round_up(s_rows(g), kPad);
+  const int64_t roff = g.r0 + (int64_t)mi * g.r_stride;
+  const int64_t sstride = (int64_t)ntri * (TT * TT) / 4;    // float4 per split
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(
+      A.kpart + g.kp0 + (int64_t)mi * g.kp_stride + (int64_t)t * (TT * TT));
+  // this thread's two float4: lane l, groups q and q + 4 (q = wn * 4 + j)
+  const int l = threadIdx.x & 63, q0 = threadIdx.x >> 6;
+  const int wmb = rb >> 2, ib = rb & 3;
+  int idx[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = q0 + 4 * h, wn = q >> 2, j = q & 3;
+    idx[h] = (((wmb * 2 + wn) * 4 + ib) * 4 + j) * 64 + l;
+  }
+  f32x4_t s0 = src[idx[0]], s1 = src[idx[1]];
+  int k = 1;
+  for (; k + 3 < g.ksplit; k += 4) {
+    f32x4_t u[4][2];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      u[p][0] = src[(k + p) * sstride + idx[0]];
+      u[p][1] = src[(k + p) * sstride + idx[1]];
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) { s0 += u[p][0]; s1 += u[p][1]; }
+  }
+  for (; k < g.ksplit; ++k) {
+    s0 += src[k * sstride + idx[0]];
+    s1 += src[k * sstride + idx[1]];
+  }
+  float mul = 1.0f;
+  if constexpr (!RAW) {
+    const float cs = A.scal ? A.scal[g.idx0 + mi * g.idx_stride] : 1.0f;
+    mul = A.mul * (A.scal_pow == 2 ? cs * cs : 1.0f);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = q0 + 4 * h, wn = q >> 2, j = q & 3;
+    const f32x4_t& sv = h ? s1 : s0;
+    const int col = 64 * wn + 16 * j + (l & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) img[4 * (l >> 4) + e][col] = sv[e] * mul;
+  }
+  __syncthreads();
+  void* hi = RAW ? static_cast<void*>(A.o_raw) : A.o_hi;
+  void* lo = RAW ? nullptr : A.o_lo;
+  const int r = threadIdx.x >> 4, c8 = (threadIdx.x & 15) * 8;   // row of the block, 8 columns
+  float v0[4], v1[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { v0[e] = img[r][c8 + e]; v1[e] = img[r][c8 + 4 + e]; }
+  const int64_t o = roff + (int64_t)(tm * TT + rb * RR + r) * Rp + tn * TT + c8;
+  store_op4<T, SPLIT>(hi, lo, o, v0);
+  store_op4<T, SPLIT>(hi, lo, o + 4, v1);
+  if (tm == tn) return;
+  // mirror: output row tn*TT + cc, columns tm*TT + rb*RR .. +RR-1 (8 per thread)
+  const int cc = threadIdx.x >> 1, e0 = (threadIdx.x & 1) * 8;
+  float w0[4], w1[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { w0[e] = img[e0 + e][cc]; w1[e] = img[e0 + 4 + e][cc]; }
+  const int64_t om = roff + (int64_t)(tn * TT + cc) * Rp + tm * TT + rb * RR + e0;
+  store_op4<T, SPLIT>(hi, lo, om, w0);
+  store_op4<T, SPLIT>(hi, lo, om + 4, w1);
+}
+
+// ---------------------------------------------------------------------------
 // Host launcher
 // ---------------------------------------------------------------------------
 // Launch configurations.
@@ -1011,7 +1144,7 @@ struct Cfg {
     size_t img = (size_t)SPLIT * BMT * (BNT * sizeof(T) + 16);
     size_t raw = (size_t)BMT * (BNT * sizeof(float) + 16);  // raw Gram is float32
     size_t m = pipe > img ? pipe : img;
-    return EPI == E_RAW && m < raw ? raw : m;
+    return EPI == E_RAW && m < raw ? raw : m;   // the raw Gram is float32
   }
 };
 using CfgWide = Cfg<bf16_t, 1, E_UPDATE, true>;
@@ -1046,21 +1179,94 @@ static hipError_t launch_epi(const GemmArgs& args, hipStream_t s) {
   }
 }
 
+static_assert(Cfg<bf16_t, 1, E_OP>::BMT == kTileSym && Cfg<bf16_t, 2, E_OP>::BMT == kTileSym &&
+                  Cfg<float, 1, E_OP>::BMT == kTileSym && Cfg<bf16_t, 1, E_OP>::BNT == kTileSym,
+              "symmetric tile");
+
+// Slabs of at least this many per split; splits only while the launch has
+// fewer than kSplitBelow upper-triangular tiles, up to kSplitTarget blocks
+// and kSplitMax splits.
+constexpr int kSplitMinSlabs = 8, kSplitBelow = 128, kSplitTarget = 256, kSplitMax = 16;
+
+static int64_t sym_slabs(int precision, int64_t gk) {
+  return gk / (precision == P_F32 ? Cfg<float, 1, E_OP>::RB / 4 : Cfg<bf16_t, 1, E_OP>::RB / 2);
+}
+
+int gemm_sym_ksplit(int precision, int64_t rp, int64_t gk, int64_t count, int* slabs) {
+  const int64_t T = rp / kTileSym, tiles = T * (T + 1) / 2 * count;
+  const int64_t nslab = sym_slabs(precision, gk);
+  *slabs = (int)nslab;
+  if (tiles >= kSplitBelow || nslab < 2 * kSplitMinSlabs) return 1;
+  int64_t want = (kSplitTarget + tiles - 1) / tiles;
+  want = std::min<int64_t>({want, nslab / kSplitMinSlabs, (int64_t)kSplitMax});
+  if (want < 2) return 1;
+  // splits of `per` slabs, per even; the last one is shorter but not empty
+  int64_t per = (nslab + want - 1) / want;
+  per += per & 1;
+  const int64_t ks = (nslab + per - 1) / per;
+  if (ks < 2) return 1;
+  *slabs = (int)per;
+  return (int)ks;
+}
+
+int64_t gemm_sym_kpart_floats(int64_t rp, int ksplit) {
+  if (ksplit <= 1) return 0;
+  const int64_t T = rp / kTileSym;
+  return T * (T + 1) / 2 * ksplit * (int64_t)kTileSym * kTileSym;
+}
+
+template <typename T, int SPLIT, bool RAW>
+static hipError_t launch_reduce(const GemmArgs& args, hipStream_t s) {
+  // the groups of the launch that were split: kTileSym / kReduceRows blocks
+  // per triangular tile
+  GemmArgs r = args;
+  std::memset(&r.G, 0, sizeof(r.G));
+  int64_t blocks = 0;
+  for (int i = 0; i < args.G.n; ++i) {
+    Group g = args.G.g[i];
+    if (g.ksplit <= 1) continue;
+    g.blocks_per_mat = g.tiles_n * (g.tiles_n + 1) / 2 * (kTileSym / kReduceRows);
+    g.block0 = (int32_t)blocks;
+    blocks += (int64_t)g.blocks_per_mat * g.count;
+    r.G.g[r.G.n++] = g;
+  }
+  if (blocks == 0) return hipSuccess;
+  r.G.total_blocks = (int32_t)blocks;
+  hipLaunchKernelGGL((k_split_reduce<T, SPLIT, RAW>), dim3(r.G.total_blocks), dim3(256), 0, s, r);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s) {
   if (args.G.total_blocks <= 0) return hipSuccess;
   // every group of a launch carries the same column tile (the host splits
   // launches by it)
   const int tile = args.G.g[0].tile;
+  bool split = false;
   for (int i = 0; i < args.G.n; ++i) {
     const Group& g = args.G.g[i];
     int tm, tn;
     gemm_tile(precision, args.epi, g.gm, g.gn, g.gk, &tm, &tn);
     if (g.tile != tile || g.gk % 128 || g.tile != tn) return hipErrorInvalidValue;
+    if (g.ksplit > 1) {
+      // only the Gram and the raw Gram split, into non-empty slab ranges
+      const int64_t nslab = sym_slabs(precision, g.gk), per = g.kslabs;
+      if ((args.epi != E_OP && args.epi != E_RAW) || !args.kpart || per < 2 || (per & 1) ||
+          (int64_t)(g.ksplit - 1) * per >= nslab || (int64_t)g.ksplit * per < nslab ||
+          g.blocks_per_mat != g.tiles_n * (g.tiles_n + 1) / 2 * g.ksplit)
+        return hipErrorInvalidValue;
+      split = true;
+    }
   }
+  hipError_t e;
   if (tile == CfgWide::BNT) return launch_one<bf16_t, 1, E_UPDATE, true>(args, s);
-  if (precision == P_F32) return launch_epi<float, 1>(args, s);
-  if (precision == P_BF16X3) return launch_epi<bf16_t, 2>(args, s);
-  return launch_epi<bf16_t, 1>(args, s);
+  if (precision == P_F32) e = launch_epi<float, 1>(args, s);
+  else if (precision == P_BF16X3) e = launch_epi<bf16_t, 2>(args, s);
+  else e = launch_epi<bf16_t, 1>(args, s);
+  if (e != hipSuccess || !split) return e;
+  if (args.epi == E_RAW) return launch_reduce<float, 1, true>(args, s);
+  if (precision == P_F32) return launch_reduce<float, 1, false>(args, s);
+  if (precision == P_BF16X3) return launch_reduce<bf16_t, 2, false>(args, s);
+  return launch_reduce<bf16_t, 1, false>(args, s);
 }
 
 template <typename T, int SPLIT, int EPI, bool WIDE = false>

@@ -33,6 +33,9 @@ struct Group {
   int64_t v0, v_stride;          // power-iteration vector offset (Rp)
   int64_t u0_0, u0_stride;       // caller start vector offset (min dim)
   int64_t c0, c_stride;          // partial-sum chunk offset
+  int64_t kp0, kp_stride;        // split-k partial tiles offset (floats)
+  int32_t ksplit;                // k splits of the long-k symmetric GEMMs
+  int32_t kslabs;                // k slabs per split (even), if ksplit > 1
   // Filled per launch: block range and per-matrix work shape.
   int32_t block0;         // first block of this group in the launch
   int32_t blocks_per_mat;
@@ -111,6 +114,9 @@ struct MatPlan {
   int64_t x_off, r_off, v_off, u0_off, c_off;
   int64_t chunks;         // padded sweep chunks of kChunk elements
   int32_t idx;
+  int32_t ks;             // k splits of its Gram (1 = none)
+  int32_t kslabs;         // k slabs per split
+  int64_t kp_off;         // its split-k partial tiles (floats), if ks > 1
 };
 
 enum Precision { P_F32 = 0, P_BF16 = 1, P_BF16X3 = 2 };
@@ -120,7 +126,7 @@ struct Plan {
   int precision = P_BF16;
   bool quintic = false;
   bool spectral = false;
-  int64_t x_total = 0, r_total = 0, v_total = 0, c_total = 0;
+  int64_t x_total = 0, r_total = 0, v_total = 0, c_total = 0, kp_total = 0;
   // workspace byte offsets (0 = absent)
   size_t off_x[2][2] = {{0, 0}, {0, 0}};  // [pingpong][hi/lo] (or f32 in [p][0])
   size_t off_b[2] = {0, 0};   // Newton-Schulz right/left factor B (hi/lo)
@@ -128,6 +134,7 @@ struct Plan {
   size_t off_araw = 0;        // spectral: raw float32 Gram
   size_t off_vec = 0;         // power vectors, 2 * v_total floats
   size_t off_part = 0;        // partial sums, c_total floats
+  size_t off_kpart = 0;       // split-k partial Gram tiles, kp_total floats
   size_t off_scal = 0;        // per-matrix c = 1/(s+eps)
   size_t off_u = 0;           // float32 polar factor (unfused paths)
   size_t off_status = 0;      // int32 status word

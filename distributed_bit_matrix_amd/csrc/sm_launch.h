@@ -39,6 +39,7 @@ struct GemmArgs {
   uint32_t* bits;                  // O_BITS (buffer of the local worker)
   void* W; int32_t w_bf16; float eta;   // O_APPLY
   const int32_t* status;           // O_APPLY is skipped when *status != 0
+  float* kpart;                    // split-k partial tiles (groups with ksplit > 1)
 };
 
 hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s);
@@ -47,6 +48,14 @@ hipError_t gemm_set_attributes();
 // depth gk; every group of one launch must carry the same tn in
 // Group::tile.
 void gemm_tile(int precision, int epi, int64_t gm, int64_t gn, int64_t gk, int* tm, int* tn);
+// k splits of a symmetric (Gram) GEMM of rp x rp output and depth gk over
+// `count` matrices of one shape: 1 unless its upper-triangular tiles are too
+// few to occupy the GPU and k is long.  *slabs receives the k slabs per
+// split: even (the pipelined k-loop takes slabs in pairs), and the last
+// split is shorter but not empty.
+int gemm_sym_ksplit(int precision, int64_t rp, int64_t gk, int64_t count, int* slabs);
+// Floats of split-k partial tiles per matrix for that split.
+int64_t gemm_sym_kpart_floats(int64_t rp, int ksplit);
 
 // ---- elementwise and small kernels (sm_elementwise.hip) ----
 hipError_t launch_momentum_flat(const float* G, const void* W, int w_bf16,

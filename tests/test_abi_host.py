@@ -99,6 +99,11 @@ def test_polar_workspace_and_validation():
     assert B.polar_ns_workspace(32768, 32768, _hp(K=5, precision="f32")) == 0
     assert B.polar_ns_workspace(32768, 32640, _hp(K=5, precision="f32")) > 0
     assert B.polar_ns_workspace(65536, 32768, hp) == 0
+    # long k with one Gram tile: the Gram is split 8 ways along k, with a
+    # float32 128x128 partial tile per split in the workspace
+    ws_long = B.polar_ns_workspace(128, 4096, hp)
+    assert ws_long >= 2 * 2 * 128 * 4096 + 8 * 128 * 128 * 4
+    assert ws_long < 2 * 2 * 128 * 4096 + 9 * 128 * 128 * 4 + 64 * 1024
     c = hp.to_c()
     U = ctypes.c_void_p(0x20000)
     assert L.signmuon_polar_ns(FAKE, U, 256, 512, ctypes.byref(c), None, FAKE, 16,

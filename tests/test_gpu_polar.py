@@ -72,6 +72,23 @@ def test_polar_quintic(shape, precision):
     check(X, B.HParams(K=5, scale="spectral", P=10, coeffs=QUINTIC, precision=precision))
 
 
+# Long k with few Gram tiles: the Gram (and the raw Gram of the spectral
+# scale) is split along k into partial tiles that a second kernel sums.
+SPLIT_K = [((128, 4096), "bf16", "fro", (1.5, -0.5, 0.0)),
+           ((4096, 128), "bf16", "spectral", (1.5, -0.5, 0.0)),
+           ((256, 3000), "bf16x3", "fro", QUINTIC),
+           ((200, 2600), "f32", "spectral", (1.5, -0.5, 0.0)),
+           ((384, 2176), "bf16", "spectral", (1.5, -0.5, 0.0))]
+
+
+@pytest.mark.parametrize("shape,precision,scale,coeffs", SPLIT_K)
+def test_polar_split_k(shape, precision, scale, coeffs):
+    X = momentum_like(shape, 5)
+    u0 = np.random.default_rng(6).standard_normal(min(shape)).astype(np.float32)
+    hp = B.HParams(K=5, scale=scale, P=6, coeffs=coeffs, precision=precision)
+    check(X, hp, u0=u0 if scale == "spectral" else None)
+
+
 @pytest.mark.parametrize("K", [0, 1, 2])
 @pytest.mark.parametrize("scale", ["fro", "spectral"])
 def test_polar_few_steps(K, scale):
