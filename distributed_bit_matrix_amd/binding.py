@@ -300,3 +300,13 @@ class StepPlan:
 
     def status(self, stream=None) -> int:
         return int(lib().signmuon_get_status(_ptr(self.ws), _stream(stream)))
+
+    def capture(self, G, W, Mom, bits, stride: int, M: int, local_worker: int = 0,
+                u0=None):
+        """Recording the step into a HIP graph is switched off: with this
+        ROCm release, ending the capture of a step (torch.cuda.graph around
+        one call, the library's internal streams joined by events) ended the
+        process with a segmentation fault inside the runtime, and no cause
+        in the library has been found.  Steps are enqueued eagerly."""
+        raise SignMuonError("StepPlan.capture", SM_EUNSUPPORTED,
+                            "HIP graph capture of the step is disabled")
