@@ -14,6 +14,7 @@
 // of the majority matrix whose last epilogue applies W <- W - eta * U.
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <functional>
 #include <map>
@@ -585,6 +586,21 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
 // another chain and run behind it.
 // ---------------------------------------------------------------------------
 constexpr int kChains = 3;
+#ifndef SM_CHAIN_MIN_GFLOP
+#define SM_CHAIN_MIN_GFLOP 200
+#endif
+// Newton-Schulz flops per call below which one chain is used; the
+// environment variable SIGNMUON_CHAIN_MIN_GFLOP (read at every call)
+// overrides the default, e.g. 0 to always use the chains.
+double chain_min_flop() {
+  const char* e = std::getenv("SIGNMUON_CHAIN_MIN_GFLOP");
+  if (e && *e) {
+    char* end = nullptr;
+    const double v = std::strtod(e, &end);
+    if (end != e && v >= 0.0) return v * 1e9;
+  }
+  return SM_CHAIN_MIN_GFLOP * 1e9;
+}
 struct ChainRes {
   hipStream_t s[kChains];
   hipEvent_t fork, join[kChains], head[kChains];
@@ -626,7 +642,15 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
                     const std::vector<Group>& groups, const std::vector<bool>& fusable,
                     const sm_hparams* hp, Bufs& B, const NsIO& io, int part_kind,
                     hipStream_t s, const ChainHooks* hooks = nullptr) {
-  const int nc = (int)std::min<size_t>(kChains, groups.size());
+  // Sets with little Newton-Schulz work are bound by the host's launch
+  // rate: one chain puts all their groups into each launch (up to
+  // kMaxGroups per launch), a third of the launches of three chains.
+  double ns_flop = 0.0;
+  for (const Group& g : groups) {
+    const double m = std::min(g.rows, g.cols), n = std::max(g.rows, g.cols);
+    ns_flop += 4.0 * hp->K * g.count * m * m * n;
+  }
+  const int nc = ns_flop < chain_min_flop() ? 1 : (int)std::min<size_t>(kChains, groups.size());
   if (nc <= 1) {
     Stages st;
     if (hooks) hooks->head(groups, s, st);

@@ -143,10 +143,19 @@ SMALL = {
 }
 
 
+@pytest.fixture(params=["auto", "chains"])
+def chain_mode(request, monkeypatch):
+    """auto: the library's choice (one chain for these small sets); chains:
+    the concurrent chains forced (SIGNMUON_CHAIN_MIN_GFLOP=0)."""
+    if request.param == "chains":
+        monkeypatch.setenv("SIGNMUON_CHAIN_MIN_GFLOP", "0")
+    return request.param
+
+
 @pytest.mark.parametrize("name", list(SMALL))
-def test_step_multistep_small(name):
+def test_step_multistep_small(name, chain_mode):
     w, _, T = SMALL[name]
-    print(f"step {name} mats={len(w.mats)} M={w.M} T={T}", flush=True)
+    print(f"step {name} mats={len(w.mats)} M={w.M} T={T} {chain_mode}", flush=True)
     hp = hparams(w)
     st = GpuState(w, hp)
     W = WL.init_weights(w)
@@ -169,7 +178,7 @@ ODD = {
 
 
 @pytest.mark.parametrize("name", list(ODD))
-def test_step_odd_sizes(name):
+def test_step_odd_sizes(name, chain_mode):
     w = ODD[name]
     assert any(o % 8 for o in w.elem_offsets)
     print(f"odd-size step {name} mats={w.mats} M={w.M}", flush=True)
@@ -268,7 +277,7 @@ def test_step_full_postvote():
 # every worker's bit equals the oracle's.
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["nanogpt", "postvote"])
-def test_all_workers_on_gpu(name):
+def test_all_workers_on_gpu(name, chain_mode):
     w, _, _ = SMALL[name]
     if name == "postvote":
         w = w.replace(M=12)
