@@ -53,6 +53,14 @@ sm_status check_hparams(const sm_hparams* hp, bool need_momentum) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The Gram-space Newton-Schulz form is used for bfloat16 cubic steps with
+// the Frobenius scale unless the environment variable SIGNMUON_NS_FORM is
+// "iterate" (read at every call).
+bool gram_space_enabled() {
+  const char* e = std::getenv("SIGNMUON_NS_FORM");
+  return !(e && std::strcmp(e, "iterate") == 0);
+}
+
 // Per-matrix placement.  Returns SM_OK or SM_EINVAL for unusable shapes.
 sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
                      bool post_vote, bool need_u, Plan& P,
@@ -64,6 +72,11 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
               : hp->ns_precision == SM_NS_BF16X3 ? P_BF16X3 : P_BF16;
   P.quintic = hp->ns_c != 0.0f;
   P.spectral = hp->scale == SM_SCALE_SPECTRAL;
+  // Gram space only with the Frobenius scale: with the spectral scale the top
+  // singular values start near or above 1, where the Gram-space rounding
+  // missed the sign gate on test matrices that the iterate form passes
+  P.gram_space = P.precision == P_BF16 && !P.quintic && !P.spectral && hp->K > 0 &&
+                 gram_space_enabled();
   int64_t x = 0, r2 = 0, v = 0, c = 0, u0 = 0, umax = 0;
   for (int i = 0; i < nm; ++i) {
     const sm_matrix& m = mats[i];
@@ -129,6 +142,7 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
   }
   P.off_part = take(c * 4);
   if ((ns || P.spectral) && kp > 0) P.off_kpart = take(kp * 4);
+  if (P.gram_space) P.off_gs = take(5 * r2 * 2);
   P.off_scal = take((size_t)nm * 4);
   if (need_u) P.off_u = take(umax * 4);
   (void)post_vote;
@@ -242,6 +256,7 @@ struct Bufs {
   float* vec;
   float* part;
   float* kpart;
+  void* gs[5];     // Gram-space A_even, A_odd, T, Q_even, Q_odd
   float* scal;
   float* u;
 };
@@ -262,6 +277,8 @@ Bufs bind(const Plan& P, void* ws) {
   B.vec = static_cast<float*>(at(P.off_vec));
   B.part = static_cast<float*>(at(P.off_part));
   B.kpart = static_cast<float*>(at(P.off_kpart));
+  for (int j = 0; j < 5; ++j)
+    B.gs[j] = P.off_gs ? B.base + P.off_gs + (size_t)j * P.r_total * 2 : nullptr;
   B.scal = static_cast<float*>(at(P.off_scal));
   B.u = static_cast<float*>(at(P.off_u));
   return B;
@@ -352,10 +369,11 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
                       const NsIO& io, int part_kind, hipStream_t s, Stages& out) {
   const int prec = P.precision;
   const bool quin = P.quintic;
-  const float gram_mul = quin ? 1.0f : hp->ns_b;   // cubic folds b into B
+  // cubic folds b into B; the quintic and the Gram-space form keep A itself
+  const float gram_mul = quin || P.gram_space ? 1.0f : hp->ns_b;
   // operand that receives the scaled first Gram
-  void* dst_hi = quin ? B.a[0] : B.b[0];
-  void* dst_lo = quin ? B.a[1] : B.b[1];
+  void* dst_hi = P.gram_space ? B.gs[0] : quin ? B.a[0] : B.b[0];
+  void* dst_lo = P.gram_space ? nullptr : quin ? B.a[1] : B.b[1];
   auto gram_fill = [&P, &mp, prec](Group& g) {
     const MatPlan& q = mp[g.idx0];
     g.gm = g.gn = (int32_t)q.Rp;
@@ -477,11 +495,118 @@ hipError_t run_square(const Plan& P, const std::vector<MatPlan>& mp,
   });
 }
 
+// The K Newton-Schulz steps in Gram space (bfloat16 cubic).  Every iterate
+// is a polynomial in the first Gram A_0 = X_0 X_0^T times X_0: with
+// P_k = a I + b A_k,
+//   X_{k+1} = P_k X_k,  A_{k+1} = X_{k+1} X_{k+1}^T = P_k (P_k A_k),
+// and the polynomials commute, so X_K = Q_K X_0 with Q_1 = P_0 and
+// Q_{k+1} = P_k Q_k.  The steps run on Rp x Rp symmetric matrices
+// (upper-triangular tiles, mirrored):
+//   Q_{k+1} = a Q_k + b A_k Q_k,   T_k = a A_k + b A_k A_k,
+//   A_{k+1} = a T_k + b A_k T_k,
+// and one product Q_K S_0 gives the output (scaled by c, through the
+// update kernel's epilogues).  A_0 comes from the pre-scale (c^2 S S^T).
+// For a matrix m x n this executes about 2 m^2 n + 12 m^3 (upper-triangular)
+// flops instead of 5 x 3 m^2 n for K = 5.
+void gram_space_stages(const Plan& P, const std::vector<MatPlan>& mp,
+                       const std::vector<Group>& groups, const std::vector<bool>& fusable,
+                       const sm_hparams* hp, Bufs& B, const NsIO& io, hipStream_t s,
+                       Stages& out) {
+  const int prec = P.precision;
+  const int K = hp->K;
+  const float ca = hp->ns_a, cb = hp->ns_b;
+  void* const Abuf[2] = {B.gs[0], B.gs[1]};
+  void* const T = B.gs[2];
+  void* const Qbuf[2] = {B.gs[3], B.gs[4]};
+  // out = a Y + b X Y for symmetric, commuting X and Y
+  auto product = [&](void* X, void* Y, void* O) {
+    out.push_back([&, X, Y, O, prec, ca, cb, s]() -> sm_status {
+      HIP_TRY(for_launches(groups, [&](Group& g) {
+        const MatPlan& q = mp[g.idx0];
+        g.gm = g.gn = g.gk = (int32_t)q.Rp;
+        set_gemm_tiles(g, prec, E_SQUARE);
+        g.ops = gemm_ops(FAM_R, FAM_R2);
+        return true;
+      }, [&](const Groups& G) {
+        GemmArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.G = G;
+        a.r_hi = X; a.r2_hi = Y;
+        a.epi = E_SQUARE; a.cb = ca; a.cc = cb;
+        a.sq_hi = Y;
+        a.o_hi = O;
+        return launch_gemm(prec, a, s);
+      }));
+      HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+      return SM_OK;
+    });
+  };
+  // Q_1 = a I + b A_0
+  out.push_back([&, prec, ca, cb, s]() -> sm_status {
+    (void)prec;
+    HIP_TRY(for_launches(groups, [&](Group& g) {
+      const int64_t Rp = mp[g.idx0].Rp;
+      g.blocks_per_mat = (int32_t)(Rp * Rp / kChunk);
+      return true;
+    }, [&](const Groups& G) { return launch_affine_ident(G, B.gs[0], ca, cb, B.gs[4], s); }));
+    HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+    return SM_OK;
+  });
+  for (int k = 0; k + 1 < K; ++k) {
+    if (k >= 1) product(Abuf[k & 1], Qbuf[k & 1], Qbuf[(k + 1) & 1]);
+    product(Abuf[k & 1], Abuf[k & 1], T);
+    product(Abuf[k & 1], T, Abuf[(k + 1) & 1]);
+  }
+  if (K >= 2) product(Abuf[(K - 1) & 1], Qbuf[(K - 1) & 1], Qbuf[K & 1]);
+  void* const QK = Qbuf[K & 1];
+  // X_K = c Q_K S_0 into the requested output
+  out.push_back([&, QK, prec, s]() -> sm_status {
+    for (int pass = 0; pass < 2; ++pass) {
+      // pass 0: matrices using the requested final output; pass 1: the
+      // unfusable ones writing U into the workspace
+      if (pass == 1 && io.final_out != O_BITS) break;
+      int launched = 0;
+      HIP_TRY(for_launches(groups, [&](Group& g) {
+        const MatPlan& q = mp[g.idx0];
+        if (io.final_out == O_BITS && fusable[g.idx0] != (pass == 0)) return false;
+        g.gm = (int32_t)q.Rp; g.gn = (int32_t)(q.tall ? q.Mp : q.Np);
+        g.gk = (int32_t)q.Rp;
+        set_gemm_tiles(g, prec, E_UPDATE);
+        g.ops = gemm_ops(FAM_R, FAM_XK);
+        return true;
+      }, [&](const Groups& G) {
+        GemmArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.G = G;
+        a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
+        a.r_hi = QK;
+        a.epi = E_UPDATE; a.ca = 0.0f; a.xsrc = XS_OP;
+        a.scal = B.scal; a.scal_pow = 1;
+        if (io.final_out == O_BITS && pass == 1) {
+          a.out = O_U; a.U = B.u;
+        } else {
+          a.out = io.final_out;
+          a.U = io.U; a.bits = io.bits;
+          a.W = io.W; a.w_bf16 = io.w_bf16; a.eta = io.eta;
+          a.status = io.status;
+        }
+        return launch_gemm(prec, a, s);
+      }, &launched));
+      if (launched) HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+    }
+    return SM_OK;
+  });
+}
+
 // The K Newton-Schulz steps: step k reads the iterate from x[(k-1) & 1]
 // and writes x[k & 1] (the last one writes the final output instead).
 void ns_stages(const Plan& P, const std::vector<MatPlan>& mp,
                const std::vector<Group>& groups, const std::vector<bool>& fusable,
                const sm_hparams* hp, Bufs& B, const NsIO& io, hipStream_t s, Stages& out) {
+  if (P.gram_space) {
+    gram_space_stages(P, mp, groups, fusable, hp, B, io, s, out);
+    return;
+  }
   const int prec = P.precision;
   const int K = hp->K;
   for (int k = 1; k <= K; ++k) {

@@ -920,6 +920,40 @@ hipError_t launch_prescale(const Groups& G, int precision, const float* araw,
 }
 
 // ---------------------------------------------------------------------------
+// Q = a I + b A over each matrix's padded Gram-sized bfloat16 buffer (the
+// first factor of the Gram-space Newton-Schulz form); 8 entries per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_affine_ident(Groups G, const bf16_t* A, float a,
+                                                      float b, bf16_t* Q) {
+  int gi, mi, q;
+  group_of_block(G, blockIdx.x, gi, mi, q);
+  const Group& g = G.g[gi];
+  const int64_t Rp = round_up(s_rows(g), kPad);
+  const int64_t roff = g.r0 + (int64_t)mi * g.r_stride;
+  const int64_t p = (int64_t)q * kChunk + threadIdx.x * 8;
+  const int64_t row = p / Rp, col0 = p - row * Rp;
+  const u32x4_t x = *reinterpret_cast<const u32x4_t*>(A + roff + p);
+  u32x4_t o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float v0 = b * __uint_as_float(x[k] << 16);
+    float v1 = b * __uint_as_float(x[k] & 0xFFFF0000u);
+    if (row == col0 + 2 * k) v0 += a;
+    if (row == col0 + 2 * k + 1) v1 += a;
+    o[k] = (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
+  }
+  *reinterpret_cast<u32x4_t*>(Q + roff + p) = o;
+}
+
+hipError_t launch_affine_ident(const Groups& G, const void* A, float a, float b, void* Q,
+                               hipStream_t s) {
+  if (G.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_affine_ident, dim3(G.total_blocks), dim3(256), 0, s, G,
+                     reinterpret_cast<const bf16_t*>(A), a, b, reinterpret_cast<bf16_t*>(Q));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // K = 0: U = c * X (caller layout), or W -= eta * c * S from the operand.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_scaled_out(ScaledOutArgs a) {

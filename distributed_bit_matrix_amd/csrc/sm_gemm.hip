@@ -154,11 +154,11 @@ template <> struct Elem<float>  { static constexpr int per16 = 4; };
 
 // Per-matrix offset and row length of an operand family.
 __device__ __forceinline__ int64_t fam_off(const Group& g, int fam, int mi) {
-  return fam == FAM_R ? g.r0 + (int64_t)mi * g.r_stride
+  return fam >= FAM_R ? g.r0 + (int64_t)mi * g.r_stride
                       : g.x0 + (int64_t)mi * g.x_stride;
 }
 __device__ __forceinline__ int64_t fam_ld(const Group& g, int fam) {
-  return round_up(fam == FAM_R ? s_rows(g) : s_cols(g), kPad);
+  return round_up(fam >= FAM_R ? s_rows(g) : s_cols(g), kPad);
 }
 
 // ---------------------------------------------------------------------------
@@ -443,9 +443,9 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     return n0 + wn * WTN + (SWAP ? 4 * (lane >> 4) + r : (lane & 15)) + 16 * j;
   };
   const void* a_hi = a_fam == FAM_R ? A.r_hi : A.x_hi;
-  const void* b_hi = b_fam == FAM_R ? A.r_hi : A.x_hi;
+  const void* b_hi = b_fam == FAM_R ? A.r_hi : b_fam == FAM_R2 ? A.r2_hi : A.x_hi;
   const void* a_lo = a_fam == FAM_R ? A.r_lo : A.x_lo;
-  const void* b_lo = b_fam == FAM_R ? A.r_lo : A.x_lo;
+  const void* b_lo = b_fam == FAM_R ? A.r_lo : b_fam == FAM_R2 ? A.r2_lo : A.x_lo;
   const T* a_src[SPLIT];
   const T* b_src[SPLIT];
   a_src[0] = reinterpret_cast<const T*>(a_hi) + fam_off(g, a_fam, mi);

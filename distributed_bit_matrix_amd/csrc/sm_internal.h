@@ -126,6 +126,9 @@ struct Plan {
   int precision = P_BF16;
   bool quintic = false;
   bool spectral = false;
+  // Newton-Schulz in Gram space (bfloat16 cubic, Frobenius scale):
+  // X_K = Q_K X_0 with the iteration carried on Rp x Rp symmetric matrices
+  bool gram_space = false;
   int64_t x_total = 0, r_total = 0, v_total = 0, c_total = 0, kp_total = 0;
   // workspace byte offsets (0 = absent)
   size_t off_x[2][2] = {{0, 0}, {0, 0}};  // [pingpong][hi/lo] (or f32 in [p][0])
@@ -135,6 +138,7 @@ struct Plan {
   size_t off_vec = 0;         // power vectors, 2 * v_total floats
   size_t off_part = 0;        // partial sums, c_total floats
   size_t off_kpart = 0;       // split-k partial Gram tiles, kp_total floats
+  size_t off_gs = 0;          // Gram-space A, A', T, Q, Q' (bfloat16, r_total each)
   size_t off_scal = 0;        // per-matrix c = 1/(s+eps)
   size_t off_u = 0;           // float32 polar factor (unfused paths)
   size_t off_status = 0;      // int32 status word

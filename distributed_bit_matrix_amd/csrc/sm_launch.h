@@ -9,8 +9,9 @@ namespace sm {
 // length Np) read with k along its rows (FAM_X) or with k down its columns
 // (FAM_XK: the LDS tile holds k as rows and the fragments are read with the
 // transposing LDS load), and the padded Gram-sized buffers (Rp x Rp, FAM_R,
-// k along rows).
-enum { FAM_X = 0, FAM_XK = 1, FAM_R = 2 };
+// k along rows; FAM_R2 is a second such buffer, for products of two
+// different symmetric matrices).
+enum { FAM_X = 0, FAM_XK = 1, FAM_R = 2, FAM_R2 = 3 };
 // Group.ops: A-operand family in bits 0-1, B-operand family in bits 2-3.
 __host__ __device__ inline int gemm_ops(int a_fam, int b_fam) {
   return a_fam | (b_fam << 2);
@@ -28,6 +29,7 @@ struct GemmArgs {
   Groups G;
   const void* x_hi; const void* x_lo;   // FAM_X operand buffers
   const void* r_hi; const void* r_lo;   // FAM_R operand buffers
+  const void* r2_hi; const void* r2_lo; // FAM_R2 operand buffers
   int32_t epi, out, xsrc, scal_pow;
   float mul, ca, cb, cc;
   void* o_hi; void* o_lo;          // E_OP / E_SQUARE (R family), O_X (X family)
@@ -143,5 +145,9 @@ struct ScaledOutArgs {
 hipError_t launch_scaled_out(const ScaledOutArgs& a, hipStream_t s);
 
 hipError_t launch_clear_status(int32_t* status, hipStream_t s);
+// Q = a I + b A on each matrix's padded Rp x Rp bfloat16 buffer
+// (blocks_per_mat = Rp * Rp / kChunk).
+hipError_t launch_affine_ident(const Groups& G, const void* A, float a, float b, void* Q,
+                               hipStream_t s);
 
 }  // namespace sm

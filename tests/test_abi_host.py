@@ -77,7 +77,25 @@ def _hp(**kw):
     return B.HParams(**kw)
 
 
-def test_polar_workspace_and_validation():
+def test_polar_workspace_gram_space(monkeypatch):
+    # the Gram-space form (bfloat16 cubic) adds five Rp x Rp bfloat16 buffers
+    hp = _hp(K=5, scale="fro")
+    gram = B.polar_ns_workspace(256, 512, hp)
+    monkeypatch.setenv("SIGNMUON_NS_FORM", "iterate")
+    it = B.polar_ns_workspace(256, 512, hp)
+    assert gram - it == 5 * 256 * 256 * 2
+    # not used for split-bfloat16, float32, the quintic or the spectral scale
+    for kw in [dict(precision="bf16x3"), dict(precision="f32"),
+               dict(coeffs=(3.4445, -4.775, 2.0315)), dict(scale="spectral", P=3)]:
+        a = B.polar_ns_workspace(256, 512, _hp(K=5, **kw))
+        monkeypatch.delenv("SIGNMUON_NS_FORM")
+        assert B.polar_ns_workspace(256, 512, _hp(K=5, **kw)) == a
+        monkeypatch.setenv("SIGNMUON_NS_FORM", "iterate")
+
+
+def test_polar_workspace_and_validation(monkeypatch):
+    # sizes of the iterate form (the Gram-space form is checked above)
+    monkeypatch.setenv("SIGNMUON_NS_FORM", "iterate")
     L = B.lib()
     hp = _hp(K=5, scale="fro")
     w = B.polar_ns_workspace(256, 512, hp)
@@ -168,11 +186,15 @@ def test_step_validation():
     assert _step(L, [(0, 5, 0, 0)], hp) == B.SM_EINVAL
 
 
-def test_step_workspace_sizes():
+def test_step_workspace_sizes(monkeypatch):
     w = WL.get("nanogpt")
     mats, d, words = B.default_layout(w.mats)
     hp = _hp()
+    gram = B.step_workspace(mats, hp, False)
+    monkeypatch.setenv("SIGNMUON_NS_FORM", "iterate")
     ws = B.step_workspace(mats, hp, False)
+    # Gram-space buffers: five bfloat16 Rp x Rp per matrix
+    assert gram - ws == 5 * 2 * sum(min(a, b) ** 2 for a, b in w.mats)
     # two bfloat16 iterates of every matrix (ping-pong), plus the Gram-sized
     # factor
     x = 2 * 2 * d
