@@ -40,17 +40,34 @@ PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 matrix-core peak
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 
 
+def ns_form(w) -> str:
+    """The library's Newton-Schulz form for this workload: Gram space for
+    bfloat16 cubic steps with the Frobenius scale (unless SIGNMUON_NS_FORM
+    is 'iterate'), else the iterate form."""
+    if os.environ.get("SIGNMUON_NS_FORM") == "iterate":
+        return "iterate"
+    if w.ns_precision == "bf16" and w.coeffs[2] == 0.0 and w.scale == "fro" and w.K > 0:
+        return "gram_space"
+    return "iterate"
+
+
 def executed_ns_gflop(w) -> float:
     """MFMA flops the library executes for one step's Newton-Schulz work:
-    operands padded to multiples of 128, the Gram (and the quintic square)
-    on the upper-triangular 128x128 tiles only, the update on every tile;
-    split-bfloat16 runs three MFMAs per product."""
+    operands padded to multiples of 128, symmetric outputs (Grams, the
+    quintic square, the Gram-space products) on their upper-triangular
+    128x128 tiles only, the update on every tile; split-bfloat16 runs three
+    MFMAs per product.  Gram space: one Gram, 3K - 3 symmetric Rp x Rp
+    products and one Rp x Rp by Rp x Np product."""
     r128 = lambda x: (x + 127) // 128 * 128  # noqa: E731
+    gram_space = ns_form(w) == "gram_space"
     tot = 0.0
     for r, c in w.mats:
         Rp, Np = r128(min(r, c)), r128(max(r, c))
         T = Rp // 128
         sym = T * (T + 1) // 2 * 2.0 * 128 * 128
+        if gram_space:
+            tot += sym * Np + max(0, 3 * w.K - 3) * sym * Rp + 2.0 * Rp * Rp * Np
+            continue
         per = sym * Np + 2.0 * Rp * Rp * Np
         if w.coeffs[2] != 0.0:
             per += sym * Rp
@@ -295,7 +312,10 @@ def main():
     # fork to the join on the launching stream (pre-scale included).
     gemm_us = phase_us.get("gemm", float("nan"))
     quintic = w.coeffs[2] != 0.0
-    gemm_per_step = w.K * (3 if quintic else 2)
+    # GEMM launches per chain and step: iterate form K Grams + K updates
+    # (+ K squares for the quintic); Gram space one Gram, 3K - 3 symmetric
+    # products and the final product
+    gemm_per_step = 3 * w.K - 1 if ns_form(w) == "gram_space" else w.K * (3 if quintic else 2)
 
     ns_flop = w.ns_gflop() * 1e9
     ns_tflops = ns_flop / (gemm_us * 1e-6) / 1e12
@@ -367,13 +387,19 @@ def main():
                      "unit": "TFLOP/s", "frac": round(ns_tflops / peak, 4),
                      "traffic": gemm_traffic(w.name), "traffic_unit": "bytes per step",
                      "kernel": "k_gemm: the step's Newton-Schulz GEMM launches, timed as one phase",
+                     "work": "algorithmic: 4 m^2 n flops per Newton-Schulz step and matrix, the "
+                             "pages' iteration; see ns_executed_tflops for the MFMA flops the "
+                             "chosen form executes",
+                     "ns_form": ns_form(w),
                      "gemm_phases_per_step": gemm_per_step,
                      "ns_phase_us": round(gemm_us, 2)},
-        "ns_mfma_util_pct": round(100 * ns_tflops / peak, 2),
-        # the same phase on the MFMA flops actually executed (symmetric Gram
-        # on its upper-triangular tiles, padded operands)
-        "ns_mfma_util_executed_pct": round(100 * exec_tflops / peak, 2),
+        # MFMA utilisation: the MFMA flops actually executed (the chosen form,
+        # symmetric outputs on their upper-triangular tiles, padded operands)
+        # over the phase time, against the peak
+        "ns_mfma_util_pct": round(100 * exec_tflops / peak, 2),
         "ns_executed_tflops": round(exec_tflops, 2),
+        # the pages' iteration's flops over the same time (the roofline above)
+        "ns_algorithmic_pct_of_peak": round(100 * ns_tflops / peak, 2),
         "vote_gbps": round(vote_bytes / (phase_us.get("vote", float("nan")) * 1e-6) / 1e9, 1),
         "vote_frac_hbm": round(vote_gbps / PEAK_HBM_GBPS, 4),
         "momentum_gbps": round(mom_gbps, 1),
