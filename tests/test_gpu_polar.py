@@ -58,6 +58,24 @@ def test_polar_fro_cubic(shape, precision):
 
 
 @pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("K", [1, 2, 5])
+def test_polar_fro_cubic_iterate_form(shape, K, monkeypatch):
+    # bfloat16 cubic with the Frobenius scale runs in Gram space by default;
+    # the iterate form is held to the same gates
+    monkeypatch.setenv("SIGNMUON_NS_FORM", "iterate")
+    X = momentum_like(shape, 1)
+    check(X, B.HParams(K=K, scale="fro", precision="bf16"))
+
+
+@pytest.mark.parametrize("shape", [(256, 512), (512, 256), (64, 147), (1, 64), (200, 1000)])
+@pytest.mark.parametrize("K", [1, 2, 3])
+def test_polar_fro_cubic_gram_space_few_steps(shape, K):
+    # the Gram-space form with K = 1 (no symmetric products), 2 and 3
+    X = momentum_like(shape, 6)
+    check(X, B.HParams(K=K, scale="fro", precision="bf16"))
+
+
+@pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("precision", ["f32", "bf16"])
 def test_polar_spectral_cubic(shape, precision):
     X = momentum_like(shape, 2)

@@ -167,6 +167,20 @@ def test_step_multistep_small(name, chain_mode):
         W, Moms = out["Wn"], out["Mom"]
 
 
+def test_step_nanogpt_iterate_form(monkeypatch):
+    # the nanoGPT set's steps run in Gram space by default; the iterate form
+    # is held to the same gates
+    monkeypatch.setenv("SIGNMUON_NS_FORM", "iterate")
+    w, _, T = SMALL["nanogpt"]
+    hp = hparams(w)
+    st = GpuState(w, hp)
+    W = WL.init_weights(w)
+    Moms = [np.zeros(w.d) for _ in range(w.M)]
+    for t in range(T):
+        out = check_step(w, st, hp, W, Moms, gradients(w, t, w.M), None)
+        W, Moms = out["Wn"], out["Mom"]
+
+
 # Sizes whose entry counts are odd: matrices start at unaligned offsets (no
 # 16-byte vector access of W), widths are not multiples of 32 (signs packed
 # by the separate pass), and the vote covers partial 2048-entry stretches.
