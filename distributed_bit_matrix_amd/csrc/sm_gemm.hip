@@ -328,23 +328,24 @@ __device__ __forceinline__ void stage_store_tile(const f32x4_t (&v)[TI][TJ], cha
   }
 }
 
-// Four consecutive values held in one accumulator register group.
-template <typename T, int SPLIT>
-__device__ __forceinline__ void store_acc4(void* hi, void* lo, int64_t i, const f32x4_t& a) {
-  const float v[4] = {a[0], a[1], a[2], a[3]};
-  store_op4<T, SPLIT>(hi, lo, i, v);
-}
-
-// Mirror tile of a symmetric output: C(row..row+3, col) goes to row `col`,
-// columns row..row+3 (one 8- or 16-byte store per accumulator tile).
-template <typename T, int SPLIT, int TI, int TJ>
-__device__ __forceinline__ void store_mirror(const f32x4_t (&v)[TI][TJ], void* hi, void* lo,
-                                             int64_t off, int64_t ld, int rbase, int cbase) {
+// Mirror tile of a symmetric output, through LDS: the transpose of the
+// tile (rows n0.., columns m0..) is staged with the transposed-tile writes
+// (the 4 rows of a register group become 4 consecutive columns) and stored
+// as 16-byte row pieces.  Waits first for every thread to have read out the
+// previous image.
+template <typename T, int SPLIT, int BMT, int BNT, int TI, int TJ, int NT>
+__device__ __forceinline__ void stage_store_mirror(const f32x4_t (&v)[TI][TJ], char* smem,
+                                                   void* dst_hi, void* dst_lo, int64_t ld,
+                                                   int m0, int n0, int row_lim, int wm, int wn,
+                                                   int lane, int tid) {
+  f32x4_t vt[TJ][TI];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
-      store_acc4<T, SPLIT>(hi, lo, off + (int64_t)(cbase + j * 16) * ld + rbase + i * 16, v[i][j]);
+    for (int j = 0; j < TJ; ++j) vt[j][i] = v[i][j];
+  __syncthreads();
+  stage_store_tile<T, SPLIT, BNT, BMT, TJ, TI, NT, true>(vt, smem, dst_hi, dst_lo, ld, n0, m0,
+                                                         row_lim, wn, wm, lane, tid);
 }
 
 // Tile of the symmetric outputs (Gram, raw Gram, quintic square).
@@ -893,7 +894,9 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   if constexpr (EPI == E_RAW) {
     stage_store_tile<float, 1, BMT, BNT, TI, TJ, NT>(acc, smem, A.o_raw + roff, nullptr, Rp, m0,
                                                      n0, (int)Rp, wm, wn, lane, tid);
-    if (tm != tn) store_mirror<float, 1, TI, TJ>(acc, A.o_raw, nullptr, roff, Rp, ar0, ac0);
+    if (tm != tn)
+      stage_store_mirror<float, 1, BMT, BNT, TI, TJ, NT>(acc, smem, A.o_raw + roff, nullptr, Rp, m0,
+                                                         n0, (int)Rp, wm, wn, lane, tid);
   } else if constexpr (EPI == E_OP) {
     const float m = A.mul * (A.scal_pow == 2 ? cs * cs : 1.0f);
 #pragma unroll
@@ -903,7 +906,10 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
                                                      offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
                                                      (int)Rp, wm, wn, lane, tid);
-    if (tm != tn) store_mirror<T, SPLIT, TI, TJ>(acc, A.o_hi, A.o_lo, roff, Rp, ar0, ac0);
+    if (tm != tn)
+      stage_store_mirror<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
+                                                         offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
+                                                         (int)Rp, wm, wn, lane, tid);
   } else if constexpr (EPI == E_SQUARE) {
     // b A + c A^2; A is symmetric, so A(row..row+3, col) = A(col, row..row+3)
     // (combined tile by tile, so that the loaded values and the accumulator
@@ -921,7 +927,10 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
                                                      offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
                                                      (int)Rp, wm, wn, lane, tid);
-    if (tm != tn) store_mirror<T, SPLIT, TI, TJ>(acc, A.o_hi, A.o_lo, roff, Rp, ar0, ac0);
+    if (tm != tn)
+      stage_store_mirror<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
+                                                         offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
+                                                         (int)Rp, wm, wn, lane, tid);
   } else {
     // E_UPDATE:  acc = a X + B X (first step: X = the unscaled source), and
     // the iterate is c^p * acc with c = 1/(s+eps) on the first step.
