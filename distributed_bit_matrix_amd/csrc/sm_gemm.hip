@@ -733,6 +733,47 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     else return false;
   };
 
+  // The square kernel's term cb Y (out = cb Y + cc X Y, Y symmetric) is
+  // taken from the B operand tiles while they pass through LDS: the B tile
+  // holds rows n0.. of Y, and the slab holding k = m0 + wm*WTM + 16 i ..
+  // holds Y(col, row) = Y(row, col) for this wave's output rows.  It is
+  // added as (cb / cc) Y into the accumulators and the epilogue multiplies by
+  // cc (cc != 0; otherwise the epilogue loads Y).
+  const int sq_k0 = m0 + wm * WTM;
+  const bool sq_lds = EPI == E_SQUARE && A.cc != 0.0f;
+  const float sq_ratio = sq_lds ? A.cb / A.cc : 0.0f;
+  auto sq_here = [&](int s) {
+    if constexpr (EPI == E_SQUARE) return sq_lds && s * BK < sq_k0 + 16 * TI && sq_k0 < (s + 1) * BK;
+    else return false;
+  };
+  auto add_sq = [&](int s, int stg) SM_INLINE {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int kb = sq_k0 + 16 * i - s * BK;   // this 16-row block's k offset in the slab
+      if (kb < 0 || kb >= BK) continue;
+      const int kk = kb + 4 * (lane >> 4);      // 4 consecutive k (rows of the output)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int brow = wn * WTN + 16 * j + (lane & 15);   // output column - n0
+        float y[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sp = 0; sp < SPLIT; ++sp) {
+          const char* p = b_tile(stg, sp) + lds_off<RB>(brow, kk / P) + (kk % P) * (int)sizeof(T);
+          if constexpr (sizeof(T) == 4) {
+            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p);
+            y[0] += v[0]; y[1] += v[1]; y[2] += v[2]; y[3] += v[3];
+          } else {
+            const u32x2_t h = *reinterpret_cast<const u32x2_t*>(p);
+            y[0] += __uint_as_float(h[0] << 16); y[1] += __uint_as_float(h[0] & 0xFFFF0000u);
+            y[2] += __uint_as_float(h[1] << 16); y[3] += __uint_as_float(h[1] & 0xFFFF0000u);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] += sq_ratio * y[r];
+      }
+    }
+  };
+
   if constexpr (!PIPE) {
 #pragma unroll
     for (int s = 0; s < NSTG - 1; ++s)
@@ -773,6 +814,10 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
         __builtin_amdgcn_sched_barrier(0);
         if (ax_here(s)) add_ax(s, stg);
       }
+      if constexpr (EPI == E_SQUARE) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (sq_here(s)) add_sq(s, stg);
+      }
     }
   } else {
     // Software-pipelined k-loop: the fragments of slab s+1 are read into a
@@ -796,6 +841,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
 #pragma unroll
     for (int q = 0; q < NF; ++q) read_one(fa0, fb0, 0, q);
     if (ax_here(0)) add_ax(0, 0);
+    if (sq_here(0)) add_sq(0, 0);
     auto step = [&](int s, u32x4_t (&ca)[NKK][NFA], u32x4_t (&cb)[NKK][NFB],
                     u32x4_t (&na)[NKK][NFA], u32x4_t (&nb)[NKK][NFB]) SM_INLINE {
       if (s + 1 < nslab) {
@@ -848,6 +894,10 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       if (s + 1 < nslab && ax_here(s + 1)) {
         __builtin_amdgcn_sched_barrier(0);
         add_ax(s + 1, nst);
+      }
+      if (s + 1 < nslab && sq_here(s + 1)) {
+        __builtin_amdgcn_sched_barrier(0);
+        add_sq(s + 1, nst);
       }
     };
     // (slab counts are even here: k is a multiple of 128 elements, and
@@ -914,16 +964,24 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     // b A + c A^2; A is symmetric, so A(row..row+3, col) = A(col, row..row+3)
     // (combined tile by tile, so that the loaded values and the accumulator
     // never have to be held in registers side by side)
+    if (sq_lds) {
+      // cb Y was added from LDS as (cb / cc) Y
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        float x[4];
-        load_op4<T, SPLIT>(A.sq_hi, A.sq_lo, roff + (int64_t)(ac0 + j * 16) * Rp + ar0 + i * 16,
-                           x);
+        for (int j = 0; j < TJ; ++j) acc[i][j] *= A.cc;
+    } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = A.cb * x[r] + A.cc * acc[i][j][r];
-      }
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          float x[4];
+          load_op4<T, SPLIT>(A.sq_hi, A.sq_lo, roff + (int64_t)(ac0 + j * 16) * Rp + ar0 + i * 16,
+                             x);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = A.cb * x[r] + A.cc * acc[i][j][r];
+        }
+    }
     stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
                                                      offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
                                                      (int)Rp, wm, wn, lane, tid);
