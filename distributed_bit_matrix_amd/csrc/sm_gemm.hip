@@ -729,7 +729,8 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     }
   };
   auto ax_here = [&](int s) {
-    if constexpr (EPI == E_UPDATE) return !ax_user && s * BK < ax_k0 + 16 * TI && ax_k0 < (s + 1) * BK;
+    if constexpr (EPI == E_UPDATE)
+      return !ax_user && A.ca != 0.0f && s * BK < ax_k0 + 16 * TI && ax_k0 < (s + 1) * BK;
     else return false;
   };
 
