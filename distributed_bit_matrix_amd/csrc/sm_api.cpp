@@ -364,6 +364,16 @@ sm_status run_stages(const Stages& st) {
 
 // Pre-scale: c = 1/(s+eps) per matrix, and (K > 0) the first Gram operand
 // scaled by c^2.
+// In the Gram-space form the first Gram also writes Q_1 = a I + b A_0 from
+// its epilogue, unless one of the groups' Grams is split along k (then a
+// separate elementwise pass makes Q_1).
+bool gram_writes_q1(const Plan& P, const std::vector<Group>& groups) {
+  if (!P.gram_space) return false;
+  for (const Group& g : groups)
+    if (g.ksplit > 1) return false;
+  return true;
+}
+
 void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
                       const std::vector<Group>& groups, const sm_hparams* hp, Bufs& B,
                       const NsIO& io, int part_kind, hipStream_t s, Stages& out) {
@@ -403,6 +413,9 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
         a.epi = E_OP; a.mul = gram_mul; a.scal = B.scal; a.scal_pow = 2;
         a.kpart = B.kpart;
         a.o_hi = dst_hi; a.o_lo = dst_lo;
+        if (gram_writes_q1(P, groups)) {
+          a.o2_hi = B.gs[4]; a.o2_a = hp->ns_a; a.o2_b = hp->ns_b;
+        }
         return launch_gemm(prec, a, s);
       }));
       HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
@@ -541,8 +554,8 @@ void gram_space_stages(const Plan& P, const std::vector<MatPlan>& mp,
       return SM_OK;
     });
   };
-  // Q_1 = a I + b A_0
-  out.push_back([&, prec, ca, cb, s]() -> sm_status {
+  // Q_1 = a I + b A_0 (unless the first Gram wrote it)
+  if (!gram_writes_q1(P, groups)) out.push_back([&, prec, ca, cb, s]() -> sm_status {
     (void)prec;
     HIP_TRY(for_launches(groups, [&](Group& g) {
       const int64_t Rp = mp[g.idx0].Rp;

@@ -961,6 +961,26 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       stage_store_mirror<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
                                                          offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
                                                          (int)Rp, wm, wn, lane, tid);
+    if constexpr (sizeof(T) == 2 && SPLIT == 1) {
+      if (A.o2_hi) {
+        // o2 = o2_a I + o2_b (this tile), the identity on the diagonal tile
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[i][j][r] = A.o2_b * acc[i][j][r] + (acc_row(i, r) == acc_col(j, r) ? A.o2_a : 0.0f);
+        __syncthreads();   // the last image has been read out
+        stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o2_hi, roff),
+                                                         nullptr, Rp, m0, n0, (int)Rp, wm, wn,
+                                                         lane, tid);
+        if (tm != tn)
+          stage_store_mirror<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o2_hi, roff),
+                                                             nullptr, Rp, m0, n0, (int)Rp, wm, wn,
+                                                             lane, tid);
+      }
+    }
   } else if constexpr (EPI == E_SQUARE) {
     // b A + c A^2; A is symmetric, so A(row..row+3, col) = A(col, row..row+3)
     // (combined tile by tile, so that the loaded values and the accumulator
@@ -1315,6 +1335,9 @@ hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s) {
     int tm, tn;
     gemm_tile(precision, args.epi, g.gm, g.gn, g.gk, &tm, &tn);
     if (g.tile != tile || g.gk % 128 || g.tile != tn) return hipErrorInvalidValue;
+    // the second Gram output: bfloat16 Grams that are not split along k
+    if (args.o2_hi && (args.epi != E_OP || precision != P_BF16 || g.ksplit > 1))
+      return hipErrorInvalidValue;
     if (g.ksplit > 1) {
       // only the Gram and the raw Gram split, into non-empty slab ranges
       const int64_t nslab = sym_slabs(precision, g.gk), per = g.kslabs;

@@ -33,6 +33,9 @@ struct GemmArgs {
   int32_t epi, out, xsrc, scal_pow;
   float mul, ca, cb, cc;
   void* o_hi; void* o_lo;          // E_OP / E_SQUARE (R family), O_X (X family)
+  // E_OP, unsplit launches: also o2 = o2_a I + o2_b (the Gram operand) in
+  // bfloat16 (the Gram-space form's first factor), when o2_hi is set
+  void* o2_hi; float o2_a, o2_b;
   float* o_raw;                    // E_RAW
   const void* sq_hi; const void* sq_lo;   // E_SQUARE: A for the b*A term
   const float* scal;               // per-matrix c = 1/(s+eps) or NULL
