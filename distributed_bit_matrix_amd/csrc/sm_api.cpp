@@ -436,41 +436,43 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
     HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
     return SM_OK;
   });
-  // power iteration: u0 -> va, then P steps alternating va / vb
+  // power iteration: P >= 1 steps alternating va / vb (P is validated); the
+  // first step reads the start vector (u0, or ones) directly, and with K > 0
+  // the prescale launch derives the scale from the final vector itself, so a
+  // separate finalize launch only runs for K = 0.
   float* va = B.vec;
   float* vb = B.vec + P.v_total;
-  out.push_back([&, hp, va, s]() -> sm_status {
-    HIP_TRY(for_launches(groups, [&](Group& g) {
-      g.blocks_per_mat = (int32_t)((mp[g.idx0].Rp + 255) / 256);
-      return true;
-    }, [&](const Groups& G) { return launch_power_init(G, io.u0, va, s); }));
-    return SM_OK;
-  });
   for (int p = 0; p < hp->P; ++p) {
-    out.push_back([&, hp, va, vb, s]() -> sm_status {
+    const bool first = p == 0;
+    out.push_back([&, hp, va, vb, first, s]() -> sm_status {
       HIP_TRY(for_launches(groups, [&](Group& g) {
         g.blocks_per_mat = (int32_t)(mp[g.idx0].Rp / 16);
         return true;
-      }, [&](const Groups& G) { return launch_power_step(G, B.araw, va, vb, s); }));
+      }, [&](const Groups& G) {
+        return launch_power_step(G, B.araw, va, vb, io.u0, first, s);
+      }));
       return SM_OK;
     });
     std::swap(va, vb);
   }
-  out.push_back([&, hp, va, s]() -> sm_status {
-    HIP_TRY(for_launches(groups, [&](Group& g) { g.blocks_per_mat = 1; return true; },
-                         [&](const Groups& G) {
-                           return launch_power_finalize(G, va, hp->eps, B.scal, s);
-                         }));
-    HIP_TRY(mark(io.prof, SM_PHASE_PRESCALE, s));
-    return SM_OK;
-  });
-  if (hp->K == 0) return;
-  out.push_back([&, hp, gram_mul, dst_hi, dst_lo, prec, s]() -> sm_status {
+  if (hp->K == 0) {
+    out.push_back([&, hp, va, s]() -> sm_status {
+      HIP_TRY(for_launches(groups, [&](Group& g) { g.blocks_per_mat = 1; return true; },
+                           [&](const Groups& G) {
+                             return launch_power_finalize(G, va, hp->eps, B.scal, s);
+                           }));
+      HIP_TRY(mark(io.prof, SM_PHASE_PRESCALE, s));
+      return SM_OK;
+    });
+    return;
+  }
+  out.push_back([&, hp, va, gram_mul, dst_hi, dst_lo, prec, s]() -> sm_status {
     HIP_TRY(for_launches(groups, [&](Group& g) {
       g.blocks_per_mat = (int32_t)(mp[g.idx0].Rp * mp[g.idx0].Rp / kChunk);
       return true;
     }, [&](const Groups& G) {
-      return launch_prescale(G, prec, B.araw, B.scal, gram_mul, dst_hi, dst_lo, s);
+      return launch_prescale(G, prec, B.araw, B.scal, gram_mul, dst_hi, dst_lo, va,
+                             hp->eps, s);
     }));
     HIP_TRY(mark(io.prof, SM_PHASE_PRESCALE, s));
     return SM_OK;

@@ -802,31 +802,13 @@ hipError_t launch_fro_finalize(const Groups& G, const float* part, float eps,
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void k_power_init(Groups G, const float* u0,
-                                                    float* vec) {
-  int gi, mi, q;
-  group_of_block(G, blockIdx.x, gi, mi, q);
-  const Group& g = G.g[gi];
-  const int r = g.rows < g.cols ? g.rows : g.cols;
-  const int64_t Rp = round_up(r, kPad);
-  const int64_t i = (int64_t)q * 256 + threadIdx.x;
-  if (i >= Rp) return;
-  float v = 0.0f;
-  if (i < r) v = u0 ? u0[g.u0_0 + (int64_t)mi * g.u0_stride + i] : 1.0f;
-  vec[g.v0 + (int64_t)mi * g.v_stride + i] = v;
-}
-
-hipError_t launch_power_init(const Groups& G, const float* u0, float* vec,
-                             hipStream_t s) {
-  if (G.total_blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_power_init, dim3(G.total_blocks), dim3(256), 0, s, G, u0, vec);
-  return hipGetLastError();
-}
-
 // dst = A * (src / |src|) for 16 rows per block (4 per wave); each lane
-// takes 4 consecutive entries per 256-entry stretch of a row.
+// takes 4 consecutive entries per 256-entry stretch of a row.  With `first`
+// set, src is the start vector itself: u0's r entries (ones when u0 is null)
+// and zeros up to Rp.
 __global__ __launch_bounds__(256) void k_power_step(Groups G, const float* araw,
-                                                    const float* src, float* dst) {
+                                                    const float* src, float* dst,
+                                                    const float* u0, int first) {
   int gi, mi, q;
   group_of_block(G, blockIdx.x, gi, mi, q);
   const Group& g = G.g[gi];
@@ -835,15 +817,28 @@ __global__ __launch_bounds__(256) void k_power_step(Groups G, const float* araw,
   const int64_t voff = g.v0 + (int64_t)mi * g.v_stride;
   const int64_t roff = g.r0 + (int64_t)mi * g.r_stride;
   const float* x = src + voff;
+  const float* u = u0 ? u0 + g.u0_0 + (int64_t)mi * g.u0_stride : nullptr;
+  auto start = [&](int64_t i) -> float {
+    return i < r ? (u ? u[i] : 1.0f) : 0.0f;
+  };
   float ss = 0.0f;
-  for (int64_t i = threadIdx.x; i < Rp; i += 256) ss += x[i] * x[i];
+  for (int64_t i = threadIdx.x; i < Rp; i += 256) {
+    const float xi = first ? start(i) : x[i];
+    ss += xi * xi;
+  }
   ss = block_sum(ss);
   const float inv = ss > 0.0f ? 1.0f / sqrtf(ss) : 0.0f;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   const int64_t row0 = (int64_t)q * 16 + wave * 4;
   for (int64_t k = 4 * lane; k < Rp; k += 256) {
-    const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(x + k);
+    f32x4_t xv;
+    if (first) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) xv[t] = start(k + t);
+    } else {
+      xv = *reinterpret_cast<const f32x4_t*>(x + k);
+    }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const f32x4_t av = *reinterpret_cast<const f32x4_t*>(araw + roff + (row0 + rr) * Rp + k);
@@ -859,11 +854,27 @@ __global__ __launch_bounds__(256) void k_power_step(Groups G, const float* araw,
 }
 
 hipError_t launch_power_step(const Groups& G, const float* araw,
-                             const float* src, float* dst, hipStream_t s) {
+                             const float* src, float* dst, const float* u0,
+                             bool first, hipStream_t s) {
   if (G.total_blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_power_step, dim3(G.total_blocks), dim3(256), 0, s, G,
-                     araw, src, dst);
+                     araw, src, dst, u0, first ? 1 : 0);
   return hipGetLastError();
+}
+
+// 1 / (sqrt(|w|) + eps) for one matrix's final power-iteration vector w
+// (|w| estimates the top eigenvalue of the raw Gram, so its square root is
+// the top singular value); every thread of the block gets the value.
+__device__ __forceinline__ float power_scale(const Group& g, int mi, const float* w,
+                                             float eps) {
+  const int r = g.rows < g.cols ? g.rows : g.cols;
+  const int64_t Rp = round_up(r, kPad);
+  const float* x = w + g.v0 + (int64_t)mi * g.v_stride;
+  float ss = 0.0f;
+  for (int64_t i = threadIdx.x; i < Rp; i += 256) ss += x[i] * x[i];
+  ss = block_sum(ss);
+  const float lam = sqrtf(ss);
+  return 1.0f / (sqrtf(lam) + eps);
 }
 
 __global__ __launch_bounds__(256) void k_power_finalize(Groups G, const float* w,
@@ -871,16 +882,8 @@ __global__ __launch_bounds__(256) void k_power_finalize(Groups G, const float* w
   int gi, mi, q;
   group_of_block(G, blockIdx.x, gi, mi, q);
   const Group& g = G.g[gi];
-  const int r = g.rows < g.cols ? g.rows : g.cols;
-  const int64_t Rp = round_up(r, kPad);
-  const float* x = w + g.v0 + (int64_t)mi * g.v_stride;
-  float ss = 0.0f;
-  for (int64_t i = threadIdx.x; i < Rp; i += 256) ss += x[i] * x[i];
-  ss = block_sum(ss);
-  if (threadIdx.x == 0) {
-    float lam = sqrtf(ss);
-    scal[g.idx0 + mi * g.idx_stride] = 1.0f / (sqrtf(lam) + eps);
-  }
+  const float c = power_scale(g, mi, w, eps);
+  if (threadIdx.x == 0) scal[g.idx0 + mi * g.idx_stride] = c;
 }
 
 hipError_t launch_power_finalize(const Groups& G, const float* w, float eps,
@@ -891,15 +894,24 @@ hipError_t launch_power_finalize(const Groups& G, const float* w, float eps,
   return hipGetLastError();
 }
 
+// With w set, each block derives c from the final power vector itself (the
+// same sum as the finalize kernel) and the matrix's first block stores it.
 __global__ __launch_bounds__(256) void k_prescale(Groups G, int precision,
                                                   const float* araw,
-                                                  const float* scal, float mul,
-                                                  void* hi, void* lo) {
+                                                  float* scal, float mul,
+                                                  void* hi, void* lo,
+                                                  const float* w, float eps) {
   int gi, mi, q;
   group_of_block(G, blockIdx.x, gi, mi, q);
   const Group& g = G.g[gi];
   const int64_t roff = g.r0 + (int64_t)mi * g.r_stride;
-  const float c = scal[g.idx0 + mi * g.idx_stride];
+  float c;
+  if (w) {
+    c = power_scale(g, mi, w, eps);
+    if (q == 0 && threadIdx.x == 0) scal[g.idx0 + mi * g.idx_stride] = c;
+  } else {
+    c = scal[g.idx0 + mi * g.idx_stride];
+  }
   const float m = mul * c * c;
   const int64_t p = roff + (int64_t)q * kChunk + threadIdx.x * 8;
   float v[8];
@@ -911,11 +923,11 @@ __global__ __launch_bounds__(256) void k_prescale(Groups G, int precision,
 }
 
 hipError_t launch_prescale(const Groups& G, int precision, const float* araw,
-                           const float* scal, float mul, void* hi, void* lo,
-                           hipStream_t s) {
+                           float* scal, float mul, void* hi, void* lo,
+                           const float* w, float eps, hipStream_t s) {
   if (G.total_blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_prescale, dim3(G.total_blocks), dim3(256), 0, s, G,
-                     precision, araw, scal, mul, hi, lo);
+                     precision, araw, scal, mul, hi, lo, w, eps);
   return hipGetLastError();
 }
 

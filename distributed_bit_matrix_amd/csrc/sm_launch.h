@@ -125,16 +125,17 @@ hipError_t launch_fro_finalize(const Groups& G, const float* part, float eps,
                                float* scal, hipStream_t s);
 
 // Power iteration on the padded raw Gram.
-hipError_t launch_power_init(const Groups& G, const float* u0, float* vec,
-                             hipStream_t s);
+// first: src is ignored and the start vector (u0, or ones) is read instead.
 hipError_t launch_power_step(const Groups& G, const float* araw,
-                             const float* src, float* dst, hipStream_t s);
+                             const float* src, float* dst, const float* u0,
+                             bool first, hipStream_t s);
 hipError_t launch_power_finalize(const Groups& G, const float* w, float eps,
                                  float* scal, hipStream_t s);
-// op = mul * c^2 * araw (padded Rp x Rp) in the operand precision.
+// op = mul * c^2 * araw (padded Rp x Rp) in the operand precision; c is
+// scal's entry, or (w non-null) the power-iteration scale of w, then stored.
 hipError_t launch_prescale(const Groups& G, int precision, const float* araw,
-                           const float* scal, float mul, void* hi, void* lo,
-                           hipStream_t s);
+                           float* scal, float mul, void* hi, void* lo,
+                           const float* w, float eps, hipStream_t s);
 // K = 0 output: v = c * x (x from caller-layout float32 or padded operand);
 // writes U (caller layout) or applies W -= eta * v.
 struct ScaledOutArgs {
