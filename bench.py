@@ -15,10 +15,11 @@ times steps in which all M workers' pipelines run on this GPU
 (signmuon_worker_pipeline for workers 1..M-1, then the step for worker 0).
 
 `other_workloads` gives the plain steps/s and phase times of further sets
-(by default the ResNet-50-shaped one).
+(by default the ResNet-50-shaped one and the nanoGPT set with both polar
+steps, before the sign and after the vote).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload nanogpt]
-                    [--also resnet50]
+                    [--also resnet50,nanogpt_prepost]
 """
 from __future__ import annotations
 
@@ -117,7 +118,7 @@ def describe(w):
     return (f"{w.name}: {parts}; W {w.w_dtype}, momentum f32; M={w.M} resident packed "
             f"sign buffers; K={w.K} {coeffs} Newton-Schulz ({ns}), {w.scale} scaling"
             + (f" P={w.P}" if w.scale == "spectral" else "")
-            + ("; post-vote polar" if w.post_vote else ""))
+            + {0: "", 1: "; post-vote polar", 2: "; pre-sign and post-vote polar"}[int(w.post_vote)])
 
 
 def cpu_baseline(w, budget_s):
@@ -274,7 +275,7 @@ def main():
     ap.add_argument("--rb-steps", type=int, default=5,
                     help="timed steps of the all-workers figure (every worker's pipeline "
                          "inside the step)")
-    ap.add_argument("--also", default="resnet50",
+    ap.add_argument("--also", default="resnet50,nanogpt_prepost",
                     help="comma-separated further workloads whose plain steps/s and phase "
                          "times are reported under other_workloads ('' = none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -352,7 +353,8 @@ def main():
     rb_elapsed = time.perf_counter() - t0
     del Moms_b
 
-    # Further workloads (the ResNet-50-shaped set by default): plain steps/s
+    # Further workloads (by default the ResNet-50-shaped set and the nanoGPT
+    # set with both polar steps): plain steps/s
     # and the instrumented phase times, same method as above.
     others = {}
     for name in [n for n in args.also.split(",") if n and n != w.name]:

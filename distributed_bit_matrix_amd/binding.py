@@ -246,7 +246,7 @@ def apply(W, eta: float, D=None, Df=None, stream=None):
     return W
 
 
-def step_workspace(mats, hp: HParams, post_vote: bool) -> int:
+def step_workspace(mats, hp: HParams, post_vote: int) -> int:
     arr = mats_array(mats)
     return int(lib().signmuon_step_workspace(arr, len(mats), ctypes.byref(hp.to_c()),
                                              int(post_vote)))
@@ -255,13 +255,14 @@ def step_workspace(mats, hp: HParams, post_vote: bool) -> int:
 class StepPlan:
     """Cached ctypes arguments of one parameter set for repeated steps."""
 
-    def __init__(self, mats, hp: HParams, post_vote: bool, device=None):
+    def __init__(self, mats, hp: HParams, post_vote: int, device=None):
         import torch
         self.mats = list(mats)
         self.arr = mats_array(self.mats)
         self.hp = hp
         self.hpc = hp.to_c()
-        self.post_vote = bool(post_vote)
+        # 0: Algorithm 2; 1: polar step after the vote; 2: both
+        self.post_vote = int(post_vote)
         nbytes = step_workspace(self.mats, hp, post_vote)
         if nbytes == 0:
             raise SignMuonError("signmuon_step_workspace", SM_EINVAL, "invalid arguments")

@@ -1005,9 +1005,10 @@ size_t signmuon_step_workspace(const sm_matrix* mats, int32_t n_mats,
                                const sm_hparams* hp, int32_t post_vote) {
   if (!mats || n_mats < 1 || n_mats > 65536) return 0;
   if (check_hparams(hp, true) != SM_OK) return 0;
+  if (post_vote < 0 || post_vote > 2) return 0;
   bool need_u = false;
   for (int i = 0; i < n_mats; ++i)
-    if (!post_vote && hp->K > 0 && mats[i].cols % 32 != 0) need_u = true;
+    if (post_vote != 1 && hp->K > 0 && mats[i].cols % 32 != 0) need_u = true;
   Plan P;
   std::vector<MatPlan> mp;
   if (build_plan(mats, n_mats, hp, post_vote != 0, need_u, P, mp) != SM_OK) return 0;
@@ -1032,7 +1033,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   if (st != SM_OK) return st;
   if (M < 1 || M > SM_MAX_WORKERS) return SM_ERANGE;
   if (local_worker < 0 || local_worker >= M) return SM_EINVAL;
-  if (post_vote != 0 && post_vote != 1) return SM_EINVAL;
+  if (post_vote < 0 || post_vote > 2) return SM_EINVAL;
   if (w_dtype != SM_F32 && w_dtype != SM_BF16) return SM_EINVAL;
   if (!G || !W || !Mom || !bits) return SM_EINVAL;
   if (worker_stride_words < 0) return SM_EINVAL;
@@ -1057,7 +1058,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   bool need_u = false;
   for (int i = 0; i < n_mats; ++i) {
     fus[i] = mats[i].cols % 32 == 0;
-    if (!post_vote && hp->K > 0 && !fus[i]) need_u = true;
+    if (post_vote != 1 && hp->K > 0 && !fus[i]) need_u = true;
   }
   Plan P;
   std::vector<MatPlan> mp;
@@ -1091,7 +1092,10 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
     return true;
   };
 
-  if (!post_vote) {
+  // post_vote 0 and 2: the local worker's pre-sign pipeline (momentum,
+  // PolarNS, packed signs); 0 then votes and applies the majority, 2 goes on
+  // to the post-vote polar step below.
+  if (post_vote != 1) {
     if (hp->K == 0) {
       // U = Mom/(s+eps) has the signs of Mom: pack them directly.
       MomSignArgs ms;
@@ -1118,7 +1122,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
       };
       io.first_xsrc = XS_USER; io.src_user = Mom;
       io.final_out = O_BITS; io.bits = local_bits; io.U = nullptr;
-      if (!prof) {
+      if (!prof && post_vote == 0) {
         // Each chain sweeps its own matrices, runs their PolarNS, packs the
         // signs the last epilogue could not, and votes over them, so one
         // chain's memory-bound sweep and vote overlap another's GEMMs.  The
@@ -1172,25 +1176,31 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
       }
     }
     if (pipeline_only) return SM_OK;
-    va.mode = VA_APPLY;
-    HIP_TRY(for_launches(groups, vote_fill, [&](const Groups& Gs) {
-      va.G = Gs; return launch_vote_groups(va, stream);
-    }));
-    HIP_TRY(mark(prof, SM_PHASE_VOTE, stream));
-    return SM_OK;
+    if (post_vote == 0) {
+      va.mode = VA_APPLY;
+      HIP_TRY(for_launches(groups, vote_fill, [&](const Groups& Gs) {
+        va.G = Gs; return launch_vote_groups(va, stream);
+      }));
+      HIP_TRY(mark(prof, SM_PHASE_VOTE, stream));
+      return SM_OK;
+    }
+  } else {
+    // ---- post-vote variant: the local worker sends the momentum's signs
+    MomSignArgs ms;
+    std::memset(&ms, 0, sizeof(ms));
+    ms.w_bf16 = w_bf16; ms.beta = hp->beta; ms.lam = hp->lambda;
+    ms.Gr = G; ms.W = W; ms.Mom = Mom; ms.bits = local_bits; ms.status = B.status;
+    HIP_TRY(for_launches(groups, [&](Group& g) {
+      g.blocks_per_mat = (int32_t)(((int64_t)g.rows * g.cols + kChunk - 1) / kChunk);
+      return true;
+    }, [&](const Groups& Gs) { ms.G = Gs; return launch_momentum_sign(ms, stream); }));
+    HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
+    if (pipeline_only) return SM_OK;
   }
 
-  // ---- post-vote variant
-  MomSignArgs ms;
-  std::memset(&ms, 0, sizeof(ms));
-  ms.w_bf16 = w_bf16; ms.beta = hp->beta; ms.lam = hp->lambda;
-  ms.Gr = G; ms.W = W; ms.Mom = Mom; ms.bits = local_bits; ms.status = B.status;
-  HIP_TRY(for_launches(groups, [&](Group& g) {
-    g.blocks_per_mat = (int32_t)(((int64_t)g.rows * g.cols + kChunk - 1) / kChunk);
-    return true;
-  }, [&](const Groups& Gs) { ms.G = Gs; return launch_momentum_sign(ms, stream); }));
-  HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
-  if (pipeline_only) return SM_OK;
+  // ---- post_vote 1 and 2: majority matrix, its polar factor, the update.
+  // (The pre-sign pass of post_vote 2 has finished with the operand and
+  // partial-sum buffers on this stream before the vote rewrites them.)
   // padding of the operand copy (only matrices with a ragged shape)
   HIP_TRY(for_launches(groups, [&](Group& g) {
     const MatPlan& q = mp[g.idx0];

@@ -51,7 +51,7 @@ class Workload:
     tie_value: int
     T: int
     warmup: int
-    post_vote: bool
+    post_vote: int          # 0: Algorithm 2; 1: polar after the vote; 2: both
     signal_std: float       # std of the shared signal S
     seed_index: int
 
@@ -130,6 +130,12 @@ WORKLOADS = {
         name="postvote", mats=((128, 128),) * 512 + ((1024, 4096),) * 64,
         w_dtype="f32", M=200, scale="spectral", P=8, ns_precision="bf16", T=10,
         warmup=2, post_vote=True, signal_std=0.5, seed_index=4, **_COMMON),
+    # The nanoGPT set with both polar steps (no configuration of its own is
+    # given for this variant).
+    "nanogpt_prepost": Workload(
+        name="nanogpt_prepost", mats=NANOGPT_LAYER * 12, w_dtype="bf16", M=8,
+        scale="fro", P=0, ns_precision="bf16", T=20, warmup=3,
+        post_vote=2, signal_std=0.3, seed_index=5, **_COMMON),
 }
 
 

@@ -174,6 +174,12 @@ sm_status signmuon_apply(void *W, int32_t w_dtype, const int8_t *D,
  * post_vote = 1 (the variant with the polar step after the vote): the signs
  *   of the new momentum go to buffer local_worker; the majority matrix S of
  *   each matrix is voted, U = PolarNS(S), and W <- W - eta * U.
+ * post_vote = 2 (both: the optional local polar step of the abstract on the
+ *   sota2.com paper record, read as an extra PolarNS of the voted matrix on
+ *   top of Algorithm 2): the local worker's pipeline of post_vote = 0, then
+ *   the vote and update of post_vote = 1.  Both PolarNS passes use the same
+ *   hyper-parameters and start vectors.
+ * Any other post_vote value is SM_EINVAL (the workspace query returns 0).
  *
  * mats[n_mats]: HOST array of matrix descriptors (1 <= n_mats <= 65536);
  * matrices must not overlap in the flat arrays or in a worker buffer.
@@ -200,9 +206,9 @@ sm_status signmuon_step(const sm_matrix *mats, int32_t n_mats,
 /*
  * The per-worker half of signmuon_step for worker `worker` (Algorithm 2's
  * local computation up to the packed signs, for every matrix of the set):
- * post_vote = 0: momentum (in place in Mom), PolarNS of the new momentum and
- * its signs packed into buffer `worker`; post_vote = 1: momentum and the
- * signs of the new momentum packed into buffer `worker`.  No vote, and W is
+ * post_vote = 0 or 2: momentum (in place in Mom), PolarNS of the new
+ * momentum and its signs packed into buffer `worker`; post_vote = 1:
+ * momentum and the signs of the new momentum packed into buffer `worker`.  No vote, and W is
  * only read.  Arguments, validation and workspace as for signmuon_step (same
  * workspace size); a non-finite G, W or momentum value is recorded for
  * signmuon_get_status.  Calling it for workers 1..M-1 and signmuon_step for

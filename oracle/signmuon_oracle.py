@@ -291,23 +291,32 @@ def apply_update(W, D, eta, w_dtype="f32"):
 # --------------------------------------------------------------------------
 # One worker's local direction and one full step over a parameter set
 # --------------------------------------------------------------------------
-def worker_direction(Mom_new, hp, u0=None, post_vote=False):
+def worker_direction(Mom_new, hp, u0=None, post_vote=0):
     """What one worker transmits for one matrix.
 
-    Pre-sign polar (Algorithm 2): U = PolarNS(Mom_new), signs of U.
-    Post-vote variant: the signs of Mom_new itself (polar happens after the
-    vote).  Returns (values whose signs are sent, polar factor or None).
+    Pre-sign polar (Algorithm 2, and the first half of the variant with both
+    polar steps, post_vote = 2): U = PolarNS(Mom_new), signs of U.
+    Post-vote variant (post_vote = 1): the signs of Mom_new itself (polar
+    happens after the vote).  Returns (values whose signs are sent, polar
+    factor or None).
     """
-    if post_vote:
+    if post_vote == 1:
         return np.asarray(Mom_new, np.float64), None
     U, _ = polar_ns(Mom_new, hp["K"], hp["eps"], hp["scale"], hp.get("P", 0),
                     hp.get("coeffs", CUBIC), u0)
     return U, U
 
 
-def step(mats, W, Moms, Gs, hp, tie_value=0, post_vote=False, w_dtype="f32",
+def step(mats, W, Moms, Gs, hp, tie_value=0, post_vote=0, w_dtype="f32",
          u0s=None):
     """One Sign-Muon step for M workers over a parameter set.
+
+    post_vote = 0: Algorithm 2 of the bittide.aicompass.dev rendering (polar
+    before the sign, W moves by eta times the majority).  1: the post-vote
+    variant (the momentum's signs are voted, W moves by eta times the polar
+    factor of the majority matrix).  2: both polar steps, the abstract's
+    optional local polar step on the sota2.com record read as a PolarNS of
+    the voted matrix after Algorithm 2's exchange, with the same settings.
 
     mats: list of (rows, cols) in storage order; the flat arrays W (length
     d, values exact in w_dtype), Moms[m] and Gs[m] (length d each) hold the
@@ -347,10 +356,13 @@ def step(mats, W, Moms, Gs, hp, tie_value=0, post_vote=False, w_dtype="f32",
             bits[:, woffs[i]:woffs[i + 1]], r * c)
     D = majority_from_sums(sums, tie_value)
     out = {"Mom": new_moms, "U": Us, "bits": bits, "sums": sums, "D": D}
-    if not post_vote:
+    if post_vote not in (0, 1, 2):
+        raise ValueError(f"post_vote must be 0, 1 or 2, not {post_vote!r}")
+    if post_vote == 0:
         out["Wn"] = apply_update(W, D, hp["eta"], w_dtype)
         return out
-    # Post-vote variant: local polar step on the aggregated sign matrix.
+    # Post-vote variant and the second half of post_vote = 2: local polar
+    # step on the aggregated sign matrix.
     Uflat = np.zeros(d, dtype=np.float64)
     Upost = []
     for i, (r, c) in enumerate(mats):

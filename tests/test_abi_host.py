@@ -140,7 +140,7 @@ def _step(L, mats, hp, M=3, local=0, stride=None, post=0, ws_bytes=None, G=FAKE)
     if stride is None:
         stride = sum((r * c + 31) // 32 for r, c, _, _ in mats)
     if ws_bytes is None:
-        ws_bytes = B.step_workspace(mats, hp, bool(post))
+        ws_bytes = B.step_workspace(mats, hp, post)
     return L.signmuon_step(arr, len(mats), ctypes.byref(hp.to_c()), G, FAKE, 1, FAKE,
                            FAKE, stride, M, local, post, None, FAKE, ws_bytes, None)
 
@@ -160,7 +160,8 @@ def test_worker_pipeline_validation():
     assert call(M=0) == B.SM_ERANGE
     assert call(worker=3) == B.SM_EINVAL
     assert call(worker=-1) == B.SM_EINVAL
-    assert call(post=2) == B.SM_EINVAL
+    assert call(post=3) == B.SM_EINVAL
+    assert call(post=-1) == B.SM_EINVAL
     assert call(G=None) == B.SM_EINVAL
     assert call(stride=words - 1) == B.SM_EINVAL
     assert call(ws_bytes=1024) == B.SM_EWORKSPACE
@@ -173,7 +174,8 @@ def test_step_validation():
     assert _step(L, mats, hp, M=0) == B.SM_ERANGE
     assert _step(L, mats, hp, M=40000) == B.SM_ERANGE
     assert _step(L, mats, hp, M=3, local=3) == B.SM_EINVAL
-    assert _step(L, mats, hp, post=2) == B.SM_EINVAL
+    assert _step(L, mats, hp, post=3) == B.SM_EINVAL
+    assert _step(L, mats, hp, post=-1) == B.SM_EINVAL
     assert _step(L, mats, hp, G=None) == B.SM_EINVAL
     assert _step(L, mats, hp, stride=words - 1) == B.SM_EINVAL
     overlap = [mats[0], (96, 64, 64 * 96 - 1, mats[1][3])]
@@ -184,6 +186,21 @@ def test_step_validation():
     assert _step(L, mats, _hp(beta=1.0)) == B.SM_EINVAL
     assert _step(L, mats, _hp(tie_value=2)) == B.SM_EINVAL
     assert _step(L, [(0, 5, 0, 0)], hp) == B.SM_EINVAL
+
+
+def test_step_workspace_post_vote_modes():
+    # 0: Algorithm 2; 1: polar after the vote; 2: both (the pre-sign pass
+    # of 0, then the post-vote pass of 1 in the same buffers)
+    hp = _hp()
+    mats, _, _ = B.default_layout(WL.get("nanogpt").mats)
+    assert B.step_workspace(mats, hp, 2) == B.step_workspace(mats, hp, 0) > 0
+    assert B.step_workspace(mats, hp, 1) > 0
+    assert B.step_workspace(mats, hp, 3) == 0
+    assert B.step_workspace(mats, hp, -1) == 0
+    # widths that are not multiples of 32 keep a float32 U for the separate
+    # packing pass of the pre-sign polar factor (0 and 2 only)
+    m1, _, _ = B.default_layout([(5, 37)])
+    assert B.step_workspace(m1, hp, 2) == B.step_workspace(m1, hp, 0) > B.step_workspace(m1, hp, 1)
 
 
 def test_step_workspace_sizes(monkeypatch):

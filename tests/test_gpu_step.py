@@ -5,11 +5,13 @@ momentum rounded to float32), so differences do not compound; the other
 workers' packed buffers are the oracle's own.  The checks per step:
 * momentum of the local worker within the float32 evaluation bound;
 * the local worker's packed signs pass the sign gate against the oracle's
-  polar factor (post-vote: against its momentum);
+  polar factor (post-vote: against its momentum; with both polar steps,
+  post_vote = 2, against the polar factor as in Algorithm 2);
 * W is bit-exact wherever the local worker's bit equals the oracle's (every
   vote input is then identical), and otherwise moves by at most one step;
-* post-vote: the polar factor recovered from the W update is within the
-  polar tolerance of the oracle's and passes the sign gate.
+* post-vote and both polar steps: the polar factor recovered from the W
+  update is within the polar tolerance of the oracle's and passes the sign
+  gate.
 Full-size workloads are checked on sampled matrices the oracle can afford.
 """
 import numpy as np
@@ -18,7 +20,8 @@ import pytest
 import oracle as O
 from distributed_bit_matrix_amd import binding as B
 from distributed_bit_matrix_amd import workloads as WL
-from tests.gpu_common import f32, momentum_tol, oracle_hp, polar_tol, sign_gate, unpack_neg
+from tests.gpu_common import (f32, momentum_tol, oracle_hp, polar_tol, sign_gate, unpack_neg,
+                               w_round_tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +72,7 @@ def check_step(w, st, hp, W, Moms, Gs, u0s, sample=None, other_bits=None):
     for i in idx:
         r, c = mats[i]
         blk = Mom_new0[offs[i]:offs[i] + r * c].reshape(r, c)
-        if w.post_vote:
+        if w.post_vote == 1:
             U0[i] = blk
         else:
             U0[i], _ = O.polar_ns(blk, o["K"], o["eps"], o["scale"], o["P"], o["coeffs"],
@@ -109,9 +112,12 @@ def check_step(w, st, hp, W, Moms, Gs, u0s, sample=None, other_bits=None):
                                   None if u0s is None else u0s[i].astype(np.float64))
             if same.all():
                 Ug = (W[sl].astype(np.float64) - Wg[sl].astype(np.float64)) / o["eta"]
-                assert np.abs(Ug - Upost.reshape(-1)).max() <= polar_tol(hp.precision) + 1e-6
-                ok, stats = sign_gate(Ug < 0, Upost.reshape(-1))
-                assert ok, (i, "post-vote", stats)
+                tol = polar_tol(hp.precision) + 1e-6 + w_round_tol(Wg[sl], w.w_dtype, o["eta"])
+                assert np.all(np.abs(Ug - Upost.reshape(-1)) <= tol), (i, "post-vote")
+                if w.w_dtype == "f32":
+                    # (a bfloat16 W keeps too few bits for the signs of small U)
+                    ok, stats = sign_gate(Ug < 0, Upost.reshape(-1))
+                    assert ok, (i, "post-vote", stats)
             continue
         D = O.majority_from_sums(sums, w.tie_value)
         Wn = O.apply_update(W[sl], D, o["eta"], w.w_dtype)
@@ -140,6 +146,12 @@ SMALL = {
                                                             ns_precision="bf16x3"), None, 2),
     "postvote": (WL.scaled(WL.get("postvote"), [(128, 128)] * 6 + [(256, 512)] * 2,
                            M=40), None, 3),
+    # both polar steps: Algorithm 2's worker pipeline, then PolarNS of the vote
+    "prepost": (WL.scaled(WL.get("nanogpt_prepost"), [(192, 576), (192, 192), (192, 768),
+                                                      (768, 192)] * 2), None, 3),
+    "prepost_spectral": (WL.scaled(WL.get("resnet50"), [(64, 147), (128, 576), (256, 512),
+                                                        (512, 256), (10, 256)],
+                                   name="resnet50-prepost").replace(post_vote=2), None, 2),
 }
 
 
@@ -188,6 +200,7 @@ ODD_MATS = [(5, 37), (33, 7), (45, 71), (64, 19), (3, 3)]
 ODD = {
     "f32_M5": WL.scaled(WL.get("single"), ODD_MATS, M=5, name="odd-f32"),
     "bf16_M6": WL.scaled(WL.get("nanogpt"), ODD_MATS, M=6, name="odd-bf16"),
+    "prepost_M5": WL.scaled(WL.get("nanogpt_prepost"), ODD_MATS, M=5, name="odd-prepost"),
 }
 
 
@@ -238,8 +251,9 @@ def test_step_deterministic_and_permutation_invariant():
     assert np.array_equal(a[0].view(np.uint32), c[0].view(np.uint32))
 
 
-def test_step_zero_steps_K0():
-    w = SMALL["nanogpt"][0].replace(K=0)
+@pytest.mark.parametrize("post_vote", [0, 2])
+def test_step_zero_steps_K0(post_vote):
+    w = SMALL["nanogpt"][0].replace(K=0, post_vote=post_vote)
     hp = hparams(w)
     st = GpuState(w, hp)
     W = WL.init_weights(w)
@@ -274,6 +288,10 @@ def test_step_full_resnet50():
     full_case("resnet50", sample=list(range(9)))
 
 
+def test_step_full_nanogpt_prepost():
+    full_case("nanogpt_prepost", sample=[0, 1, 46, 47])
+
+
 @pytest.mark.slow
 def test_step_full_llm_mlp():
     full_case("llm_mlp", sample=[0])
@@ -290,7 +308,7 @@ def test_step_full_postvote():
 # worker, W unchanged by the worker calls, and the final W bit-exact wherever
 # every worker's bit equals the oracle's.
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["nanogpt", "postvote"])
+@pytest.mark.parametrize("name", ["nanogpt", "postvote", "prepost"])
 def test_all_workers_on_gpu(name, chain_mode):
     w, _, _ = SMALL[name]
     if name == "postvote":
@@ -338,7 +356,8 @@ def test_all_workers_on_gpu(name, chain_mode):
         same = np.ones(n, bool)
         for m in range(M):
             gneg = unpack_neg(bg[m, wsl], n)
-            ref = out["Mom"][m][offs[i]:offs[i] + n] if w.post_vote else out["U"][m][i].reshape(-1)
+            ref = out["Mom"][m][offs[i]:offs[i] + n] if w.post_vote == 1 \
+                else out["U"][m][i].reshape(-1)
             ok, stats = sign_gate(gneg, ref)
             assert ok, (m, i, stats)
             same &= gneg == unpack_neg(out["bits"][m, wsl], n)
@@ -354,4 +373,6 @@ def test_all_workers_on_gpu(name, chain_mode):
                 sl = slice(offs[i], offs[i] + r * c)
                 Ug = (W[sl].astype(np.float64) - Wg[sl].astype(np.float64)) / o["eta"]
                 Uo = (W[sl].astype(np.float64) - out["Wn"][sl].astype(np.float64)) / o["eta"]
-                assert np.abs(Ug - Uo).max() <= polar_tol(hp.precision) + 1e-6, i
+                tol = (polar_tol(hp.precision) + 1e-6 + w_round_tol(Wg[sl], w.w_dtype, o["eta"])
+                       + w_round_tol(out["Wn"][sl], w.w_dtype, o["eta"]))
+                assert np.all(np.abs(Ug - Uo) <= tol), i

@@ -428,6 +428,47 @@ def test_step_eta_zero_and_bits_layout():
                               O.pack_signs(out["U"][m][0]))
 
 
+def test_step_both_polar_steps_rank_one_closed_form():
+    # post_vote = 2 with identical rank-one momenta x y^T (W = 0, Mom = 0):
+    # every worker's polar factor is x y^T / (|x| |y|), whose signs are
+    # s t^T (s = sign x, t = sign y); the vote of M = 3 identical buffers is
+    # D = s t^T; D / sqrt(mn) has its one singular value at 1, a fixed point
+    # of the cubic, so the update is W = -eta D / sqrt(mn).
+    rng = np.random.default_rng(17)
+    r, c = 5, 8
+    x = rng.standard_normal(r) + np.sign(rng.standard_normal(r)) * 0.5
+    y = rng.standard_normal(c) + np.sign(rng.standard_normal(c)) * 0.5
+    G = np.outer(x, y).reshape(-1)
+    d = r * c
+    W = np.zeros(d, np.float32)
+    out = O.step([(r, c)], W, [np.zeros(d)] * 3, [G] * 3, dict(HP, lam=0.0), 0, 2, "f32")
+    st = np.outer(np.sign(x), np.sign(y))
+    u = np.outer(x, y) / (np.linalg.norm(x) * np.linalg.norm(y))
+    assert np.allclose(out["U"][0][0], u, atol=1e-12)
+    assert np.array_equal(out["D"].reshape(r, c), st)
+    assert np.allclose(out["Upost"][0], st / np.sqrt(d), atol=1e-12)
+    want = (np.float32(0.0) - np.float32(0.02) * (st / np.sqrt(d)).astype(np.float32)).reshape(-1)
+    assert np.allclose(out["Wn"], want, rtol=2e-7, atol=0)
+
+
+def test_step_both_polar_steps_is_algorithm2_then_post_vote():
+    # post_vote = 2: the buffers are Algorithm 2's (signs of the polar factor,
+    # not of the momentum), and W moves by eta times the polar factor of the
+    # majority, not by the majority itself.
+    rng = np.random.default_rng(18)
+    mats = [(6, 10), (9, 5)]
+    W, Gs, Moms = _set(rng, mats, 3)
+    a2 = O.step(mats, W, Moms, Gs, HP, 0, 0, "bf16")
+    pv = O.step(mats, W, Moms, Gs, HP, 0, 1, "bf16")
+    both = O.step(mats, W, Moms, Gs, HP, 0, 2, "bf16")
+    assert np.array_equal(both["bits"], a2["bits"])
+    assert not np.array_equal(both["bits"], pv["bits"])
+    assert np.array_equal(both["D"], a2["D"])
+    assert not np.array_equal(both["Wn"], a2["Wn"])
+    with pytest.raises(ValueError):
+        O.step(mats, W, Moms, Gs, HP, 0, 3, "bf16")
+
+
 def test_step_post_vote_uses_majority_of_momentum_signs():
     rng = np.random.default_rng(16)
     mats = [(4, 6)]
