@@ -30,7 +30,7 @@ EXPORTS = (
     "signmuon_polar_ns_workspace", "signmuon_polar_ns", "signmuon_sign_pack",
     "signmuon_majority_vote", "signmuon_apply", "signmuon_step_workspace",
     "signmuon_step", "signmuon_step_profiled", "signmuon_get_status",
-    "signmuon_worker_pipeline",
+    "signmuon_worker_pipeline", "signmuon_sign_ternary", "signmuon_majority_vote_ternary",
 )
 PHASES = {0: "start", 1: "momentum", 2: "prescale", 3: "gemm", 4: "pack", 5: "vote"}
 
@@ -106,6 +106,8 @@ def lib():
             "signmuon_polar_ns": (i32, [vp, vp, i64, i64, hp, vp, vp, sz, vp]),
             "signmuon_sign_pack": (i32, [vp, vp, i64, vp]),
             "signmuon_majority_vote": (i32, [vp, i64, i32, i64, i32, vp, vp, vp]),
+            "signmuon_sign_ternary": (i32, [vp, vp, i64, vp]),
+            "signmuon_majority_vote_ternary": (i32, [vp, i64, i32, i64, i32, vp, vp, vp]),
             "signmuon_apply": (i32, [vp, i32, vp, vp, f32, i64, vp]),
             "signmuon_step_workspace": (sz, [mats, i32, hp, i32]),
             "signmuon_step": (i32, [mats, i32, hp, vp, vp, i32, vp, vp, i64, i32,
@@ -236,6 +238,34 @@ def majority_vote(bits, M: int, n: int, tie_value: int = 0, stride: Optional[int
         sums = torch.empty(n, dtype=torch.int16, device=bits.device)
     _check("signmuon_majority_vote", lib().signmuon_majority_vote(
         _ptr(bits), stride, M, n, tie_value, _ptr(D), _ptr(sums), _stream(stream)))
+    return (D, sums) if want_sums else D
+
+
+def sign_ternary(U, S=None, stream=None):
+    """int8 signs of U: +1, -1, or 0 for zero / NaN."""
+    import torch
+    _require(U, torch.float32, "U")
+    n = U.numel()
+    if S is None:
+        S = torch.empty(n, dtype=torch.int8, device=U.device)
+    _check("signmuon_sign_ternary", lib().signmuon_sign_ternary(_ptr(U), _ptr(S), n,
+                                                                _stream(stream)))
+    return S
+
+
+def majority_vote_ternary(S, M: int, n: int, tie_value: int = 0,
+                          stride: Optional[int] = None, D=None, sums=None,
+                          want_sums: bool = False, stream=None):
+    """S: int8 tensor holding M worker sign buffers of `stride` bytes each."""
+    import torch
+    if stride is None:
+        stride = n
+    if D is None:
+        D = torch.empty(n, dtype=torch.int8, device=S.device)
+    if want_sums and sums is None:
+        sums = torch.empty(n, dtype=torch.int16, device=S.device)
+    _check("signmuon_majority_vote_ternary", lib().signmuon_majority_vote_ternary(
+        _ptr(S), stride, M, n, tie_value, _ptr(D), _ptr(sums), _stream(stream)))
     return (D, sums) if want_sums else D
 
 

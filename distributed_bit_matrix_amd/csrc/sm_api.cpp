@@ -935,6 +935,29 @@ sm_status signmuon_majority_vote(const uint32_t* bits, int64_t worker_stride_wor
   return SM_OK;
 }
 
+sm_status signmuon_sign_ternary(const float* U, int8_t* S, int64_t n, hipStream_t stream) {
+  if (n < 0) return SM_EINVAL;
+  if (n == 0) return SM_OK;
+  if (!U || !S) return SM_EINVAL;
+  if (n > ((int64_t)1 << 36)) return SM_EINVAL;   // grid of n / 4096 blocks
+  HIP_TRY(launch_sign_ternary(U, S, n, stream));
+  return SM_OK;
+}
+
+sm_status signmuon_majority_vote_ternary(const int8_t* S, int64_t worker_stride, int32_t M,
+                                         int64_t n, int32_t tie_value, int8_t* D,
+                                         int16_t* sums, hipStream_t stream) {
+  if (n < 0) return SM_EINVAL;
+  if (M < 1 || M > SM_MAX_WORKERS) return SM_ERANGE;
+  if (tie_value != 0 && tie_value != 1) return SM_EINVAL;
+  if (n == 0) return SM_OK;
+  if (!S || !D) return SM_EINVAL;
+  if (worker_stride < 0 || (M > 1 && worker_stride < n)) return SM_EINVAL;
+  if (n > ((int64_t)1 << 36)) return SM_EINVAL;   // grid of n / 4096 blocks
+  HIP_TRY(launch_vote_ternary(S, worker_stride, M, n, tie_value, D, sums, stream));
+  return SM_OK;
+}
+
 sm_status signmuon_apply(void* W, int32_t w_dtype, const int8_t* D, const float* Df,
                          float eta, int64_t n, hipStream_t stream) {
   if (n < 0) return SM_EINVAL;

@@ -999,6 +999,82 @@ hipError_t launch_scaled_out(const ScaledOutArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Ternary (int8) sign buffers: S = sign(U) in {-1, 0, +1} (NaN -> 0), and
+// the vote over M such buffers, sum_j = sum_m S_m[j], D_j = sign(sum_j) with
+// a tie (sum 0) mapped to tie.  Each thread takes 16 consecutive entries;
+// 16-byte accesses when every buffer start is 16-byte aligned, else bytes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_sign_ternary(const float* U, int8_t* S, int64_t n) {
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 16;
+  if (e0 >= n) return;
+  const int cnt = n - e0 < 16 ? (int)(n - e0) : 16;
+  for (int k = 0; k < cnt; ++k) {
+    const float u = U[e0 + k];
+    S[e0 + k] = (int8_t)(u > 0.0f ? 1 : u < 0.0f ? -1 : 0);
+  }
+}
+
+hipError_t launch_sign_ternary(const float* U, int8_t* S, int64_t n, hipStream_t s) {
+  const int64_t blocks = (n + 16 * 256 - 1) / (16 * 256);
+  hipLaunchKernelGGL(k_sign_ternary, dim3((unsigned)blocks), dim3(256), 0, s, U, S, n);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_vote_ternary(const int8_t* S, int64_t stride, int M,
+                                                      int64_t n, int tie, int8_t* D,
+                                                      int16_t* sums, int vec) {
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 16;
+  if (e0 >= n) return;
+  int acc[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) acc[k] = 0;
+  if (vec && e0 + 16 <= n) {
+    for (int m = 0; m < M; ++m) {
+      const u32x4_t w = ld_nt(reinterpret_cast<const u32x4_t*>(S + (int64_t)m * stride + e0));
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        acc[k] += (int)(int8_t)((w[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+    }
+    u32x4_t o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int a = acc[4 * q + b];
+        const int d = a > 0 ? 1 : a < 0 ? -1 : tie;
+        v |= (uint32_t)(uint8_t)(int8_t)d << (8 * b);
+      }
+      o[q] = v;
+    }
+    *reinterpret_cast<u32x4_t*>(D + e0) = o;
+    if (sums) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) sums[e0 + k] = (int16_t)acc[k];
+    }
+    return;
+  }
+  const int cnt = n - e0 < 16 ? (int)(n - e0) : 16;
+  for (int m = 0; m < M; ++m)
+    for (int k = 0; k < cnt; ++k) acc[k] += S[(int64_t)m * stride + e0 + k];
+  for (int k = 0; k < cnt; ++k) {
+    const int a = acc[k];
+    D[e0 + k] = (int8_t)(a > 0 ? 1 : a < 0 ? -1 : tie);
+    if (sums) sums[e0 + k] = (int16_t)a;
+  }
+}
+
+hipError_t launch_vote_ternary(const int8_t* S, int64_t stride, int M, int64_t n, int tie,
+                               int8_t* D, int16_t* sums, hipStream_t s) {
+  const int vec = (reinterpret_cast<uintptr_t>(S) % 16 == 0) &&
+                  (M == 1 || stride % 16 == 0) && (reinterpret_cast<uintptr_t>(D) % 16 == 0);
+  const int64_t blocks = (n + 16 * 256 - 1) / (16 * 256);
+  hipLaunchKernelGGL(k_vote_ternary, dim3((unsigned)blocks), dim3(256), 0, s, S, stride, M, n,
+                     tie, D, sums, vec);
+  return hipGetLastError();
+}
+
 __global__ void k_clear_status(int32_t* status) {
   if (threadIdx.x == 0) status[0] = 0;
 }

@@ -68,6 +68,10 @@ hipError_t launch_momentum_flat(const float* G, const void* W, int w_bf16,
                                 hipStream_t s);
 hipError_t launch_sign_pack_flat(const float* U, uint32_t* bits, int64_t n,
                                  hipStream_t s);
+// Ternary int8 sign buffers (sign with 0 kept) and their vote.
+hipError_t launch_sign_ternary(const float* U, int8_t* S, int64_t n, hipStream_t s);
+hipError_t launch_vote_ternary(const int8_t* S, int64_t stride, int M, int64_t n, int tie,
+                               int8_t* D, int16_t* sums, hipStream_t s);
 hipError_t launch_vote_flat(const uint32_t* bits, int64_t stride, int M,
                             int64_t n, int tie, int8_t* D, int16_t* sums,
                             hipStream_t s);

@@ -152,6 +152,28 @@ sm_status signmuon_majority_vote(const uint32_t *bits,
                                  int16_t *sums, hipStream_t stream);
 
 /*
+ * Ternary sign buffers, the one-byte encoding that keeps sign(0) = 0
+ * (section 3 of the paper defines sign(0) = 0; Algorithm 2, Figure 1 and
+ * section 6 describe signs exchanged as int8).  For callers that exchange
+ * int8 signs instead of the 1-bit packed buffers.
+ *
+ * signmuon_sign_ternary: S[j] = +1, -1 or 0 for U[j] > 0, < 0, or zero / NaN.
+ *   U: float32[n], S: int8[n] (device).  0 <= n <= 2^36 else SM_EINVAL.
+ * signmuon_majority_vote_ternary: sum_j = sum over m < M of S_m[j] (exact;
+ *   |sum| <= M <= 32767), D[j] = sign(sum_j) with a zero sum giving
+ *   tie_value (0 or 1).  Worker m's buffer starts at S + m * worker_stride
+ *   bytes (worker_stride >= n when M > 1).  D: int8[n]; sums: int16[n] or
+ *   NULL.  1 <= M <= 32767 else SM_ERANGE.  Buffer starts and a stride that
+ *   are multiples of 16 bytes take the 16-byte access path.
+ */
+sm_status signmuon_sign_ternary(const float *U, int8_t *S, int64_t n,
+                                hipStream_t stream);
+sm_status signmuon_majority_vote_ternary(const int8_t *S, int64_t worker_stride,
+                                         int32_t M, int64_t n, int32_t tie_value,
+                                         int8_t *D, int16_t *sums,
+                                         hipStream_t stream);
+
+/*
  * Update (Algorithm 1 and 2, last line): W[i] <- W[i] - eta * D[i] with the
  * product and the difference each rounded to float32 (no fused
  * multiply-add) and, for a bfloat16 W, the result rounded to nearest even.

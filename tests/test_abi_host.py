@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -222,3 +222,24 @@ def test_step_workspace_sizes(monkeypatch):
     # ragged shapes are padded to multiples of 128
     m1, _, _ = B.default_layout([(10, 2048)])
     assert B.step_workspace(m1, hp, False) >= 2 * 2 * 128 * 2048
+
+
+def test_ternary_validation():
+    # argument errors return before any launch
+    L = B.lib()
+    F2 = ctypes.c_void_p(0x20000)
+    assert L.signmuon_sign_ternary(FAKE, F2, -1, None) == B.SM_EINVAL
+    assert L.signmuon_sign_ternary(None, F2, 5, None) == B.SM_EINVAL
+    assert L.signmuon_sign_ternary(FAKE, None, 5, None) == B.SM_EINVAL
+    assert L.signmuon_sign_ternary(None, None, 0, None) == B.SM_OK
+    assert L.signmuon_sign_ternary(FAKE, F2, (1 << 36) + 1, None) == B.SM_EINVAL
+    v = L.signmuon_majority_vote_ternary
+    assert v(FAKE, 10, 0, 10, 0, F2, None, None) == B.SM_ERANGE
+    assert v(FAKE, 10, 32768, 10, 0, F2, None, None) == B.SM_ERANGE
+    assert v(FAKE, 10, 3, 10, 2, F2, None, None) == B.SM_EINVAL
+    assert v(FAKE, 10, 3, -1, 0, F2, None, None) == B.SM_EINVAL
+    assert v(FAKE, 9, 3, 10, 0, F2, None, None) == B.SM_EINVAL      # stride < n
+    assert v(None, 10, 3, 10, 0, F2, None, None) == B.SM_EINVAL
+    assert v(FAKE, 10, 3, 10, 0, None, None, None) == B.SM_EINVAL
+    assert v(None, 0, 3, 0, 0, None, None, None) == B.SM_OK
+

@@ -184,3 +184,72 @@ def test_momentum_beta_zero_exact():
     Mt = dev(np.zeros(999, np.float32))
     B.momentum(dev(G), dev(np.zeros(999, np.float32)), Mt, 0.0, 0.0)
     assert np.array_equal(host(Mt), G)
+
+
+# --------------------------------------------------------------------------
+# ternary (int8) sign buffers and their vote: bit-exact against the oracle
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 4095, 4096, 4097, 100003])
+def test_sign_ternary_bit_exact(n):
+    rng = np.random.default_rng(n)
+    U = rng.standard_normal(n).astype(np.float32)
+    U[rng.integers(0, n, max(1, n // 10))] = 0.0
+    U[rng.integers(0, n, max(1, n // 20))] = -0.0
+    S = host(B.sign_ternary(dev(U)))
+    assert np.array_equal(S, O.sign_ternary(U))
+
+
+def test_sign_ternary_nan_and_inf():
+    # NaN has no sign: the library writes 0 for it (the pages define sign on
+    # real numbers only); +-inf keep their signs
+    U = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 1e-45, -1e-45], np.float32)
+    assert host(B.sign_ternary(dev(U))).tolist() == [0, 1, -1, 0, 0, 1, -1]
+
+
+def test_vote_ternary_blog_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "blog_vote_example.json")))
+    dirs = np.array(g["directions"], np.float32).reshape(3, 4)
+    S = B.sign_ternary(dev(dirs.reshape(-1)))
+    D, sums = B.majority_vote_ternary(S, 3, 4, 0, stride=4, want_sums=True)
+    assert host(D).reshape(2, 2).tolist() == g["majority"]
+    assert host(sums).tolist() == [-1, -1, 3, 1]
+
+
+@pytest.mark.parametrize("M,n,stride", [(1, 100003, None), (2, 4096, None), (3, 4097, 4112),
+                                        (8, 100000, None), (8, 100003, 100003),
+                                        (200, 70001, 70016), (301, 4099, 4099)])
+@pytest.mark.parametrize("tie", [0, 1])
+def test_vote_ternary_bit_exact(M, n, stride, tie):
+    # aligned strides take the 16-byte path, odd ones the byte path; signs
+    # include zeros, and even M plants ties
+    print(f"vote ternary M={M} n={n} stride={stride} tie={tie}", flush=True)
+    rng = np.random.default_rng(M * 7919 + n)
+    st = n if stride is None else stride
+    Sg = rng.integers(-1, 2, size=(M, st)).astype(np.int8)
+    if M % 2 == 0:
+        Sg[M // 2:, : n // 3] = -Sg[: M // 2, : n // 3]       # exact ties
+    D, sums = B.majority_vote_ternary(dev(Sg.reshape(-1)), M, n, tie, stride=st,
+                                      want_sums=True)
+    want_sums = O.vote_sums_from_signs(Sg[:, :n])
+    assert np.array_equal(host(sums).astype(np.int32), want_sums)
+    assert np.array_equal(host(D), O.majority_from_sums(want_sums, tie))
+
+
+def test_vote_ternary_unaligned_start_and_sums_beyond_int8():
+    M, n = 300, 5000
+    buf = torch.ones(M * n + 1, dtype=torch.int8, device="cuda")
+    S = buf[1:]                                   # start off a 16-byte boundary
+    D, sums = B.majority_vote_ternary(S, M, n, 0, stride=n, want_sums=True)
+    assert host(sums).tolist() == [300] * n
+    assert host(D).tolist() == [1] * n
+
+
+def test_vote_ternary_full_nanogpt_size():
+    # the nanoGPT set's 84,934,656 entries over M = 8 int8 buffers
+    from distributed_bit_matrix_amd import workloads as WL
+    w = WL.get("nanogpt")
+    n, M = w.d, w.M
+    rng = np.random.default_rng(5)
+    Sg = rng.integers(-1, 2, size=(M, n), dtype=np.int8)
+    D = B.majority_vote_ternary(dev(Sg.reshape(-1)), M, n, 0)
+    assert np.array_equal(host(D), O.majority_from_sums(O.vote_sums_from_signs(Sg), 0))
