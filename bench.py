@@ -278,6 +278,8 @@ def main():
     ap.add_argument("--also", default="resnet50,nanogpt_prepost",
                     help="comma-separated further workloads whose plain steps/s and phase "
                          "times are reported under other_workloads ('' = none)")
+    ap.add_argument("--ternary", type=int, default=1,
+                    help="also time the int8 ternary vote on the set's size (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain elementwise kernel that reads and writes "
                          "MIB MiB (reference for hardware byte counters)")
@@ -368,6 +370,32 @@ def main():
         del ro
         torch.cuda.synchronize()
 
+    # The int8 ternary vote (separate entry point, not part of the step) on
+    # the same set's size: M int8 buffers read, int8 D written.
+    tern = None
+    if args.ternary:
+        from distributed_bit_matrix_amd import binding as B
+        d_t, M_t = w.d, w.M
+        S_t = torch.randint(-1, 2, (M_t * d_t,), dtype=torch.int8, device=dev)
+        D_t = torch.empty(d_t, dtype=torch.int8, device=dev)
+        for _ in range(2):
+            B.majority_vote_ternary(S_t, M_t, d_t, 0, D=D_t)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            B.majority_vote_ternary(S_t, M_t, d_t, 0, D=D_t)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        by = (M_t + 1) * d_t
+        tern = {"us": round(us, 2), "bytes": by, "gbps": round(by / (us * 1e-6) / 1e9, 1),
+                "frac_hbm": round(by / (us * 1e-6) / 8e12, 4),
+                "what": f"signmuon_majority_vote_ternary over M={M_t} int8 buffers of "
+                        f"{d_t} entries (reads M d bytes, writes d)"}
+        del S_t, D_t
+
     steps_per_s = K / elapsed
     out = {
         "metric": METRIC,
@@ -413,6 +441,7 @@ def main():
                               "then the vote over the M buffers and the apply",
                       "momentum_buffers": n_mom + 1},
         "other_workloads": others,
+        "ternary_vote": tern,
     }
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
