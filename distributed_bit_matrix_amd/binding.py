@@ -31,6 +31,7 @@ EXPORTS = (
     "signmuon_majority_vote", "signmuon_apply", "signmuon_step_workspace",
     "signmuon_step", "signmuon_step_profiled", "signmuon_get_status",
     "signmuon_worker_pipeline", "signmuon_sign_ternary", "signmuon_majority_vote_ternary",
+    "signmuon_executor_create", "signmuon_executor_destroy", "signmuon_reset_status",
 )
 PHASES = {0: "start", 1: "momentum", 2: "prescale", 3: "gemm", 4: "pack", 5: "vote"}
 
@@ -111,13 +112,16 @@ def lib():
             "signmuon_apply": (i32, [vp, i32, vp, vp, f32, i64, vp]),
             "signmuon_step_workspace": (sz, [mats, i32, hp, i32]),
             "signmuon_step": (i32, [mats, i32, hp, vp, vp, i32, vp, vp, i64, i32,
-                                    i32, i32, vp, vp, sz, vp]),
+                                    i32, i32, vp, vp, sz, vp, vp]),
             "signmuon_worker_pipeline": (i32, [mats, i32, hp, vp, vp, i32, vp, vp, i64,
-                                               i32, i32, i32, vp, vp, sz, vp]),
+                                               i32, i32, i32, vp, vp, sz, vp, vp]),
             "signmuon_step_profiled": (i32, [mats, i32, hp, vp, vp, i32, vp, vp, i64,
                                              i32, i32, i32, vp, vp, sz,
-                                             ctypes.POINTER(SmProfile), vp]),
+                                             ctypes.POINTER(SmProfile), vp, vp]),
             "signmuon_get_status": (i32, [vp, vp]),
+            "signmuon_executor_create": (i32, [ctypes.POINTER(vp)]),
+            "signmuon_executor_destroy": (i32, [vp]),
+            "signmuon_reset_status": (i32, [vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -282,10 +286,36 @@ def step_workspace(mats, hp: HParams, post_vote: int) -> int:
                                              int(post_vote)))
 
 
-class StepPlan:
-    """Cached ctypes arguments of one parameter set for repeated steps."""
+class Executor:
+    """Owner of a signmuon_executor (the streams and events of the concurrent
+    PolarNS chains), created on the current device; freed on close() or
+    garbage collection."""
 
-    def __init__(self, mats, hp: HParams, post_vote: int, device=None):
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check("signmuon_executor_create", lib().signmuon_executor_create(ctypes.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if self.handle is not None and self.handle.value:
+            _check("signmuon_executor_destroy", lib().signmuon_executor_destroy(self.handle))
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class StepPlan:
+    """Cached ctypes arguments of one parameter set for repeated steps.
+
+    concurrent: run the PolarNS chains concurrently on an executor owned by
+    the plan (default); False enqueues every kernel on the caller's stream."""
+
+    def __init__(self, mats, hp: HParams, post_vote: int, device=None,
+                 concurrent: bool = True):
         import torch
         self.mats = list(mats)
         self.arr = mats_array(self.mats)
@@ -296,7 +326,16 @@ class StepPlan:
         nbytes = step_workspace(self.mats, hp, post_vote)
         if nbytes == 0:
             raise SignMuonError("signmuon_step_workspace", SM_EINVAL, "invalid arguments")
-        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
+        dev = torch.device(device or "cuda")
+        # zero-filled: the first bytes carry the non-finite flags
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        self.executor = None
+        if concurrent:
+            with torch.cuda.device(self.ws.device):
+                self.executor = Executor()
+
+    def _ex(self):
+        return None if self.executor is None else self.executor.handle
 
     def set_eta(self, eta: float):
         self.hp.eta = eta
@@ -308,7 +347,7 @@ class StepPlan:
             self.arr, len(self.mats), ctypes.byref(self.hpc), _ptr(G), _ptr(W),
             _wdtype(W), _ptr(Mom), _ptr(bits), stride, M, local_worker,
             int(self.post_vote), _ptr(u0), _ptr(self.ws), self.ws.numel(),
-            _stream(stream)))
+            self._ex(), _stream(stream)))
 
     def worker_pipeline(self, G, W, Mom, bits, stride: int, M: int, worker: int,
                         u0=None, stream=None):
@@ -318,7 +357,7 @@ class StepPlan:
             self.arr, len(self.mats), ctypes.byref(self.hpc), _ptr(G), _ptr(W),
             _wdtype(W), _ptr(Mom), _ptr(bits), stride, M, worker,
             int(self.post_vote), _ptr(u0), _ptr(self.ws), self.ws.numel(),
-            _stream(stream)))
+            self._ex(), _stream(stream)))
 
     def profiled(self, prof: "SmProfile", G, W, Mom, bits, stride: int, M: int,
                  local_worker: int = 0, u0=None, stream=None):
@@ -327,10 +366,14 @@ class StepPlan:
             self.arr, len(self.mats), ctypes.byref(self.hpc), _ptr(G), _ptr(W),
             _wdtype(W), _ptr(Mom), _ptr(bits), stride, M, local_worker,
             int(self.post_vote), _ptr(u0), _ptr(self.ws), self.ws.numel(),
-            ctypes.byref(prof), _stream(stream)))
+            ctypes.byref(prof), self._ex(), _stream(stream)))
 
     def status(self, stream=None) -> int:
         return int(lib().signmuon_get_status(_ptr(self.ws), _stream(stream)))
+
+    def reset_status(self, stream=None):
+        _check("signmuon_reset_status", lib().signmuon_reset_status(_ptr(self.ws),
+                                                                    _stream(stream)))
 
     def capture(self, G, W, Mom, bits, stride: int, M: int, local_worker: int = 0,
                 u0=None):

@@ -19,6 +19,7 @@
 #include <functional>
 #include <map>
 #include <mutex>
+#include <new>
 #include <vector>
 
 #include "sm_internal.h"
@@ -28,7 +29,7 @@ using namespace sm;
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 constexpr int64_t kMaxDim = 1 << 20;          // rows / cols
 constexpr int64_t kMaxPadded = (int64_t)1 << 31;  // padded rows * cols
 
@@ -714,8 +715,9 @@ sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
 
 // ---------------------------------------------------------------------------
 // PolarNS of all groups as up to kChains independent chains (pre-scale and
-// the K Newton-Schulz steps of a subset of the groups each), run on
-// internal streams forked from and joined back into the caller's stream.
+// the K Newton-Schulz steps of a subset of the groups each), run on the
+// streams of a caller-owned executor, forked from and joined back into the
+// caller's stream.
 // A chain's launches depend only on its own matrices, so the GPU runs the
 // chains side by side and one chain's next launch fills the tail of
 // another's.  The chains' launches are enqueued interleaved, one stage of
@@ -741,33 +743,23 @@ double chain_min_flop() {
   }
   return SM_CHAIN_MIN_GFLOP * 1e9;
 }
-struct ChainRes {
-  hipStream_t s[kChains];
-  hipEvent_t fork, join[kChains], head[kChains];
-  hipError_t err = hipSuccess;
-  std::mutex mu;   // one enqueue at a time per device
-};
-ChainRes g_chain[64];
-std::once_flag g_chain_once[64];
+}  // namespace
 
-hipError_t chain_resources(ChainRes** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  ChainRes& R = g_chain[dev];
-  std::call_once(g_chain_once[dev], [&] {
-    for (int c = 0; c < kChains && R.err == hipSuccess; ++c)
-      R.err = hipStreamCreateWithFlags(&R.s[c], hipStreamNonBlocking);
-    if (R.err == hipSuccess) R.err = hipEventCreateWithFlags(&R.fork, hipEventDisableTiming);
-    for (int c = 0; c < kChains && R.err == hipSuccess; ++c)
-      R.err = hipEventCreateWithFlags(&R.join[c], hipEventDisableTiming);
-    for (int c = 0; c < kChains && R.err == hipSuccess; ++c)
-      R.err = hipEventCreateWithFlags(&R.head[c], hipEventDisableTiming);
-  });
-  *out = &R;
-  return R.err;
-}
+// Caller-owned resources of the concurrent chains (signmuon_executor_create):
+// the chains' streams, created on `device`, and for each of the (at most
+// two) PolarNS passes of one step its own fork, head and join events, so no
+// event is recorded twice within a step.  `mu` keeps two threads from
+// enqueueing through one executor at the same time.
+struct sm_executor {
+  int device = -1;
+  hipStream_t s[kChains] = {};
+  hipEvent_t fork[2] = {};
+  hipEvent_t head[2][kChains] = {};
+  hipEvent_t join[2][kChains] = {};
+  std::mutex mu;
+};
+
+namespace {
 
 // Optional work of a chain around its PolarNS: `head` stages run before the
 // pre-scale on the chain's stream, `tail` stages after the last
@@ -781,16 +773,24 @@ struct ChainHooks {
 sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
                     const std::vector<Group>& groups, const std::vector<bool>& fusable,
                     const sm_hparams* hp, Bufs& B, const NsIO& io, int part_kind,
-                    hipStream_t s, const ChainHooks* hooks = nullptr) {
+                    hipStream_t s, sm_executor* ex, int pass,
+                    const ChainHooks* hooks = nullptr) {
   // Sets with little Newton-Schulz work are bound by the host's launch
   // rate: one chain puts all their groups into each launch (up to
   // kMaxGroups per launch), a third of the launches of three chains.
+  // Without an executor, or while the caller's stream is being captured
+  // into a graph, everything runs as one chain on the caller's stream.
   double ns_flop = 0.0;
   for (const Group& g : groups) {
     const double m = std::min(g.rows, g.cols), n = std::max(g.rows, g.cols);
     ns_flop += 4.0 * hp->K * g.count * m * m * n;
   }
-  const int nc = ns_flop < chain_min_flop() ? 1 : (int)std::min<size_t>(kChains, groups.size());
+  int nc = ns_flop < chain_min_flop() ? 1 : (int)std::min<size_t>(kChains, groups.size());
+  if (nc > 1) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(s, &cap));
+    if (!ex || cap != hipStreamCaptureStatusNone) nc = 1;
+  }
   if (nc <= 1) {
     Stages st;
     if (hooks) hooks->head(groups, s, st);
@@ -816,10 +816,11 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
     chain[c].push_back(groups[i]);
     load[c] += work(groups[i]);
   }
-  ChainRes* R = nullptr;
-  HIP_TRY(chain_resources(&R));
+  sm_executor* R = ex;
   std::lock_guard<std::mutex> lock(R->mu);
-  HIP_TRY(hipEventRecord(R->fork, s));
+  hipEvent_t* head_ev = R->head[pass];
+  hipEvent_t* join_ev = R->join[pass];
+  HIP_TRY(hipEventRecord(R->fork[pass], s));
   NsIO cio = io;
   cio.prof = nullptr;
   // heads[c] run (for every chain) before any stage of prog, so every head
@@ -829,16 +830,16 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
     hipStream_t cs = R->s[c];
     if (hooks) {
       hooks->head(chain[c], cs, heads[c]);
-      heads[c].push_back([R, c, cs]() -> sm_status {
-        HIP_TRY(hipEventRecord(R->head[c], cs));
+      heads[c].push_back([head_ev, c, cs]() -> sm_status {
+        HIP_TRY(hipEventRecord(head_ev[c], cs));
         return SM_OK;
       });
     }
     pre_scale_stages(P, mp, chain[c], hp, B, cio, part_kind, cs, prog[c]);
     if (hp->K > 0) ns_stages(P, mp, chain[c], fusable, hp, B, cio, cs, prog[c]);
     if (hooks) {
-      prog[c].push_back([R, nc, cs]() -> sm_status {
-        for (int o = 0; o < nc; ++o) HIP_TRY(hipStreamWaitEvent(cs, R->head[o], 0));
+      prog[c].push_back([head_ev, nc, cs]() -> sm_status {
+        for (int o = 0; o < nc; ++o) HIP_TRY(hipStreamWaitEvent(cs, head_ev[o], 0));
         return SM_OK;
       });
       hooks->tail(chain[c], cs, prog[c]);
@@ -847,7 +848,7 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
   sm_status st = SM_OK;
   int forked = 0;
   for (int c = 0; c < nc && st == SM_OK; ++c) {
-    if (hipStreamWaitEvent(R->s[c], R->fork, 0) != hipSuccess) { st = SM_EHIP; break; }
+    if (hipStreamWaitEvent(R->s[c], R->fork[pass], 0) != hipSuccess) { st = SM_EHIP; break; }
     ++forked;
   }
   for (const std::vector<Stages>* lists : {&heads, &prog}) {
@@ -860,8 +861,8 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
   // join every forked chain, also after an error, so that the caller's
   // stream orders after all work enqueued on the chains
   for (int c = 0; c < forked; ++c) {
-    if (hipEventRecord(R->join[c], R->s[c]) != hipSuccess ||
-        hipStreamWaitEvent(s, R->join[c], 0) != hipSuccess)
+    if (hipEventRecord(join_ev[c], R->s[c]) != hipSuccess ||
+        hipStreamWaitEvent(s, join_ev[c], 0) != hipSuccess)
       st = SM_EHIP;
   }
   if (st != SM_OK) return st;
@@ -1045,8 +1046,8 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
                     const float* G, void* W, int32_t w_dtype, float* Mom,
                     uint32_t* bits, int64_t worker_stride_words, int32_t M,
                     int32_t local_worker, int32_t post_vote, const float* u0,
-                    void* ws, size_t ws_bytes, sm_profile* prof, hipStream_t stream,
-                    bool pipeline_only = false) {
+                    void* ws, size_t ws_bytes, sm_profile* prof, sm_executor* ex,
+                    hipStream_t stream, bool pipeline_only = false) {
   if (prof) {
     if (!prof->events || !prof->kinds || prof->capacity < 0) return SM_EINVAL;
     prof->count = 0;
@@ -1089,6 +1090,11 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   if (st != SM_OK) return st;
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < P.total)
     return SM_EWORKSPACE;
+  if (ex) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev != ex->device) return SM_EINVAL;
+  }
   HIP_TRY(ensure_attributes());
   Bufs B = bind(P, ws);
   std::vector<int> all(n_mats);
@@ -1098,7 +1104,12 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   uint32_t* local_bits = bits + (int64_t)local_worker * worker_stride_words;
   const int w_bf16 = w_dtype == SM_BF16;
   HIP_TRY(mark(prof, SM_PHASE_START, stream));
-  HIP_TRY(launch_clear_status(B.status, stream));
+  // A step takes over the flags of the worker pipelines enqueued since the
+  // last step (word 1) as its own (word 0); a worker pipeline adds its flag
+  // to word 1, so a non-finite value in any worker's pipeline of a step
+  // skips that step's update.
+  int32_t* const flag = pipeline_only ? B.status + 1 : B.status;
+  if (!pipeline_only) HIP_TRY(launch_begin_status(B.status, stream));
 
   NsIO io;
   std::memset(&io, 0, sizeof(io));
@@ -1124,7 +1135,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
       MomSignArgs ms;
       std::memset(&ms, 0, sizeof(ms));
       ms.w_bf16 = w_bf16; ms.beta = hp->beta; ms.lam = hp->lambda;
-      ms.Gr = G; ms.W = W; ms.Mom = Mom; ms.bits = local_bits; ms.status = B.status;
+      ms.Gr = G; ms.W = W; ms.Mom = Mom; ms.bits = local_bits; ms.status = flag;
       HIP_TRY(for_launches(groups, [&](Group& g) {
         g.blocks_per_mat = (int32_t)(((int64_t)g.rows * g.cols + kChunk - 1) / kChunk);
         return true;
@@ -1138,7 +1149,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
       sw.Gr = G; sw.W = W; sw.Mom = Mom;
       sw.o_hi = B.x[0][0]; sw.o_lo = B.x[0][1];
       sw.part = P.spectral ? nullptr : B.part;
-      sw.status = B.status;
+      sw.status = flag;
       auto sweep_fill = [&](Group& g) {
         g.blocks_per_mat = (int32_t)(mp[g.idx0].Mp * mp[g.idx0].Np / 4096);
         return true;
@@ -1182,12 +1193,12 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
             return SM_OK;
           });
         };
-        return run_polar(P, mp, groups, fus, hp, B, io, 0, stream, &hooks);
+        return run_polar(P, mp, groups, fus, hp, B, io, 0, stream, ex, 0, &hooks);
       }
       HIP_TRY(for_launches(groups, sweep_fill,
                            [&](const Groups& Gs) { sw.G = Gs; return launch_sweep(sw, stream); }));
       HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
-      st = run_polar(P, mp, groups, fus, hp, B, io, 0, stream);
+      st = run_polar(P, mp, groups, fus, hp, B, io, 0, stream, ex, 0);
       if (st != SM_OK) return st;
       if (need_u) {
         for (int i = 0; i < n_mats; ++i) {
@@ -1212,7 +1223,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
     MomSignArgs ms;
     std::memset(&ms, 0, sizeof(ms));
     ms.w_bf16 = w_bf16; ms.beta = hp->beta; ms.lam = hp->lambda;
-    ms.Gr = G; ms.W = W; ms.Mom = Mom; ms.bits = local_bits; ms.status = B.status;
+    ms.Gr = G; ms.W = W; ms.Mom = Mom; ms.bits = local_bits; ms.status = flag;
     HIP_TRY(for_launches(groups, [&](Group& g) {
       g.blocks_per_mat = (int32_t)(((int64_t)g.rows * g.cols + kChunk - 1) / kChunk);
       return true;
@@ -1244,7 +1255,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   io.final_out = O_APPLY;
   if (hp->K > 0) {
     std::vector<bool> fus_all(n_mats, true);
-    return run_polar(P, mp, groups, fus_all, hp, B, io, 1, stream);
+    return run_polar(P, mp, groups, fus_all, hp, B, io, 1, stream, ex, post_vote == 2 ? 1 : 0);
   }
   st = run_pre_scale(P, mp, groups, hp, B, io, 1, stream);
   if (st != SM_OK) return st;
@@ -1265,13 +1276,58 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
 
 extern "C" {
 
+sm_status signmuon_executor_create(sm_executor** out) {
+  if (!out) return SM_EINVAL;
+  *out = nullptr;
+  sm_executor* ex = new (std::nothrow) sm_executor;
+  if (!ex) return SM_EHIP;
+  hipError_t e = hipGetDevice(&ex->device);
+  for (int c = 0; c < kChains && e == hipSuccess; ++c)
+    e = hipStreamCreateWithFlags(&ex->s[c], hipStreamNonBlocking);
+  for (int p = 0; p < 2 && e == hipSuccess; ++p) {
+    e = hipEventCreateWithFlags(&ex->fork[p], hipEventDisableTiming);
+    for (int c = 0; c < kChains && e == hipSuccess; ++c)
+      e = hipEventCreateWithFlags(&ex->head[p][c], hipEventDisableTiming);
+    for (int c = 0; c < kChains && e == hipSuccess; ++c)
+      e = hipEventCreateWithFlags(&ex->join[p][c], hipEventDisableTiming);
+  }
+  if (e != hipSuccess) {
+    signmuon_executor_destroy(ex);
+    return SM_EHIP;
+  }
+  *out = ex;
+  return SM_OK;
+}
+
+sm_status signmuon_executor_destroy(sm_executor* ex) {
+  if (!ex) return SM_OK;
+  int prev = 0;
+  const bool have_prev = hipGetDevice(&prev) == hipSuccess;
+  if (ex->device >= 0) (void)hipSetDevice(ex->device);
+  sm_status st = SM_OK;
+  for (int c = 0; c < kChains; ++c)
+    if (ex->s[c] && hipStreamSynchronize(ex->s[c]) != hipSuccess) st = SM_EHIP;
+  for (int p = 0; p < 2; ++p) {
+    if (ex->fork[p]) (void)hipEventDestroy(ex->fork[p]);
+    for (int c = 0; c < kChains; ++c) {
+      if (ex->head[p][c]) (void)hipEventDestroy(ex->head[p][c]);
+      if (ex->join[p][c]) (void)hipEventDestroy(ex->join[p][c]);
+    }
+  }
+  for (int c = 0; c < kChains; ++c)
+    if (ex->s[c]) (void)hipStreamDestroy(ex->s[c]);
+  if (have_prev) (void)hipSetDevice(prev);
+  delete ex;
+  return st;
+}
+
 sm_status signmuon_step(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
                         const float* G, void* W, int32_t w_dtype, float* Mom,
                         uint32_t* bits, int64_t worker_stride_words, int32_t M,
                         int32_t local_worker, int32_t post_vote, const float* u0,
-                        void* ws, size_t ws_bytes, hipStream_t stream) {
+                        void* ws, size_t ws_bytes, sm_executor* ex, hipStream_t stream) {
   return step_impl(mats, n_mats, hp, G, W, w_dtype, Mom, bits, worker_stride_words, M,
-                   local_worker, post_vote, u0, ws, ws_bytes, nullptr, stream);
+                   local_worker, post_vote, u0, ws, ws_bytes, nullptr, ex, stream);
 }
 
 sm_status signmuon_worker_pipeline(const sm_matrix* mats, int32_t n_mats,
@@ -1279,10 +1335,10 @@ sm_status signmuon_worker_pipeline(const sm_matrix* mats, int32_t n_mats,
                                    int32_t w_dtype, float* Mom, uint32_t* bits,
                                    int64_t worker_stride_words, int32_t M, int32_t worker,
                                    int32_t post_vote, const float* u0, void* ws,
-                                   size_t ws_bytes, hipStream_t stream) {
+                                   size_t ws_bytes, sm_executor* ex, hipStream_t stream) {
   // W is only read on this path
   return step_impl(mats, n_mats, hp, G, const_cast<void*>(W), w_dtype, Mom, bits,
-                   worker_stride_words, M, worker, post_vote, u0, ws, ws_bytes, nullptr,
+                   worker_stride_words, M, worker, post_vote, u0, ws, ws_bytes, nullptr, ex,
                    stream, true);
 }
 
@@ -1292,19 +1348,25 @@ sm_status signmuon_step_profiled(const sm_matrix* mats, int32_t n_mats,
                                  int64_t worker_stride_words, int32_t M,
                                  int32_t local_worker, int32_t post_vote,
                                  const float* u0, void* ws, size_t ws_bytes,
-                                 sm_profile* prof, hipStream_t stream) {
+                                 sm_profile* prof, sm_executor* ex, hipStream_t stream) {
   if (!prof) return SM_EINVAL;
   return step_impl(mats, n_mats, hp, G, W, w_dtype, Mom, bits, worker_stride_words, M,
-                   local_worker, post_vote, u0, ws, ws_bytes, prof, stream);
+                   local_worker, post_vote, u0, ws, ws_bytes, prof, ex, stream);
+}
+
+sm_status signmuon_reset_status(void* ws, hipStream_t stream) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return SM_EWORKSPACE;
+  HIP_TRY(launch_reset_status(static_cast<int32_t*>(ws), stream));
+  return SM_OK;
 }
 
 sm_status signmuon_get_status(const void* ws, hipStream_t stream) {
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return SM_EWORKSPACE;
-  int32_t h = 0;
-  if (hipMemcpyAsync(&h, ws, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess)
+  int32_t h[2] = {0, 0};
+  if (hipMemcpyAsync(h, ws, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess)
     return SM_EHIP;
   if (hipStreamSynchronize(stream) != hipSuccess) return SM_EHIP;
-  return h ? SM_ENONFINITE : SM_OK;
+  return h[0] || h[1] ? SM_ENONFINITE : SM_OK;
 }
 
 }  // extern "C"

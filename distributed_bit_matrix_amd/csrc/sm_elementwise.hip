@@ -1075,11 +1075,25 @@ hipError_t launch_vote_ternary(const int8_t* S, int64_t stride, int M, int64_t n
   return hipGetLastError();
 }
 
-__global__ void k_clear_status(int32_t* status) {
-  if (threadIdx.x == 0) status[0] = 0;
+// Status words of a workspace: word 0 is the flag of the current step (the
+// update of W is skipped while it is set), word 1 collects the flags of
+// worker pipelines enqueued since the last step.  A step starts by moving
+// word 1 into word 0 and clearing word 1.
+__global__ void k_begin_status(int32_t* status) {
+  if (threadIdx.x == 0) {
+    status[0] = status[1];
+    status[1] = 0;
+  }
 }
-hipError_t launch_clear_status(int32_t* status, hipStream_t s) {
-  hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(64), 0, s, status);
+hipError_t launch_begin_status(int32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(k_begin_status, dim3(1), dim3(64), 0, s, status);
+  return hipGetLastError();
+}
+__global__ void k_reset_status(int32_t* status) {
+  if (threadIdx.x < 2) status[threadIdx.x] = 0;
+}
+hipError_t launch_reset_status(int32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(k_reset_status, dim3(1), dim3(64), 0, s, status);
   return hipGetLastError();
 }
 

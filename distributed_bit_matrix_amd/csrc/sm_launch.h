@@ -152,7 +152,11 @@ struct ScaledOutArgs {
 };
 hipError_t launch_scaled_out(const ScaledOutArgs& a, hipStream_t s);
 
-hipError_t launch_clear_status(int32_t* status, hipStream_t s);
+// Start of a step: status[0] = status[1] (flags of the worker pipelines
+// enqueued since the last step), status[1] = 0.
+hipError_t launch_begin_status(int32_t* status, hipStream_t s);
+// Both status words to 0.
+hipError_t launch_reset_status(int32_t* status, hipStream_t s);
 // Q = a I + b A on each matrix's padded Rp x Rp bfloat16 buffer
 // (blocks_per_mat = Rp * Rp / kChunk).
 hipError_t launch_affine_ident(const Groups& G, const void* A, float a, float b, void* Q,

@@ -14,10 +14,20 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every array pointer is a DEVICE pointer unless stated otherwise; the
- *   caller owns all memory.  The library allocates nothing and keeps no
- *   state between calls; it is reentrant.
+ *   caller owns all memory.  The library allocates no device memory: scratch
+ *   space is a caller workspace (the *_workspace queries give its size).
+ *   The only host objects it creates are those of an executor
+ *   (signmuon_executor_create), which the caller owns and destroys; besides
+ *   that, the first call on a device sets the matrix-core kernels' LDS size
+ *   attribute once.  Calls that use different workspaces (and executors)
+ *   are independent and may run concurrently; calls that share a workspace
+ *   must be ordered on one stream.
  * - Work is enqueued asynchronously on the caller's stream (NULL = the null
- *   stream) and never synchronises, except signmuon_get_status.
+ *   stream) and never synchronises, except signmuon_get_status and
+ *   signmuon_executor_destroy.  Without an executor, and while the caller's
+ *   stream is being captured into a HIP graph, every kernel of a call is
+ *   enqueued on the caller's stream and nothing else: such calls can be
+ *   captured.
  * - Matrices are row-major and contiguous.  A parameter set is one flat
  *   array per quantity (G, W, Mom) holding every matrix back to back at
  *   sm_matrix.elem_off.
@@ -185,6 +195,23 @@ sm_status signmuon_apply(void *W, int32_t w_dtype, const int8_t *D,
                          hipStream_t stream);
 
 /*
+ * Executor: caller-owned host resources that let signmuon_step,
+ * signmuon_worker_pipeline and signmuon_step_profiled run the PolarNS work
+ * of disjoint groups of matrices as up to three concurrent chains (three
+ * non-blocking HIP streams on the device current at creation, forked from
+ * and joined back into the caller's stream with the executor's own events;
+ * each of the at most two PolarNS passes of a step has its own events).
+ * Passing NULL instead runs everything on the caller's stream (a few percent
+ * slower on large sets).  An executor may be passed only on its own device
+ * (else SM_EINVAL) and by one thread at a time (calls lock it while they
+ * enqueue).  signmuon_executor_destroy waits for the executor's streams,
+ * then frees it; NULL is a no-op.
+ */
+typedef struct sm_executor sm_executor;
+sm_status signmuon_executor_create(sm_executor **ex);
+sm_status signmuon_executor_destroy(sm_executor *ex);
+
+/*
  * One fused Sign-Muon step for the local worker over a parameter set, with
  * the M workers' packed sign buffers resident on this GPU (they stand for
  * this GPU's copy after an exchange of sign buffers).
@@ -209,11 +236,20 @@ sm_status signmuon_apply(void *W, int32_t w_dtype, const int8_t *D,
  * buffers, worker m at bits + m * worker_stride_words.  u0: float32, the
  * concatenation of every matrix's min(rows, cols) power-iteration start
  * vector, or NULL (all ones).  ws: workspace of signmuon_step_workspace()
- * bytes, 256-byte aligned; its contents on entry do not matter.
+ * bytes, 256-byte aligned.  Before its first call a step workspace must be
+ * zero-filled or passed to signmuon_reset_status: its first 8 bytes carry
+ * the non-finite flags from call to call (below); the rest is scratch
+ * whose contents on entry do not matter.
+ *
+ * ex: an executor for the concurrent chains, or NULL (see above).
  *
  * If any G, W or new momentum value is non-finite the update of W is
  * skipped (Mom and the local buffer are still written) and the next
- * signmuon_get_status on the same workspace returns SM_ENONFINITE.
+ * signmuon_get_status on the same workspace returns SM_ENONFINITE.  The
+ * same holds for a non-finite value met by any signmuon_worker_pipeline
+ * call on the same workspace enqueued since the previous step: a step
+ * starts by taking over those flags, so the vote skips the update when any
+ * worker's pipeline of the step saw a non-finite value.
  */
 size_t signmuon_step_workspace(const sm_matrix *mats, int32_t n_mats,
                                const sm_hparams *hp, int32_t post_vote);
@@ -223,7 +259,7 @@ sm_status signmuon_step(const sm_matrix *mats, int32_t n_mats,
                         int64_t worker_stride_words, int32_t M,
                         int32_t local_worker, int32_t post_vote,
                         const float *u0, void *ws, size_t ws_bytes,
-                        hipStream_t stream);
+                        sm_executor *ex, hipStream_t stream);
 
 /*
  * The per-worker half of signmuon_step for worker `worker` (Algorithm 2's
@@ -232,9 +268,11 @@ sm_status signmuon_step(const sm_matrix *mats, int32_t n_mats,
  * momentum and its signs packed into buffer `worker`; post_vote = 1:
  * momentum and the signs of the new momentum packed into buffer `worker`.  No vote, and W is
  * only read.  Arguments, validation and workspace as for signmuon_step (same
- * workspace size); a non-finite G, W or momentum value is recorded for
- * signmuon_get_status.  Calling it for workers 1..M-1 and signmuon_step for
- * worker 0 runs every worker's pipeline of one step on this GPU.
+ * workspace size); a non-finite G, W or momentum value is recorded in the
+ * workspace (it never clears a flag): signmuon_get_status reports it, and
+ * the next signmuon_step on the workspace skips its update.  Calling it for
+ * workers 1..M-1 and then signmuon_step for worker 0, with one workspace on
+ * one stream, runs every worker's pipeline of one step on this GPU.
  */
 sm_status signmuon_worker_pipeline(const sm_matrix *mats, int32_t n_mats,
                                    const sm_hparams *hp, const float *G,
@@ -242,7 +280,7 @@ sm_status signmuon_worker_pipeline(const sm_matrix *mats, int32_t n_mats,
                                    uint32_t *bits, int64_t worker_stride_words,
                                    int32_t M, int32_t worker, int32_t post_vote,
                                    const float *u0, void *ws, size_t ws_bytes,
-                                   hipStream_t stream);
+                                   sm_executor *ex, hipStream_t stream);
 
 /*
  * Instrumented step: identical work to signmuon_step, plus a hipEventRecord
@@ -273,13 +311,24 @@ sm_status signmuon_step_profiled(const sm_matrix *mats, int32_t n_mats,
                                  int64_t worker_stride_words, int32_t M,
                                  int32_t local_worker, int32_t post_vote,
                                  const float *u0, void *ws, size_t ws_bytes,
-                                 sm_profile *prof, hipStream_t stream);
+                                 sm_profile *prof, sm_executor *ex,
+                                 hipStream_t stream);
 
 /*
- * Status of the last signmuon_step that used workspace ws: waits for the
- * stream, then returns SM_OK or SM_ENONFINITE (SM_EHIP if the copy fails).
+ * Status of workspace ws: waits for the stream, then returns SM_ENONFINITE
+ * if the last signmuon_step on ws, or a signmuon_worker_pipeline call on ws
+ * enqueued after it, saw a non-finite value; else SM_OK (SM_EHIP if the
+ * copy fails).  Reading the status clears nothing.
  */
 sm_status signmuon_get_status(const void *ws, hipStream_t stream);
+
+/*
+ * Clears the non-finite flags of step workspace ws (enqueued on the stream,
+ * a kernel, so it can be captured): for a new workspace that is not
+ * zero-filled, or to drop the flags of worker pipelines whose step is
+ * abandoned.
+ */
+sm_status signmuon_reset_status(void *ws, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -26,14 +26,13 @@ def oracle_hp(hp):
                 coeffs=tuple(f32(c) for c in hp.coeffs))
 
 
-def sign_gate(U_gpu_signs_neg, U_oracle, min_agree=0.999, rel=1e-2, min_allowed=2):
+def sign_gate(U_gpu_signs_neg, U_oracle, min_agree=0.999, rel=1e-2):
     """Check packed-sign agreement.  U_gpu_signs_neg: bool array (GPU bit = 1,
     i.e. negative); U_oracle: float64 oracle polar factor.  Returns stats.
 
-    Every mismatch must sit within rel * rms of zero (where the operand
-    precision cannot decide the sign), and there may be at most a fraction
-    1 - min_agree of them, or min_allowed, whichever is larger: for matrices
-    of a thousand entries a fraction alone would allow a single such entry."""
+    At most a fraction 1 - min_agree of the entries may disagree, and every
+    disagreement must sit within rel * rms of zero (where the operand
+    precision cannot decide the sign)."""
     Uo = np.asarray(U_oracle, np.float64).reshape(-1)
     gneg = np.asarray(U_gpu_signs_neg, bool).reshape(-1)
     oneg = Uo < 0
@@ -41,7 +40,7 @@ def sign_gate(U_gpu_signs_neg, U_oracle, min_agree=0.999, rel=1e-2, min_allowed=
     rms = float(np.sqrt(np.mean(Uo ** 2))) if Uo.size else 0.0
     agree = 1.0 - float(mis.mean()) if Uo.size else 1.0
     worst = float(np.abs(Uo[mis]).max() / rms) if mis.any() and rms > 0 else 0.0
-    ok = (agree >= min_agree or int(mis.sum()) <= min_allowed) and (not mis.any() or worst < rel)
+    ok = agree >= min_agree and (not mis.any() or worst < rel)
     return ok, dict(agree=agree, worst_over_rms=worst, mismatches=int(mis.sum()))
 
 

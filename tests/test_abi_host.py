@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 18
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_strerror():
     L = B.lib()
-    assert L.signmuon_abi_version() == 1
+    assert L.signmuon_abi_version() == 2
     for code in [0, -1, -2, -3, -4, -5, -6]:
         assert len(B.strerror(code)) >= 2
     assert B.strerror(-99) == "unknown status"
@@ -142,7 +142,7 @@ def _step(L, mats, hp, M=3, local=0, stride=None, post=0, ws_bytes=None, G=FAKE)
     if ws_bytes is None:
         ws_bytes = B.step_workspace(mats, hp, post)
     return L.signmuon_step(arr, len(mats), ctypes.byref(hp.to_c()), G, FAKE, 1, FAKE,
-                           FAKE, stride, M, local, post, None, FAKE, ws_bytes, None)
+                           FAKE, stride, M, local, post, None, FAKE, ws_bytes, None, None)
 
 
 def test_worker_pipeline_validation():
@@ -156,7 +156,7 @@ def test_worker_pipeline_validation():
     def call(M=3, worker=0, post=0, G=FAKE, stride=words, ws_bytes=ws):
         return L.signmuon_worker_pipeline(arr, len(mats), ctypes.byref(hp.to_c()), G, FAKE, 1,
                                           FAKE, FAKE, stride, M, worker, post, None, FAKE,
-                                          ws_bytes, None)
+                                          ws_bytes, None, None)
     assert call(M=0) == B.SM_ERANGE
     assert call(worker=3) == B.SM_EINVAL
     assert call(worker=-1) == B.SM_EINVAL
@@ -243,3 +243,12 @@ def test_ternary_validation():
     assert v(FAKE, 10, 3, 10, 0, None, None, None) == B.SM_EINVAL
     assert v(None, 0, 3, 0, 0, None, None, None) == B.SM_OK
 
+
+
+def test_executor_arguments():
+    # a NULL destination is an argument error; destroying NULL is a no-op
+    L = B.lib()
+    assert L.signmuon_executor_create(None) == B.SM_EINVAL
+    assert L.signmuon_executor_destroy(None) == B.SM_OK
+    assert L.signmuon_reset_status(None, None) == B.SM_EWORKSPACE
+    assert L.signmuon_reset_status(ctypes.c_void_p(0x10010), None) == B.SM_EWORKSPACE

@@ -12,12 +12,16 @@ def _u(n, seed=0):
 def test_sign_gate_exact_and_near_zero_flips():
     U = _u(1216)
     assert sign_gate(U < 0, U)[0]
-    small = np.argsort(np.abs(U))[:3]          # the entries closest to zero
+    small = np.argsort(np.abs(U))[:2]          # the entries closest to zero
     neg = U < 0
-    two = neg.copy(); two[small[:2]] ^= True
-    assert sign_gate(two, U)[0]                 # two undecidable entries: allowed
-    three = neg.copy(); three[small] ^= True
-    assert not sign_gate(three, U)[0]           # a third is over both limits
+    one = neg.copy(); one[small[0]] ^= True
+    assert sign_gate(one, U)[0]                 # one undecidable entry: 0.08%
+    two = neg.copy(); two[small] ^= True
+    assert not sign_gate(two, U)[0]             # a second is over 0.1%
+    # a tiny matrix has no room for any disagreement
+    V = _u(9, 3)
+    flip = V < 0; flip[np.argmin(np.abs(V))] ^= True
+    assert not sign_gate(flip, V)[0]
 
 
 def test_sign_gate_rejects_planted_mistakes():

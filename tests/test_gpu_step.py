@@ -7,11 +7,13 @@ workers' packed buffers are the oracle's own.  The checks per step:
 * the local worker's packed signs pass the sign gate against the oracle's
   polar factor (post-vote: against its momentum; with both polar steps,
   post_vote = 2, against the polar factor as in Algorithm 2);
-* W is bit-exact wherever the local worker's bit equals the oracle's (every
-  vote input is then identical), and otherwise moves by at most one step;
-* post-vote and both polar steps: the polar factor recovered from the W
-  update is within the polar tolerance of the oracle's and passes the sign
-  gate.
+* the vote and what follows it are checked against the oracle applied to
+  the GPU's own vote inputs (the M buffers as they are after the step, the
+  local one written by the GPU): Algorithm 2's W bit-exact everywhere; for
+  the post-vote step and both polar steps, the polar factor recovered from
+  the W update within the polar tolerance of the oracle's PolarNS of that
+  majority matrix (and, with float32 W and products, the sign gate).  Every
+  sampled matrix is compared.
 Full-size workloads are checked on sampled matrices the oracle can afford.
 """
 import numpy as np
@@ -94,6 +96,7 @@ def check_step(w, st, hp, W, Moms, Gs, u0s, sample=None, other_bits=None):
     # momentum (all entries)
     tol = momentum_tol(np.float32(Moms[0]), Gs[0], W, o["beta"], o["lam"])
     assert np.all(np.abs(Mg.astype(np.float64) - Mom_new0) <= tol)
+    checked = 0
     for i in idx:
         r, c = mats[i]
         n = r * c
@@ -102,29 +105,41 @@ def check_step(w, st, hp, W, Moms, Gs, u0s, sample=None, other_bits=None):
         gneg = unpack_neg(bg[0, wsl], n)
         ok, stats = sign_gate(gneg, U0[i])
         assert ok, (i, mats[i], stats)
-        oneg = unpack_neg(bits_in[0, wsl], n)
-        same = gneg == oneg
-        # vote inputs identical where the local bit agrees
-        sums = O.vote_sums_from_bits(bits_in[:, wsl], n)
-        if w.post_vote:
-            D = O.majority_from_sums(sums, w.tie_value).astype(np.float64).reshape(r, c)
-            Upost, _ = O.polar_ns(D, o["K"], o["eps"], o["scale"], o["P"], o["coeffs"],
-                                  None if u0s is None else u0s[i].astype(np.float64))
-            if same.all():
-                Ug = (W[sl].astype(np.float64) - Wg[sl].astype(np.float64)) / o["eta"]
-                tol = polar_tol(hp.precision) + 1e-6 + w_round_tol(Wg[sl], w.w_dtype, o["eta"])
-                assert np.all(np.abs(Ug - Upost.reshape(-1)) <= tol), (i, "post-vote")
-                if w.w_dtype == "f32":
-                    # (a bfloat16 W keeps too few bits for the signs of small U)
-                    ok, stats = sign_gate(Ug < 0, Upost.reshape(-1))
-                    assert ok, (i, "post-vote", stats)
-            continue
-        D = O.majority_from_sums(sums, w.tie_value)
-        Wn = O.apply_update(W[sl], D, o["eta"], w.w_dtype)
-        assert np.array_equal(Wg[sl][same].view(np.uint32), Wn[same].view(np.uint32)), i
-        moved = np.abs(Wg[sl][~same].astype(np.float64) - W[sl][~same])
-        assert np.all(moved <= 1.01 * o["eta"] + 1e-2 * np.abs(W[sl][~same])), i
+        # the other workers' buffers are inputs: the step leaves them alone
+        assert np.array_equal(bg[1:, wsl], bits_in[1:, wsl]), i
+        check_after_vote(w, hp, W[sl], Wg[sl], bg[:, wsl], (r, c),
+                         None if u0s is None else u0s[i], i)
+        checked += 1
+    assert checked == len(idx)
     return out
+
+
+def check_after_vote(w, hp, W, Wg, bits, shape, u0, tag):
+    """The vote and the update against the oracle applied to the GPU's own
+    vote inputs `bits` (M x words of one matrix): Algorithm 2 bit-exact; the
+    post-vote polar step within the polar tolerance."""
+    o = oracle_hp(hp)
+    r, c = shape
+    n = r * c
+    D = O.majority_from_sums(O.vote_sums_from_bits(bits, n), w.tie_value)
+    if not w.post_vote:
+        Wn = O.apply_update(W, D, o["eta"], w.w_dtype)
+        assert np.array_equal(Wg.view(np.uint32), Wn.view(np.uint32)), (tag, "apply")
+        return
+    Upost, _ = O.polar_ns(D.astype(np.float64).reshape(r, c), o["K"], o["eps"], o["scale"],
+                          o["P"], o["coeffs"], None if u0 is None else u0.astype(np.float64))
+    Ug = (W.astype(np.float64) - Wg.astype(np.float64)) / o["eta"]
+    tol = polar_tol(hp.precision) + 1e-6 + w_round_tol(Wg, w.w_dtype, o["eta"])
+    err = np.abs(Ug - Upost.reshape(-1))
+    assert np.all(err <= tol), (tag, "post-vote", float(err.max()))
+    if w.w_dtype == "f32" and hp.precision == "f32":
+        # The post-vote update applies U itself, not its signs, so the polar
+        # bound above is its gate.  With float32 products the recovered U
+        # also carries the signs of the oracle's (a bfloat16 W keeps too few
+        # bits for that, and bfloat16 products leave about one undecidable
+        # sign per thousand entries on small matrices).
+        ok, stats = sign_gate(Ug < 0, Upost.reshape(-1))
+        assert ok, (tag, "post-vote", stats)
 
 
 def gradients(w, t, M):
@@ -146,6 +161,9 @@ SMALL = {
                                                             ns_precision="bf16x3"), None, 2),
     "postvote": (WL.scaled(WL.get("postvote"), [(128, 128)] * 6 + [(256, 512)] * 2,
                            M=40), None, 3),
+    # the post-vote step with float32 W and float32 products
+    "postvote_f32": (WL.scaled(WL.get("postvote"), [(128, 128)] * 2 + [(256, 512)], M=12,
+                               name="postvote-f32").replace(ns_precision="f32"), None, 2),
     # both polar steps: Algorithm 2's worker pipeline, then PolarNS of the vote
     "prepost": (WL.scaled(WL.get("nanogpt_prepost"), [(192, 576), (192, 192), (192, 768),
                                                       (768, 192)] * 2), None, 3),
@@ -196,11 +214,21 @@ def test_step_nanogpt_iterate_form(monkeypatch):
 # Sizes whose entry counts are odd: matrices start at unaligned offsets (no
 # 16-byte vector access of W), widths are not multiples of 32 (signs packed
 # by the separate pass), and the vote covers partial 2048-entry stretches.
-ODD_MATS = [(5, 37), (33, 7), (45, 71), (64, 19), (3, 3)]
+# The tiny shapes run float32 Newton-Schulz: bfloat16 operands leave about
+# one undecidable sign per thousand entries on matrices this small (a CPU
+# emulation of the bfloat16 products gave 1e-3 to 2.5e-3 on 19x64 to
+# 45x71), which the 99.9% agreement cannot absorb; the bfloat16 cases use
+# odd shapes of 15000+ entries, where the emulation gave at most 5.3e-4.
+ODD_TINY = [(5, 37), (33, 7), (45, 71), (64, 19), (3, 3)]
+ODD_BF16 = [(97, 161), (161, 97), (45, 403), (403, 45), (33, 515)]
 ODD = {
-    "f32_M5": WL.scaled(WL.get("single"), ODD_MATS, M=5, name="odd-f32"),
-    "bf16_M6": WL.scaled(WL.get("nanogpt"), ODD_MATS, M=6, name="odd-bf16"),
-    "prepost_M5": WL.scaled(WL.get("nanogpt_prepost"), ODD_MATS, M=5, name="odd-prepost"),
+    "f32_M5": WL.scaled(WL.get("single"), ODD_TINY, M=5, name="odd-f32"),
+    "bf16w_f32ns_M6": WL.scaled(WL.get("nanogpt"), ODD_TINY, M=6,
+                                name="odd-bf16w").replace(ns_precision="f32"),
+    "bf16_M6": WL.scaled(WL.get("nanogpt"), ODD_BF16, M=6, name="odd-bf16"),
+    "prepost_f32ns_M5": WL.scaled(WL.get("nanogpt_prepost"), ODD_TINY, M=5,
+                                  name="odd-prepost").replace(ns_precision="f32"),
+    "prepost_M5": WL.scaled(WL.get("nanogpt_prepost"), ODD_BF16, M=5, name="odd-prepost-bf16"),
 }
 
 
@@ -233,6 +261,43 @@ def test_step_nonfinite_skips_update():
     Wg, Mg, bg, status = st.run(W, np.zeros(w.d, np.float32), WL.gradient(w, 0, 0), bits,
                                 None)
     assert status == B.SM_OK
+
+
+@pytest.mark.parametrize("post_vote", [0, 1])
+def test_nonfinite_in_another_worker_skips_update(post_vote):
+    # a non-finite gradient in worker 3's pipeline (signmuon_worker_pipeline)
+    # reaches the step of worker 0: its update is skipped and the status
+    # reports it; the next round of finite pipelines and step updates W
+    w = SMALL["nanogpt"][0].replace(post_vote=post_vote)
+    hp = hparams(w)
+    st = GpuState(w, hp)
+    M = w.M
+    W = WL.init_weights(w)
+    W_t = torch.from_numpy(W).cuda().to(st.wdt)
+    W_in = W_t.clone()
+    Mt = [torch.zeros(w.d, dtype=torch.float32, device="cuda") for _ in range(M)]
+    b_t = torch.from_numpy(WL.random_bits(w, M).view(np.int32)).cuda()
+
+    def one_round(bad_worker):
+        for m in range(1, M):
+            G = WL.gradient(w, 0, m)
+            if m == bad_worker:
+                G[777] = np.nan
+            st.plan.worker_pipeline(torch.from_numpy(G).cuda(), W_t, Mt[m], b_t, st.words,
+                                    M, m)
+        st.plan(torch.from_numpy(WL.gradient(w, 0, 0)).cuda(), W_t, Mt[0], b_t, st.words,
+                M, 0)
+        return st.plan.status()
+
+    print(f"non-finite in worker 3, post_vote={post_vote}", flush=True)
+    assert one_round(3) == B.SM_ENONFINITE
+    torch.cuda.synchronize()
+    assert torch.equal(W_t.view(torch.int16), W_in.view(torch.int16))
+    for m in Mt:
+        m.zero_()
+    assert one_round(None) == B.SM_OK
+    torch.cuda.synchronize()
+    assert not torch.equal(W_t.view(torch.int16), W_in.view(torch.int16))
 
 
 def test_step_deterministic_and_permutation_invariant():
@@ -349,30 +414,19 @@ def test_all_workers_on_gpu(name, chain_mode):
     for m in range(M):
         tol = momentum_tol(np.float32(Moms[m]), Gs[m], W, o["beta"], o["lam"])
         assert np.all(np.abs(Mt[m].cpu().numpy().astype(np.float64) - out["Mom"][m]) <= tol), m
-    all_same = []
+    checked = 0
     for i, (r, c) in enumerate(mats):
         n = r * c
         wsl = slice(woffs[i], woffs[i] + (n + 31) // 32)
-        same = np.ones(n, bool)
+        sl = slice(offs[i], offs[i] + n)
         for m in range(M):
             gneg = unpack_neg(bg[m, wsl], n)
             ref = out["Mom"][m][offs[i]:offs[i] + n] if w.post_vote == 1 \
                 else out["U"][m][i].reshape(-1)
             ok, stats = sign_gate(gneg, ref)
             assert ok, (m, i, stats)
-            same &= gneg == unpack_neg(out["bits"][m, wsl], n)
-        all_same.append(same)
-        if not w.post_vote:
-            sl = slice(offs[i], offs[i] + n)
-            assert np.array_equal(Wg[sl][same].view(np.uint32),
-                                  out["Wn"][sl][same].view(np.uint32)), i
-    if w.post_vote:
-        # the post-vote update of a matrix is exact only if its whole majority matrix is
-        for i, (r, c) in enumerate(mats):
-            if all_same[i].all():
-                sl = slice(offs[i], offs[i] + r * c)
-                Ug = (W[sl].astype(np.float64) - Wg[sl].astype(np.float64)) / o["eta"]
-                Uo = (W[sl].astype(np.float64) - out["Wn"][sl].astype(np.float64)) / o["eta"]
-                tol = (polar_tol(hp.precision) + 1e-6 + w_round_tol(Wg[sl], w.w_dtype, o["eta"])
-                       + w_round_tol(out["Wn"][sl], w.w_dtype, o["eta"]))
-                assert np.all(np.abs(Ug - Uo) <= tol), i
+        # the vote over the M GPU-written buffers and the update
+        check_after_vote(w, hp, W[sl], Wg[sl], bg[:, wsl], (r, c),
+                         None if u0s is None else u0s[i], i)
+        checked += 1
+    assert checked == len(mats)
