@@ -32,6 +32,7 @@ EXPORTS = (
     "signmuon_step", "signmuon_step_profiled", "signmuon_get_status",
     "signmuon_worker_pipeline", "signmuon_sign_ternary", "signmuon_majority_vote_ternary",
     "signmuon_executor_create", "signmuon_executor_destroy", "signmuon_reset_status",
+    "signmuon_polar_ns_static",
 )
 PHASES = {0: "start", 1: "momentum", 2: "prescale", 3: "gemm", 4: "pack", 5: "vote"}
 
@@ -105,6 +106,7 @@ def lib():
             "signmuon_momentum": (i32, [vp, vp, i32, vp, i64, f32, f32, vp]),
             "signmuon_polar_ns_workspace": (sz, [i64, i64, hp]),
             "signmuon_polar_ns": (i32, [vp, vp, i64, i64, hp, vp, vp, sz, vp]),
+            "signmuon_polar_ns_static": (i32, [vp, vp, i64, i64, hp, vp, vp]),
             "signmuon_sign_pack": (i32, [vp, vp, i64, vp]),
             "signmuon_majority_vote": (i32, [vp, i64, i32, i64, i32, vp, vp, vp]),
             "signmuon_sign_ternary": (i32, [vp, vp, i64, vp]),
@@ -216,6 +218,25 @@ def polar_ns(X, hp: HParams, u0=None, U=None, ws=None, stream=None):
     _check("signmuon_polar_ns", lib().signmuon_polar_ns(
         _ptr(X), _ptr(U), rows, cols, ctypes.byref(hp.to_c()), _ptr(u0), _ptr(ws),
         ws.numel(), _stream(stream)))
+    return U
+
+
+STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def polar_ns_static(X, hp: HParams, u0=None, U=None, stream=None):
+    """PolarNS with the library's own per-GPU scratch array (no workspace,
+    no allocation by the library; calls on one GPU must not overlap)."""
+    import torch
+    _require(X, torch.float32, "X")
+    rows, cols = X.shape
+    if U is None:
+        U = torch.empty_like(X)
+    _require(U, torch.float32, "U")
+    if u0 is not None:
+        _require(u0, torch.float32, "u0")
+    _check("signmuon_polar_ns_static", lib().signmuon_polar_ns_static(
+        _ptr(X), _ptr(U), rows, cols, ctypes.byref(hp.to_c()), _ptr(u0), _stream(stream)))
     return U
 
 

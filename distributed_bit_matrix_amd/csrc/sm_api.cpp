@@ -1025,6 +1025,54 @@ sm_status signmuon_polar_ns(const float* X, float* U, int64_t rows, int64_t cols
   return run_ns(P, mp, groups, fus, hp, B, io, stream);
 }
 
+}  // extern "C"
+
+// Scratch memory of signmuon_polar_ns_static: one array per GPU, held from
+// the library's load until the process ends and shared by every such call
+// on that GPU.  In host code `scratch` names a host-side stand-in, not the
+// device array: kernels and copies get the device address that
+// hipGetSymbolAddress returns (scratch_on_device), never `scratch`.
+static __device__ __align__(256) char scratch[SM_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current device's scratch array, looked up once per
+// device with that device current.
+hipError_t scratch_on_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+}  // namespace
+
+extern "C" {
+
+sm_status signmuon_polar_ns_static(const float* X, float* U, int64_t rows, int64_t cols,
+                                   const sm_hparams* hp, const float* u0,
+                                   hipStream_t stream) {
+  const sm_status st = check_hparams(hp, false);
+  if (st != SM_OK) return st;
+  if (!X || !U || X == U) return SM_EINVAL;
+  const size_t need = signmuon_polar_ns_workspace(rows, cols, hp);
+  if (need == 0) return SM_EINVAL;
+  if (need > SM_STATIC_SCRATCH_BYTES) return SM_ERANGE;
+  void* ws = nullptr;
+  if (scratch_on_device(&ws) != hipSuccess || !ws) return SM_EHIP;
+  return signmuon_polar_ns(X, U, rows, cols, hp, u0, ws, SM_STATIC_SCRATCH_BYTES, stream);
+}
+
 size_t signmuon_step_workspace(const sm_matrix* mats, int32_t n_mats,
                                const sm_hparams* hp, int32_t post_vote) {
   if (!mats || n_mats < 1 || n_mats > 65536) return 0;

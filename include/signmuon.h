@@ -141,6 +141,24 @@ sm_status signmuon_polar_ns(const float *X, float *U, int64_t rows,
                             hipStream_t stream);
 
 /*
+ * signmuon_polar_ns without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The same kernels run with their
+ * scratch space in an array of SM_STATIC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends; it calls no
+ * allocator.  A matrix whose signmuon_polar_ns_workspace() exceeds that size
+ * returns SM_ERANGE (with bfloat16 products and the Frobenius scale, shapes
+ * up to about 1024 x 4096 fit); other arguments and errors as for
+ * signmuon_polar_ns.  Every such call on one GPU uses the same array:
+ * calls that overlap in time on one GPU (two streams, two threads) race and
+ * must be ordered by the caller.
+ */
+#define SM_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+sm_status signmuon_polar_ns_static(const float *X, float *U, int64_t rows,
+                                   int64_t cols, const sm_hparams *hp,
+                                   const float *u0, hipStream_t stream);
+
+/*
  * Entrywise sign with 1-bit packing (section 3 sign; section 6 packing):
  * bits[j/32] bit (j%32) = (U[j] < 0) for j < n; ceil(n/32) words written,
  * tail bits 0.  U: float32[n].

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -252,3 +252,19 @@ def test_executor_arguments():
     assert L.signmuon_executor_destroy(None) == B.SM_OK
     assert L.signmuon_reset_status(None, None) == B.SM_EWORKSPACE
     assert L.signmuon_reset_status(ctypes.c_void_p(0x10010), None) == B.SM_EWORKSPACE
+
+
+def test_polar_ns_static_limits():
+    # argument errors and sizes past the scratch array return before any
+    # device work
+    L = B.lib()
+    hp = _hp(K=5, scale="fro")
+    c = hp.to_c()
+    U = ctypes.c_void_p(0x20000)
+    f = L.signmuon_polar_ns_static
+    assert f(FAKE, U, 0, 512, ctypes.byref(c), None, None) == B.SM_EINVAL
+    assert f(FAKE, FAKE, 256, 512, ctypes.byref(c), None, None) == B.SM_EINVAL
+    assert B.polar_ns_workspace(4096, 4096, hp) > B.STATIC_SCRATCH_BYTES
+    assert f(FAKE, U, 4096, 4096, ctypes.byref(c), None, None) == B.SM_ERANGE
+    assert B.polar_ns_workspace(1024, 4096, hp) <= B.STATIC_SCRATCH_BYTES
+    assert B.polar_ns_workspace(3072, 768, hp) <= B.STATIC_SCRATCH_BYTES
