@@ -115,7 +115,8 @@ def describe(w):
     ns = {"f32": "f32", "bf16": "bf16 operands / f32 accumulate",
           "bf16x3": "split-bf16 (x3)"}[w.ns_precision]
     coeffs = "quintic" if w.coeffs[2] else "cubic"
-    return (f"{w.name}: {parts}; W {w.w_dtype}, momentum f32; M={w.M} resident packed "
+    enc = "int8 ternary" if w.encoding == "ternary" else "packed"
+    return (f"{w.name}: {parts}; W {w.w_dtype}, momentum f32; M={w.M} resident {enc} "
             f"sign buffers; K={w.K} {coeffs} Newton-Schulz ({ns}), {w.scale} scaling"
             + (f" P={w.P}" if w.scale == "spectral" else "")
             + {0: "", 1: "; post-vote polar", 2: "; pre-sign and post-vote polar"}[int(w.post_vote)])
@@ -182,14 +183,19 @@ class Run:
         self.w = w
         hp = B.HParams(eta=w.eta, beta=w.beta, lam=w.lam, eps=w.eps, K=w.K, scale=w.scale,
                        P=w.P, coeffs=w.coeffs, precision=w.ns_precision,
-                       tie_value=w.tie_value)
+                       tie_value=w.tie_value, encoding=w.encoding)
         layout, self.d, self.words = B.default_layout(w.mats)
         self.plan = B.StepPlan(layout, hp, w.post_vote, device=dev)
         wdt = torch.bfloat16 if w.w_dtype == "bf16" else torch.float32
         self.W = torch.from_numpy(WL.init_weights(w)).to(dev).to(wdt)
         self.Mom = torch.zeros(self.d, dtype=torch.float32, device=dev)
         self.G = torch.from_numpy(WL.gradient(w, 0, 0)).to(dev)
-        self.bits = torch.from_numpy(WL.random_bits(w, w.M).view(np.int32)).to(dev)
+        if w.encoding == "ternary":
+            # int8 sign buffers: d bytes per worker, matrices at their offsets
+            self.bits = torch.from_numpy(WL.random_ternary(w, w.M)).to(dev)
+            self.words = self.d
+        else:
+            self.bits = torch.from_numpy(WL.random_bits(w, w.M).view(np.int32)).to(dev)
         self.u0 = (torch.from_numpy(np.concatenate(WL.power_start(w))).to(dev)
                    if w.scale == "spectral" else None)
         torch.cuda.synchronize()
@@ -275,7 +281,7 @@ def main():
     ap.add_argument("--rb-steps", type=int, default=5,
                     help="timed steps of the all-workers figure (every worker's pipeline "
                          "inside the step)")
-    ap.add_argument("--also", default="resnet50,nanogpt_prepost",
+    ap.add_argument("--also", default="resnet50,nanogpt_prepost,nanogpt_ternary",
                     help="comma-separated further workloads whose plain steps/s and phase "
                          "times are reported under other_workloads ('' = none)")
     ap.add_argument("--ternary", type=int, default=1,

@@ -23,6 +23,7 @@ SM_OK, SM_EINVAL, SM_EWORKSPACE, SM_EHIP, SM_ENONFINITE, SM_ERANGE, SM_EUNSUPPOR
 SM_F32, SM_BF16 = 0, 1
 NS_F32, NS_BF16, NS_BF16X3 = 0, 1, 2
 SCALE_FRO, SCALE_SPECTRAL = 0, 1
+SIGNS_PACKED, SIGNS_TERNARY = 0, 1
 MAX_WORKERS = 32767
 
 EXPORTS = (
@@ -49,7 +50,8 @@ class SmHparams(ctypes.Structure):
                 ("K", ctypes.c_int32), ("scale", ctypes.c_int32),
                 ("P", ctypes.c_int32), ("ns_a", ctypes.c_float),
                 ("ns_b", ctypes.c_float), ("ns_c", ctypes.c_float),
-                ("ns_precision", ctypes.c_int32), ("tie_value", ctypes.c_int32)]
+                ("ns_precision", ctypes.c_int32), ("tie_value", ctypes.c_int32),
+                ("sign_encoding", ctypes.c_int32)]
 
 
 class SmProfile(ctypes.Structure):
@@ -75,13 +77,15 @@ class HParams:
     coeffs: Tuple[float, float, float] = (1.5, -0.5, 0.0)
     precision: str = "bf16"         # "f32" | "bf16" | "bf16x3"
     tie_value: int = 0
+    encoding: str = "packed"        # worker sign buffers: "packed" | "ternary"
 
     def to_c(self) -> SmHparams:
         prec = {"f32": NS_F32, "bf16": NS_BF16, "bf16x3": NS_BF16X3}[self.precision]
         scale = {"fro": SCALE_FRO, "spectral": SCALE_SPECTRAL}[self.scale]
+        enc = {"packed": SIGNS_PACKED, "ternary": SIGNS_TERNARY}[self.encoding]
         a, b, c = self.coeffs
         return SmHparams(self.eta, self.beta, self.lam, self.eps, int(self.K), scale,
-                         int(self.P), a, b, c, prec, int(self.tie_value))
+                         int(self.P), a, b, c, prec, int(self.tie_value), enc)
 
 
 _LIB = None
@@ -175,7 +179,9 @@ def mats_array(mats: Sequence[Tuple[int, int, int, int]]):
 
 
 def default_layout(shapes: Sequence[Tuple[int, int]]):
-    """Back-to-back layout: (rows, cols, elem_off, word_off) per matrix."""
+    """Back-to-back layout: (rows, cols, elem_off, word_off) per matrix, the
+    entry count d and the packed words per worker (int8 sign buffers take d
+    bytes per worker, each matrix at its elem_off)."""
     out, eo, wo = [], 0, 0
     for r, c in shapes:
         out.append((r, c, eo, wo))

@@ -43,6 +43,8 @@ sm_status check_hparams(const sm_hparams* hp, bool need_momentum) {
   if (hp->scale == SM_SCALE_SPECTRAL && (hp->P < 1 || hp->P > 256)) return SM_EINVAL;
   if (!finite(hp->ns_a) || !finite(hp->ns_b) || !finite(hp->ns_c)) return SM_EINVAL;
   if (hp->ns_precision < SM_NS_F32 || hp->ns_precision > SM_NS_BF16X3) return SM_EINVAL;
+  if (hp->sign_encoding != SM_SIGNS_PACKED && hp->sign_encoding != SM_SIGNS_TERNARY)
+    return SM_EINVAL;
   if (need_momentum) {
     if (!finite(hp->beta) || hp->beta < 0.f || hp->beta >= 1.f) return SM_EINVAL;
     if (!finite(hp->lambda) || hp->lambda < 0.f) return SM_EINVAL;
@@ -326,7 +328,8 @@ struct NsIO {
   const float* src_user;
   int final_out;
   float* U;
-  uint32_t* bits;         // local worker buffer base
+  uint32_t* bits;         // local worker buffer base (packed signs)
+  int8_t* tern;           // local worker buffer base (int8 signs, O_TERN)
   void* W; int w_bf16; float eta;
   const float* u0;
   const int32_t* status;
@@ -397,8 +400,12 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
     out.push_back([&, hp, part_kind, s]() -> sm_status {
       HIP_TRY(for_launches(groups, [&](Group& g) {
         g.blocks_per_mat = 1;
+        const int64_t mn = mp[g.idx0].rows * mp[g.idx0].cols;
+        // partial sums per matrix: one per sweep tile (0), per packed vote
+        // block (1) or per int8 vote block (2)
         g.gk = (int32_t)(part_kind == 0 ? mp[g.idx0].Mp * mp[g.idx0].Np / 4096
-                                        : (((mp[g.idx0].rows * mp[g.idx0].cols + 31) / 32) + 255) / 256);
+                         : part_kind == 1 ? (((mn + 31) / 32) + 255) / 256
+                                          : (mn + kTernChunk - 1) / kTernChunk);
         return true;
       }, [&](const Groups& G) { return launch_fro_finalize(G, B.part, hp->eps, B.scal, s); }));
       HIP_TRY(mark(io.prof, SM_PHASE_PRESCALE, s));
@@ -602,7 +609,7 @@ void gram_space_stages(const Plan& P, const std::vector<MatPlan>& mp,
           a.out = O_U; a.U = B.u;
         } else {
           a.out = io.final_out;
-          a.U = io.U; a.bits = io.bits;
+          a.U = io.U; a.bits = io.bits; a.tern = io.tern;
           a.W = io.W; a.w_bf16 = io.w_bf16; a.eta = io.eta;
           a.status = io.status;
         }
@@ -692,7 +699,7 @@ void ns_stages(const Plan& P, const std::vector<MatPlan>& mp,
             a.out = O_U; a.U = B.u;
           } else {
             a.out = io.final_out;
-            a.U = io.U; a.bits = io.bits;
+            a.U = io.U; a.bits = io.bits; a.tern = io.tern;
             a.W = io.W; a.w_bf16 = io.w_bf16; a.eta = io.eta;
             a.status = io.status;
           }
@@ -1080,7 +1087,9 @@ size_t signmuon_step_workspace(const sm_matrix* mats, int32_t n_mats,
   if (post_vote < 0 || post_vote > 2) return 0;
   bool need_u = false;
   for (int i = 0; i < n_mats; ++i)
-    if (post_vote != 1 && hp->K > 0 && mats[i].cols % 32 != 0) need_u = true;
+    if (post_vote != 1 && hp->K > 0 && mats[i].cols % 32 != 0 &&
+        hp->sign_encoding == SM_SIGNS_PACKED)
+      need_u = true;
   Plan P;
   std::vector<MatPlan> mp;
   if (build_plan(mats, n_mats, hp, post_vote != 0, need_u, P, mp) != SM_OK) return 0;
@@ -1109,6 +1118,9 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   if (w_dtype != SM_F32 && w_dtype != SM_BF16) return SM_EINVAL;
   if (!G || !W || !Mom || !bits) return SM_EINVAL;
   if (worker_stride_words < 0) return SM_EINVAL;
+  // int8 sign buffers: worker_stride_words counts bytes, and a matrix's
+  // signs sit at its element offset
+  const bool tern = hp->sign_encoding == SM_SIGNS_TERNARY;
   // shapes, offsets and overlap
   {
     std::vector<std::pair<int64_t, int64_t>> es, wsg;
@@ -1117,19 +1129,23 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
       if (m.rows < 1 || m.cols < 1 || m.rows > kMaxDim || m.cols > kMaxDim) return SM_EINVAL;
       if (m.elem_off < 0 || m.word_off < 0) return SM_EINVAL;
       int64_t mn = m.rows * m.cols, nw = (mn + 31) / 32;
-      if (m.word_off + nw > worker_stride_words) return SM_EINVAL;
+      if (tern ? m.elem_off + mn > worker_stride_words : m.word_off + nw > worker_stride_words)
+        return SM_EINVAL;
       es.push_back({m.elem_off, m.elem_off + mn});
-      wsg.push_back({m.word_off, m.word_off + nw});
+      wsg.push_back(tern ? std::make_pair(m.elem_off, m.elem_off + mn)
+                         : std::make_pair(m.word_off, m.word_off + nw));
     }
     std::sort(es.begin(), es.end());
     std::sort(wsg.begin(), wsg.end());
     for (int i = 1; i < n_mats; ++i)
       if (es[i].first < es[i - 1].second || wsg[i].first < wsg[i - 1].second) return SM_EINVAL;
   }
+  // packed signs are written from the last epilogue for widths that are a
+  // multiple of 32 (else from U in the workspace); int8 signs always are
   std::vector<bool> fus(n_mats);
   bool need_u = false;
   for (int i = 0; i < n_mats; ++i) {
-    fus[i] = mats[i].cols % 32 == 0;
+    fus[i] = tern || mats[i].cols % 32 == 0;
     if (post_vote != 1 && hp->K > 0 && !fus[i]) need_u = true;
   }
   Plan P;
@@ -1149,7 +1165,9 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   for (int i = 0; i < n_mats; ++i) all[i] = i;
   std::vector<Group> groups = make_groups(mp, all);
   set_vec_ok(groups, aligned16(G) && aligned16(W) && aligned16(Mom));
-  uint32_t* local_bits = bits + (int64_t)local_worker * worker_stride_words;
+  uint32_t* local_bits = tern ? nullptr : bits + (int64_t)local_worker * worker_stride_words;
+  int8_t* const tern_bufs = tern ? reinterpret_cast<int8_t*>(bits) : nullptr;
+  int8_t* local_tern = tern ? tern_bufs + (int64_t)local_worker * worker_stride_words : nullptr;
   const int w_bf16 = w_dtype == SM_BF16;
   HIP_TRY(mark(prof, SM_PHASE_START, stream));
   // A step takes over the flags of the worker pipelines enqueued since the
@@ -1167,10 +1185,14 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   VoteArgs va;
   std::memset(&va, 0, sizeof(va));
   va.M = M; va.tie = hp->tie_value; va.w_bf16 = w_bf16; va.precision = P.precision;
-  va.bits = bits; va.stride = worker_stride_words;
+  va.bits = tern ? nullptr : bits; va.tern = tern_bufs; va.stride = worker_stride_words;
   va.W = W; va.eta = hp->eta; va.status = B.status;
+  auto vote_blocks = [tern](int mode, const Group& g) {
+    return tern ? (int32_t)(((int64_t)g.rows * g.cols + kTernChunk - 1) / kTernChunk)
+                : vote_blocks_per_mat(mode, g.rows, g.cols);
+  };
   auto vote_fill = [&](Group& g) {
-    g.blocks_per_mat = vote_blocks_per_mat(va.mode, g.rows, g.cols);
+    g.blocks_per_mat = vote_blocks(va.mode, g);
     return true;
   };
 
@@ -1183,7 +1205,8 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
       MomSignArgs ms;
       std::memset(&ms, 0, sizeof(ms));
       ms.w_bf16 = w_bf16; ms.beta = hp->beta; ms.lam = hp->lambda;
-      ms.Gr = G; ms.W = W; ms.Mom = Mom; ms.bits = local_bits; ms.status = flag;
+      ms.Gr = G; ms.W = W; ms.Mom = Mom; ms.bits = local_bits; ms.tern = local_tern;
+      ms.status = flag;
       HIP_TRY(for_launches(groups, [&](Group& g) {
         g.blocks_per_mat = (int32_t)(((int64_t)g.rows * g.cols + kChunk - 1) / kChunk);
         return true;
@@ -1203,7 +1226,8 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
         return true;
       };
       io.first_xsrc = XS_USER; io.src_user = Mom;
-      io.final_out = O_BITS; io.bits = local_bits; io.U = nullptr;
+      io.final_out = tern ? O_TERN : O_BITS; io.bits = local_bits; io.tern = local_tern;
+      io.U = nullptr;
       if (!prof && post_vote == 0) {
         // Each chain sweeps its own matrices, runs their PolarNS, packs the
         // signs the last epilogue could not, and votes over them, so one
@@ -1235,7 +1259,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
             VoteArgs a = va;
             a.mode = VA_APPLY;
             HIP_TRY(for_launches(*pcg, [&](Group& g) {
-              g.blocks_per_mat = vote_blocks_per_mat(VA_APPLY, g.rows, g.cols);
+              g.blocks_per_mat = vote_blocks(VA_APPLY, g);
               return true;
             }, [&](const Groups& Gs) { a.G = Gs; return launch_vote_groups(a, cs); }));
             return SM_OK;
@@ -1271,7 +1295,8 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
     MomSignArgs ms;
     std::memset(&ms, 0, sizeof(ms));
     ms.w_bf16 = w_bf16; ms.beta = hp->beta; ms.lam = hp->lambda;
-    ms.Gr = G; ms.W = W; ms.Mom = Mom; ms.bits = local_bits; ms.status = flag;
+    ms.Gr = G; ms.W = W; ms.Mom = Mom; ms.bits = local_bits; ms.tern = local_tern;
+    ms.status = flag;
     HIP_TRY(for_launches(groups, [&](Group& g) {
       g.blocks_per_mat = (int32_t)(((int64_t)g.rows * g.cols + kChunk - 1) / kChunk);
       return true;
@@ -1303,9 +1328,10 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   io.final_out = O_APPLY;
   if (hp->K > 0) {
     std::vector<bool> fus_all(n_mats, true);
-    return run_polar(P, mp, groups, fus_all, hp, B, io, 1, stream, ex, post_vote == 2 ? 1 : 0);
+    return run_polar(P, mp, groups, fus_all, hp, B, io, tern ? 2 : 1, stream, ex,
+                     post_vote == 2 ? 1 : 0);
   }
-  st = run_pre_scale(P, mp, groups, hp, B, io, 1, stream);
+  st = run_pre_scale(P, mp, groups, hp, B, io, tern ? 2 : 1, stream);
   if (st != SM_OK) return st;
   {
     ScaledOutArgs so;

@@ -510,7 +510,9 @@ __global__ __launch_bounds__(256) void k_momentum_sign(MomSignArgs a) {
       bad |= !__builtin_isfinite(gv[it]) || !__builtin_isfinite(wv[it]) ||
              !__builtin_isfinite(mk);
       neg = mk < 0.0f;
+      if (a.tern) a.tern[eoff + e] = (int8_t)(mk > 0.0f ? 1 : neg ? -1 : 0);
     }
+    if (a.tern) continue;
     const uint64_t m = __ballot(neg);
     const int64_t w0 = base >> 5;
     if (lane < 2 && w0 + lane < nw) a.bits[woff + w0 + lane] = (uint32_t)(m >> (32 * lane));
@@ -725,6 +727,112 @@ __global__ __launch_bounds__(256) void k_vote_apply(VoteArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Vote over M int8 sign buffers of each matrix (exact integer sums, a zero
+// sign adds nothing): VA_APPLY updates W, VA_SBAR writes the majority matrix
+// into the padded operand copy (+ partial sums of squares per block).  A
+// thread takes 16 consecutive entries of one matrix (kTernChunk per block);
+// the 16 signs of a worker are one 16-byte load when the buffers allow it.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_vote_tern(VoteArgs a) {
+  if (a.mode == VA_APPLY && a.status && a.status[0] != 0) return;
+  int gi, mi, q;
+  group_of_block(a.G, blockIdx.x, gi, mi, q);
+  const Group& g = a.G.g[gi];
+  const int rows = g.rows, cols = g.cols;
+  const int64_t mn = (int64_t)rows * cols;
+  const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
+  const int64_t e0 = (int64_t)q * kTernChunk + threadIdx.x * 16;
+  float ss = 0.0f;
+  if (e0 < mn) {
+    const int cnt = mn - e0 < 16 ? (int)(mn - e0) : 16;
+    int acc[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] = 0;
+    const int8_t* src = a.tern + eoff + e0;
+    const bool vec = cnt == 16 && (a.stride & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+    if (vec) {
+      for (int m = 0; m < a.M; ++m) {
+        const u32x4_t w = ld_nt(reinterpret_cast<const u32x4_t*>(src + (int64_t)m * a.stride));
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          acc[k] += (int)(int8_t)((w[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+      }
+    } else {
+      for (int m = 0; m < a.M; ++m) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (k < cnt) acc[k] += src[(int64_t)m * a.stride + k];
+      }
+    }
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = (float)majority(acc[k], a.tie);
+    if (a.mode == VA_APPLY) {
+      if (g.vec_ok && cnt == 16) {
+        // e0 and the matrix offset are multiples of 8: 16-byte W accesses
+        if (a.w_bf16) {
+          u32x4_t* wp = reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(a.W) + eoff + e0);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            u32x4_t x = ld_nt(wp + h);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const bf16_t r0 = f32_to_bf16(apply_value(__uint_as_float(x[k] << 16), a.eta,
+                                                        v[8 * h + 2 * k]));
+              const bf16_t r1 = f32_to_bf16(apply_value(__uint_as_float(x[k] & 0xFFFF0000u),
+                                                        a.eta, v[8 * h + 2 * k + 1]));
+              x[k] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+            }
+            st_nt(wp + h, x);
+          }
+        } else {
+          f32x4_t* wp = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.W) + eoff + e0);
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            f32x4_t x = ld_nt(wp + h);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) x[k] = apply_value(x[k], a.eta, v[4 * h + k]);
+            st_nt(wp + h, x);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (k < cnt) apply_store(a.W, a.w_bf16, eoff + e0 + k, a.eta, v[k]);
+      }
+    } else {
+      // VA_SBAR: the majority matrix into the padded operand copy
+      const int64_t Np = round_up(cols, kPad);
+      const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (k < cnt) ss += v[k] * v[k];
+      if (cnt == 16 && cols % 16 == 0 && !s_tall(g)) {
+        const int row = (int)(e0 / cols), col = (int)(e0 - (int64_t)row * cols);
+        float h0[8], h1[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { h0[k] = v[k]; h1[k] = v[8 + k]; }
+        store_op8(a.precision, a.o_hi, a.o_lo, xoff + (int64_t)row * Np + col, h0);
+        store_op8(a.precision, a.o_hi, a.o_lo, xoff + (int64_t)row * Np + col + 8, h1);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          if (k >= cnt) continue;
+          const int64_t e = e0 + k;
+          const int row = (int)(e / cols), col = (int)(e - (int64_t)row * cols);
+          store_opv(a.precision, a.o_hi, a.o_lo, xoff + s_index(g, row, col), v[k]);
+        }
+      }
+    }
+  }
+  if (a.mode == VA_SBAR && a.part) {
+    float t = block_sum(ss);
+    if (threadIdx.x == 0) a.part[g.c0 + (int64_t)mi * g.c_stride + q] = t;
+  }
+}
+
 int vote_blocks_per_mat(int mode, int64_t rows, int64_t cols) {
   const int64_t mn = rows * cols;
   if (mode == VA_APPLY) return (int)((mn + 8191) / 8192);
@@ -734,6 +842,10 @@ int vote_blocks_per_mat(int mode, int64_t rows, int64_t cols) {
 hipError_t launch_vote_groups(const VoteArgs& a, hipStream_t s) {
   if (a.G.total_blocks <= 0) return hipSuccess;
   dim3 grid(a.G.total_blocks), block(256);
+  if (a.tern) {
+    hipLaunchKernelGGL(k_vote_tern, grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   if (a.mode == VA_APPLY) {
     if (a.M <= 15)
       hipLaunchKernelGGL(k_vote_apply<4>, grid, block, 0, s, a);

@@ -834,6 +834,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     // even (k is a multiple of 128).
     constexpr int NM = NKK * TI * TJ;                 // MFMA tiles per slab
     u32x4_t fa0[NKK][NFA], fb0[NKK][NFB], fa1[NKK][NFA], fb1[NKK][NFB];
+    // (every launch has at least NSTG slabs: the host checks k)
 #pragma unroll
     for (int p = 0; p < NSTG; ++p) issue(p);
     wait_vmcnt<(NSTG - 1) * LOADS>();
@@ -1023,7 +1024,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT, SWAP>(acc, smem, offset_ptr<T>(A.o_hi, xoff),
                                                              offset_ptr<T>(A.o_lo, xoff), Cp, m0,
                                                              n0, (int)Rp, wm, wn, lane, tid);
-    } else if (A.out == O_U || A.out == O_APPLY) {
+    } else if (A.out == O_U || A.out == O_APPLY || A.out == O_TERN) {
       if (A.out == O_APPLY && A.status && A.status[0] != 0) return;
 #pragma unroll
       for (int i = 0; i < TI; ++i)
@@ -1034,8 +1035,10 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
             const int si = acc_row(i, r), sj = acc_col(j, r);
             if (si < sr && sj < sc) {
               const int64_t e = eoff + (tall ? (int64_t)sj * cols + si : (int64_t)si * cols + sj);
-              if (A.out == O_U) A.U[e] = acc[i][j][r];
-              else apply_one(A.W, A.w_bf16, e, A.eta, acc[i][j][r]);
+              const float u = acc[i][j][r];
+              if (A.out == O_U) A.U[e] = u;
+              else if (A.out == O_TERN) A.tern[e] = (int8_t)(u > 0.0f ? 1 : u < 0.0f ? -1 : 0);
+              else apply_one(A.W, A.w_bf16, e, A.eta, u);
             }
           }
     } else {
@@ -1212,13 +1215,55 @@ __global__ __launch_bounds__(256) void k_split_reduce(GemmArgs A) {
 #ifndef SM_GEMM_PIPE
 #define SM_GEMM_PIPE 1
 #endif
+// Pipeline of the bfloat16 128x128 kernels per epilogue (Gram and raw Gram,
+// which share the split-k slab count; symmetric product; update): stages,
+// slab row bytes and blocks per CU the register allocation leaves room for.
+#ifndef SM_OP_NSTG
+#define SM_OP_NSTG 2
+#endif
+#ifndef SM_OP_RB
+#define SM_OP_RB 128
+#endif
+#ifndef SM_OP_WPE
+#define SM_OP_WPE 2
+#endif
+#ifndef SM_SQ_NSTG
+#define SM_SQ_NSTG 2
+#endif
+#ifndef SM_SQ_RB
+#define SM_SQ_RB 128
+#endif
+#ifndef SM_SQ_WPE
+#define SM_SQ_WPE 2
+#endif
+#ifndef SM_UP_NSTG
+#define SM_UP_NSTG 2
+#endif
+#ifndef SM_UP_RB
+#define SM_UP_RB 128
+#endif
+#ifndef SM_UP_WPE
+#define SM_UP_WPE 2
+#endif
 template <typename T, int SPLIT, int EPI, bool WIDE = false>
 struct Cfg {
+  static constexpr bool BF = sizeof(T) == 2 && SPLIT == 1 && !WIDE;
   static constexpr int WM = 2;
   static constexpr int TI = 4, TJ = WIDE ? 8 : 4;
-  static constexpr int RB = WIDE ? 64 : 128;
-  static constexpr int NSTG = WIDE ? 3 : 2;
-  static constexpr int WPE = 2;
+  static constexpr int RB = WIDE ? 64
+                          : !BF ? 128
+                          : EPI == E_OP || EPI == E_RAW ? SM_OP_RB
+                          : EPI == E_SQUARE ? SM_SQ_RB
+                          : EPI == E_UPDATE ? SM_UP_RB : 128;
+  static constexpr int NSTG = WIDE ? 3
+                            : !BF ? 2
+                            : EPI == E_OP || EPI == E_RAW ? SM_OP_NSTG
+                            : EPI == E_SQUARE ? SM_SQ_NSTG
+                            : EPI == E_UPDATE ? SM_UP_NSTG : 2;
+  static constexpr int WPE = !BF ? 2
+                           : EPI == E_OP || EPI == E_RAW ? SM_OP_WPE
+                           : EPI == E_SQUARE ? SM_SQ_WPE
+                           : EPI == E_UPDATE ? SM_UP_WPE : 2;
   // software pipelining holds two slabs of fragments: used where those and
   // the accumulators fit in 192 registers
   static constexpr bool PIPE = SM_GEMM_PIPE && sizeof(T) == 2 && SPLIT == 1 &&
@@ -1252,6 +1297,19 @@ void gemm_tile(int precision, int epi, int64_t gm, int64_t gn, int64_t gk, int* 
 template <typename T, int SPLIT, int EPI, bool WIDE = false>
 static hipError_t launch_one(const GemmArgs& args, hipStream_t s) {
   using C = Cfg<T, SPLIT, EPI, WIDE>;
+  // the pipelined k-loop fills all NSTG stages before its first slab: every
+  // block needs at least NSTG slabs (and, pipelined, an even count)
+  constexpr int BK = C::RB / (int)sizeof(T);
+  for (int i = 0; i < args.G.n; ++i) {
+    const Group& g = args.G.g[i];
+    if (g.gk % BK) return hipErrorInvalidValue;
+    int64_t fewest = g.gk / BK;
+    if (g.ksplit > 1) {
+      const int64_t last = fewest - (int64_t)(g.ksplit - 1) * g.kslabs;
+      fewest = std::min<int64_t>(g.kslabs, last);
+    }
+    if (fewest < C::NSTG || (C::PIPE && (fewest & 1))) return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL((k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE, C::PIPE, C::TRACC>),
                      dim3(args.G.total_blocks), dim3(128 * C::WM), C::lds(), s, args);
   return hipGetLastError();

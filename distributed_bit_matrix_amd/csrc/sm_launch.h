@@ -18,7 +18,7 @@ __host__ __device__ inline int gemm_ops(int a_fam, int b_fam) {
 }
 
 enum Epi { E_RAW = 0, E_OP = 1, E_SQUARE = 2, E_UPDATE = 3 };
-enum Out { O_X = 0, O_U = 1, O_BITS = 2, O_APPLY = 3 };
+enum Out { O_X = 0, O_U = 1, O_BITS = 2, O_APPLY = 3, O_TERN = 4 };
 
 // Source of the update's a X term on the first Newton-Schulz step: the
 // caller's float32 matrix (XS_USER, full precision) or the bf16/f32 operand
@@ -42,6 +42,7 @@ struct GemmArgs {
   const float* xs_user;            // XS_USER: float32 source in caller layout
   float* U;                        // O_U
   uint32_t* bits;                  // O_BITS (buffer of the local worker)
+  int8_t* tern;                    // O_TERN: int8 signs, caller layout (local worker)
   void* W; int32_t w_bf16; float eta;   // O_APPLY
   const int32_t* status;           // O_APPLY is skipped when *status != 0
   float* kpart;                    // split-k partial tiles (groups with ksplit > 1)
@@ -101,6 +102,7 @@ struct MomSignArgs {
   int32_t w_bf16;
   float beta, lam;
   const float* Gr; const void* W; float* Mom; uint32_t* bits;
+  int8_t* tern;         // non-NULL: int8 signs (sign(0) = 0) instead of bits
   int32_t* status;
 };
 hipError_t launch_momentum_sign(const MomSignArgs& a, hipStream_t s);
@@ -112,13 +114,19 @@ struct VoteArgs {
   Groups G;
   int32_t mode, M, tie, w_bf16, precision;
   const uint32_t* bits; int64_t stride;
+  // non-NULL: int8 sign buffers (worker m at tern + m * stride bytes, a
+  // matrix at its element offset) instead of the packed bits
+  const int8_t* tern;
   void* W; float eta;
   void* o_hi; void* o_lo; float* part;
   const int32_t* status;
 };
 hipError_t launch_vote_groups(const VoteArgs& a, hipStream_t s);
-// Group::blocks_per_mat of a vote launch in mode `mode`.
+// Group::blocks_per_mat of a vote launch in mode `mode` (packed bits) and
+// of a vote over int8 sign buffers (kTernChunk entries per block, both
+// modes).
 int vote_blocks_per_mat(int mode, int64_t rows, int64_t cols);
+constexpr int kTernChunk = 4096;
 
 // Zero the padding of the padded operand copies.
 hipError_t launch_zero_pad(const Groups& G, int precision, void* hi, void* lo,

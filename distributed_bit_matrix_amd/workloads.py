@@ -20,6 +20,8 @@ gradients stand in for them):
   gradients with a rank-16 signal; cubic and quintic coefficients.
 * ``postvote`` 512 x (128x128) + 64 x (1024x4096) float32, M = 200, the
   post-vote polar variant with spectral P = 8 and correlated worker noise.
+* ``nanogpt_ternary`` the nanoGPT set with int8 ternary sign buffers;
+  ``nanogpt_prepost`` the nanoGPT set with both polar steps.
 """
 from __future__ import annotations
 
@@ -54,6 +56,7 @@ class Workload:
     post_vote: int          # 0: Algorithm 2; 1: polar after the vote; 2: both
     signal_std: float       # std of the shared signal S
     seed_index: int
+    encoding: str = "packed"   # worker sign buffers: "packed" | "ternary" (int8)
 
     @property
     def d(self) -> int:
@@ -130,6 +133,12 @@ WORKLOADS = {
         name="postvote", mats=((128, 128),) * 512 + ((1024, 4096),) * 64,
         w_dtype="f32", M=200, scale="spectral", P=8, ns_precision="bf16", T=10,
         warmup=2, post_vote=True, signal_std=0.5, seed_index=4, **_COMMON),
+    # The nanoGPT set with int8 ternary sign buffers (one byte per entry and
+    # worker, a zero sign kept as 0).
+    "nanogpt_ternary": Workload(
+        name="nanogpt_ternary", mats=NANOGPT_LAYER * 12, w_dtype="bf16", M=8,
+        scale="fro", P=0, ns_precision="bf16", T=20, warmup=3,
+        post_vote=False, signal_std=0.3, seed_index=6, encoding="ternary", **_COMMON),
     # The nanoGPT set with both polar steps (no configuration of its own is
     # given for this variant).
     "nanogpt_prepost": Workload(
@@ -229,6 +238,16 @@ def random_bits(w: Workload, workers: int, tag: int = 0) -> np.ndarray:
     """Uniform random packed sign buffers, shape (workers, words), uint32."""
     g = _rng(w.seed, _TAG_BITS, tag)
     return g.integers(0, 2 ** 32, size=(workers, w.words), dtype=np.uint32)
+
+
+def random_ternary(w: Workload, workers: int, zero_frac: float = 0.02,
+                   tag: int = 0) -> np.ndarray:
+    """Random int8 sign buffers, shape (workers, d): +1 or -1 with equal
+    probability, 0 on a fraction zero_frac of the entries."""
+    g = _rng(w.seed, _TAG_BITS, 100 + tag)
+    s = np.where(g.random((workers, w.d)) < 0.5, -1, 1).astype(np.int8)
+    s[g.random((workers, w.d)) < zero_frac] = 0
+    return s
 
 
 def planted_tie_bits(w: Workload, frac: float = 0.01, tag: int = 1) -> np.ndarray:

@@ -78,9 +78,19 @@ typedef enum sm_ns_precision {
  * s = sqrt(|A u|) at the last step. */
 typedef enum sm_scale { SM_SCALE_FRO = 0, SM_SCALE_SPECTRAL = 1 } sm_scale;
 
+/* Encoding of the worker sign buffers of signmuon_step and
+ * signmuon_worker_pipeline.  PACKED: 1 bit per entry (the blog's d/8-byte
+ * payload), bit = 1 for a negative value, so a zero travels as +1.
+ * TERNARY: one int8 per entry in {-1, 0, +1} (section 3: sign(0) = 0;
+ * Algorithm 2 and Figure 1 exchange int8 signs), so an exact zero adds
+ * nothing to the vote. */
+typedef enum sm_sign_encoding {
+  SM_SIGNS_PACKED = 0, SM_SIGNS_TERNARY = 1
+} sm_sign_encoding;
+
 /* Hyper-parameters: the inputs of Algorithm 1 (eta, beta, lambda, K, eps,
- * scale, P) plus the Newton-Schulz coefficients, the product precision and
- * the tie policy.  One Newton-Schulz step is X <- a X + (b A + c A^2) X with
+ * scale, P) plus the Newton-Schulz coefficients, the product precision, the
+ * tie policy and the sign encoding.  One Newton-Schulz step is X <- a X + (b A + c A^2) X with
  * A = X X^T for a wide matrix (rows <= cols), and X <- a X + X (b A + c A^2)
  * with A = X^T X for a tall one; the cubic of section 4 is (1.5, -0.5, 0). */
 typedef struct sm_hparams {
@@ -94,6 +104,7 @@ typedef struct sm_hparams {
   float ns_a, ns_b, ns_c;
   int32_t ns_precision;  /* sm_ns_precision */
   int32_t tie_value;     /* value of a tied vote: 0 (default) or 1 */
+  int32_t sign_encoding; /* sm_sign_encoding (steps only; else ignored) */
 } sm_hparams;
 
 /* One matrix of a parameter set. */
@@ -251,7 +262,11 @@ sm_status signmuon_executor_destroy(sm_executor *ex);
  * mats[n_mats]: HOST array of matrix descriptors (1 <= n_mats <= 65536);
  * matrices must not overlap in the flat arrays or in a worker buffer.
  * G, Mom: float32 flat arrays; W: w_dtype flat array.  bits: M worker
- * buffers, worker m at bits + m * worker_stride_words.  u0: float32, the
+ * buffers, worker m at bits + m * worker_stride_words.  With
+ * hp->sign_encoding = SM_SIGNS_TERNARY, bits points to int8 buffers instead:
+ * worker m at (int8_t *)bits + m * worker_stride_words (then a count of
+ * bytes), matrix i's signs at its elem_off (word_off is ignored), and
+ * elem_off + rows * cols <= worker_stride_words.  u0: float32, the
  * concatenation of every matrix's min(rows, cols) power-iteration start
  * vector, or NULL (all ones).  ws: workspace of signmuon_step_workspace()
  * bytes, 256-byte aligned.  Before its first call a step workspace must be

@@ -308,7 +308,7 @@ def worker_direction(Mom_new, hp, u0=None, post_vote=0):
 
 
 def step(mats, W, Moms, Gs, hp, tie_value=0, post_vote=0, w_dtype="f32",
-         u0s=None):
+         u0s=None, encoding="packed"):
     """One Sign-Muon step for M workers over a parameter set.
 
     post_vote = 0: Algorithm 2 of the bittide.aicompass.dev rendering (polar
@@ -324,13 +324,22 @@ def step(mats, W, Moms, Gs, hp, tie_value=0, post_vote=0, w_dtype="f32",
     scale, P and optionally coeffs.  u0s: optional list (per matrix) of
     power-iteration start vectors.
 
+    encoding: what each worker sends.  "packed": the 1-bit buffers of the
+    blog's byte count, where a zero travels as the +1 bit.  "ternary": the
+    signs as int8 values in {-1, 0, +1} (section 3 defines sign(0) = 0;
+    Algorithm 2 and Figure 1 sum the workers' signs as int8 in one
+    all-reduce), so an exact zero adds nothing to the vote.
+
     Returns a dict: Mom (list of new momenta, float64), U (per worker, list
     of per-matrix polar factors or None), bits (M x words, uint32 per matrix
-    concatenated with each matrix starting on a word boundary), sums
-    (int32, length d), D (int8 ternary majority), Wn (new W, float32 array
-    of w_dtype values), and for the post-vote variant Upost (per-matrix
-    polar factor of the majority matrix).
+    concatenated with each matrix starting on a word boundary; packed only),
+    signs (M x d int8 ternary signs; ternary only), sums (int32, length d),
+    D (int8 ternary majority), Wn (new W, float32 array of w_dtype values),
+    and for the post-vote variant Upost (per-matrix polar factor of the
+    majority matrix).
     """
+    if encoding not in ("packed", "ternary"):
+        raise ValueError(f"encoding must be 'packed' or 'ternary', not {encoding!r}")
     M = len(Gs)
     offs = np.cumsum([0] + [r * c for r, c in mats])
     d = int(offs[-1])
@@ -339,6 +348,7 @@ def step(mats, W, Moms, Gs, hp, tie_value=0, post_vote=0, w_dtype="f32",
     W = np.asarray(W, np.float64)
     new_moms, Us = [], []
     bits = np.zeros((M, int(woffs[-1])), dtype=np.uint32)
+    signs = np.zeros((M, d), dtype=np.int8)
     for m in range(M):
         Mom_new = momentum_update(Moms[m], Gs[m], W, hp["beta"], hp["lam"])
         new_moms.append(Mom_new)
@@ -348,14 +358,24 @@ def step(mats, W, Moms, Gs, hp, tie_value=0, post_vote=0, w_dtype="f32",
             u0 = None if u0s is None else u0s[i]
             vals, U = worker_direction(blk, hp, u0, post_vote)
             per.append(U)
-            bits[m, woffs[i]:woffs[i + 1]] = pack_signs(vals)
+            if encoding == "packed":
+                bits[m, woffs[i]:woffs[i + 1]] = pack_signs(vals)
+            else:
+                signs[m, offs[i]:offs[i + 1]] = sign_ternary(vals).reshape(-1)
         Us.append(per)
     sums = np.zeros(d, dtype=np.int32)
     for i, (r, c) in enumerate(mats):
-        sums[offs[i]:offs[i + 1]] = vote_sums_from_bits(
-            bits[:, woffs[i]:woffs[i + 1]], r * c)
+        if encoding == "packed":
+            sums[offs[i]:offs[i + 1]] = vote_sums_from_bits(
+                bits[:, woffs[i]:woffs[i + 1]], r * c)
+        else:
+            sums[offs[i]:offs[i + 1]] = vote_sums_from_signs(signs[:, offs[i]:offs[i + 1]])
     D = majority_from_sums(sums, tie_value)
-    out = {"Mom": new_moms, "U": Us, "bits": bits, "sums": sums, "D": D}
+    out = {"Mom": new_moms, "U": Us, "sums": sums, "D": D}
+    if encoding == "packed":
+        out["bits"] = bits
+    else:
+        out["signs"] = signs
     if post_vote not in (0, 1, 2):
         raise ValueError(f"post_vote must be 0, 1 or 2, not {post_vote!r}")
     if post_vote == 0:

@@ -44,6 +44,21 @@ def sign_gate(U_gpu_signs_neg, U_oracle, min_agree=0.999, rel=1e-2):
     return ok, dict(agree=agree, worst_over_rms=worst, mismatches=int(mis.sum()))
 
 
+def ternary_gate(S_gpu, U_oracle, min_agree=0.999, rel=1e-2):
+    """sign_gate for int8 signs in {-1, 0, +1}: a disagreement is any entry
+    whose sign differs from the oracle's (np.sign, with sign(0) = 0), held to
+    the same fraction and magnitude bounds."""
+    Uo = np.asarray(U_oracle, np.float64).reshape(-1)
+    Sg = np.asarray(S_gpu).astype(np.int64).reshape(-1)
+    mis = Sg != np.sign(Uo).astype(np.int64)
+    rms = float(np.sqrt(np.mean(Uo ** 2))) if Uo.size else 0.0
+    agree = 1.0 - float(mis.mean()) if Uo.size else 1.0
+    worst = float(np.abs(Uo[mis]).max() / rms) if mis.any() and rms > 0 else 0.0
+    ok = agree >= min_agree and (not mis.any() or worst < rel) and \
+        bool(np.all(np.isin(Sg, (-1, 0, 1))))
+    return ok, dict(agree=agree, worst_over_rms=worst, mismatches=int(mis.sum()))
+
+
 def unpack_neg(words, n):
     """GPU packed words -> bool 'negative' array (test-side decoding)."""
     by = np.asarray(words).astype("<u4").view(np.uint8)

@@ -268,3 +268,25 @@ def test_polar_ns_static_limits():
     assert f(FAKE, U, 4096, 4096, ctypes.byref(c), None, None) == B.SM_ERANGE
     assert B.polar_ns_workspace(1024, 4096, hp) <= B.STATIC_SCRATCH_BYTES
     assert B.polar_ns_workspace(3072, 768, hp) <= B.STATIC_SCRATCH_BYTES
+
+
+def test_step_ternary_validation():
+    # int8 sign buffers: the stride counts bytes and must cover every
+    # matrix's elem_off + rows * cols; word_off is not used; an unknown
+    # encoding is an argument error
+    L = B.lib()
+    hp = _hp(encoding="ternary")
+    mats, d, words = B.default_layout([(64, 96), (96, 64)])
+    assert _step(L, mats, hp, stride=d - 1) == B.SM_EINVAL
+    assert _step(L, mats, hp, stride=words) == B.SM_EINVAL
+    same_words = [mats[0], (96, 64, mats[1][2], 0)]          # word_off ignored
+    assert _step(L, same_words, hp, stride=d, ws_bytes=1024) == B.SM_EWORKSPACE
+    c = hp.to_c()
+    c.sign_encoding = 2
+    arr = B.mats_array(mats)
+    assert L.signmuon_step(arr, len(mats), ctypes.byref(c), FAKE, FAKE, 1, FAKE, FAKE, d, 3,
+                           0, 0, None, FAKE, 1 << 30, None, None) == B.SM_EINVAL
+    assert B.step_workspace(mats, hp, 0) > 0
+    # int8 signs come straight from the last epilogue: no float32 U is kept
+    m1, _, _ = B.default_layout([(5, 37)])
+    assert B.step_workspace(m1, hp, 0) < B.step_workspace(m1, _hp(), 0)

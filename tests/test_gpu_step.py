@@ -22,8 +22,8 @@ import pytest
 import oracle as O
 from distributed_bit_matrix_amd import binding as B
 from distributed_bit_matrix_amd import workloads as WL
-from tests.gpu_common import (f32, momentum_tol, oracle_hp, polar_tol, sign_gate, unpack_neg,
-                               w_round_tol)
+from tests.gpu_common import (f32, momentum_tol, oracle_hp, polar_tol, sign_gate, ternary_gate,
+                               unpack_neg, w_round_tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,27 +33,65 @@ torch = pytest.importorskip("torch")
 def hparams(w):
     return B.HParams(eta=w.eta, beta=w.beta, lam=w.lam, eps=w.eps, K=w.K, scale=w.scale,
                      P=w.P, coeffs=w.coeffs, precision=w.ns_precision,
-                     tie_value=w.tie_value)
+                     tie_value=w.tie_value, encoding=w.encoding)
 
 
 class GpuState:
+    """The step on the GPU for workload w.  Sign buffers are M x words
+    uint32 (packed) or M x d int8 (ternary)."""
+
     def __init__(self, w, hp):
         self.w = w
+        self.tern = w.encoding == "ternary"
         self.layout, self.d, self.words = B.default_layout(w.mats)
+        self.stride = self.d if self.tern else self.words
         self.plan = B.StepPlan(self.layout, hp, w.post_vote)
         self.wdt = torch.bfloat16 if w.w_dtype == "bf16" else torch.float32
+
+    def to_dev(self, bufs):
+        a = np.ascontiguousarray(bufs)
+        return torch.from_numpy(a if self.tern else a.view(np.int32)).cuda()
+
+    def from_dev(self, t):
+        a = t.cpu().numpy()
+        return a if self.tern else a.view(np.uint32)
 
     def run(self, W, Mom0, G0, bits, u0):
         W_t = torch.from_numpy(np.ascontiguousarray(W, np.float32)).cuda().to(self.wdt)
         M_t = torch.from_numpy(np.ascontiguousarray(Mom0, np.float32)).cuda()
         G_t = torch.from_numpy(np.ascontiguousarray(G0, np.float32)).cuda()
-        b_t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int32)).cuda()
+        b_t = self.to_dev(bits)
         u_t = None if u0 is None else torch.from_numpy(u0).cuda()
-        self.plan(G_t, W_t, M_t, b_t, self.words, bits.shape[0], 0, u0=u_t)
+        self.plan(G_t, W_t, M_t, b_t, self.stride, bits.shape[0], 0, u0=u_t)
         st = self.plan.status()
         torch.cuda.synchronize()
-        return (W_t.float().cpu().numpy(), M_t.cpu().numpy(),
-                b_t.cpu().numpy().view(np.uint32), st)
+        return (W_t.float().cpu().numpy(), M_t.cpu().numpy(), self.from_dev(b_t), st)
+
+
+def buf_slice(w, i):
+    """Slice of matrix i in a worker buffer (words, or int8 entries)."""
+    r, c = w.mats[i]
+    if w.encoding == "ternary":
+        return slice(w.elem_offsets[i], w.elem_offsets[i] + r * c)
+    return slice(w.word_offsets[i], w.word_offsets[i] + (r * c + 31) // 32)
+
+
+def encode(w, U):
+    """The oracle's buffer segment for values U (packed words or int8 signs)."""
+    return O.sign_ternary(U).reshape(-1) if w.encoding == "ternary" else O.pack_signs(U)
+
+
+def local_gate(w, seg, U_oracle, n):
+    """Sign gate of one worker's buffer segment against the oracle's U."""
+    if w.encoding == "ternary":
+        return ternary_gate(seg, U_oracle)
+    return sign_gate(unpack_neg(seg, n), U_oracle)
+
+
+def vote_sums(w, segs, n):
+    if w.encoding == "ternary":
+        return O.vote_sums_from_signs(segs)
+    return O.vote_sums_from_bits(segs, n)
 
 
 def u0_concat(w):
@@ -82,14 +120,14 @@ def check_step(w, st, hp, W, Moms, Gs, u0s, sample=None, other_bits=None):
     if other_bits is None:
         # the other workers are the oracle's own pipelines
         out = O.step(mats, W, Moms, Gs, o, w.tie_value, w.post_vote, w.w_dtype,
-                     None if u0s is None else [u.astype(np.float64) for u in u0s])
-        bits_in = out["bits"].copy()
+                     None if u0s is None else [u.astype(np.float64) for u in u0s],
+                     encoding=w.encoding)
+        bits_in = (out["signs"] if w.encoding == "ternary" else out["bits"]).copy()
     else:
         out = None
         bits_in = other_bits.copy()
         for i in idx:
-            bits_in[0, woffs[i]:woffs[i] + (mats[i][0] * mats[i][1] + 31) // 32] = \
-                O.pack_signs(U0[i])
+            bits_in[0, buf_slice(w, i)] = encode(w, U0[i])
     u0 = None if u0s is None else np.concatenate(u0s).astype(np.float32)
     Wg, Mg, bg, status = st.run(W, np.float32(Moms[0]), Gs[0], bits_in, u0)
     assert status == B.SM_OK
@@ -101,13 +139,12 @@ def check_step(w, st, hp, W, Moms, Gs, u0s, sample=None, other_bits=None):
         r, c = mats[i]
         n = r * c
         sl = slice(offs[i], offs[i] + n)
-        wsl = slice(woffs[i], woffs[i] + (n + 31) // 32)
-        gneg = unpack_neg(bg[0, wsl], n)
-        ok, stats = sign_gate(gneg, U0[i])
+        bsl = buf_slice(w, i)
+        ok, stats = local_gate(w, bg[0, bsl], U0[i], n)
         assert ok, (i, mats[i], stats)
         # the other workers' buffers are inputs: the step leaves them alone
-        assert np.array_equal(bg[1:, wsl], bits_in[1:, wsl]), i
-        check_after_vote(w, hp, W[sl], Wg[sl], bg[:, wsl], (r, c),
+        assert np.array_equal(bg[1:, bsl], bits_in[1:, bsl]), i
+        check_after_vote(w, hp, W[sl], Wg[sl], bg[:, bsl], (r, c),
                          None if u0s is None else u0s[i], i)
         checked += 1
     assert checked == len(idx)
@@ -116,12 +153,12 @@ def check_step(w, st, hp, W, Moms, Gs, u0s, sample=None, other_bits=None):
 
 def check_after_vote(w, hp, W, Wg, bits, shape, u0, tag):
     """The vote and the update against the oracle applied to the GPU's own
-    vote inputs `bits` (M x words of one matrix): Algorithm 2 bit-exact; the
-    post-vote polar step within the polar tolerance."""
+    vote inputs `bits` (the M buffer segments of one matrix): Algorithm 2
+    bit-exact; the post-vote polar step within the polar tolerance."""
     o = oracle_hp(hp)
     r, c = shape
     n = r * c
-    D = O.majority_from_sums(O.vote_sums_from_bits(bits, n), w.tie_value)
+    D = O.majority_from_sums(vote_sums(w, bits, n), w.tie_value)
     if not w.post_vote:
         Wn = O.apply_update(W, D, o["eta"], w.w_dtype)
         assert np.array_equal(Wg.view(np.uint32), Wn.view(np.uint32)), (tag, "apply")
@@ -161,6 +198,19 @@ SMALL = {
                                                             ns_precision="bf16x3"), None, 2),
     "postvote": (WL.scaled(WL.get("postvote"), [(128, 128)] * 6 + [(256, 512)] * 2,
                            M=40), None, 3),
+    # int8 ternary sign buffers: Algorithm 2, the post-vote step, both
+    "nanogpt_ternary": (WL.scaled(WL.get("nanogpt_ternary"), [(192, 576), (192, 192),
+                                                              (192, 768), (768, 192)] * 2),
+                        None, 3),
+    "resnet50_ternary": (WL.scaled(WL.get("resnet50"), [(64, 147), (128, 576), (256, 512),
+                                                        (512, 256), (10, 256)],
+                                   name="resnet50-ternary").replace(encoding="ternary"),
+                         None, 2),
+    "postvote_ternary": (WL.scaled(WL.get("postvote"), [(128, 128)] * 6 + [(256, 512)] * 2,
+                                   M=40, name="postvote-ternary").replace(encoding="ternary"),
+                         None, 2),
+    "prepost_ternary": (WL.scaled(WL.get("nanogpt_prepost"), [(192, 576), (768, 192)] * 2,
+                                  name="prepost-ternary").replace(encoding="ternary"), None, 2),
     # the post-vote step with float32 W and float32 products
     "postvote_f32": (WL.scaled(WL.get("postvote"), [(128, 128)] * 2 + [(256, 512)], M=12,
                                name="postvote-f32").replace(ns_precision="f32"), None, 2),
@@ -229,6 +279,10 @@ ODD = {
     "prepost_f32ns_M5": WL.scaled(WL.get("nanogpt_prepost"), ODD_TINY, M=5,
                                   name="odd-prepost").replace(ns_precision="f32"),
     "prepost_M5": WL.scaled(WL.get("nanogpt_prepost"), ODD_BF16, M=5, name="odd-prepost-bf16"),
+    "ternary_f32ns_M5": WL.scaled(WL.get("nanogpt"), ODD_TINY, M=5, name="odd-ternary")
+    .replace(ns_precision="f32", encoding="ternary"),
+    "ternary_M6": WL.scaled(WL.get("nanogpt"), ODD_BF16, M=6, name="odd-ternary-bf16")
+    .replace(encoding="ternary"),
 }
 
 
@@ -331,6 +385,8 @@ def test_step_zero_steps_K0(post_vote):
 # --------------------------------------------------------------------------
 def full_case(name, sample, bits_kind="random"):
     w = WL.get(name)
+    if w.encoding == "ternary":
+        bits_kind = "ternary"
     print(f"full-size step {name} d={w.d} M={w.M} sample={sample}", flush=True)
     hp = hparams(w)
     st = GpuState(w, hp)
@@ -339,6 +395,8 @@ def full_case(name, sample, bits_kind="random"):
     G0 = WL.gradient(w, 0, 0).astype(np.float64)
     if bits_kind == "ties":
         bits, _ = WL.planted_tie_bits(w)
+    elif bits_kind == "ternary":
+        bits = WL.random_ternary(w, w.M)
     else:
         bits = WL.random_bits(w, w.M)
     u0s = WL.power_start(w) if w.scale == "spectral" else None
@@ -351,6 +409,43 @@ def test_step_full_nanogpt():
 
 def test_step_full_resnet50():
     full_case("resnet50", sample=list(range(9)))
+
+
+def test_step_full_nanogpt_ternary():
+    full_case("nanogpt_ternary", sample=[0, 1, 2, 3, 46, 47])
+
+
+def test_step_ternary_diagonal_zeros_vote_nothing():
+    # diagonal momenta: every polar factor is exactly 0 off the diagonal;
+    # as int8 signs those zeros add nothing to the vote, which ties at 0 and
+    # leaves W bit for bit unchanged there (the packed bits would move it)
+    w = WL.scaled(WL.get("nanogpt_ternary"), [(256, 384), (384, 256)], M=3,
+                  name="ternary-diag").replace(lam=0.0)
+    hp = hparams(w)
+    st = GpuState(w, hp)
+    W = WL.init_weights(w)
+    Gs = []
+    rng = np.random.default_rng(5)
+    for m in range(w.M):
+        G = np.zeros(w.d, np.float32)
+        for (r, c), off in zip(w.mats, w.elem_offsets):
+            k = np.arange(min(r, c))
+            blk = np.zeros((r, c), np.float32)
+            blk[k, k] = rng.choice([-1.0, 1.0], k.size) * (1.0 + rng.random(k.size))
+            G[off:off + r * c] = blk.reshape(-1)
+        Gs.append(G.astype(np.float64))
+    o = oracle_hp(hp)
+    out = O.step(list(w.mats), W, [np.zeros(w.d)] * w.M, Gs, o, w.tie_value, 0, w.w_dtype,
+                 encoding="ternary")
+    Wg, Mg, bg, status = st.run(W, np.zeros(w.d, np.float32), Gs[0], out["signs"].copy(),
+                                None)
+    assert status == B.SM_OK
+    assert np.array_equal(bg, out["signs"])              # exact zeros, exact signs
+    assert np.array_equal(Wg.view(np.uint32), out["Wn"].view(np.uint32))
+    for (r, c), off in zip(w.mats, w.elem_offsets):
+        off_diag = ~np.eye(r, c, dtype=bool).reshape(-1)
+        sl = slice(off, off + r * c)
+        assert np.array_equal(Wg[sl][off_diag].view(np.uint32), W[sl][off_diag].view(np.uint32))
 
 
 def test_step_full_nanogpt_prepost():
@@ -373,60 +468,63 @@ def test_step_full_postvote():
 # worker, W unchanged by the worker calls, and the final W bit-exact wherever
 # every worker's bit equals the oracle's.
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["nanogpt", "postvote", "prepost"])
+@pytest.mark.parametrize("name", ["nanogpt", "postvote", "prepost", "nanogpt_ternary",
+                                  "postvote_ternary"])
 def test_all_workers_on_gpu(name, chain_mode):
     w, _, _ = SMALL[name]
-    if name == "postvote":
+    if name.startswith("postvote"):
         w = w.replace(M=12)
     print(f"all workers {name} mats={len(w.mats)} M={w.M}", flush=True)
     hp = hparams(w)
     o = oracle_hp(hp)
     st = GpuState(w, hp)
     mats = list(w.mats)
-    offs, woffs = w.elem_offsets, w.word_offsets
+    offs = w.elem_offsets
     M = w.M
     W = WL.init_weights(w)
     Moms = [0.05 * WL.init_momentum(w, m, std=1.0) for m in range(M)]
     Gs = gradients(w, 0, M)
     u0s = WL.power_start(w) if w.scale == "spectral" else None
     out = O.step(mats, W, Moms, Gs, o, w.tie_value, w.post_vote, w.w_dtype,
-                 None if u0s is None else [u.astype(np.float64) for u in u0s])
+                 None if u0s is None else [u.astype(np.float64) for u in u0s],
+                 encoding=w.encoding)
 
     W_t = torch.from_numpy(np.ascontiguousarray(W, np.float32)).cuda().to(st.wdt)
     W_in = W_t.clone()
     Mt = [torch.from_numpy(np.ascontiguousarray(np.float32(Moms[m]))).cuda() for m in range(M)]
     Gt = [torch.from_numpy(np.ascontiguousarray(Gs[m], np.float32)).cuda() for m in range(M)]
     rng = np.random.default_rng(7)
-    b_t = torch.from_numpy(rng.integers(0, 2**31, size=(M, st.words), dtype=np.int64)
-                           .astype(np.int32)).cuda()
+    # every buffer starts as garbage: the pipelines overwrite all of it
+    garbage = (rng.integers(-1, 2, size=(M, st.d), dtype=np.int8) if st.tern else
+               rng.integers(0, 2**31, size=(M, st.words), dtype=np.int64).astype(np.uint32))
+    b_t = st.to_dev(garbage)
     u_t = None if u0s is None else torch.from_numpy(np.concatenate(u0s).astype(np.float32)).cuda()
     for m in range(1, M):
-        st.plan.worker_pipeline(Gt[m], W_t, Mt[m], b_t, st.words, M, m, u0=u_t)
+        st.plan.worker_pipeline(Gt[m], W_t, Mt[m], b_t, st.stride, M, m, u0=u_t)
     torch.cuda.synchronize()
     assert st.plan.status() == B.SM_OK
     assert torch.equal(W_t.view(torch.int16) if st.wdt == torch.bfloat16 else W_t.view(torch.int32),
                        W_in.view(torch.int16) if st.wdt == torch.bfloat16 else W_in.view(torch.int32))
-    st.plan(Gt[0], W_t, Mt[0], b_t, st.words, M, 0, u0=u_t)
+    st.plan(Gt[0], W_t, Mt[0], b_t, st.stride, M, 0, u0=u_t)
     assert st.plan.status() == B.SM_OK
     torch.cuda.synchronize()
     Wg = W_t.float().cpu().numpy()
-    bg = b_t.cpu().numpy().view(np.uint32)
+    bg = st.from_dev(b_t)
     for m in range(M):
         tol = momentum_tol(np.float32(Moms[m]), Gs[m], W, o["beta"], o["lam"])
         assert np.all(np.abs(Mt[m].cpu().numpy().astype(np.float64) - out["Mom"][m]) <= tol), m
     checked = 0
     for i, (r, c) in enumerate(mats):
         n = r * c
-        wsl = slice(woffs[i], woffs[i] + (n + 31) // 32)
+        bsl = buf_slice(w, i)
         sl = slice(offs[i], offs[i] + n)
         for m in range(M):
-            gneg = unpack_neg(bg[m, wsl], n)
             ref = out["Mom"][m][offs[i]:offs[i] + n] if w.post_vote == 1 \
                 else out["U"][m][i].reshape(-1)
-            ok, stats = sign_gate(gneg, ref)
+            ok, stats = local_gate(w, bg[m, bsl], ref, n)
             assert ok, (m, i, stats)
         # the vote over the M GPU-written buffers and the update
-        check_after_vote(w, hp, W[sl], Wg[sl], bg[:, wsl], (r, c),
+        check_after_vote(w, hp, W[sl], Wg[sl], bg[:, bsl], (r, c),
                          None if u0s is None else u0s[i], i)
         checked += 1
     assert checked == len(mats)

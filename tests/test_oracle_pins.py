@@ -481,3 +481,85 @@ def test_step_post_vote_uses_majority_of_momentum_signs():
     Up, _ = O.polar_ns(want_D.reshape(4, 6).astype(np.float64), 5, 1e-7,
                        "spectral", 8)
     assert np.allclose(out["Upost"][0], Up, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# Ternary sign buffers (section 3: sign(0) = 0; Algorithm 2 and Figure 1: the
+# workers' signs summed as int8).  Diagonal momenta give polar factors that
+# are exactly zero off the diagonal: sent as ternary signs those entries add
+# nothing to the vote, which ties at 0 there and leaves W unchanged; sent as
+# packed bits the same zeros vote +1 and move W by -eta.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("post_vote", [0, 2])
+def test_step_ternary_diagonal_closed_form(post_vote):
+    r, c, M = 4, 7, 3
+    d = r * c
+    diag = np.zeros((r, c), bool)
+    diag[np.arange(r), np.arange(r)] = True
+    # worker m's gradient is diagonal with signs s[m] on the diagonal
+    s = np.array([[1, -1, 1, -1], [1, 1, -1, -1], [-1, -1, 1, 1]])
+    Gs = []
+    for m in range(M):
+        G = np.zeros((r, c))
+        G[np.arange(r), np.arange(r)] = s[m] * (1.0 + 0.25 * np.arange(r))
+        Gs.append(G.reshape(-1))
+    W = O.bf16_round_nearest_even(np.linspace(-0.05, 0.05, d).astype(np.float32))
+    hp = dict(HP, lam=0.0)
+    tern = O.step([(r, c)], W, [np.zeros(d)] * M, Gs, hp, 0, post_vote, "bf16",
+                  encoding="ternary")
+    pack = O.step([(r, c)], W, [np.zeros(d)] * M, Gs, hp, 0, post_vote, "bf16")
+    # every worker's polar factor is diagonal with the signs of its gradient
+    for m in range(M):
+        U = tern["U"][m][0]
+        assert np.all(U[~diag] == 0.0)
+        assert np.array_equal(np.sign(U[np.arange(r), np.arange(r)]), s[m])
+        assert np.array_equal(tern["signs"][m].reshape(r, c),
+                              np.where(diag, np.sign(Gs[m].reshape(r, c)), 0))
+    maj = np.sign(s.sum(axis=0))                       # M = 3: no ties
+    want_t = np.zeros((r, c), np.int64)
+    want_t[np.arange(r), np.arange(r)] = maj
+    assert np.array_equal(tern["D"].reshape(r, c), want_t)
+    want_p = np.ones((r, c), np.int64)                 # zeros travel as +1
+    want_p[np.arange(r), np.arange(r)] = maj
+    assert np.array_equal(pack["D"].reshape(r, c), want_p)
+    assert "bits" not in tern and "signs" not in pack
+    if post_vote == 0:
+        # off the diagonal the ternary step leaves W bit for bit unchanged
+        Wt = tern["Wn"].reshape(r, c)
+        assert np.array_equal(Wt[~diag].view(np.uint32), W.reshape(r, c)[~diag].view(np.uint32))
+        Wp = pack["Wn"].reshape(r, c)
+        want = O.bf16_round_nearest_even(
+            (W.reshape(r, c)[~diag] - np.float32(0.02)).astype(np.float32))
+        assert np.array_equal(Wp[~diag].view(np.uint32), want.view(np.uint32))
+    else:
+        # the majority is diagonal with r singular values 1: the Frobenius
+        # scale puts them at 1/sqrt(r), and K cubic steps map that through
+        # the scalar polynomial; off the diagonal the factor stays exactly 0
+        Up = tern["Upost"][0]
+        assert np.all(Up[~diag] == 0.0)
+        sig = 1.0 / (np.sqrt(r) + 1e-7)
+        for _ in range(5):
+            sig = 1.5 * sig - 0.5 * sig ** 3
+        assert np.allclose(Up[np.arange(r), np.arange(r)], maj * sig, rtol=1e-12, atol=0)
+        # packed: the +1 votes off the diagonal give a dense majority instead
+        assert np.all(pack["Upost"][0][~diag] != 0.0)
+
+
+def test_step_ternary_matches_packed_without_zeros():
+    # with no exact zeros the two encodings carry the same signs
+    rng = np.random.default_rng(19)
+    mats = [(6, 10), (9, 5)]
+    W, Gs, Moms = _set(rng, mats, 4)
+    a = O.step(mats, W, Moms, Gs, HP, 0, 0, "bf16")
+    b = O.step(mats, W, Moms, Gs, HP, 0, 0, "bf16", encoding="ternary")
+    assert np.array_equal(a["D"], b["D"])
+    assert np.array_equal(a["Wn"].view(np.uint32), b["Wn"].view(np.uint32))
+    offs = np.cumsum([0] + [r * c for r, c in mats])
+    woffs = np.cumsum([0] + [(r * c + 31) // 32 for r, c in mats])
+    for m in range(4):
+        for i, (r, c) in enumerate(mats):
+            t = b["signs"][m, offs[i]:offs[i + 1]]
+            assert np.all(t != 0)
+            assert np.array_equal(O.pack_signs(t), a["bits"][m, woffs[i]:woffs[i + 1]])
+    with pytest.raises(ValueError):
+        O.step(mats, W, Moms, Gs, HP, 0, 0, "bf16", encoding="int4")
