@@ -4,22 +4,24 @@
 Times the fused step (signmuon_step: momentum sweep, PolarNS by Newton-Schulz
 on the matrix cores, sign + 1-bit pack into the local worker's buffer, vote
 over the M resident packed buffers fused with the update of W) on a synthetic
-parameter set with all inputs resident in HBM.  Prints one JSON line with
-steps/s, a per-phase breakdown measured with HIP events recorded on the
-launch stream inside instrumented steps (the same work with the phases in
-sequence), the roofline of the dominant kernel (the Newton-Schulz GEMM) and
-the CPU oracle timed on a bounded sample.  `value` times plain steps, in
-which the momentum sweep, Newton-Schulz and vote of different matrix groups
-overlap on the library's internal streams.  An extra figure, `all_workers`,
-times steps in which all M workers' pipelines run on this GPU
-(signmuon_worker_pipeline for workers 1..M-1, then the step for worker 0).
+parameter set with all inputs resident in HBM, and prints one JSON line:
 
-`other_workloads` gives the plain steps/s and phase times of further sets
-(by default the ResNet-50-shaped one and the nanoGPT set with both polar
-steps, before the sign and after the vote).
+* `value`: steps/s of plain steps (the PolarNS work of different matrix
+  groups runs as concurrent chains on the plan's executor);
+* `phases_us` and the `ns_*` / `vote_*` / `momentum_*` rates: instrumented
+  steps with a HIP event after each phase, on the launch stream;
+* `roofline`: the dominant matrix-core kernel, timed per launch between HIP
+  events in sequential steps (no executor: each launch alone on the stream);
+* `other_workloads`: the same figures for the other parameter sets (the
+  ResNet-50-shaped set, the single 256x512 matrix, the LLM-MLP matrices with
+  the cubic and the quintic, the post-vote set with M = 200, and the nanoGPT
+  set with both polar steps, int8 ternary buffers and the normalized sign
+  step); `k_curve`: the main set at other Newton-Schulz step counts;
+* `all_workers`: steps in which all M workers' pipelines run on this GPU;
+* `cpu_baseline`: the CPU oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload nanogpt]
-                    [--also resnet50,nanogpt_prepost]
+                    [--also resnet50,...] [--k-curve 3,10]
 """
 from __future__ import annotations
 
@@ -76,7 +78,7 @@ def executed_ns_gflop(w) -> float:
     return tot * (3 if w.ns_precision == "bf16x3" else 1) / 1e9
 
 
-def gemm_traffic(workload):
+def gemm_traffic(workload):  # noqa: C901
     """HBM bytes of one step's Newton-Schulz GEMM launches from the committed
     counter summary, if it was taken on the current GEMM source; else None."""
     import hashlib
@@ -119,21 +121,47 @@ def describe(w):
     return (f"{w.name}: {parts}; W {w.w_dtype}, momentum f32; M={w.M} resident {enc} "
             f"sign buffers; K={w.K} {coeffs} Newton-Schulz ({ns}), {w.scale} scaling"
             + (f" P={w.P}" if w.scale == "spectral" else "")
-            + {0: "", 1: "; post-vote polar", 2: "; pre-sign and post-vote polar"}[int(w.post_vote)])
+            + {0: "", 1: "; post-vote polar", 2: "; pre-sign and post-vote polar",
+               3: "; normalized sign step D/||D||_2"}[int(w.post_vote)])
+
+
+def host_info():
+    """CPU model, thread count and NumPy's BLAS on this host."""
+    model = None
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except Exception:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        infos = threadpool_info()
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}"
+                                 for i in infos if i.get("user_api") == "blas"})) or None
+    except Exception:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "numpy_blas": blas}
 
 
 def cpu_baseline(w, budget_s):
-    """Oracle seconds per step on a bounded sample, scaled to the whole set."""
+    """Oracle seconds per step on a bounded sample, scaled to the whole set:
+    worker 0's momentum, float64 Newton-Schulz and sign packing, the vote over
+    M buffers and the apply for the first transformer layer's matrices, with
+    all BLAS threads; then one pass of the same sample on one thread."""
     import oracle as O
     from distributed_bit_matrix_amd import workloads as WL
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:   # threadpoolctl missing: report the visible CPUs
+        threadpool_limits = None
         cores = os.cpu_count()
-    # sample: the first 1/L of the matrices (one transformer layer for the
-    # nanoGPT set), worker 0's pipeline + vote over M + apply
-    per_layer = 4 if w.name == "nanogpt" else 1
+    per_layer = 4 if w.name.startswith("nanogpt") else 1
     n_layers = len(w.mats) // per_layer
     sub = WL.scaled(w, w.mats[:per_layer], name=w.name + "-sample")
     hp = dict(eta=w.eta, beta=w.beta, lam=w.lam, eps=w.eps, K=w.K, scale=w.scale,
@@ -143,9 +171,8 @@ def cpu_baseline(w, budget_s):
     G = WL.gradient(sub, 0, 0).astype(np.float64)
     others = WL.random_bits(sub, w.M)
     u0s = WL.power_start(sub) if w.scale == "spectral" else None
-    times = []
-    t_all = time.perf_counter()
-    while True:
+
+    def one_pass():
         t0 = time.perf_counter()
         Mn = O.momentum_update(Mom, G, W, hp["beta"], hp["lam"])
         bits = others.copy()
@@ -158,62 +185,79 @@ def cpu_baseline(w, budget_s):
             sums = O.vote_sums_from_bits(bits[:, woff:woff + (r * c + 31) // 32], r * c)
             D = O.majority_from_sums(sums, w.tie_value)
             O.apply_update(W[off:off + r * c], D, hp["eta"], w.w_dtype)
-        times.append(time.perf_counter() - t0)
+        return time.perf_counter() - t0
+
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        times.append(one_pass())
         if time.perf_counter() - t_all > budget_s or len(times) >= 5:
             break
     t_sample = float(np.median(times))
+    single = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t1 = one_pass()
+        single = {"value": 1.0 / (t1 * n_layers), "seconds_per_step": t1 * n_layers,
+                  "cores": 1}
     t_step = t_sample * n_layers
     return {"value": 1.0 / t_step, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
             "sample": (f"{per_layer} of {len(w.mats)} matrices ({sub.d} of {w.d} parameters), "
                        f"worker-0 momentum + float64 Newton-Schulz + pack, vote over M={w.M} "
                        f"and apply; median of {len(times)} runs = {t_sample:.3f} s, "
                        f"x{n_layers} for the whole set"),
-            "seconds_per_step": t_step}
+            "seconds_per_step": t_step, "single_thread": single, "host": host_info()}
 
 
 class Run:
-    """One workload on the GPU: its plan, resident inputs, and the timing of
-    K plain steps followed by K instrumented steps (phases in sequence, an
-    event after each phase)."""
+    """One workload on the GPU: its plans, resident inputs, and the timing of
+    K plain steps, K instrumented steps (phases in sequence, an event after
+    each phase; the Newton-Schulz chains run concurrently inside their phase)
+    and K sequential instrumented steps (no executor: every matrix-core launch
+    alone on the stream, an event after each)."""
 
-    def __init__(self, w, dev):
+    def __init__(self, w, dev, seed=0):
         import torch
         from distributed_bit_matrix_amd import binding as B
         from distributed_bit_matrix_amd import workloads as WL
         self.w = w
-        hp = B.HParams(eta=w.eta, beta=w.beta, lam=w.lam, eps=w.eps, K=w.K, scale=w.scale,
-                       P=w.P, coeffs=w.coeffs, precision=w.ns_precision,
-                       tie_value=w.tie_value, encoding=w.encoding)
-        layout, self.d, self.words = B.default_layout(w.mats)
-        self.plan = B.StepPlan(layout, hp, w.post_vote, device=dev)
+        self.hp = B.HParams(eta=w.eta, beta=w.beta, lam=w.lam, eps=w.eps, K=w.K,
+                            scale=w.scale, P=w.P, coeffs=w.coeffs, precision=w.ns_precision,
+                            tie_value=w.tie_value, encoding=w.encoding)
+        self.layout, self.d, self.words = B.default_layout(w.mats)
+        self.plan = B.StepPlan(self.layout, self.hp, w.post_vote, device=dev)
+        self.plan_seq = None
         wdt = torch.bfloat16 if w.w_dtype == "bf16" else torch.float32
         self.W = torch.from_numpy(WL.init_weights(w)).to(dev).to(wdt)
         self.Mom = torch.zeros(self.d, dtype=torch.float32, device=dev)
         self.G = torch.from_numpy(WL.gradient(w, 0, 0)).to(dev)
+        # the other workers' buffers: seeded random signs generated on the
+        # device (their values do not change the time)
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed + 1000 * seed)
         if w.encoding == "ternary":
             # int8 sign buffers: d bytes per worker, matrices at their offsets
-            self.bits = torch.from_numpy(WL.random_ternary(w, w.M)).to(dev)
+            self.bits = torch.randint(-1, 2, (w.M, self.d), dtype=torch.int8, device=dev,
+                                      generator=g)
             self.words = self.d
         else:
-            self.bits = torch.from_numpy(WL.random_bits(w, w.M).view(np.int32)).to(dev)
+            self.bits = torch.randint(-2 ** 31, 2 ** 31 - 1, (w.M, self.words),
+                                      dtype=torch.int32, device=dev, generator=g)
         self.u0 = (torch.from_numpy(np.concatenate(WL.power_start(w))).to(dev)
                    if w.scale == "spectral" else None)
+        self.dev = dev
         torch.cuda.synchronize()
 
     def step(self):
         self.plan(self.G, self.W, self.Mom, self.bits, self.words, self.w.M, 0, u0=self.u0)
 
-    def measure(self, K, warmup):
-        """Returns (seconds for K plain steps, mean per-phase microseconds)."""
+    def _profiled(self, plan, K):
+        """K instrumented steps on `plan`: per-phase and per-kind durations
+        (microseconds per step) and per-launch durations by kind."""
         import torch
         from distributed_bit_matrix_amd import binding as B
-        for _ in range(warmup):
-            self.step()
-        torch.cuda.synchronize()
-
-        # events for the instrumented steps
         hip = hip_runtime()
-        cap = 64
+        cap = 128
         evs = (ctypes.c_void_p * (cap * K))()
         ev_list = []
         for i in range(cap * K):
@@ -233,40 +277,117 @@ class Run:
             p.capacity = cap
             p.count = 0
             profs.append(p)
-
-        # timed region: K production steps (the whole step runs as concurrent
-        # chains on the library's streams), bracketed by device synchronization
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for k in range(K):
-            self.step()
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-
-        # K instrumented steps for the phase breakdown: the same work with the
-        # phases in sequence and an event after each (Newton-Schulz chains
-        # only inside the polar phase)
         torch.cuda.synchronize()
         w = self.w
         for k in range(K):
-            self.plan.profiled(profs[k], self.G, self.W, self.Mom, self.bits, self.words,
-                               w.M, 0, u0=self.u0)
+            plan.profiled(profs[k], self.G, self.W, self.Mom, self.bits, self.words, w.M, 0,
+                          u0=self.u0)
         torch.cuda.synchronize()
-
-        # per-phase durations from consecutive events of each step
-        phase = {}
+        phase, launches = {}, {}
         ms = ctypes.c_float()
         for k in range(K):
             p = profs[k]
+            if p.count >= cap:
+                raise RuntimeError("profile capacity too small")
             base = k * cap
             for i in range(1, p.count):
                 hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(evs[base + i - 1]),
                                         ctypes.c_void_p(evs[base + i]))
                 name = B.PHASES[kinds[base + i]]
                 phase[name] = phase.get(name, 0.0) + ms.value * 1e3
+                launches.setdefault(name, []).append(ms.value * 1e3)
         for e in ev_list:
             hip.hipEventDestroy(ctypes.c_void_p(e))
-        return elapsed, {k: v / K for k, v in phase.items()}
+        return {k: v / K for k, v in phase.items()}, launches
+
+    def measure(self, K, warmup):
+        """Returns (seconds for K plain steps, mean per-phase microseconds of
+        the instrumented steps)."""
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        # timed region: K production steps (the PolarNS work runs as
+        # concurrent chains on the plan's executor), bracketed by device
+        # synchronization
+        t0 = time.perf_counter()
+        for k in range(K):
+            self.step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        phase, _ = self._profiled(self.plan, K)
+        return elapsed, phase
+
+    def measure_launches(self, K):
+        """K sequential instrumented steps: mean microseconds per launch of
+        each matrix-core kernel kind (gram, square, update) and per step."""
+        from distributed_bit_matrix_amd import binding as B
+        if self.plan_seq is None:
+            self.plan_seq = B.StepPlan(self.layout, self.hp, self.w.post_vote, device=self.dev,
+                                       concurrent=False)
+        self._profiled(self.plan_seq, 1)          # warm-up
+        phase, launches = self._profiled(self.plan_seq, K)
+        per_launch = {k: float(np.mean(v)) for k, v in launches.items()}
+        counts = {k: len(v) // K for k, v in launches.items()}
+        return phase, per_launch, counts
+
+
+def launch_flops(w):
+    """Executed MFMA flops of one launch of each matrix-core kernel kind over
+    the whole set (operands padded to multiples of 128; symmetric outputs on
+    their upper-triangular 128x128 tiles; three MFMAs per product in
+    split-bfloat16), for the launches the sequential step makes."""
+    r128 = lambda x: (x + 127) // 128 * 128  # noqa: E731
+    mul = 3 if w.ns_precision == "bf16x3" else 1
+    gram = square = update = 0.0
+    for r, c in w.mats:
+        Rp, Np = r128(min(r, c)), r128(max(r, c))
+        T = Rp // 128
+        sym = T * (T + 1) // 2 * 2.0 * 128 * 128
+        gram += sym * Np
+        square += sym * Rp
+        update += 2.0 * Rp * Rp * Np
+    return {"gram": gram * mul, "square": square * mul, "update": update * mul}
+
+
+def workload_metrics(w, d, elapsed, K, phase_us):
+    """Steps/s, the Newton-Schulz phase as algorithmic and executed TFLOP/s
+    against the matrix-core peak, and vote / momentum GB/s against HBM."""
+    peak = PEAK_F32_TFLOPS if w.ns_precision == "f32" else PEAK_BF16_TFLOPS
+    gemm_us = phase_us.get("gemm", 0.0) + phase_us.get("gram", 0.0) + \
+        phase_us.get("square", 0.0) + phase_us.get("update", 0.0)
+    wbytes = 2 if w.w_dtype == "bf16" else 4
+    sign_bytes = 1.0 if w.encoding == "ternary" else 1 / 8.0
+    out = {"value": round(K / elapsed, 3), "unit": "steps/s",
+           "ms_per_step": round(elapsed / K * 1e3, 4), "config": describe(w), "params": d,
+           "phases_us": {k: round(v, 2) for k, v in phase_us.items()}}
+    if gemm_us > 0 and w.K > 0:
+        alg = w.ns_gflop() * 1e9 / (gemm_us * 1e-6) / 1e12
+        exe = executed_ns_gflop(w) * 1e9 / (gemm_us * 1e-6) / 1e12
+        if w.post_vote == 2:      # two Newton-Schulz passes per step
+            alg, exe = 2 * alg, 2 * exe
+        out.update({"ns_phase_us": round(gemm_us, 2), "ns_form": ns_form(w),
+                    "ns_algorithmic_tflops": round(alg, 1),
+                    "ns_algorithmic_frac": round(alg / peak, 4),
+                    "ns_executed_tflops": round(exe, 1),
+                    "ns_mfma_util_pct": round(100 * exe / peak, 2)})
+    if w.post_vote == 0 and phase_us.get("vote"):
+        vb = (w.M * sign_bytes + 2 * wbytes) * d
+        out["vote_apply_gbps"] = round(vb / (phase_us["vote"] * 1e-6) / 1e9, 1)
+        out["vote_apply_frac_hbm"] = round(vb / (phase_us["vote"] * 1e-6) / 1e9 /
+                                           PEAK_HBM_GBPS, 4)
+    elif phase_us.get("vote"):
+        # majority matrix written into the bfloat16 operand copy
+        vb = (w.M * sign_bytes + 2) * d
+        out["vote_gbps"] = round(vb / (phase_us["vote"] * 1e-6) / 1e9, 1)
+        out["vote_frac_hbm"] = round(vb / (phase_us["vote"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
+    if phase_us.get("momentum"):
+        mb = (4 + wbytes + 4 + 4 + (0 if w.post_vote == 1 else 2)) * d + \
+            (sign_bytes * d if w.post_vote == 1 else 0)
+        out["momentum_gbps"] = round(mb / (phase_us["momentum"] * 1e-6) / 1e9, 1)
+        out["momentum_frac_hbm"] = round(mb / (phase_us["momentum"] * 1e-6) / 1e9 /
+                                         PEAK_HBM_GBPS, 4)
+    return out
 
 
 def main():
@@ -280,10 +401,14 @@ def main():
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--rb-steps", type=int, default=5,
                     help="timed steps of the all-workers figure (every worker's pipeline "
-                         "inside the step)")
-    ap.add_argument("--also", default="resnet50,nanogpt_prepost,nanogpt_ternary",
-                    help="comma-separated further workloads whose plain steps/s and phase "
-                         "times are reported under other_workloads ('' = none)")
+                         "inside the step; 0 = skip)")
+    ap.add_argument("--also", default=("resnet50,single,llm_mlp,llm_mlp_quintic,postvote,"
+                                       "nanogpt_prepost,nanogpt_ternary,nanogpt_normalized"),
+                    help="comma-separated further workloads whose steps/s, phase times and "
+                         "rates are reported under other_workloads ('' = none)")
+    ap.add_argument("--k-curve", default="3,10",
+                    help="Newton-Schulz step counts K at which the main workload is also "
+                         "timed ('' = none)")
     ap.add_argument("--ternary", type=int, default=1,
                     help="also time the int8 ternary vote on the set's size (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -313,28 +438,43 @@ def main():
     run = Run(w, dev)
     K = args.steps
     elapsed, phase_us = run.measure(K, args.warmup)
+    main_metrics = workload_metrics(w, run.d, elapsed, K, phase_us)
+    # Roofline of the dominant kernel: the matrix-core launches of K
+    # sequential instrumented steps (no executor), each timed alone between
+    # HIP events on its stream.  In the Gram-space form the symmetric
+    # Rp x Rp products take most of the Newton-Schulz time.
+    seq_phase, per_launch, counts = run.measure_launches(K)
+    lf = launch_flops(w)
+    kinds = [k for k in ("gram", "square", "update") if k in per_launch]
+    dom = max(kinds, key=lambda k: per_launch[k] * counts[k])
+    peak = PEAK_F32_TFLOPS if w.ns_precision == "f32" else PEAK_BF16_TFLOPS
+    achieved = lf[dom] / (per_launch[dom] * 1e-6) / 1e12
+    names = {"gram": "k_gemm Gram S S^T (E_OP)",
+             "square": "k_gemm symmetric Rp x Rp product (E_SQUARE)",
+             "update": "k_gemm update / final product (E_UPDATE)"}
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": gemm_traffic(w.name), "traffic_unit": "bytes per step",
+                "kernel": names[dom] + f": one launch covers all {len(w.mats)} matrices",
+                "work_per_launch_gflop": round(lf[dom] / 1e9, 3),
+                "work": {"square": "2 Rp^3 flops per matrix (Rp = the short side padded "
+                                   "to 128) on the upper-triangular 128x128 tiles of the "
+                                   "symmetric output",
+                         "gram": "2 Rp^2 Np flops per matrix on the upper-triangular tiles "
+                                 "of the symmetric Gram",
+                         "update": "2 Rp^2 Np flops per matrix"}[dom]
+                        + (" (x3 MFMAs in split-bfloat16)" if w.ns_precision == "bf16x3" else ""),
+                "avg_launch_us": round(per_launch[dom], 2), "launches_per_step": counts[dom],
+                "timed_launches": counts[dom] * K,
+                "per_kind": {k: {"avg_launch_us": round(per_launch[k], 2),
+                                 "launches_per_step": counts[k],
+                                 "tflops": round(lf[k] / (per_launch[k] * 1e-6) / 1e12, 1),
+                                 "frac": round(lf[k] / (per_launch[k] * 1e-6) / 1e12 / peak, 4)}
+                             for k in kinds},
+                "sequential_step_phases_us": {k: round(v, 2) for k, v in seq_phase.items()}}
     d, words, plan = run.d, run.words, run.plan
     G, W, bits, u0 = run.G, run.W, run.bits, run.u0
     step = run.step
-    # The Newton-Schulz GEMM launches of a step run as concurrent chains on
-    # the library's internal streams; the "gemm" phase is the span from the
-    # fork to the join on the launching stream (pre-scale included).
-    gemm_us = phase_us.get("gemm", float("nan"))
-    quintic = w.coeffs[2] != 0.0
-    # GEMM launches per chain and step: iterate form K Grams + K updates
-    # (+ K squares for the quintic); Gram space one Gram, 3K - 3 symmetric
-    # products and the final product
-    gemm_per_step = 3 * w.K - 1 if ns_form(w) == "gram_space" else w.K * (3 if quintic else 2)
-
-    ns_flop = w.ns_gflop() * 1e9
-    ns_tflops = ns_flop / (gemm_us * 1e-6) / 1e12
-    exec_tflops = executed_ns_gflop(w) * 1e9 / (gemm_us * 1e-6) / 1e12
-    peak = PEAK_F32_TFLOPS if w.ns_precision == "f32" else PEAK_BF16_TFLOPS
-    wbytes = 2 if w.w_dtype == "bf16" else 4
-    vote_bytes = (w.M / 8.0 + 2 * wbytes) * d
-    vote_gbps = vote_bytes / (phase_us.get("vote", float("nan")) * 1e-6) / 1e9
-    mom_bytes = (4 + wbytes + 4 + 4 + 2) * d
-    mom_gbps = mom_bytes / (phase_us.get("momentum", float("nan")) * 1e-6) / 1e9
 
     # An extra figure: every worker's pipeline inside the step.
     # Workers 1..M-1 run signmuon_worker_pipeline into their buffers with
@@ -343,41 +483,33 @@ def main():
     # over the M fresh buffers and the apply).
     # (At most 8 momentum buffers are kept and reused in turn: the work per
     # worker is the same, and 200 workers' momenta would not fit in HBM.)
-    rb_steps = max(1, min(args.rb_steps, K))
-    n_mom = min(w.M - 1, 8)
-    Moms_b = [torch.zeros(d, dtype=torch.float32, device=dev) for _ in range(n_mom)]
+    all_workers = None
+    if args.rb_steps > 0:
+        rb_steps = min(args.rb_steps, K)
+        n_mom = min(w.M - 1, 8)
+        Moms_b = [torch.zeros(d, dtype=torch.float32, device=dev) for _ in range(n_mom)]
 
-    def step_all_workers():
-        for m in range(1, w.M):
-            plan.worker_pipeline(G, W, Moms_b[(m - 1) % n_mom], bits, words, w.M, m, u0=u0)
-        step()
+        def step_all_workers():
+            for m in range(1, w.M):
+                plan.worker_pipeline(G, W, Moms_b[(m - 1) % n_mom], bits, words, w.M, m, u0=u0)
+            step()
 
-    step_all_workers()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(rb_steps):
         step_all_workers()
-    torch.cuda.synchronize()
-    rb_elapsed = time.perf_counter() - t0
-    del Moms_b
-
-    # Further workloads (by default the ResNet-50-shaped set and the nanoGPT
-    # set with both polar steps): plain steps/s
-    # and the instrumented phase times, same method as above.
-    others = {}
-    for name in [n for n in args.also.split(",") if n and n != w.name]:
-        wo = WL.get(name)
-        ro = Run(wo, dev)
-        el, ph = ro.measure(K, args.warmup)
-        others[name] = {"value": round(K / el, 3), "unit": "steps/s",
-                        "ms_per_step": round(el / K * 1e3, 4), "config": describe(wo),
-                        "params": ro.d,
-                        "phases_us": {k: round(v, 2) for k, v in ph.items()}}
-        del ro
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(rb_steps):
+            step_all_workers()
+        torch.cuda.synchronize()
+        rb_elapsed = time.perf_counter() - t0
+        del Moms_b
+        all_workers = {"value": round(rb_steps / rb_elapsed, 3), "unit": "steps/s",
+                       "steps": rb_steps, "ms_per_step": round(rb_elapsed / rb_steps * 1e3, 3),
+                       "what": f"all {w.M} workers' momentum + PolarNS + pack on this GPU, "
+                               "then the vote over the M buffers and the apply",
+                       "momentum_buffers": n_mom + 1}
 
-    # The int8 ternary vote (separate entry point, not part of the step) on
-    # the same set's size: M int8 buffers read, int8 D written.
+    # The int8 ternary vote (separate entry point) on the same set's size:
+    # M int8 buffers read, int8 D written.
     tern = None
     if args.ternary:
         from distributed_bit_matrix_amd import binding as B
@@ -401,6 +533,30 @@ def main():
                 "what": f"signmuon_majority_vote_ternary over M={M_t} int8 buffers of "
                         f"{d_t} entries (reads M d bytes, writes d)"}
         del S_t, D_t
+    del run, plan, G, W, bits, u0, step
+    torch.cuda.empty_cache()
+
+    # Further workloads: the same plain and instrumented timing
+    others = {}
+    for name in [n for n in args.also.split(",") if n and n != w.name]:
+        wo = WL.get(name)
+        ro = Run(wo, dev)
+        el, ph = ro.measure(K, args.warmup)
+        others[name] = workload_metrics(wo, ro.d, el, K, ph)
+        del ro
+        torch.cuda.empty_cache()
+
+    # Newton-Schulz step count: the main workload at other K
+    k_curve = {str(w.K): {"value": main_metrics["value"],
+                          "ns_phase_us": main_metrics.get("ns_phase_us")}}
+    for k in [int(x) for x in args.k_curve.split(",") if x]:
+        wk = w.replace(K=k)
+        rk = Run(wk, dev)
+        el, ph = rk.measure(K, args.warmup)
+        mk = workload_metrics(wk, rk.d, el, K, ph)
+        k_curve[str(k)] = {"value": mk["value"], "ns_phase_us": mk.get("ns_phase_us")}
+        del rk
+        torch.cuda.empty_cache()
 
     steps_per_s = K / elapsed
     out = {
@@ -419,33 +575,24 @@ def main():
         "config": {"workload": describe(w), "params": d, "matrices": len(w.mats),
                    "workers": w.M, "reading": "local worker pipeline + vote over M "
                    "resident buffers + apply"},
-        "roofline": {"bound": "mfma", "achieved": round(ns_tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(ns_tflops / peak, 4),
-                     "traffic": gemm_traffic(w.name), "traffic_unit": "bytes per step",
-                     "kernel": "k_gemm: the step's Newton-Schulz GEMM launches, timed as one phase",
-                     "work": "algorithmic: 4 m^2 n flops per Newton-Schulz step and matrix, the "
-                             "pages' iteration; see ns_executed_tflops for the MFMA flops the "
-                             "chosen form executes",
-                     "ns_form": ns_form(w),
-                     "gemm_phases_per_step": gemm_per_step,
-                     "ns_phase_us": round(gemm_us, 2)},
-        # MFMA utilisation: the MFMA flops actually executed (the chosen form,
-        # symmetric outputs on their upper-triangular tiles, padded operands)
-        # over the phase time, against the peak
-        "ns_mfma_util_pct": round(100 * exec_tflops / peak, 2),
-        "ns_executed_tflops": round(exec_tflops, 2),
-        # the pages' iteration's flops over the same time (the roofline above)
-        "ns_algorithmic_pct_of_peak": round(100 * ns_tflops / peak, 2),
-        "vote_gbps": round(vote_bytes / (phase_us.get("vote", float("nan")) * 1e-6) / 1e9, 1),
-        "vote_frac_hbm": round(vote_gbps / PEAK_HBM_GBPS, 4),
-        "momentum_gbps": round(mom_gbps, 1),
+        "roofline": roofline,
+        # the Newton-Schulz phase of the plain step's instrumented twin (the
+        # chains run concurrently inside it): the pages' iteration's flops and
+        # the MFMA flops the chosen form executes, over the phase time
+        "ns_phase_us": main_metrics.get("ns_phase_us"),
+        "ns_form": main_metrics.get("ns_form"),
+        "ns_mfma_util_pct": main_metrics.get("ns_mfma_util_pct"),
+        "ns_executed_tflops": main_metrics.get("ns_executed_tflops"),
+        "ns_algorithmic_tflops": main_metrics.get("ns_algorithmic_tflops"),
+        "ns_algorithmic_pct_of_peak": round(100 * main_metrics.get("ns_algorithmic_frac", 0), 2),
+        "vote_gbps": main_metrics.get("vote_apply_gbps"),
+        "vote_frac_hbm": main_metrics.get("vote_apply_frac_hbm"),
+        "momentum_gbps": main_metrics.get("momentum_gbps"),
+        "momentum_frac_hbm": main_metrics.get("momentum_frac_hbm"),
         "phases_us": {k: round(v, 2) for k, v in phase_us.items()},
         "instrumented_us_per_step": round(sum(phase_us.values()), 2),
-        "all_workers": {"value": round(rb_steps / rb_elapsed, 3), "unit": "steps/s",
-                      "steps": rb_steps, "ms_per_step": round(rb_elapsed / rb_steps * 1e3, 3),
-                      "what": f"all {w.M} workers' momentum + PolarNS + pack on this GPU, "
-                              "then the vote over the M buffers and the apply",
-                      "momentum_buffers": n_mom + 1},
+        "all_workers": all_workers,
+        "k_curve": k_curve,
         "other_workloads": others,
         "ternary_vote": tern,
     }

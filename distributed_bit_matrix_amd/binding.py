@@ -35,7 +35,8 @@ EXPORTS = (
     "signmuon_executor_create", "signmuon_executor_destroy", "signmuon_reset_status",
     "signmuon_polar_ns_static",
 )
-PHASES = {0: "start", 1: "momentum", 2: "prescale", 3: "gemm", 4: "pack", 5: "vote"}
+PHASES = {0: "start", 1: "momentum", 2: "prescale", 3: "gemm", 4: "pack", 5: "vote",
+          6: "gram", 7: "square", 8: "update"}
 
 
 class SignMuonError(RuntimeError):

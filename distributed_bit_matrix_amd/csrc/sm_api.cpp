@@ -66,7 +66,7 @@ bool gram_space_enabled() {
 
 // Per-matrix placement.  Returns SM_OK or SM_EINVAL for unusable shapes.
 sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
-                     bool post_vote, bool need_u, Plan& P,
+                     int post_vote, bool need_u, Plan& P,
                      std::vector<MatPlan>& mp) {
   mp.assign(nm, MatPlan{});
   P = Plan{};
@@ -139,16 +139,18 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
       if (split) P.off_a[1] = take(r2 * opb);
     }
   }
-  if (P.spectral) {
+  // the normalized sign step (post_vote 3) estimates ||D||_2 by power
+  // iteration on the raw Gram of the majority matrix, whatever the scale
+  const bool power = P.spectral || post_vote == 3;
+  if (power) {
     P.off_araw = take(r2 * 4);
     P.off_vec = take(2 * v * 4);
   }
   P.off_part = take(c * 4);
-  if ((ns || P.spectral) && kp > 0) P.off_kpart = take(kp * 4);
+  if ((ns || power) && kp > 0) P.off_kpart = take(kp * 4);
   if (P.gram_space) P.off_gs = take(5 * r2 * 2);
   P.off_scal = take((size_t)nm * 4);
   if (need_u) P.off_u = take(umax * 4);
-  (void)post_vote;
   P.total = off;
   return SM_OK;
 }
@@ -426,7 +428,7 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
         }
         return launch_gemm(prec, a, s);
       }));
-      HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+      HIP_TRY(mark(io.prof, SM_PHASE_GRAM, s));
       return SM_OK;
     });
     return;
@@ -441,7 +443,7 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
       a.kpart = B.kpart;
       return launch_gemm(prec, a, s);
     }));
-    HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+    HIP_TRY(mark(io.prof, SM_PHASE_GRAM, s));
     return SM_OK;
   });
   // power iteration: P >= 1 steps alternating va / vb (P is validated); the
@@ -560,7 +562,7 @@ void gram_space_stages(const Plan& P, const std::vector<MatPlan>& mp,
         a.o_hi = O;
         return launch_gemm(prec, a, s);
       }));
-      HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+      HIP_TRY(mark(io.prof, SM_PHASE_SQUARE, s));
       return SM_OK;
     });
   };
@@ -615,7 +617,7 @@ void gram_space_stages(const Plan& P, const std::vector<MatPlan>& mp,
         }
         return launch_gemm(prec, a, s);
       }, &launched));
-      if (launched) HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+      if (launched) HIP_TRY(mark(io.prof, SM_PHASE_UPDATE, s));
     }
     return SM_OK;
   });
@@ -655,14 +657,14 @@ void ns_stages(const Plan& P, const std::vector<MatPlan>& mp,
           a.o_lo = P.quintic ? B.a[1] : B.b[1];
           return launch_gemm(prec, a, s);
         }));
-        HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+        HIP_TRY(mark(io.prof, SM_PHASE_GRAM, s));
         return SM_OK;
       });
     }
     if (P.quintic) {
       out.push_back([&, hp, s]() -> sm_status {
         HIP_TRY(run_square(P, mp, groups, hp, B, s));
-        HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+        HIP_TRY(mark(io.prof, SM_PHASE_SQUARE, s));
         return SM_OK;
       });
     }
@@ -705,7 +707,7 @@ void ns_stages(const Plan& P, const std::vector<MatPlan>& mp,
           }
           return launch_gemm(prec, a, s);
         }, &launched));
-        if (launched) HIP_TRY(mark(io.prof, SM_PHASE_GEMM, s));
+        if (launched) HIP_TRY(mark(io.prof, SM_PHASE_UPDATE, s));
       }
       return SM_OK;
     });
@@ -983,7 +985,7 @@ size_t signmuon_polar_ns_workspace(int64_t rows, int64_t cols, const sm_hparams*
   sm_matrix m{rows, cols, 0, 0};
   Plan P;
   std::vector<MatPlan> mp;
-  if (build_plan(&m, 1, hp, false, false, P, mp) != SM_OK) return 0;
+  if (build_plan(&m, 1, hp, 0, false, P, mp) != SM_OK) return 0;
   return P.total;
 }
 
@@ -996,7 +998,7 @@ sm_status signmuon_polar_ns(const float* X, float* U, int64_t rows, int64_t cols
   sm_matrix m{rows, cols, 0, 0};
   Plan P;
   std::vector<MatPlan> mp;
-  st = build_plan(&m, 1, hp, false, false, P, mp);
+  st = build_plan(&m, 1, hp, 0, false, P, mp);
   if (st != SM_OK) return st;
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < P.total)
     return SM_EWORKSPACE;
@@ -1084,7 +1086,8 @@ size_t signmuon_step_workspace(const sm_matrix* mats, int32_t n_mats,
                                const sm_hparams* hp, int32_t post_vote) {
   if (!mats || n_mats < 1 || n_mats > 65536) return 0;
   if (check_hparams(hp, true) != SM_OK) return 0;
-  if (post_vote < 0 || post_vote > 2) return 0;
+  if (post_vote < 0 || post_vote > 3) return 0;
+  if (post_vote == 3 && (hp->P < 1 || hp->P > 256)) return 0;
   bool need_u = false;
   for (int i = 0; i < n_mats; ++i)
     if (post_vote != 1 && hp->K > 0 && mats[i].cols % 32 != 0 &&
@@ -1092,7 +1095,7 @@ size_t signmuon_step_workspace(const sm_matrix* mats, int32_t n_mats,
       need_u = true;
   Plan P;
   std::vector<MatPlan> mp;
-  if (build_plan(mats, n_mats, hp, post_vote != 0, need_u, P, mp) != SM_OK) return 0;
+  if (build_plan(mats, n_mats, hp, post_vote, need_u, P, mp) != SM_OK) return 0;
   return P.total;
 }
 
@@ -1114,7 +1117,8 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   if (st != SM_OK) return st;
   if (M < 1 || M > SM_MAX_WORKERS) return SM_ERANGE;
   if (local_worker < 0 || local_worker >= M) return SM_EINVAL;
-  if (post_vote < 0 || post_vote > 2) return SM_EINVAL;
+  if (post_vote < 0 || post_vote > 3) return SM_EINVAL;
+  if (post_vote == 3 && (hp->P < 1 || hp->P > 256)) return SM_EINVAL;
   if (w_dtype != SM_F32 && w_dtype != SM_BF16) return SM_EINVAL;
   if (!G || !W || !Mom || !bits) return SM_EINVAL;
   if (worker_stride_words < 0) return SM_EINVAL;
@@ -1150,7 +1154,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   }
   Plan P;
   std::vector<MatPlan> mp;
-  st = build_plan(mats, n_mats, hp, post_vote != 0, need_u, P, mp);
+  st = build_plan(mats, n_mats, hp, post_vote, need_u, P, mp);
   if (st != SM_OK) return st;
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < P.total)
     return SM_EWORKSPACE;
@@ -1196,9 +1200,9 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
     return true;
   };
 
-  // post_vote 0 and 2: the local worker's pre-sign pipeline (momentum,
-  // PolarNS, packed signs); 0 then votes and applies the majority, 2 goes on
-  // to the post-vote polar step below.
+  // post_vote 0, 2 and 3: the local worker's pre-sign pipeline (momentum,
+  // PolarNS, signs); 0 then votes and applies the majority, 2 goes on to the
+  // post-vote polar step below, 3 to the normalized sign step.
   if (post_vote != 1) {
     if (hp->K == 0) {
       // U = Mom/(s+eps) has the signs of Mom: pack them directly.
@@ -1305,9 +1309,11 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
     if (pipeline_only) return SM_OK;
   }
 
-  // ---- post_vote 1 and 2: majority matrix, its polar factor, the update.
-  // (The pre-sign pass of post_vote 2 has finished with the operand and
-  // partial-sum buffers on this stream before the vote rewrites them.)
+  // ---- post_vote 1 and 2: majority matrix, its polar factor, the update;
+  // post_vote 3: majority matrix D, ||D||_2 by power iteration, and
+  // W <- W - eta D / (||D||_2 + eps).
+  // (The pre-sign pass of post_vote 2 and 3 has finished with the operand
+  // and partial-sum buffers on this stream before the vote rewrites them.)
   // padding of the operand copy (only matrices with a ragged shape)
   HIP_TRY(for_launches(groups, [&](Group& g) {
     const MatPlan& q = mp[g.idx0];
@@ -1326,12 +1332,23 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   HIP_TRY(mark(prof, SM_PHASE_VOTE, stream));
   io.first_xsrc = XS_OP; io.src_user = nullptr;
   io.final_out = O_APPLY;
-  if (hp->K > 0) {
+  if (post_vote != 3 && hp->K > 0) {
     std::vector<bool> fus_all(n_mats, true);
     return run_polar(P, mp, groups, fus_all, hp, B, io, tern ? 2 : 1, stream, ex,
                      post_vote == 2 ? 1 : 0);
   }
-  st = run_pre_scale(P, mp, groups, hp, B, io, tern ? 2 : 1, stream);
+  // W <- W - eta c S with c = 1/(s + eps): the post-vote step with K = 0, or
+  // the normalized sign step (a spectral pre-scale without Newton-Schulz
+  // steps on the majority matrix, whose power vectors the plan holds)
+  Plan Pn = P;
+  sm_hparams hn = *hp;
+  if (post_vote == 3) {
+    Pn.spectral = true;
+    Pn.gram_space = false;
+    hn.scale = SM_SCALE_SPECTRAL;
+    hn.K = 0;
+  }
+  st = run_pre_scale(Pn, mp, groups, &hn, B, io, tern ? 2 : 1, stream);
   if (st != SM_OK) return st;
   {
     ScaledOutArgs so;

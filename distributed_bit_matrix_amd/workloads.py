@@ -17,11 +17,13 @@ gradients stand in for them):
 * ``nanogpt``  12 transformer layers x {qkv 768x2304, attn-out 768x768,
   fc 768x3072, proj 3072x768}, bf16 weights, M = 8, Frobenius scaling.
 * ``llm_mlp``  4096x4096 and 4096x16384 bf16, M = 16, spectral P = 10,
-  gradients with a rank-16 signal; cubic and quintic coefficients.
+  gradients with a rank-16 signal, cubic coefficients; ``llm_mlp_quintic``
+  the same with the quintic coefficients in split-bfloat16.
 * ``postvote`` 512 x (128x128) + 64 x (1024x4096) float32, M = 200, the
   post-vote polar variant with spectral P = 8 and correlated worker noise.
 * ``nanogpt_ternary`` the nanoGPT set with int8 ternary sign buffers;
-  ``nanogpt_prepost`` the nanoGPT set with both polar steps.
+  ``nanogpt_prepost`` the nanoGPT set with both polar steps;
+  ``nanogpt_normalized`` the nanoGPT set with the normalized sign step.
 """
 from __future__ import annotations
 
@@ -53,7 +55,8 @@ class Workload:
     tie_value: int
     T: int
     warmup: int
-    post_vote: int          # 0: Algorithm 2; 1: polar after the vote; 2: both
+    post_vote: int          # 0: Algorithm 2; 1: polar after the vote; 2: both;
+                            # 3: the spectral-norm normalized sign step
     signal_std: float       # std of the shared signal S
     seed_index: int
     encoding: str = "packed"   # worker sign buffers: "packed" | "ternary" (int8)
@@ -129,6 +132,13 @@ WORKLOADS = {
         name="llm_mlp", mats=((4096, 4096), (4096, 16384)), w_dtype="bf16", M=16,
         scale="spectral", P=10, ns_precision="bf16", T=5, warmup=2,
         post_vote=False, signal_std=0.0, seed_index=3, **_COMMON),
+    # The same matrices with the quintic coefficients, in split-bfloat16 (the
+    # precision in which the quintic meets the sign gate).
+    "llm_mlp_quintic": Workload(
+        name="llm_mlp_quintic", mats=((4096, 4096), (4096, 16384)), w_dtype="bf16", M=16,
+        scale="spectral", P=10, ns_precision="bf16x3", T=5, warmup=2,
+        post_vote=False, signal_std=0.0, seed_index=3,
+        **dict(_COMMON, coeffs=QUINTIC)),
     "postvote": Workload(
         name="postvote", mats=((128, 128),) * 512 + ((1024, 4096),) * 64,
         w_dtype="f32", M=200, scale="spectral", P=8, ns_precision="bf16", T=10,
@@ -139,6 +149,12 @@ WORKLOADS = {
         name="nanogpt_ternary", mats=NANOGPT_LAYER * 12, w_dtype="bf16", M=8,
         scale="fro", P=0, ns_precision="bf16", T=20, warmup=3,
         post_vote=False, signal_std=0.3, seed_index=6, encoding="ternary", **_COMMON),
+    # The nanoGPT set with the spectral-norm normalized sign step
+    # (post_vote = 3): ||D||_2 of each majority matrix from P = 5 power steps.
+    "nanogpt_normalized": Workload(
+        name="nanogpt_normalized", mats=NANOGPT_LAYER * 12, w_dtype="bf16", M=8,
+        scale="fro", P=5, ns_precision="bf16", T=20, warmup=3,
+        post_vote=3, signal_std=0.3, seed_index=7, **_COMMON),
     # The nanoGPT set with both polar steps (no configuration of its own is
     # given for this variant).
     "nanogpt_prepost": Workload(

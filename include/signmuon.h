@@ -257,6 +257,14 @@ sm_status signmuon_executor_destroy(sm_executor *ex);
  *   top of Algorithm 2): the local worker's pipeline of post_vote = 0, then
  *   the vote and update of post_vote = 1.  Both PolarNS passes use the same
  *   hyper-parameters and start vectors.
+ * post_vote = 3 (the spectral-norm normalized sign step under which the
+ *   abstract states its O(1/sqrt(T)) rate; section 4 normalizes D_t in the
+ *   analysis and estimates spectral norms by power iteration, locally): the
+ *   local worker's pipeline of post_vote = 0, then the majority matrix D of
+ *   each matrix, s = an estimate of ||D||_2 from hp->P power-iteration steps
+ *   on its smaller Gram matrix (start vectors u0, as for the spectral
+ *   pre-scale), and W <- W - eta * D / (s + eps).  Needs 1 <= hp->P <= 256
+ *   whatever hp->scale is.
  * Any other post_vote value is SM_EINVAL (the workspace query returns 0).
  *
  * mats[n_mats]: HOST array of matrix descriptors (1 <= n_mats <= 65536);
@@ -328,9 +336,16 @@ typedef enum sm_phase {
   SM_PHASE_START = 0,     /* opening event */
   SM_PHASE_MOMENTUM = 1,  /* momentum sweep (+ signs in the post-vote form) */
   SM_PHASE_PRESCALE = 2,  /* Frobenius finalize / power iteration */
-  SM_PHASE_GEMM = 3,      /* one Newton-Schulz matrix-core launch */
+  SM_PHASE_GEMM = 3,      /* the concurrent PolarNS chains (closed at their
+                             join), or an elementwise Newton-Schulz launch */
   SM_PHASE_PACK = 4,      /* unfused sign packing */
-  SM_PHASE_VOTE = 5       /* vote (+ apply, or majority matrix) */
+  SM_PHASE_VOTE = 5,      /* vote (+ apply, or majority matrix) */
+  /* single Newton-Schulz matrix-core launches (only recorded outside the
+     concurrent chains: without an executor, or for sets run as one chain) */
+  SM_PHASE_GRAM = 6,      /* Gram or raw Gram S S^T */
+  SM_PHASE_SQUARE = 7,    /* symmetric Rp x Rp product (Gram-space steps,
+                             quintic square) */
+  SM_PHASE_UPDATE = 8     /* update B S, or the final product Q_K S_0 */
 } sm_phase;
 typedef struct sm_profile {
   hipEvent_t *events;

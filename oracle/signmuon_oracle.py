@@ -302,9 +302,26 @@ def worker_direction(Mom_new, hp, u0=None, post_vote=0):
     """
     if post_vote == 1:
         return np.asarray(Mom_new, np.float64), None
+    # post_vote 0, 2 and 3: Algorithm 2's worker pipeline
     U, _ = polar_ns(Mom_new, hp["K"], hp["eps"], hp["scale"], hp.get("P", 0),
                     hp.get("coeffs", CUBIC), u0)
     return U, U
+
+
+def normalized_sign(D, P, eps, u0=None):
+    """The spectral-norm normalized sign step of the analysis: D / ||D||_2.
+
+    The abstract states the O(1/sqrt(T)) rate for the spectral-norm
+    normalized sign step; section 4 (single-worker variant) normalizes D_t
+    explicitly in the analysis, and section 4 (Newton-Schulz paragraph)
+    estimates spectral norms by power iteration, all locally.  ||D||_2 is
+    estimated as in the spectral pre-scale (P power steps on the smaller
+    Gram from u0, s = sqrt(|w_P|)) and, as there, eps is added:
+    returns D / (s + eps), so a zero D gives a zero step.
+    """
+    D = np.asarray(D, np.float64)
+    s = spectral_scale(D, P, u0)
+    return D / (s + float(eps))
 
 
 def step(mats, W, Moms, Gs, hp, tie_value=0, post_vote=0, w_dtype="f32",
@@ -317,6 +334,8 @@ def step(mats, W, Moms, Gs, hp, tie_value=0, post_vote=0, w_dtype="f32",
     factor of the majority matrix).  2: both polar steps, the abstract's
     optional local polar step on the sota2.com record read as a PolarNS of
     the voted matrix after Algorithm 2's exchange, with the same settings.
+    3: the spectral-norm normalized sign step (Algorithm 2's workers, then
+    W moves by eta times normalized_sign(majority), with hp's P and eps).
 
     mats: list of (rows, cols) in storage order; the flat arrays W (length
     d, values exact in w_dtype), Moms[m] and Gs[m] (length d each) hold the
@@ -376,20 +395,24 @@ def step(mats, W, Moms, Gs, hp, tie_value=0, post_vote=0, w_dtype="f32",
         out["bits"] = bits
     else:
         out["signs"] = signs
-    if post_vote not in (0, 1, 2):
-        raise ValueError(f"post_vote must be 0, 1 or 2, not {post_vote!r}")
+    if post_vote not in (0, 1, 2, 3):
+        raise ValueError(f"post_vote must be 0, 1, 2 or 3, not {post_vote!r}")
     if post_vote == 0:
         out["Wn"] = apply_update(W, D, hp["eta"], w_dtype)
         return out
     # Post-vote variant and the second half of post_vote = 2: local polar
-    # step on the aggregated sign matrix.
+    # step on the aggregated sign matrix; post_vote = 3: the majority
+    # normalized by its spectral norm.
     Uflat = np.zeros(d, dtype=np.float64)
     Upost = []
     for i, (r, c) in enumerate(mats):
         Sbar = D[offs[i]:offs[i + 1]].astype(np.float64).reshape(r, c)
         u0 = None if u0s is None else u0s[i]
-        U, _ = polar_ns(Sbar, hp["K"], hp["eps"], hp["scale"], hp.get("P", 0),
-                        hp.get("coeffs", CUBIC), u0)
+        if post_vote == 3:
+            U = normalized_sign(Sbar, hp["P"], hp["eps"], u0)
+        else:
+            U, _ = polar_ns(Sbar, hp["K"], hp["eps"], hp["scale"], hp.get("P", 0),
+                            hp.get("coeffs", CUBIC), u0)
         Upost.append(U)
         Uflat[offs[i]:offs[i + 1]] = U.reshape(-1)
     out["Upost"] = Upost

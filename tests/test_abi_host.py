@@ -160,7 +160,7 @@ def test_worker_pipeline_validation():
     assert call(M=0) == B.SM_ERANGE
     assert call(worker=3) == B.SM_EINVAL
     assert call(worker=-1) == B.SM_EINVAL
-    assert call(post=3) == B.SM_EINVAL
+    assert call(post=4) == B.SM_EINVAL
     assert call(post=-1) == B.SM_EINVAL
     assert call(G=None) == B.SM_EINVAL
     assert call(stride=words - 1) == B.SM_EINVAL
@@ -174,7 +174,7 @@ def test_step_validation():
     assert _step(L, mats, hp, M=0) == B.SM_ERANGE
     assert _step(L, mats, hp, M=40000) == B.SM_ERANGE
     assert _step(L, mats, hp, M=3, local=3) == B.SM_EINVAL
-    assert _step(L, mats, hp, post=3) == B.SM_EINVAL
+    assert _step(L, mats, hp, post=4) == B.SM_EINVAL
     assert _step(L, mats, hp, post=-1) == B.SM_EINVAL
     assert _step(L, mats, hp, G=None) == B.SM_EINVAL
     assert _step(L, mats, hp, stride=words - 1) == B.SM_EINVAL
@@ -195,7 +195,7 @@ def test_step_workspace_post_vote_modes():
     mats, _, _ = B.default_layout(WL.get("nanogpt").mats)
     assert B.step_workspace(mats, hp, 2) == B.step_workspace(mats, hp, 0) > 0
     assert B.step_workspace(mats, hp, 1) > 0
-    assert B.step_workspace(mats, hp, 3) == 0
+    assert B.step_workspace(mats, hp, 4) == 0
     assert B.step_workspace(mats, hp, -1) == 0
     # widths that are not multiples of 32 keep a float32 U for the separate
     # packing pass of the pre-sign polar factor (0 and 2 only)
@@ -290,3 +290,15 @@ def test_step_ternary_validation():
     # int8 signs come straight from the last epilogue: no float32 U is kept
     m1, _, _ = B.default_layout([(5, 37)])
     assert B.step_workspace(m1, hp, 0) < B.step_workspace(m1, _hp(), 0)
+
+
+def test_step_normalized_validation():
+    # the normalized sign step needs P >= 1 power steps whatever the scale,
+    # and keeps the raw Gram and power vectors in its workspace
+    L = B.lib()
+    mats, d, words = B.default_layout([(64, 96), (96, 64)])
+    assert _step(L, mats, _hp(P=0), post=3) == B.SM_EINVAL
+    assert _step(L, mats, _hp(P=300), post=3) == B.SM_EINVAL
+    assert B.step_workspace(mats, _hp(P=0), 3) == 0
+    assert B.step_workspace(mats, _hp(P=5), 3) > B.step_workspace(mats, _hp(P=5), 0)
+    assert B.step_workspace(mats, _hp(P=5), 4) == 0

@@ -163,13 +163,21 @@ def check_after_vote(w, hp, W, Wg, bits, shape, u0, tag):
         Wn = O.apply_update(W, D, o["eta"], w.w_dtype)
         assert np.array_equal(Wg.view(np.uint32), Wn.view(np.uint32)), (tag, "apply")
         return
-    Upost, _ = O.polar_ns(D.astype(np.float64).reshape(r, c), o["K"], o["eps"], o["scale"],
-                          o["P"], o["coeffs"], None if u0 is None else u0.astype(np.float64))
+    u0d = None if u0 is None else u0.astype(np.float64)
+    if w.post_vote == 3:
+        # D / (||D||_2 + eps): float32 power iteration on an exact integer
+        # Gram, held to the float32 polar bound
+        Upost = O.normalized_sign(D.astype(np.float64).reshape(r, c), o["P"], o["eps"], u0d)
+        ptol = polar_tol("f32")
+    else:
+        Upost, _ = O.polar_ns(D.astype(np.float64).reshape(r, c), o["K"], o["eps"], o["scale"],
+                              o["P"], o["coeffs"], u0d)
+        ptol = polar_tol(hp.precision)
     Ug = (W.astype(np.float64) - Wg.astype(np.float64)) / o["eta"]
-    tol = polar_tol(hp.precision) + 1e-6 + w_round_tol(Wg, w.w_dtype, o["eta"])
+    tol = ptol + 1e-6 + w_round_tol(Wg, w.w_dtype, o["eta"])
     err = np.abs(Ug - Upost.reshape(-1))
     assert np.all(err <= tol), (tag, "post-vote", float(err.max()))
-    if w.w_dtype == "f32" and hp.precision == "f32":
+    if w.w_dtype == "f32" and (hp.precision == "f32" or w.post_vote == 3):
         # The post-vote update applies U itself, not its signs, so the polar
         # bound above is its gate.  With float32 products the recovered U
         # also carries the signs of the oracle's (a bfloat16 W keeps too few
@@ -211,6 +219,18 @@ SMALL = {
                          None, 2),
     "prepost_ternary": (WL.scaled(WL.get("nanogpt_prepost"), [(192, 576), (768, 192)] * 2,
                                   name="prepost-ternary").replace(encoding="ternary"), None, 2),
+    # the normalized sign step D / ||D||_2 (||D||_2 by P power steps)
+    "normalized": (WL.scaled(WL.get("nanogpt_normalized"), [(192, 576), (192, 192),
+                                                            (192, 768), (768, 192)] * 2),
+                   None, 3),
+    "normalized_spectral_f32w": (WL.scaled(WL.get("resnet50"), [(64, 147), (128, 576),
+                                                                (256, 512), (512, 256),
+                                                                (10, 256)],
+                                           name="resnet50-normalized").replace(post_vote=3),
+                                 None, 2),
+    "normalized_ternary": (WL.scaled(WL.get("nanogpt_normalized"), [(192, 576), (768, 192)],
+                                     name="normalized-ternary").replace(encoding="ternary"),
+                           None, 2),
     # the post-vote step with float32 W and float32 products
     "postvote_f32": (WL.scaled(WL.get("postvote"), [(128, 128)] * 2 + [(256, 512)], M=12,
                                name="postvote-f32").replace(ns_precision="f32"), None, 2),
@@ -283,6 +303,8 @@ ODD = {
     .replace(ns_precision="f32", encoding="ternary"),
     "ternary_M6": WL.scaled(WL.get("nanogpt"), ODD_BF16, M=6, name="odd-ternary-bf16")
     .replace(encoding="ternary"),
+    "normalized_M5": WL.scaled(WL.get("nanogpt_normalized"), ODD_BF16, M=5,
+                               name="odd-normalized"),
 }
 
 
@@ -448,6 +470,10 @@ def test_step_ternary_diagonal_zeros_vote_nothing():
         assert np.array_equal(Wg[sl][off_diag].view(np.uint32), W[sl][off_diag].view(np.uint32))
 
 
+def test_step_full_nanogpt_normalized():
+    full_case("nanogpt_normalized", sample=[0, 1, 46, 47])
+
+
 def test_step_full_nanogpt_prepost():
     full_case("nanogpt_prepost", sample=[0, 1, 46, 47])
 
@@ -469,7 +495,7 @@ def test_step_full_postvote():
 # every worker's bit equals the oracle's.
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["nanogpt", "postvote", "prepost", "nanogpt_ternary",
-                                  "postvote_ternary"])
+                                  "postvote_ternary", "normalized"])
 def test_all_workers_on_gpu(name, chain_mode):
     w, _, _ = SMALL[name]
     if name.startswith("postvote"):

@@ -563,3 +563,54 @@ def test_step_ternary_matches_packed_without_zeros():
             assert np.array_equal(O.pack_signs(t), a["bits"][m, woffs[i]:woffs[i + 1]])
     with pytest.raises(ValueError):
         O.step(mats, W, Moms, Gs, HP, 0, 0, "bf16", encoding="int4")
+
+
+# --------------------------------------------------------------------------
+# The spectral-norm normalized sign step (post_vote = 3): W moves by
+# eta D / (||D||_2 + eps), ||D||_2 from P power steps.
+# --------------------------------------------------------------------------
+def test_normalized_sign_rank_one_closed_form():
+    # D = s t^T with s, t in {-1, +1}: D D^T = n s s^T has one eigenvalue
+    # m n, reached exactly after the first power step, so ||D||_2 = sqrt(mn)
+    rng = np.random.default_rng(21)
+    for (m, n) in [(4, 9), (9, 4), (6, 6)]:
+        st = np.outer(rng.choice([-1, 1], m), rng.choice([-1, 1], n)).astype(np.float64)
+        u0 = rng.standard_normal(min(m, n))
+        for P in (2, 3, 7):
+            got = O.normalized_sign(st, P, 1e-7, u0)
+            assert np.allclose(got, st / (np.sqrt(m * n) + 1e-7), rtol=1e-14, atol=0)
+    # a diagonal +-1 majority has all singular values 1
+    D = np.zeros((3, 5)); D[0, 0], D[1, 1], D[2, 2] = 1, -1, 1
+    assert np.allclose(O.normalized_sign(D, 4, 1e-7), D / (1 + 1e-7), rtol=1e-15)
+    # a zero majority (every vote tied) gives a zero step
+    assert np.all(O.normalized_sign(np.zeros((4, 4)), 3, 1e-7) == 0.0)
+
+
+def test_normalized_sign_converges_to_spectral_norm():
+    rng = np.random.default_rng(22)
+    D = np.sign(rng.standard_normal((12, 30)))
+    sig = np.linalg.norm(D, 2)
+    got = O.normalized_sign(D, 200, 1e-7, rng.standard_normal(12))
+    assert np.allclose(got, D / (sig + 1e-7), rtol=1e-10)
+    assert abs(np.linalg.norm(got, 2) - 1.0) < 1e-6
+
+
+def test_step_normalized_sign_uses_algorithm2_signs():
+    rng = np.random.default_rng(23)
+    mats = [(6, 10), (9, 5)]
+    W, Gs, Moms = _set(rng, mats, 3)
+    hp = dict(HP, P=6)
+    a2 = O.step(mats, W, Moms, Gs, hp, 0, 0, "f32")
+    ns = O.step(mats, W, Moms, Gs, hp, 0, 3, "f32")
+    assert np.array_equal(ns["bits"], a2["bits"])          # the same workers
+    assert np.array_equal(ns["D"], a2["D"])
+    offs = np.cumsum([0] + [r * c for r, c in mats])
+    for i, (r, c) in enumerate(mats):
+        D = a2["D"][offs[i]:offs[i + 1]].astype(np.float64).reshape(r, c)
+        assert np.array_equal(ns["Upost"][i], O.normalized_sign(D, 6, 1e-7))
+        # a step of spectral norm at most about 1 (the estimate is below
+        # ||D||_2, so slightly above 1 is possible)
+        assert np.linalg.norm(ns["Upost"][i], 2) < 1.2
+    want = (W - (np.float32(0.02) * np.concatenate(
+        [u.reshape(-1) for u in ns["Upost"]]).astype(np.float32))).astype(np.float32)
+    assert np.array_equal(ns["Wn"], want)
