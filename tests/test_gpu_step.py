@@ -484,6 +484,12 @@ def test_step_full_llm_mlp():
 
 
 @pytest.mark.slow
+def test_step_full_llm_mlp_quintic():
+    # the quintic on the 4096 x 4096 matrix (split-bfloat16, spectral P = 10)
+    full_case("llm_mlp_quintic", sample=[0])
+
+
+@pytest.mark.slow
 def test_step_full_postvote():
     full_case("postvote", sample=[0, 1, 511, 512], bits_kind="ties")
 
