@@ -756,34 +756,23 @@ double chain_min_flop() {
 
 // Caller-owned resources of the concurrent chains (signmuon_executor_create):
 // the chains' streams, created on `device`, and for each of the (at most
-// two) PolarNS passes of one step its own fork, head and join events, so no
-// event is recorded twice within a step.  `mu` keeps two threads from
+// two) PolarNS passes of one step its own fork and join events, so no event
+// is recorded twice within a step.  `mu` keeps two threads from
 // enqueueing through one executor at the same time.
 struct sm_executor {
   int device = -1;
   hipStream_t s[kChains] = {};
   hipEvent_t fork[2] = {};
-  hipEvent_t head[2][kChains] = {};
   hipEvent_t join[2][kChains] = {};
   std::mutex mu;
 };
 
 namespace {
 
-// Optional work of a chain around its PolarNS: `head` stages run before the
-// pre-scale on the chain's stream, `tail` stages after the last
-// Newton-Schulz step, and every chain's tail waits until every chain's head
-// has finished (so work that must follow all heads, like a vote that is
-// skipped when any head found a non-finite value, can go in a tail).
-struct ChainHooks {
-  std::function<void(const std::vector<Group>&, hipStream_t, Stages&)> head, tail;
-};
-
 sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
                     const std::vector<Group>& groups, const std::vector<bool>& fusable,
                     const sm_hparams* hp, Bufs& B, const NsIO& io, int part_kind,
-                    hipStream_t s, sm_executor* ex, int pass,
-                    const ChainHooks* hooks = nullptr) {
+                    hipStream_t s, sm_executor* ex, int pass) {
   // Sets with little Newton-Schulz work are bound by the host's launch
   // rate: one chain puts all their groups into each launch (up to
   // kMaxGroups per launch), a third of the launches of three chains.
@@ -802,10 +791,8 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
   }
   if (nc <= 1) {
     Stages st;
-    if (hooks) hooks->head(groups, s, st);
     pre_scale_stages(P, mp, groups, hp, B, io, part_kind, s, st);
     if (hp->K > 0) ns_stages(P, mp, groups, fusable, hp, B, io, s, st);
-    if (hooks) hooks->tail(groups, s, st);
     return run_stages(st);
   }
   // longest-processing-time assignment of the groups to the chains, by
@@ -827,32 +814,15 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
   }
   sm_executor* R = ex;
   std::lock_guard<std::mutex> lock(R->mu);
-  hipEvent_t* head_ev = R->head[pass];
   hipEvent_t* join_ev = R->join[pass];
   HIP_TRY(hipEventRecord(R->fork[pass], s));
   NsIO cio = io;
   cio.prof = nullptr;
-  // heads[c] run (for every chain) before any stage of prog, so every head
-  // event is recorded before a tail waits for it
-  std::vector<Stages> heads(nc), prog(nc);
+  std::vector<Stages> prog(nc);
   for (int c = 0; c < nc; ++c) {
     hipStream_t cs = R->s[c];
-    if (hooks) {
-      hooks->head(chain[c], cs, heads[c]);
-      heads[c].push_back([head_ev, c, cs]() -> sm_status {
-        HIP_TRY(hipEventRecord(head_ev[c], cs));
-        return SM_OK;
-      });
-    }
     pre_scale_stages(P, mp, chain[c], hp, B, cio, part_kind, cs, prog[c]);
     if (hp->K > 0) ns_stages(P, mp, chain[c], fusable, hp, B, cio, cs, prog[c]);
-    if (hooks) {
-      prog[c].push_back([head_ev, nc, cs]() -> sm_status {
-        for (int o = 0; o < nc; ++o) HIP_TRY(hipStreamWaitEvent(cs, head_ev[o], 0));
-        return SM_OK;
-      });
-      hooks->tail(chain[c], cs, prog[c]);
-    }
   }
   sm_status st = SM_OK;
   int forked = 0;
@@ -860,13 +830,11 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
     if (hipStreamWaitEvent(R->s[c], R->fork[pass], 0) != hipSuccess) { st = SM_EHIP; break; }
     ++forked;
   }
-  for (const std::vector<Stages>* lists : {&heads, &prog}) {
-    size_t longest = 0;
-    for (const Stages& p : *lists) longest = std::max(longest, p.size());
-    for (size_t i = 0; i < longest && st == SM_OK; ++i)
-      for (int c = 0; c < forked && st == SM_OK; ++c)
-        if (i < (*lists)[c].size()) st = (*lists)[c][i]();
-  }
+  size_t longest = 0;
+  for (const Stages& p : prog) longest = std::max(longest, p.size());
+  for (size_t i = 0; i < longest && st == SM_OK; ++i)
+    for (int c = 0; c < forked && st == SM_OK; ++c)
+      if (i < prog[c].size()) st = prog[c][i]();
   // join every forked chain, also after an error, so that the caller's
   // stream orders after all work enqueued on the chains
   for (int c = 0; c < forked; ++c) {
@@ -1232,45 +1200,6 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
       io.first_xsrc = XS_USER; io.src_user = Mom;
       io.final_out = tern ? O_TERN : O_BITS; io.bits = local_bits; io.tern = local_tern;
       io.U = nullptr;
-      if (!prof && post_vote == 0) {
-        // Each chain sweeps its own matrices, runs their PolarNS, packs the
-        // signs the last epilogue could not, and votes over them, so one
-        // chain's memory-bound sweep and vote overlap another's GEMMs.  The
-        // votes wait for every chain's sweep: the update of W is skipped when
-        // any sweep found a non-finite value.
-        ChainHooks hooks;
-        hooks.head = [&](const std::vector<Group>& cg, hipStream_t cs, Stages& out) {
-          out.push_back([&, cs, pcg = &cg]() -> sm_status {
-            SweepArgs a = sw;
-            HIP_TRY(for_launches(*pcg, sweep_fill, [&](const Groups& Gs) {
-              a.G = Gs; return launch_sweep(a, cs);
-            }));
-            return SM_OK;
-          });
-        };
-        hooks.tail = [&](const std::vector<Group>& cg, hipStream_t cs, Stages& out) {
-          out.push_back([&, cs, pcg = &cg]() -> sm_status {
-            if (need_u)
-              for (const Group& g : *pcg)
-                for (int k = 0; k < g.count; ++k) {
-                  const int i = g.idx0 + k * g.idx_stride;
-                  if (fus[i]) continue;
-                  HIP_TRY(launch_sign_pack_flat(B.u + mats[i].elem_off,
-                                                local_bits + mats[i].word_off,
-                                                mats[i].rows * mats[i].cols, cs));
-                }
-            if (pipeline_only) return SM_OK;
-            VoteArgs a = va;
-            a.mode = VA_APPLY;
-            HIP_TRY(for_launches(*pcg, [&](Group& g) {
-              g.blocks_per_mat = vote_blocks(VA_APPLY, g);
-              return true;
-            }, [&](const Groups& Gs) { a.G = Gs; return launch_vote_groups(a, cs); }));
-            return SM_OK;
-          });
-        };
-        return run_polar(P, mp, groups, fus, hp, B, io, 0, stream, ex, 0, &hooks);
-      }
       HIP_TRY(for_launches(groups, sweep_fill,
                            [&](const Groups& Gs) { sw.G = Gs; return launch_sweep(sw, stream); }));
       HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
@@ -1378,8 +1307,6 @@ sm_status signmuon_executor_create(sm_executor** out) {
   for (int p = 0; p < 2 && e == hipSuccess; ++p) {
     e = hipEventCreateWithFlags(&ex->fork[p], hipEventDisableTiming);
     for (int c = 0; c < kChains && e == hipSuccess; ++c)
-      e = hipEventCreateWithFlags(&ex->head[p][c], hipEventDisableTiming);
-    for (int c = 0; c < kChains && e == hipSuccess; ++c)
       e = hipEventCreateWithFlags(&ex->join[p][c], hipEventDisableTiming);
   }
   if (e != hipSuccess) {
@@ -1400,10 +1327,8 @@ sm_status signmuon_executor_destroy(sm_executor* ex) {
     if (ex->s[c] && hipStreamSynchronize(ex->s[c]) != hipSuccess) st = SM_EHIP;
   for (int p = 0; p < 2; ++p) {
     if (ex->fork[p]) (void)hipEventDestroy(ex->fork[p]);
-    for (int c = 0; c < kChains; ++c) {
-      if (ex->head[p][c]) (void)hipEventDestroy(ex->head[p][c]);
+    for (int c = 0; c < kChains; ++c)
       if (ex->join[p][c]) (void)hipEventDestroy(ex->join[p][c]);
-    }
   }
   for (int c = 0; c < kChains; ++c)
     if (ex->s[c]) (void)hipStreamDestroy(ex->s[c]);
