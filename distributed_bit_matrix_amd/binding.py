@@ -407,8 +407,10 @@ class StepPlan:
                 u0=None):
         """Recording the step into a HIP graph is switched off: with this
         ROCm release, ending the capture of a step (torch.cuda.graph around
-        one call, the library's internal streams joined by events) ended the
-        process with a segmentation fault inside the runtime, and no cause
-        in the library has been found.  Steps are enqueued eagerly."""
+        one call) ended the process with a segmentation fault inside the
+        runtime, also for sets that run as one chain on the capturing stream
+        (so the fork and join of the executor's streams is not the cause),
+        and no cause in the library has been found.  Steps are enqueued
+        eagerly."""
         raise SignMuonError("StepPlan.capture", SM_EUNSUPPORTED,
                             "HIP graph capture of the step is disabled")
