@@ -64,6 +64,14 @@ bool gram_space_enabled() {
   return !(e && std::strcmp(e, "iterate") == 0);
 }
 
+// bfloat16 symmetric operands are stored as their upper-triangular tiles
+// unless the environment variable SIGNMUON_SYM_STORAGE is "full" (read at
+// every call; then every symmetric output also writes its mirror tiles).
+bool sym_upper_enabled() {
+  const char* e = std::getenv("SIGNMUON_SYM_STORAGE");
+  return !(e && std::strcmp(e, "full") == 0);
+}
+
 // Per-matrix placement.  Returns SM_OK or SM_EINVAL for unusable shapes.
 sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
                      int post_vote, bool need_u, Plan& P,
@@ -80,6 +88,7 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
   // missed the sign gate on test matrices that the iterate form passes
   P.gram_space = P.precision == P_BF16 && !P.quintic && !P.spectral && hp->K > 0 &&
                  gram_space_enabled();
+  P.upper = P.precision == P_BF16 && sym_upper_enabled();
   int64_t x = 0, r2 = 0, v = 0, c = 0, u0 = 0, umax = 0;
   for (int i = 0; i < nm; ++i) {
     const sm_matrix& m = mats[i];
@@ -420,7 +429,7 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
         std::memset(&a, 0, sizeof(a));
         a.G = G;
         a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
-        a.epi = E_OP; a.mul = gram_mul; a.scal = B.scal; a.scal_pow = 2;
+        a.epi = E_OP; a.upper = P.upper; a.mul = gram_mul; a.scal = B.scal; a.scal_pow = 2;
         a.kpart = B.kpart;
         a.o_hi = dst_hi; a.o_lo = dst_lo;
         if (gram_writes_q1(P, groups)) {
@@ -513,7 +522,7 @@ hipError_t run_square(const Plan& P, const std::vector<MatPlan>& mp,
     std::memset(&a, 0, sizeof(a));
     a.G = G;
     a.r_hi = B.a[0]; a.r_lo = B.a[1];
-    a.epi = E_SQUARE; a.cb = hp->ns_b; a.cc = hp->ns_c;
+    a.epi = E_SQUARE; a.upper = P.upper; a.cb = hp->ns_b; a.cc = hp->ns_c;
     a.sq_hi = B.a[0]; a.sq_lo = B.a[1];
     a.o_hi = B.b[0]; a.o_lo = B.b[1];
     return launch_gemm(P.precision, a, s);
@@ -557,7 +566,7 @@ void gram_space_stages(const Plan& P, const std::vector<MatPlan>& mp,
         std::memset(&a, 0, sizeof(a));
         a.G = G;
         a.r_hi = X; a.r2_hi = Y;
-        a.epi = E_SQUARE; a.cb = ca; a.cc = cb;
+        a.epi = E_SQUARE; a.upper = P.upper; a.cb = ca; a.cc = cb;
         a.sq_hi = Y;
         a.o_hi = O;
         return launch_gemm(prec, a, s);
@@ -605,7 +614,7 @@ void gram_space_stages(const Plan& P, const std::vector<MatPlan>& mp,
         a.G = G;
         a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
         a.r_hi = QK;
-        a.epi = E_UPDATE; a.ca = 0.0f; a.xsrc = XS_OP;
+        a.epi = E_UPDATE; a.upper = P.upper; a.ca = 0.0f; a.xsrc = XS_OP;
         a.scal = B.scal; a.scal_pow = 1;
         if (io.final_out == O_BITS && pass == 1) {
           a.out = O_U; a.U = B.u;
@@ -651,7 +660,7 @@ void ns_stages(const Plan& P, const std::vector<MatPlan>& mp,
           std::memset(&a, 0, sizeof(a));
           a.G = G;
           a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
-          a.epi = E_OP; a.mul = P.quintic ? 1.0f : hp->ns_b; a.scal_pow = 0;
+          a.epi = E_OP; a.upper = P.upper; a.mul = P.quintic ? 1.0f : hp->ns_b; a.scal_pow = 0;
           a.kpart = B.kpart;
           a.o_hi = P.quintic ? B.a[0] : B.b[0];
           a.o_lo = P.quintic ? B.a[1] : B.b[1];
@@ -690,7 +699,7 @@ void ns_stages(const Plan& P, const std::vector<MatPlan>& mp,
           a.G = G;
           a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
           a.r_hi = B.b[0]; a.r_lo = B.b[1];
-          a.epi = E_UPDATE; a.ca = hp->ns_a;
+          a.epi = E_UPDATE; a.upper = P.upper; a.ca = hp->ns_a;
           a.xsrc = k == 1 ? io.first_xsrc : XS_OP;
           a.xs_user = io.src_user;
           a.scal = B.scal; a.scal_pow = k == 1 ? 1 : 0;

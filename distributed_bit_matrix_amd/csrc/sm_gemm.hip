@@ -140,6 +140,16 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
+// A uniform pointer made opaque to the optimizer (an empty asm statement
+// that keeps it in scalar registers), so that it cannot be folded with
+// per-lane offsets into 64-bit vector addresses carried across the loop: a
+// load then keeps the scalar-base + 32-bit vector-offset form.
+__device__ __forceinline__ const char* scalar_ptr(const char* p) {
+  uint64_t v = reinterpret_cast<uint64_t>(p);
+  asm volatile("" : "+s"(v));
+  return reinterpret_cast<const char*>(v);
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>
@@ -429,6 +439,19 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   // Operand layouts are fixed by the product: only the update's S operand
   // (B) is read k-major.  (The host sets the operand families to match.)
   constexpr bool a_km = false, b_km = EPI == E_UPDATE;
+  // Upper-triangular storage of the bfloat16 symmetric operands (A.upper):
+  // row block t of a stored Rp x Rp operand has its k-slabs left of the
+  // diagonal (k < 128 t) only in the tile above the diagonal, so those
+  // slabs are fetched k-major from there: the A operand of the symmetric
+  // product and of the update (row block tm) below slab sA, the B operand
+  // of the symmetric product (row block tn) below slab sB.  For an upper
+  // tile tm <= tn, so sA <= sB.
+  constexpr bool UPK = sizeof(T) == 2 && SPLIT == 1;
+  constexpr bool UPR = UPK && (EPI == E_SQUARE || EPI == E_UPDATE);
+  const bool upper = UPK && A.upper != 0;
+  constexpr int TPS = kTileSym / (RB / (int)sizeof(T));   // slabs per 128-wide tile
+  const int sA = UPR && upper ? tm * TPS : 0;
+  const int sB = UPR && EPI == E_SQUARE && upper ? tn * TPS : 0;
   // Accumulator layout.  Register r of lane l in tile (i, j) holds C(row, col):
   //   C tiles:       row = m0 + wm*WTM + 16 i + 4 (l/16) + r,  col = n0 + wn*WTN + 16 j + l % 16
   //   transposed:    row = m0 + wm*WTM + 16 i + l % 16,  col = n0 + wn*WTN + 16 j + 4 (l/16) + r
@@ -486,6 +509,22 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   for (int q = 0; q < QA; ++q) aoff[q] = (uint32_t)(dma_off(a_km, wave * QA + q, m0, g.gm, lda, BMT) * (int64_t)sizeof(T));
 #pragma unroll
   for (int q = 0; q < QB; ++q) boff[q] = (uint32_t)(dma_off(b_km, wave * QB + q, n0, g.gn, ldb, BNT) * (int64_t)sizeof(T));
+  // k-major offsets of the slabs taken from the tile above the diagonal,
+  // one register per operand: load q of a wave fills LDS rows 4 (QA w + q)
+  // .. +3 (256-byte rows), so loads q and q + 1 (q even) are 4 rows apart
+  // with the same swizzle, and loads 2 apart are 8 rows apart with the
+  // swizzle's row bit 3 flipped, i.e. bit 7 of the byte offset (rows start
+  // at multiples of 256 bytes).  Holds for 128-wide tiles of 2-byte
+  // elements with 2 or 4 loads per wave.
+  constexpr bool UPB = UPR && EPI == E_SQUARE;
+  // the update's S operand (always k-major) uses the same scheme when its
+  // tile is 128 wide
+  constexpr bool BKC = sizeof(T) == 2 && b_km && BNT == 128;
+  static_assert(!UPR || (BMT == 128 && (QA == 2 || QA == 4)), "k-major offset scheme");
+  static_assert(!(UPB || BKC) || (BNT == 128 && (QB == 2 || QB == 4)), "k-major offset scheme");
+  const uint32_t aoff_t = UPR ? (uint32_t)(dma_off(true, wave * QA, m0, g.gm, lda, BMT) * 2) : 0u;
+  const uint32_t boff_t = UPB || BKC ? (uint32_t)(dma_off(true, wave * QB, n0, g.gn, ldb, BNT) * 2)
+                                     : 0u;
   // elements between consecutive slabs
   const int64_t a_kst = a_km ? (int64_t)BK * lda : BK, b_kst = b_km ? (int64_t)BK * ldb : BK;
 
@@ -493,18 +532,38 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   // the tile and 16-byte chunk (kk*4 + lane/16) of the slab row.  The
   // swizzle depends on row bits that i*16 does not touch, so one offset per
   // kk serves all i (j) with a constant stride.
-  int fa_off[NKK], fb_off[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    fa_off[kk] = lds_off<RB>(wm * WTM + (lane & 15), kk * 4 + (lane >> 4));
-    fb_off[kk] = lds_off<RB>(wn * WTN + (lane & 15), kk * 4 + (lane >> 4));
-  }
+  // (k-step kk is chunk 4 kk + lane/16: for kk < 2 that XORs bit 6 of the
+  // k-step 0 offset, since the swizzle is below 8)
+  static_assert(NKK <= 2, "fragment offsets");
+  const int fa_off0 = lds_off<RB>(wm * WTM + (lane & 15), lane >> 4);
+  const int fb_off0 = lds_off<RB>(wn * WTN + (lane & 15), lane >> 4);
   // A fragment of a k-major tile: MFMA tile columns c0 .. c0+15, k-step kk.
   //  bf16: two transposing reads, rows kk*32 + 8 (lane/16) + (lane%16)/4 and
   //   4 rows down, bytes 2 c0 + 8 (lane % 4): lane l gets k = 8 (l/16) .. +7
   //   of column c0 + l % 16, the MFMA operand layout.
   //  float32: the 16x16x4 MFMA takes k = 4 (kk*4 + l/16) + e, e = 0..3, of
   //   column c0 + l % 16 in register e (as the k-along-rows reads).
+  // bf16: per-lane byte offset of the first transposing read of MFMA tile
+  // i = 0, k-step 0 in a k-major tile of width W whose wave columns start
+  // at cw; tile i and k-step kk are at (base ^ 32 i) + kk * 64 W (the
+  // swizzle XORs the 32-byte chunk index, and 16 i columns are chunk i; 32
+  // rows down leave it unchanged), the second read 4 rows (8 W bytes) down.
+  auto km_base = [&](auto wc, int cw) SM_INLINE -> int {
+    constexpr int W = decltype(wc)::value;
+    return km_off<T, W>(8 * (lane >> 4) + ((lane & 15) >> 2), 2 * cw + 8 * (lane & 3));
+  };
+  int kmA = 0, kmB = 0;
+  if constexpr (sizeof(T) == 2) {
+    if constexpr (UPR) kmA = km_base(std::integral_constant<int, BMT>{}, wm * WTM);
+    if constexpr (b_km || UPB) kmB = km_base(std::integral_constant<int, BNT>{}, wn * WTN);
+  }
+  auto km_frag2 = [&](auto wc, const char* tile, int base, int i, int kk) SM_INLINE -> u32x4_t {
+    constexpr int W = decltype(wc)::value;
+    const char* p = tile + (base ^ (i << 5)) + kk * 64 * W;
+    const u32x2_t lo4 = lds_read_tr16(p);
+    const u32x2_t hi4 = lds_read_tr16(p + 8 * W);
+    return u32x4_t{lo4[0], lo4[1], hi4[0], hi4[1]};
+  };
   auto km_frag = [&](auto wc, const char* tile, int c0, int kk) SM_INLINE -> u32x4_t {
     constexpr int W = decltype(wc)::value;
     if constexpr (sizeof(T) == 2) {
@@ -538,27 +597,50 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     }
   }
 
+  // With upper-triangular storage the k-slabs run in rotated order,
+  // starting at the diagonal tile's column (srot = sB for the symmetric
+  // product, sA for the update) and wrapping around: every block then
+  // starts with slabs of one layout (k along rows for both operands of the
+  // symmetric product, for A of the update), and the loop below meets the
+  // layouts in a fixed order.  Loop position s reads k-slab ks_of(s).
+  const int srot = UPR ? (EPI == E_SQUARE ? sB : sA) : 0;
+  auto ks_of = [&](int s) SM_INLINE { const int k = s + srot; return k >= nslab ? k - nslab : k; };
+
   // LDS stage: [A split 0][A split 1..][B split 0][B split 1..]
   auto a_tile = [&](int st, int sp) -> char* { return smem + st * STAGEB + sp * ATILE; };
   auto b_tile = [&](int st, int sp) -> char* {
     return smem + st * STAGEB + SPLIT * ATILE + sp * BTILE;
   };
-  auto issue = [&](int s) SM_INLINE {
-    const int st = s % NSTG;
+  // one slab of one operand, k along rows (offsets off[]) or k-major from
+  // the tile above the diagonal (offset offt, base at row k of slab s)
+  auto issue_op = [&](const T* src, const uint32_t* off, uint32_t offt, int64_t kst, int64_t ld,
+                      bool km_slab, char* lds, int s, auto nq) SM_INLINE {
+    constexpr int NQ = decltype(nq)::value;
+    // (selects instead of branches: the fetch sits inside the MFMA sequence;
+    // each load's base pointer is made opaque and scalar, so that the load
+    // keeps the scalar-base + 32-bit offset form instead of per-lane 64-bit
+    // addresses carried across the loop)
+    const char* base = reinterpret_cast<const char*>(src + (km_slab ? (int64_t)s * BK * ld : s * kst));
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int64_t dq = km_slab ? (int64_t)((q & 1) * 4 + (q >> 1) * 8) * ld * (int64_t)sizeof(T) : 0;
+      const uint32_t o = km_slab ? ((q >> 1) ? (offt ^ 128u) : offt) : off[q];
+      __builtin_amdgcn_global_load_lds((const void*)(scalar_ptr(base + dq) + o),
+                                       (lds_void*)(lds + q * 1024), 16, 0, 0);
+    }
+  };
+  auto issue = [&](int sq) SM_INLINE {
+    const int st = sq % NSTG, s = ks_of(sq);
 #pragma unroll
     for (int sp = 0; sp < SPLIT; ++sp) {
-      char* ta = a_tile(st, sp) + wave * QA * 1024;
-      char* tb = b_tile(st, sp) + wave * QB * 1024;
-      const char* abase = reinterpret_cast<const char*>(a_src[sp] + s * a_kst);
-      const char* bbase = reinterpret_cast<const char*>(b_src[sp] + s * b_kst);
-#pragma unroll
-      for (int q = 0; q < QA; ++q)
-        __builtin_amdgcn_global_load_lds((const void*)(abase + aoff[q]),
-                                         (lds_void*)(ta + q * 1024), 16, 0, 0);
-#pragma unroll
-      for (int q = 0; q < QB; ++q)
-        __builtin_amdgcn_global_load_lds((const void*)(bbase + boff[q]),
-                                         (lds_void*)(tb + q * 1024), 16, 0, 0);
+      issue_op(a_src[sp], aoff, aoff_t, a_kst, lda, UPR && s < sA, a_tile(st, sp) + wave * QA * 1024,
+               s, std::integral_constant<int, QA>{});
+      if constexpr (BKC)   // (b_kst is the k-major slab stride)
+        issue_op(b_src[sp], boff, boff_t, BK, ldb, true, b_tile(st, sp) + wave * QB * 1024, s,
+                 std::integral_constant<int, QB>{});
+      else
+        issue_op(b_src[sp], boff, boff_t, b_kst, ldb, UPB && s < sB,
+                 b_tile(st, sp) + wave * QB * 1024, s, std::integral_constant<int, QB>{});
     }
   };
 
@@ -711,23 +793,33 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
 
   // fragments of one slab: [kk][split * TI + i] (A) and [kk][split * TJ + j] (B)
   constexpr int NFA = SPLIT * TI, NFB = SPLIT * TJ, NF = NKK * (NFA + NFB);
-  // fragment q of a slab (q = kk * (NFA + NFB) + A fragments, then B)
-  auto read_one = [&](u32x4_t (&fa)[NKK][NFA], u32x4_t (&fb)[NKK][NFB], int stg, int q) SM_INLINE {
+  // fragment q of a slab (q = kk * (NFA + NFB) + A fragments, then B),
+  // with the slab's operand layouts (k-major or k along rows) given as
+  // compile-time constants akc, bkc
+  auto read_one = [&](auto akc, auto bkc, u32x4_t (&fa)[NKK][NFA], u32x4_t (&fb)[NKK][NFB],
+                      int stg, int q) SM_INLINE {
+    constexpr bool AT = decltype(akc)::value, BT = decltype(bkc)::value;
     const int kk = q / (NFA + NFB), r = q % (NFA + NFB);
     if (r < NFA) {
       const int sp = r / TI, i = r % TI;
-      if constexpr (a_km)
+      if constexpr (AT && sizeof(T) == 2)
+        fa[kk][r] = km_frag2(std::integral_constant<int, BMT>{}, a_tile(stg, sp), kmA, i, kk);
+      else if constexpr (AT)
         fa[kk][r] = km_frag(std::integral_constant<int, BMT>{}, a_tile(stg, sp), wm * WTM + 16 * i, kk);
       else
-        fa[kk][r] = *reinterpret_cast<const u32x4_t*>(a_tile(stg, sp) + fa_off[kk] + i * 16 * RB);
+        fa[kk][r] = *reinterpret_cast<const u32x4_t*>(a_tile(stg, sp) + (fa_off0 ^ (kk << 6)) + i * 16 * RB);
     } else {
       const int rb = r - NFA, sp = rb / TJ, j = rb % TJ;
-      if constexpr (b_km)
+      if constexpr (BT && sizeof(T) == 2)
+        fb[kk][rb] = km_frag2(std::integral_constant<int, BNT>{}, b_tile(stg, sp), kmB, j, kk);
+      else if constexpr (BT)
         fb[kk][rb] = km_frag(std::integral_constant<int, BNT>{}, b_tile(stg, sp), wn * WTN + 16 * j, kk);
       else
-        fb[kk][rb] = *reinterpret_cast<const u32x4_t*>(b_tile(stg, sp) + fb_off[kk] + j * 16 * RB);
+        fb[kk][rb] = *reinterpret_cast<const u32x4_t*>(b_tile(stg, sp) + (fb_off0 ^ (kk << 6)) + j * 16 * RB);
     }
   };
+  using kTrue = std::true_type;
+  using kFalse = std::false_type;
   auto ax_here = [&](int s) {
     if constexpr (EPI == E_UPDATE)
       return !ax_user && A.ca != 0.0f && s * BK < ax_k0 + 16 * TI && ax_k0 < (s + 1) * BK;
@@ -747,7 +839,29 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     if constexpr (EPI == E_SQUARE) return sq_lds && s * BK < sq_k0 + 16 * TI && sq_k0 < (s + 1) * BK;
     else return false;
   };
-  auto add_sq = [&](int s, int stg) SM_INLINE {
+  auto add_sq = [&](auto bkc, int s, int stg) SM_INLINE {
+    if constexpr (EPI == E_SQUARE && decltype(bkc)::value) {
+      // off the diagonal with upper-triangular storage the slab holds
+      // Y(k, n0 + c) k-major: 4 consecutive k of one column per lane are
+      // one transposing read
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int kb = sq_k0 + 16 * i - s * BK;
+        if (kb < 0 || kb >= BK) continue;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int c0 = wn * WTN + 16 * j;
+          const u32x2_t h = lds_read_tr16(
+              b_tile(stg, 0) + km_off<T, BNT>(kb + 4 * (lane >> 4) + ((lane & 15) >> 2),
+                                              2 * c0 + 8 * (lane & 3)));
+          acc[i][j][0] += sq_ratio * __uint_as_float(h[0] << 16);
+          acc[i][j][1] += sq_ratio * __uint_as_float(h[0] & 0xFFFF0000u);
+          acc[i][j][2] += sq_ratio * __uint_as_float(h[1] << 16);
+          acc[i][j][3] += sq_ratio * __uint_as_float(h[1] & 0xFFFF0000u);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int kb = sq_k0 + 16 * i - s * BK;   // this 16-row block's k offset in the slab
@@ -780,7 +894,9 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     for (int s = 0; s < NSTG - 1; ++s)
       if (s < nslab) issue(s);
 
-    for (int s = 0; s < nslab; ++s) {
+    // one slab with compile-time layouts; the layouts come in runs of the
+    // rotated slab order, one loop per run (as in the pipelined loop below)
+    auto slab = [&](auto akc, auto bkc, int s) SM_INLINE {
       // slab s has landed for this wave once at most the later slabs' loads
       // are outstanding; the barrier extends that to every wave and also
       // frees stage (s-1) % NSTG for the next fetch.
@@ -800,7 +916,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       // waits for every LDS DMA load issued before it
       u32x4_t fa[NKK][NFA], fb[NKK][NFB];
 #pragma unroll
-      for (int q = 0; q < NF; ++q) read_one(fa, fb, stg, q);
+      for (int q = 0; q < NF; ++q) read_one(akc, bkc, fa, fb, stg, q);
       __builtin_amdgcn_sched_barrier(0);
       if (s + NSTG - 1 < nslab) issue(s + NSTG - 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -813,12 +929,26 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       if constexpr (EPI == E_UPDATE) {
         // after the slab's MFMAs, when the fragment registers are free again
         __builtin_amdgcn_sched_barrier(0);
-        if (ax_here(s)) add_ax(s, stg);
+        if (ax_here(ks_of(s))) add_ax(ks_of(s), stg);
       }
       if constexpr (EPI == E_SQUARE) {
         __builtin_amdgcn_sched_barrier(0);
-        if (sq_here(s)) add_sq(s, stg);
+        if (sq_here(ks_of(s))) add_sq(bkc, ks_of(s), stg);
       }
+    };
+    int s = 0;
+    auto run = [&](auto akc, auto bkc, int end) SM_INLINE {
+      for (; s < end; ++s) slab(akc, bkc, s);
+    };
+    if constexpr (UPR && EPI == E_SQUARE) {
+      run(kFalse{}, kFalse{}, nslab - sB);
+      run(kTrue{}, kTrue{}, nslab - sB + sA);
+      run(kFalse{}, kTrue{}, nslab);
+    } else if constexpr (UPR) {
+      run(kFalse{}, kTrue{}, nslab - sA);
+      run(kTrue{}, kTrue{}, nslab);
+    } else {
+      run(std::integral_constant<bool, a_km>{}, std::integral_constant<bool, b_km>{}, nslab);
     }
   } else {
     // Software-pipelined k-loop: the fragments of slab s+1 are read into a
@@ -827,8 +957,8 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     // reads of slab s, barrier (then stage s % NSTG is free and slab s+1 is
     // in LDS for every wave), then the MFMAs of slab s interleaved with the
     // reads of slab s+1 and the fetch of slab s+NSTG into stage s % NSTG
-    // (the Gram fetches first; the update reads its transposed fragments
-    // first, see below).
+    // (a slab read with plain loads only is fetched first; k-major
+    // fragments are read before the fetch, see below).
     // After the last slab those reads hit a stale stage and are never used,
     // which keeps the MFMA sequence free of branches.  The slab count is
     // even (k is a multiple of 128).
@@ -840,12 +970,26 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     wait_vmcnt<(NSTG - 1) * LOADS>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    // The step's reads of slab s+1 use that slab's operand layouts (akc,
+    // bkc).  The compiler makes a transposing LDS read wait for every LDS
+    // DMA load issued before it (vmcnt(0)), which would wait for the fetch
+    // just issued; plain reads get no such wait.  So with k-major fragments
+    // those reads go with the first MFMAs, then the fetch, then the plain
+    // reads; with none the fetch goes first and a read follows every second
+    // MFMA.
+    // (the last step, lastc = true, only runs the MFMAs of its slab)
+    auto step = [&](auto akc, auto bkc, auto lastc, int s, u32x4_t (&ca)[NKK][NFA],
+                    u32x4_t (&cb)[NKK][NFB], u32x4_t (&na)[NKK][NFA],
+                    u32x4_t (&nb)[NKK][NFB]) SM_INLINE {
+      constexpr bool AT = decltype(akc)::value, BT = decltype(bkc)::value;
+      if constexpr (decltype(lastc)::value) {
 #pragma unroll
-    for (int q = 0; q < NF; ++q) read_one(fa0, fb0, 0, q);
-    if (ax_here(0)) add_ax(0, 0);
-    if (sq_here(0)) add_sq(0, 0);
-    auto step = [&](int s, u32x4_t (&ca)[NKK][NFA], u32x4_t (&cb)[NKK][NFB],
-                    u32x4_t (&na)[NKK][NFA], u32x4_t (&nb)[NKK][NFB]) SM_INLINE {
+        for (int t = 0; t < NM; ++t) {
+          const int kk = t / (TI * TJ), i = (t / TJ) % TI, j = t % TJ;
+          mfma_tile(&ca[kk][i], &cb[kk][j], i, j);
+        }
+        return;
+      }
       if (s + 1 < nslab) {
         // slab s+1 landed for this wave (later fetches may be in flight)
         if (s + NSTG - 1 < nslab) wait_vmcnt<(NSTG - 2) * LOADS>();
@@ -856,58 +1000,92 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       }
       const int nst = (s + 1) % NSTG;
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (!b_km) {
-        // fetch first, then the MFMAs with one read of slab s+1 after every
-        // second MFMA
+      if constexpr (!UPR && !AT && !BT) {
         if (s + 1 < nslab && s + NSTG < nslab) issue(s + NSTG);   // into stage s % NSTG, read out already
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < NM; ++t) {
           const int kk = t / (TI * TJ), i = (t / TJ) % TI, j = t % TJ;
           mfma_tile(&ca[kk][i], &cb[kk][j], i, j);
-          if ((t & 1) && (t >> 1) < NF) read_one(na, nb, nst, t >> 1);
+          if ((t & 1) && (t >> 1) < NF) read_one(akc, bkc, na, nb, nst, t >> 1);
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int q = NM / 2; q < NF; ++q) read_one(na, nb, nst, q);
+        for (int q = NM / 2; q < NF; ++q) read_one(akc, bkc, na, nb, nst, q);
       } else {
-        // The compiler makes a transposing LDS read wait for every LDS DMA
-        // load issued before it (vmcnt(0)), which would wait for the fetch
-        // just issued; plain reads get no such wait.  So the B fragments
-        // (transposing reads) go with the first MFMAs, then the fetch, then
-        // the A fragments.
+        // B's fragments, then A's, one with each of the first MFMAs, at the
+        // same points whatever the slab's layouts (so that every layout
+        // keeps the fragments in the same registers); the fetch goes after
+        // the last k-major read, or first when there is none.
         constexpr int NB = NKK * NFB, NA = NKK * NFA;
+        constexpr int NKM = (AT ? NA : 0) + (BT ? NB : 0);
         static_assert(NB + NA <= NM, "read schedule");
+        static_assert(BT || !AT, "A k-major implies B k-major");
         auto qb = [&](int u) { return (u / NFB) * (NFA + NFB) + NFA + u % NFB; };
         auto qa = [&](int u) { return (u / NFA) * (NFA + NFB) + u % NFA; };
+        if constexpr (NKM == 0) {
+          if (s + 1 < nslab && s + NSTG < nslab) issue(s + NSTG);
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int t = 0; t < NM; ++t) {
           const int kk = t / (TI * TJ), i = (t / TJ) % TI, j = t % TJ;
           mfma_tile(&ca[kk][i], &cb[kk][j], i, j);
-          if (t < NB) read_one(na, nb, nst, qb(t));
-          else if (t < NB + NA) read_one(na, nb, nst, qa(t - NB));
-          if (t == NB - 1 && s + 1 < nslab && s + NSTG < nslab) {
+          if (t < NB) read_one(akc, bkc, na, nb, nst, qb(t));
+          else if (t < NB + NA) read_one(akc, bkc, na, nb, nst, qa(t - NB));
+          if (NKM > 0 && t == NKM - 1 && s + 1 < nslab && s + NSTG < nslab) {
             __builtin_amdgcn_sched_barrier(0);
             issue(s + NSTG);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (s + 1 < nslab && ax_here(s + 1)) {
+      if (s + 1 < nslab && ax_here(ks_of(s + 1))) {
         __builtin_amdgcn_sched_barrier(0);
-        add_ax(s + 1, nst);
+        add_ax(ks_of(s + 1), nst);
       }
-      if (s + 1 < nslab && sq_here(s + 1)) {
+      if (s + 1 < nslab && sq_here(ks_of(s + 1))) {
         __builtin_amdgcn_sched_barrier(0);
-        add_sq(s + 1, nst);
+        add_sq(bkc, ks_of(s + 1), nst);
       }
     };
-    // (slab counts are even here: k is a multiple of 128 elements, and
-    // split-k ranges are even)
-    for (int s = 0; s < nslab; s += 2) {
-      step(s, fa0, fb0, fa1, fb1);
-      step(s + 1, fa1, fb1, fa0, fb0);
+    // Step s reads slab s+1 with that slab's layouts.  In the rotated slab
+    // order the layouts change only at even positions (sA and sB are
+    // multiples of the slabs per tile, an even number), and the first
+    // slabs take k along rows for A (and for B of the symmetric product).
+    // So the loop runs pairs of steps (s odd, s+1), which read slabs s+1
+    // and s+2 of one layout, one loop per layout, each with a single
+    // schedule (a change of schedule from step to step inside one loop made
+    // the register allocation spill).  Before them the reads of slab 0 and
+    // step 0 (reading slab 1), after them the last step.  (Slab counts are
+    // even here: k is a multiple of 128 elements, and split-k ranges are
+    // even.)
+    using kBkm = std::integral_constant<bool, b_km>;
+#pragma unroll
+    for (int q = 0; q < NF; ++q) read_one(kFalse{}, kBkm{}, fa0, fb0, 0, q);
+    if (ax_here(ks_of(0))) add_ax(ks_of(0), 0);
+    if (sq_here(ks_of(0))) add_sq(kFalse{}, ks_of(0), 0);
+    step(kFalse{}, kBkm{}, kFalse{}, 0, fa0, fb0, fa1, fb1);
+    const int last = nslab - 1;
+    int s = 1;
+    auto pairs = [&](auto akc, auto bkc, int end) SM_INLINE {
+      // pairs (s, s+1) with s + 1 < end (the first slab they read)
+      for (; s < last && s + 1 < end; s += 2) {
+        step(akc, bkc, kFalse{}, s, fa1, fb1, fa0, fb0);
+        step(akc, bkc, kFalse{}, s + 1, fa0, fb0, fa1, fb1);
+      }
+    };
+    if constexpr (UPR && EPI == E_SQUARE) {
+      pairs(kFalse{}, kFalse{}, nslab - sB);        // k >= 128 tn: both along rows
+      pairs(kTrue{}, kTrue{}, nslab - sB + sA);     // k < 128 tm: both k-major
+      pairs(kFalse{}, kTrue{}, nslab);              // B k-major
+    } else if constexpr (UPR) {
+      pairs(kFalse{}, kTrue{}, nslab - sA);         // k >= 128 tm: A along rows
+      pairs(kTrue{}, kTrue{}, nslab);
+    } else {
+      pairs(std::integral_constant<bool, a_km>{}, kBkm{}, nslab);
     }
+    step(kFalse{}, kBkm{}, kTrue{}, last, fa1, fb1, fa0, fb0);
   }
 
   // ---- epilogue (accumulator coordinates: acc_row / acc_col).  For the
@@ -958,7 +1136,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
                                                      offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
                                                      (int)Rp, wm, wn, lane, tid);
-    if (tm != tn)
+    if (tm != tn && !upper)
       stage_store_mirror<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
                                                          offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
                                                          (int)Rp, wm, wn, lane, tid);
@@ -976,7 +1154,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
         stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o2_hi, roff),
                                                          nullptr, Rp, m0, n0, (int)Rp, wm, wn,
                                                          lane, tid);
-        if (tm != tn)
+        if (tm != tn && !upper)
           stage_store_mirror<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o2_hi, roff),
                                                              nullptr, Rp, m0, n0, (int)Rp, wm, wn,
                                                              lane, tid);
@@ -998,8 +1176,16 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
           float x[4];
-          load_op4<T, SPLIT>(A.sq_hi, A.sq_lo, roff + (int64_t)(ac0 + j * 16) * Rp + ar0 + i * 16,
-                             x);
+          if (upper) {
+            // only the upper tile (tm, tn) is stored: Y(row + r, col) itself
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              x[r] = load_op<T, SPLIT>(A.sq_hi, A.sq_lo,
+                                       roff + (int64_t)(ar0 + i * 16 + r) * Rp + ac0 + j * 16);
+          } else {
+            load_op4<T, SPLIT>(A.sq_hi, A.sq_lo, roff + (int64_t)(ac0 + j * 16) * Rp + ar0 + i * 16,
+                               x);
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i][j][r] = A.cb * x[r] + A.cc * acc[i][j][r];
         }
@@ -1007,7 +1193,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
                                                      offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
                                                      (int)Rp, wm, wn, lane, tid);
-    if (tm != tn)
+    if (tm != tn && !upper)
       stage_store_mirror<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
                                                          offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
                                                          (int)Rp, wm, wn, lane, tid);
@@ -1180,7 +1366,8 @@ __global__ __launch_bounds__(256) void k_split_reduce(GemmArgs A) {
   const int64_t o = roff + (int64_t)(tm * TT + rb * RR + r) * Rp + tn * TT + c8;
   store_op4<T, SPLIT>(hi, lo, o, v0);
   store_op4<T, SPLIT>(hi, lo, o + 4, v1);
-  if (tm == tn) return;
+  // (bfloat16 Gram operands stored as upper-triangular tiles: no mirror)
+  if (tm == tn || (!RAW && sizeof(T) == 2 && SPLIT == 1 && A.upper)) return;
   // mirror: output row tn*TT + cc, columns tm*TT + rb*RR .. +RR-1 (8 per thread)
   const int cc = threadIdx.x >> 1, e0 = (threadIdx.x & 1) * 8;
   float w0[4], w1[4];

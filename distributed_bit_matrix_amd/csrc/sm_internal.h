@@ -129,6 +129,9 @@ struct Plan {
   // Newton-Schulz in Gram space (bfloat16 cubic, Frobenius scale):
   // X_K = Q_K X_0 with the iteration carried on Rp x Rp symmetric matrices
   bool gram_space = false;
+  // bfloat16 symmetric Rp x Rp operands (Gram operands, the quintic square,
+  // the Gram-space iterates) stored as their upper-triangular 128x128 tiles
+  bool upper = false;
   int64_t x_total = 0, r_total = 0, v_total = 0, c_total = 0, kp_total = 0;
   // workspace byte offsets (0 = absent)
   size_t off_x[2][2] = {{0, 0}, {0, 0}};  // [pingpong][hi/lo] (or f32 in [p][0])

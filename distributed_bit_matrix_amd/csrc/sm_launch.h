@@ -31,6 +31,12 @@ struct GemmArgs {
   const void* r_hi; const void* r_lo;   // FAM_R operand buffers
   const void* r2_hi; const void* r2_lo; // FAM_R2 operand buffers
   int32_t epi, out, xsrc, scal_pow;
+  // bfloat16 symmetric Rp x Rp operands and outputs (the R families; not
+  // the raw Gram) are stored as their upper-triangular 128x128 tiles only:
+  // symmetric outputs skip the mirror tile, and a product reading row
+  // block t of such an operand takes its k-slabs left of the diagonal
+  // (k < 128 t) from the stored tile above the diagonal, k-major.
+  int32_t upper;
   float mul, ca, cb, cc;
   void* o_hi; void* o_lo;          // E_OP / E_SQUARE (R family), O_X (X family)
   // E_OP, unsplit launches: also o2 = o2_a I + o2_b (the Gram operand) in
