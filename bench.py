@@ -78,9 +78,10 @@ def executed_ns_gflop(w) -> float:
     return tot * (3 if w.ns_precision == "bf16x3" else 1) / 1e9
 
 
-def gemm_traffic(workload):  # noqa: C901
-    """HBM bytes of one step's Newton-Schulz GEMM launches from the committed
-    counter summary, if it was taken on the current GEMM source; else None."""
+def gemm_traffic(workload, kind):
+    """HBM bytes (read + written) of one launch of the matrix-core kernel
+    `kind` in the sequential steps, from the committed counter summary, if
+    it was taken on the current GEMM source; else None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"k_gemm_{workload}_hbm_traffic.md")
     src = os.path.join(ROOT, "distributed_bit_matrix_amd", "csrc", "sm_gemm.hip")
@@ -95,7 +96,7 @@ def gemm_traffic(workload):  # noqa: C901
     if fields.get("gemm_source_sha256") != digest:
         return None
     try:
-        return int(fields["gemm_traffic_bytes_per_step"])
+        return int(fields[f"traffic_bytes_per_launch_{kind}"])
     except (KeyError, ValueError):
         return None
 
@@ -454,7 +455,7 @@ def main():
              "update": "k_gemm update / final product (E_UPDATE)"}
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": gemm_traffic(w.name), "traffic_unit": "bytes per step",
+                "traffic": gemm_traffic(w.name, dom), "traffic_unit": "HBM bytes per launch",
                 "kernel": names[dom] + f": one launch covers all {len(w.mats)} matrices",
                 "work_per_launch_gflop": round(lf[dom] / 1e9, 3),
                 "work": {"square": "2 Rp^3 flops per matrix (Rp = the short side padded "

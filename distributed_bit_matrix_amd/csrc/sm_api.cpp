@@ -128,6 +128,16 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
     q.kp_off = kp;
     kp += gemm_sym_kpart_floats(q.Rp, q.ks);
   }
+  // Upper-triangular storage needs every product that reads a symmetric
+  // operand to take its slabs left of the diagonal k-major; the 128 x 256
+  // update tile (long bfloat16 updates) reads whole rows, so a set with
+  // such an update keeps mirrored storage.
+  for (int i = 0; i < nm && P.upper; ++i) {
+    const MatPlan& q = mp[i];
+    int tm = 0, tn = 0;
+    gemm_tile(P.precision, E_UPDATE, q.Rp, q.tall ? q.Mp : q.Np, q.Rp, &tm, &tn);
+    if (tn != tm) P.upper = false;
+  }
   P.x_total = x; P.r_total = r2; P.v_total = v; P.c_total = c; P.kp_total = kp;
   const size_t opb = P.precision == P_F32 ? 4 : 2;   // bytes per operand part
   const bool split = P.precision == P_BF16X3;

@@ -442,16 +442,23 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   // Upper-triangular storage of the bfloat16 symmetric operands (A.upper):
   // row block t of a stored Rp x Rp operand has its k-slabs left of the
   // diagonal (k < 128 t) only in the tile above the diagonal, so those
-  // slabs are fetched k-major from there: the A operand of the symmetric
-  // product and of the update (row block tm) below slab sA, the B operand
-  // of the symmetric product (row block tn) below slab sB.  For an upper
-  // tile tm <= tn, so sA <= sB.
+  // slabs are fetched k-major from there.  The diagonal tile is itself
+  // symmetric and may be read either way, so the k-major range includes
+  // it: the A operand of the symmetric product and of the update (row block
+  // tm) is k-major below slab sA = TPS (tm + 1), the B operand of the
+  // symmetric product (row block tn) below sB = TPS (tn + 1), with TPS
+  // slabs per 128-wide tile.  Every block then starts with both operands
+  // k-major, meets the layouts in the same order, and reads k in natural
+  // order (blocks sharing an operand block stay in step through L2).  With
+  // mirrored storage (A.upper = 0) the same reads are valid, since every
+  // tile is present and the operands are symmetric: A.upper only decides
+  // whether symmetric outputs also write their mirror tiles.
   constexpr bool UPK = sizeof(T) == 2 && SPLIT == 1;
-  constexpr bool UPR = UPK && (EPI == E_SQUARE || EPI == E_UPDATE);
+  constexpr bool UPR = UPK && (EPI == E_SQUARE || EPI == E_UPDATE) && BNT == kTileSym;
   const bool upper = UPK && A.upper != 0;
   constexpr int TPS = kTileSym / (RB / (int)sizeof(T));   // slabs per 128-wide tile
-  const int sA = UPR && upper ? tm * TPS : 0;
-  const int sB = UPR && EPI == E_SQUARE && upper ? tn * TPS : 0;
+  const int sA = UPR ? (tm + 1) * TPS : 0;
+  const int sB = UPR && EPI == E_SQUARE ? (tn + 1) * TPS : 0;
   // Accumulator layout.  Register r of lane l in tile (i, j) holds C(row, col):
   //   C tiles:       row = m0 + wm*WTM + 16 i + 4 (l/16) + r,  col = n0 + wn*WTN + 16 j + l % 16
   //   transposed:    row = m0 + wm*WTM + 16 i + l % 16,  col = n0 + wn*WTN + 16 j + 4 (l/16) + r
@@ -518,7 +525,8 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   // elements with 2 or 4 loads per wave.
   constexpr bool UPB = UPR && EPI == E_SQUARE;
   // the update's S operand (always k-major) uses the same scheme when its
-  // tile is 128 wide
+  // tile is 128 wide.  (The 128 x 256 update reads its A operand whole:
+  // the host keeps mirrored storage for sets that use it.)
   constexpr bool BKC = sizeof(T) == 2 && b_km && BNT == 128;
   static_assert(!UPR || (BMT == 128 && (QA == 2 || QA == 4)), "k-major offset scheme");
   static_assert(!(UPB || BKC) || (BNT == 128 && (QB == 2 || QB == 4)), "k-major offset scheme");
@@ -597,14 +605,6 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     }
   }
 
-  // With upper-triangular storage the k-slabs run in rotated order,
-  // starting at the diagonal tile's column (srot = sB for the symmetric
-  // product, sA for the update) and wrapping around: every block then
-  // starts with slabs of one layout (k along rows for both operands of the
-  // symmetric product, for A of the update), and the loop below meets the
-  // layouts in a fixed order.  Loop position s reads k-slab ks_of(s).
-  const int srot = UPR ? (EPI == E_SQUARE ? sB : sA) : 0;
-  auto ks_of = [&](int s) SM_INLINE { const int k = s + srot; return k >= nslab ? k - nslab : k; };
 
   // LDS stage: [A split 0][A split 1..][B split 0][B split 1..]
   auto a_tile = [&](int st, int sp) -> char* { return smem + st * STAGEB + sp * ATILE; };
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     }
   };
   auto issue = [&](int sq) SM_INLINE {
-    const int st = sq % NSTG, s = ks_of(sq);
+    const int st = sq % NSTG, s = sq;
 #pragma unroll
     for (int sp = 0; sp < SPLIT; ++sp) {
       issue_op(a_src[sp], aoff, aoff_t, a_kst, lda, UPR && s < sA, a_tile(st, sp) + wave * QA * 1024,
@@ -897,6 +897,11 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     // one slab with compile-time layouts; the layouts come in runs of the
     // rotated slab order, one loop per run (as in the pipelined loop below)
     auto slab = [&](auto akc, auto bkc, int s) SM_INLINE {
+      // the k-major read addresses derive from one register per operand;
+      // redefining it opaquely here keeps the derived addresses from being
+      // hoisted out of the loops and held in registers
+      if constexpr (decltype(akc)::value && sizeof(T) == 2) asm volatile("" : "+v"(kmA));
+      if constexpr (decltype(bkc)::value && sizeof(T) == 2) asm volatile("" : "+v"(kmB));
       // slab s has landed for this wave once at most the later slabs' loads
       // are outstanding; the barrier extends that to every wave and also
       // frees stage (s-1) % NSTG for the next fetch.
@@ -929,11 +934,11 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       if constexpr (EPI == E_UPDATE) {
         // after the slab's MFMAs, when the fragment registers are free again
         __builtin_amdgcn_sched_barrier(0);
-        if (ax_here(ks_of(s))) add_ax(ks_of(s), stg);
+        if (ax_here(s)) add_ax(s, stg);
       }
       if constexpr (EPI == E_SQUARE) {
         __builtin_amdgcn_sched_barrier(0);
-        if (sq_here(ks_of(s))) add_sq(bkc, ks_of(s), stg);
+        if (sq_here(s)) add_sq(bkc, s, stg);
       }
     };
     int s = 0;
@@ -941,12 +946,12 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       for (; s < end; ++s) slab(akc, bkc, s);
     };
     if constexpr (UPR && EPI == E_SQUARE) {
-      run(kFalse{}, kFalse{}, nslab - sB);
-      run(kTrue{}, kTrue{}, nslab - sB + sA);
-      run(kFalse{}, kTrue{}, nslab);
+      run(kTrue{}, kTrue{}, sA);
+      run(kFalse{}, kTrue{}, sB);
+      run(kFalse{}, kFalse{}, nslab);
     } else if constexpr (UPR) {
-      run(kFalse{}, kTrue{}, nslab - sA);
-      run(kTrue{}, kTrue{}, nslab);
+      run(kTrue{}, kTrue{}, sA);
+      run(kFalse{}, kTrue{}, nslab);
     } else {
       run(std::integral_constant<bool, a_km>{}, std::integral_constant<bool, b_km>{}, nslab);
     }
@@ -1040,32 +1045,33 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (s + 1 < nslab && ax_here(ks_of(s + 1))) {
+      if (s + 1 < nslab && ax_here(s + 1)) {
         __builtin_amdgcn_sched_barrier(0);
-        add_ax(ks_of(s + 1), nst);
+        add_ax(s + 1, nst);
       }
-      if (s + 1 < nslab && sq_here(ks_of(s + 1))) {
+      if (s + 1 < nslab && sq_here(s + 1)) {
         __builtin_amdgcn_sched_barrier(0);
-        add_sq(bkc, ks_of(s + 1), nst);
+        add_sq(bkc, s + 1, nst);
       }
     };
-    // Step s reads slab s+1 with that slab's layouts.  In the rotated slab
-    // order the layouts change only at even positions (sA and sB are
-    // multiples of the slabs per tile, an even number), and the first
-    // slabs take k along rows for A (and for B of the symmetric product).
-    // So the loop runs pairs of steps (s odd, s+1), which read slabs s+1
-    // and s+2 of one layout, one loop per layout, each with a single
-    // schedule (a change of schedule from step to step inside one loop made
-    // the register allocation spill).  Before them the reads of slab 0 and
-    // step 0 (reading slab 1), after them the last step.  (Slab counts are
-    // even here: k is a multiple of 128 elements, and split-k ranges are
-    // even.)
+    // Step s reads slab s+1 with that slab's layouts, which change only at
+    // even slabs (sA and sB are multiples of the slabs per tile, an even
+    // number), and slabs 0 and 1 are k-major for both operands whenever
+    // the operands are symmetric.  So the loop runs pairs of steps (s odd,
+    // s+1), which read slabs s+1 and s+2 of one layout, one loop per layout,
+    // each with a single schedule (a change of schedule from step to step
+    // inside one loop made the register allocation spill).  Before them the
+    // reads of slab 0 and step 0 (reading slab 1), after them the last step.
+    // (Slab counts are even here: k is a multiple of 128 elements, and
+    // split-k ranges are even.)
     using kBkm = std::integral_constant<bool, b_km>;
+    using kA0 = std::integral_constant<bool, UPR || a_km>;
+    using kB0 = std::integral_constant<bool, UPR || b_km>;
 #pragma unroll
-    for (int q = 0; q < NF; ++q) read_one(kFalse{}, kBkm{}, fa0, fb0, 0, q);
-    if (ax_here(ks_of(0))) add_ax(ks_of(0), 0);
-    if (sq_here(ks_of(0))) add_sq(kFalse{}, ks_of(0), 0);
-    step(kFalse{}, kBkm{}, kFalse{}, 0, fa0, fb0, fa1, fb1);
+    for (int q = 0; q < NF; ++q) read_one(kA0{}, kB0{}, fa0, fb0, 0, q);
+    if (ax_here(0)) add_ax(0, 0);
+    if (sq_here(0)) add_sq(kB0{}, 0, 0);
+    step(kA0{}, kB0{}, kFalse{}, 0, fa0, fb0, fa1, fb1);
     const int last = nslab - 1;
     int s = 1;
     auto pairs = [&](auto akc, auto bkc, int end) SM_INLINE {
@@ -1076,12 +1082,12 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       }
     };
     if constexpr (UPR && EPI == E_SQUARE) {
-      pairs(kFalse{}, kFalse{}, nslab - sB);        // k >= 128 tn: both along rows
-      pairs(kTrue{}, kTrue{}, nslab - sB + sA);     // k < 128 tm: both k-major
-      pairs(kFalse{}, kTrue{}, nslab);              // B k-major
+      pairs(kTrue{}, kTrue{}, sA);      // k < 128 (tm + 1): both k-major
+      pairs(kFalse{}, kTrue{}, sB);     // B k-major
+      pairs(kFalse{}, kFalse{}, nslab);
     } else if constexpr (UPR) {
-      pairs(kFalse{}, kTrue{}, nslab - sA);         // k >= 128 tm: A along rows
-      pairs(kTrue{}, kTrue{}, nslab);
+      pairs(kTrue{}, kTrue{}, sA);      // k < 128 (tm + 1): A k-major
+      pairs(kFalse{}, kTrue{}, nslab);
     } else {
       pairs(std::integral_constant<bool, a_km>{}, kBkm{}, nslab);
     }

@@ -90,6 +90,36 @@ def test_polar_quintic(shape, precision):
     check(X, B.HParams(K=5, scale="spectral", P=10, coeffs=QUINTIC, precision=precision))
 
 
+@pytest.mark.parametrize("shape", [(256, 512), (512, 256), (384, 640)])
+def test_polar_quintic_bf16(shape):
+    # Plain bfloat16 quintic (its squares run on the symmetric product with
+    # upper-triangular operands): held to the polar bound only, since plain
+    # bfloat16 leaves too many undecidable signs for the sign gate (a CPU
+    # emulation of these shapes gave a largest error of 4e-3 to 6e-3)
+    X = momentum_like(shape, 4)
+    u0 = np.random.default_rng(7).standard_normal(min(shape)).astype(np.float32)
+    check(X, B.HParams(K=5, scale="spectral", P=10, coeffs=QUINTIC, precision="bf16"), u0=u0,
+          gate=False)
+
+
+@pytest.mark.parametrize("shape", [(256, 512), (512, 256), (384, 640), (200, 1000), (64, 147)])
+@pytest.mark.parametrize("form", ["gram_space", "iterate", "spectral"])
+def test_polar_bf16_mirrored_storage(shape, form, monkeypatch):
+    # bfloat16 symmetric operands are stored as upper-triangular tiles by
+    # default; with SIGNMUON_SYM_STORAGE=full every symmetric output also
+    # writes its mirror tiles and products read whole rows: held to the
+    # same gates
+    monkeypatch.setenv("SIGNMUON_SYM_STORAGE", "full")
+    if form == "iterate":
+        monkeypatch.setenv("SIGNMUON_NS_FORM", "iterate")
+    X = momentum_like(shape, 8)
+    if form == "spectral":
+        u0 = np.random.default_rng(9).standard_normal(min(shape)).astype(np.float32)
+        check(X, B.HParams(K=5, scale="spectral", P=5, precision="bf16"), u0=u0)
+    else:
+        check(X, B.HParams(K=5, scale="fro", precision="bf16"))
+
+
 # Long k with few Gram tiles: the Gram (and the raw Gram of the spectral
 # scale) is split along k into partial tiles that a second kernel sums.
 SPLIT_K = [((128, 4096), "bf16", "fro", (1.5, -0.5, 0.0)),

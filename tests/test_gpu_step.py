@@ -281,6 +281,22 @@ def test_step_nanogpt_iterate_form(monkeypatch):
         W, Moms = out["Wn"], out["Mom"]
 
 
+@pytest.mark.parametrize("name", ["nanogpt", "resnet50"])
+def test_step_mirrored_storage(name, monkeypatch):
+    # bfloat16 symmetric operands are stored as upper-triangular tiles by
+    # default; the mirrored storage is held to the same gates
+    monkeypatch.setenv("SIGNMUON_SYM_STORAGE", "full")
+    w, _, T = SMALL[name]
+    hp = hparams(w)
+    st = GpuState(w, hp)
+    W = WL.init_weights(w)
+    Moms = [np.zeros(w.d) for _ in range(w.M)]
+    u0s = WL.power_start(w) if w.scale == "spectral" else None
+    for t in range(T):
+        out = check_step(w, st, hp, W, Moms, gradients(w, t, w.M), u0s)
+        W, Moms = out["Wn"], out["Mom"]
+
+
 # Sizes whose entry counts are odd: matrices start at unaligned offsets (no
 # 16-byte vector access of W), widths are not multiples of 32 (signs packed
 # by the separate pass), and the vote covers partial 2048-entry stretches.
