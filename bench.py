@@ -321,7 +321,8 @@ class Run:
 
     def measure_launches(self, K):
         """K sequential instrumented steps: mean microseconds per launch of
-        each matrix-core kernel kind (gram, square, update) and per step."""
+        each matrix-core kernel kind (gram, square, update; the kernel's own
+        start-to-stop time) and per step."""
         from distributed_bit_matrix_amd import binding as B
         if self.plan_seq is None:
             self.plan_seq = B.StepPlan(self.layout, self.hp, self.w.post_vote, device=self.dev,
@@ -355,8 +356,10 @@ def workload_metrics(w, d, elapsed, K, phase_us):
     """Steps/s, the Newton-Schulz phase as algorithmic and executed TFLOP/s
     against the matrix-core peak, and vote / momentum GB/s against HBM."""
     peak = PEAK_F32_TFLOPS if w.ns_precision == "f32" else PEAK_BF16_TFLOPS
+    # (the matrix-core launches and the gaps between them: launch latency and
+    # split-k reductions)
     gemm_us = phase_us.get("gemm", 0.0) + phase_us.get("gram", 0.0) + \
-        phase_us.get("square", 0.0) + phase_us.get("update", 0.0)
+        phase_us.get("square", 0.0) + phase_us.get("update", 0.0) + phase_us.get("gap", 0.0)
     wbytes = 2 if w.w_dtype == "bf16" else 4
     sign_bytes = 1.0 if w.encoding == "ternary" else 1 / 8.0
     out = {"value": round(K / elapsed, 3), "unit": "steps/s",

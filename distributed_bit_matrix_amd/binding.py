@@ -36,7 +36,7 @@ EXPORTS = (
     "signmuon_polar_ns_static",
 )
 PHASES = {0: "start", 1: "momentum", 2: "prescale", 3: "gemm", 4: "pack", 5: "vote",
-          6: "gram", 7: "square", 8: "update"}
+          6: "gram", 7: "square", 8: "update", 9: "gap"}
 
 
 class SignMuonError(RuntimeError):

@@ -334,6 +334,25 @@ hipError_t mark(sm_profile* prof, int kind, hipStream_t s) {
   return e;
 }
 
+// Start and stop events of one matrix-core launch (taken by the kernel
+// itself): the interval up to its start is recorded as a gap, the kernel
+// as `kind`.  Both null without a profile or room for two events.
+struct KernelEvents { hipEvent_t t0 = nullptr, t1 = nullptr; };
+KernelEvents kernel_events(sm_profile* prof, int kind) {
+  KernelEvents k;
+  if (!prof || prof->count + 2 > prof->capacity) return k;
+  k.t0 = prof->events[prof->count];
+  prof->kinds[prof->count++] = SM_PHASE_GAP;
+  k.t1 = prof->events[prof->count];
+  prof->kinds[prof->count++] = kind;
+  return k;
+}
+hipError_t launch_gemm_timed(int precision, const GemmArgs& a, hipStream_t s, sm_profile* prof,
+                             int kind) {
+  const KernelEvents k = kernel_events(prof, kind);
+  return launch_gemm(precision, a, s, k.t0, k.t1);
+}
+
 // ---------------------------------------------------------------------------
 // PolarNS pipeline over all matrices of a plan, starting from the padded
 // operand copies in x[0] with partial sums in part (Frobenius).
@@ -445,9 +464,8 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
         if (gram_writes_q1(P, groups)) {
           a.o2_hi = B.gs[4]; a.o2_a = hp->ns_a; a.o2_b = hp->ns_b;
         }
-        return launch_gemm(prec, a, s);
+        return launch_gemm_timed(prec, a, s, io.prof, SM_PHASE_GRAM);
       }));
-      HIP_TRY(mark(io.prof, SM_PHASE_GRAM, s));
       return SM_OK;
     });
     return;
@@ -460,9 +478,8 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
       a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
       a.epi = E_RAW; a.o_raw = B.araw;
       a.kpart = B.kpart;
-      return launch_gemm(prec, a, s);
+      return launch_gemm_timed(prec, a, s, io.prof, SM_PHASE_GRAM);
     }));
-    HIP_TRY(mark(io.prof, SM_PHASE_GRAM, s));
     return SM_OK;
   });
   // power iteration: P >= 1 steps alternating va / vb (P is validated); the
@@ -520,7 +537,7 @@ sm_status run_pre_scale(const Plan& P, const std::vector<MatPlan>& mp,
 // B = b A + c A^2 from the operand A (quintic).
 hipError_t run_square(const Plan& P, const std::vector<MatPlan>& mp,
                       const std::vector<Group>& groups, const sm_hparams* hp,
-                      Bufs& B, hipStream_t s) {
+                      Bufs& B, hipStream_t s, sm_profile* prof) {
   return for_launches(groups, [&](Group& g) {
     const MatPlan& q = mp[g.idx0];
     g.gm = g.gn = g.gk = (int32_t)q.Rp;
@@ -535,7 +552,7 @@ hipError_t run_square(const Plan& P, const std::vector<MatPlan>& mp,
     a.epi = E_SQUARE; a.upper = P.upper; a.cb = hp->ns_b; a.cc = hp->ns_c;
     a.sq_hi = B.a[0]; a.sq_lo = B.a[1];
     a.o_hi = B.b[0]; a.o_lo = B.b[1];
-    return launch_gemm(P.precision, a, s);
+    return launch_gemm_timed(P.precision, a, s, prof, SM_PHASE_SQUARE);
   });
 }
 
@@ -579,9 +596,8 @@ void gram_space_stages(const Plan& P, const std::vector<MatPlan>& mp,
         a.epi = E_SQUARE; a.upper = P.upper; a.cb = ca; a.cc = cb;
         a.sq_hi = Y;
         a.o_hi = O;
-        return launch_gemm(prec, a, s);
+        return launch_gemm_timed(prec, a, s, io.prof, SM_PHASE_SQUARE);
       }));
-      HIP_TRY(mark(io.prof, SM_PHASE_SQUARE, s));
       return SM_OK;
     });
   };
@@ -609,7 +625,6 @@ void gram_space_stages(const Plan& P, const std::vector<MatPlan>& mp,
       // pass 0: matrices using the requested final output; pass 1: the
       // unfusable ones writing U into the workspace
       if (pass == 1 && io.final_out != O_BITS) break;
-      int launched = 0;
       HIP_TRY(for_launches(groups, [&](Group& g) {
         const MatPlan& q = mp[g.idx0];
         if (io.final_out == O_BITS && fusable[g.idx0] != (pass == 0)) return false;
@@ -634,9 +649,8 @@ void gram_space_stages(const Plan& P, const std::vector<MatPlan>& mp,
           a.W = io.W; a.w_bf16 = io.w_bf16; a.eta = io.eta;
           a.status = io.status;
         }
-        return launch_gemm(prec, a, s);
-      }, &launched));
-      if (launched) HIP_TRY(mark(io.prof, SM_PHASE_UPDATE, s));
+        return launch_gemm_timed(prec, a, s, io.prof, SM_PHASE_UPDATE);
+      }));
     }
     return SM_OK;
   });
@@ -674,16 +688,14 @@ void ns_stages(const Plan& P, const std::vector<MatPlan>& mp,
           a.kpart = B.kpart;
           a.o_hi = P.quintic ? B.a[0] : B.b[0];
           a.o_lo = P.quintic ? B.a[1] : B.b[1];
-          return launch_gemm(prec, a, s);
+          return launch_gemm_timed(prec, a, s, io.prof, SM_PHASE_GRAM);
         }));
-        HIP_TRY(mark(io.prof, SM_PHASE_GRAM, s));
         return SM_OK;
       });
     }
     if (P.quintic) {
       out.push_back([&, hp, s]() -> sm_status {
-        HIP_TRY(run_square(P, mp, groups, hp, B, s));
-        HIP_TRY(mark(io.prof, SM_PHASE_SQUARE, s));
+        HIP_TRY(run_square(P, mp, groups, hp, B, s, io.prof));
         return SM_OK;
       });
     }
@@ -694,8 +706,7 @@ void ns_stages(const Plan& P, const std::vector<MatPlan>& mp,
         // pass 0: matrices using the requested final output; pass 1: the
         // unfusable ones writing U into the workspace (only when last).
         if (pass == 1 && !(last && io.final_out == O_BITS)) break;
-        int launched = 0;
-        HIP_TRY(for_launches(groups, [&](Group& g) {
+          HIP_TRY(for_launches(groups, [&](Group& g) {
           const MatPlan& q = mp[g.idx0];
           if (last && io.final_out == O_BITS && fusable[g.idx0] != (pass == 0)) return false;
           g.gm = (int32_t)q.Rp; g.gn = (int32_t)(q.tall ? q.Mp : q.Np);
@@ -724,9 +735,8 @@ void ns_stages(const Plan& P, const std::vector<MatPlan>& mp,
             a.W = io.W; a.w_bf16 = io.w_bf16; a.eta = io.eta;
             a.status = io.status;
           }
-          return launch_gemm(prec, a, s);
-        }, &launched));
-        if (launched) HIP_TRY(mark(io.prof, SM_PHASE_UPDATE, s));
+          return launch_gemm_timed(prec, a, s, io.prof, SM_PHASE_UPDATE);
+        }));
       }
       return SM_OK;
     });

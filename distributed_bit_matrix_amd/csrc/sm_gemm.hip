@@ -25,6 +25,8 @@
 #include <cstring>
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "sm_internal.h"
 #include "sm_launch.h"
 
@@ -1488,7 +1490,7 @@ void gemm_tile(int precision, int epi, int64_t gm, int64_t gn, int64_t gk, int* 
 }
 
 template <typename T, int SPLIT, int EPI, bool WIDE = false>
-static hipError_t launch_one(const GemmArgs& args, hipStream_t s) {
+static hipError_t launch_one(const GemmArgs& args, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   using C = Cfg<T, SPLIT, EPI, WIDE>;
   // the pipelined k-loop fills all NSTG stages before its first slab: every
   // block needs at least NSTG slabs (and, pipelined, an even count)
@@ -1503,18 +1505,22 @@ static hipError_t launch_one(const GemmArgs& args, hipStream_t s) {
     }
     if (fewest < C::NSTG || (C::PIPE && (fewest & 1))) return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE, C::PIPE, C::TRACC>),
-                     dim3(args.G.total_blocks), dim3(128 * C::WM), C::lds(), s, args);
+  auto kern = k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE, C::PIPE, C::TRACC>;
+  if (t0 || t1)   // the events take the kernel's own start and stop times
+    hipExtLaunchKernelGGL(kern, dim3(args.G.total_blocks), dim3(128 * C::WM), (uint32_t)C::lds(), s,
+                          t0, t1, 0, args);
+  else
+    hipLaunchKernelGGL(kern, dim3(args.G.total_blocks), dim3(128 * C::WM), C::lds(), s, args);
   return hipGetLastError();
 }
 
 template <typename T, int SPLIT>
-static hipError_t launch_epi(const GemmArgs& args, hipStream_t s) {
+static hipError_t launch_epi(const GemmArgs& args, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   switch (args.epi) {
-    case E_RAW: return launch_one<T, SPLIT, E_RAW>(args, s);
-    case E_OP: return launch_one<T, SPLIT, E_OP>(args, s);
-    case E_SQUARE: return launch_one<T, SPLIT, E_SQUARE>(args, s);
-    default: return launch_one<T, SPLIT, E_UPDATE>(args, s);
+    case E_RAW: return launch_one<T, SPLIT, E_RAW>(args, s, t0, t1);
+    case E_OP: return launch_one<T, SPLIT, E_OP>(args, s, t0, t1);
+    case E_SQUARE: return launch_one<T, SPLIT, E_SQUARE>(args, s, t0, t1);
+    default: return launch_one<T, SPLIT, E_UPDATE>(args, s, t0, t1);
   }
 }
 
@@ -1575,7 +1581,8 @@ static hipError_t launch_reduce(const GemmArgs& args, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s) {
+hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s, hipEvent_t t0,
+                       hipEvent_t t1) {
   if (args.G.total_blocks <= 0) return hipSuccess;
   // every group of a launch carries the same column tile (the host splits
   // launches by it)
@@ -1600,10 +1607,10 @@ hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s) {
     }
   }
   hipError_t e;
-  if (tile == CfgWide::BNT) return launch_one<bf16_t, 1, E_UPDATE, true>(args, s);
-  if (precision == P_F32) e = launch_epi<float, 1>(args, s);
-  else if (precision == P_BF16X3) e = launch_epi<bf16_t, 2>(args, s);
-  else e = launch_epi<bf16_t, 1>(args, s);
+  if (tile == CfgWide::BNT) return launch_one<bf16_t, 1, E_UPDATE, true>(args, s, t0, t1);
+  if (precision == P_F32) e = launch_epi<float, 1>(args, s, t0, t1);
+  else if (precision == P_BF16X3) e = launch_epi<bf16_t, 2>(args, s, t0, t1);
+  else e = launch_epi<bf16_t, 1>(args, s, t0, t1);
   if (e != hipSuccess || !split) return e;
   if (args.epi == E_RAW) return launch_reduce<float, 1, true>(args, s);
   if (precision == P_F32) return launch_reduce<float, 1, false>(args, s);

@@ -54,7 +54,10 @@ struct GemmArgs {
   float* kpart;                    // split-k partial tiles (groups with ksplit > 1)
 };
 
-hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s);
+// t0 / t1 (optional): events that take the start and stop time of the GEMM
+// kernel itself (not of a split-k reduction that follows it)
+hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s,
+                       hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t gemm_set_attributes();
 // Block tile (tm rows x tn columns) of a GEMM with output gm x gn and
 // depth gk; every group of one launch must carry the same tn in

@@ -576,3 +576,83 @@ def test_all_workers_on_gpu(name, chain_mode):
                          None if u0s is None else u0s[i], i)
         checked += 1
     assert checked == len(mats)
+
+
+def _events(n):
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = (ctypes.c_void_p * n)()
+    for i in range(n):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs[i] = e.value
+    return hip, evs
+
+
+@pytest.mark.parametrize("name,concurrent", [("nanogpt", True), ("nanogpt", False),
+                                             ("resnet50", False)])
+def test_step_profiled_matches_plain(name, concurrent, monkeypatch):
+    # signmuon_step_profiled does the same work as signmuon_step (bit-exact
+    # results) and records its events in order: phases, and without the
+    # concurrent chains one gap + kernel pair per matrix-core launch
+    import ctypes
+    if concurrent:
+        monkeypatch.setenv("SIGNMUON_CHAIN_MIN_GFLOP", "0")   # chains even for this small set
+    w, _, _ = SMALL[name]
+    print(f"profiled step {name} concurrent={concurrent}", flush=True)
+    hp = hparams(w)
+    layout, d, words = B.default_layout(w.mats)
+    plan = B.StepPlan(layout, hp, w.post_vote, concurrent=concurrent)
+    wdt = torch.bfloat16 if w.w_dtype == "bf16" else torch.float32
+    W0 = torch.from_numpy(WL.init_weights(w)).cuda().to(wdt)
+    G = torch.from_numpy(WL.gradient(w, 0, 0)).cuda()
+    bits0 = torch.from_numpy(WL.random_bits(w, w.M).view(np.int32)).cuda()
+    u0 = (torch.from_numpy(np.concatenate(WL.power_start(w))).cuda()
+          if w.scale == "spectral" else None)
+    outs = []
+    cap = 256
+    hip, evs = _events(cap)
+    kinds = (ctypes.c_int32 * cap)()
+    for profiled in (False, True):
+        W = W0.clone()
+        Mom = torch.zeros(d, dtype=torch.float32, device="cuda")
+        bits = bits0.clone()
+        for _ in range(2):
+            if profiled:
+                p = B.SmProfile()
+                p.events = ctypes.cast(evs, ctypes.POINTER(ctypes.c_void_p))
+                p.kinds = ctypes.cast(kinds, ctypes.POINTER(ctypes.c_int32))
+                p.capacity = cap
+                p.count = 0
+                plan.profiled(p, G, W, Mom, bits, words, w.M, 0, u0=u0)
+            else:
+                plan(G, W, Mom, bits, words, w.M, 0, u0=u0)
+        torch.cuda.synchronize()
+        outs.append((W.view(torch.int16 if wdt == torch.bfloat16 else torch.int32).cpu(),
+                     Mom.view(torch.int32).cpu(), bits.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    n = p.count
+    assert 2 < n < cap
+    ks = [kinds[i] for i in range(n)]
+    assert ks[0] == 0 and all(k in B.PHASES for k in ks)
+    ms = ctypes.c_float()
+    for i in range(1, n):
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(evs[i - 1]),
+                                       ctypes.c_void_p(evs[i])) == 0
+        assert ms.value >= -1e-3
+    kernel = [k for k in ks if k in (6, 7, 8)]
+    if concurrent and name == "nanogpt":
+        assert not kernel and 3 in ks                # one Newton-Schulz phase
+    else:
+        assert kernel and 3 not in ks
+        # every kernel interval opens with a gap
+        for i, k in enumerate(ks):
+            if k in (6, 7, 8):
+                assert ks[i - 1] == 9
+    for i in range(cap):
+        hip.hipEventDestroy(ctypes.c_void_p(evs[i]))
