@@ -1308,18 +1308,16 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   }
   st = run_pre_scale(Pn, mp, groups, &hn, B, io, tern ? 2 : 1, stream);
   if (st != SM_OK) return st;
-  {
-    ScaledOutArgs so;
-    std::memset(&so, 0, sizeof(so));
-    so.precision = P.precision; so.from_op = 1; so.apply = 1; so.w_bf16 = w_bf16;
-    so.x_hi = B.x[0][0]; so.x_lo = B.x[0][1]; so.scal = B.scal;
-    so.W = W; so.eta = hp->eta; so.status = B.status;
-    HIP_TRY(for_launches(groups, [&](Group& g) {
-      g.blocks_per_mat = (int32_t)(((int64_t)g.rows * g.cols + kChunk - 1) / kChunk);
-      return true;
-    }, [&](const Groups& Gs) { so.G = Gs; return launch_scaled_out(so, stream); }));
-    return SM_OK;
-  }
+  // the update votes again from the sign buffers (the M buffers cost M/8
+  // (packed) or M bytes per entry, and are read in the caller's layout,
+  // whereas the operand copy of a tall matrix is transposed), scaled by c
+  va.mode = VA_APPLY;
+  va.scal = B.scal;
+  HIP_TRY(for_launches(groups, vote_fill, [&](const Groups& Gs) {
+    va.G = Gs; return launch_vote_groups(va, stream);
+  }));
+  HIP_TRY(mark(prof, SM_PHASE_VOTE, stream));
+  return SM_OK;
 }
 }  // namespace
 

@@ -596,10 +596,11 @@ __device__ __forceinline__ uint32_t count_gt(const uint32_t (&c)[NB], int K) {
   return gt;
 }
 
-// Vote value of bit k of a word's masks: +1 (fewer than M/2 negative
-// votes), -1 (more), else the tie value.
-__device__ __forceinline__ float vote_of(uint32_t pos, uint32_t neg, int k, int tie) {
-  return ((pos >> k) & 1u) ? 1.0f : (((neg >> k) & 1u) ? -1.0f : (float)tie);
+// Vote value of bit k of a word's masks times c: +c (fewer than M/2
+// negative votes), -c (more), else c times the tie value (c = 1 but for the
+// normalized step).
+__device__ __forceinline__ float vote_of(uint32_t pos, uint32_t neg, int k, int tie, float c) {
+  return ((pos >> k) & 1u) ? c : (((neg >> k) & 1u) ? -c : c * (float)tie);
 }
 
 // VA_APPLY: a wave takes 2048 consecutive entries of one matrix.  Lane l
@@ -623,6 +624,8 @@ __global__ __launch_bounds__(256) void k_vote_apply(VoteArgs a) {
   const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
   const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
   const int64_t wi = (ew >> 5) + lane;
+  // W moves by eta c D (c = 1 unless a per-matrix scale is given)
+  const float c = a.scal ? a.scal[g.idx0 + mi * g.idx_stride] : 1.0f;
   auto masks = [&](uint32_t& pos, uint32_t& neg) {
     pos = neg = 0;
     if (wi < nw) {
@@ -649,9 +652,9 @@ __global__ __launch_bounds__(256) void k_vote_apply(VoteArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const bf16_t r0 = f32_to_bf16(apply_value(__uint_as_float(x[j][k] << 16), a.eta,
-                                                    vote_of(pb, nb, 2 * k, a.tie)));
+                                                    vote_of(pb, nb, 2 * k, a.tie, c)));
           const bf16_t r1 = f32_to_bf16(apply_value(__uint_as_float(x[j][k] & 0xFFFF0000u),
-                                                    a.eta, vote_of(pb, nb, 2 * k + 1, a.tie)));
+                                                    a.eta, vote_of(pb, nb, 2 * k + 1, a.tie, c)));
           x[j][k] = (uint32_t)r0 | ((uint32_t)r1 << 16);
         }
         st_nt(wp + 64 * j, x[j]);
@@ -668,7 +671,7 @@ __global__ __launch_bounds__(256) void k_vote_apply(VoteArgs a) {
         const uint32_t pb = (uint32_t)__shfl((int)pos, src) >> sh;
         const uint32_t nb = (uint32_t)__shfl((int)neg, src) >> sh;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) x[j][k] = apply_value(x[j][k], a.eta, vote_of(pb, nb, k, a.tie));
+        for (int k = 0; k < 4; ++k) x[j][k] = apply_value(x[j][k], a.eta, vote_of(pb, nb, k, a.tie, c));
         st_nt(wp + 64 * j, x[j]);
       }
     }
@@ -692,15 +695,15 @@ __global__ __launch_bounds__(256) void k_vote_apply(VoteArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const bf16_t r0 = f32_to_bf16(apply_value(__uint_as_float(x[k] << 16), a.eta,
-                                                    vote_of(pb, nb, 2 * k, a.tie)));
+                                                    vote_of(pb, nb, 2 * k, a.tie, c)));
           const bf16_t r1 = f32_to_bf16(apply_value(__uint_as_float(x[k] & 0xFFFF0000u), a.eta,
-                                                    vote_of(pb, nb, 2 * k + 1, a.tie)));
+                                                    vote_of(pb, nb, 2 * k + 1, a.tie, c)));
           x[k] = (uint32_t)r0 | ((uint32_t)r1 << 16);
         }
         st_nt(wp, x);
       } else {
         for (int k = 0; k < 8 && e + k < mn; ++k)
-          apply_store(a.W, 1, eoff + e + k, a.eta, vote_of(pb, nb, k, a.tie));
+          apply_store(a.W, 1, eoff + e + k, a.eta, vote_of(pb, nb, k, a.tie, c));
       }
     }
   } else {
@@ -717,11 +720,11 @@ __global__ __launch_bounds__(256) void k_vote_apply(VoteArgs a) {
         f32x4_t* wp = reinterpret_cast<f32x4_t*>(W + eoff + e);
         f32x4_t x = ld_nt(wp);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) x[k] = apply_value(x[k], a.eta, vote_of(pb, nb, k, a.tie));
+        for (int k = 0; k < 4; ++k) x[k] = apply_value(x[k], a.eta, vote_of(pb, nb, k, a.tie, c));
         st_nt(wp, x);
       } else {
         for (int k = 0; k < 4 && e + k < mn; ++k)
-          apply_store(a.W, 0, eoff + e + k, a.eta, vote_of(pb, nb, k, a.tie));
+          apply_store(a.W, 0, eoff + e + k, a.eta, vote_of(pb, nb, k, a.tie, c));
       }
     }
   }
@@ -770,6 +773,12 @@ __global__ __launch_bounds__(256) void k_vote_tern(VoteArgs a) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) v[k] = (float)majority(acc[k], a.tie);
     if (a.mode == VA_APPLY) {
+      // W moves by eta c D (c = 1 unless a per-matrix scale is given)
+      if (a.scal) {
+        const float c = a.scal[g.idx0 + mi * g.idx_stride];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] *= c;
+      }
       if (g.vec_ok && cnt == 16) {
         // e0 and the matrix offset are multiples of 8: 16-byte W accesses
         if (a.w_bf16) {

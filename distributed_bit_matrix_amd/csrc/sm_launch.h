@@ -127,6 +127,10 @@ struct VoteArgs {
   // matrix at its element offset) instead of the packed bits
   const int8_t* tern;
   void* W; float eta;
+  // VA_APPLY: NULL, or per-matrix c (indexed as the matrices' scale
+  // factors): W moves by eta c D (the normalized step, and the post-vote
+  // step with K = 0)
+  const float* scal;
   void* o_hi; void* o_lo; float* part;
   const int32_t* status;
 };
