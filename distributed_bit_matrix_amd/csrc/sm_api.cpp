@@ -1019,7 +1019,6 @@ sm_status signmuon_polar_ns(const float* X, float* U, int64_t rows, int64_t cols
   if (hp->K == 0) {
     ScaledOutArgs so;
     std::memset(&so, 0, sizeof(so));
-    so.precision = P.precision; so.from_op = 0; so.apply = 0;
     so.x_user = X; so.scal = B.scal; so.U = U;
     HIP_TRY(for_launches(groups, [&](Group& g) {
       g.blocks_per_mat = (int32_t)((rows * cols + kChunk - 1) / kChunk);

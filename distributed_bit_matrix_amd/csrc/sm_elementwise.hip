@@ -87,13 +87,6 @@ __device__ __forceinline__ void store_opv(int precision, void* hi, void* lo,
     reinterpret_cast<bf16_t*>(hi)[i] = f32_to_bf16(v);
   }
 }
-__device__ __forceinline__ float load_opv(int precision, const void* hi,
-                                          const void* lo, int64_t i) {
-  if (precision == P_F32) return reinterpret_cast<const float*>(hi)[i];
-  float v = bf16_to_f32(reinterpret_cast<const bf16_t*>(hi)[i]);
-  if (precision == P_BF16X3) v += bf16_to_f32(reinterpret_cast<const bf16_t*>(lo)[i]);
-  return v;
-}
 // 8 consecutive operand values (16-byte aligned destination).
 __device__ __forceinline__ void store_op8(int precision, void* hi, void* lo,
                                           int64_t i, const float (&v)[8]) {
@@ -1087,30 +1080,19 @@ hipError_t launch_affine_ident(const Groups& G, const void* A, float a, float b,
 }
 
 // ---------------------------------------------------------------------------
-// K = 0: U = c * X (caller layout), or W -= eta * c * S from the operand.
+// PolarNS with K = 0: U = c X (caller layout).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_scaled_out(ScaledOutArgs a) {
-  if (a.apply && a.status && a.status[0] != 0) return;
   int gi, mi, q;
   group_of_block(a.G, blockIdx.x, gi, mi, q);
   const Group& g = a.G.g[gi];
   const int64_t mn = (int64_t)g.rows * g.cols;
   const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
-  const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
   const float c = a.scal[g.idx0 + mi * g.idx_stride];
   for (int k = 0; k < 8; ++k) {
-    int64_t e = (int64_t)q * kChunk + k * 256 + threadIdx.x;
+    const int64_t e = (int64_t)q * kChunk + k * 256 + threadIdx.x;
     if (e >= mn) break;
-    float x;
-    if (a.from_op) {
-      int64_t row = e / g.cols, col = e - row * g.cols;
-      x = load_opv(a.precision, a.x_hi, a.x_lo, xoff + s_index(g, row, col));
-    } else {
-      x = a.x_user[eoff + e];
-    }
-    float v = c * x;
-    if (a.apply) apply_store(a.W, a.w_bf16, eoff + e, a.eta, v);
-    else a.U[eoff + e] = v;
+    a.U[eoff + e] = c * a.x_user[eoff + e];
   }
 }
 

@@ -163,13 +163,12 @@ hipError_t launch_prescale(const Groups& G, int precision, const float* araw,
                            const float* w, float eps, hipStream_t s);
 // K = 0 output: v = c * x (x from caller-layout float32 or padded operand);
 // writes U (caller layout) or applies W -= eta * v.
+// PolarNS with K = 0: U = c X in the caller's layout (X float32).
 struct ScaledOutArgs {
   Groups G;
-  int32_t precision, from_op, apply, w_bf16;
-  const float* x_user; const void* x_hi; const void* x_lo;
+  const float* x_user;
   const float* scal;
-  float* U; void* W; float eta;
-  const int32_t* status;
+  float* U;
 };
 hipError_t launch_scaled_out(const ScaledOutArgs& a, hipStream_t s);
 
