@@ -342,10 +342,11 @@ __device__ __forceinline__ void stage_store_tile(const f32x4_t (&v)[TI][TJ], cha
 
 // Mirror tile of a symmetric output, through LDS: the transpose of the
 // tile (rows n0.., columns m0..) is staged with the transposed-tile writes
-// (the 4 rows of a register group become 4 consecutive columns) and stored
+// (the 4 rows of a register group become 4 consecutive columns; TRSRC:
+// the accumulators hold transposed tiles, whose 4 columns become 4 rows) and stored
 // as 16-byte row pieces.  Waits first for every thread to have read out the
 // previous image.
-template <typename T, int SPLIT, int BMT, int BNT, int TI, int TJ, int NT>
+template <typename T, int SPLIT, int BMT, int BNT, int TI, int TJ, int NT, bool TRSRC = false>
 __device__ __forceinline__ void stage_store_mirror(const f32x4_t (&v)[TI][TJ], char* smem,
                                                    void* dst_hi, void* dst_lo, int64_t ld,
                                                    int m0, int n0, int row_lim, int wm, int wn,
@@ -356,8 +357,8 @@ __device__ __forceinline__ void stage_store_mirror(const f32x4_t (&v)[TI][TJ], c
 #pragma unroll
     for (int j = 0; j < TJ; ++j) vt[j][i] = v[i][j];
   __syncthreads();
-  stage_store_tile<T, SPLIT, BNT, BMT, TJ, TI, NT, true>(vt, smem, dst_hi, dst_lo, ld, n0, m0,
-                                                         row_lim, wn, wm, lane, tid);
+  stage_store_tile<T, SPLIT, BNT, BMT, TJ, TI, NT, !TRSRC>(vt, smem, dst_hi, dst_lo, ld, n0, m0,
+                                                           row_lim, wn, wm, lane, tid);
 }
 
 // Tile of the symmetric outputs (Gram, raw Gram, quintic square).
@@ -468,7 +469,8 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   // An update with TRACC runs its MFMAs with the operands swapped, which
   // gives the transposed tiles.
   constexpr bool SWAP = TRACC;
-  static_assert(!TRACC || EPI == E_UPDATE, "transposed tiles are an update layout");
+  static_assert(!TRACC || EPI == E_UPDATE || EPI == E_SQUARE,
+                "transposed tiles: update and symmetric product");
   auto acc_row = [&](int i, int r) SM_INLINE {
     return m0 + wm * WTM + (SWAP ? (lane & 15) : 4 * (lane >> 4) + r) + 16 * i;
   };
@@ -842,6 +844,38 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
     else return false;
   };
   auto add_sq = [&](auto bkc, int s, int stg) SM_INLINE {
+    if constexpr (SWAP) {
+      // transposed tiles: lane l holds row 16 i + l % 16 of the wave tile,
+      // columns 16 j + 4 (l / 16) .. +3
+      static_assert(sizeof(T) == 2 && SPLIT == 1, "transposed symmetric tiles are bf16");
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int kb = sq_k0 + 16 * i - s * BK;
+        if (kb < 0 || kb >= BK) continue;
+        const int kr = kb + (lane & 15);          // this lane's row k in the slab
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int cb0 = wn * WTN + 16 * j + 4 * (lane >> 4);   // first column - n0
+          float y[4];
+          if constexpr (decltype(bkc)::value) {
+            // k-major slab: Y(k, n0 + c .. +3) is one 8-byte read
+            const u32x2_t h = *reinterpret_cast<const u32x2_t*>(
+                b_tile(stg, 0) + km_off<T, BNT>(kr, 2 * cb0));
+            y[0] = __uint_as_float(h[0] << 16); y[1] = __uint_as_float(h[0] & 0xFFFF0000u);
+            y[2] = __uint_as_float(h[1] << 16); y[3] = __uint_as_float(h[1] & 0xFFFF0000u);
+          } else {
+            // slab along rows (the diagonal tile): Y(k, col) = Y(col, k)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              y[r] = bf16_to_f32(*reinterpret_cast<const bf16_t*>(
+                  b_tile(stg, 0) + lds_off<RB>(cb0 + r, kr / P) + (kr % P) * 2));
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] += sq_ratio * y[r];
+        }
+      }
+      return;
+    }
     if constexpr (EPI == E_SQUARE && decltype(bkc)::value) {
       // off the diagonal with upper-triangular storage the slab holds
       // Y(k, n0 + c) k-major: 4 consecutive k of one column per lane are
@@ -897,7 +931,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
       if (s < nslab) issue(s);
 
     // one slab with compile-time layouts; the layouts come in runs of the
-    // rotated slab order, one loop per run (as in the pipelined loop below)
+    // slab order, one loop per run (as in the pipelined loop below)
     auto slab = [&](auto akc, auto bkc, int s) SM_INLINE {
       // the k-major read addresses derive from one register per operand;
       // redefining it opaquely here keeps the derived addresses from being
@@ -1108,11 +1142,10 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
   const int64_t Rp = round_up(sr, kPad);   // rows of S (padded)
   const int64_t Cp = round_up(sc, kPad);   // columns of S (padded)
-  const int ar0 = acc_row(0, 0), ac0 = acc_col(0, 0);
   // every wave is done reading the operand stages: LDS is free for staging
   __syncthreads();
 
-  if constexpr (SYM) {
+  if constexpr (EPI == E_OP || EPI == E_RAW) {   // (only Grams are split along k)
     if (g.ksplit > 1) {
       // split-k: the raw float32 tile of this split in accumulator order
       // (register group (i, j) of lane l of wave w at float4 index
@@ -1182,29 +1215,22 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          float x[4];
-          if (upper) {
-            // only the upper tile (tm, tn) is stored: Y(row + r, col) itself
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              x[r] = load_op<T, SPLIT>(A.sq_hi, A.sq_lo,
-                                       roff + (int64_t)(ar0 + i * 16 + r) * Rp + ac0 + j * 16);
-          } else {
-            load_op4<T, SPLIT>(A.sq_hi, A.sq_lo, roff + (int64_t)(ac0 + j * 16) * Rp + ar0 + i * 16,
-                               x);
+          for (int r = 0; r < 4; ++r) {
+            // Y(row, col) of this upper tile (tm, tn), stored in every layout
+            const float x = load_op<T, SPLIT>(
+                A.sq_hi, A.sq_lo, roff + (int64_t)acc_row(i, r) * Rp + acc_col(j, r));
+            acc[i][j][r] = A.cb * x + A.cc * acc[i][j][r];
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = A.cb * x[r] + A.cc * acc[i][j][r];
-        }
     }
-    stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
-                                                     offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
-                                                     (int)Rp, wm, wn, lane, tid);
+    stage_store_tile<T, SPLIT, BMT, BNT, TI, TJ, NT, SWAP>(acc, smem, offset_ptr<T>(A.o_hi, roff),
+                                                           offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
+                                                           (int)Rp, wm, wn, lane, tid);
     if (tm != tn && !upper)
-      stage_store_mirror<T, SPLIT, BMT, BNT, TI, TJ, NT>(acc, smem, offset_ptr<T>(A.o_hi, roff),
-                                                         offset_ptr<T>(A.o_lo, roff), Rp, m0, n0,
-                                                         (int)Rp, wm, wn, lane, tid);
+      stage_store_mirror<T, SPLIT, BMT, BNT, TI, TJ, NT, SWAP>(
+          acc, smem, offset_ptr<T>(A.o_hi, roff), offset_ptr<T>(A.o_lo, roff), Rp, m0, n0, (int)Rp,
+          wm, wn, lane, tid);
   } else {
     // E_UPDATE:  acc = a X + B X (first step: X = the unscaled source), and
     // the iterate is c^p * acc with c = 1/(s+eps) on the first step.
@@ -1422,6 +1448,9 @@ __global__ __launch_bounds__(256) void k_split_reduce(GemmArgs A) {
 #ifndef SM_OP_WPE
 #define SM_OP_WPE 2
 #endif
+#ifndef SM_SQ_TRACC
+#define SM_SQ_TRACC 1
+#endif
 #ifndef SM_SQ_NSTG
 #define SM_SQ_NSTG 2
 #endif
@@ -1465,7 +1494,8 @@ struct Cfg {
                                TI * TJ * 4 + 2 * (RB / 64) * (TI + TJ) * 4 <= 192;
   // transposed accumulator tiles for the 128x128 update (measured: the
   // nanoGPT set gains 1.4%, the 128x256 update of the MLP set loses 0.6%)
-  static constexpr bool TRACC = EPI == E_UPDATE && !WIDE;
+  // and the bf16 symmetric product (8-byte staging writes of its output)
+  static constexpr bool TRACC = (EPI == E_UPDATE && !WIDE) || (EPI == E_SQUARE && BF && SM_SQ_TRACC);
   static constexpr int BMT = WM * 16 * TI, BNT = 32 * TJ;
   static constexpr size_t lds() {
     size_t pipe = (size_t)NSTG * SPLIT * (BMT + BNT) * RB;
