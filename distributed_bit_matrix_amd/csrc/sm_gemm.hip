@@ -17,10 +17,14 @@
 // Gram, B for the update) land as 128-byte slab rows and are read with
 // 16-byte loads; the update's S operand has k down its columns, lands as
 // k-rows and is read with the transposing LDS load (ds_read_b64_tr_b16),
-// so no transposed copy of S is ever stored.  NSTG LDS stages form the
-// prefetch pipeline; completion is tracked with explicit vmcnt waits and a
-// bare s_barrier.  All operand copies are zero padded to multiples of 128,
-// so no load is predicated and padding contributes exact zeros.
+// so no transposed copy of S is ever stored.  bfloat16 symmetric operands
+// (Gram operand, Gram-space iterates) are stored as their upper-triangular
+// tiles: a product reads the slabs of a row block left of the diagonal
+// k-major from the tiles above it, with the same transposing loads.  NSTG
+// LDS stages form the prefetch pipeline; completion is tracked with
+// explicit vmcnt waits and a bare s_barrier.  All operand copies are zero
+// padded to multiples of 128, so no load is predicated and padding
+// contributes exact zeros.
 #include <algorithm>
 #include <cstring>
 #include <type_traits>
@@ -410,8 +414,9 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   const int lb = b - g.block0;
   const int mi = lb / g.blocks_per_mat;
   const int t = lb - mi * g.blocks_per_mat;
-  // Symmetric outputs (Gram, raw Gram, quintic square) are computed on the
-  // upper-triangular tiles only; the epilogue also writes the mirror tile.
+  // Symmetric outputs (Gram, raw Gram, symmetric products) are computed on
+  // the upper-triangular tiles only; the epilogue also writes the mirror
+  // tile unless the operand is stored upper-triangular.
   constexpr bool SYM = EPI != E_UPDATE;
   const int a_fam = g.ops & 3, b_fam = (g.ops >> 2) & 3;
   int tm, tn;
