@@ -108,8 +108,9 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
     q.r_off = r2; r2 += q.Rp * q.Rp;
     q.v_off = v; v += q.Rp;
     q.u0_off = u0; u0 += q.r;
-    int64_t nw = (m.rows * m.cols + 31) / 32;
-    q.chunks = std::max<int64_t>(q.Mp * q.Np / kChunk, (nw + 255) / 256);
+    // partial sums: one per sweep chunk or per packed-vote block
+    q.chunks = std::max<int64_t>(q.Mp * q.Np / kChunk,
+                                 vote_blocks_per_mat(VA_SBAR, m.rows, m.cols));
     q.c_off = c; c += q.chunks;
     q.idx = i;
     umax = std::max<int64_t>(umax, m.elem_off + m.rows * m.cols);
@@ -444,7 +445,8 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
         // partial sums per matrix: one per sweep tile (0), per packed vote
         // block (1) or per int8 vote block (2)
         g.gk = (int32_t)(part_kind == 0 ? mp[g.idx0].Mp * mp[g.idx0].Np / 4096
-                         : part_kind == 1 ? (((mn + 31) / 32) + 255) / 256
+                         : part_kind == 1 ? vote_blocks_per_mat(VA_SBAR, mp[g.idx0].rows,
+                                                                mp[g.idx0].cols)
                                           : (mn + kTernChunk - 1) / kTernChunk);
         return true;
       }, [&](const Groups& G) { return launch_fro_finalize(G, B.part, hp->eps, B.scal, s); }));

@@ -524,53 +524,6 @@ hipError_t launch_momentum_sign(const MomSignArgs& a, hipStream_t s) {
 // the padded operand copy (VA_SBAR, a thread per packed word) or the update
 // of W (VA_APPLY, k_vote_apply below).
 // ---------------------------------------------------------------------------
-template <int NB>
-__global__ __launch_bounds__(256) void k_vote_groups(VoteArgs a) {
-  int gi, mi, q;
-  group_of_block(a.G, blockIdx.x, gi, mi, q);
-  const Group& g = a.G.g[gi];
-  const int rows = g.rows, cols = g.cols;
-  const int64_t mn = (int64_t)rows * cols;
-  const int64_t nw = (mn + 31) >> 5;
-  const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
-  const int64_t w = (int64_t)q * 256 + threadIdx.x;
-  float ss = 0.0f;
-  if (w < nw) {
-    uint32_t c[NB];
-    count_votes<NB>(a.bits, a.stride, a.M, woff + w, c);
-    const int64_t e0 = w * 32;
-    // VA_SBAR: majority matrix into the padded operand copy S (a tall
-    // matrix is written transposed, one element at a time)
-    const int64_t Np = round_up(cols, kPad);
-    const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
-    if (cols % 32 == 0 && !s_tall(g)) {
-      int row = (int)(e0 / cols), col = (int)(e0 - (int64_t)row * cols);
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        float v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          v[k] = (float)majority(vote_sum_at<NB>(c, a.M, 8 * h + k), a.tie);
-          ss += v[k] * v[k];
-        }
-        store_op8(a.precision, a.o_hi, a.o_lo, xoff + (int64_t)row * Np + col + 8 * h, v);
-      }
-    } else {
-      for (int b = 0; b < 32 && e0 + b < mn; ++b) {
-        int64_t e = e0 + b;
-        int row = (int)(e / cols), col = (int)(e - (int64_t)row * cols);
-        float v = (float)majority(vote_sum_at<NB>(c, a.M, b), a.tie);
-        ss += v * v;
-        store_opv(a.precision, a.o_hi, a.o_lo, xoff + s_index(g, row, col), v);
-      }
-    }
-  }
-  if (a.part) {
-    float t = block_sum(ss);
-    if (threadIdx.x == 0) a.part[g.c0 + (int64_t)mi * g.c_stride + q] = t;
-  }
-}
-
 // Majority masks from bit-sliced counts: the positions whose count of
 // negative votes exceeds the constant K (0 <= K < 2^NB), compared from the
 // most significant counter bit down.
@@ -594,6 +547,134 @@ __device__ __forceinline__ uint32_t count_gt(const uint32_t (&c)[NB], int K) {
 // normalized step).
 __device__ __forceinline__ float vote_of(uint32_t pos, uint32_t neg, int k, int tie, float c) {
   return ((pos >> k) & 1u) ? c : (((neg >> k) & 1u) ? -c : c * (float)tie);
+}
+
+// Majority masks of one packed word: bit k of pos (neg) is set where fewer
+// (more) than half of the M workers voted negative.
+template <int NB>
+__device__ __forceinline__ void vote_masks(const uint32_t (&c)[NB], int M, uint32_t& pos,
+                                           uint32_t& neg) {
+  neg = count_gt<NB>(c, M / 2);             // 2 cnt > M
+  pos = ~count_gt<NB>(c, (M - 1) / 2);      // 2 cnt < M
+}
+
+// VA_SBAR of a tall matrix (stored transposed) whose rows are whole packed
+// words: a block takes a tile of 64 rows x 128 columns of the matrix.  Each
+// thread counts one word (a row, 32 columns) and leaves its masks in LDS;
+// the block then writes the 128 rows of S the tile covers, 64 entries (128
+// bytes in bfloat16) per row, 8 consecutive entries per lane.
+constexpr int kVtRows = 64, kVtCols = 128;
+template <int NB>
+__device__ __forceinline__ float vote_sbar_tall(const VoteArgs& a, const Group& g, int mi,
+                                                int q) {
+  __shared__ uint32_t pm[4][64], nm[4][64];   // [word column][8 (row % 8) + row / 8]
+  const int rows = g.rows, cols = g.cols;
+  const int tiles_c = (cols + kVtCols - 1) / kVtCols;
+  const int r0 = (q / tiles_c) * kVtRows, c0 = (q % tiles_c) * kVtCols;
+  const int64_t wpr = cols >> 5;                       // packed words per row
+  const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
+  const int lr = threadIdx.x >> 2, wc = threadIdx.x & 3;
+  const int row = r0 + lr, wcol = (c0 >> 5) + wc;
+  uint32_t pos = 0, neg = 0;
+  float ss = 0.0f;
+  if (row < rows && wcol < wpr) {
+    uint32_t c[NB];
+    count_votes<NB>(a.bits, a.stride, a.M, woff + row * wpr + wcol, c);
+    vote_masks<NB>(c, a.M, pos, neg);
+    const int nz = __popc(pos) + __popc(neg);
+    ss = (float)nz + (float)(a.tie * a.tie) * (float)(32 - nz);
+  }
+  pm[wc][8 * (lr & 7) + (lr >> 3)] = pos;
+  nm[wc][8 * (lr & 7) + (lr >> 3)] = neg;
+  __syncthreads();
+  const int64_t ld = round_up(rows, kPad);
+  const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
+  const int ch = threadIdx.x & 7, bit = threadIdx.x >> 3;
+  const int rr = r0 + 8 * ch;                         // first column of S (row of X)
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int col = c0 + 32 * p + bit;                // row of S (column of X)
+    if (col >= cols || rr >= rows) continue;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = vote_of(pm[p][8 * j + ch], nm[p][8 * j + ch], bit, a.tie, 1.0f);
+    const int64_t o = xoff + (int64_t)col * ld + rr;
+    if (rr + 8 <= rows) {
+      store_op8(a.precision, a.o_hi, a.o_lo, o, v);
+    } else {
+      for (int j = 0; j < 8 && rr + j < rows; ++j) store_opv(a.precision, a.o_hi, a.o_lo, o + j, v[j]);
+    }
+  }
+  return ss;
+}
+
+template <int NB>
+__global__ __launch_bounds__(256) void k_vote_groups(VoteArgs a) {
+  int gi, mi, q;
+  group_of_block(a.G, blockIdx.x, gi, mi, q);
+  const Group& g = a.G.g[gi];
+  const int rows = g.rows, cols = g.cols;
+  if (s_tall(g) && cols % 32 == 0) {
+    const float ss = vote_sbar_tall<NB>(a, g, mi, q);
+    if (a.part) {
+      float t = block_sum(ss);
+      if (threadIdx.x == 0) a.part[g.c0 + (int64_t)mi * g.c_stride + q] = t;
+    }
+    return;
+  }
+  const int64_t mn = (int64_t)rows * cols;
+  const int64_t nw = (mn + 31) >> 5;
+  const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
+  const int64_t w = (int64_t)q * 256 + threadIdx.x;
+  const int64_t Np = round_up(cols, kPad);
+  const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
+  float ss = 0.0f;
+  if (cols % 32 == 0) {
+    // S = X, rows of whole words: lane l counts word l of the wave's 2048
+    // entries; the stores then run over the stretch in lane order, 8
+    // entries (16 bytes in bfloat16) per lane, each lane taking the mask
+    // bits of its entries from the lane that counted them.
+    const int lane = threadIdx.x & 63;
+    uint32_t pos = 0, neg = 0;
+    if (w < nw) {
+      uint32_t c[NB];
+      count_votes<NB>(a.bits, a.stride, a.M, woff + w, c);
+      vote_masks<NB>(c, a.M, pos, neg);
+      const int nz = __popc(pos) + __popc(neg);
+      ss = (float)nz + (float)(a.tie * a.tie) * (float)(32 - nz);
+    }
+    const uint32_t ew = (uint32_t)(w - lane) * 32u;   // entries < 2^31
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int src = 16 * j + (lane >> 2), sh = 8 * (lane & 3);
+      const uint32_t pb = (uint32_t)__shfl((int)pos, src) >> sh;
+      const uint32_t nb = (uint32_t)__shfl((int)neg, src) >> sh;
+      const uint32_t e = ew + 512u * j + 8u * lane;
+      if (e >= mn) continue;
+      const uint32_t row = e / (uint32_t)cols, col = e - row * (uint32_t)cols;
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = vote_of(pb, nb, k, a.tie, 1.0f);
+      store_op8(a.precision, a.o_hi, a.o_lo, xoff + (int64_t)row * Np + col, v);
+    }
+  } else if (w < nw) {
+    // rows that split packed words: one entry at a time
+    uint32_t c[NB];
+    count_votes<NB>(a.bits, a.stride, a.M, woff + w, c);
+    const int64_t e0 = w * 32;
+    for (int b = 0; b < 32 && e0 + b < mn; ++b) {
+      int64_t e = e0 + b;
+      int row = (int)(e / cols), col = (int)(e - (int64_t)row * cols);
+      float v = (float)majority(vote_sum_at<NB>(c, a.M, b), a.tie);
+      ss += v * v;
+      store_opv(a.precision, a.o_hi, a.o_lo, xoff + s_index(g, row, col), v);
+    }
+  }
+  if (a.part) {
+    float t = block_sum(ss);
+    if (threadIdx.x == 0) a.part[g.c0 + (int64_t)mi * g.c_stride + q] = t;
+  }
 }
 
 // VA_APPLY: a wave takes 2048 consecutive entries of one matrix.  Lane l
@@ -624,8 +705,7 @@ __global__ __launch_bounds__(256) void k_vote_apply(VoteArgs a) {
     if (wi < nw) {
       uint32_t c[NB];
       count_votes<NB>(a.bits, a.stride, a.M, woff + wi, c);
-      neg = count_gt<NB>(c, a.M / 2);           // 2 cnt > M
-      pos = ~count_gt<NB>(c, (a.M - 1) / 2);    // 2 cnt < M
+      vote_masks<NB>(c, a.M, pos, neg);
     }
   };
   uint32_t pos, neg;
@@ -838,6 +918,8 @@ __global__ __launch_bounds__(256) void k_vote_tern(VoteArgs a) {
 int vote_blocks_per_mat(int mode, int64_t rows, int64_t cols) {
   const int64_t mn = rows * cols;
   if (mode == VA_APPLY) return (int)((mn + 8191) / 8192);
+  if (rows > cols && cols % 32 == 0)   // tiles of vote_sbar_tall
+    return (int)(((rows + kVtRows - 1) / kVtRows) * ((cols + kVtCols - 1) / kVtCols));
   return (int)(((mn + 31) / 32 + 255) / 256);
 }
 

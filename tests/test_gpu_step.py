@@ -305,8 +305,11 @@ def test_step_mirrored_storage(name, monkeypatch):
 # emulation of the bfloat16 products gave 1e-3 to 2.5e-3 on 19x64 to
 # 45x71), which the 99.9% agreement cannot absorb; the bfloat16 cases use
 # odd shapes of 15000+ entries, where the emulation gave at most 5.3e-4.
-ODD_TINY = [(5, 37), (33, 7), (45, 71), (64, 19), (3, 3)]
-ODD_BF16 = [(97, 161), (161, 97), (45, 403), (403, 45), (33, 515)]
+# (70, 32) and (203, 96) are tall with whole packed words per row: the vote
+# of the post-vote steps writes them through LDS tiles of 64 x 128, here
+# with partial tiles in both directions.
+ODD_TINY = [(5, 37), (33, 7), (45, 71), (64, 19), (3, 3), (70, 32)]
+ODD_BF16 = [(97, 161), (161, 97), (45, 403), (403, 45), (33, 515), (203, 96)]
 ODD = {
     "f32_M5": WL.scaled(WL.get("single"), ODD_TINY, M=5, name="odd-f32"),
     "bf16w_f32ns_M6": WL.scaled(WL.get("nanogpt"), ODD_TINY, M=6,
@@ -321,6 +324,7 @@ ODD = {
     .replace(encoding="ternary"),
     "normalized_M5": WL.scaled(WL.get("nanogpt_normalized"), ODD_BF16, M=5,
                                name="odd-normalized"),
+    "postvote_M5": WL.scaled(WL.get("postvote"), ODD_BF16, M=5, name="odd-postvote"),
 }
 
 
