@@ -64,6 +64,14 @@ bool gram_space_enabled() {
   return !(e && std::strcmp(e, "iterate") == 0);
 }
 
+// The P power steps of small sets run in one launch unless the environment
+// variable SIGNMUON_POWER_ITER is "steps" (one launch per step; read at
+// every call).
+bool power_iter_fused() {
+  const char* e = std::getenv("SIGNMUON_POWER_ITER");
+  return !(e && std::strcmp(e, "steps") == 0);
+}
+
 // bfloat16 symmetric operands are stored as their upper-triangular tiles
 // unless the environment variable SIGNMUON_SYM_STORAGE is "full" (read at
 // every call; then every symmetric output also writes its mirror tiles).
@@ -165,6 +173,7 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
   if (power) {
     P.off_araw = take(r2 * 4);
     P.off_vec = take(2 * v * 4);
+    P.off_tag = take(2 * v * 8);
   }
   P.off_part = take(c * 4);
   if ((ns || power) && kp > 0) P.off_kpart = take(kp * 4);
@@ -279,6 +288,7 @@ struct Bufs {
   void* a[2];
   float* araw;
   float* vec;
+  uint64_t* tag;   // tagged vectors of the one-launch power iteration
   float* part;
   float* kpart;
   void* gs[5];     // Gram-space A_even, A_odd, T, Q_even, Q_odd
@@ -300,6 +310,7 @@ Bufs bind(const Plan& P, void* ws) {
   B.a[0] = at(P.off_a[0]); B.a[1] = at(P.off_a[1]);
   B.araw = static_cast<float*>(at(P.off_araw));
   B.vec = static_cast<float*>(at(P.off_vec));
+  B.tag = static_cast<uint64_t*>(at(P.off_tag));
   B.part = static_cast<float*>(at(P.off_part));
   B.kpart = static_cast<float*>(at(P.off_kpart));
   for (int j = 0; j < 5; ++j)
@@ -472,7 +483,17 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
     });
     return;
   }
-  out.push_back([&, hp, gram_fill, prec, s]() -> sm_status {
+  // Small sets (few rows of raw Gram in all) run the P power steps and the
+  // scale in one launch whose blocks keep their rows in LDS; the raw Gram
+  // launch clears the tagged vectors they exchange.
+  int64_t pblocks = 0, rp_max = 0;
+  for (const Group& g : groups) {
+    pblocks += mp[g.idx0].Rp / kPowerRows * g.count;
+    rp_max = std::max<int64_t>(rp_max, mp[g.idx0].Rp);
+  }
+  const bool fused = power_iter_fused() && B.tag && pblocks <= kPowerIterMaxBlocks &&
+                     rp_max <= kPowerIterMaxRp;
+  out.push_back([&, hp, gram_fill, prec, fused, s]() -> sm_status {
     HIP_TRY(for_launches(groups, gram_fill, [&](const Groups& G) {
       GemmArgs a;
       std::memset(&a, 0, sizeof(a));
@@ -480,10 +501,37 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
       a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
       a.epi = E_RAW; a.o_raw = B.araw;
       a.kpart = B.kpart;
+      if (fused) {
+        a.tag = B.tag;
+        a.tag_stride = P.v_total;
+      }
       return launch_gemm_timed(prec, a, s, io.prof, SM_PHASE_GRAM);
     }));
     return SM_OK;
   });
+  if (fused) {
+    out.push_back([&, hp, gram_mul, dst_hi, dst_lo, prec, s]() -> sm_status {
+      HIP_TRY(for_launches(groups, [&](Group& g) {
+        g.blocks_per_mat = (int32_t)(mp[g.idx0].Rp / kPowerRows);
+        return true;
+      }, [&](const Groups& G) {
+        PowerIterArgs pa;
+        std::memset(&pa, 0, sizeof(pa));
+        pa.G = G;
+        pa.araw = B.araw; pa.va = B.vec; pa.vb = B.vec + P.v_total; pa.u0 = io.u0;
+        pa.P = hp->P; pa.scaled_op = hp->K > 0 ? 1 : 0; pa.precision = prec;
+        pa.mul = gram_mul; pa.eps = hp->eps; pa.scal = B.scal;
+        pa.hi = dst_hi; pa.lo = dst_lo; pa.status = B.status;
+        pa.tag = B.tag; pa.tag_stride = P.v_total;
+        int64_t rpl = 0;
+        for (int i = 0; i < G.n; ++i) rpl = std::max<int64_t>(rpl, mp[G.g[i].idx0].Rp);
+        return launch_power_iter(pa, rpl, s);
+      }));
+      HIP_TRY(mark(io.prof, SM_PHASE_PRESCALE, s));
+      return SM_OK;
+    });
+    return;
+  }
   // power iteration: P >= 1 steps alternating va / vb (P is validated); the
   // first step reads the start vector (u0, or ones) directly, and with K > 0
   // the prescale launch derives the scale from the final vector itself, so a
@@ -1410,6 +1458,7 @@ sm_status signmuon_get_status(const void* ws, hipStream_t stream) {
   if (hipMemcpyAsync(h, ws, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess)
     return SM_EHIP;
   if (hipStreamSynchronize(stream) != hipSuccess) return SM_EHIP;
+  if ((h[0] | h[1]) & 2) return SM_EHIP;
   return h[0] || h[1] ? SM_ENONFINITE : SM_OK;
 }
 

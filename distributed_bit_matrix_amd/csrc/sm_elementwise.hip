@@ -1073,6 +1073,139 @@ __device__ __forceinline__ float power_scale(const Group& g, int mi, const float
   return 1.0f / (sqrtf(lam) + eps);
 }
 
+// The one-launch power iteration.  The blocks of a matrix exchange each
+// step's vector as tagged entries: one 8-byte word per entry holding the
+// float and the number of the step that wrote it (zero: not yet written;
+// the raw Gram launch before clears them), written and read with
+// device-scope atomic accesses, which go to the device's coherence point
+// rather than to an XCD's own L2.  A reader polls each entry until its tag
+// is the step it waits for (bounded), so the vector's arrival is the
+// barrier: no counter and no cache writeback or invalidation.  Step p
+// writes tag p + 1 into buffer (p + 1) % 2; a writer can be at most one
+// step ahead of any reader, so two buffers suffice.
+constexpr int kTagSpins = 1 << 20;
+__device__ __forceinline__ void put_tagged(uint64_t* t, float v, uint32_t tag) {
+  const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
+  __hip_atomic_store(t, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Entries i = threadIdx.x + 256 j (< n) of a tagged vector into xs, once
+// each carries `tag`; false if any poll ran out (the same for every thread).
+__device__ __forceinline__ bool get_tagged(const uint64_t* t, int64_t n, uint32_t tag,
+                                           float* xs) {
+  __shared__ int late;
+  if (threadIdx.x == 0) late = 0;
+  __syncthreads();
+  constexpr int kMax = kPowerIterMaxRp / 256;
+  uint64_t w[kMax];
+#pragma unroll
+  for (int j = 0; j < kMax; ++j) {
+    const int64_t i = threadIdx.x + 256 * j;
+    w[j] = i < n ? __hip_atomic_load(t + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : ((uint64_t)tag << 32);
+  }
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < kMax; ++j) {
+    const int64_t i = threadIdx.x + 256 * j;
+    int spins = 0;
+    while ((uint32_t)(w[j] >> 32) != tag && spins < kTagSpins) {
+      __builtin_amdgcn_s_sleep(1);
+      w[j] = __hip_atomic_load(t + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ++spins;
+    }
+    if ((uint32_t)(w[j] >> 32) != tag) ok = false;
+    if (i < n) xs[i] = __uint_as_float((uint32_t)w[j]);
+  }
+  if (!ok) late = 1;
+  __syncthreads();
+  return late == 0;
+}
+
+// The P power steps of k_power_step (same arithmetic, same order), with
+// the block's kPowerRows rows of the raw Gram read once into LDS, then the
+// scale (as power_scale) and, with scaled_op, the scaled operand of
+// k_prescale for those rows.
+__global__ __launch_bounds__(256) void k_power_iter(PowerIterArgs a) {
+  extern __shared__ f32x4_t slab4[];
+  float* slab = reinterpret_cast<float*>(slab4);   // kPowerRows x Rp, then x (Rp)
+  int gi, mi, q;
+  group_of_block(a.G, blockIdx.x, gi, mi, q);
+  const Group& g = a.G.g[gi];
+  const int r = g.rows < g.cols ? g.rows : g.cols;
+  const int64_t Rp = round_up(r, kPad);
+  const int midx = g.idx0 + mi * g.idx_stride;
+  const int64_t voff = g.v0 + (int64_t)mi * g.v_stride;
+  const int64_t soff = g.r0 + (int64_t)mi * g.r_stride + (int64_t)q * kPowerRows * Rp;
+  float* xs = slab + kPowerRows * Rp;
+  uint64_t* tb[2] = {a.tag + voff, a.tag + a.tag_stride + voff};
+  const float* u = a.u0 ? a.u0 + g.u0_0 + (int64_t)mi * g.u0_stride : nullptr;
+  for (int64_t i = 4 * threadIdx.x; i < kPowerRows * Rp; i += 1024)
+    *reinterpret_cast<f32x4_t*>(slab + i) = *reinterpret_cast<const f32x4_t*>(a.araw + soff + i);
+  for (int64_t i = threadIdx.x; i < Rp; i += 256) xs[i] = i < r ? (u ? u[i] : 1.0f) : 0.0f;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int p = 0; p < a.P; ++p) {
+    if (p > 0 && !get_tagged(tb[p & 1], Rp, (uint32_t)p, xs)) {
+      if (threadIdx.x == 0) {
+        atomicOr(a.status, 2);
+        atomicOr(a.status + 1, 2);
+      }
+      return;
+    }
+    float ss = 0.0f;
+    for (int64_t i = threadIdx.x; i < Rp; i += 256) ss += xs[i] * xs[i];
+    ss = block_sum(ss);
+    const float inv = ss > 0.0f ? 1.0f / sqrtf(ss) : 0.0f;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t k = 4 * lane; k < Rp; k += 256) {
+      const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(xs + k);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x4_t av = *reinterpret_cast<const f32x4_t*>(slab + (wave * 4 + rr) * Rp + k);
+        acc[rr] += av[0] * (xv[0] * inv) + av[1] * (xv[1] * inv) + av[2] * (xv[2] * inv) +
+                   av[3] * (xv[3] * inv);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float t = wave_sum(acc[rr]);
+      if (lane == 0)
+        put_tagged(tb[(p + 1) & 1] + (int64_t)q * kPowerRows + wave * 4 + rr, t, (uint32_t)(p + 1));
+    }
+  }
+  // the scale of power_scale, from the final vector
+  if (!get_tagged(tb[a.P & 1], Rp, (uint32_t)a.P, xs)) {
+    if (threadIdx.x == 0) {
+      atomicOr(a.status, 2);
+      atomicOr(a.status + 1, 2);
+    }
+    return;
+  }
+  float ws = 0.0f;
+  for (int64_t i = threadIdx.x; i < Rp; i += 256) ws += xs[i] * xs[i];
+  ws = block_sum(ws);
+  const float c = 1.0f / (sqrtf(sqrtf(ws)) + a.eps);
+  if (q == 0 && threadIdx.x == 0) a.scal[midx] = c;
+  if (a.scaled_op) {
+    const float m = a.mul * c * c;
+    for (int64_t i = 8 * threadIdx.x; i < kPowerRows * Rp; i += 2048) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = m * slab[i + k];
+      store_op8(a.precision, a.hi, a.lo, soff + i, v);
+    }
+  }
+}
+
+hipError_t launch_power_iter(const PowerIterArgs& a, int64_t rp_max, hipStream_t s) {
+  if (a.G.total_blocks <= 0) return hipSuccess;
+  if (a.G.total_blocks > kPowerIterMaxBlocks || rp_max > kPowerIterMaxRp || a.P < 1)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_power_iter, dim3(a.G.total_blocks), dim3(256),
+                     (size_t)(kPowerRows + 1) * rp_max * sizeof(float), s, a);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void k_power_finalize(Groups G, const float* w,
                                                         float eps, float* scal) {
   int gi, mi, q;

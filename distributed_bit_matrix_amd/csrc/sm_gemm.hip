@@ -397,6 +397,22 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   static_assert(EPI == E_UPDATE || BMT == BNT, "symmetric outputs use square tiles");
 
   const int tid = threadIdx.x;
+  if constexpr (EPI == E_RAW) {
+    // clear the tagged vectors of the one-launch power iteration that reads
+    // this Gram (gm = Rp entries per matrix, in both buffers)
+    if (A.tag && blockIdx.x == 0) {
+      for (int i = 0; i < A.G.n; ++i) {
+        const Group& gz = A.G.g[i];
+        for (int m = 0; m < gz.count; ++m) {
+          uint64_t* t0 = A.tag + gz.v0 + (int64_t)m * gz.v_stride;
+          for (int e = tid; e < gz.gm; e += NT) {
+            t0[e] = 0;
+            t0[A.tag_stride + e] = 0;
+          }
+        }
+      }
+    }
+  }
   // the wave index is uniform: keep it (and everything derived from it) scalar
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;

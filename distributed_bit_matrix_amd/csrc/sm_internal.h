@@ -139,6 +139,7 @@ struct Plan {
   size_t off_a[2] = {0, 0};   // quintic: A (hi/lo)
   size_t off_araw = 0;        // spectral: raw float32 Gram
   size_t off_vec = 0;         // power vectors, 2 * v_total floats
+  size_t off_tag = 0;         // one-launch power iteration: 2 * v_total tagged entries
   size_t off_part = 0;        // partial sums, c_total floats
   size_t off_kpart = 0;       // split-k partial Gram tiles, kp_total floats
   size_t off_gs = 0;          // Gram-space A, A', T, Q, Q' (bfloat16, r_total each)

@@ -43,6 +43,10 @@ struct GemmArgs {
   // bfloat16 (the Gram-space form's first factor), when o2_hi is set
   void* o2_hi; float o2_a, o2_b;
   float* o_raw;                    // E_RAW
+  // E_RAW: when set, block 0 clears the tagged vector entries (two
+  // buffers, tag_stride apart, at each matrix's vector offset) that the
+  // one-launch power iteration after it exchanges
+  uint64_t* tag; int64_t tag_stride;
   const void* sq_hi; const void* sq_lo;   // E_SQUARE: A for the b*A term
   const float* scal;               // per-matrix c = 1/(s+eps) or NULL
   const float* xs_user;            // XS_USER: float32 source in caller layout
@@ -154,6 +158,35 @@ hipError_t launch_fro_finalize(const Groups& G, const float* part, float eps,
 hipError_t launch_power_step(const Groups& G, const float* araw,
                              const float* src, float* dst, const float* u0,
                              bool first, hipStream_t s);
+// The P power steps and the scale of every matrix of a small set in one
+// launch.  A block holds kPowerRows rows of the raw Gram in LDS for all P
+// steps (blocks_per_mat = Rp / kPowerRows) and does the arithmetic of
+// k_power_step; the blocks of a matrix exchange each step's vector as
+// tagged entries (zero on entry: the raw Gram launch clears them) and wait
+// for the whole vector before the next step.  The launch holds at most
+// kPowerIterMaxBlocks blocks of at most (kPowerRows + 1) kPowerIterMaxRp
+// floats of LDS each, which the GPU keeps resident together, and every
+// wait is bounded: a block whose vector does not arrive sets bit 2 of both
+// status words.
+constexpr int kPowerRows = 16;
+constexpr int kPowerIterMaxBlocks = 256;
+constexpr int kPowerIterMaxRp = 768;
+struct PowerIterArgs {
+  Groups G;
+  const float* araw;
+  float* va; float* vb;      // step p reads (p odd ? vb : va), writes the other
+  const float* u0;           // start vectors, or NULL for ones
+  int32_t P;                 // power steps, >= 1
+  int32_t scaled_op;         // 1: also write the scaled operand mul c^2 A to hi / lo
+  int32_t precision;
+  float mul, eps;
+  float* scal;               // per-matrix c = 1 / (sqrt(|w|) + eps)
+  void* hi; void* lo;
+  uint64_t* tag;             // tagged vectors: 2 buffers of v_total entries,
+  int64_t tag_stride;        //   tag_stride apart
+  int32_t* status;           // the two status words
+};
+hipError_t launch_power_iter(const PowerIterArgs& a, int64_t rp_max, hipStream_t s);
 hipError_t launch_power_finalize(const Groups& G, const float* w, float eps,
                                  float* scal, hipStream_t s);
 // op = mul * c^2 * araw (padded Rp x Rp) in the operand precision; c is

@@ -371,8 +371,12 @@ sm_status signmuon_step_profiled(const sm_matrix *mats, int32_t n_mats,
 /*
  * Status of workspace ws: waits for the stream, then returns SM_ENONFINITE
  * if the last signmuon_step on ws, or a signmuon_worker_pipeline call on ws
- * enqueued after it, saw a non-finite value; else SM_OK (SM_EHIP if the
- * copy fails).  Reading the status clears nothing.
+ * enqueued after it, saw a non-finite value; else SM_OK.  SM_EHIP if the
+ * copy fails, or if the one-launch power iteration of a spectral scale
+ * (sets whose raw Grams have at most 4096 rows in all, none wider than
+ * 768) found its blocks not all resident within its bounded wait (then the
+ * step's update is skipped, as for a non-finite value).  Reading the status
+ * clears nothing.
  */
 sm_status signmuon_get_status(const void *ws, hipStream_t stream);
 

@@ -170,3 +170,30 @@ def test_polar_orthogonal_fixed_point():
     Q = Q.astype(np.float32)
     Ug = run(Q, B.HParams(K=5, scale="spectral", P=3, precision="f32"))
     assert np.abs(Ug - Q).max() < 1e-4
+
+
+# Sets whose raw Grams have few rows run the P power steps and the scale in
+# one launch (each block keeps its 16 rows of the raw Gram in LDS, and the
+# blocks of a matrix meet after every step); it does the arithmetic of the
+# launch-per-step path in the same order, so the two agree bit for bit.
+POWER_ONE_LAUNCH = [((256, 512), 5, "bf16", True, 5), ((512, 256), 1, "bf16", False, 5),
+                    ((300, 10), 2, "f32", True, 5), ((64, 147), 8, "bf16x3", True, 5),
+                    ((700, 1000), 3, "bf16", True, 5),   # Rp = 768: the widest rows kept
+                    ((384, 640), 4, "bf16", True, 0)]    # K = 0: the scale alone
+
+
+@pytest.mark.parametrize("shape,P,precision,with_u0,K", POWER_ONE_LAUNCH)
+def test_power_iter_one_launch_equals_steps(shape, P, precision, with_u0, K, monkeypatch):
+    X = momentum_like(shape, 11)
+    u0 = (np.random.default_rng(12).standard_normal(min(shape)).astype(np.float32)
+          if with_u0 else None)
+    hp = B.HParams(K=K, scale="spectral", P=P, precision=precision)
+    print(f"power iteration, one launch vs steps: {shape} P={P} K={K} {precision}",
+          flush=True)
+    U1 = run(X, hp, u0)
+    monkeypatch.setenv("SIGNMUON_POWER_ITER", "steps")
+    U2 = run(X, hp, u0)
+    assert np.array_equal(U1, U2)
+    monkeypatch.delenv("SIGNMUON_POWER_ITER")
+    if K > 0:
+        check(X, hp, u0=u0)

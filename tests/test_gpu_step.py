@@ -660,3 +660,35 @@ def test_step_profiled_matches_plain(name, concurrent, monkeypatch):
                 assert ks[i - 1] == 9
     for i in range(cap):
         hip.hipEventDestroy(ctypes.c_void_p(evs[i]))
+
+
+@pytest.mark.parametrize("name", ["resnet50", "normalized_spectral_f32w", "prepost_spectral"])
+def test_step_power_iter_one_launch_equals_steps(name, monkeypatch):
+    # the small sets' power iteration in one launch (blocks meet after each
+    # step) against one launch per step: the same arithmetic, so W, the
+    # momentum and the sign buffers agree bit for bit over two steps
+    w, _, _ = SMALL[name]
+    print(f"power iteration one launch vs steps: {name}", flush=True)
+    hp = hparams(w)
+    layout, d, words = B.default_layout(w.mats)
+    plan = B.StepPlan(layout, hp, w.post_vote)
+    wdt = torch.bfloat16 if w.w_dtype == "bf16" else torch.float32
+    W0 = torch.from_numpy(WL.init_weights(w)).cuda().to(wdt)
+    bits0 = torch.from_numpy(WL.random_bits(w, w.M).view(np.int32)).cuda()
+    u0 = torch.from_numpy(np.concatenate(WL.power_start(w))).cuda()
+    outs = []
+    for mode in (None, "steps"):
+        if mode:
+            monkeypatch.setenv("SIGNMUON_POWER_ITER", mode)
+        W = W0.clone()
+        Mom = torch.zeros(d, dtype=torch.float32, device="cuda")
+        bits = bits0.clone()
+        for t in range(2):
+            G = torch.from_numpy(WL.gradient(w, t, 0)).cuda()
+            plan(G, W, Mom, bits, words, w.M, 0, u0=u0)
+        torch.cuda.synchronize()
+        assert plan.status() == B.SM_OK
+        outs.append((W.view(torch.int16 if wdt == torch.bfloat16 else torch.int32).cpu(),
+                     Mom.view(torch.int32).cpu(), bits.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
