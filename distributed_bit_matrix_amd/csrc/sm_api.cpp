@@ -116,9 +116,10 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
     q.r_off = r2; r2 += q.Rp * q.Rp;
     q.v_off = v; v += q.Rp;
     q.u0_off = u0; u0 += q.r;
-    // partial sums: one per sweep chunk or per packed-vote block
-    q.chunks = std::max<int64_t>(q.Mp * q.Np / kChunk,
-                                 vote_blocks_per_mat(VA_SBAR, m.rows, m.cols));
+    // partial sums: one per sweep chunk or per vote block
+    q.chunks = std::max<int64_t>({q.Mp * q.Np / kChunk,
+                                  (int64_t)vote_blocks_per_mat(VA_SBAR, m.rows, m.cols),
+                                  (int64_t)tern_vote_blocks_per_mat(VA_SBAR, m.rows, m.cols)});
     q.c_off = c; c += q.chunks;
     q.idx = i;
     umax = std::max<int64_t>(umax, m.elem_off + m.rows * m.cols);
@@ -458,7 +459,8 @@ void pre_scale_stages(const Plan& P, const std::vector<MatPlan>& mp,
         g.gk = (int32_t)(part_kind == 0 ? mp[g.idx0].Mp * mp[g.idx0].Np / 4096
                          : part_kind == 1 ? vote_blocks_per_mat(VA_SBAR, mp[g.idx0].rows,
                                                                 mp[g.idx0].cols)
-                                          : (mn + kTernChunk - 1) / kTernChunk);
+                                          : tern_vote_blocks_per_mat(VA_SBAR, mp[g.idx0].rows,
+                                                                     mp[g.idx0].cols));
         return true;
       }, [&](const Groups& G) { return launch_fro_finalize(G, B.part, hp->eps, B.scal, s); }));
       HIP_TRY(mark(io.prof, SM_PHASE_PRESCALE, s));
@@ -1238,7 +1240,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   va.bits = tern ? nullptr : bits; va.tern = tern_bufs; va.stride = worker_stride_words;
   va.W = W; va.eta = hp->eta; va.status = B.status;
   auto vote_blocks = [tern](int mode, const Group& g) {
-    return tern ? (int32_t)(((int64_t)g.rows * g.cols + kTernChunk - 1) / kTernChunk)
+    return tern ? (int32_t)tern_vote_blocks_per_mat(mode, g.rows, g.cols)
                 : vote_blocks_per_mat(mode, g.rows, g.cols);
   };
   auto vote_fill = [&](Group& g) {

@@ -810,12 +810,83 @@ __global__ __launch_bounds__(256) void k_vote_apply(VoteArgs a) {
 // thread takes 16 consecutive entries of one matrix (kTernChunk per block);
 // the 16 signs of a worker are one 16-byte load when the buffers allow it.
 // ---------------------------------------------------------------------------
+// VA_SBAR over int8 buffers of a tall matrix (stored transposed) whose rows
+// are whole 16-entry pieces: a block takes a tile of 64 rows x 64 columns.
+// Each thread sums one piece (a row, 16 columns) over the M buffers and
+// leaves its majority values in LDS (as bytes, transposed); the block then
+// writes the 64 rows of S the tile covers, 64 entries (128 bytes in
+// bfloat16) per row, 8 consecutive entries per lane.
+constexpr int kTtRows = 64, kTtCols = 64;
+__device__ __forceinline__ float vote_tern_sbar_tall(const VoteArgs& a, const Group& g, int mi,
+                                                     int q) {
+  __shared__ int8_t tv[kTtCols][kTtRows + 8];   // [column][row] of the tile
+  const int rows = g.rows, cols = g.cols;
+  const int tiles_c = (cols + kTtCols - 1) / kTtCols;
+  const int r0 = (q / tiles_c) * kTtRows, c0 = (q % tiles_c) * kTtCols;
+  const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
+  const int lr = threadIdx.x >> 2, pc = (threadIdx.x & 3) * 16;
+  const int row = r0 + lr, col = c0 + pc;
+  float ss = 0.0f;
+  if (row < rows && col < cols) {
+    int acc[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] = 0;
+    const int8_t* src = a.tern + eoff + (int64_t)row * cols + col;
+    const bool vec = (a.stride & 15) == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+    for (int m = 0; m < a.M; ++m) {
+      if (vec) {
+        const u32x4_t w = ld_nt(reinterpret_cast<const u32x4_t*>(src + (int64_t)m * a.stride));
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          acc[k] += (int)(int8_t)((w[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) acc[k] += src[(int64_t)m * a.stride + k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int v = majority(acc[k], a.tie);
+      ss += (float)(v * v);
+      tv[pc + k][lr] = (int8_t)v;
+    }
+  }
+  __syncthreads();
+  const int64_t ld = round_up(rows, kPad);
+  const int64_t xoff = g.x0 + (int64_t)mi * g.x_stride;
+  const int ch = threadIdx.x & 7, rr = r0 + 8 * ch;   // first column of S (row of X)
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int cl = 32 * p + (threadIdx.x >> 3);
+    const int scol = c0 + cl;                        // row of S (column of X)
+    if (scol >= cols || rr >= rows) continue;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (float)tv[cl][8 * ch + j];
+    const int64_t o = xoff + (int64_t)scol * ld + rr;
+    if (rr + 8 <= rows) {
+      store_op8(a.precision, a.o_hi, a.o_lo, o, v);
+    } else {
+      for (int j = 0; j < 8 && rr + j < rows; ++j) store_opv(a.precision, a.o_hi, a.o_lo, o + j, v[j]);
+    }
+  }
+  return ss;
+}
+
 __global__ __launch_bounds__(256) void k_vote_tern(VoteArgs a) {
   if (a.mode == VA_APPLY && a.status && a.status[0] != 0) return;
   int gi, mi, q;
   group_of_block(a.G, blockIdx.x, gi, mi, q);
   const Group& g = a.G.g[gi];
   const int rows = g.rows, cols = g.cols;
+  if (a.mode == VA_SBAR && s_tall(g) && cols % 16 == 0) {
+    const float ss = vote_tern_sbar_tall(a, g, mi, q);
+    if (a.part) {
+      float t = block_sum(ss);
+      if (threadIdx.x == 0) a.part[g.c0 + (int64_t)mi * g.c_stride + q] = t;
+    }
+    return;
+  }
   const int64_t mn = (int64_t)rows * cols;
   const int64_t eoff = g.elem0 + (int64_t)mi * g.elem_stride;
   const int64_t e0 = (int64_t)q * kTernChunk + threadIdx.x * 16;
@@ -913,6 +984,12 @@ __global__ __launch_bounds__(256) void k_vote_tern(VoteArgs a) {
     float t = block_sum(ss);
     if (threadIdx.x == 0) a.part[g.c0 + (int64_t)mi * g.c_stride + q] = t;
   }
+}
+
+int tern_vote_blocks_per_mat(int mode, int64_t rows, int64_t cols) {
+  if (mode == VA_SBAR && rows > cols && cols % 16 == 0)   // tiles of vote_tern_sbar_tall
+    return (int)(((rows + kTtRows - 1) / kTtRows) * ((cols + kTtCols - 1) / kTtCols));
+  return (int)((rows * cols + kTernChunk - 1) / kTernChunk);
 }
 
 int vote_blocks_per_mat(int mode, int64_t rows, int64_t cols) {

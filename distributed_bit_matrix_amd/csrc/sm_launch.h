@@ -139,10 +139,12 @@ struct VoteArgs {
   const int32_t* status;
 };
 hipError_t launch_vote_groups(const VoteArgs& a, hipStream_t s);
-// Group::blocks_per_mat of a vote launch in mode `mode` (packed bits) and
-// of a vote over int8 sign buffers (kTernChunk entries per block, both
-// modes).
+// Group::blocks_per_mat of a vote launch in mode `mode` over packed bits,
+// and over int8 sign buffers (kTernChunk entries per block, or one 64 x 64
+// tile of a tall matrix with whole 16-entry pieces per row in VA_SBAR);
+// also the count of partial sums of squares a VA_SBAR vote leaves.
 int vote_blocks_per_mat(int mode, int64_t rows, int64_t cols);
+int tern_vote_blocks_per_mat(int mode, int64_t rows, int64_t cols);
 constexpr int kTernChunk = 4096;
 
 // Zero the padding of the padded operand copies.

@@ -306,8 +306,8 @@ def test_step_mirrored_storage(name, monkeypatch):
 # 45x71), which the 99.9% agreement cannot absorb; the bfloat16 cases use
 # odd shapes of 15000+ entries, where the emulation gave at most 5.3e-4.
 # (70, 32) and (203, 96) are tall with whole packed words per row: the vote
-# of the post-vote steps writes them through LDS tiles of 64 x 128, here
-# with partial tiles in both directions.
+# of the post-vote steps writes them through LDS tiles (64 x 128 for packed
+# signs, 64 x 64 for int8 ones), here with partial tiles in both directions.
 ODD_TINY = [(5, 37), (33, 7), (45, 71), (64, 19), (3, 3), (70, 32)]
 ODD_BF16 = [(97, 161), (161, 97), (45, 403), (403, 45), (33, 515), (203, 96)]
 ODD = {
@@ -325,6 +325,8 @@ ODD = {
     "normalized_M5": WL.scaled(WL.get("nanogpt_normalized"), ODD_BF16, M=5,
                                name="odd-normalized"),
     "postvote_M5": WL.scaled(WL.get("postvote"), ODD_BF16, M=5, name="odd-postvote"),
+    "prepost_ternary_M5": WL.scaled(WL.get("nanogpt_prepost"), ODD_BF16, M=5,
+                                    name="odd-prepost-ternary").replace(encoding="ternary"),
 }
 
 
