@@ -26,6 +26,7 @@
 // padded to multiples of 128, so no load is predicated and padding
 // contributes exact zeros.
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <type_traits>
 
@@ -418,12 +419,24 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---- block -> (group, matrix, tile), XCD-aware: the 8 XCDs take blocks
-  // round-robin, so consecutive logical tiles are given to one XCD.
-  int nb = A.G.total_blocks;
+  // round-robin, so consecutive logical tiles are given to one XCD: in
+  // chunks of C = xcd_chunk logical blocks (whole matrices) dealt to the
+  // XCDs in turn for as many full rounds of 8 C as fit, and the rest (or
+  // everything, for C = 0) as one contiguous range per XCD.
   int b = blockIdx.x;
   {
-    int per = nb >> 3, rem = nb & 7, x = b & 7, k = b >> 3;
-    b = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + k;
+    const int C = A.xcd_chunk;
+    int x = b & 7, k = b >> 3, base = 0, nb = A.G.total_blocks;
+    const int rounds = C > 0 ? nb / (8 * C) : 0;
+    if (k < rounds * C) {
+      b = (k / C) * 8 * C + x * C + k % C;
+    } else {
+      base = rounds * 8 * C;
+      nb -= base;
+      k -= rounds * C;
+      const int per = nb >> 3, rem = nb & 7;
+      b = base + (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + k;
+    }
   }
   const int gi = find_group(A.G, b);
   const Group& g = A.G.g[gi];
@@ -1632,6 +1645,13 @@ static hipError_t launch_reduce(const GemmArgs& args, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Whole matrices of a Gram launch go to the XCDs in turn unless the
+// environment variable SIGNMUON_XCD_DEAL is "0" (read at every launch).
+static bool xcd_deal_enabled() {
+  const char* e = std::getenv("SIGNMUON_XCD_DEAL");
+  return !(e && std::strcmp(e, "0") == 0);
+}
+
 hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s, hipEvent_t t0,
                        hipEvent_t t1) {
   if (args.G.total_blocks <= 0) return hipSuccess;
@@ -1657,11 +1677,21 @@ hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s, hipEv
       split = true;
     }
   }
+  // Grams (k = the long side, which differs between shapes): whole
+  // matrices to the XCDs in turn when they all have the same block count
+  GemmArgs a = args;
+  a.xcd_chunk = 0;
+  if ((args.epi == E_OP || args.epi == E_RAW) && xcd_deal_enabled()) {
+    int c = args.G.g[0].blocks_per_mat;
+    for (int i = 1; i < args.G.n; ++i)
+      if (args.G.g[i].blocks_per_mat != c) c = 0;
+    a.xcd_chunk = c;
+  }
   hipError_t e;
-  if (tile == CfgWide::BNT) return launch_one<bf16_t, 1, E_UPDATE, true>(args, s, t0, t1);
-  if (precision == P_F32) e = launch_epi<float, 1>(args, s, t0, t1);
-  else if (precision == P_BF16X3) e = launch_epi<bf16_t, 2>(args, s, t0, t1);
-  else e = launch_epi<bf16_t, 1>(args, s, t0, t1);
+  if (tile == CfgWide::BNT) return launch_one<bf16_t, 1, E_UPDATE, true>(a, s, t0, t1);
+  if (precision == P_F32) e = launch_epi<float, 1>(a, s, t0, t1);
+  else if (precision == P_BF16X3) e = launch_epi<bf16_t, 2>(a, s, t0, t1);
+  else e = launch_epi<bf16_t, 1>(a, s, t0, t1);
   if (e != hipSuccess || !split) return e;
   if (args.epi == E_RAW) return launch_reduce<float, 1, true>(args, s);
   if (precision == P_F32) return launch_reduce<float, 1, false>(args, s);

@@ -56,6 +56,10 @@ struct GemmArgs {
   void* W; int32_t w_bf16; float eta;   // O_APPLY
   const int32_t* status;           // O_APPLY is skipped when *status != 0
   float* kpart;                    // split-k partial tiles (groups with ksplit > 1)
+  // Set by launch_gemm: blocks per XCD chunk (0: one contiguous range per
+  // XCD).  Gram launches whose matrices all have C blocks give whole
+  // matrices to the XCDs in turn, so that runs of long and short k mix.
+  int32_t xcd_chunk;
 };
 
 // t0 / t1 (optional): events that take the start and stop time of the GEMM
