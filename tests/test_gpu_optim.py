@@ -67,6 +67,6 @@ def test_synthetic_regression_trains():
         opt.zero_grad(set_to_none=False)
         loss.backward()
         opt.step()
-        losses.append(float(loss))
+        losses.append(float(loss.detach()))
     assert not opt.nonfinite()
     assert np.mean(losses[-10:]) < 0.3 * np.mean(losses[:5]), losses[::10]
