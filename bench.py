@@ -9,7 +9,10 @@ parameter set with all inputs resident in HBM, and prints one JSON line:
 * `value`: steps/s of plain steps (the PolarNS work of different matrix
   groups runs as concurrent chains on the plan's executor);
 * `phases_us` and the `ns_*` / `vote_*` / `momentum_*` rates: instrumented
-  steps with a HIP event after each phase, on the launch stream;
+  steps with a HIP event after each phase, on the launch stream; the
+  momentum sweep and the vote + apply of the pre-sign form are timed by
+  their own kernel start and stop (the interval before each is `hbm_gap`),
+  as are the matrix-core launches outside the concurrent chains (`gap`);
 * `roofline`: the dominant matrix-core kernel, timed per launch between HIP
   events in sequential steps (no executor: each launch alone on the stream);
 * `other_workloads`: the same figures for the other parameter sets (the
@@ -295,6 +298,12 @@ class Run:
                 hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(evs[base + i - 1]),
                                         ctypes.c_void_p(evs[base + i]))
                 name = B.PHASES[kinds[base + i]]
+                # the gap before the sweep or the vote (which the profiled
+                # step times by their own start and stop) is not part of
+                # the Newton-Schulz phase
+                if name == "gap" and i + 1 < p.count and \
+                        B.PHASES[kinds[base + i + 1]] in ("momentum", "vote"):
+                    name = "hbm_gap"
                 phase[name] = phase.get(name, 0.0) + ms.value * 1e3
                 launches.setdefault(name, []).append(ms.value * 1e3)
         for e in ev_list:

@@ -1280,9 +1280,13 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
       io.first_xsrc = XS_USER; io.src_user = Mom;
       io.final_out = tern ? O_TERN : O_BITS; io.bits = local_bits; io.tern = local_tern;
       io.U = nullptr;
-      HIP_TRY(for_launches(groups, sweep_fill,
-                           [&](const Groups& Gs) { sw.G = Gs; return launch_sweep(sw, stream); }));
-      HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
+      // profiled: the sweep's own start and stop times (the interval before
+      // it, with the status launch, closes as a gap)
+      HIP_TRY(for_launches(groups, sweep_fill, [&](const Groups& Gs) {
+        sw.G = Gs;
+        const KernelEvents k = kernel_events(prof, SM_PHASE_MOMENTUM);
+        return launch_sweep(sw, stream, k.t0, k.t1);
+      }));
       st = run_polar(P, mp, groups, fus, hp, B, io, 0, stream, ex, 0);
       if (st != SM_OK) return st;
       if (need_u) {
@@ -1298,9 +1302,10 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
     if (post_vote == 0) {
       va.mode = VA_APPLY;
       HIP_TRY(for_launches(groups, vote_fill, [&](const Groups& Gs) {
-        va.G = Gs; return launch_vote_groups(va, stream);
+        va.G = Gs;
+        const KernelEvents k = kernel_events(prof, SM_PHASE_VOTE);
+        return launch_vote_groups(va, stream, k.t0, k.t1);
       }));
-      HIP_TRY(mark(prof, SM_PHASE_VOTE, stream));
       return SM_OK;
     }
   } else {

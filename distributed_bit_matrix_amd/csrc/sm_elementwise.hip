@@ -4,6 +4,8 @@
 // threshold, blog tie rule), the update of W (Algorithm 1/2 last line), and
 // the small pre-scale kernels of PolarNS (section 4: Frobenius norm or power
 // iteration).  No floating-point atomics: every reduction has a fixed order.
+#include <hip/hip_ext.h>
+
 #include "sm_internal.h"
 #include "sm_launch.h"
 
@@ -459,9 +461,12 @@ __global__ __launch_bounds__(256) void k_sweep(SweepArgs a) {
   }
 }
 
-hipError_t launch_sweep(const SweepArgs& a, hipStream_t s) {
+hipError_t launch_sweep(const SweepArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   if (a.G.total_blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_sweep, dim3(a.G.total_blocks), dim3(256), 0, s, a);
+  if (t0 || t1)
+    hipExtLaunchKernelGGL(k_sweep, dim3(a.G.total_blocks), dim3(256), 0, s, t0, t1, 0, a);
+  else
+    hipLaunchKernelGGL(k_sweep, dim3(a.G.total_blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1000,28 +1005,28 @@ int vote_blocks_per_mat(int mode, int64_t rows, int64_t cols) {
   return (int)(((mn + 31) / 32 + 255) / 256);
 }
 
-hipError_t launch_vote_groups(const VoteArgs& a, hipStream_t s) {
-  if (a.G.total_blocks <= 0) return hipSuccess;
-  dim3 grid(a.G.total_blocks), block(256);
-  if (a.tern) {
-    hipLaunchKernelGGL(k_vote_tern, grid, block, 0, s, a);
-    return hipGetLastError();
-  }
-  if (a.mode == VA_APPLY) {
-    if (a.M <= 15)
-      hipLaunchKernelGGL(k_vote_apply<4>, grid, block, 0, s, a);
-    else if (a.M <= 255)
-      hipLaunchKernelGGL(k_vote_apply<8>, grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL(k_vote_apply<16>, grid, block, 0, s, a);
-    return hipGetLastError();
-  }
-  if (a.M <= 15)
-    hipLaunchKernelGGL(k_vote_groups<4>, grid, block, 0, s, a);
-  else if (a.M <= 255)
-    hipLaunchKernelGGL(k_vote_groups<8>, grid, block, 0, s, a);
+// Launches kernel K (grid, 256 threads) on s; with t0 / t1, events that take
+// the kernel's own start and stop times.
+template <typename K>
+static void launch_timed(K kern, dim3 grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1,
+                         const VoteArgs& a) {
+  if (t0 || t1)
+    hipExtLaunchKernelGGL(kern, grid, dim3(256), 0, s, t0, t1, 0, a);
   else
-    hipLaunchKernelGGL(k_vote_groups<16>, grid, block, 0, s, a);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a);
+}
+
+hipError_t launch_vote_groups(const VoteArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (a.G.total_blocks <= 0) return hipSuccess;
+  const dim3 grid(a.G.total_blocks);
+  if (a.tern)
+    launch_timed(k_vote_tern, grid, s, t0, t1, a);
+  else if (a.mode == VA_APPLY)
+    launch_timed(a.M <= 15 ? k_vote_apply<4> : a.M <= 255 ? k_vote_apply<8> : k_vote_apply<16>,
+                 grid, s, t0, t1, a);
+  else
+    launch_timed(a.M <= 15 ? k_vote_groups<4> : a.M <= 255 ? k_vote_groups<8> : k_vote_groups<16>,
+                 grid, s, t0, t1, a);
   return hipGetLastError();
 }
 

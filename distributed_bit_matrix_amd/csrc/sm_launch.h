@@ -110,7 +110,10 @@ struct SweepArgs {
   float* part;          // partial sums per chunk, NULL to skip
   int32_t* status;      // non-finite flag, NULL to skip
 };
-hipError_t launch_sweep(const SweepArgs& a, hipStream_t s);
+// t0 / t1 (optional, here and for the vote): events that take the kernel's
+// own start and stop times
+hipError_t launch_sweep(const SweepArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
+                        hipEvent_t t1 = nullptr);
 
 // Momentum with the signs of the new momentum packed into `bits` (post-vote
 // variant and K = 0).
@@ -142,7 +145,8 @@ struct VoteArgs {
   void* o_hi; void* o_lo; float* part;
   const int32_t* status;
 };
-hipError_t launch_vote_groups(const VoteArgs& a, hipStream_t s);
+hipError_t launch_vote_groups(const VoteArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
+                              hipEvent_t t1 = nullptr);
 // Group::blocks_per_mat of a vote launch in mode `mode` over packed bits,
 // and over int8 sign buffers (kTernChunk entries per block, or one 64 x 64
 // tile of a tall matrix with whole 16-entry pieces per row in VA_SBAR);

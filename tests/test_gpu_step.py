@@ -603,8 +603,9 @@ def _events(n):
                                              ("resnet50", False)])
 def test_step_profiled_matches_plain(name, concurrent, monkeypatch):
     # signmuon_step_profiled does the same work as signmuon_step (bit-exact
-    # results) and records its events in order: phases, and without the
-    # concurrent chains one gap + kernel pair per matrix-core launch
+    # results) and records its events in order: phases, and one gap + kernel
+    # pair per sweep and vote launch and, without the concurrent chains, per
+    # matrix-core launch
     import ctypes
     if concurrent:
         monkeypatch.setenv("SIGNMUON_CHAIN_MIN_GFLOP", "0")   # chains even for this small set
@@ -652,6 +653,10 @@ def test_step_profiled_matches_plain(name, concurrent, monkeypatch):
                                        ctypes.c_void_p(evs[i])) == 0
         assert ms.value >= -1e-3
     kernel = [k for k in ks if k in (6, 7, 8)]
+    # the momentum sweep and the vote + apply take their own start and stop
+    # events, each opened by a gap
+    for k in (1, 5):
+        assert ks.count(k) >= 1 and all(ks[i - 1] == 9 for i, x in enumerate(ks) if x == k)
     if concurrent and name == "nanogpt":
         assert not kernel and 3 in ks                # one Newton-Schulz phase
     else:
