@@ -1482,6 +1482,9 @@ __global__ __launch_bounds__(256) void k_split_reduce(GemmArgs A) {
 #ifndef SM_OP_WPE
 #define SM_OP_WPE 2
 #endif
+#ifndef SM_SPLIT_MIN_SLABS_F32
+#define SM_SPLIT_MIN_SLABS_F32 2
+#endif
 #ifndef SM_SQ_TRACC
 #define SM_SQ_TRACC 1
 #endif
@@ -1592,10 +1595,13 @@ static_assert(Cfg<bf16_t, 1, E_OP>::BMT == kTileSym && Cfg<bf16_t, 2, E_OP>::BMT
                   Cfg<float, 1, E_OP>::BMT == kTileSym && Cfg<bf16_t, 1, E_OP>::BNT == kTileSym,
               "symmetric tile");
 
-// Slabs of at least this many per split; splits only while the launch has
-// fewer than kSplitBelow upper-triangular tiles, up to kSplitTarget blocks
-// and kSplitMax splits.
-constexpr int kSplitMinSlabs = 8, kSplitBelow = 128, kSplitTarget = 256, kSplitMax = 16;
+// Slabs of at least kSplitMinSlabs per split (float32: kSplitMinSlabsF32,
+// since a float32 slab carries eight times the matrix-core time of a
+// bfloat16 one: half the k at a sixteenth of the rate); splits only while
+// the launch has fewer than kSplitBelow upper-triangular tiles, up to
+// kSplitTarget blocks and kSplitMax splits.
+constexpr int kSplitMinSlabs = 8, kSplitMinSlabsF32 = SM_SPLIT_MIN_SLABS_F32, kSplitBelow = 128,
+              kSplitTarget = 256, kSplitMax = 16;
 
 static int64_t sym_slabs(int precision, int64_t gk) {
   return gk / (precision == P_F32 ? Cfg<float, 1, E_OP>::RB / 4 : Cfg<bf16_t, 1, E_OP>::RB / 2);
@@ -1605,9 +1611,10 @@ int gemm_sym_ksplit(int precision, int64_t rp, int64_t gk, int64_t count, int* s
   const int64_t T = rp / kTileSym, tiles = T * (T + 1) / 2 * count;
   const int64_t nslab = sym_slabs(precision, gk);
   *slabs = (int)nslab;
-  if (tiles >= kSplitBelow || nslab < 2 * kSplitMinSlabs) return 1;
+  const int64_t least = precision == P_F32 ? kSplitMinSlabsF32 : kSplitMinSlabs;
+  if (tiles >= kSplitBelow || nslab < 2 * least) return 1;
   int64_t want = (kSplitTarget + tiles - 1) / tiles;
-  want = std::min<int64_t>({want, nslab / kSplitMinSlabs, (int64_t)kSplitMax});
+  want = std::min<int64_t>({want, nslab / least, (int64_t)kSplitMax});
   if (want < 2) return 1;
   // splits of `per` slabs, per even; the last one is shorter but not empty
   int64_t per = (nslab + want - 1) / want;
