@@ -1482,6 +1482,9 @@ __global__ __launch_bounds__(256) void k_split_reduce(GemmArgs A) {
 #ifndef SM_OP_WPE
 #define SM_OP_WPE 2
 #endif
+#ifndef SM_SPLIT_MIN_SLABS
+#define SM_SPLIT_MIN_SLABS 8
+#endif
 #ifndef SM_SPLIT_MIN_SLABS_F32
 #define SM_SPLIT_MIN_SLABS_F32 2
 #endif
@@ -1600,7 +1603,8 @@ static_assert(Cfg<bf16_t, 1, E_OP>::BMT == kTileSym && Cfg<bf16_t, 2, E_OP>::BMT
 // bfloat16 one: half the k at a sixteenth of the rate); splits only while
 // the launch has fewer than kSplitBelow upper-triangular tiles, up to
 // kSplitTarget blocks and kSplitMax splits.
-constexpr int kSplitMinSlabs = 8, kSplitMinSlabsF32 = SM_SPLIT_MIN_SLABS_F32, kSplitBelow = 128,
+constexpr int kSplitMinSlabs = SM_SPLIT_MIN_SLABS, kSplitMinSlabsF32 = SM_SPLIT_MIN_SLABS_F32,
+              kSplitBelow = 128,
               kSplitTarget = 256, kSplitMax = 16;
 
 static int64_t sym_slabs(int precision, int64_t gk) {
