@@ -10,9 +10,9 @@ parameter set with all inputs resident in HBM, and prints one JSON line:
   groups runs as concurrent chains on the plan's executor);
 * `phases_us` and the `ns_*` / `vote_*` / `momentum_*` rates: instrumented
   steps with a HIP event after each phase, on the launch stream; the
-  momentum sweep and the vote + apply of the pre-sign form are timed by
-  their own kernel start and stop (the interval before each is `hbm_gap`),
-  as are the matrix-core launches outside the concurrent chains (`gap`);
+  momentum pass and every vote launch are timed by their own kernel start
+  and stop (the interval before each is `hbm_gap`), as are the matrix-core
+  launches outside the concurrent chains (`gap`);
 * `roofline`: the dominant matrix-core kernel, timed per launch between HIP
   events in sequential steps (no executor: each launch alone on the stream);
 * `other_workloads`: the same figures for the other parameter sets (the
@@ -390,8 +390,11 @@ def workload_metrics(w, d, elapsed, K, phase_us):
         out["vote_apply_frac_hbm"] = round(vb / (phase_us["vote"] * 1e-6) / 1e9 /
                                            PEAK_HBM_GBPS, 4)
     elif phase_us.get("vote"):
-        # majority matrix written into the bfloat16 operand copy
+        # majority matrix written into the bfloat16 operand copy (the
+        # normalized step then votes again, applying c D to W)
         vb = (w.M * sign_bytes + 2) * d
+        if w.post_vote == 3:
+            vb += (w.M * sign_bytes + 2 * wbytes) * d
         out["vote_gbps"] = round(vb / (phase_us["vote"] * 1e-6) / 1e9, 1)
         out["vote_frac_hbm"] = round(vb / (phase_us["vote"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
     if phase_us.get("momentum"):

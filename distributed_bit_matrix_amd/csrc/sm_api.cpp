@@ -1262,8 +1262,11 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
       HIP_TRY(for_launches(groups, [&](Group& g) {
         g.blocks_per_mat = (int32_t)(((int64_t)g.rows * g.cols + kChunk - 1) / kChunk);
         return true;
-      }, [&](const Groups& Gs) { ms.G = Gs; return launch_momentum_sign(ms, stream); }));
-      HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
+      }, [&](const Groups& Gs) {
+        ms.G = Gs;
+        const KernelEvents k = kernel_events(prof, SM_PHASE_MOMENTUM);
+        return launch_momentum_sign(ms, stream, k.t0, k.t1);
+      }));
     } else {
       SweepArgs sw;
       std::memset(&sw, 0, sizeof(sw));
@@ -1318,8 +1321,11 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
     HIP_TRY(for_launches(groups, [&](Group& g) {
       g.blocks_per_mat = (int32_t)(((int64_t)g.rows * g.cols + kChunk - 1) / kChunk);
       return true;
-    }, [&](const Groups& Gs) { ms.G = Gs; return launch_momentum_sign(ms, stream); }));
-    HIP_TRY(mark(prof, SM_PHASE_MOMENTUM, stream));
+    }, [&](const Groups& Gs) {
+      ms.G = Gs;
+      const KernelEvents k = kernel_events(prof, SM_PHASE_MOMENTUM);
+      return launch_momentum_sign(ms, stream, k.t0, k.t1);
+    }));
     if (pipeline_only) return SM_OK;
   }
 
@@ -1341,9 +1347,10 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   va.o_hi = B.x[0][0]; va.o_lo = B.x[0][1];
   va.part = B.part;
   HIP_TRY(for_launches(groups, vote_fill, [&](const Groups& Gs) {
-    va.G = Gs; return launch_vote_groups(va, stream);
+    va.G = Gs;
+    const KernelEvents k = kernel_events(prof, SM_PHASE_VOTE);
+    return launch_vote_groups(va, stream, k.t0, k.t1);
   }));
-  HIP_TRY(mark(prof, SM_PHASE_VOTE, stream));
   io.first_xsrc = XS_OP; io.src_user = nullptr;
   io.final_out = O_APPLY;
   if (post_vote != 3 && hp->K > 0) {
@@ -1370,9 +1377,10 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   va.mode = VA_APPLY;
   va.scal = B.scal;
   HIP_TRY(for_launches(groups, vote_fill, [&](const Groups& Gs) {
-    va.G = Gs; return launch_vote_groups(va, stream);
+    va.G = Gs;
+    const KernelEvents k = kernel_events(prof, SM_PHASE_VOTE);
+    return launch_vote_groups(va, stream, k.t0, k.t1);
   }));
-  HIP_TRY(mark(prof, SM_PHASE_VOTE, stream));
   return SM_OK;
 }
 }  // namespace

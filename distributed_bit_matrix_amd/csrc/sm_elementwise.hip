@@ -518,9 +518,13 @@ __global__ __launch_bounds__(256) void k_momentum_sign(MomSignArgs a) {
   if (bad && a.status) a.status[0] = 1;
 }
 
-hipError_t launch_momentum_sign(const MomSignArgs& a, hipStream_t s) {
+hipError_t launch_momentum_sign(const MomSignArgs& a, hipStream_t s, hipEvent_t t0,
+                                hipEvent_t t1) {
   if (a.G.total_blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_momentum_sign, dim3(a.G.total_blocks), dim3(256), 0, s, a);
+  if (t0 || t1)
+    hipExtLaunchKernelGGL(k_momentum_sign, dim3(a.G.total_blocks), dim3(256), 0, s, t0, t1, 0, a);
+  else
+    hipLaunchKernelGGL(k_momentum_sign, dim3(a.G.total_blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

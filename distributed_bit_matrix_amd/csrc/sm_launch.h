@@ -125,7 +125,8 @@ struct MomSignArgs {
   int8_t* tern;         // non-NULL: int8 signs (sign(0) = 0) instead of bits
   int32_t* status;
 };
-hipError_t launch_momentum_sign(const MomSignArgs& a, hipStream_t s);
+hipError_t launch_momentum_sign(const MomSignArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
+                                hipEvent_t t1 = nullptr);
 
 // Vote over M buffers per matrix: mode VA_APPLY updates W, VA_SBAR writes
 // the majority matrix into the padded operand (+ partial sums of squares).

@@ -327,10 +327,10 @@ sm_status signmuon_worker_pipeline(const sm_matrix *mats, int32_t n_mats,
  * Instrumented step: identical work to signmuon_step, plus a hipEventRecord
  * on `stream` after each phase so a caller can time the kernels of one step
  * (events[i] closes the phase kinds[i]; the first event opens the step).
- * Matrix-core launches outside the concurrent chains, and the momentum
- * sweep and the vote + apply of the pre-sign form, take two events that the
- * kernel itself sets to its start and stop time (hipExtLaunchKernel): the
- * first closes an SM_PHASE_GAP interval, the second the kernel's own
+ * Matrix-core launches outside the concurrent chains, the momentum pass
+ * (sweep, or momentum + signs) and every vote launch take two events that
+ * the kernel itself sets to its start and stop time (hipExtLaunchKernel):
+ * the first closes an SM_PHASE_GAP interval, the second the kernel's own
  * duration (SM_PHASE_GRAM / SQUARE / UPDATE / MOMENTUM / VOTE).
  * events[capacity]: caller-created events (HOST array of handles);
  * kinds[capacity]: HOST array receiving the phase of each event
@@ -353,7 +353,9 @@ typedef enum sm_phase {
   SM_PHASE_UPDATE = 8,    /* update B S, or the final product Q_K S_0 */
   SM_PHASE_GAP = 9        /* the interval before a kernel with its own start
                              and stop events starts (launch gap; a split-k
-                             reduction; before the sweep, the status launch) */
+                             reduction; before the momentum pass, the status
+                             launch; before the post-vote vote, the padding
+                             launch) */
 } sm_phase;
 typedef struct sm_profile {
   hipEvent_t *events;

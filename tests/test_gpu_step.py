@@ -600,7 +600,7 @@ def _events(n):
 
 
 @pytest.mark.parametrize("name,concurrent", [("nanogpt", True), ("nanogpt", False),
-                                             ("resnet50", False)])
+                                             ("resnet50", False), ("postvote", False)])
 def test_step_profiled_matches_plain(name, concurrent, monkeypatch):
     # signmuon_step_profiled does the same work as signmuon_step (bit-exact
     # results) and records its events in order: phases, and one gap + kernel
