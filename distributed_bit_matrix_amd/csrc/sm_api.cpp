@@ -82,7 +82,7 @@ bool sym_upper_enabled() {
 
 // Per-matrix placement.  Returns SM_OK or SM_EINVAL for unusable shapes.
 sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
-                     int post_vote, bool need_u, Plan& P,
+                     int post_vote, Plan& P,
                      std::vector<MatPlan>& mp) {
   mp.assign(nm, MatPlan{});
   P = Plan{};
@@ -97,7 +97,7 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
   P.gram_space = P.precision == P_BF16 && !P.quintic && !P.spectral && hp->K > 0 &&
                  gram_space_enabled();
   P.upper = P.precision == P_BF16 && sym_upper_enabled();
-  int64_t x = 0, r2 = 0, v = 0, c = 0, u0 = 0, umax = 0;
+  int64_t x = 0, r2 = 0, v = 0, c = 0, u0 = 0;
   for (int i = 0; i < nm; ++i) {
     const sm_matrix& m = mats[i];
     if (m.rows < 1 || m.cols < 1 || m.rows > kMaxDim || m.cols > kMaxDim) return SM_EINVAL;
@@ -122,7 +122,6 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
                                   (int64_t)tern_vote_blocks_per_mat(VA_SBAR, m.rows, m.cols)});
     q.c_off = c; c += q.chunks;
     q.idx = i;
-    umax = std::max<int64_t>(umax, m.elem_off + m.rows * m.cols);
   }
   // split-k of the long-k Grams of shapes with few triangular tiles (the
   // decision counts every matrix of the shape, as one launch holds them)
@@ -180,7 +179,6 @@ sm_status build_plan(const sm_matrix* mats, int nm, const sm_hparams* hp,
   if ((ns || power) && kp > 0) P.off_kpart = take(kp * 4);
   if (P.gram_space) P.off_gs = take(5 * r2 * 2);
   P.off_scal = take((size_t)nm * 4);
-  if (need_u) P.off_u = take(umax * 4);
   P.total = off;
   return SM_OK;
 }
@@ -294,7 +292,6 @@ struct Bufs {
   float* kpart;
   void* gs[5];     // Gram-space A_even, A_odd, T, Q_even, Q_odd
   float* scal;
-  float* u;
 };
 
 Bufs bind(const Plan& P, void* ws) {
@@ -317,7 +314,6 @@ Bufs bind(const Plan& P, void* ws) {
   for (int j = 0; j < 5; ++j)
     B.gs[j] = P.off_gs ? B.base + P.off_gs + (size_t)j * P.r_total * 2 : nullptr;
   B.scal = static_cast<float*>(at(P.off_scal));
-  B.u = static_cast<float*>(at(P.off_u));
   return B;
 }
 
@@ -372,9 +368,8 @@ hipError_t launch_gemm_timed(int precision, const GemmArgs& a, hipStream_t s, sm
 //   first: XS_USER (the first a X term from src_user, the caller's float32
 //   source, e.g. the momentum) or XS_OP (from the operand copy, e.g. the
 //   majority matrix, whose entries the operand holds exactly).
-//   final: O_U (write U), O_BITS (pack into bits), O_APPLY (update W).
-// `fusable[i]` says whether matrix i may use O_BITS; others write U into
-// the workspace and are packed afterwards.
+//   final: O_U (write U), O_BITS (pack into bits), O_TERN (int8 signs),
+//   O_APPLY (update W).
 // ---------------------------------------------------------------------------
 struct NsIO {
   int first_xsrc;
@@ -622,7 +617,7 @@ hipError_t run_square(const Plan& P, const std::vector<MatPlan>& mp,
 // For a matrix m x n this executes about 2 m^2 n + 12 m^3 (upper-triangular)
 // flops instead of 5 x 3 m^2 n for K = 5.
 void gram_space_stages(const Plan& P, const std::vector<MatPlan>& mp,
-                       const std::vector<Group>& groups, const std::vector<bool>& fusable,
+                       const std::vector<Group>& groups,
                        const sm_hparams* hp, Bufs& B, const NsIO& io, hipStream_t s,
                        Stages& out) {
   const int prec = P.precision;
@@ -673,37 +668,27 @@ void gram_space_stages(const Plan& P, const std::vector<MatPlan>& mp,
   void* const QK = Qbuf[K & 1];
   // X_K = c Q_K S_0 into the requested output
   out.push_back([&, QK, prec, s]() -> sm_status {
-    for (int pass = 0; pass < 2; ++pass) {
-      // pass 0: matrices using the requested final output; pass 1: the
-      // unfusable ones writing U into the workspace
-      if (pass == 1 && io.final_out != O_BITS) break;
-      HIP_TRY(for_launches(groups, [&](Group& g) {
-        const MatPlan& q = mp[g.idx0];
-        if (io.final_out == O_BITS && fusable[g.idx0] != (pass == 0)) return false;
-        g.gm = (int32_t)q.Rp; g.gn = (int32_t)(q.tall ? q.Mp : q.Np);
-        g.gk = (int32_t)q.Rp;
-        set_gemm_tiles(g, prec, E_UPDATE);
-        g.ops = gemm_ops(FAM_R, FAM_XK);
-        return true;
-      }, [&](const Groups& G) {
-        GemmArgs a;
-        std::memset(&a, 0, sizeof(a));
-        a.G = G;
-        a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
-        a.r_hi = QK;
-        a.epi = E_UPDATE; a.upper = P.upper; a.ca = 0.0f; a.xsrc = XS_OP;
-        a.scal = B.scal; a.scal_pow = 1;
-        if (io.final_out == O_BITS && pass == 1) {
-          a.out = O_U; a.U = B.u;
-        } else {
-          a.out = io.final_out;
-          a.U = io.U; a.bits = io.bits; a.tern = io.tern;
-          a.W = io.W; a.w_bf16 = io.w_bf16; a.eta = io.eta;
-          a.status = io.status;
-        }
-        return launch_gemm_timed(prec, a, s, io.prof, SM_PHASE_UPDATE);
-      }));
-    }
+    HIP_TRY(for_launches(groups, [&](Group& g) {
+      const MatPlan& q = mp[g.idx0];
+      g.gm = (int32_t)q.Rp; g.gn = (int32_t)(q.tall ? q.Mp : q.Np);
+      g.gk = (int32_t)q.Rp;
+      set_gemm_tiles(g, prec, E_UPDATE);
+      g.ops = gemm_ops(FAM_R, FAM_XK);
+      return true;
+    }, [&](const Groups& G) {
+      GemmArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.G = G;
+      a.x_hi = B.x[0][0]; a.x_lo = B.x[0][1];
+      a.r_hi = QK;
+      a.epi = E_UPDATE; a.upper = P.upper; a.ca = 0.0f; a.xsrc = XS_OP;
+      a.scal = B.scal; a.scal_pow = 1;
+      a.out = io.final_out;
+      a.U = io.U; a.bits = io.bits; a.tern = io.tern;
+      a.W = io.W; a.w_bf16 = io.w_bf16; a.eta = io.eta;
+      a.status = io.status;
+      return launch_gemm_timed(prec, a, s, io.prof, SM_PHASE_UPDATE);
+    }));
     return SM_OK;
   });
 }
@@ -711,10 +696,10 @@ void gram_space_stages(const Plan& P, const std::vector<MatPlan>& mp,
 // The K Newton-Schulz steps: step k reads the iterate from x[(k-1) & 1]
 // and writes x[k & 1] (the last one writes the final output instead).
 void ns_stages(const Plan& P, const std::vector<MatPlan>& mp,
-               const std::vector<Group>& groups, const std::vector<bool>& fusable,
+               const std::vector<Group>& groups,
                const sm_hparams* hp, Bufs& B, const NsIO& io, hipStream_t s, Stages& out) {
   if (P.gram_space) {
-    gram_space_stages(P, mp, groups, fusable, hp, B, io, s, out);
+    gram_space_stages(P, mp, groups, hp, B, io, s, out);
     return;
   }
   const int prec = P.precision;
@@ -754,52 +739,44 @@ void ns_stages(const Plan& P, const std::vector<MatPlan>& mp,
     // update: S <- a S + B S
     out.push_back([&, hp, k, K, cur, prec, s]() -> sm_status {
       const bool last = k == K;
-      for (int pass = 0; pass < 2; ++pass) {
-        // pass 0: matrices using the requested final output; pass 1: the
-        // unfusable ones writing U into the workspace (only when last).
-        if (pass == 1 && !(last && io.final_out == O_BITS)) break;
-          HIP_TRY(for_launches(groups, [&](Group& g) {
-          const MatPlan& q = mp[g.idx0];
-          if (last && io.final_out == O_BITS && fusable[g.idx0] != (pass == 0)) return false;
-          g.gm = (int32_t)q.Rp; g.gn = (int32_t)(q.tall ? q.Mp : q.Np);
-          g.gk = (int32_t)q.Rp;
-          set_gemm_tiles(g, prec, E_UPDATE);
-          g.ops = gemm_ops(FAM_R, FAM_XK);
-          return true;
-        }, [&](const Groups& G) {
-          GemmArgs a;
-          std::memset(&a, 0, sizeof(a));
-          a.G = G;
-          a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
-          a.r_hi = B.b[0]; a.r_lo = B.b[1];
-          a.epi = E_UPDATE; a.upper = P.upper; a.ca = hp->ns_a;
-          a.xsrc = k == 1 ? io.first_xsrc : XS_OP;
-          a.xs_user = io.src_user;
-          a.scal = B.scal; a.scal_pow = k == 1 ? 1 : 0;
-          if (!last) {
-            a.out = O_X;
-            a.o_hi = B.x[cur ^ 1][0]; a.o_lo = B.x[cur ^ 1][1];
-          } else if (io.final_out == O_BITS && pass == 1) {
-            a.out = O_U; a.U = B.u;
-          } else {
-            a.out = io.final_out;
-            a.U = io.U; a.bits = io.bits; a.tern = io.tern;
-            a.W = io.W; a.w_bf16 = io.w_bf16; a.eta = io.eta;
-            a.status = io.status;
-          }
-          return launch_gemm_timed(prec, a, s, io.prof, SM_PHASE_UPDATE);
-        }));
-      }
+      HIP_TRY(for_launches(groups, [&](Group& g) {
+        const MatPlan& q = mp[g.idx0];
+        g.gm = (int32_t)q.Rp; g.gn = (int32_t)(q.tall ? q.Mp : q.Np);
+        g.gk = (int32_t)q.Rp;
+        set_gemm_tiles(g, prec, E_UPDATE);
+        g.ops = gemm_ops(FAM_R, FAM_XK);
+        return true;
+      }, [&](const Groups& G) {
+        GemmArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.G = G;
+        a.x_hi = B.x[cur][0]; a.x_lo = B.x[cur][1];
+        a.r_hi = B.b[0]; a.r_lo = B.b[1];
+        a.epi = E_UPDATE; a.upper = P.upper; a.ca = hp->ns_a;
+        a.xsrc = k == 1 ? io.first_xsrc : XS_OP;
+        a.xs_user = io.src_user;
+        a.scal = B.scal; a.scal_pow = k == 1 ? 1 : 0;
+        if (!last) {
+          a.out = O_X;
+          a.o_hi = B.x[cur ^ 1][0]; a.o_lo = B.x[cur ^ 1][1];
+        } else {
+          a.out = io.final_out;
+          a.U = io.U; a.bits = io.bits; a.tern = io.tern;
+          a.W = io.W; a.w_bf16 = io.w_bf16; a.eta = io.eta;
+          a.status = io.status;
+        }
+        return launch_gemm_timed(prec, a, s, io.prof, SM_PHASE_UPDATE);
+      }));
       return SM_OK;
     });
   }
 }
 
 sm_status run_ns(const Plan& P, const std::vector<MatPlan>& mp,
-                 const std::vector<Group>& groups, const std::vector<bool>& fusable,
+                 const std::vector<Group>& groups,
                  const sm_hparams* hp, Bufs& B, const NsIO& io, hipStream_t s) {
   Stages st;
-  ns_stages(P, mp, groups, fusable, hp, B, io, s, st);
+  ns_stages(P, mp, groups, hp, B, io, s, st);
   return run_stages(st);
 }
 
@@ -851,7 +828,7 @@ struct sm_executor {
 namespace {
 
 sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
-                    const std::vector<Group>& groups, const std::vector<bool>& fusable,
+                    const std::vector<Group>& groups,
                     const sm_hparams* hp, Bufs& B, const NsIO& io, int part_kind,
                     hipStream_t s, sm_executor* ex, int pass) {
   // Sets with little Newton-Schulz work are bound by the host's launch
@@ -873,7 +850,7 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
   if (nc <= 1) {
     Stages st;
     pre_scale_stages(P, mp, groups, hp, B, io, part_kind, s, st);
-    if (hp->K > 0) ns_stages(P, mp, groups, fusable, hp, B, io, s, st);
+    if (hp->K > 0) ns_stages(P, mp, groups, hp, B, io, s, st);
     return run_stages(st);
   }
   // longest-processing-time assignment of the groups to the chains, by
@@ -903,7 +880,7 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
   for (int c = 0; c < nc; ++c) {
     hipStream_t cs = R->s[c];
     pre_scale_stages(P, mp, chain[c], hp, B, cio, part_kind, cs, prog[c]);
-    if (hp->K > 0) ns_stages(P, mp, chain[c], fusable, hp, B, cio, cs, prog[c]);
+    if (hp->K > 0) ns_stages(P, mp, chain[c], hp, B, cio, cs, prog[c]);
   }
   sm_status st = SM_OK;
   int forked = 0;
@@ -1034,7 +1011,7 @@ size_t signmuon_polar_ns_workspace(int64_t rows, int64_t cols, const sm_hparams*
   sm_matrix m{rows, cols, 0, 0};
   Plan P;
   std::vector<MatPlan> mp;
-  if (build_plan(&m, 1, hp, 0, false, P, mp) != SM_OK) return 0;
+  if (build_plan(&m, 1, hp, 0, P, mp) != SM_OK) return 0;
   return P.total;
 }
 
@@ -1047,7 +1024,7 @@ sm_status signmuon_polar_ns(const float* X, float* U, int64_t rows, int64_t cols
   sm_matrix m{rows, cols, 0, 0};
   Plan P;
   std::vector<MatPlan> mp;
-  st = build_plan(&m, 1, hp, 0, false, P, mp);
+  st = build_plan(&m, 1, hp, 0, P, mp);
   if (st != SM_OK) return st;
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < P.total)
     return SM_EWORKSPACE;
@@ -1078,8 +1055,7 @@ sm_status signmuon_polar_ns(const float* X, float* U, int64_t rows, int64_t cols
     }, [&](const Groups& G) { so.G = G; return launch_scaled_out(so, stream); }));
     return SM_OK;
   }
-  std::vector<bool> fus(1, true);
-  return run_ns(P, mp, groups, fus, hp, B, io, stream);
+  return run_ns(P, mp, groups, hp, B, io, stream);
 }
 
 }  // extern "C"
@@ -1136,14 +1112,9 @@ size_t signmuon_step_workspace(const sm_matrix* mats, int32_t n_mats,
   if (check_hparams(hp, true) != SM_OK) return 0;
   if (post_vote < 0 || post_vote > 3) return 0;
   if (post_vote == 3 && (hp->P < 1 || hp->P > 256)) return 0;
-  bool need_u = false;
-  for (int i = 0; i < n_mats; ++i)
-    if (post_vote != 1 && hp->K > 0 && mats[i].cols % 32 != 0 &&
-        hp->sign_encoding == SM_SIGNS_PACKED)
-      need_u = true;
   Plan P;
   std::vector<MatPlan> mp;
-  if (build_plan(mats, n_mats, hp, post_vote, need_u, P, mp) != SM_OK) return 0;
+  if (build_plan(mats, n_mats, hp, post_vote, P, mp) != SM_OK) return 0;
   return P.total;
 }
 
@@ -1192,17 +1163,11 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
     for (int i = 1; i < n_mats; ++i)
       if (es[i].first < es[i - 1].second || wsg[i].first < wsg[i - 1].second) return SM_EINVAL;
   }
-  // packed signs are written from the last epilogue for widths that are a
-  // multiple of 32 (else from U in the workspace); int8 signs always are
-  std::vector<bool> fus(n_mats);
-  bool need_u = false;
-  for (int i = 0; i < n_mats; ++i) {
-    fus[i] = tern || mats[i].cols % 32 == 0;
-    if (post_vote != 1 && hp->K > 0 && !fus[i]) need_u = true;
-  }
+  // the signs (packed or int8) are written from the last epilogue for every
+  // width (packed words that span two lines of X take their bits by atomics)
   Plan P;
   std::vector<MatPlan> mp;
-  st = build_plan(mats, n_mats, hp, post_vote, need_u, P, mp);
+  st = build_plan(mats, n_mats, hp, post_vote, P, mp);
   if (st != SM_OK) return st;
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < P.total)
     return SM_EWORKSPACE;
@@ -1290,16 +1255,8 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
         const KernelEvents k = kernel_events(prof, SM_PHASE_MOMENTUM);
         return launch_sweep(sw, stream, k.t0, k.t1);
       }));
-      st = run_polar(P, mp, groups, fus, hp, B, io, 0, stream, ex, 0);
+      st = run_polar(P, mp, groups, hp, B, io, 0, stream, ex, 0);
       if (st != SM_OK) return st;
-      if (need_u) {
-        for (int i = 0; i < n_mats; ++i) {
-          if (fus[i]) continue;
-          HIP_TRY(launch_sign_pack_flat(B.u + mats[i].elem_off, local_bits + mats[i].word_off,
-                                        mats[i].rows * mats[i].cols, stream));
-        }
-        HIP_TRY(mark(prof, SM_PHASE_PACK, stream));
-      }
     }
     if (pipeline_only) return SM_OK;
     if (post_vote == 0) {
@@ -1354,8 +1311,7 @@ sm_status step_impl(const sm_matrix* mats, int32_t n_mats, const sm_hparams* hp,
   io.first_xsrc = XS_OP; io.src_user = nullptr;
   io.final_out = O_APPLY;
   if (post_vote != 3 && hp->K > 0) {
-    std::vector<bool> fus_all(n_mats, true);
-    return run_polar(P, mp, groups, fus_all, hp, B, io, tern ? 2 : 1, stream, ex,
+    return run_polar(P, mp, groups, hp, B, io, tern ? 2 : 1, stream, ex,
                      post_vote == 2 ? 1 : 0);
   }
   // W <- W - eta c S with c = 1/(s + eps): the post-vote step with K = 0, or

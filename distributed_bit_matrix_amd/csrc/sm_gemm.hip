@@ -1297,10 +1297,36 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
           }
     } else {
       // O_BITS: entrywise sign packed into 32-bit words along the rows of
-      // X (cols % 32 == 0): along the rows of S, or down its columns when
-      // X is tall.  A word covers two neighbouring tiles.
+      // X: along the rows of S, or down its columns when X is tall.  With
+      // cols % 32 == 0 a word covers two neighbouring tiles of one line.
       const int64_t woff = g.word0 + (int64_t)mi * g.word_stride;
-      if (tall == SWAP) {
+      if (cols % 32 != 0) {
+        // a word may take bits from two lines of X, and so from other
+        // blocks: each entry sets or clears its own bit with an atomic
+        // (bitwise, so the order does not matter), and the matrix's last
+        // entry also clears the bits of its word past the end
+        const int64_t last = (int64_t)rows * cols - 1;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int si = acc_row(i, r), sj = acc_col(j, r);
+              if (si < sr && sj < sc) {
+                const int64_t e = tall ? (int64_t)sj * cols + si : (int64_t)si * cols + sj;
+                uint32_t* w = A.bits + woff + (e >> 5);
+                const uint32_t bit = 1u << (e & 31);
+                const uint32_t keep = e == last ? (bit << 1) - 1u : 0xFFFFFFFFu;
+                if (acc[i][j][r] < 0.0f) {
+                  atomicOr(w, bit);
+                  if (keep != 0xFFFFFFFFu) atomicAnd(w, keep);
+                } else {
+                  atomicAnd(w, ~bit & keep);
+                }
+              }
+            }
+      } else if (tall == SWAP) {
         // lanes 0..15 of a tile run along the word: a wave ballot of
         // register r gives 4 x 16 sign bits, one 16-bit half-word for each
         // lane group q, and lane q < 4 writes the word of line 4 q + r

@@ -144,7 +144,6 @@ struct Plan {
   size_t off_kpart = 0;       // split-k partial Gram tiles, kp_total floats
   size_t off_gs = 0;          // Gram-space A, A', T, Q, Q' (bfloat16, r_total each)
   size_t off_scal = 0;        // per-matrix c = 1/(s+eps)
-  size_t off_u = 0;           // float32 polar factor (unfused paths)
   size_t off_status = 0;      // int32 status word
   size_t total = 0;
 };

@@ -197,10 +197,12 @@ def test_step_workspace_post_vote_modes():
     assert B.step_workspace(mats, hp, 1) > 0
     assert B.step_workspace(mats, hp, 4) == 0
     assert B.step_workspace(mats, hp, -1) == 0
-    # widths that are not multiples of 32 keep a float32 U for the separate
-    # packing pass of the pre-sign polar factor (0 and 2 only)
+    # widths that are not multiples of 32 pack their signs in the last
+    # epilogue as well (no float32 U in the workspace): the pre-sign modes
+    # need no more than the post-vote one
     m1, _, _ = B.default_layout([(5, 37)])
-    assert B.step_workspace(m1, hp, 2) == B.step_workspace(m1, hp, 0) > B.step_workspace(m1, hp, 1)
+    assert B.step_workspace(m1, hp, 2) == B.step_workspace(m1, hp, 0) == \
+        B.step_workspace(m1, hp, 1) > 0
 
 
 def test_step_workspace_sizes(monkeypatch):
@@ -287,9 +289,10 @@ def test_step_ternary_validation():
     assert L.signmuon_step(arr, len(mats), ctypes.byref(c), FAKE, FAKE, 1, FAKE, FAKE, d, 3,
                            0, 0, None, FAKE, 1 << 30, None, None) == B.SM_EINVAL
     assert B.step_workspace(mats, hp, 0) > 0
-    # int8 signs come straight from the last epilogue: no float32 U is kept
+    # int8 and packed signs both come straight from the last epilogue (no
+    # float32 U is kept for any width)
     m1, _, _ = B.default_layout([(5, 37)])
-    assert B.step_workspace(m1, hp, 0) < B.step_workspace(m1, _hp(), 0)
+    assert B.step_workspace(m1, hp, 0) == B.step_workspace(m1, _hp(), 0) > 0
 
 
 def test_step_normalized_validation():
