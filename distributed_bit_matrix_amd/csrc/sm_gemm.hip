@@ -1535,11 +1535,12 @@ __global__ __launch_bounds__(256) void k_split_reduce(GemmArgs A) {
 #ifndef SM_UP_WPE
 #define SM_UP_WPE 2
 #endif
-template <typename T, int SPLIT, int EPI, bool WIDE = false>
+template <typename T, int SPLIT, int EPI, bool WIDE = false, bool SMALL = false>
 struct Cfg {
+  static_assert(!SMALL || (sizeof(T) == 4 && EPI == E_UPDATE && !WIDE), "64x64: float32 update");
   static constexpr bool BF = sizeof(T) == 2 && SPLIT == 1 && !WIDE;
   static constexpr int WM = 2;
-  static constexpr int TI = 4, TJ = WIDE ? 8 : 4;
+  static constexpr int TI = SMALL ? 2 : 4, TJ = WIDE ? 8 : SMALL ? 2 : 4;
   static constexpr int RB = WIDE ? 64
                           : !BF ? 128
                           : EPI == E_OP || EPI == E_RAW ? SM_OP_RB
@@ -1573,6 +1574,13 @@ struct Cfg {
 };
 using CfgWide = Cfg<bf16_t, 1, E_UPDATE, true>;
 constexpr int kWideMinK = 2048;
+// 64x64 tiles for the float32 update of small matrices: a 128x128 float32
+// tile carries eight times the matrix-core time of a bfloat16 one per slab,
+// so a matrix of a few such tiles leaves the GPU nearly idle for the
+// length of one block; 64x64 tiles give four times the blocks at a quarter
+// of the work each (matrices of at most kSmallMaxTiles 128x128 tiles).
+using CfgSmall = Cfg<float, 1, E_UPDATE, false, true>;
+constexpr int kSmallMaxTiles = 16;
 constexpr int kTile = Cfg<bf16_t, 1, E_UPDATE>::BMT;
 static_assert(Cfg<bf16_t, 1, E_UPDATE>::BNT == kTile, "square tile");
 static_assert(CfgWide::BMT == kTile, "wide tiles keep the row height");
@@ -1580,14 +1588,21 @@ static_assert(CfgWide::BMT == kTile, "wide tiles keep the row height");
 void gemm_tile(int precision, int epi, int64_t gm, int64_t gn, int64_t gk, int* tm, int* tn) {
   *tm = kTile;
   *tn = kTile;
+  if (epi == E_UPDATE && precision == P_F32 && gm % CfgSmall::BMT == 0 &&
+      gn % CfgSmall::BNT == 0 &&
+      ((gm + kTile - 1) / kTile) * ((gn + kTile - 1) / kTile) <= kSmallMaxTiles) {
+    *tm = CfgSmall::BMT;
+    *tn = CfgSmall::BNT;
+    return;
+  }
   if (SM_GEMM_WIDE_UPDATE && epi == E_UPDATE && precision == P_BF16 && gm % kTile == 0 &&
       gn % CfgWide::BNT == 0 && gk >= kWideMinK)
     *tn = CfgWide::BNT;
 }
 
-template <typename T, int SPLIT, int EPI, bool WIDE = false>
+template <typename T, int SPLIT, int EPI, bool WIDE = false, bool SMALL = false>
 static hipError_t launch_one(const GemmArgs& args, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  using C = Cfg<T, SPLIT, EPI, WIDE>;
+  using C = Cfg<T, SPLIT, EPI, WIDE, SMALL>;
   // the pipelined k-loop fills all NSTG stages before its first slab: every
   // block needs at least NSTG slabs (and, pipelined, an even count)
   constexpr int BK = C::RB / (int)sizeof(T);
@@ -1726,6 +1741,10 @@ hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s, hipEv
   }
   hipError_t e;
   if (tile == CfgWide::BNT) return launch_one<bf16_t, 1, E_UPDATE, true>(a, s, t0, t1);
+  if (tile == CfgSmall::BNT) {
+    if (precision != P_F32 || args.epi != E_UPDATE) return hipErrorInvalidValue;
+    return launch_one<float, 1, E_UPDATE, false, true>(a, s, t0, t1);
+  }
   if (precision == P_F32) e = launch_epi<float, 1>(a, s, t0, t1);
   else if (precision == P_BF16X3) e = launch_epi<bf16_t, 2>(a, s, t0, t1);
   else e = launch_epi<bf16_t, 1>(a, s, t0, t1);
@@ -1736,9 +1755,9 @@ hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s, hipEv
   return launch_reduce<bf16_t, 1, false>(args, s);
 }
 
-template <typename T, int SPLIT, int EPI, bool WIDE = false>
+template <typename T, int SPLIT, int EPI, bool WIDE = false, bool SMALL = false>
 static hipError_t set_lds() {
-  using C = Cfg<T, SPLIT, EPI, WIDE>;
+  using C = Cfg<T, SPLIT, EPI, WIDE, SMALL>;
   return hipFuncSetAttribute(
       reinterpret_cast<const void*>(&k_gemm<T, SPLIT, EPI, C::NSTG, C::WM, C::TI, C::TJ, C::RB, C::WPE, C::PIPE, C::TRACC>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::lds());
@@ -1757,6 +1776,7 @@ hipError_t gemm_set_attributes() {
   if ((e = set_lds_all<bf16_t, 1>()) != hipSuccess) return e;
   if ((e = set_lds_all<bf16_t, 2>()) != hipSuccess) return e;
   if ((e = set_lds_all<float, 1>()) != hipSuccess) return e;
+  if ((e = set_lds<float, 1, E_UPDATE, false, true>()) != hipSuccess) return e;
   return set_lds<bf16_t, 1, E_UPDATE, true>();
 }
 
