@@ -64,6 +64,13 @@ bool gram_space_enabled() {
   return !(e && std::strcmp(e, "iterate") == 0);
 }
 
+// One of the concurrent chains runs on the caller's stream unless the
+// environment variable SIGNMUON_CALLER_CHAIN is "0" (read at every call).
+bool caller_chain_enabled() {
+  const char* e = std::getenv("SIGNMUON_CALLER_CHAIN");
+  return !(e && std::strcmp(e, "0") == 0);
+}
+
 // The P power steps of small sets run in one launch unless the environment
 // variable SIGNMUON_POWER_ITER is "steps" (one launch per step; read at
 // every call).
@@ -870,22 +877,39 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
     chain[c].push_back(groups[i]);
     load[c] += work(groups[i]);
   }
+  // The chain with the most matrices (whose launches hold the most blocks,
+  // so that it tends to finish last) runs on the caller's stream itself:
+  // it starts without waiting on another queue, and the vote after the
+  // join follows it directly.
+  int home = -1;
+  if (caller_chain_enabled()) {
+    int most = -1;
+    for (int c = 0; c < nc; ++c) {
+      int n = 0;
+      for (const Group& g : chain[c]) n += g.count;
+      if (n > most) { most = n; home = c; }
+    }
+  }
   sm_executor* R = ex;
   std::lock_guard<std::mutex> lock(R->mu);
   hipEvent_t* join_ev = R->join[pass];
+  auto stream_of = [&](int c) { return c == home ? s : R->s[c]; };
   HIP_TRY(hipEventRecord(R->fork[pass], s));
   NsIO cio = io;
   cio.prof = nullptr;
   std::vector<Stages> prog(nc);
   for (int c = 0; c < nc; ++c) {
-    hipStream_t cs = R->s[c];
+    hipStream_t cs = stream_of(c);
     pre_scale_stages(P, mp, chain[c], hp, B, cio, part_kind, cs, prog[c]);
     if (hp->K > 0) ns_stages(P, mp, chain[c], hp, B, cio, cs, prog[c]);
   }
   sm_status st = SM_OK;
   int forked = 0;
   for (int c = 0; c < nc && st == SM_OK; ++c) {
-    if (hipStreamWaitEvent(R->s[c], R->fork[pass], 0) != hipSuccess) { st = SM_EHIP; break; }
+    if (c != home && hipStreamWaitEvent(R->s[c], R->fork[pass], 0) != hipSuccess) {
+      st = SM_EHIP;
+      break;
+    }
     ++forked;
   }
   size_t longest = 0;
@@ -896,6 +920,7 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
   // join every forked chain, also after an error, so that the caller's
   // stream orders after all work enqueued on the chains
   for (int c = 0; c < forked; ++c) {
+    if (c == home) continue;
     if (hipEventRecord(join_ev[c], R->s[c]) != hipSuccess ||
         hipStreamWaitEvent(s, join_ev[c], 0) != hipSuccess)
       st = SM_EHIP;

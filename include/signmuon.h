@@ -229,7 +229,8 @@ sm_status signmuon_apply(void *W, int32_t w_dtype, const int8_t *D,
  * of disjoint groups of matrices as up to three concurrent chains (three
  * non-blocking HIP streams on the device current at creation, forked from
  * and joined back into the caller's stream with the executor's own events;
- * each of the at most two PolarNS passes of a step has its own events).
+ * each of the at most two PolarNS passes of a step has its own events; the
+ * chain with the most matrices runs on the caller's stream itself).
  * Passing NULL instead runs everything on the caller's stream (a few percent
  * slower on large sets).  An executor may be passed only on its own device
  * (else SM_EINVAL) and by one thread at a time (calls lock it while they
