@@ -1514,6 +1514,9 @@ __global__ __launch_bounds__(256) void k_split_reduce(GemmArgs A) {
 #ifndef SM_SPLIT_MIN_SLABS_F32
 #define SM_SPLIT_MIN_SLABS_F32 2
 #endif
+#ifndef SM_DEAL_TILES
+#define SM_DEAL_TILES 16
+#endif
 #ifndef SM_SQ_TRACC
 #define SM_SQ_TRACC 1
 #endif
@@ -1697,6 +1700,7 @@ static hipError_t launch_reduce(const GemmArgs& args, hipStream_t s) {
   return hipGetLastError();
 }
 
+constexpr int kDealTiles = SM_DEAL_TILES;
 // Whole matrices of a Gram launch go to the XCDs in turn unless the
 // environment variable SIGNMUON_XCD_DEAL is "0" (read at every launch).
 static bool xcd_deal_enabled() {
@@ -1730,13 +1734,21 @@ hipError_t launch_gemm(int precision, const GemmArgs& args, hipStream_t s, hipEv
     }
   }
   // Grams (k = the long side, which differs between shapes): whole
-  // matrices to the XCDs in turn when they all have the same block count
+  // matrices to the XCDs in turn when they all have the same block count.
+  // When matrices of different k give less than a full round of whole
+  // matrices, or their block counts differ, runs of kDealTiles blocks go
+  // round instead, so that the long-k tiles spread over every XCD; equal k
+  // keeps the contiguous split, which shares rows in each L2.
   GemmArgs a = args;
   a.xcd_chunk = 0;
   if ((args.epi == E_OP || args.epi == E_RAW) && xcd_deal_enabled()) {
     int c = args.G.g[0].blocks_per_mat;
-    for (int i = 1; i < args.G.n; ++i)
+    bool mixed_k = false;
+    for (int i = 1; i < args.G.n; ++i) {
       if (args.G.g[i].blocks_per_mat != c) c = 0;
+      if (args.G.g[i].gk != args.G.g[0].gk) mixed_k = true;
+    }
+    if (mixed_k && (c == 0 || 8 * c > args.G.total_blocks)) c = kDealTiles;
     a.xcd_chunk = c;
   }
   hipError_t e;
