@@ -877,10 +877,12 @@ sm_status run_polar(const Plan& P, const std::vector<MatPlan>& mp,
     chain[c].push_back(groups[i]);
     load[c] += work(groups[i]);
   }
-  // The chain with the most matrices (whose launches hold the most blocks,
-  // so that it tends to finish last) runs on the caller's stream itself:
-  // it starts without waiting on another queue, and the vote after the
-  // join follows it directly.
+  // The chain with the most matrices runs on the caller's stream itself:
+  // it starts right after the momentum pass without waiting on another
+  // queue, and the vote after the join follows it on the same queue.  (Its
+  // launches hold the most blocks and take the larger share of the CUs, so
+  // on the nanoGPT-shaped set it ends before the other chains, and the vote
+  // still waits for their join events.)
   int home = -1;
   if (caller_chain_enabled()) {
     int most = -1;
