@@ -500,6 +500,31 @@ def test_step_full_nanogpt_prepost():
     full_case("nanogpt_prepost", sample=[0, 1, 46, 47])
 
 
+@pytest.mark.parametrize("scale", ["fro", "spectral"])
+def test_step_mixed_k_grouped_gram(scale):
+    """The whole set as one chain (no executor), so that each Gram launch
+    holds 6 x (768 x 3072) and 2 x (512 x 4096): two k (3072, 4096), split
+    along k into 3 and 8 parts, 63 and 80 blocks per matrix, 538 blocks in
+    all, which the GEMM deals to the XCDs in runs of 16 blocks (four full
+    rounds of 128, then 26 blocks split contiguously).  Frobenius: the
+    Gram-space form's first Gram; spectral: the raw Gram of the power steps
+    and the iterate form's Gram at every step."""
+    base = WL.get("nanogpt")
+    w = WL.scaled(base, [(768, 3072)] * 6 + [(512, 4096)] * 2, name=f"mixed-k-{scale}")
+    if scale == "spectral":
+        w = w.replace(scale="spectral", P=5)
+    print(f"mixed-k grouped Gram step {scale} d={w.d} M={w.M}", flush=True)
+    hp = hparams(w)
+    st = GpuState(w, hp)
+    st.plan = B.StepPlan(st.layout, hp, w.post_vote, concurrent=False)
+    W = WL.init_weights(w)
+    Mom0 = WL.init_momentum(w, 0, std=0.05).astype(np.float64)
+    G0 = WL.gradient(w, 0, 0).astype(np.float64)
+    bits = WL.random_bits(w, w.M)
+    u0s = WL.power_start(w) if w.scale == "spectral" else None
+    check_step(w, st, hp, W, [Mom0], [G0], u0s, sample=[0, 5, 6, 7], other_bits=bits)
+
+
 @pytest.mark.slow
 def test_step_full_llm_mlp():
     full_case("llm_mlp", sample=[0])
