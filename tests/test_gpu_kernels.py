@@ -253,3 +253,102 @@ def test_vote_ternary_full_nanogpt_size():
     Sg = rng.integers(-1, 2, size=(M, n), dtype=np.int8)
     D = B.majority_vote_ternary(dev(Sg.reshape(-1)), M, n, 0)
     assert np.array_equal(host(D), O.majority_from_sums(O.vote_sums_from_signs(Sg), 0))
+
+
+# --------------------------------------------------------------------------
+# every flat call past 2^31 entries (64-bit indexing), checked at samples
+# --------------------------------------------------------------------------
+def _sampled_words(n):
+    """Words (32-entry groups) to check: the first ones, those around entry
+    2^31, the last ones (the last one partial), and 600 at random."""
+    nw = (n + 31) // 32
+    rng = np.random.default_rng(2031)
+    mid = (1 << 31) // 32
+    w = [0, 1, 2] + list(range(mid - 3, mid + 3)) + list(range(nw - 3, nw)) + \
+        rng.integers(0, nw, 600).tolist()
+    return np.unique(np.array(w, np.int64))
+
+
+def _entries_of(words, n):
+    """Entry index of every entry of the given words (past n: -1)."""
+    e = words[:, None] * 32 + np.arange(32)[None, :]
+    return np.where(e < n, e, -1)
+
+
+def _gather(t, idx):
+    """Values of device tensor t at host indices idx (-1 gives 0)."""
+    i = torch.from_numpy(np.where(idx < 0, 0, idx).reshape(-1)).cuda()
+    v = host(t.index_select(0, i)).reshape(idx.shape)
+    return np.where(idx < 0, np.zeros((), v.dtype), v)
+
+
+def test_flat_calls_past_2_31_entries():
+    n = (1 << 31) + 4099          # neither a whole 32-entry word nor a whole vector
+    free, _ = torch.cuda.mem_get_info()
+    if free < (48 << 30):
+        pytest.skip("needs 48 GiB of free device memory")
+    print(f"flat calls n={n}", flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2031)
+    words = _sampled_words(n)
+    ent = _entries_of(words, n)                       # (k, 32)
+    valid = ent >= 0
+    nw = (n + 31) // 32
+
+    # momentum, bfloat16 W
+    G = torch.randn(n, device="cuda", generator=gen)
+    Mom = torch.randn(n, device="cuda", generator=gen).mul_(0.3)
+    W = torch.randn(n, device="cuda", generator=gen).mul_(0.02).to(torch.bfloat16)
+    g_s, m_s = _gather(G, ent), _gather(Mom, ent)
+    w_s = _gather(W.view(torch.int16), ent).astype(np.uint16).astype(np.uint32) << 16
+    w_s = w_s.view(np.float32)
+    beta, lam = 0.9, 0.01
+    B.momentum(G, W, Mom, beta, lam)
+    del G
+    got = _gather(Mom, ent).astype(np.float64)
+    want = O.momentum_update(m_s, g_s, w_s, f32(beta), f32(lam))
+    tol = momentum_tol(m_s, g_s, w_s, f32(beta), f32(lam))
+    assert np.all((np.abs(got - want) <= tol)[valid])
+
+    # signs of the new momentum, with zeros planted in the sampled words
+    zero_at = torch.from_numpy(ent[valid][::5].copy()).cuda()
+    Mom.index_fill_(0, zero_at, 0.0)
+    U = Mom
+    u_s = _gather(U, ent)
+    bits = torch.empty((3, nw), dtype=torch.int32, device="cuda")
+    B.sign_pack(U, bits=bits[0])
+    bits[1:].random_(-(1 << 31), 1 << 31, generator=gen)     # workers 1 and 2
+    b_s = host(bits.index_select(1, torch.from_numpy(words).cuda())).view(np.uint32)  # (3, k)
+    for r, wd in enumerate(words):
+        m = valid[r]
+        assert O.pack_signs(u_s[r][m])[0] == b_s[0, r], ("pack", int(wd))
+
+    # vote over the three packed buffers, then the apply with its result
+    D, S = B.majority_vote(bits, 3, n, 0, stride=nw, want_sums=True)
+    d_s, s_s = _gather(D, ent), _gather(S, ent).astype(np.int32)
+    for r, wd in enumerate(words):
+        m = int(valid[r].sum())
+        sums = O.vote_sums_from_bits(b_s[:, r:r + 1], m)
+        assert np.array_equal(s_s[r, :m], sums), ("vote sums", int(wd))
+        assert np.array_equal(d_s[r, :m], O.majority_from_sums(sums, 0)), ("vote", int(wd))
+    del S, bits
+    eta = 0.0123
+    B.apply(W, eta, D=D)
+    got_w = _gather(W.view(torch.int16), ent).astype(np.uint16)
+    want_w = O.apply_update(w_s[valid], d_s[valid], f32(eta), "bf16")
+    assert np.array_equal(got_w[valid].astype(np.uint32) << 16, want_w.view(np.uint32))
+    del D, W
+
+    # ternary signs and their vote over two buffers (16-byte stride)
+    st = (n + 15) // 16 * 16
+    T = torch.empty(2 * st, dtype=torch.int8, device="cuda")
+    B.sign_ternary(U, S=T[:n])
+    T[st:].random_(-1, 2, generator=gen)
+    t0 = _gather(T, ent)
+    assert np.array_equal(t0[valid], O.sign_ternary(u_s[valid]))
+    t1 = _gather(T, np.where(ent < 0, -1, ent + st))
+    D2, S2 = B.majority_vote_ternary(T, 2, n, 1, stride=st, want_sums=True)
+    got_s2 = _gather(S2, ent).astype(np.int32)[valid]
+    want_s2 = O.vote_sums_from_signs(np.stack([t0[valid], t1[valid]]))
+    assert np.array_equal(got_s2, want_s2)
+    assert np.array_equal(_gather(D2, ent)[valid], O.majority_from_sums(want_s2, 1))
