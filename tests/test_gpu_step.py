@@ -525,6 +525,57 @@ def test_step_mixed_k_grouped_gram(scale):
     check_step(w, st, hp, W, [Mom0], [G0], u0s, sample=[0, 5, 6, 7], other_bits=bits)
 
 
+def test_step_past_2_31_entries():
+    """1040 matrices of 128 x 16384, 2,181,038,080 entries in all (matrix
+    1024 starts at entry 2^31): the step with inputs drawn on the GPU from a
+    seeded generator, against the oracle on matrices 0, 1023, 1024 and 1039
+    (momentum, the local worker's signs, the vote and the update)."""
+    free, _ = torch.cuda.mem_get_info()
+    if free < (64 << 30):
+        pytest.skip("needs 64 GiB of free device memory")
+    r, c = 128, 16384
+    w = WL.scaled(WL.get("nanogpt"), [(r, c)] * 1040, M=3, name="past-2-31")
+    hp = hparams(w)
+    layout, d, words = B.default_layout(w.mats)
+    assert d > (1 << 31)
+    print(f"step past 2^31 entries d={d} M={w.M}", flush=True)
+    plan = B.StepPlan(layout, hp, w.post_vote)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2131)
+    G = torch.randn(d, device="cuda", generator=gen)
+    Mom = torch.randn(d, device="cuda", generator=gen).mul_(0.05)
+    W = torch.randn(d, device="cuda", generator=gen).mul_(0.02).to(torch.bfloat16)
+    bits = torch.empty((w.M, words), dtype=torch.int32, device="cuda")
+    bits.random_(-(1 << 31), 1 << 31, generator=gen)
+    n = r * c
+    offs, woffs = w.elem_offsets, w.word_offsets
+    sample = [0, 1023, 1024, 1039]
+    assert offs[1024] == 1 << 31
+
+    def seg(t, i):
+        return t[offs[i]:offs[i] + n]
+
+    before = {i: (seg(G, i).cpu().numpy(), seg(Mom, i).cpu().numpy(),
+                  seg(W, i).float().cpu().numpy()) for i in sample}
+    plan(G, W, Mom, bits, words, w.M, 0)
+    assert plan.status() == B.SM_OK
+    torch.cuda.synchronize()
+    o = oracle_hp(hp)
+    for i in sample:
+        g, m, wv = before[i]
+        Mom_new = O.momentum_update(m.astype(np.float64), g.astype(np.float64), wv,
+                                    o["beta"], o["lam"])
+        got = seg(Mom, i).cpu().numpy().astype(np.float64)
+        tol = momentum_tol(m, g.astype(np.float64), wv, o["beta"], o["lam"])
+        assert np.all(np.abs(got - Mom_new) <= tol), (i, "momentum")
+        U, _ = O.polar_ns(Mom_new.reshape(r, c), o["K"], o["eps"], o["scale"], o["P"],
+                          o["coeffs"])
+        bg = bits[:, woffs[i]:woffs[i] + n // 32].cpu().numpy().view(np.uint32)
+        ok, stats = local_gate(w, bg[0], U, n)
+        assert ok, (i, stats)
+        check_after_vote(w, hp, wv, seg(W, i).float().cpu().numpy(), bg, (r, c), None, i)
+
+
 @pytest.mark.slow
 def test_step_full_llm_mlp():
     full_case("llm_mlp", sample=[0])
