@@ -576,6 +576,72 @@ def test_step_past_2_31_entries():
         check_after_vote(w, hp, wv, seg(W, i).float().cpu().numpy(), bg, (r, c), None, i)
 
 
+def _hadamard_rows(i, cols, xp):
+    """Rows i of the Sylvester-Hadamard matrix of order 65536, first `cols`
+    columns: H[i, j] = (-1)^parity(i & j) (i, j < 2^16); xp is numpy or
+    torch."""
+    j = np.arange(cols) if xp is np else xp.arange(cols, device=i.device)
+    x = i[:, None] & j[None, :]
+    for sh in (8, 4, 2, 1):
+        x = x ^ (x >> sh)
+    return 1 - 2 * (x & 1)
+
+
+@pytest.mark.parametrize("shape", [(32640, 65536), (65536, 32640)])
+def test_step_largest_matrix_hadamard(shape):
+    """The largest matrix a step takes (padded rows x cols just under 2^31:
+    4.28e9 bytes of bfloat16 operand, so the GEMMs' 32-bit byte offsets run
+    past 2^31), wide and tall.  The gradient is Hadamard rows (columns): the
+    short side's vectors are orthogonal and of equal norm, so the Gram is a
+    multiple of I exactly (every product is a sum of +-c^2 terms, exact in
+    float32) and the polar factor is a positive multiple of the gradient:
+    the local worker's buffer must hold the gradient's signs exactly, every
+    entry.  The vote and the update against the oracle on sampled rows."""
+    free, _ = torch.cuda.mem_get_info()
+    if free < (80 << 30):
+        pytest.skip("needs 80 GiB of free device memory")
+    r, c = shape
+    w = WL.scaled(WL.get("nanogpt"), [(r, c)], M=3, name=f"hadamard-{r}x{c}")
+    hp = hparams(w)
+    layout, d, words = B.default_layout(w.mats)
+    print(f"largest matrix {r}x{c} d={d}", flush=True)
+    plan = B.StepPlan(layout, hp, w.post_vote)
+    G = torch.empty(d, device="cuda")
+    for r0 in range(0, r, 1024):
+        i = torch.arange(r0, min(r, r0 + 1024), device="cuda", dtype=torch.int32)
+        G[r0 * c:(r0 + len(i)) * c] = _hadamard_rows(i, c, torch).float().reshape(-1)
+    Mom = torch.zeros(d, device="cuda")
+    W = torch.zeros(d, device="cuda", dtype=torch.bfloat16)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4099)
+    bits = torch.empty((w.M, words), dtype=torch.int32, device="cuda")
+    bits.random_(-(1 << 31), 1 << 31, generator=gen)
+    plan(G, W, Mom, bits, words, w.M, 0)
+    assert plan.status() == B.SM_OK
+    torch.cuda.synchronize()
+    # every entry: bit j of the local buffer is set iff G[j] < 0
+    shifts = torch.arange(32, device="cuda", dtype=torch.int64)
+    wpr = c // 32                                   # words per row
+    for r0 in range(0, r, 1024):
+        r1 = min(r, r0 + 1024)
+        neg = (G[r0 * c:r1 * c] < 0).view(-1, 32).to(torch.int64)
+        want = ((neg << shifts).sum(1) & 0xFFFFFFFF).to(torch.int64)
+        got = bits[0, r0 * wpr:r1 * wpr].to(torch.int64) & 0xFFFFFFFF
+        assert torch.equal(got, want), ("signs", r0)
+    # sampled rows against the oracle: signs of the closed form, vote, update
+    o = oracle_hp(hp)
+    for i in (0, 1, r // 2 + 7, r - 1):
+        Hrow = _hadamard_rows(np.array([i], np.int64), c, np).reshape(-1).astype(np.float64)
+        seg = bits[:, i * wpr:(i + 1) * wpr].cpu().numpy().view(np.uint32)
+        assert np.array_equal(seg[0], O.pack_signs(Hrow)), ("row", i)
+        Wg = W[i * c:(i + 1) * c].float().cpu().numpy()
+        check_after_vote(w, hp, np.zeros(c, np.float32), Wg, seg, (1, c), None, i)
+        Mg = Mom[i * c:(i + 1) * c].cpu().numpy().astype(np.float64)
+        Mn = O.momentum_update(np.zeros(c), Hrow, np.zeros(c, np.float32), o["beta"], o["lam"])
+        assert np.all(np.abs(Mg - Mn) <= momentum_tol(np.zeros(c), Hrow, np.zeros(c),
+                                                      o["beta"], o["lam"])), ("momentum", i)
+
+
 @pytest.mark.slow
 def test_step_full_llm_mlp():
     full_case("llm_mlp", sample=[0])
