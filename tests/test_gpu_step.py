@@ -310,6 +310,8 @@ def test_step_mirrored_storage(name, monkeypatch):
 # signs, 64 x 64 for int8 ones), here with partial tiles in both directions.
 ODD_TINY = [(5, 37), (33, 7), (45, 71), (64, 19), (3, 3), (70, 32)]
 ODD_BF16 = [(97, 161), (161, 97), (45, 403), (403, 45), (33, 515), (203, 96)]
+# degenerate shapes: a scalar, row and column vectors (a 1 x 1 Gram), 2 x 2
+DEGEN = [(1, 1), (1, 37), (300, 1), (1, 4096), (2, 2), (4096, 1)]
 ODD = {
     "f32_M5": WL.scaled(WL.get("single"), ODD_TINY, M=5, name="odd-f32"),
     "bf16w_f32ns_M6": WL.scaled(WL.get("nanogpt"), ODD_TINY, M=6,
@@ -327,6 +329,13 @@ ODD = {
     "postvote_M5": WL.scaled(WL.get("postvote"), ODD_BF16, M=5, name="odd-postvote"),
     "prepost_ternary_M5": WL.scaled(WL.get("nanogpt_prepost"), ODD_BF16, M=5,
                                     name="odd-prepost-ternary").replace(encoding="ternary"),
+    "degenerate_bf16_M3": WL.scaled(WL.get("nanogpt"), DEGEN, M=3, name="degenerate"),
+    "degenerate_spectral_M5": WL.scaled(WL.get("resnet50"), DEGEN, M=5,
+                                        name="degenerate-spectral"),
+    "degenerate_postvote_M5": WL.scaled(WL.get("postvote"), DEGEN, M=5,
+                                        name="degenerate-postvote"),
+    "degenerate_ternary_M4": WL.scaled(WL.get("nanogpt"), DEGEN, M=4,
+                                       name="degenerate-ternary").replace(encoding="ternary"),
 }
 
 
