@@ -352,3 +352,37 @@ def test_flat_calls_past_2_31_entries():
     want_s2 = O.vote_sums_from_signs(np.stack([t0[valid], t1[valid]]))
     assert np.array_equal(got_s2, want_s2)
     assert np.array_equal(_gather(D2, ent)[valid], O.majority_from_sums(want_s2, 1))
+
+
+# --------------------------------------------------------------------------
+# the largest worker count: sums reach +-32767 (int16)
+# --------------------------------------------------------------------------
+def test_vote_max_workers():
+    M, n = 32767, 4099
+    print(f"vote M={M} n={n}", flush=True)
+    rng = np.random.default_rng(32767)
+    words = (n + 31) // 32
+    bits = rng.integers(0, 2 ** 32, size=(M, words), dtype=np.uint32)
+    bits[:, 0] = 0                       # entries 0..31: every worker +1
+    bits[:, 1] = 0xFFFFFFFF              # entries 32..63: every worker -1
+    D, S = B.majority_vote(dev(bits.view(np.int32)), M, n, 0, want_sums=True)
+    sums = O.vote_sums_from_bits(bits, n)
+    assert sums[0] == M and sums[32] == -M
+    assert np.array_equal(host(S).astype(np.int32), sums)
+    assert np.array_equal(host(D), O.majority_from_sums(sums, 0))
+
+
+def test_vote_ternary_max_workers():
+    M, n = 32767, 4099
+    print(f"vote ternary M={M} n={n}", flush=True)
+    rng = np.random.default_rng(32768)
+    Sg = rng.integers(-1, 2, size=(M, n)).astype(np.int8)
+    Sg[:, :16] = 1
+    Sg[:, 16:32] = -1
+    for tie in (0, 1):
+        D, sums = B.majority_vote_ternary(dev(Sg.reshape(-1)), M, n, tie, stride=n,
+                                          want_sums=True)
+        want = O.vote_sums_from_signs(Sg)
+        assert want[0] == M and want[16] == -M
+        assert np.array_equal(host(sums).astype(np.int32), want)
+        assert np.array_equal(host(D), O.majority_from_sums(want, tie))
