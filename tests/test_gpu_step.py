@@ -585,6 +585,26 @@ def test_step_past_2_31_entries():
         check_after_vote(w, hp, wv, seg(W, i).float().cpu().numpy(), bg, (r, c), None, i)
 
 
+@pytest.mark.parametrize("post_vote", [0, 1])
+def test_step_max_workers(post_vote):
+    """The largest worker count, M = 32767 (vote sums up to +-32767 in
+    int16): the other workers' buffers random, every entry of the first
+    words agreeing in all of them."""
+    base = WL.get("postvote" if post_vote else "nanogpt")
+    w = WL.scaled(base, [(64, 96), (33, 7)], M=32767, name=f"max-workers-{post_vote}")
+    print(f"step M={w.M} post_vote={post_vote}", flush=True)
+    hp = hparams(w)
+    st = GpuState(w, hp)
+    W = WL.init_weights(w)
+    Mom0 = WL.init_momentum(w, 0, std=0.05).astype(np.float64)
+    G0 = WL.gradient(w, 0, 0).astype(np.float64)
+    bits = WL.random_bits(w, w.M)
+    bits[:, 0] = 0
+    bits[:, 1] = 0xFFFFFFFF
+    u0s = WL.power_start(w) if w.scale == "spectral" else None
+    check_step(w, st, hp, W, [Mom0], [G0], u0s, other_bits=bits)
+
+
 def _hadamard_rows(i, cols, xp):
     """Rows i of the Sylvester-Hadamard matrix of order 65536, first `cols`
     columns: H[i, j] = (-1)^parity(i & j) (i, j < 2^16); xp is numpy or
