@@ -622,10 +622,12 @@ def test_step_largest_matrix_hadamard(shape):
     4.28e9 bytes of bfloat16 operand, so the GEMMs' 32-bit byte offsets run
     past 2^31), wide and tall.  The gradient is Hadamard rows (columns): the
     short side's vectors are orthogonal and of equal norm, so the Gram is a
-    multiple of I exactly (every product is a sum of +-c^2 terms, exact in
-    float32) and the polar factor is a positive multiple of the gradient:
-    the local worker's buffer must hold the gradient's signs exactly, every
-    entry.  The vote and the update against the oracle on sampled rows."""
+    multiple of I (its off-diagonal sums of +-c^2 terms cancel up to float32
+    rounding of the partial sums, ~2^-24 relative) and the polar factor is a
+    positive multiple of the gradient up to perturbations that many orders
+    of magnitude smaller than its entries: the local worker's buffer must
+    hold the gradient's signs, every entry.  The vote and the update against
+    the oracle on sampled rows."""
     free, _ = torch.cuda.mem_get_info()
     if free < (80 << 30):
         pytest.skip("needs 80 GiB of free device memory")
