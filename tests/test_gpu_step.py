@@ -616,11 +616,17 @@ def _hadamard_rows(i, cols, xp):
     return 1 - 2 * (x & 1)
 
 
-@pytest.mark.parametrize("shape", [(32640, 65536), (65536, 32640)])
-def test_step_largest_matrix_hadamard(shape):
-    """The largest matrix a step takes (padded rows x cols just under 2^31:
-    4.28e9 bytes of bfloat16 operand, so the GEMMs' 32-bit byte offsets run
-    past 2^31), wide and tall.  The gradient is Hadamard rows (columns): the
+@pytest.mark.parametrize("base,shape", [("nanogpt", (32640, 65536)),
+                                        ("nanogpt", (65536, 32640)),
+                                        ("single", (16256, 65536)),
+                                        ("llm_mlp_quintic", (32640, 65536))])
+def test_step_largest_matrix_hadamard(base, shape):
+    """The largest matrix a step takes in each precision: padded rows x cols
+    just under 2^31 with bfloat16 operands (the nanoGPT recipe, wide and
+    tall; the split-bfloat16 quintic with the spectral scale of the LLM-MLP
+    recipe) and under 2^30 with float32 ones (the single-matrix recipe): up
+    to 4.28e9 bytes of operand, so the GEMMs' 32-bit byte offsets run past
+    2^31.  The gradient is Hadamard rows (columns): the
     short side's vectors are orthogonal and of equal norm, so the Gram is a
     multiple of I (its off-diagonal sums of +-c^2 terms cancel up to float32
     rounding of the partial sums, ~2^-24 relative) and the polar factor is a
@@ -632,17 +638,18 @@ def test_step_largest_matrix_hadamard(shape):
     if free < (80 << 30):
         pytest.skip("needs 80 GiB of free device memory")
     r, c = shape
-    w = WL.scaled(WL.get("nanogpt"), [(r, c)], M=3, name=f"hadamard-{r}x{c}")
+    w = WL.scaled(WL.get(base), [(r, c)], M=3, name=f"hadamard-{base}-{r}x{c}")
     hp = hparams(w)
     layout, d, words = B.default_layout(w.mats)
-    print(f"largest matrix {r}x{c} d={d}", flush=True)
+    print(f"largest matrix {base} {r}x{c} d={d} {w.ns_precision} {w.scale}", flush=True)
     plan = B.StepPlan(layout, hp, w.post_vote)
     G = torch.empty(d, device="cuda")
     for r0 in range(0, r, 1024):
         i = torch.arange(r0, min(r, r0 + 1024), device="cuda", dtype=torch.int32)
         G[r0 * c:(r0 + len(i)) * c] = _hadamard_rows(i, c, torch).float().reshape(-1)
     Mom = torch.zeros(d, device="cuda")
-    W = torch.zeros(d, device="cuda", dtype=torch.bfloat16)
+    W = torch.zeros(d, device="cuda",
+                    dtype=torch.bfloat16 if w.w_dtype == "bf16" else torch.float32)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(4099)
     bits = torch.empty((w.M, words), dtype=torch.int32, device="cuda")
@@ -666,7 +673,7 @@ def test_step_largest_matrix_hadamard(shape):
         seg = bits[:, i * wpr:(i + 1) * wpr].cpu().numpy().view(np.uint32)
         assert np.array_equal(seg[0], O.pack_signs(Hrow)), ("row", i)
         Wg = W[i * c:(i + 1) * c].float().cpu().numpy()
-        check_after_vote(w, hp, np.zeros(c, np.float32), Wg, seg, (1, c), None, i)
+        check_after_vote(w, hp, np.zeros(c, np.float32), Wg, seg, (1, c), None, (base, i))
         Mg = Mom[i * c:(i + 1) * c].cpu().numpy().astype(np.float64)
         Mn = O.momentum_update(np.zeros(c), Hrow, np.zeros(c, np.float32), o["beta"], o["lam"])
         assert np.all(np.abs(Mg - Mn) <= momentum_tol(np.zeros(c), Hrow, np.zeros(c),
