@@ -197,3 +197,50 @@ def test_power_iter_one_launch_equals_steps(shape, P, precision, with_u0, K, mon
     monkeypatch.delenv("SIGNMUON_POWER_ITER")
     if K > 0:
         check(X, hp, u0=u0)
+
+
+# --------------------------------------------------------------------------
+# the largest matrix, with a closed form: Hadamard rows
+# --------------------------------------------------------------------------
+def _hadamard_into(X, r, c):
+    """X[i, j] = (-1)^parity(i & j): rows (columns) of the order-65536
+    Sylvester-Hadamard matrix, orthogonal and of equal norm."""
+    j = torch.arange(c, device="cuda", dtype=torch.int32)
+    for r0 in range(0, r, 1024):
+        i = torch.arange(r0, min(r, r0 + 1024), device="cuda", dtype=torch.int32)
+        x = i[:, None] & j[None, :]
+        for sh in (8, 4, 2, 1):
+            x = x ^ (x >> sh)
+        X[r0:r0 + len(i)] = (1 - 2 * (x & 1)).float()
+
+
+@pytest.mark.parametrize("shape,precision,rel", [((32640, 65536), "bf16", 0.03),
+                                                 ((65536, 32640), "bf16", 0.03),
+                                                 ((16256, 65536), "f32", 1e-4)])
+def test_polar_largest_matrix_hadamard(shape, precision, rel):
+    """PolarNS of the largest matrix each precision takes, on Hadamard rows
+    (columns): every singular value is sqrt(max(r, c)), so the iterate stays
+    a multiple of the input and U = s_K H / sqrt(max(r, c)), with s_K the
+    Newton-Schulz recurrence of the common singular value from
+    s_0 = sqrt(max(r, c)) / (|H|_F + eps) -- which the oracle's Newton-Schulz
+    on the 1 x 1 matrix [s_0] computes.  Every entry within `rel` of it."""
+    free, _ = torch.cuda.mem_get_info()
+    if free < (80 << 30):
+        pytest.skip("needs 80 GiB of free device memory")
+    r, c = shape
+    print(f"polar_ns largest {r}x{c} {precision}", flush=True)
+    hp = B.HParams(K=5, scale="fro", precision=precision)
+    X = torch.empty((r, c), device="cuda")
+    _hadamard_into(X, r, c)
+    U = B.polar_ns(X, hp)
+    torch.cuda.synchronize()
+    o = oracle_hp(hp)
+    big = max(r, c)
+    s0 = np.sqrt(big) / (np.sqrt(float(r) * c) + o["eps"])
+    sK = float(O.newton_schulz(np.array([[s0]]), o["K"], o["coeffs"])[0, 0])
+    scale = sK / np.sqrt(big)
+    worst = 0.0
+    for r0 in range(0, r, 1024):
+        err = (U[r0:r0 + 1024] / (scale * X[r0:r0 + 1024]) - 1).abs().max().item()
+        worst = max(worst, err)
+    assert worst <= rel, worst
