@@ -214,29 +214,34 @@ def _hadamard_into(X, r, c):
         X[r0:r0 + len(i)] = (1 - 2 * (x & 1)).float()
 
 
-@pytest.mark.parametrize("shape,precision,rel", [((32640, 65536), "bf16", 0.03),
-                                                 ((65536, 32640), "bf16", 0.03),
-                                                 ((16256, 65536), "f32", 1e-4)])
-def test_polar_largest_matrix_hadamard(shape, precision, rel):
+@pytest.mark.parametrize("shape,precision,scale,rel",
+                         [((32640, 65536), "bf16", "fro", 0.03),
+                          ((65536, 32640), "bf16", "fro", 0.03),
+                          ((32640, 65536), "bf16", "spectral", 0.03),
+                          ((16256, 65536), "f32", "fro", 1e-4)])
+def test_polar_largest_matrix_hadamard(shape, precision, scale, rel):
     """PolarNS of the largest matrix each precision takes, on Hadamard rows
     (columns): every singular value is sqrt(max(r, c)), so the iterate stays
     a multiple of the input and U = s_K H / sqrt(max(r, c)), with s_K the
     Newton-Schulz recurrence of the common singular value from
-    s_0 = sqrt(max(r, c)) / (|H|_F + eps) -- which the oracle's Newton-Schulz
-    on the 1 x 1 matrix [s_0] computes.  Every entry within `rel` of it."""
+    s_0 = sqrt(max(r, c)) / (s + eps), s = |H|_F or (spectral: the power
+    iteration on a Gram that is a multiple of I, exact from any start)
+    sqrt(max(r, c)) -- which the oracle's Newton-Schulz on the 1 x 1 matrix
+    [s_0] computes.  Every entry within `rel` of it."""
     free, _ = torch.cuda.mem_get_info()
     if free < (80 << 30):
         pytest.skip("needs 80 GiB of free device memory")
     r, c = shape
-    print(f"polar_ns largest {r}x{c} {precision}", flush=True)
-    hp = B.HParams(K=5, scale="fro", precision=precision)
+    print(f"polar_ns largest {r}x{c} {precision} {scale}", flush=True)
+    hp = B.HParams(K=5, scale=scale, P=5, precision=precision)
     X = torch.empty((r, c), device="cuda")
     _hadamard_into(X, r, c)
     U = B.polar_ns(X, hp)
     torch.cuda.synchronize()
     o = oracle_hp(hp)
     big = max(r, c)
-    s0 = np.sqrt(big) / (np.sqrt(float(r) * c) + o["eps"])
+    s = np.sqrt(float(r) * c) if scale == "fro" else np.sqrt(big)
+    s0 = np.sqrt(big) / (s + o["eps"])
     sK = float(O.newton_schulz(np.array([[s0]]), o["K"], o["coeffs"])[0, 0])
     scale = sK / np.sqrt(big)
     worst = 0.0
