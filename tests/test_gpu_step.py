@@ -353,6 +353,53 @@ def test_step_odd_sizes(name, chain_mode):
         W, Moms = out["Wn"], out["Mom"]
 
 
+def _same(a, b):
+    return torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+def test_two_callers_on_two_streams(monkeypatch):
+    """Two plans, each with its own workspace and executor, stepped on two
+    streams at once (enqueued back to back with no synchronisation between
+    them) with the concurrent chains forced: each gives the weights,
+    momentum and buffers that the same plan gives alone (the step is
+    deterministic), in every one of three rounds."""
+    monkeypatch.setenv("SIGNMUON_CHAIN_MIN_GFLOP", "0")
+    w = SMALL["nanogpt"][0]
+    hp = hparams(w)
+    layout, d, words = B.default_layout(w.mats)
+    plans = [B.StepPlan(layout, hp, w.post_vote) for _ in range(2)]
+    print(f"two callers mats={len(w.mats)} M={w.M}", flush=True)
+
+    def inputs(k):
+        W = torch.from_numpy(WL.init_weights(w)).cuda().to(torch.bfloat16)
+        Mom = torch.from_numpy(WL.init_momentum(w, k, std=0.1).astype(np.float32)).cuda()
+        G = torch.from_numpy(WL.gradient(w, k, 0)).cuda()
+        bits = torch.from_numpy(WL.random_bits(w, w.M, tag=k).view(np.int32)).cuda()
+        return G, W, Mom, bits
+
+    ref = []
+    for k, p in enumerate(plans):
+        G, W, Mom, bits = inputs(k)
+        p(G, W, Mom, bits, words, w.M, 0)
+        torch.cuda.synchronize()
+        assert p.status() == B.SM_OK
+        ref.append((W.clone(), Mom.clone(), bits.clone()))
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    for rep in range(3):
+        ins = [inputs(k) for k in range(2)]
+        torch.cuda.synchronize()
+        for k, p in enumerate(plans):
+            G, W, Mom, bits = ins[k]
+            p(G, W, Mom, bits, words, w.M, 0, stream=streams[k])
+        torch.cuda.synchronize()
+        for k in range(2):
+            _, W, Mom, bits = ins[k]
+            assert _same(W, ref[k][0]) and _same(Mom, ref[k][1]) and _same(bits, ref[k][2]), \
+                (rep, k)
+            assert plans[k].status(stream=streams[k]) == B.SM_OK
+
+
 def test_step_nonfinite_skips_update():
     w = SMALL["nanogpt"][0]
     hp = hparams(w)
