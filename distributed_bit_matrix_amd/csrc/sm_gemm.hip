@@ -165,6 +165,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
 
+// s_waitcnt lgkmcnt(0): this wave's LDS reads (and scalar loads) have
+// returned; the vector-memory and export counters are left alone.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> { static constexpr int per16 = 8; };
 template <> struct Elem<float>  { static constexpr int per16 = 4; };
@@ -1069,7 +1075,7 @@ __global__ __launch_bounds__(128 * WM, WPE) void k_gemm(GemmArgs A) {
         // slab s+1 landed for this wave (later fetches may be in flight)
         if (s + NSTG - 1 < nslab) wait_vmcnt<(NSTG - 2) * LOADS>();
         else wait_vmcnt<0>();
-        __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4) | 15 | (3 << 14));  // lgkmcnt(0)
+        wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       }
